@@ -1,0 +1,384 @@
+"""CPU oracle of the CIERA exponent-reuse codec -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call this module.  The product path (the HIP
+library and its Python binding) never does, and shares no code with it.
+
+It is plain, slow and written to be checked by eye against the pages:
+
+  CIERA: Cross-Iteration Exponent Reuse for Lossless Allgather in Sharded MoE
+  Training (arXiv 2609.04609v1), cited below as [CIERA].
+
+  * [CIERA section 3.1] every value is split into its exponent bits and its
+    sign-plus-mantissa bits; the exponents of the previous iteration are
+    cached; the sender transmits the sign-plus-mantissa bits of every value,
+    a bitmap with one bit per block of B values marking the blocks whose
+    exponents changed, and the changed exponents; the receiver takes the old
+    exponents from its cache, replaces the changed ones and merges them with
+    the received sign-plus-mantissa bits.  Reconstruction is bitwise exact
+    [CIERA abstract; section 4.6, Figure 10].
+  * [CIERA Appendix A, Algorithm 1] sender: split, per-block change test,
+    bitmap, payload of changed exponents; receiver: update the exponent cache
+    for changed blocks, then merge.
+  * [CIERA section 3.2] payload model S_{s+m} + S_bm + q*S_e with
+    S_b = ceil(N/B) blocks and S_bm = ceil(S_b/8) bitmap bytes; compression is
+    applied only to shards with a positive latency gain.
+
+Readings where the pages leave the step open (each is listed with its reason
+in the design notes of the repository):
+  R1  change detection compares each exponent with the cached one exactly (the
+      pages hash whole blocks; the exact compare is what the 128-bit hash
+      approximates).
+  R2  the changed exponents travel as (u32 shard-local index, u8 exponent)
+      records in ascending index order, not entropy-coded.
+  R3  bitmap bit b (byte b//8, bit b%8, least significant first) is set when
+      block b holds at least one changed exponent; the bitmap is omitted when
+      nothing changed.
+  R4  sign|mantissa bytes: bf16 -> one byte (sign in bit 7, mantissa in bits
+      6..0); fp32 -> three little-endian bytes of (sign << 23 | mantissa).
+  R5  a 64-byte little-endian header (layout in ``HEADER_FIELDS``).
+  R6  the gain subtracts all codec costs; the link term is linear in bytes.
+  R7  the plan's change rate is the element change fraction (ppm).
+  R8  a stream is COMPRESSED only when strictly shorter than the raw stream.
+  R9  decoding a RAW stream still refreshes the cache from the raw values.
+  R12 row-sharding: rank r holds floor(R/W) + [r < R mod W] consecutive rows.
+
+Parity status: split/join, lengths, cache update and encode/decode round trip
+are pinned by exhaustive and closed-form tests; the byte layout (R2-R5) is
+pinned by hand-derived known-answer streams of the written format; the plan is
+pinned by a hand-computed decision table.  None of the byte layout is fixed by
+the pages themselves.
+"""
+from __future__ import annotations
+
+import struct
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+# ------------------------------------------------------------------ constants
+
+HEADER_BYTES = 64
+MAGIC = b"CIER"
+VERSION = 1
+BF16 = 1
+FP32 = 2
+MODE_RAW = 0
+MODE_COMPRESSED = 1
+PATCH_BYTES = 5                    # u32 index + u8 exponent
+
+# decode status bits
+ST_MAGIC = 1       # bad magic or version
+ST_FIELD = 2       # dtype / block size / n / offset / rank / world / mode mismatch
+ST_LENGTH = 4      # total_len or n_changed inconsistent, or larger than the slot
+ST_PATCH = 8       # a patch index >= n, or indices not strictly ascending
+ST_BITMAP = 16     # bitmap disagrees with the patch list (unspecified if ST_PATCH)
+
+# (name, byte offset, struct code) -- little-endian
+HEADER_FIELDS = [
+    ("magic", 0, "4s"), ("version", 4, "<H"), ("dtype", 6, "B"), ("mode", 7, "B"),
+    ("block_size", 8, "<I"), ("reserved0", 12, "<I"), ("n", 16, "<Q"),
+    ("n_changed", 24, "<Q"), ("total_len", 32, "<Q"), ("offset", 40, "<Q"),
+    ("rank", 48, "<I"), ("world", 52, "<I"), ("reserved1", 56, "<Q"),
+]
+
+
+def elem_bytes(dtype: int) -> int:
+    """e: bytes per value (16-bit bf16 and 32-bit fp32) [CIERA 3.2: S = N*b/8]."""
+    return {BF16: 2, FP32: 4}[dtype]
+
+
+def sm_bytes(dtype: int) -> int:
+    """k: sign|mantissa bytes per value (R4): everything but the 8 exponent bits."""
+    return {BF16: 1, FP32: 3}[dtype]
+
+
+def int_dtype(dtype: int):
+    return {BF16: np.uint16, FP32: np.uint32}[dtype]
+
+
+# -------------------------------------------------------- field split / merge
+# [CIERA 3.1] "splits each weight value into exponent bits and sign-plus-mantissa
+# bits".  Bit positions are those of IEEE-754 binary32 and of bfloat16 (binary32
+# with the low 16 mantissa bits dropped): sign | 8 exponent bits | mantissa.
+
+def exponent_field(u: np.ndarray, dtype: int) -> np.ndarray:
+    u = np.asarray(u).astype(np.uint32)
+    shift = 7 if dtype == BF16 else 23
+    return ((u >> shift) & 0xFF).astype(np.uint8)
+
+
+def sign_mantissa_field(u: np.ndarray, dtype: int) -> np.ndarray:
+    """bf16 -> sign<<7 | mantissa(7);  fp32 -> sign<<23 | mantissa(23)."""
+    u = np.asarray(u).astype(np.uint32)
+    if dtype == BF16:
+        return ((u >> 15) << 7) | (u & 0x7F)
+    return ((u >> 31) << 23) | (u & 0x7FFFFF)
+
+
+def join_fields(sm: np.ndarray, ex: np.ndarray, dtype: int) -> np.ndarray:
+    """Inverse of the split: Merge(exponent, sign|mantissa) [CIERA Alg. 1, receiver]."""
+    sm = np.asarray(sm).astype(np.uint32)
+    ex = np.asarray(ex).astype(np.uint32)
+    if dtype == BF16:
+        return (((sm >> 7) << 15) | (ex << 7) | (sm & 0x7F)).astype(np.uint16)
+    return (((sm >> 23) << 31) | (ex << 23) | (sm & 0x7FFFFF)).astype(np.uint32)
+
+
+def pack_sm(sm: np.ndarray, dtype: int) -> np.ndarray:
+    """Byte-pack sign|mantissa values: k little-endian bytes each (R4)."""
+    sm = np.asarray(sm).astype(np.uint32)
+    if dtype == BF16:
+        return sm.astype(np.uint8)
+    b = np.stack([sm & 0xFF, (sm >> 8) & 0xFF, (sm >> 16) & 0xFF], axis=1)
+    return b.astype(np.uint8).reshape(-1)
+
+
+def unpack_sm(b: np.ndarray, dtype: int) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    if dtype == BF16:
+        return b.astype(np.uint32)
+    t = b.reshape(-1, 3).astype(np.uint32)
+    return t[:, 0] | (t[:, 1] << 8) | (t[:, 2] << 16)
+
+
+# ------------------------------------------------------------------ sharding
+
+def shard(rows: int, cols: int, world: int, rank: int) -> Tuple[int, int]:
+    """(element offset, element count) of rank's row shard (R12).
+
+    ZeRO-3 style even partition of a row-major tensor: rank r holds
+    floor(R/W) + [r < R mod W] consecutive rows."""
+    q, rem = divmod(rows, world)
+    rows_before = rank * q + min(rank, rem)
+    my_rows = q + (1 if rank < rem else 0)
+    return rows_before * cols, my_rows * cols
+
+
+# ------------------------------------------------------------------- lengths
+# [CIERA 3.2] S_b = ceil(N/B) blocks, S_bm = ceil(S_b/8) bitmap bytes.
+
+def n_blocks(n: int, block_size: int) -> int:
+    return -(-n // block_size)
+
+
+def bitmap_bytes(n: int, block_size: int) -> int:
+    return -(-n_blocks(n, block_size) // 8)
+
+
+def raw_len(n: int, dtype: int) -> int:
+    return HEADER_BYTES + n * elem_bytes(dtype)
+
+
+def comp_len(n: int, n_changed: int, dtype: int, block_size: int) -> int:
+    """Header + all sign|mantissa bytes (+ bitmap + 5-byte patches if anything changed)."""
+    base = HEADER_BYTES + n * sm_bytes(dtype)
+    if n_changed == 0:
+        return base
+    return base + bitmap_bytes(n, block_size) + PATCH_BYTES * n_changed
+
+
+# ------------------------------------------------------------------- header
+
+def pack_header(**f) -> bytes:
+    out = bytearray(HEADER_BYTES)
+    for name, off, code in HEADER_FIELDS:
+        val = f.get(name, MAGIC if name == "magic" else 0)
+        struct.pack_into(code, out, off, val)
+    return bytes(out)
+
+
+def parse_header(buf) -> dict:
+    b = bytes(np.asarray(buf, dtype=np.uint8)[:HEADER_BYTES])
+    if len(b) < HEADER_BYTES:
+        raise ValueError("stream shorter than its header")
+    return {name: struct.unpack_from(code, b, off)[0] for name, off, code in HEADER_FIELDS}
+
+
+# -------------------------------------------------------------- cache update
+
+def cache_update(w: np.ndarray, dtype: int) -> np.ndarray:
+    """ExpCache <- exponents of the given (full) tensor [CIERA 3.1; Alg. 1 state]."""
+    return exponent_field(np.asarray(w).reshape(-1), dtype)
+
+
+# -------------------------------------------------------------------- encode
+
+def encode(x: np.ndarray, cache_slice: np.ndarray, dtype: int, block_size: int,
+           compress: bool, offset: int = 0, rank: int = 0, world: int = 1) -> np.ndarray:
+    """Sender side of one Allgather for one shard [CIERA 3.1, Alg. 1 sender].
+
+    x            -- the shard as integer bit patterns (uint16 for bf16, uint32 fp32)
+    cache_slice  -- uint8 exponents cached for the same positions last iteration
+    compress     -- the plan's decision (a RAW stream is written when 0)
+    Returns the whole stream (header included) as a uint8 array of total_len bytes.
+    """
+    x = np.ascontiguousarray(np.asarray(x).reshape(-1)).astype(int_dtype(dtype))
+    cache_slice = np.asarray(cache_slice, dtype=np.uint8).reshape(-1)
+    n = x.size
+    if cache_slice.size != n:
+        raise ValueError("cache slice and shard differ in length")
+    # 1. split
+    ex = exponent_field(x, dtype)
+    sm = sign_mantissa_field(x, dtype)
+    # 2. change detection, per element (R1)
+    changed = ex != cache_slice
+    idx = np.nonzero(changed)[0]
+    n_changed = int(idx.size)
+    # 3. lengths and mode (R8)
+    c_len = comp_len(n, n_changed, dtype, block_size)
+    r_len = raw_len(n, dtype)
+    mode = MODE_COMPRESSED if (compress and c_len < r_len) else MODE_RAW
+    total = c_len if mode == MODE_COMPRESSED else r_len
+    hdr = pack_header(version=VERSION, dtype=dtype, mode=mode, block_size=block_size,
+                      n=n, n_changed=n_changed, total_len=total, offset=offset,
+                      rank=rank, world=world)
+    out = np.zeros(total, dtype=np.uint8)
+    out[:HEADER_BYTES] = np.frombuffer(hdr, dtype=np.uint8)
+    if mode == MODE_RAW:
+        le = np.dtype(int_dtype(dtype)).newbyteorder("<")
+        out[HEADER_BYTES:] = x.astype(le).view(np.uint8)
+        return out
+    # 4. sign|mantissa bytes of every value
+    pos = HEADER_BYTES
+    out[pos:pos + n * sm_bytes(dtype)] = pack_sm(sm, dtype)
+    pos += n * sm_bytes(dtype)
+    if n_changed == 0:
+        return out
+    # 5. bitmap: one bit per block of B values that holds a change (R3)
+    nbm = bitmap_bytes(n, block_size)
+    bm = np.zeros(nbm, dtype=np.uint8)
+    blocks = np.unique(idx // block_size)
+    np.bitwise_or.at(bm, blocks // 8, (1 << (blocks % 8)).astype(np.uint8))
+    out[pos:pos + nbm] = bm
+    pos += nbm
+    # 6. changed exponents as (index, exponent) records, ascending (R2)
+    rec = np.zeros((n_changed, PATCH_BYTES), dtype=np.uint8)
+    rec[:, 0:4] = idx.astype("<u4").view(np.uint8).reshape(n_changed, 4)
+    rec[:, 4] = ex[idx]
+    out[pos:pos + PATCH_BYTES * n_changed] = rec.reshape(-1)
+    return out
+
+
+# -------------------------------------------------------------------- decode
+
+def _check_header(s: np.ndarray, dtype: int, block_size: int, n: int, offset: int,
+                  rank: int, world: int) -> Tuple[int, Optional[dict]]:
+    """Header and length validation of one received stream; (status bits, header)."""
+    if s.size < HEADER_BYTES:
+        return ST_LENGTH, None
+    h = parse_header(s)
+    if h["magic"] != MAGIC or h["version"] != VERSION:
+        return ST_MAGIC, None
+    if (h["dtype"] != dtype or h["block_size"] != block_size or h["n"] != n
+            or h["offset"] != offset or h["rank"] != rank or h["world"] != world
+            or h["mode"] not in (MODE_RAW, MODE_COMPRESSED)):
+        return ST_FIELD, None
+    p = h["n_changed"]
+    if p > n or h["total_len"] > s.size:
+        return ST_LENGTH, None
+    want = raw_len(n, dtype) if h["mode"] == MODE_RAW else comp_len(n, p, dtype, block_size)
+    if h["total_len"] != want:
+        return ST_LENGTH, None
+    return 0, h
+
+
+def decode_stream(s: np.ndarray, dtype: int, block_size: int, n: int, offset: int,
+                  rank: int, world: int, cache_slice: np.ndarray):
+    """Receiver side for one stream [CIERA 3.1, Alg. 1 receiver].
+
+    Returns (values or None, new cache slice or None, status bits)."""
+    s = np.asarray(s, dtype=np.uint8)
+    st, h = _check_header(s, dtype, block_size, n, offset, rank, world)
+    if st:
+        return None, None, st
+    pos = HEADER_BYTES
+    if h["mode"] == MODE_RAW:
+        le = np.dtype(int_dtype(dtype)).newbyteorder("<")
+        x = s[pos:pos + n * elem_bytes(dtype)].view(le).astype(int_dtype(dtype))
+        return x, exponent_field(x, dtype), 0          # R9
+    k = sm_bytes(dtype)
+    sm = unpack_sm(s[pos:pos + n * k], dtype)
+    pos += n * k
+    ex = np.array(cache_slice, dtype=np.uint8, copy=True)   # previous exponents
+    p = h["n_changed"]
+    if p > 0:
+        nbm = bitmap_bytes(n, block_size)
+        bm = s[pos:pos + nbm]
+        pos += nbm
+        rec = s[pos:pos + PATCH_BYTES * p].reshape(p, PATCH_BYTES)
+        idx = np.ascontiguousarray(rec[:, 0:4]).view("<u4").reshape(-1).astype(np.int64)
+        val = rec[:, 4]
+        if np.any(idx >= n) or np.any(np.diff(idx) <= 0):
+            st |= ST_PATCH
+        ok = idx < n
+        # bitmap must mark exactly the blocks that hold a patch (tail bits zero)
+        want = np.zeros(nbm, dtype=np.uint8)
+        blocks = np.unique(idx[ok] // block_size)
+        np.bitwise_or.at(want, blocks // 8, (1 << (blocks % 8)).astype(np.uint8))
+        if not np.array_equal(want, bm):
+            st |= ST_BITMAP
+        ex[idx[ok]] = val[ok]                            # replace changed exponents
+    return join_fields(sm, ex, dtype), ex, st
+
+
+def decode(streams: Sequence[np.ndarray], rows: int, cols: int, dtype: int,
+           block_size: int, world: int, cache_full: np.ndarray,
+           out_full: Optional[np.ndarray] = None):
+    """Rebuild the full tensor from all W ranks' streams and update the cache.
+
+    streams[r] is rank r's receive slot (at least total_len bytes).  Returns
+    (full tensor as integer bit patterns, updated cache, OR of status bits).
+    Shards whose stream fails the header/length checks are left untouched."""
+    N = rows * cols
+    cache = np.array(cache_full, dtype=np.uint8, copy=True).reshape(-1)
+    out = (np.zeros(N, dtype=int_dtype(dtype)) if out_full is None
+           else np.array(out_full, copy=True).reshape(-1))
+    status = 0
+    for r in range(world):
+        off, n = shard(rows, cols, world, r)
+        x, ex, st = decode_stream(streams[r], dtype, block_size, n, off, r, world,
+                                  cache[off:off + n])
+        status |= st
+        if x is None:
+            continue
+        out[off:off + n] = x
+        cache[off:off + n] = ex
+    return out, cache, status
+
+
+# ---------------------------------------------------------------------- plan
+# [CIERA 3.2] g_i = Comm(S^i) - [Comm(S_{s+m} + S_bm + q_i S_e) + T_hash + T_cmp + T_decmp];
+# keep the shard only if g_i > 0.  With pipelining, T_hash and T_cmp are off the
+# critical path.  Comm is linear in bytes (alpha cancels); every quantity is an
+# integer and every division floors, in the order written (R6, R7).
+
+DEFAULT_COST = dict(link_bytes_per_us=8000,         # ~8 GB/s cross-node AllGather bus BW [CIERA 4.1]
+                    hbm_bytes_per_us=5_600_000,     # 70% of 8 TB/s HBM3E
+                    fixed_ns=5000,
+                    overlap_encode=1)
+
+
+def plan(rows: int, cols: int, dtype: int, block_size: int, world: int,
+         change_ppm: int, cost: Optional[dict] = None) -> dict:
+    c = dict(DEFAULT_COST)
+    if cost:
+        c.update(cost)
+    e = elem_bytes(dtype)
+    _, n = shard(rows, cols, world, 0)                 # the largest shard
+    raw = raw_len(n, dtype)
+    p_hat = (change_ppm * n + 999_999) // 1_000_000    # ceil
+    comp = comp_len(n, p_hat, dtype, block_size)
+    res = dict(raw_stream_bytes=raw, max_stream_bytes=raw, cache_bytes=rows * cols,
+               expected_changed=p_hat)
+    if comp >= raw:
+        res.update(compress=0, expected_stream_bytes=raw, gain_ns=0)
+        return res
+    save = (raw - comp) * (world - 1) * 1000 // c["link_bytes_per_us"]
+    dec = c["fixed_ns"] + world * (comp + n + n + n * e) * 1000 // c["hbm_bytes_per_us"]
+    enc = 0 if c["overlap_encode"] else (
+        c["fixed_ns"] + (n * e + n + comp) * 1000 // c["hbm_bytes_per_us"])
+    gain = save - dec - enc
+    compress = 1 if gain > 0 else 0
+    res.update(compress=compress, expected_stream_bytes=comp if compress else raw, gain_ns=gain)
+    return res

@@ -1,0 +1,154 @@
+"""Planted mistakes in the oracle (CPU only) must each fail at least one pin.
+
+Every mutation is a plausible slip -- a wrong shift, a dropped term, a flipped
+bit order, an off-by-one that encode and decode share -- monkeypatched into the
+oracle for the duration of one check."""
+import numpy as np
+import pytest
+
+from oracle import ciera_oracle as O
+from tests import test_oracle_brute_plan as TB
+from tests import test_oracle_fields as TF
+from tests import test_oracle_stream as TS
+
+PINS = [
+    TF.test_bf16_exponent_matches_frexp_exhaustive,
+    TF.test_bf16_sign_mantissa_rebuilds_value_exhaustive,
+    TF.test_known_values,
+    TS.test_known_answer_bf16,
+    TS.test_known_answer_fp32,
+    TS.test_known_answer_fp32_raw_fallback,
+    TS.test_known_answer_zero_change_and_plan_raw,
+    TS.test_exhaustive_bf16_round_trip,
+    TS.test_tie_is_raw,
+    TS.test_payload_model_matches_pages,
+    lambda: [TB.test_plan_decision_table(r) for r in TB.PLAN_TABLE],
+    TB.test_corruption_classes,
+]
+
+
+def _some_pin_fails():
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+def _wrong_exp_shift(u, dtype):
+    u = np.asarray(u).astype(np.uint32)
+    return ((u >> (8 if dtype == O.BF16 else 23)) & 0xFF).astype(np.uint8)
+
+
+def _sm_without_sign(u, dtype):
+    u = np.asarray(u).astype(np.uint32)
+    return u & (0x7F if dtype == O.BF16 else 0x7FFFFF)
+
+
+def _comp_len_no_bitmap(n, p, dtype, B):
+    base = O.HEADER_BYTES + n * O.sm_bytes(dtype)
+    return base if p == 0 else base + O.PATCH_BYTES * p
+
+
+def _comp_len_always_bitmap(n, p, dtype, B):
+    return O.HEADER_BYTES + n * O.sm_bytes(dtype) + O.bitmap_bytes(n, B) + O.PATCH_BYTES * p
+
+
+def _msb_first_encode(orig):
+    def enc(*a, **k):
+        s = orig(*a, **k)
+        h = O.parse_header(s)
+        if h["mode"] == O.MODE_COMPRESSED and h["n_changed"]:
+            n = h["n"]
+            off = 64 + n * O.sm_bytes(h["dtype"])
+            nbm = O.bitmap_bytes(n, h["block_size"])
+            bm = s[off:off + nbm]
+            s = s.copy()
+            s[off:off + nbm] = np.packbits(np.unpackbits(bm, bitorder="little"), bitorder="big")
+        return s
+    return enc
+
+
+def _index_plus_one(orig_enc, orig_dec):
+    def enc(*a, **k):
+        s = orig_enc(*a, **k).copy()
+        h = O.parse_header(s)
+        if h["mode"] == O.MODE_COMPRESSED and h["n_changed"]:
+            n, p = h["n"], h["n_changed"]
+            pb = 64 + n * O.sm_bytes(h["dtype"]) + O.bitmap_bytes(n, h["block_size"])
+            rec = s[pb:pb + 5 * p].reshape(p, 5)
+            idx = rec[:, :4].copy().view("<u4").reshape(-1) + 1
+            rec[:, :4] = idx.astype("<u4").view(np.uint8).reshape(p, 4)
+        return s
+
+    def dec(s, dtype, B, n, off, rank, world, cache_slice):
+        s = np.asarray(s, np.uint8).copy()
+        try:
+            h = O.parse_header(s)
+        except ValueError:
+            return orig_dec(s, dtype, B, n, off, rank, world, cache_slice)
+        if h["magic"] == O.MAGIC and h["mode"] == O.MODE_COMPRESSED and 0 < h["n_changed"] <= n:
+            p = h["n_changed"]
+            pb = 64 + n * O.sm_bytes(dtype) + O.bitmap_bytes(n, B)
+            if pb + 5 * p <= s.size:
+                rec = s[pb:pb + 5 * p].reshape(p, 5)
+                idx = rec[:, :4].copy().view("<u4").reshape(-1) - 1
+                rec[:, :4] = idx.astype("<u4").view(np.uint8).reshape(p, 4)
+        return orig_dec(s, dtype, B, n, off, rank, world, cache_slice)
+    return enc, dec
+
+
+def _decode_skips_patches(orig):
+    def dec(s, dtype, B, n, off, rank, world, cache_slice):
+        x, ex, st = orig(s, dtype, B, n, off, rank, world, cache_slice)
+        if x is None or O.parse_header(np.asarray(s, np.uint8))["mode"] == O.MODE_RAW:
+            return x, ex, st
+        sm = O.sign_mantissa_field(x, dtype)
+        return O.join_fields(sm, cache_slice, dtype), np.array(cache_slice), st
+    return dec
+
+
+def _plan_dec_without_world(rows, cols, dtype, B, world, ppm, cost=None):
+    c = dict(O.DEFAULT_COST)
+    _, n = O.shard(rows, cols, world, 0)
+    raw = O.raw_len(n, dtype)
+    p_hat = (ppm * n + 999_999) // 1_000_000
+    comp = O.comp_len(n, p_hat, dtype, B)
+    if comp >= raw:
+        return dict(compress=0, expected_stream_bytes=raw, gain_ns=0)
+    save = (raw - comp) * (world - 1) * 1000 // c["link_bytes_per_us"]
+    dec = c["fixed_ns"] + (comp + 2 * n + n * O.elem_bytes(dtype)) * 1000 // c["hbm_bytes_per_us"]
+    g = save - dec
+    return dict(compress=int(g > 0), expected_stream_bytes=comp if g > 0 else raw, gain_ns=g)
+
+
+def _check_raw_tie_compress(orig):
+    def cl(n, p, dtype, B):
+        return orig(n, p, dtype, B) - (1 if p else 0)
+    return cl
+
+
+MUTATIONS = {
+    "exponent shift off by one bit": lambda mp: mp.setattr(O, "exponent_field", _wrong_exp_shift),
+    "sign bit dropped": lambda mp: mp.setattr(O, "sign_mantissa_field", _sm_without_sign),
+    "bitmap length dropped": lambda mp: mp.setattr(O, "comp_len", _comp_len_no_bitmap),
+    "bitmap kept when nothing changed": lambda mp: mp.setattr(O, "comp_len", _comp_len_always_bitmap),
+    "bitmap most-significant bit first": lambda mp: mp.setattr(O, "encode", _msb_first_encode(O.encode)),
+    "patch index off by one (shared)": lambda mp: (
+        lambda ed: (mp.setattr(O, "encode", ed[0]), mp.setattr(O, "decode_stream", ed[1])))(
+        _index_plus_one(O.encode, O.decode_stream)),
+    "decode ignores patches": lambda mp: mp.setattr(O, "decode_stream", _decode_skips_patches(O.decode_stream)),
+    "plan drops the W factor of decode": lambda mp: mp.setattr(O, "plan", _plan_dec_without_world),
+    "tie resolved as compressed": lambda mp: mp.setattr(O, "comp_len", _check_raw_tie_compress(O.comp_len)),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    MUTATIONS[name](monkeypatch)
+    assert _some_pin_fails(), f"no pin caught: {name}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert not _some_pin_fails()
