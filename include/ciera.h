@@ -1,0 +1,187 @@
+/*
+ * ciera.h -- C ABI of the CIERA exponent-reuse codec for MI355X (gfx950).
+ *
+ * Method: "CIERA: Cross-Iteration Exponent Reuse for Lossless Allgather in
+ * Sharded MoE Training" (arXiv 2609.04609v1), cited as [CIERA].  Every value of
+ * a rank's weight shard is split into exponent and sign|mantissa bits; the
+ * exponents of the previous iteration are cached on every rank; a rank sends
+ * the sign|mantissa bits of all its values plus only the exponents that
+ * changed, and every receiver rebuilds the full tensor bit-exactly from its
+ * cache [CIERA section 3.1; Appendix A, Algorithm 1].  A per-tensor selector
+ * keeps compression only where it saves time [CIERA section 3.2].
+ *
+ * Stream format (one stream per (tensor, rank); all integers little-endian):
+ *   header, 64 bytes:
+ *     [0,4) "CIER"  [4,6) version=1  [6] dtype  [7] mode (0 RAW, 1 COMPRESSED)
+ *     [8,12) block size B  [12,16) 0  [16,24) n  [24,32) n_changed
+ *     [32,40) total_len  [40,48) element offset of the shard in the tensor
+ *     [48,52) rank  [52,56) world  [56,64) 0
+ *   COMPRESSED body: n sign|mantissa records (bf16: 1 byte, sign in bit 7 and
+ *     the 7 mantissa bits below; fp32: 3 bytes of sign<<23|mantissa), then --
+ *     only if n_changed > 0 -- a bitmap of ceil(ceil(n/B)/8) bytes (bit b =
+ *     byte b/8, bit b%8: block b of B values holds a changed exponent), then
+ *     n_changed records of 5 bytes (u32 shard-local index, u8 exponent) in
+ *     strictly ascending index order.
+ *   RAW body: the n values as stored (2 or 4 bytes each).
+ *   A stream is COMPRESSED only if the plan asked for it and it is strictly
+ *   shorter than the RAW stream (64 + n*element bytes).
+ *
+ * Sharding: a tensor of rows x cols (row-major; a 1-D vector is rows=len,
+ * cols=1) is split over W ranks by rows; rank r holds floor(R/W) + [r < R%W]
+ * consecutive rows (ZeRO-style even partition).
+ *
+ * Conventions for every device call:
+ *   - all pointers are device pointers of the current HIP device unless noted;
+ *     the caller owns every buffer; nothing is retained after the call returns
+ *     except what the call's kernels still read until they complete;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream);
+ *     calls are asynchronous on it and never synchronize the host with it;
+ *   - argument errors are returned synchronously, before anything is enqueued;
+ *     CIERA_ERR_DEVICE reports a failed HIP call (copy or launch);
+ *   - a call may be issued concurrently with other calls on other streams only
+ *     with scratch buffers of its own.
+ */
+#ifndef CIERA_H
+#define CIERA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CIERA_ABI_VERSION 1u
+#define CIERA_HEADER_BYTES 64u
+
+typedef enum { CIERA_BF16 = 1, CIERA_FP32 = 2 } ciera_dtype_t;
+
+typedef enum {
+  CIERA_OK = 0,
+  CIERA_ERR_INVALID_ARG = 1,      /* null / misaligned pointer, bad dtype, B, world, rank */
+  CIERA_ERR_BUFFER_TOO_SMALL = 2, /* stream capacity, slot or scratch too small */
+  CIERA_ERR_UNSUPPORTED = 3,      /* a shard of >= 2^32 values, or sizes beyond 2^48 */
+  CIERA_ERR_DEVICE = 4            /* a HIP runtime call failed */
+} ciera_status_t;
+
+/* Bits OR-ed into *status_dev by ciera_decode (the caller zeroes it first). */
+#define CIERA_ST_MAGIC 1u  /* bad magic or version */
+#define CIERA_ST_FIELD 2u  /* dtype, B, n, offset, rank, world or mode mismatch */
+#define CIERA_ST_LENGTH 4u /* total_len / n_changed inconsistent or beyond the slot */
+#define CIERA_ST_PATCH 8u  /* a patch index >= n, or indices not strictly ascending */
+#define CIERA_ST_BITMAP 16u /* bitmap disagrees with the patches (unspecified with ST_PATCH) */
+
+/* One logical tensor and how it is sharded.  block_size is B, a power of two in
+ * [64, 4096] (the pages sweep 256..4096 and default to 512 [CIERA 4.1, 4.5]). */
+typedef struct {
+  uint64_t rows, cols;
+  uint32_t dtype;      /* ciera_dtype_t */
+  uint32_t block_size; /* B */
+  uint32_t world;      /* W >= 1 */
+  uint32_t reserved;   /* 0 */
+} ciera_tensor_t;
+
+/* Cost model of the selector: bytes per microsecond of the Allgather bus and of
+ * HBM, a fixed per-kernel cost, and whether encode is overlapped with other work
+ * (then it costs nothing on the critical path [CIERA 3.2, 3.3]). */
+typedef struct {
+  uint64_t link_bytes_per_us; /* default 8000: ~8 GB/s cross-node AllGather bus [CIERA 4.1] */
+  uint64_t hbm_bytes_per_us;  /* default 5,600,000: 70% of 8 TB/s */
+  uint64_t fixed_ns;          /* default 5000 */
+  uint32_t overlap_encode;    /* default 1 */
+  uint32_t reserved;
+} ciera_cost_model_t;
+
+typedef struct {
+  uint32_t compress;              /* 1: encode COMPRESSED (subject to the length rule) */
+  uint32_t reserved;
+  uint64_t raw_stream_bytes;      /* 64 + n0*e for the largest shard n0 (rank 0) */
+  uint64_t max_stream_bytes;      /* capacity every stream / receive slot needs */
+  uint64_t expected_stream_bytes; /* model payload of rank 0 at the given change rate */
+  uint64_t expected_changed;      /* ceil(change_ppm * n0 / 1e6) */
+  uint64_t cache_bytes;           /* exponent cache per rank: one byte per tensor value */
+  int64_t gain_ns;                /* modelled saving per Allgather; 0 when comp >= raw */
+} ciera_plan_t;
+
+/* ciera_plan -- per-tensor selector [CIERA 3.2]:
+ *   g = Comm(S) - [Comm(S') + T_enc + T_dec], compress iff g > 0.
+ * With n0 = rank 0's shard, P = ceil(change_ppm*n0/1e6), comp/raw the stream
+ * lengths above (all integer, divisions floor in this order):
+ *   save = (raw-comp)*(W-1)*1000 / link;  dec = fixed + W*(comp+2*n0+n0*e)*1000 / hbm;
+ *   enc  = overlap ? 0 : fixed + (n0*e+n0+comp)*1000 / hbm;  gain = save-dec-enc.
+ * If comp >= raw the answer is RAW with gain 0.  Host only, pure; cm may be NULL
+ * for the defaults.  Errors: INVALID_ARG for a bad tensor or null t/out. */
+ciera_status_t ciera_plan(const ciera_tensor_t* t, uint32_t change_ppm,
+                          const ciera_cost_model_t* cm, ciera_plan_t* out);
+
+/* ciera_shard -- element offset and count of rank's row shard.  Host only. */
+ciera_status_t ciera_shard(const ciera_tensor_t* t, uint32_t rank, uint64_t* offset,
+                           uint64_t* n);
+
+/* One rank's shard of one tensor to encode. */
+typedef struct {
+  ciera_tensor_t t;
+  uint32_t rank;              /* < t.world */
+  uint32_t compress;          /* the plan's decision; 0 always writes RAW */
+  const void* shard;          /* n_r values of t.dtype; 16-byte aligned */
+  const uint8_t* cache_full;  /* N = rows*cols cached exponents; [off_r, off_r+n_r) is read */
+  uint8_t* stream;            /* output; 16-byte aligned */
+  uint64_t stream_capacity;   /* >= 64 + n_r*e (the RAW length) */
+} ciera_encode_item_t;
+
+/* ciera_encode_scratch_bytes -- device scratch ciera_encode needs for this batch. */
+ciera_status_t ciera_encode_scratch_bytes(const ciera_encode_item_t* items, uint32_t count,
+                                          uint64_t* bytes);
+
+/* ciera_encode -- sender side of one Allgather for `count` shards in one batch
+ * [CIERA 3.1; Algorithm 1 sender]: split every value, compare its exponent with
+ * the cached one, write the sign|mantissa bytes, the per-block bitmap and the
+ * ascending (index, exponent) patch list, or a RAW stream when the plan says so
+ * or when the compressed stream would not be shorter.  Each stream's header
+ * (total_len, n_changed, mode) is written on the device; the host is never
+ * synchronized.  Bytes of a stream past its total_len are unspecified.
+ * `items` is a host array.  Scratch: a device buffer of at least
+ * ciera_encode_scratch_bytes, 256-byte aligned, used only until the call's
+ * kernels complete.  Encode cannot fail on data: every bit pattern is valid. */
+ciera_status_t ciera_encode(const ciera_encode_item_t* items, uint32_t count, void* scratch,
+                            uint64_t scratch_bytes, void* stream);
+
+/* The W received streams of one tensor. */
+typedef struct {
+  ciera_tensor_t t;
+  const uint8_t* streams; /* rank r's stream starts at streams + r*slot_bytes; 16-byte aligned */
+  uint64_t slot_bytes;    /* multiple of 16, >= 64; every stream must fit its slot */
+  void* out_full;         /* N values, rebuilt; 16-byte aligned */
+  uint8_t* cache_full;    /* N bytes: exponents of the previous iteration, updated in place */
+} ciera_decode_item_t;
+
+/* ciera_decode_scratch_bytes -- device scratch ciera_decode needs for this batch. */
+ciera_status_t ciera_decode_scratch_bytes(const ciera_decode_item_t* items, uint32_t count,
+                                          uint64_t* bytes);
+
+/* ciera_decode -- receiver side [CIERA 3.1; Algorithm 1 receiver]: for every
+ * rank's stream take the cached exponents of its shard, replace the changed
+ * ones, merge them with the sign|mantissa bytes into out_full and leave the
+ * cache equal to the exponents of the rebuilt values.  RAW streams are copied
+ * and refresh the cache too.  Validation sets CIERA_ST_* bits in *status_dev
+ * (a device uint32_t the caller zeroed); a shard whose header or lengths are
+ * bad is left untouched, a shard with bad patches or bitmap is rebuilt in an
+ * unspecified way -- in no case is memory outside the item's buffers touched.
+ * `items` is a host array.  Scratch as for encode. */
+ciera_status_t ciera_decode(const ciera_decode_item_t* items, uint32_t count,
+                            uint32_t* status_dev, void* scratch, uint64_t scratch_bytes,
+                            void* stream);
+
+/* ciera_cache_update -- cache_full[i] = exponent of weights_full[i] for the
+ * whole tensor: seeds the cache when exponent reuse is switched on after
+ * warmup [CIERA 2.2, 3.1].  weights_full 16-byte aligned. */
+ciera_status_t ciera_cache_update(const ciera_tensor_t* t, const void* weights_full,
+                                  uint8_t* cache_full, void* stream);
+
+const char* ciera_status_str(ciera_status_t s);
+uint32_t ciera_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CIERA_H */

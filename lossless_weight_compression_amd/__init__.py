@@ -1,0 +1,12 @@
+"""CIERA exponent-reuse codec for MI355X (gfx950).
+
+``_binding`` mirrors include/ciera.h (ciera_plan, ciera_shard, ciera_encode,
+ciera_decode, ciera_cache_update, ...) over the in-tree libciera.so; ``layer``
+holds a layer's caches, receive slots and outputs in flat device buffers.
+Importing fails loudly when the library has not been built.
+"""
+from ._binding import *  # noqa: F401,F403
+from ._binding import (CieraError, CostModel, DecodeItem, EncodeItem, Plan, Tensor,  # noqa: F401
+                       ciera_abi_version, ciera_cache_update, ciera_decode,
+                       ciera_decode_scratch_bytes, ciera_encode, ciera_encode_scratch_bytes,
+                       ciera_plan, ciera_shard, ciera_status_str, decode_item, encode_item)

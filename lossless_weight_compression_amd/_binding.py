@@ -1,0 +1,186 @@
+"""ctypes binding of libciera.so: same names as include/ciera.h, argument
+marshalling only.  Every step of encode/decode runs in the HIP kernels; there
+is no fallback -- importing this module fails if the library is not built."""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_int, c_int64, c_uint32, c_uint64, c_void_p
+from typing import List, Optional, Sequence, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libciera.so")
+
+CIERA_BF16, CIERA_FP32 = 1, 2
+CIERA_OK, CIERA_ERR_INVALID_ARG, CIERA_ERR_BUFFER_TOO_SMALL, CIERA_ERR_UNSUPPORTED, CIERA_ERR_DEVICE = range(5)
+CIERA_ST_MAGIC, CIERA_ST_FIELD, CIERA_ST_LENGTH, CIERA_ST_PATCH, CIERA_ST_BITMAP = 1, 2, 4, 8, 16
+HEADER_BYTES = 64
+
+# every symbol include/ciera.h declares
+EXPORTS = ["ciera_plan", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
+           "ciera_decode_scratch_bytes", "ciera_decode", "ciera_cache_update",
+           "ciera_status_str", "ciera_abi_version"]
+
+
+class CieraError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {_lib.ciera_status_str(code).decode()} ({code})")
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("rows", c_uint64), ("cols", c_uint64), ("dtype", c_uint32),
+                ("block_size", c_uint32), ("world", c_uint32), ("reserved", c_uint32)]
+
+    def __init__(self, rows=0, cols=1, dtype=CIERA_BF16, block_size=512, world=1):
+        super().__init__(rows, cols, dtype, block_size, world, 0)
+
+
+class CostModel(ctypes.Structure):
+    _fields_ = [("link_bytes_per_us", c_uint64), ("hbm_bytes_per_us", c_uint64),
+                ("fixed_ns", c_uint64), ("overlap_encode", c_uint32), ("reserved", c_uint32)]
+
+    def __init__(self, link_bytes_per_us=8000, hbm_bytes_per_us=5_600_000, fixed_ns=5000,
+                 overlap_encode=1):
+        super().__init__(link_bytes_per_us, hbm_bytes_per_us, fixed_ns, overlap_encode, 0)
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("compress", c_uint32), ("reserved", c_uint32), ("raw_stream_bytes", c_uint64),
+                ("max_stream_bytes", c_uint64), ("expected_stream_bytes", c_uint64),
+                ("expected_changed", c_uint64), ("cache_bytes", c_uint64), ("gain_ns", c_int64)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+
+
+class EncodeItem(ctypes.Structure):
+    _fields_ = [("t", Tensor), ("rank", c_uint32), ("compress", c_uint32), ("shard", c_void_p),
+                ("cache_full", c_void_p), ("stream", c_void_p), ("stream_capacity", c_uint64)]
+
+
+class DecodeItem(ctypes.Structure):
+    _fields_ = [("t", Tensor), ("streams", c_void_p), ("slot_bytes", c_uint64),
+                ("out_full", c_void_p), ("cache_full", c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "ciera_plan": (c_int, [POINTER(Tensor), c_uint32, POINTER(CostModel), POINTER(Plan)]),
+        "ciera_shard": (c_int, [POINTER(Tensor), c_uint32, POINTER(c_uint64), POINTER(c_uint64)]),
+        "ciera_encode_scratch_bytes": (c_int, [POINTER(EncodeItem), c_uint32, POINTER(c_uint64)]),
+        "ciera_encode": (c_int, [POINTER(EncodeItem), c_uint32, c_void_p, c_uint64, c_void_p]),
+        "ciera_decode_scratch_bytes": (c_int, [POINTER(DecodeItem), c_uint32, POINTER(c_uint64)]),
+        "ciera_decode": (c_int, [POINTER(DecodeItem), c_uint32, c_void_p, c_void_p, c_uint64, c_void_p]),
+        "ciera_cache_update": (c_int, [POINTER(Tensor), c_void_p, c_void_p, c_void_p]),
+        "ciera_status_str": (c_char_p, [c_int]),
+        "ciera_abi_version": (c_uint32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(code: int, where: str) -> None:
+    if code != CIERA_OK:
+        raise CieraError(code, where)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a torch tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _items_array(cls, items: Sequence):
+    arr = (cls * max(len(items), 1))()
+    for i, it in enumerate(items):
+        arr[i] = it
+    return arr
+
+
+# ------------------------------------------------------------------ host calls
+
+def ciera_abi_version() -> int:
+    return _lib.ciera_abi_version()
+
+
+def ciera_status_str(code: int) -> str:
+    return _lib.ciera_status_str(code).decode()
+
+
+def ciera_plan(t: Tensor, change_ppm: int, cost: Optional[CostModel] = None) -> Plan:
+    out = Plan()
+    _check(_lib.ciera_plan(byref(t), change_ppm, byref(cost) if cost is not None else None,
+                           byref(out)), "ciera_plan")
+    return out
+
+
+def ciera_shard(t: Tensor, rank: int) -> Tuple[int, int]:
+    off, n = c_uint64(), c_uint64()
+    _check(_lib.ciera_shard(byref(t), rank, byref(off), byref(n)), "ciera_shard")
+    return off.value, n.value
+
+
+def ciera_encode_scratch_bytes(items: Sequence[EncodeItem]) -> int:
+    b = c_uint64()
+    _check(_lib.ciera_encode_scratch_bytes(_items_array(EncodeItem, items), len(items), byref(b)),
+           "ciera_encode_scratch_bytes")
+    return b.value
+
+
+def ciera_decode_scratch_bytes(items: Sequence[DecodeItem]) -> int:
+    b = c_uint64()
+    _check(_lib.ciera_decode_scratch_bytes(_items_array(DecodeItem, items), len(items), byref(b)),
+           "ciera_decode_scratch_bytes")
+    return b.value
+
+
+# ---------------------------------------------------------------- device calls
+
+def encode_item(t: Tensor, rank: int, compress: int, shard, cache_full, stream_buf,
+                capacity: Optional[int] = None) -> EncodeItem:
+    cap = capacity if capacity is not None else stream_buf.numel() * stream_buf.element_size()
+    return EncodeItem(t, rank, 1 if compress else 0, _ptr(shard), _ptr(cache_full), _ptr(stream_buf), cap)
+
+
+def decode_item(t: Tensor, streams, slot_bytes: int, out_full, cache_full) -> DecodeItem:
+    return DecodeItem(t, _ptr(streams), slot_bytes, _ptr(out_full), _ptr(cache_full))
+
+
+def ciera_encode(items: Sequence[EncodeItem], scratch, scratch_bytes: Optional[int] = None,
+                 stream=None) -> None:
+    nbytes = scratch_bytes if scratch_bytes is not None else scratch.numel() * scratch.element_size()
+    _check(_lib.ciera_encode(_items_array(EncodeItem, items), len(items), _ptr(scratch), nbytes,
+                             _stream(stream)), "ciera_encode")
+
+
+def ciera_decode(items: Sequence[DecodeItem], status, scratch, scratch_bytes: Optional[int] = None,
+                 stream=None) -> None:
+    nbytes = scratch_bytes if scratch_bytes is not None else scratch.numel() * scratch.element_size()
+    _check(_lib.ciera_decode(_items_array(DecodeItem, items), len(items), _ptr(status), _ptr(scratch),
+                             nbytes, _stream(stream)), "ciera_decode")
+
+
+def ciera_cache_update(t: Tensor, weights_full, cache_full, stream=None) -> None:
+    _check(_lib.ciera_cache_update(byref(t), _ptr(weights_full), _ptr(cache_full), _stream(stream)),
+           "ciera_cache_update")

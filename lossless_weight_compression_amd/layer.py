@@ -1,0 +1,116 @@
+"""A layer's worth of codec state on one GPU, laid out for HBM.
+
+For a list of tensors sharded over W ranks this holds, in three flat device
+buffers, what one rank keeps across iterations and receives each iteration:
+
+  cache   -- one byte per value of every full tensor (the exponent cache)
+  streams -- the receive buffer of the Allgather: per tensor, W slots of
+             ``slot_bytes`` (the RAW length of the largest shard, rounded up to
+             16 bytes); rank r's stream of tensor i sits in slot (i, r)
+  out     -- the rebuilt full tensors
+
+and issues one batched ``ciera_encode`` (a rank's shards of every tensor) or one
+batched ``ciera_decode`` (every tensor from all W slots) per call.  torch is
+used for device memory and streams only.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _binding as B
+
+TORCH_TO_CIERA = {torch.bfloat16: B.CIERA_BF16, torch.float32: B.CIERA_FP32}
+ELEM = {B.CIERA_BF16: 2, B.CIERA_FP32: 4}
+
+
+def _align(x: int, a: int) -> int:
+    return (x + a - 1) // a * a
+
+
+class LayerCodec:
+    def __init__(self, shapes: Sequence[Tuple[int, int]], dtype: torch.dtype, world: int,
+                 block_size: int = 512, device="cuda", change_ppm: int = 10_000,
+                 cost: Optional[B.CostModel] = None, with_out: bool = True):
+        self.dtype = dtype
+        self.cdtype = TORCH_TO_CIERA[dtype]
+        self.e = ELEM[self.cdtype]
+        self.world = world
+        self.device = torch.device(device)
+        self.tensors = [B.Tensor(r, c, self.cdtype, block_size, world) for r, c in shapes]
+        self.numel = [r * c for r, c in shapes]
+        self.plans = [B.ciera_plan(t, change_ppm, cost) for t in self.tensors]
+        self.slot_bytes = [_align(p.max_stream_bytes, 16) for p in self.plans]
+        # flat buffers with 256-byte aligned per-tensor regions
+        self.cache_off, self.stream_off, self.out_off = [], [], []
+        c = s = o = 0
+        for i, n in enumerate(self.numel):
+            self.cache_off.append(c)
+            c += _align(n, 256)
+            self.stream_off.append(s)
+            s += _align(self.slot_bytes[i] * world, 256)
+            self.out_off.append(o)
+            o += _align(n * self.e, 256)
+        self.cache = torch.zeros(max(c, 256), dtype=torch.uint8, device=self.device)
+        self.streams = torch.zeros(max(s, 256), dtype=torch.uint8, device=self.device)
+        self.out = (torch.zeros(max(o, 256), dtype=torch.uint8, device=self.device)
+                    if with_out else None)
+        self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self._dec_items = [B.decode_item(t, self.streams.data_ptr() + self.stream_off[i], self.slot_bytes[i],
+                                         (self.out.data_ptr() + self.out_off[i]) if with_out else None,
+                                         self.cache.data_ptr() + self.cache_off[i])
+                           for i, t in enumerate(self.tensors)]
+        self.dec_scratch = torch.empty(max(B.ciera_decode_scratch_bytes(self._dec_items), 256),
+                                       dtype=torch.uint8, device=self.device)
+        self._enc_scratch = None
+
+    # ------------------------------------------------------------------ views
+    def shard(self, i: int, rank: int) -> Tuple[int, int]:
+        return B.ciera_shard(self.tensors[i], rank)
+
+    def cache_view(self, i: int) -> torch.Tensor:
+        return self.cache[self.cache_off[i]:self.cache_off[i] + self.numel[i]]
+
+    def slot(self, i: int, rank: int) -> torch.Tensor:
+        a = self.stream_off[i] + rank * self.slot_bytes[i]
+        return self.streams[a:a + self.slot_bytes[i]]
+
+    def out_view(self, i: int) -> torch.Tensor:
+        a = self.out_off[i]
+        return self.out[a:a + self.numel[i] * self.e].view(self.dtype)
+
+    # ------------------------------------------------------------------ calls
+    def seed_cache(self, weights: Sequence[torch.Tensor], stream=None) -> None:
+        """cache <- exponents of the given full tensors (exponent reuse switched on)."""
+        for i, w in enumerate(weights):
+            B.ciera_cache_update(self.tensors[i], w, self.cache.data_ptr() + self.cache_off[i], stream)
+
+    def encode_items(self, rank: int, shards: Sequence[torch.Tensor],
+                     compress: Optional[Sequence[int]] = None) -> List[B.EncodeItem]:
+        items = []
+        for i, t in enumerate(self.tensors):
+            c = self.plans[i].compress if compress is None else compress[i]
+            a = self.stream_off[i] + rank * self.slot_bytes[i]
+            items.append(B.encode_item(t, rank, c, shards[i], self.cache.data_ptr() + self.cache_off[i],
+                                       self.streams.data_ptr() + a, self.slot_bytes[i]))
+        return items
+
+    def encode_scratch(self, items: Sequence[B.EncodeItem]) -> torch.Tensor:
+        need = max(B.ciera_encode_scratch_bytes(items), 256)
+        if self._enc_scratch is None or self._enc_scratch.numel() < need:
+            self._enc_scratch = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._enc_scratch
+
+    def encode(self, rank: int, shards: Sequence[torch.Tensor], stream=None,
+               compress: Optional[Sequence[int]] = None, items=None) -> None:
+        """Encode rank's shard of every tensor into its slots (one batched call)."""
+        items = items if items is not None else self.encode_items(rank, shards, compress)
+        B.ciera_encode(items, self.encode_scratch(items), stream=stream)
+
+    def decode(self, stream=None, zero_status: bool = True) -> torch.Tensor:
+        """Rebuild every tensor from its W slots and update the cache (one batched call)."""
+        if zero_status:
+            self.status.zero_()
+        B.ciera_decode(self._dec_items, self.status, self.dec_scratch, stream=stream)
+        return self.status

@@ -1,0 +1,146 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-only logic (plan, shard, argument checks) agrees with
+the oracle.  No device call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import ciera_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ciera.h")
+
+L = pytest.importorskip("lossless_weight_compression_amd")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ciera_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(L._binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", L._binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ciera_\w+)", out))
+    missing = set(declared_symbols()) - exported
+    assert not missing, missing
+    lib = ctypes.CDLL(L._binding.LIB_PATH)
+    for s in declared_symbols():
+        assert hasattr(lib, s)
+
+
+def test_abi_version_and_strings():
+    assert L.ciera_abi_version() == 1
+    assert L.ciera_status_str(0) == "ok"
+    assert "buffer" in L.ciera_status_str(2)
+
+
+def _rand_tensors(seed, count):
+    rng = np.random.default_rng(seed)
+    for _ in range(count):
+        rows = int(rng.choice([0, 1, 7, 448, 1024, 2048, 7168, int(rng.integers(1, 100000))]))
+        cols = int(rng.choice([1, 3, 256, 1024, 2048, int(rng.integers(1, 5000))]))
+        yield (rows, cols, int(rng.choice([1, 2])), int(2 ** rng.integers(6, 13)),
+               int(rng.choice([1, 2, 4, 8, 16, 64, int(rng.integers(1, 200))])))
+
+
+def test_plan_parity_with_oracle():
+    rng = np.random.default_rng(3)
+    for rows, cols, dt, B, W in _rand_tensors(1, 3000):
+        ppm = int(rng.choice([0, 1, 100, 1000, 10000, 50000, 190000, 300000, 1000000,
+                              int(rng.integers(0, 1000001))]))
+        cost = dict(link_bytes_per_us=int(rng.choice([8000, 153000, 1, 10 ** 7])),
+                    hbm_bytes_per_us=int(rng.choice([5_600_000, 8_000_000, 1000])),
+                    fixed_ns=int(rng.choice([0, 5000, 100000])),
+                    overlap_encode=int(rng.integers(0, 2)))
+        p = L.ciera_plan(L.Tensor(rows, cols, dt, B, W), ppm, L.CostModel(**cost))
+        q = O.plan(rows, cols, dt, B, W, ppm, cost)
+        assert p.compress == q["compress"]
+        assert p.raw_stream_bytes == q["raw_stream_bytes"] == p.max_stream_bytes
+        assert p.expected_stream_bytes == q["expected_stream_bytes"]
+        assert p.gain_ns == q["gain_ns"]
+        assert p.expected_changed == q["expected_changed"]
+        assert p.cache_bytes == rows * cols
+
+
+def test_plan_defaults_match_hand_table():
+    from tests.test_oracle_brute_plan import PLAN_TABLE
+    for rows, cols, dt, W, ppm, compress, expected, gain in PLAN_TABLE:
+        p = L.ciera_plan(L.Tensor(rows, cols, dt, 512, W), ppm)
+        assert (p.compress, p.expected_stream_bytes, p.gain_ns) == (compress, expected, gain)
+
+
+def test_shard_parity_with_oracle():
+    for rows, cols, dt, B, W in _rand_tensors(2, 500):
+        t = L.Tensor(rows, cols, dt, B, W)
+        for r in range(W):
+            assert L.ciera_shard(t, r) == O.shard(rows, cols, W, r)
+
+
+def test_argument_errors_are_synchronous():
+    bad = [L.Tensor(4, 4, 3, 512, 1), L.Tensor(4, 4, 1, 500, 1), L.Tensor(4, 4, 1, 32, 1),
+           L.Tensor(4, 4, 1, 8192, 1), L.Tensor(4, 4, 1, 512, 0)]
+    for t in bad:
+        with pytest.raises(L.CieraError) as e:
+            L.ciera_plan(t, 100)
+        assert e.value.code == 1
+    with pytest.raises(L.CieraError):
+        L.ciera_plan(L.Tensor(4, 4, 1, 512, 1), 1_000_001)
+    with pytest.raises(L.CieraError) as e:
+        L.ciera_shard(L.Tensor(4, 4, 1, 512, 2), 2)
+    assert e.value.code == 1
+    with pytest.raises(L.CieraError) as e:
+        L.ciera_plan(L.Tensor(1 << 33, 1 << 20, 1, 512, 1), 100)
+    assert e.value.code == 3
+
+
+def test_encode_decode_validation_without_device():
+    t = L.Tensor(64, 64, 1, 512, 2)
+    good = dict(shard=0x10000, cache_full=0x20000, stream_buf=0x30000)
+
+    def enc(**kw):
+        a = dict(good, **kw)
+        it = L.encode_item(t, kw.get("rank", 0), 1, a["shard"], a["cache_full"], a["stream_buf"],
+                           kw.get("cap", 64 + 32 * 64 * 2))
+        need = L.ciera_encode_scratch_bytes([it])
+        L.ciera_encode([it], kw.get("scratch", 0x40000), kw.get("sbytes", need), stream=0)
+
+    cases = [(dict(shard=0x10008), 1), (dict(stream_buf=0x30004), 1), (dict(stream_buf=0), 1),
+             (dict(cap=64 + 32 * 64 * 2 - 1), 2), (dict(scratch=0x40010), 1), (dict(sbytes=16), 2),
+             (dict(rank=2), 1)]
+    for kw, code in cases:
+        with pytest.raises(L.CieraError) as e:
+            enc(**kw)
+        assert e.value.code == code, kw
+    # decode
+    d = L.decode_item(t, 0x30000, 64 + 32 * 64 * 2 + 16, 0x50000, 0x20000)
+    need = L.ciera_decode_scratch_bytes([d])
+    for kw, code in [(dict(streams=0x30008), 1), (dict(slot_bytes=40), 1), (dict(slot_bytes=48), 2),
+                     (dict(out_full=0x50002), 1)]:
+        a = dict(streams=0x30000, slot_bytes=64 + 32 * 64 * 2 + 16, out_full=0x50000)
+        a.update(kw)
+        di = L.decode_item(t, a["streams"], a["slot_bytes"], a["out_full"], 0x20000)
+        with pytest.raises(L.CieraError) as e:
+            L.ciera_decode([di], 0x60000, 0x40000, need, stream=0)
+        assert e.value.code == code, kw
+    with pytest.raises(L.CieraError):
+        L.ciera_decode([d], 0, 0x40000, need, stream=0)          # no status word
+
+
+def test_scratch_sizes_grow_with_work():
+    t1 = L.Tensor(2048, 1024, 1, 512, 16)
+    it = L.encode_item(t1, 0, 1, 0x10000, 0x20000, 0x30000, 1 << 30)
+    a = L.ciera_encode_scratch_bytes([it])
+    b = L.ciera_encode_scratch_bytes([it] * 64)
+    assert 0 < a < b and a % 256 == 0
+    d = L.decode_item(t1, 0x30000, 1 << 20, 0x50000, 0x20000)
+    assert L.ciera_decode_scratch_bytes([d] * 10) > L.ciera_decode_scratch_bytes([d])

@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle, byte for byte.
+
+Streams (header, sign|mantissa bytes, bitmap, patches), rebuilt values, caches
+and decode status must be identical -- integer work, zero tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from gen import workloads as W
+from oracle import ciera_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # the CPU suite deselects these; be explicit anyway
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests.gpu_harness import Case, say, to_np  # noqa: E402
+
+
+def _pairs(specs, cfg, device="cpu"):
+    win = W.layer_windows(specs, cfg)
+    w0, w1 = [], []
+    for i in range(len(specs)):
+        a, b = W.weight_pair(specs, i, cfg, device=device, windows=win)
+        w0.append(a)
+        w1.append(b)
+    return w0, w1
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny2pct", "expert"])
+def test_named_configs(name):
+    specs, cfg, world = W.config(name)
+    say(f"[gpu] config {name}: {[(s.rows, s.cols) for s in specs]} W={world}")
+    w0, w1 = _pairs(specs, cfg)
+    case = Case([(s.rows, s.cols) for s in specs], cfg.dtype, world)
+    res = case.run(w0, w1)
+    assert res["status"] == 0 and res["ostatus"] == 0
+    rate = np.mean([np.mean(O.exponent_field(to_np(a), O.BF16) != O.exponent_field(to_np(b), O.BF16))
+                    for a, b in zip(w0, w1)])
+    say(f"[gpu] config {name}: exponent change rate {rate:.5%}")
+
+
+EDGE = [
+    # rows, cols, world, B, dtype, frac
+    (1, 1, 1, 512, torch.bfloat16, 0.5),
+    (17, 1, 16, 64, torch.bfloat16, 0.3),
+    (3, 5, 8, 512, torch.bfloat16, 0.2),        # ranks 3..7 hold no rows
+    (10, 3, 4, 64, torch.bfloat16, 0.1),        # shard offsets not 16-aligned
+    (10, 3, 4, 64, torch.float32, 0.1),
+    (33, 7, 2, 128, torch.float32, 0.05),
+    (1, 4097, 1, 512, torch.bfloat16, 0.01),    # one value past a tile
+    (2, 8193, 1, 64, torch.bfloat16, 0.002),
+    (4101, 3, 3, 256, torch.bfloat16, 0.01),
+    (64, 1000, 4, 1024, torch.bfloat16, 0.01),  # two 4096-value sub-tiles per tile
+    (64, 1000, 4, 2048, torch.float32, 0.01),
+    (96, 4096, 2, 4096, torch.bfloat16, 0.001),
+    (96, 4096, 2, 4096, torch.float32, 0.0),
+    (1000, 1000, 16, 512, torch.bfloat16, 0.0),
+    (1000, 1000, 16, 512, torch.float32, 0.003),
+    (7168, 1, 16, 512, torch.bfloat16, 0.01),   # an RMSNorm vector
+]
+
+
+@pytest.mark.parametrize("rows,cols,world,B,dtype,frac", EDGE)
+def test_edge_shapes(rows, cols, world, B, dtype, frac):
+    say(f"[gpu] edge {rows}x{cols} W={world} B={B} {dtype} f={frac}")
+    spec = [W.TensorSpec("e", rows, cols)]
+    w0 = [W.base_weights(spec[0], W.tensor_seed("edge", rows, cols, B), dtype)]
+    mask = W.mask_uniform(rows * cols, frac, W.tensor_seed("edge-m", rows, cols, B))
+    w1 = [W.perturb_exact(w0[0], mask, W.tensor_seed("edge-p", rows, cols, B))]
+    for compress in ([1], [0]):
+        case = Case([(rows, cols)], dtype, world, B)
+        res = case.run(w0, w1, compress=compress)
+        assert res["status"] == 0 and res["ostatus"] == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("frac", [0.0, 0.005, 0.19, 0.3, 1.0])
+def test_change_rates_and_raw_fallback(dtype, frac):
+    """Forced compress=1 at every rate: high rates must come out RAW through the
+    fallback rewrite, low rates COMPRESSED."""
+    say(f"[gpu] rates {dtype} f={frac}")
+    specs = [W.TensorSpec("a", 256, 512), W.TensorSpec("b", 128, 1024), W.TensorSpec("c", 64, 333)]
+    w0, w1 = [], []
+    for i, s in enumerate(specs):
+        a = W.base_weights(s, W.tensor_seed("rates", i), dtype)
+        m = W.mask_uniform(s.numel, frac, W.tensor_seed("rates-m", i, frac))
+        w0.append(a)
+        w1.append(W.perturb_exact(a, m, W.tensor_seed("rates-p", i, frac)))
+    case = Case([(s.rows, s.cols) for s in specs], dtype, 4)
+    res = case.run(w0, w1, compress=[1, 1, 1])
+    assert res["status"] == 0 and res["ostatus"] == 0
+    modes = {int(O.parse_header(case.codec.slot(i, r).cpu().numpy())["mode"])
+             for i in range(3) for r in range(4)}
+    if frac >= 0.3:
+        assert modes == {O.MODE_RAW}
+    if frac <= 0.005:
+        assert modes == {O.MODE_COMPRESSED}
+
+
+def test_specials_and_all_bf16_patterns():
+    """Every bf16 bit pattern (+-0, subnormals, Inf, all NaN payloads) survives."""
+    say("[gpu] all 65536 bf16 patterns")
+    x = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).reshape(256, 256)
+    rng = np.random.default_rng(5)
+    perm = torch.from_numpy(rng.permutation(65536))
+    w0 = [x.reshape(-1)[perm].reshape(256, 256).clone()]
+    w1 = [x.clone()]
+    for world in (1, 4, 16):
+        res = Case([(256, 256)], torch.bfloat16, world).run(w0, w1, compress=[1])
+        assert res["status"] == 0
+    spec = [W.TensorSpec("r", 448, 256)]
+    cfg = W.PairConfig("sp-test", frac=0.01, specials=1e-2)
+    w0, w1 = _pairs(spec, cfg)
+    assert Case([(448, 256)], torch.bfloat16, 16).run(w0, w1)["status"] == 0
+
+
+def _corrupt_case():
+    spec = [W.TensorSpec("k", 64, 3000)]
+    a = W.base_weights(spec[0], 77, torch.bfloat16)
+    m = W.mask_uniform(spec[0].numel, 0.01, 78)
+    return spec, [a], [W.perturb_exact(a, m, 79)]
+
+
+def test_decode_status_classes_match_oracle():
+    spec, w0, w1 = _corrupt_case()
+    rows, cols, world, B = 64, 3000, 4, 64
+    n = 16 * cols
+    ref = Case([(rows, cols)], torch.bfloat16, world, B)
+    ref.run(w0, w1, compress=[1])
+    s = ref.codec.slot(0, 1).cpu().numpy()
+    h = O.parse_header(s)
+    p = h["n_changed"]
+    assert h["mode"] == O.MODE_COMPRESSED and p > 2
+    nbm = O.bitmap_bytes(n, B)
+    pb = 64 + n + nbm
+    bm = s[64 + n:64 + n + nbm]
+    j = int(np.nonzero(bm)[0][0])
+    rec0, rec1 = bytes(s[pb:pb + 5]), bytes(s[pb + 5:pb + 10])
+    edits = {
+        "magic": [(0, 1, 0, b"X")],
+        "version": [(0, 1, 4, b"\x07")],
+        "dtype": [(0, 1, 6, b"\x02")],
+        "mode": [(0, 1, 7, b"\x09")],
+        "block": [(0, 1, 8, (128).to_bytes(4, "little"))],
+        "n": [(0, 1, 16, (n + 1).to_bytes(8, "little"))],
+        "offset": [(0, 1, 40, (1).to_bytes(8, "little"))],
+        "rank": [(0, 1, 48, (2).to_bytes(4, "little"))],
+        "world": [(0, 1, 52, (8).to_bytes(4, "little"))],
+        "total_len": [(0, 1, 32, (int(h["total_len"]) + 5).to_bytes(8, "little"))],
+        "n_changed": [(0, 1, 24, (p - 1).to_bytes(8, "little"))],
+        "n_changed>n": [(0, 1, 24, (n + 1).to_bytes(8, "little"))],
+        "index>=n": [(0, 1, pb + 5 * (p - 1), (n + 7).to_bytes(4, "little"))],
+        "swap": [(0, 1, pb, rec1), (0, 1, pb + 5, rec0)],
+        "duplicate": [(0, 1, pb + 5, rec0)],
+        "bitmap-clear": [(0, 1, 64 + n + j, bytes([0]))],
+        "bitmap-tail": [(0, 1, 64 + n + nbm - 1, bytes([int(bm[-1]) | 0x80]))],
+    }
+    assert O.n_blocks(n, B) % 8 != 0
+    for name, e in edits.items():
+        say(f"[gpu] corruption {name}")
+        res = Case([(rows, cols)], torch.bfloat16, world, B).run(w0, w1, compress=[1], edits=e)
+        g, o = res["status"], res["ostatus"]
+        assert o != 0, name
+        if o & O.ST_PATCH:          # bitmap bit unspecified alongside a patch error
+            g &= ~O.ST_BITMAP
+            o &= ~O.ST_BITMAP
+        assert g == o, (name, g, o)
+
+
+def test_encode_is_deterministic():
+    """Two encodes of the same inputs give identical bytes (look-back race check)."""
+    specs = W.olmoe_expert_specs()
+    cfg = W.PairConfig("det", frac=0.01)
+    w0, w1 = _pairs(specs, cfg)
+    case = Case([(s.rows, s.cols) for s in specs], torch.bfloat16, 16)
+    case.run(w0, w1)
+    first = case.codec.streams.clone()
+    for _ in range(3):
+        case.run(w0, w1)
+        assert torch.equal(first, case.codec.streams)
