@@ -129,6 +129,17 @@ typedef struct {
   uint64_t stream_capacity;   /* >= 64 + n_r*e (the RAW length) */
 } ciera_encode_item_t;
 
+/* A prepared batch: host-side handle of a batch whose descriptor tables already
+ * sit in the caller's device scratch, so that each launch enqueues kernels only
+ * (no host-to-device traffic).  Caller-owned plain bytes; not shareable between
+ * threads during a call.  The scratch belongs to the batch until it is prepared
+ * anew: preparing another batch in the same scratch invalidates this one (its
+ * kernels then detect the foreign contents and write nothing). */
+#define CIERA_BATCH_BYTES 4096u
+typedef struct {
+  uint64_t opaque[CIERA_BATCH_BYTES / 8];
+} ciera_batch_t;
+
 /* ciera_encode_scratch_bytes -- device scratch ciera_encode needs for this batch. */
 ciera_status_t ciera_encode_scratch_bytes(const ciera_encode_item_t* items, uint32_t count,
                                           uint64_t* bytes);
@@ -146,11 +157,23 @@ ciera_status_t ciera_encode_scratch_bytes(const ciera_encode_item_t* items, uint
 ciera_status_t ciera_encode(const ciera_encode_item_t* items, uint32_t count, void* scratch,
                             uint64_t scratch_bytes, void* stream);
 
+/* ciera_encode_prepare -- validate `items` (host array) exactly as ciera_encode
+ * does, write the batch's tables into `scratch` (one host-to-device copy on
+ * `stream`) and fill *batch.  The items' buffers are bound to the batch: every
+ * launch encodes whatever they hold at that point of the stream.
+ * ciera_encode_launch -- one encode of a prepared batch on `stream` (the one it
+ * was prepared on, or a stream ordered after it).  ciera_encode is prepare +
+ * launch.  Launches of one batch must not overlap in time. */
+ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t count, void* scratch,
+                                    uint64_t scratch_bytes, ciera_batch_t* batch, void* stream);
+ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream);
+
 /* The W received streams of one tensor. */
 typedef struct {
   ciera_tensor_t t;
   const uint8_t* streams; /* rank r's stream starts at streams + r*slot_bytes; 16-byte aligned */
-  uint64_t slot_bytes;    /* multiple of 16, >= 64; every stream must fit its slot */
+  uint64_t slot_bytes;    /* multiple of 16, >= the RAW length of rank 0's shard
+                             (ciera_plan's max_stream_bytes): every slot can hold any stream */
   void* out_full;         /* N values, rebuilt; 16-byte aligned */
   uint8_t* cache_full;    /* N bytes: exponents of the previous iteration, updated in place */
 } ciera_decode_item_t;
@@ -171,6 +194,13 @@ ciera_status_t ciera_decode_scratch_bytes(const ciera_decode_item_t* items, uint
 ciera_status_t ciera_decode(const ciera_decode_item_t* items, uint32_t count,
                             uint32_t* status_dev, void* scratch, uint64_t scratch_bytes,
                             void* stream);
+
+/* ciera_decode_prepare / ciera_decode_launch -- the prepared form of
+ * ciera_decode, as for encode; status_dev is bound to the batch. */
+ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t count,
+                                    uint32_t* status_dev, void* scratch, uint64_t scratch_bytes,
+                                    ciera_batch_t* batch, void* stream);
+ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream);
 
 /* ciera_cache_update -- cache_full[i] = exponent of weights_full[i] for the
  * whole tensor: seeds the cache when exponent reuse is switched on after

@@ -17,7 +17,8 @@ HEADER_BYTES = 64
 
 # every symbol include/ciera.h declares
 EXPORTS = ["ciera_plan", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
-           "ciera_decode_scratch_bytes", "ciera_decode", "ciera_cache_update",
+           "ciera_encode_prepare", "ciera_encode_launch", "ciera_decode_scratch_bytes",
+           "ciera_decode", "ciera_decode_prepare", "ciera_decode_launch", "ciera_cache_update",
            "ciera_status_str", "ciera_abi_version"]
 
 
@@ -63,6 +64,11 @@ class DecodeItem(ctypes.Structure):
                 ("out_full", c_void_p), ("cache_full", c_void_p)]
 
 
+class Batch(ctypes.Structure):
+    """Host handle of a prepared batch (CIERA_BATCH_BYTES opaque bytes)."""
+    _fields_ = [("opaque", c_uint64 * 512)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -75,6 +81,12 @@ def _load() -> ctypes.CDLL:
         "ciera_encode": (c_int, [POINTER(EncodeItem), c_uint32, c_void_p, c_uint64, c_void_p]),
         "ciera_decode_scratch_bytes": (c_int, [POINTER(DecodeItem), c_uint32, POINTER(c_uint64)]),
         "ciera_decode": (c_int, [POINTER(DecodeItem), c_uint32, c_void_p, c_void_p, c_uint64, c_void_p]),
+        "ciera_encode_prepare": (c_int, [POINTER(EncodeItem), c_uint32, c_void_p, c_uint64, POINTER(Batch),
+                                         c_void_p]),
+        "ciera_encode_launch": (c_int, [POINTER(Batch), c_void_p]),
+        "ciera_decode_prepare": (c_int, [POINTER(DecodeItem), c_uint32, c_void_p, c_void_p, c_uint64,
+                                         POINTER(Batch), c_void_p]),
+        "ciera_decode_launch": (c_int, [POINTER(Batch), c_void_p]),
         "ciera_cache_update": (c_int, [POINTER(Tensor), c_void_p, c_void_p, c_void_p]),
         "ciera_status_str": (c_char_p, [c_int]),
         "ciera_abi_version": (c_uint32, []),
@@ -184,3 +196,29 @@ def ciera_decode(items: Sequence[DecodeItem], status, scratch, scratch_bytes: Op
 def ciera_cache_update(t: Tensor, weights_full, cache_full, stream=None) -> None:
     _check(_lib.ciera_cache_update(byref(t), _ptr(weights_full), _ptr(cache_full), _stream(stream)),
            "ciera_cache_update")
+
+
+def ciera_encode_prepare(items: Sequence[EncodeItem], scratch, scratch_bytes: Optional[int] = None,
+                         stream=None) -> Batch:
+    nbytes = scratch_bytes if scratch_bytes is not None else scratch.numel() * scratch.element_size()
+    b = Batch()
+    _check(_lib.ciera_encode_prepare(_items_array(EncodeItem, items), len(items), _ptr(scratch), nbytes,
+                                     byref(b), _stream(stream)), "ciera_encode_prepare")
+    return b
+
+
+def ciera_encode_launch(batch: Batch, stream=None) -> None:
+    _check(_lib.ciera_encode_launch(byref(batch), _stream(stream)), "ciera_encode_launch")
+
+
+def ciera_decode_prepare(items: Sequence[DecodeItem], status, scratch, scratch_bytes: Optional[int] = None,
+                         stream=None) -> Batch:
+    nbytes = scratch_bytes if scratch_bytes is not None else scratch.numel() * scratch.element_size()
+    b = Batch()
+    _check(_lib.ciera_decode_prepare(_items_array(DecodeItem, items), len(items), _ptr(status), _ptr(scratch),
+                                     nbytes, byref(b), _stream(stream)), "ciera_decode_prepare")
+    return b
+
+
+def ciera_decode_launch(batch: Batch, stream=None) -> None:
+    _check(_lib.ciera_decode_launch(byref(batch), _stream(stream)), "ciera_decode_launch")

@@ -1,5 +1,6 @@
 // Host side of the CIERA codec library: argument validation, the per-tensor
-// selector, descriptor tables and kernel launches.  See include/ciera.h.
+// selector, prepared batches (descriptor tables resident in the caller's
+// scratch) and kernel launches.  See include/ciera.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -8,6 +9,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <unordered_map>
 #include <vector>
 
@@ -21,11 +23,16 @@ namespace {
 typedef unsigned __int128 u128;
 
 constexpr uint64_t kMaxElems = (uint64_t)1 << 48;
+constexpr uint64_t kEncMagic = 0x434945524145454eull;  // batch kinds
+constexpr uint64_t kDecMagic = 0x4349455241444543ull;
+constexpr int kMaxGroups = 64;
 
 uint32_t elem_bytes(uint32_t dt) { return dt == CIERA_BF16 ? 2u : 4u; }
 uint32_t sm_bytes(uint32_t dt) { return dt == CIERA_BF16 ? 1u : 3u; }
-
 bool pow2(uint32_t x) { return x && !(x & (x - 1)); }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+uint64_t bitmap_bytes(uint64_t n, uint32_t B) { return ((n + B - 1) / B + 7) / 8; }
 
 ciera_status_t check_tensor(const ciera_tensor_t* t) {
   if (!t) return CIERA_ERR_INVALID_ARG;
@@ -41,16 +48,9 @@ ciera_status_t check_tensor(const ciera_tensor_t* t) {
 void shard_of(const ciera_tensor_t* t, uint32_t r, uint64_t* off, uint64_t* n) {
   const uint64_t q = t->rows / t->world, rem = t->rows % t->world;
   const uint64_t rows_before = (uint64_t)r * q + std::min<uint64_t>(r, rem);
-  const uint64_t my_rows = q + (r < rem ? 1 : 0);
   *off = rows_before * t->cols;
-  *n = my_rows * t->cols;
+  *n = (q + (r < rem ? 1 : 0)) * t->cols;
 }
-
-uint64_t bitmap_bytes(uint64_t n, uint32_t B) { return ((n + B - 1) / B + 7) / 8; }
-
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- staging
 // Descriptor tables travel host -> device through a small ring of pinned
@@ -107,24 +107,56 @@ hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) 
   return hipSuccess;
 }
 
-// Per-call epoch of the encode look-back words; starts from a clock-derived
-// value so that words left by an earlier process do not match.
-std::atomic<uint32_t> g_epoch{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u};
+// Batch ids and launch tags: distinct per prepare / per launch, never 0.
+std::atomic<uint32_t> g_ids{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u};
+uint32_t next_id() {
+  uint32_t v;
+  do v = g_ids.fetch_add(0x9E3779B9u) ^ 0x5bd1e995u; while (v == 0);
+  return v;
+}
 
-// ------------------------------------------------------------ encode plan
-struct EncGroup {
-  uint32_t dtype, sub;
-  std::vector<uint32_t> idx;  // item indices
-  uint32_t tiles = 0;
-  uint64_t off_ctl = 0, off_raw = 0, off_tb = 0, off_items = 0, up_end = 0, off_status = 0;
+// ------------------------------------------------------------------ batches
+struct Group {
+  uint32_t dtype, unit;  // unit: encode sub-tiles S, decode chunk rows U
+  uint32_t item0, nitems;
+  uint32_t tpi;          // encode: tiles per item
+  uint32_t tpr, world;   // decode: tiles per rank, world
+  uint32_t pad;
+  uint64_t status_off;   // encode: byte offset of the group's look-back words
+};
+struct BatchImpl {
+  uint64_t magic;
+  uint8_t* scratch;
+  uint64_t scratch_bytes;
+  uint32_t* status_dev;
+  uint32_t count, ngroups;
+  uint32_t batch_id, tag_base;
+  uint32_t launches, any_compress;
+  uint64_t off_flags, off_ctr, off_items;
+  Group g[kMaxGroups];
+};
+static_assert(sizeof(BatchImpl) <= sizeof(ciera_batch_t), "batch handle too small");
+
+BatchImpl* impl(ciera_batch_t* b) { return reinterpret_cast<BatchImpl*>(b); }
+
+// Encode tile: S rows of 4096 values, at least 8*B values so every tile owns
+// whole bitmap bytes; two rows once the shard exceeds one row.
+uint32_t enc_sub(uint32_t B, uint64_t n) {
+  uint32_t s = std::max<uint32_t>(1u, B / 512u);
+  if (n > (uint64_t)kSub && s < 2) s = 2;
+  return s;
+}
+uint32_t dec_unit(uint64_t n0) { return n0 > (uint64_t)kSub ? 2u : 1u; }
+
+struct EncPlan {
+  std::vector<uint32_t> order;  // items in group order
+  std::vector<Group> groups;
+  uint64_t off_flags = 0, off_ctr = 0, off_items = 0, upload = 0, total = 0;
 };
 
-uint32_t sub_for(uint32_t B) { return std::max<uint32_t>(1u, B / 512u); }
-
-ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count,
-                          std::vector<EncGroup>* groups, uint64_t* upload_bytes, uint64_t* total) {
+ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncPlan* pl) {
   if (count && !items) return CIERA_ERR_INVALID_ARG;
-  std::map<std::pair<uint32_t, uint32_t>, size_t> gi;
+  std::map<std::tuple<uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
   for (uint32_t i = 0; i < count; ++i) {
     const ciera_encode_item_t& it = items[i];
     ciera_status_t s = check_tensor(&it.t);
@@ -133,49 +165,45 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count,
     uint64_t off, n;
     shard_of(&it.t, it.rank, &off, &n);
     if (n >= ((uint64_t)1 << 32)) return CIERA_ERR_UNSUPPORTED;
-    const auto key = std::make_pair(it.t.dtype, sub_for(it.t.block_size));
-    auto f = gi.find(key);
-    if (f == gi.end()) {
-      gi[key] = groups->size();
-      groups->push_back(EncGroup{key.first, key.second, {}});
-      f = gi.find(key);
-    }
-    EncGroup& g = (*groups)[f->second];
-    const uint64_t T = (uint64_t)kSub * g.sub;
-    const uint64_t nt = std::max<uint64_t>(1, (n + T - 1) / T);
-    if ((uint64_t)g.tiles + nt >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
-    g.tiles += (uint32_t)nt;
-    g.idx.push_back(i);
+    const uint32_t S = enc_sub(it.t.block_size, n);
+    const uint64_t T = (uint64_t)kSub * S;
+    const uint64_t tpi = std::max<uint64_t>(1, (n + T - 1) / T);
+    by[std::make_tuple(it.t.dtype, S, (uint32_t)tpi)].push_back(i);
   }
-  uint64_t cur = 0;
-  for (EncGroup& g : *groups) {
-    const uint64_t c = g.idx.size();
-    g.off_ctl = align_up(cur, 256);
-    g.off_raw = g.off_ctl + sizeof(EncCtl);
-    g.off_tb = align_up(g.off_raw + 4 * c, 64);
-    g.off_items = align_up(g.off_tb + 4 * c, 64);
-    g.up_end = g.off_items + sizeof(EncItem) * c;
-    cur = g.up_end;
+  if (by.size() > (size_t)kMaxGroups) return CIERA_ERR_UNSUPPORTED;
+  uint64_t tiles = 0;
+  for (auto& kv : by) {
+    Group g{};
+    g.dtype = std::get<0>(kv.first);
+    g.unit = std::get<1>(kv.first);
+    g.tpi = std::get<2>(kv.first);
+    g.item0 = (uint32_t)pl->order.size();
+    g.nitems = (uint32_t)kv.second.size();
+    if ((uint64_t)g.nitems * g.tpi >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
+    g.status_off = tiles;  // in words for now
+    tiles += (uint64_t)g.nitems * g.tpi;
+    pl->order.insert(pl->order.end(), kv.second.begin(), kv.second.end());
+    pl->groups.push_back(g);
   }
-  *upload_bytes = cur;
-  for (EncGroup& g : *groups) {
-    g.off_status = align_up(cur, 256);
-    cur = g.off_status + 8ull * g.tiles;
-  }
-  *total = align_up(cur, 256);
+  pl->off_flags = 256;
+  pl->off_ctr = align_up(pl->off_flags + 4ull * count, 64);
+  pl->off_items = align_up(pl->off_ctr + 4ull * count, 64);
+  pl->upload = pl->off_items + sizeof(EncItem) * (uint64_t)count;
+  const uint64_t st = align_up(pl->upload, 256);
+  for (Group& g : pl->groups) g.status_off = st + 8 * g.status_off;
+  pl->total = align_up(st + 8 * tiles, 256);
   return CIERA_OK;
 }
 
-struct DecGroup {
-  uint32_t dtype;
-  std::vector<uint32_t> idx;
-  uint32_t tiles = 0;
-  uint64_t off_tb = 0, off_items = 0;
+struct DecPlan {
+  std::vector<uint32_t> order;
+  std::vector<Group> groups;
+  uint64_t off_items = 0, total = 0;
 };
 
-ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count,
-                          std::vector<DecGroup>* groups, uint64_t* total) {
+ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count, DecPlan* pl) {
   if (count && !items) return CIERA_ERR_INVALID_ARG;
+  std::map<std::tuple<uint32_t, uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
   for (uint32_t i = 0; i < count; ++i) {
     const ciera_decode_item_t& it = items[i];
     ciera_status_t s = check_tensor(&it.t);
@@ -183,26 +211,26 @@ ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count,
     uint64_t off, n0;
     shard_of(&it.t, 0, &off, &n0);
     if (n0 >= ((uint64_t)1 << 32)) return CIERA_ERR_UNSUPPORTED;
-    DecGroup* g = nullptr;
-    for (DecGroup& x : *groups)
-      if (x.dtype == it.t.dtype) g = &x;
-    if (!g) {
-      groups->push_back(DecGroup{it.t.dtype, {}});
-      g = &groups->back();
-    }
-    const uint64_t tpr = std::max<uint64_t>(1, (n0 + kDecTile - 1) / kDecTile);
-    const uint64_t nt = tpr * it.t.world;
-    if ((uint64_t)g->tiles + nt >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
-    g->tiles += (uint32_t)nt;
-    g->idx.push_back(i);
+    const uint32_t U = dec_unit(n0);
+    const uint64_t T = (uint64_t)kSub * U;
+    const uint64_t tpr = std::max<uint64_t>(1, (n0 + T - 1) / T);
+    by[std::make_tuple(it.t.dtype, U, (uint32_t)tpr, it.t.world)].push_back(i);
   }
-  uint64_t cur = 0;
-  for (DecGroup& g : *groups) {
-    g.off_tb = align_up(cur, 256);
-    g.off_items = align_up(g.off_tb + 4 * g.idx.size(), 64);
-    cur = g.off_items + sizeof(DecItem) * g.idx.size();
+  if (by.size() > (size_t)kMaxGroups) return CIERA_ERR_UNSUPPORTED;
+  for (auto& kv : by) {
+    Group g{};
+    g.dtype = std::get<0>(kv.first);
+    g.unit = std::get<1>(kv.first);
+    g.tpr = std::get<2>(kv.first);
+    g.world = std::get<3>(kv.first);
+    g.item0 = (uint32_t)pl->order.size();
+    g.nitems = (uint32_t)kv.second.size();
+    if ((u128)g.nitems * g.tpr * g.world >= ((u128)1 << 31)) return CIERA_ERR_UNSUPPORTED;
+    pl->order.insert(pl->order.end(), kv.second.begin(), kv.second.end());
+    pl->groups.push_back(g);
   }
-  *total = align_up(cur, 256);
+  pl->off_items = 256;
+  pl->total = align_up(pl->off_items + sizeof(DecItem) * (uint64_t)count, 256);
   return CIERA_OK;
 }
 
@@ -266,26 +294,26 @@ ciera_status_t ciera_plan(const ciera_tensor_t* t, uint32_t change_ppm, const ci
   return CIERA_OK;
 }
 
-ciera_status_t ciera_encode_scratch_bytes(const ciera_encode_item_t* items, uint32_t count,
-                                          uint64_t* bytes) {
+// ------------------------------------------------------------------ encode
+
+ciera_status_t ciera_encode_scratch_bytes(const ciera_encode_item_t* items, uint32_t count, uint64_t* bytes) {
   if (!bytes) return CIERA_ERR_INVALID_ARG;
-  std::vector<EncGroup> groups;
-  uint64_t up = 0, total = 0;
-  ciera_status_t s = enc_layout(items, count, &groups, &up, &total);
+  EncPlan pl;
+  ciera_status_t s = enc_layout(items, count, &pl);
   if (s) return s;
-  *bytes = total;
+  *bytes = pl.total;
   return CIERA_OK;
 }
 
-ciera_status_t ciera_encode(const ciera_encode_item_t* items, uint32_t count, void* scratch,
-                            uint64_t scratch_bytes, void* stream) {
-  if (count == 0) return CIERA_OK;
-  std::vector<EncGroup> groups;
-  uint64_t up = 0, total = 0;
-  ciera_status_t s = enc_layout(items, count, &groups, &up, &total);
+ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t count, void* scratch,
+                                    uint64_t scratch_bytes, ciera_batch_t* batch, void* stream) {
+  if (!batch) return CIERA_ERR_INVALID_ARG;
+  std::memset(batch, 0, sizeof(*batch));
+  EncPlan pl;
+  ciera_status_t s = enc_layout(items, count, &pl);
   if (s) return s;
   if (!scratch || !aligned(scratch, 256)) return CIERA_ERR_INVALID_ARG;
-  if (scratch_bytes < total) return CIERA_ERR_BUFFER_TOO_SMALL;
+  if (scratch_bytes < pl.total) return CIERA_ERR_BUFFER_TOO_SMALL;
   for (uint32_t i = 0; i < count; ++i) {
     const ciera_encode_item_t& it = items[i];
     uint64_t off, n;
@@ -294,119 +322,179 @@ ciera_status_t ciera_encode(const ciera_encode_item_t* items, uint32_t count, vo
     if (!it.stream || !aligned(it.stream, 16)) return CIERA_ERR_INVALID_ARG;
     if (it.stream_capacity < kHeader + n * elem_bytes(it.t.dtype)) return CIERA_ERR_BUFFER_TOO_SMALL;
   }
-  std::vector<uint8_t> blob(up, 0);  // zeroed control blocks included
-  for (EncGroup& g : groups) {
-    uint32_t* tb = reinterpret_cast<uint32_t*>(blob.data() + g.off_tb);
-    EncItem* di = reinterpret_cast<EncItem*>(blob.data() + g.off_items);
-    const uint64_t T = (uint64_t)kSub * g.sub;
-    uint32_t tile = 0;
-    for (size_t j = 0; j < g.idx.size(); ++j) {
-      const ciera_encode_item_t& it = items[g.idx[j]];
-      uint64_t off, n;
-      shard_of(&it.t, it.rank, &off, &n);
-      EncItem& d = di[j];
-      d.x = static_cast<const uint8_t*>(it.shard);
-      d.cache = it.cache_full + off;
-      d.stream = it.stream;
-      d.n = n;
-      d.off = off;
-      d.capacity = it.stream_capacity;
-      d.tile_begin = tile;
-      d.ntiles = (uint32_t)std::max<uint64_t>(1, (n + T - 1) / T);
-      d.rank = it.rank;
-      d.world = it.t.world;
-      d.block_size = it.t.block_size;
-      d.compress = it.compress ? 1u : 0u;
-      d.cache_aligned = aligned(d.cache, 16) ? 1u : 0u;
-      d.pad = 0;
-      tb[j] = tile;
-      tile += d.ntiles;
-    }
+  BatchImpl* b = impl(batch);
+  b->batch_id = next_id();
+  b->tag_base = next_id();
+  std::vector<uint8_t> blob(pl.upload, 0);
+  reinterpret_cast<uint32_t*>(blob.data())[0] = b->batch_id;
+  EncItem* di = reinterpret_cast<EncItem*>(blob.data() + pl.off_items);
+  uint32_t any = 0;
+  for (uint32_t j = 0; j < count; ++j) {
+    const ciera_encode_item_t& it = items[pl.order[j]];
+    uint64_t off, n;
+    shard_of(&it.t, it.rank, &off, &n);
+    EncItem& d = di[j];
+    d.x = static_cast<const uint8_t*>(it.shard);
+    d.cache = it.cache_full + off;
+    d.stream = it.stream;
+    d.n = n;
+    d.off = off;
+    d.capacity = it.stream_capacity;
+    d.rank = it.rank;
+    d.world = it.t.world;
+    d.block_size = it.t.block_size;
+    d.compress = it.compress ? 1u : 0u;
+    d.cache_aligned = aligned(d.cache, 16) ? 1u : 0u;
+    d.elem_bytes = elem_bytes(it.t.dtype);
+    any |= d.compress;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  uint8_t* base = static_cast<uint8_t*>(scratch);
-  if (upload(base, blob.data(), up, st) != hipSuccess) return CIERA_ERR_DEVICE;
-  const uint32_t epoch = g_epoch.fetch_add(1u);
-  for (EncGroup& g : groups) {
-    const EncItem* di = reinterpret_cast<const EncItem*>(base + g.off_items);
-    EncCtl* ctl = reinterpret_cast<EncCtl*>(base + g.off_ctl);
-    uint32_t* raw = reinterpret_cast<uint32_t*>(base + g.off_raw);
-    if (launch_encode(g.dtype, g.sub, di, reinterpret_cast<const uint32_t*>(base + g.off_tb),
-                      (uint32_t)g.idx.size(), g.tiles, ctl, raw,
-                      reinterpret_cast<uint64_t*>(base + g.off_status), epoch, st) != hipSuccess)
+  if (upload(scratch, blob.data(), blob.size(), st) != hipSuccess) return CIERA_ERR_DEVICE;
+  b->magic = kEncMagic;
+  b->scratch = static_cast<uint8_t*>(scratch);
+  b->scratch_bytes = scratch_bytes;
+  b->count = count;
+  b->ngroups = (uint32_t)pl.groups.size();
+  b->any_compress = any;
+  b->off_flags = pl.off_flags;
+  b->off_ctr = pl.off_ctr;
+  b->off_items = pl.off_items;
+  for (size_t g = 0; g < pl.groups.size(); ++g) b->g[g] = pl.groups[g];
+  return CIERA_OK;
+}
+
+ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
+  if (!batch) return CIERA_ERR_INVALID_ARG;
+  BatchImpl* b = impl(batch);
+  if (b->magic != kEncMagic) return CIERA_ERR_INVALID_ARG;
+  if (b->count == 0) return CIERA_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t tag = 1u + (b->tag_base + b->launches) % 0x3FFFFFFEu;
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(b->scratch);
+  const EncItem* items = reinterpret_cast<const EncItem*>(b->scratch + b->off_items);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(b->scratch + b->off_flags);
+  for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
+    const Group& g = b->g[gi];
+    EncArgs a;
+    a.items = items;
+    a.item0 = g.item0;
+    a.tpi = g.tpi;
+    a.ctr = reinterpret_cast<uint32_t*>(b->scratch + b->off_ctr);
+    a.launch = b->launches;
+    a.tag = tag;
+    a.status = reinterpret_cast<uint64_t*>(b->scratch + g.status_off);
+    a.raw_flag = flags;
+    a.any_raw = ctl + 1;
+    if (launch_encode(g.dtype, g.unit, g.nitems, a, ctl, b->batch_id, st) != hipSuccess) {
+      b->magic = 0;  // counters may be out of step now: the batch must be prepared again
       return CIERA_ERR_DEVICE;
-    if (launch_encode_fixup(g.dtype, di, ctl, raw, st) != hipSuccess) return CIERA_ERR_DEVICE;
+    }
   }
+  if (b->any_compress && launch_encode_fixup(items, b->count, flags, ctl + 1, tag, st) != hipSuccess) {
+    b->magic = 0;
+    return CIERA_ERR_DEVICE;
+  }
+  b->launches += 1;
   return CIERA_OK;
 }
 
-ciera_status_t ciera_decode_scratch_bytes(const ciera_decode_item_t* items, uint32_t count,
-                                          uint64_t* bytes) {
-  if (!bytes) return CIERA_ERR_INVALID_ARG;
-  std::vector<DecGroup> groups;
-  uint64_t total = 0;
-  ciera_status_t s = dec_layout(items, count, &groups, &total);
-  if (s) return s;
-  *bytes = total;
-  return CIERA_OK;
-}
-
-ciera_status_t ciera_decode(const ciera_decode_item_t* items, uint32_t count, uint32_t* status_dev,
-                            void* scratch, uint64_t scratch_bytes, void* stream) {
+ciera_status_t ciera_encode(const ciera_encode_item_t* items, uint32_t count, void* scratch,
+                            uint64_t scratch_bytes, void* stream) {
   if (count == 0) return CIERA_OK;
-  std::vector<DecGroup> groups;
-  uint64_t total = 0;
-  ciera_status_t s = dec_layout(items, count, &groups, &total);
+  ciera_batch_t b;
+  ciera_status_t s = ciera_encode_prepare(items, count, scratch, scratch_bytes, &b, stream);
   if (s) return s;
-  if (!scratch || !aligned(scratch, 256) || !status_dev || !aligned(status_dev, 4))
-    return CIERA_ERR_INVALID_ARG;
-  if (scratch_bytes < total) return CIERA_ERR_BUFFER_TOO_SMALL;
+  return ciera_encode_launch(&b, stream);
+}
+
+// ------------------------------------------------------------------ decode
+
+ciera_status_t ciera_decode_scratch_bytes(const ciera_decode_item_t* items, uint32_t count, uint64_t* bytes) {
+  if (!bytes) return CIERA_ERR_INVALID_ARG;
+  DecPlan pl;
+  ciera_status_t s = dec_layout(items, count, &pl);
+  if (s) return s;
+  *bytes = pl.total;
+  return CIERA_OK;
+}
+
+ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t count, uint32_t* status_dev,
+                                    void* scratch, uint64_t scratch_bytes, ciera_batch_t* batch, void* stream) {
+  if (!batch) return CIERA_ERR_INVALID_ARG;
+  std::memset(batch, 0, sizeof(*batch));
+  DecPlan pl;
+  ciera_status_t s = dec_layout(items, count, &pl);
+  if (s) return s;
+  if (!scratch || !aligned(scratch, 256) || !status_dev || !aligned(status_dev, 4)) return CIERA_ERR_INVALID_ARG;
+  if (scratch_bytes < pl.total) return CIERA_ERR_BUFFER_TOO_SMALL;
   for (uint32_t i = 0; i < count; ++i) {
     const ciera_decode_item_t& it = items[i];
+    uint64_t off, n0;
+    shard_of(&it.t, 0, &off, &n0);
     if (!it.streams || !aligned(it.streams, 16)) return CIERA_ERR_INVALID_ARG;
     if (it.slot_bytes % 16 != 0) return CIERA_ERR_INVALID_ARG;
-    if (it.slot_bytes < kHeader) return CIERA_ERR_BUFFER_TOO_SMALL;
+    if (it.slot_bytes < kHeader + n0 * elem_bytes(it.t.dtype)) return CIERA_ERR_BUFFER_TOO_SMALL;
     if (it.t.rows * it.t.cols && (!it.out_full || !aligned(it.out_full, 16) || !it.cache_full))
       return CIERA_ERR_INVALID_ARG;
   }
-  std::vector<uint8_t> blob(total, 0);
-  for (DecGroup& g : groups) {
-    uint32_t* tb = reinterpret_cast<uint32_t*>(blob.data() + g.off_tb);
-    DecItem* di = reinterpret_cast<DecItem*>(blob.data() + g.off_items);
-    uint32_t tile = 0;
-    for (size_t j = 0; j < g.idx.size(); ++j) {
-      const ciera_decode_item_t& it = items[g.idx[j]];
-      uint64_t off, n0;
-      shard_of(&it.t, 0, &off, &n0);
-      DecItem& d = di[j];
-      d.streams = it.streams;
-      d.slot = it.slot_bytes;
-      d.out = static_cast<uint8_t*>(it.out_full);
-      d.cache = it.cache_full;
-      d.rows = it.t.rows;
-      d.cols = it.t.cols;
-      d.tile_begin = tile;
-      d.tiles_per_rank = (uint32_t)std::max<uint64_t>(1, (n0 + kDecTile - 1) / kDecTile);
-      d.world = it.t.world;
-      d.block_size = it.t.block_size;
-      tb[j] = tile;
-      tile += d.tiles_per_rank * d.world;
-    }
+  BatchImpl* b = impl(batch);
+  b->batch_id = next_id();
+  std::vector<uint8_t> blob(pl.total, 0);
+  reinterpret_cast<uint32_t*>(blob.data())[0] = b->batch_id;
+  DecItem* di = reinterpret_cast<DecItem*>(blob.data() + pl.off_items);
+  for (uint32_t j = 0; j < count; ++j) {
+    const ciera_decode_item_t& it = items[pl.order[j]];
+    DecItem& d = di[j];
+    d.streams = it.streams;
+    d.slot = it.slot_bytes;
+    d.out = static_cast<uint8_t*>(it.out_full);
+    d.cache = it.cache_full;
+    d.rows = it.t.rows;
+    d.cols = it.t.cols;
+    d.world = it.t.world;
+    d.block_size = it.t.block_size;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  uint8_t* base = static_cast<uint8_t*>(scratch);
-  if (upload(base, blob.data(), total, st) != hipSuccess) return CIERA_ERR_DEVICE;
-  for (DecGroup& g : groups) {
-    if (launch_decode(g.dtype, reinterpret_cast<const DecItem*>(base + g.off_items),
-                      reinterpret_cast<const uint32_t*>(base + g.off_tb), (uint32_t)g.idx.size(),
-                      g.tiles, status_dev, st) != hipSuccess)
-      return CIERA_ERR_DEVICE;
-  }
+  if (upload(scratch, blob.data(), blob.size(), st) != hipSuccess) return CIERA_ERR_DEVICE;
+  b->magic = kDecMagic;
+  b->scratch = static_cast<uint8_t*>(scratch);
+  b->scratch_bytes = scratch_bytes;
+  b->status_dev = status_dev;
+  b->count = count;
+  b->ngroups = (uint32_t)pl.groups.size();
+  b->off_items = pl.off_items;
+  for (size_t g = 0; g < pl.groups.size(); ++g) b->g[g] = pl.groups[g];
   return CIERA_OK;
 }
 
-ciera_status_t ciera_cache_update(const ciera_tensor_t* t, const void* weights_full,
-                                  uint8_t* cache_full, void* stream) {
+ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream) {
+  if (!batch) return CIERA_ERR_INVALID_ARG;
+  BatchImpl* b = impl(batch);
+  if (b->magic != kDecMagic) return CIERA_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t* ctl = reinterpret_cast<const uint32_t*>(b->scratch);
+  const DecItem* items = reinterpret_cast<const DecItem*>(b->scratch + b->off_items);
+  for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
+    const Group& g = b->g[gi];
+    if (launch_decode(g.dtype, g.unit, items, g.item0, g.nitems, g.tpr, g.world, b->status_dev, ctl,
+                      b->batch_id, st) != hipSuccess)
+      return CIERA_ERR_DEVICE;
+  }
+  b->launches += 1;
+  return CIERA_OK;
+}
+
+ciera_status_t ciera_decode(const ciera_decode_item_t* items, uint32_t count, uint32_t* status_dev, void* scratch,
+                            uint64_t scratch_bytes, void* stream) {
+  if (count == 0) return CIERA_OK;
+  ciera_batch_t b;
+  ciera_status_t s = ciera_decode_prepare(items, count, status_dev, scratch, scratch_bytes, &b, stream);
+  if (s) return s;
+  return ciera_decode_launch(&b, stream);
+}
+
+ciera_status_t ciera_cache_update(const ciera_tensor_t* t, const void* weights_full, uint8_t* cache_full,
+                                  void* stream) {
   ciera_status_t s = check_tensor(t);
   if (s) return s;
   const uint64_t N = t->rows * t->cols;

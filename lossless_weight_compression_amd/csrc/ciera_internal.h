@@ -7,13 +7,12 @@
 
 namespace ciera {
 
-constexpr int kThreads = 256;               // one workgroup = 4 wave64
-constexpr int kEPT = 16;                    // values per thread per sub-tile
-constexpr int kSub = kThreads * kEPT;       // 4096 values per sub-tile
-constexpr int kDecTile = kSub;              // decode tile
+constexpr int kThreads = 256;          // one workgroup = 4 wave64
+constexpr int kEPT = 16;               // values per thread per chunk
+constexpr int kSub = kThreads * kEPT;  // 4096 values per chunk row of a tile
 constexpr uint64_t kHeader = 64;
 
-// One encode item as the kernels see it (built on the host, uploaded per call).
+// One encode item as the kernels see it.
 struct EncItem {
   const uint8_t* x;      // shard values
   const uint8_t* cache;  // cache_full + offset of the shard
@@ -21,43 +20,52 @@ struct EncItem {
   uint64_t n;
   uint64_t off;
   uint64_t capacity;
-  uint32_t tile_begin;   // first tile of this item in the group's tile space
-  uint32_t ntiles;       // >= 1
   uint32_t rank, world;
   uint32_t block_size;
   uint32_t compress;
   uint32_t cache_aligned;  // (cache_full + off) is 16-byte aligned
-  uint32_t pad;
+  uint32_t elem_bytes;     // 2 (bf16) or 4 (fp32)
+  uint32_t pad[2];
 };
 
-// Control block at the start of an encode group's scratch; zeroed by the
-// per-call descriptor upload.  raw_list[] follows it.
-struct EncCtl {
-  uint32_t tile_counter;  // dynamic tile ids
-  uint32_t raw_count;     // items whose COMPRESSED stream was not shorter
-  uint32_t pad[62];
-};
-
+// One decode item: a tensor and its W receive slots.
 struct DecItem {
   const uint8_t* streams;
   uint64_t slot;
   uint8_t* out;
   uint8_t* cache;
   uint64_t rows, cols;
-  uint32_t tile_begin;
-  uint32_t tiles_per_rank;   // ceil(n0 / kDecTile), >= 1
   uint32_t world;
   uint32_t block_size;
 };
 
-hipError_t launch_encode(int dtype, int sub, const EncItem* items, const uint32_t* tile_begin,
-                         uint32_t count, uint32_t total_tiles, EncCtl* ctl, uint32_t* raw_list,
-                         uint64_t* status, uint32_t epoch, hipStream_t s);
-hipError_t launch_encode_fixup(int dtype, const EncItem* items, const EncCtl* ctl,
-                               const uint32_t* raw_list, hipStream_t s);
-hipError_t launch_decode(int dtype, const DecItem* items, const uint32_t* tile_begin,
-                         uint32_t count, uint32_t total_tiles, uint32_t* status, hipStream_t s);
-hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n,
-                               hipStream_t s);
+// Encode scratch layout (offsets in bytes from the scratch base):
+//   ctl      : u32 [batch id, any_raw, error] (+ padding to 256 B)
+//   raw_flag : u32 per item -- equals the launch tag if the item must be rewritten RAW
+//   ctr      : u32 per item -- dynamic tile counter, grows by tiles-per-item per launch
+//   items    : EncItem per item, ordered by group
+//   status   : u64 per tile, look-back words tagged with the launch tag
+struct EncArgs {
+  const EncItem* items;
+  uint32_t item0;      // first item of the group
+  uint32_t tpi;        // tiles per item in the group
+  uint32_t* ctr;       // per-item counters (indexed by absolute item)
+  uint32_t launch;     // launches of this batch so far
+  uint32_t tag;        // launch tag, never 0
+  uint64_t* status;    // group's status words, (item - item0) * tpi + tile
+  uint32_t* raw_flag;  // per absolute item
+  uint32_t* any_raw;
+};
+
+// ctl: the control words at the start of a batch's scratch; ctl[0] holds the
+// batch id written at prepare time, kernels exit at once when it differs.
+hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
+                         uint32_t batch_id, hipStream_t s);
+hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, const uint32_t* raw_flag,
+                               const uint32_t* any_raw, uint32_t tag, hipStream_t s);
+hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
+                         uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,
+                         uint32_t batch_id, hipStream_t s);
+hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n, hipStream_t s);
 
 }  // namespace ciera

@@ -19,6 +19,20 @@
 namespace ciera {
 namespace {
 
+// Every device buffer is reached through these casts to the global address
+// space: pointers read from descriptor tables would otherwise compile to flat
+// instructions, which also count against the LDS wait counter and so make every
+// LDS access and barrier wait for all outstanding HBM loads.
+#define G1 __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ G1 T* gp(T* p) { return (G1 T*)p; }
+template <class T>
+__device__ __forceinline__ const G1 T* gp(const T* p) { return (const G1 T*)p; }
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // one 16-byte global access
+__device__ __forceinline__ v4u ldg16(const void* p) { return *gp(reinterpret_cast<const v4u*>(p)); }
+__device__ __forceinline__ void stg16(void* p, v4u v) { *gp(reinterpret_cast<v4u*>(p)) = v; }
+
 template <int DT>
 struct Tr;
 template <>
@@ -59,8 +73,8 @@ template <int DT>
 __device__ __forceinline__ void load16(const uint8_t* p, int cnt, uint32_t v[16]) {
   if (cnt == 16) {
     if constexpr (DT == 1) {
-      const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-      const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+      const v4u a = ldg16(p);
+      const v4u b = ldg16(p + 16);
       const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -70,7 +84,7 @@ __device__ __forceinline__ void load16(const uint8_t* p, int cnt, uint32_t v[16]
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 a = reinterpret_cast<const uint4*>(p)[q];
+        const v4u a = ldg16(p + 16 * q);
         v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
       }
     }
@@ -78,8 +92,8 @@ __device__ __forceinline__ void load16(const uint8_t* p, int cnt, uint32_t v[16]
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < cnt) {
-        if constexpr (DT == 1) v[j] = reinterpret_cast<const uint16_t*>(p)[j];
-        else v[j] = reinterpret_cast<const uint32_t*>(p)[j];
+        if constexpr (DT == 1) v[j] = gp(reinterpret_cast<const uint16_t*>(p))[j];
+        else v[j] = gp(reinterpret_cast<const uint32_t*>(p))[j];
       } else {
         v[j] = 0;
       }
@@ -91,27 +105,27 @@ template <int DT>
 __device__ __forceinline__ void store16(uint8_t* p, int cnt, const uint32_t v[16], bool vec = true) {
   if (cnt == 16 && vec) {
     if constexpr (DT == 1) {
-      uint4 a, b;
+      v4u a, b;
       a.x = v[0] | (v[1] << 16); a.y = v[2] | (v[3] << 16);
       a.z = v[4] | (v[5] << 16); a.w = v[6] | (v[7] << 16);
       b.x = v[8] | (v[9] << 16); b.y = v[10] | (v[11] << 16);
       b.z = v[12] | (v[13] << 16); b.w = v[14] | (v[15] << 16);
-      reinterpret_cast<uint4*>(p)[0] = a;
-      reinterpret_cast<uint4*>(p)[1] = b;
+      stg16(p, a);
+      stg16(p + 16, b);
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        uint4 a;
+        v4u a;
         a.x = v[4 * q]; a.y = v[4 * q + 1]; a.z = v[4 * q + 2]; a.w = v[4 * q + 3];
-        reinterpret_cast<uint4*>(p)[q] = a;
+        stg16(p + 16 * q, a);
       }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < cnt) {
-        if constexpr (DT == 1) reinterpret_cast<uint16_t*>(p)[j] = (uint16_t)v[j];
-        else reinterpret_cast<uint32_t*>(p)[j] = v[j];
+        if constexpr (DT == 1) gp(reinterpret_cast<uint16_t*>(p))[j] = (uint16_t)v[j];
+        else gp(reinterpret_cast<uint32_t*>(p))[j] = v[j];
       }
     }
   }
@@ -120,25 +134,25 @@ __device__ __forceinline__ void store16(uint8_t* p, int cnt, const uint32_t v[16
 // 16 bytes (cache exponents) as four little-endian words.
 __device__ __forceinline__ void load_bytes16(const uint8_t* p, int cnt, bool aligned, uint32_t c[4]) {
   if (cnt == 16 && aligned) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const v4u a = ldg16(p);
     c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
   } else {
     c[0] = c[1] = c[2] = c[3] = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (j < cnt) c[j >> 2] |= (uint32_t)p[j] << (8 * (j & 3));
+      if (j < cnt) c[j >> 2] |= (uint32_t)gp(p)[j] << (8 * (j & 3));
   }
 }
 
 __device__ __forceinline__ void store_bytes16(uint8_t* p, int cnt, bool aligned, const uint32_t c[4]) {
   if (cnt == 16 && aligned) {
-    uint4 a;
+    v4u a;
     a.x = c[0]; a.y = c[1]; a.z = c[2]; a.w = c[3];
-    *reinterpret_cast<uint4*>(p) = a;
+    stg16(p, a);
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (j < cnt) p[j] = (uint8_t)(c[j >> 2] >> (8 * (j & 3)));
+      if (j < cnt) gp(p)[j] = (uint8_t)(c[j >> 2] >> (8 * (j & 3)));
   }
 }
 
@@ -167,110 +181,128 @@ __device__ __forceinline__ void store_sm16(uint8_t* p, int cnt, const uint32_t s
       }
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
-        uint4 o;
+        v4u o;
         o.x = w[4 * q]; o.y = w[4 * q + 1]; o.z = w[4 * q + 2]; o.w = w[4 * q + 3];
-        reinterpret_cast<uint4*>(p)[q] = o;
+        stg16(p + 16 * q, o);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         if (j < cnt) {
-          p[3 * j] = (uint8_t)sm[j];
-          p[3 * j + 1] = (uint8_t)(sm[j] >> 8);
-          p[3 * j + 2] = (uint8_t)(sm[j] >> 16);
+          gp(p)[3 * j] = (uint8_t)sm[j];
+          gp(p)[3 * j + 1] = (uint8_t)(sm[j] >> 8);
+          gp(p)[3 * j + 2] = (uint8_t)(sm[j] >> 16);
         }
       }
     }
   }
 }
 
-template <int DT>
-__device__ __forceinline__ void load_sm16(const uint8_t* p, int cnt, uint32_t sm[16]) {
-  if constexpr (DT == 1) {
-    uint32_t c[4];
-    load_bytes16(p, cnt, true, c);
+// Raw 32-bit words of nbytes <= 4*NW bytes at p (vector loads when complete and allowed).
+template <int NW>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t nbytes, bool vec, uint32_t w[NW]) {
+  if (vec && nbytes == NW * 4) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sm[j] = byte_of(c, j);
-  } else {
-    if (cnt == 16) {
-      uint32_t w[12];
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const uint4 a = reinterpret_cast<const uint4*>(p)[q];
-        w[4 * q] = a.x; w[4 * q + 1] = a.y; w[4 * q + 2] = a.z; w[4 * q + 3] = a.w;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t w0 = w[3 * q], w1 = w[3 * q + 1], w2 = w[3 * q + 2];
-        sm[4 * q] = w0 & 0xFFFFFFu;
-        sm[4 * q + 1] = (w0 >> 24) | ((w1 & 0xFFFFu) << 8);
-        sm[4 * q + 2] = (w1 >> 16) | ((w2 & 0xFFu) << 16);
-        sm[4 * q + 3] = w2 >> 8;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        sm[j] = (j < cnt) ? ((uint32_t)p[3 * j] | ((uint32_t)p[3 * j + 1] << 8) |
-                             ((uint32_t)p[3 * j + 2] << 16))
-                          : 0u;
+    for (int q = 0; q < NW / 4; ++q) {
+      const v4u a = ldg16(p + 16 * q);
+      w[4 * q] = a.x; w[4 * q + 1] = a.y; w[4 * q + 2] = a.z; w[4 * q + 3] = a.w;
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = 0;
+#pragma unroll
+    for (int b = 0; b < NW * 4; ++b)
+      if ((uint32_t)b < nbytes) w[b >> 2] |= (uint32_t)gp(p)[b] << (8 * (b & 3));
   }
 }
 
-__device__ __forceinline__ uint32_t load_u32_le(const uint8_t* p) {
-  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+// sign|mantissa of value j from the raw words of a 16-value chunk.
+template <int DT>
+__device__ __forceinline__ uint32_t sm_from_words(const uint32_t* w, int j) {
+  if constexpr (DT == 1) {
+    return (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+  } else {
+    const int q = j >> 2, k = j & 3;
+    const uint32_t w0 = w[3 * q], w1 = w[3 * q + 1], w2 = w[3 * q + 2];
+    if (k == 0) return w0 & 0xFFFFFFu;
+    if (k == 1) return (w0 >> 24) | ((w1 & 0xFFFFu) << 8);
+    if (k == 2) return (w1 >> 16) | ((w2 & 0xFFu) << 16);
+    return w2 >> 8;
+  }
 }
 
-// Item i with tb[i] <= tile < tb[i+1]; tb strictly ascending from 0.  Called by
-// all 64 lanes of one wave; the result is wave-uniform.
-__device__ uint32_t find_item(const uint32_t* tb, uint32_t count, uint32_t tile) {
-  uint32_t lo = 0, hi = count;
-  const uint32_t lane = lane_id();
-  while (hi - lo > 1) {
-    const uint32_t step = (hi - lo + 63u) / 64u;
-    const uint32_t p = lo + lane * step;
-    const bool pred = (p < hi) && (tb[p] <= tile);
-    const uint64_t m = __ballot(pred);
-    const uint32_t last = 63u - (uint32_t)__clzll(m);
-    const uint32_t nlo = lo + last * step;
-    hi = min(hi, nlo + step);
-    lo = nlo;
-  }
-  return lo;
+// Bits [start, start+nbits) of a least-significant-first bit array, nbits <= 32.
+__device__ __forceinline__ uint32_t get_bits(const uint8_t* bm, uint64_t start, uint32_t nbits) {
+  const uint64_t b0 = start >> 3;
+  const uint32_t sh = (uint32_t)(start & 7u);
+  const uint32_t nbytes = (sh + nbits + 7u) >> 3;
+  uint64_t v = 0;
+  for (uint32_t i = 0; i < nbytes; ++i) v |= (uint64_t)gp(bm)[b0 + i] << (8 * i);
+  v >>= sh;
+  return nbits >= 32 ? (uint32_t)v : (uint32_t)(v & ((1u << nbits) - 1u));
+}
+
+// Patch record p (u32 index, u8 exponent, 5 bytes at recs + 5p) read as the two
+// aligned words that cover it; both words start inside the stream, and the slot
+// is a multiple of 16 bytes, so neither can leave it.
+__device__ __forceinline__ void read_rec(const uint8_t* st, uint64_t recs, uint64_t p, uint32_t& idx,
+                                         uint32_t& ex) {
+  const uint64_t o = recs + 5 * p;
+  const uint64_t a = o & ~(uint64_t)3;
+  const G1 uint32_t* w = gp(reinterpret_cast<const uint32_t*>(st + a));
+  const uint64_t v = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+  const uint32_t sh = (uint32_t)(o - a) * 8u;
+  idx = (uint32_t)(v >> sh);
+  ex = (uint32_t)(v >> (sh + 32u)) & 0xFFu;
+}
+
+// ORs decode status bits into the caller's word; a plain read first keeps a
+// stream of identical errors (every tile of a corrupt batch) from serializing
+// on one address.
+__device__ __forceinline__ void report(uint32_t* status, uint32_t bits) {
+  if ((__hip_atomic_load(gp(status), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & bits) != bits)
+    __hip_atomic_fetch_or(gp(status), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------- decoupled look-back
-// One 64-bit word per tile: [63:62] flag, [61:32] epoch, [31:0] count.
-// The epoch (per call) makes words of earlier calls read as "not ready", so the
-// status array needs no clearing between calls.
+// One 64-bit word per tile: [63:62] flag, [61:32] launch tag, [31:0] count.
+// Words of earlier launches carry another tag and read as "not ready", so the
+// array is never cleared.
 constexpr uint64_t kFlagAgg = 1, kFlagIncl = 2;
+constexpr uint32_t kSpinCap = 1u << 22;  // only reached if the scratch was tampered with
 
-__device__ __forceinline__ uint64_t pack_status(uint64_t flag, uint32_t epoch, uint32_t v) {
-  return (flag << 62) | ((uint64_t)(epoch & 0x3FFFFFFFu) << 32) | v;
+__device__ __forceinline__ uint64_t pack_status(uint64_t flag, uint32_t tag, uint32_t v) {
+  return (flag << 62) | ((uint64_t)(tag & 0x3FFFFFFFu) << 32) | v;
 }
 __device__ __forceinline__ void publish(uint64_t* w, uint64_t val) {
-  __hip_atomic_store(w, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(w), val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t peek(uint64_t* w) {
-  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Exclusive prefix of this tile's count within its item.  Wave-wide call.
-// Every predecessor read has a lower dynamic tile id, i.e. its workgroup is
-// already running, so every wait ends.
-__device__ uint32_t look_back(uint64_t* status, uint32_t tile, uint32_t first_tile,
-                              uint32_t epoch) {
+// Exclusive prefix of tile `local`'s count among the tiles of its item
+// (status words sw[0..local)).  Wave-wide.  Every tile read holds a smaller
+// dynamic id of the same item, so its workgroup is already running and its
+// word arrives; the spin cap only guards against a corrupted scratch.
+__device__ uint32_t look_back(uint64_t* sw, uint32_t local, uint32_t tag, uint32_t* err) {
   const uint32_t lane = lane_id();
   uint32_t excl = 0;
-  int64_t hi = (int64_t)tile - 1;
+  int64_t hi = (int64_t)local - 1;
   while (true) {
     const int64_t j = hi - (int64_t)lane;
-    const bool valid = j >= (int64_t)first_tile;
+    const bool valid = j >= 0;
     uint64_t w;
+    uint32_t spins = 0;
     while (true) {
-      w = valid ? peek(status + j) : pack_status(kFlagIncl, epoch, 0u);
-      const bool ready = ((w >> 62) != 0) && (((uint32_t)(w >> 32) & 0x3FFFFFFFu) == (epoch & 0x3FFFFFFFu));
+      w = valid ? peek(sw + j) : pack_status(kFlagIncl, tag, 0u);
+      const bool ready = ((w >> 62) != 0) && (((uint32_t)(w >> 32) & 0x3FFFFFFFu) == (tag & 0x3FFFFFFFu));
       if (__all(ready)) break;
+      if (++spins >= kSpinCap) {
+        if (lane == 0) __hip_atomic_fetch_or(gp(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w = ready ? w : pack_status(kFlagIncl, tag, 0u);
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     const uint64_t incl = __ballot((w >> 62) == kFlagIncl);
@@ -279,7 +311,6 @@ __device__ uint32_t look_back(uint64_t* status, uint32_t tile, uint32_t first_ti
       const uint32_t stop = (uint32_t)__ffsll((unsigned long long)incl) - 1u;  // nearest inclusive
       if (lane > stop) mine = 0;
     }
-    // wave sum
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o);
     excl += mine;
@@ -290,64 +321,69 @@ __device__ uint32_t look_back(uint64_t* status, uint32_t tile, uint32_t first_ti
 }
 
 // --------------------------------------------------------------------- encode
+// One workgroup per tile of S*4096 values of one item; items of a group share a
+// tile count, so the item is blockIdx / tpi and only the tile's place inside the
+// item is taken dynamically (per-item counter), which keeps the look-back free
+// of deadlock without a global hot counter.
 
 template <int DT, int S>
-__global__ __launch_bounds__(kThreads) void encode_kernel(const EncItem* __restrict__ items,
-                                                          const uint32_t* __restrict__ tile_begin,
-                                                          uint32_t count, uint32_t total_tiles,
-                                                          EncCtl* ctl, uint32_t* raw_list,
-                                                          uint64_t* status, uint32_t epoch) {
+__global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* ctl, uint32_t batch_id) {
   constexpr int E = Tr<DT>::E, K = Tr<DT>::K;
   constexpr uint32_t T = (uint32_t)kSub * S;
-  __shared__ uint32_t s_tile, s_item, s_excl;
+  constexpr int XW = 4 * E;  // words of 16 raw values
+  __shared__ uint32_t s_local, s_excl;
   __shared__ uint32_t s_wtot[4 * S];
-  __shared__ uint32_t s_bm[2];
+  __shared__ uint32_t s_bm[2 * S];  // one bit per block of the tile: T/B <= T/64 = 64*S bits
 
+  if (gp(ctl)[0] != batch_id) return;  // scratch does not hold this batch (uniform)
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  if (tid == 0) s_tile = atomicAdd(&ctl->tile_counter, 1u);
-  if (tid < 2) s_bm[tid] = 0;
+  const uint32_t item = a.item0 + blockIdx.x / a.tpi;
+  if (tid == 0)
+    s_local = __hip_atomic_fetch_add(gp(a.ctr + item), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+              a.launch * a.tpi;
+  if (tid < 2 * S) s_bm[tid] = 0;
   __syncthreads();
-  const uint32_t tile = s_tile;
-  if (tile >= total_tiles) return;  // uniform
-  if (wave == 0) {
-    const uint32_t it = find_item(tile_begin, count, tile);
-    if (lane == 0) s_item = it;
-  }
-  __syncthreads();
-  const uint32_t item = s_item;
-  const EncItem d = items[item];
-  const uint32_t t_local = tile - d.tile_begin;
-  const uint64_t base = (uint64_t)t_local * T;
+  const uint32_t local = s_local;
+  if (local >= a.tpi) return;  // uniform; cannot happen while counters match launches
+  const EncItem d = a.items[item];
+  const uint64_t base = (uint64_t)local * T;
   const uint64_t n = d.n;
   const uint32_t B = d.block_size;
   const bool compress = d.compress != 0;
   const bool caligned = d.cache_aligned != 0;
 
+  // all loads of the tile first
+  uint32_t xw[S][XW], cw[S][4];
+  int cnt[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+    cnt[s] = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
+    if (cnt[s] > 0) {
+      load_words<XW>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
+      load_words<4>(d.cache + c0, (uint32_t)cnt[s], caligned, cw[s]);
+    }
+  }
   uint32_t mask[S];
   uint32_t expk[S][4];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-    const int cnt = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
-    uint32_t v[16], c[4];
     mask[s] = 0;
     expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
-    if (cnt > 0) {
-      load16<DT>(d.x + c0 * E, cnt, v);
-      load_bytes16(d.cache + c0, cnt, caligned, c);
-      uint32_t sm[16];
+    if (cnt[s] > 0) {
+      uint32_t v[16], sm[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
+        if constexpr (DT == 1) v[j] = (xw[s][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        else v[j] = xw[s][j];
         const uint32_t e = exp_of<DT>(v[j]);
         expk[s][j >> 2] |= e << (8 * (j & 3));
-        if (j < cnt && e != byte_of(c, j)) mask[s] |= 1u << j;
+        if (j < cnt[s] && e != byte_of(cw[s], j)) mask[s] |= 1u << j;
         sm[j] = sm_of<DT>(v[j]);
       }
-      if (compress) {
-        store_sm16<DT>(d.stream + kHeader + c0 * K, cnt, sm);
-      } else {
-        store16<DT>(d.stream + kHeader + c0 * E, cnt, v);
-      }
+      if (compress) store_sm16<DT>(d.stream + kHeader + c0 * K, cnt[s], sm);
+      else store16<DT>(d.stream + kHeader + c0 * E, cnt[s], v);
       if (mask[s]) {
         const uint32_t rel = (uint32_t)(((uint64_t)s * kSub + (uint64_t)tid * kEPT) / B);
         atomicOr(&s_bm[rel >> 5], 1u << (rel & 31u));
@@ -355,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncItem* __restr
     }
   }
 
-  // block-wide exclusive scan of the per-thread change counts, sub-tile major
+  // block-wide exclusive scan of the per-thread change counts, chunk-row major
   uint32_t lpre[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -383,15 +419,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncItem* __restr
     }
   }
 
-  // global offset of this tile's first patch
+  uint64_t* sw = a.status + (uint64_t)(item - a.item0) * a.tpi;
   if (wave == 0) {
     uint32_t excl = 0;
-    if (t_local == 0) {
-      if (lane == 0) publish(status + tile, pack_status(kFlagIncl, epoch, agg));
+    if (local == 0) {
+      if (lane == 0) publish(sw, pack_status(kFlagIncl, a.tag, agg));
     } else {
-      if (lane == 0) publish(status + tile, pack_status(kFlagAgg, epoch, agg));
-      excl = look_back(status, tile, d.tile_begin, epoch);
-      if (lane == 0) publish(status + tile, pack_status(kFlagIncl, epoch, excl + agg));
+      if (lane == 0) publish(sw + local, pack_status(kFlagAgg, a.tag, agg));
+      excl = look_back(sw, local, a.tag, ctl + 2);
+      if (lane == 0) publish(sw + local, pack_status(kFlagIncl, a.tag, excl + agg));
     }
     if (lane == 0) s_excl = excl;
   }
@@ -401,14 +437,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncItem* __restr
   const uint64_t nb = (n + B - 1) / B;
   const uint64_t nbm = (nb + 7) / 8;
   if (compress) {
-    // bitmap bytes of this tile's blocks (the tile spans a whole number of bytes)
+    // bitmap bytes of this tile's blocks (a tile spans whole bitmap bytes)
     const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
     const uint32_t tblocks = (uint32_t)((in_tile + B - 1) / B);
     const uint32_t tbytes = (tblocks + 7) / 8;
-    if (tid < tbytes) {
-      const uint32_t word = s_bm[tid >> 2];
-      d.stream[kHeader + n * K + base / ((uint64_t)B * 8) + tid] = (uint8_t)(word >> (8 * (tid & 3)));
-    }
+    if (tid < tbytes)
+      gp(d.stream)[kHeader + n * K + base / ((uint64_t)B * 8) + tid] = (uint8_t)(s_bm[tid >> 2] >> (8 * (tid & 3)));
     // (index, exponent) records
     const uint64_t pbase = kHeader + n * K + nbm;
 #pragma unroll
@@ -422,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncItem* __restr
         const uint64_t pos = pbase + 5 * g;
         if (pos + 5 <= d.capacity) {
           const uint32_t idx = (uint32_t)(c0 + j);
-          uint8_t* q = d.stream + pos;
+          G1 uint8_t* q = gp(d.stream + pos);
           q[0] = (uint8_t)idx; q[1] = (uint8_t)(idx >> 8);
           q[2] = (uint8_t)(idx >> 16); q[3] = (uint8_t)(idx >> 24);
           q[4] = (uint8_t)byte_of(expk[s], j);
@@ -433,17 +467,17 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncItem* __restr
   }
 
   // the item's last tile knows the total and writes the header
-  if (t_local == d.ntiles - 1 && tid == 0) {
+  if (local == a.tpi - 1 && tid == 0) {
     const uint64_t P = (uint64_t)excl + agg;
     const uint64_t comp = kHeader + n * K + (P ? nbm + 5 * P : 0);
     const uint64_t raw = kHeader + n * E;
     const bool cmode = compress && comp < raw;
     if (compress && !cmode) {
-      const uint32_t k = atomicAdd(&ctl->raw_count, 1u);
-      raw_list[k] = item;
+      gp(a.raw_flag)[item] = a.tag;
+      *gp(a.any_raw) = a.tag;
     }
     uint32_t h[16];
-    h[0] = 0x52454943u;                               // "CIER"
+    h[0] = 0x52454943u;  // "CIER"
     h[1] = 1u | ((uint32_t)DT << 16) | ((cmode ? 1u : 0u) << 24);
     h[2] = B;
     h[3] = 0;
@@ -453,82 +487,93 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncItem* __restr
     h[8] = (uint32_t)tot; h[9] = (uint32_t)(tot >> 32);
     h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
     h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
-    uint4* hp = reinterpret_cast<uint4*>(d.stream);
+
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint4 o;
+      v4u o;
       o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
-      hp[q] = o;
+      stg16(d.stream + 16 * q, o);
     }
   }
 }
 
 // Rewrites as RAW the streams whose COMPRESSED form turned out not shorter.
-template <int DT>
-__global__ __launch_bounds__(kThreads) void encode_fixup_kernel(const EncItem* __restrict__ items,
-                                                                const EncCtl* ctl,
-                                                                const uint32_t* raw_list) {
-  constexpr int E = Tr<DT>::E;
-  const uint32_t cnt = ctl->raw_count;
-  if (cnt == 0) return;
+__global__ __launch_bounds__(kThreads) void encode_fixup_kernel(const EncItem* __restrict__ items, uint32_t count,
+                                                                const uint32_t* raw_flag, const uint32_t* any_raw,
+                                                                uint32_t tag) {
+  if (*gp(any_raw) != tag) return;
   const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
-  for (uint32_t k = 0; k < cnt; ++k) {
-    const EncItem d = items[raw_list[k]];
-    const uint64_t bytes = d.n * E;
+  for (uint32_t k = 0; k < count; ++k) {
+    if (gp(raw_flag)[k] != tag) continue;
+    const EncItem d = items[k];
+    if (d.stream == nullptr) continue;
+    const uint64_t bytes = d.n * d.elem_bytes;
     const uint64_t vec = bytes / 16;
-    const uint4* src = reinterpret_cast<const uint4*>(d.x);
-    uint4* dst = reinterpret_cast<uint4*>(d.stream + kHeader);
-    for (uint64_t i = gtid; i < vec; i += gsz) dst[i] = src[i];
-    for (uint64_t i = vec * 16 + gtid; i < bytes; i += gsz) d.stream[kHeader + i] = d.x[i];
+    for (uint64_t i = gtid; i < vec; i += gsz) stg16(d.stream + kHeader + 16 * i, ldg16(d.x + 16 * i));
+    for (uint64_t i = vec * 16 + gtid; i < bytes; i += gsz) gp(d.stream)[kHeader + i] = gp(d.x)[i];
   }
 }
 
 // --------------------------------------------------------------------- decode
+// One workgroup per tile of U*4096 values of one rank's stream.  The bulk loads
+// (sign|mantissa bytes and cached exponents) are issued before the header and
+// the patch range are known, so their latency overlaps that chain.
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restrict__ items,
-                                                          const uint32_t* __restrict__ tile_begin,
-                                                          uint32_t count, uint32_t* status_out) {
+template <int DT, int U>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restrict__ items, uint32_t item0,
+                                                          uint32_t tpr, uint32_t world, uint32_t* status_out,
+                                                          const uint32_t* ctl, uint32_t batch_id) {
   constexpr int E = Tr<DT>::E, K = Tr<DT>::K;
-  constexpr uint32_t T = kDecTile;
-  __shared__ uint32_t s_item;
+  constexpr uint32_t T = (uint32_t)kSub * U;
+  constexpr uint32_t BMW = (T / 64 + 31) / 32;  // words of per-tile block bits (B >= 64)
+  constexpr int SW = 4 * K;                     // words of 16 sign|mantissa records
   __shared__ uint32_t s_hdr[16];
   __shared__ uint32_t s_lohi[2];
-  __shared__ uint32_t s_expbm[2];
+  __shared__ uint32_t s_expbm[BMW];
   __shared__ uint32_t s_err;
   __shared__ __align__(16) uint8_t s_ov[T];
 
+  if (gp(ctl)[0] != batch_id) return;  // scratch does not hold this batch (uniform)
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const uint32_t tile = blockIdx.x;
-  if (wave == 0) {
-    const uint32_t it = find_item(tile_begin, count, tile);
-    if (lane == 0) s_item = it;
-  }
-  if (tid < 2) s_expbm[tid] = 0;
-  if (tid == 0) s_err = 0;
-  __syncthreads();
-  const DecItem d = items[s_item];
-  const uint32_t rel = tile - d.tile_begin;
-  const uint32_t r = rel / d.tiles_per_rank;
-  const uint32_t t_in = rel - r * d.tiles_per_rank;
-  const uint64_t W = d.world;
-  const uint64_t q = d.rows / W, rem = d.rows % W;
-  const uint64_t my_rows = q + (r < rem ? 1 : 0);
+  const uint32_t tpi = tpr * world;
+  const uint32_t blk = blockIdx.x / tpi;
+  const uint32_t item = item0 + blk;
+  const uint32_t rel = blockIdx.x - blk * tpi;
+  const uint32_t r = rel / tpr;
+  const uint32_t t_in = rel - r * tpr;
+  const DecItem d = items[item];
+  const uint64_t q = d.rows / world, rem = d.rows % world;
   const uint64_t off = ((uint64_t)r * q + min<uint64_t>(r, rem)) * d.cols;
-  const uint64_t n = my_rows * d.cols;
+  const uint64_t n = (q + (r < rem ? 1u : 0u)) * d.cols;
   const uint64_t ts = (uint64_t)t_in * T;
   if (ts >= n && t_in != 0) return;  // past this shard (uniform)
   const uint64_t te = min<uint64_t>(n, ts + T);
   const uint8_t* st = d.streams + (uint64_t)r * d.slot;
   const uint32_t B = d.block_size;
+  const bool aligned = (off & 15u) == 0;
+  uint8_t* const cache = d.cache + off;
 
+  // 1. bulk loads, COMPRESSED layout (in bounds for either mode: a slot holds a RAW stream)
+  uint32_t sw[U][SW], cw[U][4];
+  int cnt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
+    cnt[u] = c0 < te ? (int)min<uint64_t>(16, te - c0) : 0;
+    if (cnt[u] > 0) {
+      load_words<SW>(st + kHeader + c0 * K, (uint32_t)cnt[u] * K, true, sw[u]);
+      load_words<4>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
+    }
+  }
+  // 2. header
   if (tid < 4) {
-    const uint4 h = reinterpret_cast<const uint4*>(st)[tid];
+    const v4u h = ldg16(st + 16 * tid);
     s_hdr[4 * tid] = h.x; s_hdr[4 * tid + 1] = h.y; s_hdr[4 * tid + 2] = h.z; s_hdr[4 * tid + 3] = h.w;
   }
+  if (tid < BMW) s_expbm[tid] = 0;
+  if (tid == 0) s_err = 0;
   __syncthreads();
-  // header and length validation (uniform)
   const uint32_t h_dtype = (s_hdr[1] >> 16) & 0xFFu, h_mode = s_hdr[1] >> 24;
   const uint64_t h_n = s_hdr[4] | ((uint64_t)s_hdr[5] << 32);
   const uint64_t P = s_hdr[6] | ((uint64_t)s_hdr[7] << 32);
@@ -539,138 +584,149 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
   uint32_t bad = 0;
   if (s_hdr[0] != 0x52454943u || (s_hdr[1] & 0xFFFFu) != 1u) {
     bad = CIERA_ST_MAGIC;
-  } else if (h_dtype != (uint32_t)DT || s_hdr[2] != B || h_n != n || h_off != off ||
-             s_hdr[12] != r || s_hdr[13] != d.world || h_mode > 1u) {
+  } else if (h_dtype != (uint32_t)DT || s_hdr[2] != B || h_n != n || h_off != off || s_hdr[12] != r ||
+             s_hdr[13] != world || h_mode > 1u) {
     bad = CIERA_ST_FIELD;
   } else {
-    const uint64_t want = h_mode == 0 ? kHeader + n * E
-                                      : kHeader + n * K + (P ? nbm + 5 * P : 0);
+    const uint64_t want = h_mode == 0 ? kHeader + n * E : kHeader + n * K + (P ? nbm + 5 * P : 0);
     if (P > n || h_tot > d.slot || h_tot != want) bad = CIERA_ST_LENGTH;
   }
   if (bad) {
-    if (t_in == 0 && tid == 0) atomicOr(status_out, bad);
+    if (t_in == 0 && tid == 0) report(status_out, bad);
     return;  // uniform
   }
-  const bool aligned = (off & 15u) == 0;
-  const uint64_t c0 = ts + (uint64_t)tid * kEPT;
-  const int cnt = c0 < te ? (int)min<uint64_t>(16, te - c0) : 0;
-  uint8_t* out = d.out + (off + c0) * E;
-  uint8_t* cache = d.cache + off + c0;
+  uint8_t* const out = d.out + off * E;
 
   if (h_mode == 0) {  // RAW: copy and refresh the cache
-    if (cnt > 0) {
-      uint32_t v[16], ex[4] = {0, 0, 0, 0};
-      load16<DT>(st + kHeader + c0 * E, cnt, v);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) ex[j >> 2] |= exp_of<DT>(v[j]) << (8 * (j & 3));
-      store16<DT>(out, cnt, v, aligned);
-      store_bytes16(cache, cnt, aligned, ex);
+    for (int u = 0; u < U; ++u) {
+      if (cnt[u] > 0) {
+        const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
+        uint32_t v[16], ex[4] = {0, 0, 0, 0};
+        load16<DT>(st + kHeader + c0 * E, cnt[u], v);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ex[j >> 2] |= exp_of<DT>(v[j]) << (8 * (j & 3));
+        store16<DT>(out + c0 * E, cnt[u], v, aligned);
+        store_bytes16(cache + c0, cnt[u], aligned, ex);
+      }
     }
     return;
   }
 
-  // COMPRESSED.  Patch range [lo, hi) of this tile, by a 64-ary search.
-  const uint8_t* recs = st + kHeader + n * K + nbm;
+  // 3. COMPRESSED: this tile's patch range [lo, hi)
+  const uint64_t recs = kHeader + n * K + nbm;
   uint32_t lo = 0, hi = 0;
   if (P > 0) {
-    if (wave == 0) {
-      uint32_t bounds[2];
+    if (tpr == 1) {
+      hi = (uint32_t)P;
+    } else {
+      if (wave == 0) {
+        uint32_t bounds[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const uint64_t key = b == 0 ? ts : te;
-        // first position p in [0, P] with idx[p] >= key (predicate idx < key assumed monotone)
-        uint64_t a = 0, z = P;  // answer in [a, z]
-        while (z > a) {
-          const uint64_t span = z - a;
-          const uint64_t step = (span + 63) / 64;
-          const uint64_t p = a + (uint64_t)lane * step;
-          const bool less = (p < z) && (load_u32_le(recs + 5 * p) < key);
-          const uint64_t m = __ballot(less);
-          if (m == 0) {
-            z = a;
-          } else {
-            const uint32_t last = 63u - (uint32_t)__clzll(m);
-            a = a + (uint64_t)last * step + 1;
-            z = min<uint64_t>(z, a - 1 + step);
+        for (int b = 0; b < 2; ++b) {
+          const uint64_t key = b == 0 ? ts : te;
+          uint64_t a = 0, z = P;  // first p with idx[p] >= key lies in [a, z]
+          while (z > a) {
+            const uint64_t step = (z - a + 63) / 64;
+            const uint64_t p = a + (uint64_t)lane * step;
+            uint32_t idx = 0, ex = 0;
+            if (p < z) read_rec(st, recs, p, idx, ex);
+            const uint64_t m = __ballot((p < z) && (idx < key));
+            if (m == 0) {
+              z = a;
+            } else {
+              const uint32_t last = 63u - (uint32_t)__clzll(m);
+              a = a + (uint64_t)last * step + 1;
+              z = min<uint64_t>(z, a - 1 + step);
+            }
           }
+          bounds[b] = (uint32_t)a;
         }
-        bounds[b] = (uint32_t)a;
+        if (lane == 0) {
+          uint32_t e = 0, l = bounds[0], h = bounds[1];
+          if (h < l) { e |= CIERA_ST_PATCH; h = l; }
+          if (te == n && h != P) e |= CIERA_ST_PATCH;
+          s_lohi[0] = l; s_lohi[1] = h;
+          if (e) s_err = e;
+        }
       }
-      if (lane == 0) {
-        uint32_t e = 0;
-        uint32_t l = bounds[0], h = bounds[1];
-        if (h < l) { e |= CIERA_ST_PATCH; h = l; }
-        if (te == n && h != P) e |= CIERA_ST_PATCH;
-        s_lohi[0] = l; s_lohi[1] = h;
-        if (e) s_err = e;
-      }
+      __syncthreads();
+      lo = s_lohi[0];
+      hi = s_lohi[1];
     }
-    __syncthreads();
-    lo = s_lohi[0];
-    hi = s_lohi[1];
   }
 
-  uint32_t sm[16], c[4];
-  if (cnt > 0) {
-    load_sm16<DT>(st + kHeader + c0 * K, cnt, sm);
-    load_bytes16(cache, cnt, aligned, c);
-  }
-  uint32_t ex[4] = {c[0], c[1], c[2], c[3]};
-  const bool patched = hi > lo;   // uniform
+  // 4. merged exponents: cached ones, overridden by this tile's patches
+  uint32_t ex[U][4];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ex[u][k] = cw[u][k];
+  const bool patched = hi > lo;  // uniform
   if (patched) {
-    if (cnt > 0) {
-      reinterpret_cast<uint4*>(s_ov)[tid] = make_uint4(c[0], c[1], c[2], c[3]);
-    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (cnt[u] > 0)
+        reinterpret_cast<uint4*>(s_ov)[u * kThreads + tid] = make_uint4(cw[u][0], cw[u][1], cw[u][2], cw[u][3]);
     __syncthreads();
     const uint64_t b0 = ts / B;
     for (uint32_t p = lo + tid; p < hi; p += kThreads) {
-      const uint32_t idx = load_u32_le(recs + 5 * (uint64_t)p);
-      const uint8_t v = recs[5 * (uint64_t)p + 4];
-      uint32_t e = 0;
-      if (p > 0 && load_u32_le(recs + 5 * (uint64_t)(p - 1)) >= idx) e |= CIERA_ST_PATCH;
+      uint32_t idx, v, e = 0;
+      read_rec(st, recs, p, idx, v);
+      if (p > 0) {
+        uint32_t pidx, pv;
+        read_rec(st, recs, p - 1, pidx, pv);
+        if (pidx >= idx) e |= CIERA_ST_PATCH;
+      }
       if (idx < ts || idx >= te) {
         e |= CIERA_ST_PATCH;
       } else {
-        s_ov[idx - ts] = v;
+        s_ov[idx - ts] = (uint8_t)v;
         const uint32_t bb = (uint32_t)(idx / B - b0);
         atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
       }
       if (e) atomicOr(&s_err, e);
     }
     __syncthreads();
-    if (cnt > 0) {
-      const uint4 o = reinterpret_cast<const uint4*>(s_ov)[tid];
-      ex[0] = o.x; ex[1] = o.y; ex[2] = o.z; ex[3] = o.w;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (cnt[u] > 0) {
+        const uint4 o = reinterpret_cast<const uint4*>(s_ov)[u * kThreads + tid];
+        ex[u][0] = o.x; ex[u][1] = o.y; ex[u][2] = o.z; ex[u][3] = o.w;
+      }
     }
   }
 
-  // bitmap check: this tile's bits must mark exactly the blocks holding patches
-  if (P > 0 && tid == 0) {
-    const uint8_t* bm = st + kHeader + n * K;
-    const uint64_t b0 = ts / B;
-    const uint64_t b1 = (te + B - 1) / B;
+  // 5. bitmap check: the tile's bits mark exactly the blocks that hold patches
+  if (P > 0) {
+    const uint64_t b0 = ts / B, b1 = (te + B - 1) / B;
     const uint32_t nbt = (uint32_t)(b1 - b0);
-    uint64_t got = 0;
-    for (uint64_t by = b0 / 8; by <= (b1 - 1) / 8; ++by) got |= (uint64_t)bm[by] << (8 * (by - b0 / 8));
-    got >>= (b0 & 7u);
-    if (nbt < 64) got &= ((uint64_t)1 << nbt) - 1;
-    const uint64_t want = (uint64_t)s_expbm[0] | ((uint64_t)s_expbm[1] << 32);
-    uint32_t e = got != want ? CIERA_ST_BITMAP : 0u;
-    if (te == n && (nb & 7u) != 0 && (bm[nbm - 1] >> (nb & 7u)) != 0) e |= CIERA_ST_BITMAP;
-    if (e) atomicOr(&s_err, e);
+    const uint8_t* bm = st + kHeader + n * K;
+    if (tid * 32 < nbt) {
+      const uint32_t len = min(32u, nbt - tid * 32);
+      const uint32_t got = get_bits(bm, b0 + tid * 32, len);
+      if (got != s_expbm[tid]) atomicOr(&s_err, (uint32_t)CIERA_ST_BITMAP);
+    }
+    if (te == n && tid == 0 && (nb & 7u) != 0 && (gp(bm)[nbm - 1] >> (nb & 7u)) != 0)
+      atomicOr(&s_err, (uint32_t)CIERA_ST_BITMAP);
   }
 
-  if (cnt > 0) {
-    uint32_t v[16];
+  // 6. merge and store; write back only cache chunks that changed
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm[j], byte_of(ex, j));
-    store16<DT>(out, cnt, v, aligned);
-    if (patched && (ex[0] != c[0] || ex[1] != c[1] || ex[2] != c[2] || ex[3] != c[3]))
-      store_bytes16(cache, cnt, aligned, ex);
+  for (int u = 0; u < U; ++u) {
+    if (cnt[u] > 0) {
+      const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
+      uint32_t v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
+      store16<DT>(out + c0 * E, cnt[u], v, aligned);
+      if (patched && (ex[u][0] != cw[u][0] || ex[u][1] != cw[u][1] || ex[u][2] != cw[u][2] || ex[u][3] != cw[u][3]))
+        store_bytes16(cache + c0, cnt[u], aligned, ex[u]);
+    }
   }
   if (P > 0) {
     __syncthreads();
-    if (tid == 0 && s_err) atomicOr(status_out, s_err);
+    if (tid == 0 && s_err) report(status_out, s_err);
   }
 }
 
@@ -678,8 +734,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void cache_update_kernel(const uint8_t* __restrict__ w,
-                                                                uint8_t* __restrict__ cache,
-                                                                uint64_t n) {
+                                                                uint8_t* __restrict__ cache, uint64_t n) {
   constexpr int E = Tr<DT>::E;
   const bool aligned = (reinterpret_cast<uintptr_t>(cache) & 15u) == 0;
   const uint64_t chunks = (n + 15) / 16;
@@ -699,12 +754,10 @@ __global__ __launch_bounds__(kThreads) void cache_update_kernel(const uint8_t* _
 
 // ------------------------------------------------------------------- launchers
 
-hipError_t launch_encode(int dtype, int sub, const EncItem* items, const uint32_t* tile_begin,
-                         uint32_t count, uint32_t total_tiles, EncCtl* ctl, uint32_t* raw_list,
-                         uint64_t* status, uint32_t epoch, hipStream_t s) {
-  const dim3 grid(total_tiles), block(kThreads);
-#define CIERA_ENC(DT, S) \
-  hipLaunchKernelGGL((encode_kernel<DT, S>), grid, block, 0, s, items, tile_begin, count, total_tiles, ctl, raw_list, status, epoch)
+hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
+                         uint32_t batch_id, hipStream_t s) {
+  const dim3 grid(nitems * a.tpi), block(kThreads);
+#define CIERA_ENC(DT, S) hipLaunchKernelGGL((encode_kernel<DT, S>), grid, block, 0, s, a, ctl, batch_id)
   if (dtype == 1) {
     switch (sub) {
       case 1: CIERA_ENC(1, 1); break;
@@ -726,24 +779,39 @@ hipError_t launch_encode(int dtype, int sub, const EncItem* items, const uint32_
   return hipGetLastError();
 }
 
-hipError_t launch_encode_fixup(int dtype, const EncItem* items, const EncCtl* ctl,
-                               const uint32_t* raw_list, hipStream_t s) {
-  const dim3 grid(1024), block(kThreads);
-  if (dtype == 1) hipLaunchKernelGGL((encode_fixup_kernel<1>), grid, block, 0, s, items, ctl, raw_list);
-  else hipLaunchKernelGGL((encode_fixup_kernel<2>), grid, block, 0, s, items, ctl, raw_list);
+hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, const uint32_t* raw_flag,
+                               const uint32_t* any_raw, uint32_t tag, hipStream_t s) {
+  const dim3 grid(512), block(kThreads);
+  hipLaunchKernelGGL(encode_fixup_kernel, grid, block, 0, s, items, count, raw_flag, any_raw, tag);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int dtype, const DecItem* items, const uint32_t* tile_begin,
-                         uint32_t count, uint32_t total_tiles, uint32_t* status, hipStream_t s) {
-  const dim3 grid(total_tiles), block(kThreads);
-  if (dtype == 1) hipLaunchKernelGGL((decode_kernel<1>), grid, block, 0, s, items, tile_begin, count, status);
-  else hipLaunchKernelGGL((decode_kernel<2>), grid, block, 0, s, items, tile_begin, count, status);
+hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems, uint32_t tpr,
+                         uint32_t world, uint32_t* status, const uint32_t* ctl, uint32_t batch_id,
+                         hipStream_t s) {
+  const dim3 grid(nitems * tpr * world), block(kThreads);
+#define CIERA_DEC(DT, U) \
+  hipLaunchKernelGGL((decode_kernel<DT, U>), grid, block, 0, s, items, item0, tpr, world, status, ctl, batch_id)
+  if (dtype == 1) {
+    switch (u) {
+      case 1: CIERA_DEC(1, 1); break;
+      case 2: CIERA_DEC(1, 2); break;
+      case 4: CIERA_DEC(1, 4); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (u) {
+      case 1: CIERA_DEC(2, 1); break;
+      case 2: CIERA_DEC(2, 2); break;
+      case 4: CIERA_DEC(2, 4); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef CIERA_DEC
   return hipGetLastError();
 }
 
-hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n,
-                               hipStream_t s) {
+hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n, hipStream_t s) {
   const uint64_t chunks = (n + 15) / 16;
   uint64_t blocks = (chunks + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;

@@ -63,6 +63,7 @@ class LayerCodec:
                            for i, t in enumerate(self.tensors)]
         self.dec_scratch = torch.empty(max(B.ciera_decode_scratch_bytes(self._dec_items), 256),
                                        dtype=torch.uint8, device=self.device)
+        self._dec_batch = None
         self._enc_scratch = None
 
     # ------------------------------------------------------------------ views
@@ -109,8 +110,29 @@ class LayerCodec:
         B.ciera_encode(items, self.encode_scratch(items), stream=stream)
 
     def decode(self, stream=None, zero_status: bool = True) -> torch.Tensor:
-        """Rebuild every tensor from its W slots and update the cache (one batched call)."""
+        """Rebuild every tensor from its W slots and update the cache (one launch of
+        the prepared decode batch; its tables are uploaded on the first call)."""
         if zero_status:
             self.status.zero_()
-        B.ciera_decode(self._dec_items, self.status, self.dec_scratch, stream=stream)
+        if self._dec_batch is None:
+            self._dec_batch = B.ciera_decode_prepare(self._dec_items, self.status, self.dec_scratch,
+                                                     stream=stream)
+        B.ciera_decode_launch(self._dec_batch, stream=stream)
         return self.status
+
+    def prepare_encode(self, rank: int, shards: Sequence[torch.Tensor],
+                       compress: Optional[Sequence[int]] = None, stream=None) -> "PreparedEncode":
+        """A prepared encode of rank's shards: tables uploaded once, each launch
+        then only enqueues kernels (the shard buffers stay bound)."""
+        items = self.encode_items(rank, shards, compress)
+        scratch = torch.empty(max(B.ciera_encode_scratch_bytes(items), 256), dtype=torch.uint8,
+                              device=self.device)
+        return PreparedEncode(B.ciera_encode_prepare(items, scratch, stream=stream), scratch, list(shards))
+
+
+class PreparedEncode:
+    def __init__(self, batch: "B.Batch", scratch: torch.Tensor, keep: list):
+        self.batch, self.scratch, self._keep = batch, scratch, keep
+
+    def launch(self, stream=None) -> None:
+        B.ciera_encode_launch(self.batch, stream=stream)
