@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the CIERA encode/decode hot path on one MI355X.
+
+Workload: a full OLMoE-shaped MoE layer in bf16 -- 64 experts x (2048x1024,
+2048x1024, 1024x2048) = 402,653,184 weights -- row-sharded over 16 ranks, with
+1% of exponents changing per iteration (uniform; --clustered for 4 KiB runs).
+
+One step is one iteration of the hot path as one rank runs it:
+  plan    -- ciera_plan for all 192 tensors (host);
+  encode  -- this rank's 1/16 shard of every tensor, one batched launch;
+  decode  -- every tensor rebuilt from all 16 ranks' streams + cache update,
+             one batched launch.
+The other 15 ranks' streams are encoded locally before timing.  Steps alternate
+between two states so that every step sees exactly the configured change rate:
+state A encodes W1 against the cache of W0 (decode leaves the cache at W1),
+state B encodes W0 against the cache of W1 (decode leaves it at W0).
+
+Prints one JSON line (see the keys below).  --gpus above 1 is refused: this
+build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--frac", type=float, default=0.01)
+    ap.add_argument("--clustered", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy five times (the reference "
+                         "kernel for scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.gpus != 1:
+        log("bench.py runs on one GPU only: the collective is outside this build; "
+            "run with --gpus 1")
+        sys.exit(2)
+    import torch
+
+    from gen import workloads as W
+    import lossless_weight_compression_amd as L
+    from lossless_weight_compression_amd.layer import LayerCodec
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    specs = W.olmoe_layer_specs()
+    cfg = W.PairConfig(f"bench-{args.frac}-{'c' if args.clustered else 'u'}", frac=args.frac,
+                       clustered=args.clustered)
+    world, block = 16, 512
+    shapes = [(s.rows, s.cols) for s in specs]
+    N = sum(s.numel for s in specs)
+    ppm = int(round(args.frac * 1e6))
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    win = W.layer_windows(specs, cfg)
+    w0, w1 = [], []
+    for i in range(len(specs)):
+        a, b = W.weight_pair(specs, i, cfg, device=dev, windows=win)
+        w0.append(a)
+        w1.append(b)
+    torch.cuda.synchronize()
+    log(f"generated {N} weights in {time.time() - t0:.1f}s")
+
+    A = LayerCodec(shapes, torch.bfloat16, world, block, dev, ppm)
+    Bc = LayerCodec(shapes, torch.bfloat16, world, block, dev, ppm, cache=A.cache)
+
+    def shards(ws, r):
+        out = []
+        for i in range(len(specs)):
+            off, n = A.shard(i, r)
+            out.append(ws[i].reshape(-1)[off:off + n])
+        return out
+
+    # cache <- exp(W0); state A streams (W1 vs exp(W0)) for all ranks
+    A.seed_cache(w0)
+    for r in range(world):
+        A.encode(r, shards(w1, r))
+    stA = A.decode()
+    for r in range(world):
+        Bc.encode(r, shards(w0, r))
+    stB = Bc.decode()
+    torch.cuda.synchronize()
+    assert stA.item() == 0 and stB.item() == 0, "decode reported corrupt streams"
+    for i in range(len(specs)):
+        assert torch.equal(A.out_view(i).view(torch.int16), w1[i].reshape(-1).view(torch.int16)), i
+        assert torch.equal(Bc.out_view(i).view(torch.int16), w0[i].reshape(-1).view(torch.int16)), i
+    log("setup round trip W0 -> W1 -> W0 bit-exact")
+
+    # stream accounting from the headers (state A; B moves the same positions)
+    def headers(codec):
+        idx = torch.cat([torch.arange(codec.stream_off[i] + r * codec.slot_bytes[i],
+                                      codec.stream_off[i] + r * codec.slot_bytes[i] + 64)
+                         for i in range(len(specs)) for r in range(world)]).to(dev)
+        h = codec.streams[idx].view(-1, 64).cpu()
+        q = h.view(torch.int64)  # 8 little-endian u64 per header
+        return {"n": q[:, 2], "n_changed": q[:, 3], "total_len": q[:, 4], "mode": h[:, 7]}
+
+    hA = headers(A)
+    P_total = int(hA["n_changed"].sum())
+    stream_bytes = int(hA["total_len"].sum())
+    raw_bytes = int((64 + 2 * hA["n"]).sum())
+    r0 = [i * world for i in range(len(specs))]  # rank-0 rows in header order
+    enc_stream_bytes = int(hA["total_len"][r0].sum())
+    n_enc = int(hA["n"][r0].sum())
+    assert int(hA["n"].sum()) == N
+    dec_bytes = stream_bytes + N + 2 * N + P_total          # read streams + cache, write values + changed cache
+    enc_bytes = 2 * n_enc + n_enc + enc_stream_bytes       # read shard + cache slice, write streams
+    log(f"P={P_total} ({P_total / N:.4%}), streams {stream_bytes} B vs raw {raw_bytes} B "
+        f"(ratio {raw_bytes / stream_bytes:.4f}), COMPRESSED streams {int((hA['mode'] == 1).sum())}/{len(hA['mode'])}")
+
+    # prepared launches (tables uploaded once)
+    plans_expected = [p.compress for p in A.plans]
+    encA = A.prepare_encode(0, shards(w1, 0))
+    encB = Bc.prepare_encode(0, shards(w0, 0))
+    stream = torch.cuda.current_stream()
+
+    def step(k, ev=None):
+        codec, enc = (A, encA) if k % 2 == 0 else (Bc, encB)
+        # plan: the per-tensor selector (host), consumed by the prepared batch
+        for i, t in enumerate(codec.tensors):
+            if L.ciera_plan(t, ppm).compress != plans_expected[i]:
+                raise RuntimeError("plan changed: the prepared batch would be stale")
+        if ev is not None:
+            ev[0].record(stream)
+        enc.launch(stream)
+        if ev is not None:
+            ev[1].record(stream)
+        codec.decode(stream, zero_status=False)
+        if ev is not None:
+            ev[2].record(stream)
+
+    A.status.zero_()
+    Bc.status.zero_()
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, evs[k])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    enc_avg = sum(enc_ms) / len(enc_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    ms_step = t_total * 1e3 / args.steps
+    assert A.status.item() == 0 and Bc.status.item() == 0, "decode reported corrupt streams"
+    last = A if (args.warmup + args.steps - 1) % 2 == 0 else Bc
+    want = w1 if last is A else w0
+    for i in range(0, len(specs), 17):
+        assert torch.equal(last.out_view(i).view(torch.int16), want[i].reshape(-1).view(torch.int16)), i
+    log(f"steps {args.steps}: {ms_step:.4f} ms/step; encode avg {enc_avg * 1e3:.1f} us "
+        f"(p10 {enc_ms[len(enc_ms) // 10] * 1e3:.1f}, p90 {enc_ms[9 * len(enc_ms) // 10] * 1e3:.1f}); "
+        f"decode avg {dec_avg * 1e3:.1f} us (p10 {dec_ms[len(dec_ms) // 10] * 1e3:.1f}, "
+        f"p90 {dec_ms[9 * len(dec_ms) // 10] * 1e3:.1f})")
+
+    logical = 2 * n_enc + 2 * N
+    value = logical / (ms_step * 1e-3) / 1e9
+    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
+    enc_gbps = enc_bytes / (enc_avg * 1e-3) / 1e9
+
+    # HBM traffic of the decode kernel from the committed PMC summary, if it was
+    # taken on the current kernel source
+    traffic = None
+    src = os.path.join(ROOT, "lossless_weight_compression_amd", "csrc", "ciera_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    tf = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if os.path.exists(tf):
+        t = json.load(open(tf))
+        if t.get("kernel_source_sha256") == sha and t.get("workload") == "olmoe_layer_bf16_1pct_uniform" \
+                and not args.clustered and ppm == 10000:
+            traffic = t.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(specs, w0, w1, world, block, A, args.cpu_seconds)
+
+    out = {
+        "metric": "encode/decode GB/s (bf16 OLMoE MoE layer, 1% exp change) and % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": "olmoe_moe_layer_bf16_" + ("clustered" if args.clustered else "uniform"),
+                   "experts": 64, "tensors": len(specs), "elements": N, "world": world,
+                   "block_size": block, "change_frac": args.frac,
+                   "step": "plan(192) + encode(rank 0 shard) + decode(full layer, 16 streams)"},
+        "encode": {"avg_us": round(enc_avg * 1e3, 2), "elements": n_enc,
+                   "logical_GBps": round(2 * n_enc / (enc_avg * 1e-3) / 1e9, 1),
+                   "algorithmic_bytes": enc_bytes, "achieved_GBps": round(enc_gbps, 1),
+                   "hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4)},
+        "decode": {"avg_us": round(dec_avg * 1e3, 2), "elements": N,
+                   "logical_GBps": round(2 * N / (dec_avg * 1e-3) / 1e9, 1),
+                   "algorithmic_bytes": dec_bytes, "achieved_GBps": round(dec_gbps, 1),
+                   "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4)},
+        "compression_ratio": round(raw_bytes / stream_bytes, 4),
+        "changed_exponents": P_total,
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<bf16,2>",
+                     "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(specs, w0, w1, world, block, codec, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    for whole tensors in layer order, encode rank 0's shard and decode the
+    full tensor from all 16 streams, until the CPU time budget is spent.  Its
+    rank-0 streams are also compared with the GPU's bytes (state A)."""
+    import numpy as np
+    import torch
+
+    from oracle import ciera_oracle as O
+
+    def bits(t):
+        return t.reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)
+
+    t_enc = t_dec = 0.0
+    logical = 0
+    done = 0
+    for i, s in enumerate(specs):
+        x0, x1 = bits(w0[i]), bits(w1[i])
+        cache = O.cache_update(x0, O.BF16)
+        streams = []
+        for r in range(world):
+            off, n = O.shard(s.rows, s.cols, world, r)
+            if r == 0:
+                t = time.perf_counter()
+            st = O.encode(x1[off:off + n], cache[off:off + n], O.BF16, block, bool(codec.plans[i].compress),
+                          off, r, world)
+            if r == 0:
+                t_enc += time.perf_counter() - t
+                gpu = codec.slot(i, 0)[:st.size].cpu().numpy()
+                if not np.array_equal(gpu, st):
+                    raise RuntimeError(f"GPU stream of tensor {i} rank 0 differs from the oracle")
+                logical += 2 * n
+            streams.append(st)
+        t = time.perf_counter()
+        out, new_cache, status = O.decode(streams, s.rows, s.cols, O.BF16, block, world, cache)
+        t_dec += time.perf_counter() - t
+        assert status == 0 and np.array_equal(out, x1)
+        logical += 2 * s.numel
+        done += 1
+        if t_enc + t_dec >= budget_s:
+            break
+    secs = t_enc + t_dec
+    return {"value": round(logical / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(specs)} tensors: rank-0 encode + full decode from 16 streams "
+                      f"({logical} logical bytes, {secs:.1f} s single-threaded numpy)",
+            "encode_s": round(t_enc, 3), "decode_s": round(t_dec, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,8 @@ def _align(x: int, a: int) -> int:
 class LayerCodec:
     def __init__(self, shapes: Sequence[Tuple[int, int]], dtype: torch.dtype, world: int,
                  block_size: int = 512, device="cuda", change_ppm: int = 10_000,
-                 cost: Optional[B.CostModel] = None, with_out: bool = True):
+                 cost: Optional[B.CostModel] = None, with_out: bool = True,
+                 cache: Optional[torch.Tensor] = None):
         self.dtype = dtype
         self.cdtype = TORCH_TO_CIERA[dtype]
         self.e = ELEM[self.cdtype]
@@ -52,7 +53,11 @@ class LayerCodec:
             s += _align(self.slot_bytes[i] * world, 256)
             self.out_off.append(o)
             o += _align(n * self.e, 256)
-        self.cache = torch.zeros(max(c, 256), dtype=torch.uint8, device=self.device)
+        if cache is not None:  # share another codec's cache (same shapes, same layout)
+            assert cache.dtype == torch.uint8 and cache.numel() >= max(c, 256)
+            self.cache = cache
+        else:
+            self.cache = torch.zeros(max(c, 256), dtype=torch.uint8, device=self.device)
         self.streams = torch.zeros(max(s, 256), dtype=torch.uint8, device=self.device)
         self.out = (torch.zeros(max(o, 256), dtype=torch.uint8, device=self.device)
                     if with_out else None)
