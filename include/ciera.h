@@ -211,6 +211,10 @@ ciera_status_t ciera_cache_update(const ciera_tensor_t* t, const void* weights_f
 const char* ciera_status_str(ciera_status_t s);
 uint32_t ciera_abi_version(void);
 
+/* ciera_last_error -- which HIP call failed, and how, behind the calling
+ * thread's most recent CIERA_ERR_DEVICE (a static per-thread string). */
+const char* ciera_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

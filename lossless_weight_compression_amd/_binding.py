@@ -19,13 +19,14 @@ HEADER_BYTES = 64
 EXPORTS = ["ciera_plan", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
            "ciera_encode_prepare", "ciera_encode_launch", "ciera_decode_scratch_bytes",
            "ciera_decode", "ciera_decode_prepare", "ciera_decode_launch", "ciera_cache_update",
-           "ciera_status_str", "ciera_abi_version"]
+           "ciera_status_str", "ciera_abi_version", "ciera_last_error"]
 
 
 class CieraError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__(f"{where}: {_lib.ciera_status_str(code).decode()} ({code})")
+        detail = f" [{_lib.ciera_last_error().decode()}]" if code == CIERA_ERR_DEVICE else ""
+        super().__init__(f"{where}: {_lib.ciera_status_str(code).decode()} ({code}){detail}")
 
 
 class Tensor(ctypes.Structure):
@@ -69,11 +70,27 @@ class Batch(ctypes.Structure):
     _fields_ = [("opaque", c_uint64 * 512)]
 
 
+def _hip_runtimes() -> set:
+    """Paths of every HIP runtime library mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return set()
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                           "(hipcc --offload-arch=gfx950) first")
+    # torch ships its own HIP runtime under the same soname.  Loading torch first
+    # makes libciera.so bind to that copy; loading libciera.so first would map a
+    # second HIP/HSA runtime into the process, and one of them then finds no GPU.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped into this process: {sorted(runtimes)}")
     sig = {
         "ciera_plan": (c_int, [POINTER(Tensor), c_uint32, POINTER(CostModel), POINTER(Plan)]),
         "ciera_shard": (c_int, [POINTER(Tensor), c_uint32, POINTER(c_uint64), POINTER(c_uint64)]),
@@ -90,6 +107,7 @@ def _load() -> ctypes.CDLL:
         "ciera_cache_update": (c_int, [POINTER(Tensor), c_void_p, c_void_p, c_void_p]),
         "ciera_status_str": (c_char_p, [c_int]),
         "ciera_abi_version": (c_uint32, []),
+        "ciera_last_error": (c_char_p, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

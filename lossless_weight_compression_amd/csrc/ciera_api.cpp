@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <atomic>
 #include <chrono>
 #include <cstring>
@@ -33,6 +34,14 @@ bool pow2(uint32_t x) { return x && !(x & (x - 1)); }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 uint64_t bitmap_bytes(uint64_t n, uint32_t B) { return ((n + B - 1) / B + 7) / 8; }
+
+// The HIP error behind the calling thread's last CIERA_ERR_DEVICE.
+thread_local char g_last_error[256] = "no error";
+
+ciera_status_t device_error(const char* what, hipError_t e) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return CIERA_ERR_DEVICE;
+}
 
 ciera_status_t check_tensor(const ciera_tensor_t* t) {
   if (!t) return CIERA_ERR_INVALID_ARG;
@@ -240,6 +249,8 @@ extern "C" {
 
 uint32_t ciera_abi_version(void) { return CIERA_ABI_VERSION; }
 
+const char* ciera_last_error(void) { return g_last_error; }
+
 const char* ciera_status_str(ciera_status_t s) {
   switch (s) {
     case CIERA_OK: return "ok";
@@ -349,7 +360,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     any |= d.compress;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (upload(scratch, blob.data(), blob.size(), st) != hipSuccess) return CIERA_ERR_DEVICE;
+  if (hipError_t e = upload(scratch, blob.data(), blob.size(), st)) return device_error("descriptor upload", e);
   b->magic = kEncMagic;
   b->scratch = static_cast<uint8_t*>(scratch);
   b->scratch_bytes = scratch_bytes;
@@ -385,14 +396,16 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
     a.status = reinterpret_cast<uint64_t*>(b->scratch + g.status_off);
     a.raw_flag = flags;
     a.any_raw = ctl + 1;
-    if (launch_encode(g.dtype, g.unit, g.nitems, a, ctl, b->batch_id, st) != hipSuccess) {
+    if (hipError_t e = launch_encode(g.dtype, g.unit, g.nitems, a, ctl, b->batch_id, st)) {
       b->magic = 0;  // counters may be out of step now: the batch must be prepared again
-      return CIERA_ERR_DEVICE;
+      return device_error("encode launch", e);
     }
   }
-  if (b->any_compress && launch_encode_fixup(items, b->count, flags, ctl + 1, tag, st) != hipSuccess) {
-    b->magic = 0;
-    return CIERA_ERR_DEVICE;
+  if (b->any_compress) {
+    if (hipError_t e = launch_encode_fixup(items, b->count, flags, ctl + 1, tag, st)) {
+      b->magic = 0;
+      return device_error("encode fallback launch", e);
+    }
   }
   b->launches += 1;
   return CIERA_OK;
@@ -455,7 +468,7 @@ ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t c
     d.block_size = it.t.block_size;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (upload(scratch, blob.data(), blob.size(), st) != hipSuccess) return CIERA_ERR_DEVICE;
+  if (hipError_t e = upload(scratch, blob.data(), blob.size(), st)) return device_error("descriptor upload", e);
   b->magic = kDecMagic;
   b->scratch = static_cast<uint8_t*>(scratch);
   b->scratch_bytes = scratch_bytes;
@@ -476,9 +489,9 @@ ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream) {
   const DecItem* items = reinterpret_cast<const DecItem*>(b->scratch + b->off_items);
   for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
     const Group& g = b->g[gi];
-    if (launch_decode(g.dtype, g.unit, items, g.item0, g.nitems, g.tpr, g.world, b->status_dev, ctl,
-                      b->batch_id, st) != hipSuccess)
-      return CIERA_ERR_DEVICE;
+    if (hipError_t e = launch_decode(g.dtype, g.unit, items, g.item0, g.nitems, g.tpr, g.world, b->status_dev,
+                                     ctl, b->batch_id, st))
+      return device_error("decode launch", e);
   }
   b->launches += 1;
   return CIERA_OK;
@@ -500,9 +513,9 @@ ciera_status_t ciera_cache_update(const ciera_tensor_t* t, const void* weights_f
   const uint64_t N = t->rows * t->cols;
   if (N == 0) return CIERA_OK;
   if (!weights_full || !aligned(weights_full, 16) || !cache_full) return CIERA_ERR_INVALID_ARG;
-  if (launch_cache_update(t->dtype, static_cast<const uint8_t*>(weights_full), cache_full, N,
-                          reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-    return CIERA_ERR_DEVICE;
+  if (hipError_t e = launch_cache_update(t->dtype, static_cast<const uint8_t*>(weights_full), cache_full, N,
+                                         reinterpret_cast<hipStream_t>(stream)))
+    return device_error("cache update launch", e);
   return CIERA_OK;
 }
 

@@ -529,10 +529,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
   constexpr uint32_t BMW = (T / 64 + 31) / 32;  // words of per-tile block bits (B >= 64)
   constexpr int SW = 4 * K;                     // words of 16 sign|mantissa records
   __shared__ uint32_t s_hdr[16];
-  __shared__ uint32_t s_lohi[2];
-  __shared__ uint32_t s_expbm[BMW];
+  __shared__ uint32_t s_expbm[BMW];  // blocks of the tile that hold a patch
+  __shared__ uint32_t s_pm[T / 32];  // positions of the tile that hold a patch
   __shared__ uint32_t s_err;
-  __shared__ __align__(16) uint8_t s_ov[T];
+  __shared__ uint8_t s_pv[T];        // patch exponents (valid where s_pm is set)
 
   if (gp(ctl)[0] != batch_id) return;  // scratch does not hold this batch (uniform)
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -572,6 +572,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
     s_hdr[4 * tid] = h.x; s_hdr[4 * tid + 1] = h.y; s_hdr[4 * tid + 2] = h.z; s_hdr[4 * tid + 3] = h.w;
   }
   if (tid < BMW) s_expbm[tid] = 0;
+  for (uint32_t w = tid; w < T / 32; w += kThreads) s_pm[w] = 0;
   if (tid == 0) s_err = 0;
   __syncthreads();
   const uint32_t h_dtype = (s_hdr[1] >> 16) & 0xFFu, h_mode = s_hdr[1] >> 24;
@@ -613,62 +614,59 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
     return;
   }
 
-  // 3. COMPRESSED: this tile's patch range [lo, hi)
+  // 3. COMPRESSED: this tile's patch range [lo, hi).  Every wave finds it on its
+  //    own (two searches sharing a first round of 64 probes, then 32 lanes per
+  //    key), so the records can be read without a barrier in between.
   const uint64_t recs = kHeader + n * K + nbm;
   uint32_t lo = 0, hi = 0;
   if (P > 0) {
     if (tpr == 1) {
       hi = (uint32_t)P;
     } else {
-      if (wave == 0) {
-        uint32_t bounds[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const uint64_t key = b == 0 ? ts : te;
-          uint64_t a = 0, z = P;  // first p with idx[p] >= key lies in [a, z]
-          while (z > a) {
-            const uint64_t step = (z - a + 63) / 64;
-            const uint64_t p = a + (uint64_t)lane * step;
-            uint32_t idx = 0, ex = 0;
-            if (p < z) read_rec(st, recs, p, idx, ex);
-            const uint64_t m = __ballot((p < z) && (idx < key));
-            if (m == 0) {
-              z = a;
-            } else {
-              const uint32_t last = 63u - (uint32_t)__clzll(m);
-              a = a + (uint64_t)last * step + 1;
-              z = min<uint64_t>(z, a - 1 + step);
-            }
-          }
-          bounds[b] = (uint32_t)a;
+      uint64_t a0 = 0, z0 = 0, a1 = 0, z1 = 0;  // first p with idx[p] >= key lies in [a, z]
+      {
+        const uint64_t step = (P + 63) / 64;
+        const uint64_t p = (uint64_t)lane * step;
+        uint32_t idx = 0, ex = 0;
+        if (p < P) read_rec(st, recs, p, idx, ex);
+        const uint64_t m0 = __ballot(p < P && idx < ts), m1 = __ballot(p < P && idx < te);
+        if (m0) { a0 = (uint64_t)(63u - (uint32_t)__clzll(m0)) * step + 1; z0 = min<uint64_t>(P, a0 - 1 + step); }
+        if (m1) { a1 = (uint64_t)(63u - (uint32_t)__clzll(m1)) * step + 1; z1 = min<uint64_t>(P, a1 - 1 + step); }
+      }
+      while (z0 > a0 || z1 > a1) {
+        const bool second = lane >= 32;
+        const uint64_t a = second ? a1 : a0, z = second ? z1 : z0, key = second ? te : ts;
+        const uint64_t step = (z - a + 31) / 32;
+        const uint64_t p = a + (uint64_t)(lane & 31u) * step;
+        const bool valid = z > a && p < z;
+        uint32_t idx = 0, ex = 0;
+        if (valid) read_rec(st, recs, p, idx, ex);
+        const uint64_t m = __ballot(valid && idx < key);
+        const uint32_t h0 = (uint32_t)m, h1 = (uint32_t)(m >> 32);
+        if (z0 > a0) {
+          const uint64_t s0 = (z0 - a0 + 31) / 32;
+          if (h0 == 0) { z0 = a0; } else { a0 = a0 + (uint64_t)(31u - (uint32_t)__clz(h0)) * s0 + 1; z0 = min<uint64_t>(z0, a0 - 1 + s0); }
         }
-        if (lane == 0) {
-          uint32_t e = 0, l = bounds[0], h = bounds[1];
-          if (h < l) { e |= CIERA_ST_PATCH; h = l; }
-          if (te == n && h != P) e |= CIERA_ST_PATCH;
-          s_lohi[0] = l; s_lohi[1] = h;
-          if (e) s_err = e;
+        if (z1 > a1) {
+          const uint64_t s1 = (z1 - a1 + 31) / 32;
+          if (h1 == 0) { z1 = a1; } else { a1 = a1 + (uint64_t)(31u - (uint32_t)__clz(h1)) * s1 + 1; z1 = min<uint64_t>(z1, a1 - 1 + s1); }
         }
       }
-      __syncthreads();
-      lo = s_lohi[0];
-      hi = s_lohi[1];
+      lo = (uint32_t)a0;
+      hi = (uint32_t)a1;
+      if (tid == 0) {
+        uint32_t e = 0;
+        if (hi < lo) e |= CIERA_ST_PATCH;
+        if (te == n && hi != P) e |= CIERA_ST_PATCH;
+        if (e) atomicOr(&s_err, e);
+      }
+      if (hi < lo) hi = lo;
     }
   }
 
-  // 4. merged exponents: cached ones, overridden by this tile's patches
-  uint32_t ex[U][4];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ex[u][k] = cw[u][k];
+  // 4. patches of the tile into LDS: exponent values plus a presence bitmap
   const bool patched = hi > lo;  // uniform
   if (patched) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (cnt[u] > 0)
-        reinterpret_cast<uint4*>(s_ov)[u * kThreads + tid] = make_uint4(cw[u][0], cw[u][1], cw[u][2], cw[u][3]);
-    __syncthreads();
     const uint64_t b0 = ts / B;
     for (uint32_t p = lo + tid; p < hi; p += kThreads) {
       uint32_t idx, v, e = 0;
@@ -681,18 +679,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
       if (idx < ts || idx >= te) {
         e |= CIERA_ST_PATCH;
       } else {
-        s_ov[idx - ts] = (uint8_t)v;
+        const uint32_t o = (uint32_t)(idx - ts);
+        s_pv[o] = (uint8_t)v;
+        atomicOr(&s_pm[o >> 5], 1u << (o & 31u));
         const uint32_t bb = (uint32_t)(idx / B - b0);
         atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
       }
       if (e) atomicOr(&s_err, e);
     }
-    __syncthreads();
+  }
+  if (P > 0) __syncthreads();
+  uint32_t ex[U][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (cnt[u] > 0) {
-        const uint4 o = reinterpret_cast<const uint4*>(s_ov)[u * kThreads + tid];
-        ex[u][0] = o.x; ex[u][1] = o.y; ex[u][2] = o.z; ex[u][3] = o.w;
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ex[u][k] = cw[u][k];
+    if (patched && cnt[u] > 0) {
+      const uint32_t o0 = (uint32_t)u * kSub + tid * kEPT;  // 16-aligned: one half-word of s_pm
+      uint32_t pm = (s_pm[o0 >> 5] >> (o0 & 31u)) & 0xFFFFu;
+      while (pm) {
+        const int j = __ffs(pm) - 1;
+        pm &= pm - 1;
+        const uint32_t sh = 8u * (j & 3);
+        ex[u][j >> 2] = (ex[u][j >> 2] & ~(0xFFu << sh)) | ((uint32_t)s_pv[o0 + j] << sh);
       }
     }
   }
@@ -711,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
       atomicOr(&s_err, (uint32_t)CIERA_ST_BITMAP);
   }
 
-  // 6. merge and store; write back only cache chunks that changed
+  // 6. merge and store; write back the cache lines that changed
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (cnt[u] > 0) {
@@ -720,8 +729,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
       store16<DT>(out + c0 * E, cnt[u], v, aligned);
-      if (patched && (ex[u][0] != cw[u][0] || ex[u][1] != cw[u][1] || ex[u][2] != cw[u][2] || ex[u][3] != cw[u][3]))
-        store_bytes16(cache + c0, cnt[u], aligned, ex[u]);
+    }
+    // cache write-back in whole 128-byte lines (8 lanes): scattered partial
+    // lines cost more HBM time than the extra bytes of full lines
+    const bool dirty = cnt[u] > 0 && (ex[u][0] != cw[u][0] || ex[u][1] != cw[u][1] ||
+                                      ex[u][2] != cw[u][2] || ex[u][3] != cw[u][3]);
+    const uint64_t m = patched ? __ballot(dirty) : 0ull;
+    if (cnt[u] > 0 && ((m >> (lane & ~7u)) & 0xFFu)) {
+      const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
+      store_bytes16(cache + c0, cnt[u], aligned, ex[u]);
     }
   }
   if (P > 0) {
@@ -753,9 +769,12 @@ __global__ __launch_bounds__(kThreads) void cache_update_kernel(const uint8_t* _
 }  // namespace
 
 // ------------------------------------------------------------------- launchers
+// Each launcher clears the thread's last-error state first, so that the error it
+// returns is the launch's own and not one left by an unrelated earlier call.
 
 hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
                          uint32_t batch_id, hipStream_t s) {
+  (void)hipGetLastError();
   const dim3 grid(nitems * a.tpi), block(kThreads);
 #define CIERA_ENC(DT, S) hipLaunchKernelGGL((encode_kernel<DT, S>), grid, block, 0, s, a, ctl, batch_id)
   if (dtype == 1) {
@@ -781,6 +800,7 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
 
 hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, const uint32_t* raw_flag,
                                const uint32_t* any_raw, uint32_t tag, hipStream_t s) {
+  (void)hipGetLastError();
   const dim3 grid(512), block(kThreads);
   hipLaunchKernelGGL(encode_fixup_kernel, grid, block, 0, s, items, count, raw_flag, any_raw, tag);
   return hipGetLastError();
@@ -789,6 +809,7 @@ hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, const uint3
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems, uint32_t tpr,
                          uint32_t world, uint32_t* status, const uint32_t* ctl, uint32_t batch_id,
                          hipStream_t s) {
+  (void)hipGetLastError();
   const dim3 grid(nitems * tpr * world), block(kThreads);
 #define CIERA_DEC(DT, U) \
   hipLaunchKernelGGL((decode_kernel<DT, U>), grid, block, 0, s, items, item0, tpr, world, status, ctl, batch_id)
@@ -816,6 +837,7 @@ hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint
   uint64_t blocks = (chunks + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;
   if (blocks == 0) return hipSuccess;
+  (void)hipGetLastError();
   const dim3 grid((uint32_t)blocks), block(kThreads);
   if (dtype == 1) hipLaunchKernelGGL((cache_update_kernel<1>), grid, block, 0, s, w, cache, n);
   else hipLaunchKernelGGL((cache_update_kernel<2>), grid, block, 0, s, w, cache, n);
