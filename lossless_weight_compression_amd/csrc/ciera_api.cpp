@@ -357,6 +357,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     d.compress = it.compress ? 1u : 0u;
     d.cache_aligned = aligned(d.cache, 16) ? 1u : 0u;
     d.elem_bytes = elem_bytes(it.t.dtype);
+    d.batch_id = b->batch_id;
     any |= d.compress;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -402,7 +403,7 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
     }
   }
   if (b->any_compress) {
-    if (hipError_t e = launch_encode_fixup(items, b->count, flags, ctl + 1, tag, st)) {
+    if (hipError_t e = launch_encode_fixup(items, b->count, flags, ctl + 1, tag, b->batch_id, st)) {
       b->magic = 0;
       return device_error("encode fallback launch", e);
     }
@@ -466,6 +467,7 @@ ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t c
     d.cols = it.t.cols;
     d.world = it.t.world;
     d.block_size = it.t.block_size;
+    d.batch_id = b->batch_id;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (hipError_t e = upload(scratch, blob.data(), blob.size(), st)) return device_error("descriptor upload", e);

@@ -25,7 +25,8 @@ struct EncItem {
   uint32_t compress;
   uint32_t cache_aligned;  // (cache_full + off) is 16-byte aligned
   uint32_t elem_bytes;     // 2 (bf16) or 4 (fp32)
-  uint32_t pad[2];
+  uint32_t batch_id;       // the batch that wrote this descriptor
+  uint32_t pad;
 };
 
 // One decode item: a tensor and its W receive slots.
@@ -37,6 +38,8 @@ struct DecItem {
   uint64_t rows, cols;
   uint32_t world;
   uint32_t block_size;
+  uint32_t batch_id;       // the batch that wrote this descriptor
+  uint32_t pad;
 };
 
 // Encode scratch layout (offsets in bytes from the scratch base):
@@ -57,12 +60,13 @@ struct EncArgs {
   uint32_t* any_raw;
 };
 
-// ctl: the control words at the start of a batch's scratch; ctl[0] holds the
-// batch id written at prepare time, kernels exit at once when it differs.
+// ctl: the control words at the start of a batch's scratch.  Every descriptor
+// carries the id of the batch that wrote it; kernels exit at once when the
+// descriptor they read belongs to another batch (the scratch was taken over).
 hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
                          uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, const uint32_t* raw_flag,
-                               const uint32_t* any_raw, uint32_t tag, hipStream_t s);
+                               const uint32_t* any_raw, uint32_t tag, uint32_t batch_id, hipStream_t s);
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
                          uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,
                          uint32_t batch_id, hipStream_t s);

@@ -335,9 +335,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   __shared__ uint32_t s_wtot[4 * S];
   __shared__ uint32_t s_bm[2 * S];  // one bit per block of the tile: T/B <= T/64 = 64*S bits
 
-  if (gp(ctl)[0] != batch_id) return;  // scratch does not hold this batch (uniform)
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t item = a.item0 + blockIdx.x / a.tpi;
+  const EncItem d = a.items[item];
+  if (d.batch_id != batch_id) return;  // the scratch holds another batch (uniform)
   if (tid == 0)
     s_local = __hip_atomic_fetch_add(gp(a.ctr + item), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
               a.launch * a.tpi;
@@ -345,7 +346,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   __syncthreads();
   const uint32_t local = s_local;
   if (local >= a.tpi) return;  // uniform; cannot happen while counters match launches
-  const EncItem d = a.items[item];
   const uint64_t base = (uint64_t)local * T;
   const uint64_t n = d.n;
   const uint32_t B = d.block_size;
@@ -500,13 +500,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
 // Rewrites as RAW the streams whose COMPRESSED form turned out not shorter.
 __global__ __launch_bounds__(kThreads) void encode_fixup_kernel(const EncItem* __restrict__ items, uint32_t count,
                                                                 const uint32_t* raw_flag, const uint32_t* any_raw,
-                                                                uint32_t tag) {
+                                                                uint32_t tag, uint32_t batch_id) {
   if (*gp(any_raw) != tag) return;
   const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
   for (uint32_t k = 0; k < count; ++k) {
     if (gp(raw_flag)[k] != tag) continue;
     const EncItem d = items[k];
+    if (d.batch_id != batch_id) return;
     if (d.stream == nullptr) continue;
     const uint64_t bytes = d.n * d.elem_bytes;
     const uint64_t vec = bytes / 16;
@@ -531,10 +532,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
   __shared__ uint32_t s_hdr[16];
   __shared__ uint32_t s_expbm[BMW];  // blocks of the tile that hold a patch
   __shared__ uint32_t s_pm[T / 32];  // positions of the tile that hold a patch
-  __shared__ uint32_t s_err;
   __shared__ uint8_t s_pv[T];        // patch exponents (valid where s_pm is set)
 
-  if (gp(ctl)[0] != batch_id) return;  // scratch does not hold this batch (uniform)
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t tpi = tpr * world;
   const uint32_t blk = blockIdx.x / tpi;
@@ -543,6 +542,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
   const uint32_t r = rel / tpr;
   const uint32_t t_in = rel - r * tpr;
   const DecItem d = items[item];
+  if (d.batch_id != batch_id) return;  // the scratch holds another batch (uniform)
   const uint64_t q = d.rows / world, rem = d.rows % world;
   const uint64_t off = ((uint64_t)r * q + min<uint64_t>(r, rem)) * d.cols;
   const uint64_t n = (q + (r < rem ? 1u : 0u)) * d.cols;
@@ -566,6 +566,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
       load_words<4>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
     }
   }
+  const uint64_t nb = (n + B - 1) / B;
+  const uint64_t nbm = (nb + 7) / 8;
+
   // 2. header
   if (tid < 4) {
     const v4u h = ldg16(st + 16 * tid);
@@ -573,15 +576,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
   }
   if (tid < BMW) s_expbm[tid] = 0;
   for (uint32_t w = tid; w < T / 32; w += kThreads) s_pm[w] = 0;
-  if (tid == 0) s_err = 0;
   __syncthreads();
   const uint32_t h_dtype = (s_hdr[1] >> 16) & 0xFFu, h_mode = s_hdr[1] >> 24;
   const uint64_t h_n = s_hdr[4] | ((uint64_t)s_hdr[5] << 32);
   const uint64_t P = s_hdr[6] | ((uint64_t)s_hdr[7] << 32);
   const uint64_t h_tot = s_hdr[8] | ((uint64_t)s_hdr[9] << 32);
   const uint64_t h_off = s_hdr[10] | ((uint64_t)s_hdr[11] << 32);
-  const uint64_t nb = (n + B - 1) / B;
-  const uint64_t nbm = (nb + 7) / 8;
   uint32_t bad = 0;
   if (s_hdr[0] != 0x52454943u || (s_hdr[1] & 0xFFFFu) != 1u) {
     bad = CIERA_ST_MAGIC;
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
         uint32_t e = 0;
         if (hi < lo) e |= CIERA_ST_PATCH;
         if (te == n && hi != P) e |= CIERA_ST_PATCH;
-        if (e) atomicOr(&s_err, e);
+        if (e) report(status_out, e);
       }
       if (hi < lo) hi = lo;
     }
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
         const uint32_t bb = (uint32_t)(idx / B - b0);
         atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
       }
-      if (e) atomicOr(&s_err, e);
+      if (e) report(status_out, e);
     }
   }
   if (P > 0) __syncthreads();
@@ -708,16 +708,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
 
   // 5. bitmap check: the tile's bits mark exactly the blocks that hold patches
   if (P > 0) {
-    const uint64_t b0 = ts / B, b1 = (te + B - 1) / B;
-    const uint32_t nbt = (uint32_t)(b1 - b0);
+    const uint64_t tb0 = ts / B, tb1 = (te + B - 1) / B;
+    const uint32_t nbt = (uint32_t)(tb1 - tb0);
     const uint8_t* bm = st + kHeader + n * K;
-    if (tid * 32 < nbt) {
-      const uint32_t len = min(32u, nbt - tid * 32);
-      const uint32_t got = get_bits(bm, b0 + tid * 32, len);
-      if (got != s_expbm[tid]) atomicOr(&s_err, (uint32_t)CIERA_ST_BITMAP);
-    }
-    if (te == n && tid == 0 && (nb & 7u) != 0 && (gp(bm)[nbm - 1] >> (nb & 7u)) != 0)
-      atomicOr(&s_err, (uint32_t)CIERA_ST_BITMAP);
+    uint32_t e = 0;
+    if (tid * 32 < nbt && get_bits(bm, tb0 + tid * 32, min(32u, nbt - tid * 32)) != s_expbm[tid])
+      e |= CIERA_ST_BITMAP;
+    if (te == n && tid == 0 && (nb & 7u) != 0 && (gp(bm)[nbm - 1] >> (nb & 7u)) != 0) e |= CIERA_ST_BITMAP;
+    if (e) report(status_out, e);
   }
 
   // 6. merge and store; write back the cache lines that changed
@@ -739,10 +737,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
       const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
       store_bytes16(cache + c0, cnt[u], aligned, ex[u]);
     }
-  }
-  if (P > 0) {
-    __syncthreads();
-    if (tid == 0 && s_err) report(status_out, s_err);
   }
 }
 
@@ -799,10 +793,10 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
 }
 
 hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, const uint32_t* raw_flag,
-                               const uint32_t* any_raw, uint32_t tag, hipStream_t s) {
+                               const uint32_t* any_raw, uint32_t tag, uint32_t batch_id, hipStream_t s) {
   (void)hipGetLastError();
-  const dim3 grid(512), block(kThreads);
-  hipLaunchKernelGGL(encode_fixup_kernel, grid, block, 0, s, items, count, raw_flag, any_raw, tag);
+  const dim3 grid(64), block(kThreads);
+  hipLaunchKernelGGL(encode_fixup_kernel, grid, block, 0, s, items, count, raw_flag, any_raw, tag, batch_id);
   return hipGetLastError();
 }
 
