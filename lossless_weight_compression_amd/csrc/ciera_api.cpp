@@ -155,7 +155,7 @@ uint32_t enc_sub(uint32_t B, uint64_t n) {
   if (n > (uint64_t)kSub && s < 2) s = 2;
   return s;
 }
-uint32_t dec_unit(uint64_t n0) { return n0 > (uint64_t)kSub ? 2u : 1u; }
+uint32_t dec_unit(uint64_t n0) { return n0 > (uint64_t)kDecRow ? 2u : 1u; }
 
 struct EncPlan {
   std::vector<uint32_t> order;  // items in group order
@@ -221,7 +221,7 @@ ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count, DecP
     shard_of(&it.t, 0, &off, &n0);
     if (n0 >= ((uint64_t)1 << 32)) return CIERA_ERR_UNSUPPORTED;
     const uint32_t U = dec_unit(n0);
-    const uint64_t T = (uint64_t)kSub * U;
+    const uint64_t T = (uint64_t)kDecRow * U;
     const uint64_t tpr = std::max<uint64_t>(1, (n0 + T - 1) / T);
     by[std::make_tuple(it.t.dtype, U, (uint32_t)tpr, it.t.world)].push_back(i);
   }

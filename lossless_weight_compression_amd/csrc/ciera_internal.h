@@ -12,6 +12,14 @@ constexpr int kEPT = 16;               // values per thread per chunk
 constexpr int kSub = kThreads * kEPT;  // 4096 values per chunk row of a tile
 constexpr uint64_t kHeader = 64;
 
+// Decode workgroups: kDecThreads threads, 16 values each per chunk row; a tile
+// is U chunk rows.  (512- and 1024-thread groups, which put more data behind
+// each tile's chain of dependent reads, measured no faster on gfx950.)
+constexpr int kDecThreads = 256;
+constexpr int kDecRow = kDecThreads * kEPT;
+constexpr int kRecBatch = 4;  // consecutive patch records per decode thread per round
+constexpr int kRecWords = (3 + 5 * kRecBatch + 3) / 4;  // aligned words that cover them
+
 // One encode item as the kernels see it.
 struct EncItem {
   const uint8_t* x;      // shard values

@@ -231,29 +231,40 @@ __device__ __forceinline__ uint32_t sm_from_words(const uint32_t* w, int j) {
   }
 }
 
-// Bits [start, start+nbits) of a least-significant-first bit array, nbits <= 32.
-__device__ __forceinline__ uint32_t get_bits(const uint8_t* bm, uint64_t start, uint32_t nbits) {
-  const uint64_t b0 = start >> 3;
-  const uint32_t sh = (uint32_t)(start & 7u);
-  const uint32_t nbytes = (sh + nbits + 7u) >> 3;
-  uint64_t v = 0;
-  for (uint32_t i = 0; i < nbytes; ++i) v |= (uint64_t)gp(bm)[b0 + i] << (8 * i);
-  v >>= sh;
+// The two aligned words that cover bits [start, start+32) of the bit array at
+// p; the bits are taken out by bits_of() once the words are needed, so the
+// load joins the round of loads around it.  The caller guarantees that the
+// stream goes on for at least 5 bytes past the first needed byte (a patch
+// record follows the bitmap), so both words start inside the stream.
+struct Words2 { uint32_t w0, w1, sh; };
+__device__ __forceinline__ Words2 load_bits_w(const uint8_t* p, uint64_t start) {
+  const uintptr_t at = reinterpret_cast<uintptr_t>(p) + (start >> 3);
+  const uint32_t o = (uint32_t)(at & 3u);
+  const G1 uint32_t* w = gp(reinterpret_cast<const uint32_t*>(at - o));
+  return Words2{w[0], w[1], 8u * o + (uint32_t)(start & 7u)};
+}
+__device__ __forceinline__ uint32_t bits_of(const Words2& r, uint32_t nbits) {
+  const uint64_t v = ((uint64_t)r.w0 | ((uint64_t)r.w1 << 32)) >> r.sh;
   return nbits >= 32 ? (uint32_t)v : (uint32_t)(v & ((1u << nbits) - 1u));
 }
 
 // Patch record p (u32 index, u8 exponent, 5 bytes at recs + 5p) read as the two
 // aligned words that cover it; both words start inside the stream, and the slot
 // is a multiple of 16 bytes, so neither can leave it.
-__device__ __forceinline__ void read_rec(const uint8_t* st, uint64_t recs, uint64_t p, uint32_t& idx,
-                                         uint32_t& ex) {
+__device__ __forceinline__ Words2 load_rec(const uint8_t* st, uint64_t recs, uint64_t p) {
   const uint64_t o = recs + 5 * p;
   const uint64_t a = o & ~(uint64_t)3;
   const G1 uint32_t* w = gp(reinterpret_cast<const uint32_t*>(st + a));
-  const uint64_t v = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
-  const uint32_t sh = (uint32_t)(o - a) * 8u;
-  idx = (uint32_t)(v >> sh);
-  ex = (uint32_t)(v >> (sh + 32u)) & 0xFFu;
+  return Words2{w[0], w[1], (uint32_t)(o - a) * 8u};
+}
+__device__ __forceinline__ void rec_fields(const Words2& r, uint32_t& idx, uint32_t& ex) {
+  const uint64_t v = ((uint64_t)r.w0 | ((uint64_t)r.w1 << 32)) >> r.sh;
+  idx = (uint32_t)v;
+  ex = (uint32_t)(v >> 32) & 0xFFu;
+}
+__device__ __forceinline__ void read_rec(const uint8_t* st, uint64_t recs, uint64_t p, uint32_t& idx,
+                                         uint32_t& ex) {
+  rec_fields(load_rec(st, recs, p), idx, ex);
 }
 
 // ORs decode status bits into the caller's word; a plain read first keeps a
@@ -522,11 +533,11 @@ __global__ __launch_bounds__(kThreads) void encode_fixup_kernel(const EncItem* _
 // the patch range are known, so their latency overlaps that chain.
 
 template <int DT, int U>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restrict__ items, uint32_t item0,
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __restrict__ items, uint32_t item0,
                                                           uint32_t tpr, uint32_t world, uint32_t* status_out,
                                                           const uint32_t* ctl, uint32_t batch_id) {
   constexpr int E = Tr<DT>::E, K = Tr<DT>::K;
-  constexpr uint32_t T = (uint32_t)kSub * U;
+  constexpr uint32_t T = (uint32_t)kDecRow * U;
   constexpr uint32_t BMW = (T / 64 + 31) / 32;  // words of per-tile block bits (B >= 64)
   constexpr int SW = 4 * K;                     // words of 16 sign|mantissa records
   __shared__ uint32_t s_hdr[16];
@@ -559,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
   int cnt[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
+    const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
     cnt[u] = c0 < te ? (int)min<uint64_t>(16, te - c0) : 0;
     if (cnt[u] > 0) {
       load_words<SW>(st + kHeader + c0 * K, (uint32_t)cnt[u] * K, true, sw[u]);
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
     s_hdr[4 * tid] = h.x; s_hdr[4 * tid + 1] = h.y; s_hdr[4 * tid + 2] = h.z; s_hdr[4 * tid + 3] = h.w;
   }
   if (tid < BMW) s_expbm[tid] = 0;
-  for (uint32_t w = tid; w < T / 32; w += kThreads) s_pm[w] = 0;
+  for (uint32_t w = tid; w < T / 32; w += kDecThreads) s_pm[w] = 0;
   __syncthreads();
   const uint32_t h_dtype = (s_hdr[1] >> 16) & 0xFFu, h_mode = s_hdr[1] >> 24;
   const uint64_t h_n = s_hdr[4] | ((uint64_t)s_hdr[5] << 32);
@@ -602,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (cnt[u] > 0) {
-        const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
+        const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
         uint32_t v[16], ex[4] = {0, 0, 0, 0};
         load16<DT>(st + kHeader + c0 * E, cnt[u], v);
 #pragma unroll
@@ -664,28 +675,96 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
     }
   }
 
-  // 4. patches of the tile into LDS: exponent values plus a presence bitmap
+  // 4. patches of the tile into LDS: exponent values plus a presence bitmap.
+  //    Each pass gives every thread c <= kRecBatch consecutive records (c as
+  //    small as the pass allows, so the records spread over all waves), read
+  //    as one round of aligned words; the first pass shares its round with
+  //    the tile's bitmap bits.  A record's predecessor, for the ascending-order
+  //    check, is the thread's previous record or the last one of the lane
+  //    below (lane 0 reads it).
   const bool patched = hi > lo;  // uniform
+  const uint64_t tb0 = ts / B, tb1 = (te + B - 1) / B;
+  const uint32_t nbt = (uint32_t)(tb1 - tb0);
+  const uint8_t* bm = st + kHeader + n * K;
+  const bool bm_mine = P > 0 && tid * 32 < nbt;
+  Words2 bmw{0, 0, 0};
+  uint32_t bm_tail = 0;
+  uint32_t bm_got = 0;
+  if (bm_mine) {
+    bmw = load_bits_w(bm, tb0 + tid * 32);
+    bm_got = bits_of(bmw, min(32u, nbt - tid * 32));
+  }
+  if (P > 0 && te == n && tid == 0 && (nb & 7u) != 0) bm_tail = gp(bm)[nbm - 1] >> (nb & 7u);
+  // Puts record p (index idx, exponent v) into LDS after checking it: strictly
+  // after its predecessor's index pidx, and inside the tile.
+  auto put = [&](uint32_t p, uint32_t idx, uint32_t v, uint32_t pidx) {
+    uint32_t e = 0;
+    if (p > 0 && pidx >= idx) e |= CIERA_ST_PATCH;
+    if (idx < ts || idx >= te) {
+      e |= CIERA_ST_PATCH;
+    } else {
+      const uint32_t o = (uint32_t)(idx - ts);
+      s_pv[o] = (uint8_t)v;
+      atomicOr(&s_pm[o >> 5], 1u << (o & 31u));
+      const uint32_t bb = (uint32_t)(idx / B - tb0);
+      atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
+    }
+    if (e) report(status_out, e);
+  };
   if (patched) {
-    const uint64_t b0 = ts / B;
-    for (uint32_t p = lo + tid; p < hi; p += kThreads) {
-      uint32_t idx, v, e = 0;
-      read_rec(st, recs, p, idx, v);
-      if (p > 0) {
-        uint32_t pidx, pv;
-        read_rec(st, recs, p - 1, pidx, pv);
-        if (pidx >= idx) e |= CIERA_ST_PATCH;
+    const uint64_t send = recs + 5 * P;  // end of the stream
+    for (uint32_t base = lo, c; base < hi; base += c * kDecThreads) {  // uniform loop
+      c = min<uint32_t>(kRecBatch, (hi - base + kDecThreads - 1) / kDecThreads);
+      if (c == 1) {  // one record per thread: the two words that hold it
+        const uint32_t p = base + tid;
+        uint32_t idx = 0, v = 0, pidx = 0, pv;
+        if (p < hi) read_rec(st, recs, p, idx, v);
+        if (lane == 0 && p < hi && p > 0) read_rec(st, recs, p - 1, pidx, pv);
+        const uint32_t up = __shfl_up(idx, 1);
+        if (lane != 0) pidx = up;
+        if (p < hi) put(p, idx, v, pidx);
+        continue;
       }
-      if (idx < ts || idx >= te) {
-        e |= CIERA_ST_PATCH;
-      } else {
-        const uint32_t o = (uint32_t)(idx - ts);
-        s_pv[o] = (uint8_t)v;
-        atomicOr(&s_pm[o >> 5], 1u << (o & 31u));
-        const uint32_t bb = (uint32_t)(idx / B - b0);
-        atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
+      const uint32_t q0 = base + c * tid;
+      const uint64_t o0 = recs + 5ull * q0, a0 = o0 & ~(uint64_t)3;
+      const uint64_t wend = min<uint64_t>(send, o0 + 5u * c);  // words starting before this end
+      const G1 uint32_t* wp = gp(reinterpret_cast<const uint32_t*>(st + a0));
+      uint32_t w[kRecWords];
+#pragma unroll
+      for (int j = 0; j < kRecWords; ++j) w[j] = 0;
+      Words2 pw{0, 0, 0};
+      if (q0 < hi) {
+        w[0] = wp[0];  // the first two words hold record q0
+        w[1] = wp[1];
+#pragma unroll
+        for (int j = 2; j < kRecWords; ++j)
+          if (a0 + 4u * j < wend) w[j] = wp[j];
+        if (lane == 0 && q0 > 0) pw = load_rec(st, recs, q0 - 1);
       }
-      if (e) report(status_out, e);
+      const uint32_t b0 = (uint32_t)(o0 - a0);
+      uint32_t idx[kRecBatch], v[kRecBatch];
+#pragma unroll
+      for (int k = 0; k < kRecBatch; ++k) {  // record k starts at byte b0 + 5k of w
+        const int jl = (5 * k) >> 2;
+        const uint32_t b = b0 + 5u * k;
+        const bool up1 = (int)(b >> 2) != jl;
+        const uint32_t x0 = up1 ? w[jl + 1] : w[jl], x1 = up1 ? w[jl + 2] : w[jl + 1];
+        const uint64_t z = ((uint64_t)x0 | ((uint64_t)x1 << 32)) >> (8u * (b & 3u));
+        idx[k] = (uint32_t)z;
+        v[k] = (uint32_t)(z >> 32) & 0xFFu;
+      }
+      uint32_t pidx, pv;
+      rec_fields(pw, pidx, pv);
+      uint32_t last = idx[0];
+#pragma unroll
+      for (int k = 1; k < kRecBatch; ++k) last = (uint32_t)k < c ? idx[k] : last;
+      const uint32_t up = __shfl_up(last, 1);
+      if (lane != 0) pidx = up;
+#pragma unroll
+      for (int k = 0; k < kRecBatch; ++k) {
+        const uint32_t p = q0 + (uint32_t)k;
+        if ((uint32_t)k < c && p < hi) put(p, idx[k], v[k], k == 0 ? pidx : idx[k > 0 ? k - 1 : 0]);
+      }
     }
   }
   if (P > 0) __syncthreads();
@@ -695,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
 #pragma unroll
     for (int k = 0; k < 4; ++k) ex[u][k] = cw[u][k];
     if (patched && cnt[u] > 0) {
-      const uint32_t o0 = (uint32_t)u * kSub + tid * kEPT;  // 16-aligned: one half-word of s_pm
+      const uint32_t o0 = (uint32_t)u * kDecRow + tid * kEPT;  // 16-aligned: one half-word of s_pm
       uint32_t pm = (s_pm[o0 >> 5] >> (o0 & 31u)) & 0xFFFFu;
       while (pm) {
         const int j = __ffs(pm) - 1;
@@ -708,13 +787,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
 
   // 5. bitmap check: the tile's bits mark exactly the blocks that hold patches
   if (P > 0) {
-    const uint64_t tb0 = ts / B, tb1 = (te + B - 1) / B;
-    const uint32_t nbt = (uint32_t)(tb1 - tb0);
-    const uint8_t* bm = st + kHeader + n * K;
     uint32_t e = 0;
-    if (tid * 32 < nbt && get_bits(bm, tb0 + tid * 32, min(32u, nbt - tid * 32)) != s_expbm[tid])
-      e |= CIERA_ST_BITMAP;
-    if (te == n && tid == 0 && (nb & 7u) != 0 && (gp(bm)[nbm - 1] >> (nb & 7u)) != 0) e |= CIERA_ST_BITMAP;
+    if (bm_mine && bm_got != s_expbm[tid]) e |= CIERA_ST_BITMAP;
+    if (bm_tail != 0) e |= CIERA_ST_BITMAP;
     if (e) report(status_out, e);
   }
 
@@ -722,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (cnt[u] > 0) {
-      const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
+      const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
       uint32_t v[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
@@ -734,7 +809,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecItem* __restr
                                       ex[u][2] != cw[u][2] || ex[u][3] != cw[u][3]);
     const uint64_t m = patched ? __ballot(dirty) : 0ull;
     if (cnt[u] > 0 && ((m >> (lane & ~7u)) & 0xFFu)) {
-      const uint64_t c0 = ts + (uint64_t)u * kSub + (uint64_t)tid * kEPT;
+      const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
       store_bytes16(cache + c0, cnt[u], aligned, ex[u]);
     }
   }
@@ -804,7 +879,7 @@ hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0,
                          uint32_t world, uint32_t* status, const uint32_t* ctl, uint32_t batch_id,
                          hipStream_t s) {
   (void)hipGetLastError();
-  const dim3 grid(nitems * tpr * world), block(kThreads);
+  const dim3 grid(nitems * tpr * world), block(kDecThreads);
 #define CIERA_DEC(DT, U) \
   hipLaunchKernelGGL((decode_kernel<DT, U>), grid, block, 0, s, items, item0, tpr, world, status, ctl, batch_id)
   if (dtype == 1) {

@@ -115,10 +115,10 @@ def test_specials_and_all_bf16_patterns():
     assert Case([(448, 256)], torch.bfloat16, 16).run(w0, w1)["status"] == 0
 
 
-def _corrupt_case():
+def _corrupt_case(frac=0.01):
     spec = [W.TensorSpec("k", 64, 3000)]
     a = W.base_weights(spec[0], 77, torch.bfloat16)
-    m = W.mask_uniform(spec[0].numel, 0.01, 78)
+    m = W.mask_uniform(spec[0].numel, frac, 78)
     return spec, [a], [W.perturb_exact(a, m, 79)]
 
 
@@ -166,6 +166,34 @@ def test_decode_status_classes_match_oracle():
             g &= ~O.ST_BITMAP
             o &= ~O.ST_BITMAP
         assert g == o, (name, g, o)
+
+
+@pytest.mark.parametrize("frac", [0.01, 0.15])
+def test_patch_record_order_errors_at_many_positions(frac):
+    """Swapped and repeated patch records at many positions of a stream (first
+    records of a lane, a wave, a pass of the record loop; the middle; the end)
+    give the oracle's status.  At 1% a tile holds under one record per decode
+    thread, at 15% several, so both record-loading paths are covered."""
+    spec, w0, w1 = _corrupt_case(frac)
+    rows, cols, world, B = 64, 3000, 4, 64
+    n = 16 * cols
+    ref = Case([(rows, cols)], torch.bfloat16, world, B)
+    ref.run(w0, w1, compress=[1])
+    s = ref.codec.slot(0, 1).cpu().numpy()
+    h = O.parse_header(s)
+    p = int(h["n_changed"])
+    assert h["mode"] == O.MODE_COMPRESSED
+    assert p > (2000 if frac > 0.1 else 300)
+    pb = 64 + n + O.bitmap_bytes(n, B)
+    rec = [bytes(s[pb + 5 * i:pb + 5 * i + 5]) for i in range(p)]
+    pos = sorted({i for i in (0, 1, 3, 4, 63, 64, 255, 256, 1023, 1024, 1100, p // 2, p - 2) if i + 1 < p})
+    for i in pos:
+        for kind, e in (("swap", [(0, 1, pb + 5 * i, rec[i + 1]), (0, 1, pb + 5 * i + 5, rec[i])]),
+                        ("repeat", [(0, 1, pb + 5 * i + 5, rec[i])])):
+            res = Case([(rows, cols)], torch.bfloat16, world, B).run(w0, w1, compress=[1], edits=e)
+            g, o = res["status"], res["ostatus"]
+            assert o & O.ST_PATCH, (kind, i)
+            assert g & ~O.ST_BITMAP == o & ~O.ST_BITMAP, (kind, i, g, o)
 
 
 def test_encode_is_deterministic():
