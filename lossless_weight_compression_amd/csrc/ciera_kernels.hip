@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ciera.h"
 #include "ciera_internal.h"
 
@@ -216,6 +218,54 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t nbytes, bo
   }
 }
 
+// Stores the first nbytes <= 4*NW bytes of the words w at p (vector stores
+// when complete and allowed).
+template <int NW>
+__device__ __forceinline__ void store_words(uint8_t* p, uint32_t nbytes, bool vec, const uint32_t w[NW]) {
+  if (vec && nbytes == NW * 4) {
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+      v4u a;
+      a.x = w[4 * q]; a.y = w[4 * q + 1]; a.z = w[4 * q + 2]; a.w = w[4 * q + 3];
+      stg16(p + 16 * q, a);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NW * 4; ++b)
+      if ((uint32_t)b < nbytes) gp(p)[b] = (uint8_t)(w[b >> 2] >> (8 * (b & 3)));
+  }
+}
+
+// bf16, four values at a time.  A pair of words w0 = (v1 << 16) | v0 and
+// w1 = (v3 << 16) | v2 gives the four exponent bytes (bits 7..14 of each value
+// are byte 1 of the value shifted left once) and the four sign|mantissa bytes
+// (sign from each value's high byte, mantissa from its low byte) with byte
+// permutes; the merge goes the other way.
+__device__ __forceinline__ uint32_t bf16x4_exp(uint32_t w0, uint32_t w1) {
+  return __builtin_amdgcn_perm(w1 << 1, w0 << 1, 0x07050301u);
+}
+__device__ __forceinline__ uint32_t bf16x4_sm(uint32_t w0, uint32_t w1) {
+  const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x06040200u);
+  const uint32_t hi = __builtin_amdgcn_perm(w1, w0, 0x07050301u);
+  return (hi & 0x80808080u) | (lo & 0x7F7F7F7Fu);
+}
+__device__ __forceinline__ void bf16x4_join(uint32_t sm, uint32_t ex, uint32_t& w0, uint32_t& w1) {
+  const uint32_t lo = (sm & 0x7F7F7F7Fu) | ((ex << 7) & 0x80808080u);  // low bytes of the values
+  const uint32_t hi = (sm & 0x80808080u) | ((ex >> 1) & 0x7F7F7F7Fu);  // high bytes
+  w0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  w1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+// Bit j set iff byte j of the 4 words is nonzero (16 bits).
+__device__ __forceinline__ uint32_t nonzero_bytes16(const uint32_t d[4]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t t = (((d[q] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | d[q]) & 0x80808080u;  // bit 7 of each nonzero byte
+    m |= ((t >> 7) | (t >> 14) | (t >> 21) | (t >> 28)) << (4 * q) & (0xFu << (4 * q));
+  }
+  return m;
+}
+
 // sign|mantissa of value j from the raw words of a 16-value chunk.
 template <int DT>
 __device__ __forceinline__ uint32_t sm_from_words(const uint32_t* w, int j) {
@@ -363,44 +413,67 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   const bool compress = d.compress != 0;
   const bool caligned = d.cache_aligned != 0;
 
-  // all loads of the tile first
-  uint32_t xw[S][XW], cw[S][4];
-  int cnt[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-    cnt[s] = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
-    if (cnt[s] > 0) {
-      load_words<XW>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
-      load_words<4>(d.cache + c0, (uint32_t)cnt[s], caligned, cw[s]);
-    }
-  }
+  // Loads, split and compare, sign|mantissa (or RAW) stores, bitmap bits in
+  // LDS.  A tile wholly inside its item with an aligned cache takes a
+  // straight-line copy of this code (FULL: every chunk has 16 values).
   uint32_t mask[S];
   uint32_t expk[S][4];
+  auto split_tile = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    uint32_t xw[S][XW], cw[S][4];
+    int cnt[S];
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-    mask[s] = 0;
-    expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
-    if (cnt[s] > 0) {
-      uint32_t v[16], sm[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if constexpr (DT == 1) v[j] = (xw[s][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        else v[j] = xw[s][j];
-        const uint32_t e = exp_of<DT>(v[j]);
-        expk[s][j >> 2] |= e << (8 * (j & 3));
-        if (j < cnt[s] && e != byte_of(cw[s], j)) mask[s] |= 1u << j;
-        sm[j] = sm_of<DT>(v[j]);
-      }
-      if (compress) store_sm16<DT>(d.stream + kHeader + c0 * K, cnt[s], sm);
-      else store16<DT>(d.stream + kHeader + c0 * E, cnt[s], v);
-      if (mask[s]) {
-        const uint32_t rel = (uint32_t)(((uint64_t)s * kSub + (uint64_t)tid * kEPT) / B);
-        atomicOr(&s_bm[rel >> 5], 1u << (rel & 31u));
+    for (int s = 0; s < S; ++s) {  // all loads of the tile first
+      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+      cnt[s] = FULL ? 16 : (c0 < n ? (int)min<uint64_t>(16, n - c0) : 0);
+      if (cnt[s] > 0) {
+        load_words<XW>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
+        load_words<4>(d.cache + c0, (uint32_t)cnt[s], FULL || caligned, cw[s]);
       }
     }
-  }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+      mask[s] = 0;
+      expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
+      if (cnt[s] > 0) {
+        if constexpr (DT == 1) {
+          uint32_t smw[4], dif[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            expk[s][q] = bf16x4_exp(xw[s][2 * q], xw[s][2 * q + 1]);
+            smw[q] = bf16x4_sm(xw[s][2 * q], xw[s][2 * q + 1]);
+            dif[q] = expk[s][q] ^ cw[s][q];
+            if (!FULL) {  // only the cnt values present
+              const int nv = cnt[s] - 4 * q;
+              dif[q] &= nv >= 4 ? 0xFFFFFFFFu : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
+            }
+          }
+          if (dif[0] | dif[1] | dif[2] | dif[3]) mask[s] = nonzero_bytes16(dif);
+          if (compress) store_words<4>(d.stream + kHeader + c0, (uint32_t)cnt[s], true, smw);
+          else store_words<XW>(d.stream + kHeader + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
+        } else {
+          uint32_t v[16], sm[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            v[j] = xw[s][j];
+            const uint32_t e = exp_of<DT>(v[j]);
+            expk[s][j >> 2] |= e << (8 * (j & 3));
+            if (j < cnt[s] && e != byte_of(cw[s], j)) mask[s] |= 1u << j;
+            sm[j] = sm_of<DT>(v[j]);
+          }
+          if (compress) store_sm16<DT>(d.stream + kHeader + c0 * K, cnt[s], sm);
+          else store16<DT>(d.stream + kHeader + c0 * E, cnt[s], v);
+        }
+        if (mask[s]) {
+          const uint32_t rel = (uint32_t)(((uint64_t)s * kSub + (uint64_t)tid * kEPT) / B);
+          atomicOr(&s_bm[rel >> 5], 1u << (rel & 31u));
+        }
+      }
+    }
+  };
+  if (caligned && base + T <= n) split_tile(std::true_type{});  // uniform
+  else split_tile(std::false_type{});
 
   // block-wide exclusive scan of the per-thread change counts, chunk-row major
   uint32_t lpre[S];
@@ -798,10 +871,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   for (int u = 0; u < U; ++u) {
     if (cnt[u] > 0) {
       const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
-      uint32_t v[16];
+      if constexpr (DT == 1) {
+        uint32_t o[8];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
-      store16<DT>(out + c0 * E, cnt[u], v, aligned);
+        for (int q = 0; q < 4; ++q) bf16x4_join(sw[u][q], ex[u][q], o[2 * q], o[2 * q + 1]);
+        store_words<8>(out + c0 * E, (uint32_t)cnt[u] * E, aligned, o);
+      } else {
+        uint32_t v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
+        store16<DT>(out + c0 * E, cnt[u], v, aligned);
+      }
     }
     // cache write-back in whole 128-byte lines (8 lanes): scattered partial
     // lines cost more HBM time than the extra bytes of full lines
