@@ -463,7 +463,8 @@ ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t c
     d.slot = it.slot_bytes;
     d.out = static_cast<uint8_t*>(it.out_full);
     d.cache = it.cache_full;
-    d.rows = it.t.rows;
+    d.q = it.t.rows / it.t.world;
+    d.rem = (uint32_t)(it.t.rows % it.t.world);
     d.cols = it.t.cols;
     d.world = it.t.world;
     d.block_size = it.t.block_size;

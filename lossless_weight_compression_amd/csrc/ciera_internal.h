@@ -43,11 +43,12 @@ struct DecItem {
   uint64_t slot;
   uint8_t* out;
   uint8_t* cache;
-  uint64_t rows, cols;
+  uint64_t q;              // rows / world: rows of every rank ...
+  uint64_t cols;
   uint32_t world;
   uint32_t block_size;
   uint32_t batch_id;       // the batch that wrote this descriptor
-  uint32_t pad;
+  uint32_t rem;            // ... plus one for ranks below rows % world
 };
 
 // Encode scratch layout (offsets in bytes from the scratch base):

@@ -410,6 +410,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   const uint64_t base = (uint64_t)local * T;
   const uint64_t n = d.n;
   const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;  // B is a power of two (checked by the API)
   const bool compress = d.compress != 0;
   const bool caligned = d.cache_aligned != 0;
 
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
           else store16<DT>(d.stream + kHeader + c0 * E, cnt[s], v);
         }
         if (mask[s]) {
-          const uint32_t rel = (uint32_t)(((uint64_t)s * kSub + (uint64_t)tid * kEPT) / B);
+          const uint32_t rel = ((uint32_t)s * kSub + tid * kEPT) >> lb;
           atomicOr(&s_bm[rel >> 5], 1u << (rel & 31u));
         }
       }
@@ -518,15 +519,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   __syncthreads();
   const uint32_t excl = s_excl;
 
-  const uint64_t nb = (n + B - 1) / B;
+  const uint64_t nb = (n + B - 1) >> lb;
   const uint64_t nbm = (nb + 7) / 8;
   if (compress) {
     // bitmap bytes of this tile's blocks (a tile spans whole bitmap bytes)
     const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
-    const uint32_t tblocks = (uint32_t)((in_tile + B - 1) / B);
+    const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
     const uint32_t tbytes = (tblocks + 7) / 8;
     if (tid < tbytes)
-      gp(d.stream)[kHeader + n * K + base / ((uint64_t)B * 8) + tid] = (uint8_t)(s_bm[tid >> 2] >> (8 * (tid & 3)));
+      gp(d.stream)[kHeader + n * K + (base >> (lb + 3)) + tid] = (uint8_t)(s_bm[tid >> 2] >> (8 * (tid & 3)));
     // (index, exponent) records
     const uint64_t pbase = kHeader + n * K + nbm;
 #pragma unroll
@@ -615,8 +616,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   constexpr int SW = 4 * K;                     // words of 16 sign|mantissa records
   __shared__ uint32_t s_hdr[16];
   __shared__ uint32_t s_expbm[BMW];  // blocks of the tile that hold a patch
-  __shared__ uint32_t s_pm[T / 32];  // positions of the tile that hold a patch
-  __shared__ uint8_t s_pv[T];        // patch exponents (valid where s_pm is set)
+  __shared__ uint32_t s_ex[T / 4];   // the tile's exponents: cached, then patched in place
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t tpi = tpr * world;
@@ -627,7 +627,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   const uint32_t t_in = rel - r * tpr;
   const DecItem d = items[item];
   if (d.batch_id != batch_id) return;  // the scratch holds another batch (uniform)
-  const uint64_t q = d.rows / world, rem = d.rows % world;
+  const uint64_t q = d.q, rem = d.rem;  // rows per rank, ranks with one more
   const uint64_t off = ((uint64_t)r * q + min<uint64_t>(r, rem)) * d.cols;
   const uint64_t n = (q + (r < rem ? 1u : 0u)) * d.cols;
   const uint64_t ts = (uint64_t)t_in * T;
@@ -635,6 +635,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   const uint64_t te = min<uint64_t>(n, ts + T);
   const uint8_t* st = d.streams + (uint64_t)r * d.slot;
   const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;  // B is a power of two (checked by the API)
   const bool aligned = (off & 15u) == 0;
   uint8_t* const cache = d.cache + off;
 
@@ -650,7 +651,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
       load_words<4>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
     }
   }
-  const uint64_t nb = (n + B - 1) / B;
+  const uint64_t nb = (n + B - 1) >> lb;
   const uint64_t nbm = (nb + 7) / 8;
 
   // 2. header
@@ -659,7 +660,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     s_hdr[4 * tid] = h.x; s_hdr[4 * tid + 1] = h.y; s_hdr[4 * tid + 2] = h.z; s_hdr[4 * tid + 3] = h.w;
   }
   if (tid < BMW) s_expbm[tid] = 0;
-  for (uint32_t w = tid; w < T / 32; w += kDecThreads) s_pm[w] = 0;
+  // the cached exponents go to LDS now: the header read above already waits
+  // for the bulk loads (loads complete in order), and patches overwrite them
+  // after the next barrier
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (cnt[u] > 0) {
+      v4u e;
+      e.x = cw[u][0]; e.y = cw[u][1]; e.z = cw[u][2]; e.w = cw[u][3];
+      *reinterpret_cast<v4u*>(&s_ex[((uint32_t)u * kDecRow + tid * kEPT) / 4]) = e;
+    }
+  }
   __syncthreads();
   const uint32_t h_dtype = (s_hdr[1] >> 16) & 0xFFu, h_mode = s_hdr[1] >> 24;
   const uint64_t h_n = s_hdr[4] | ((uint64_t)s_hdr[5] << 32);
@@ -748,7 +759,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     }
   }
 
-  // 4. patches of the tile into LDS: exponent values plus a presence bitmap.
+  // 4. patches of the tile into LDS, over the cached exponents.
   //    Each pass gives every thread c <= kRecBatch consecutive records (c as
   //    small as the pass allows, so the records spread over all waves), read
   //    as one round of aligned words; the first pass shares its round with
@@ -756,7 +767,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   //    check, is the thread's previous record or the last one of the lane
   //    below (lane 0 reads it).
   const bool patched = hi > lo;  // uniform
-  const uint64_t tb0 = ts / B, tb1 = (te + B - 1) / B;
+  const uint64_t tb0 = ts >> lb, tb1 = (te + B - 1) >> lb;
   const uint32_t nbt = (uint32_t)(tb1 - tb0);
   const uint8_t* bm = st + kHeader + n * K;
   const bool bm_mine = P > 0 && tid * 32 < nbt;
@@ -769,18 +780,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   }
   if (P > 0 && te == n && tid == 0 && (nb & 7u) != 0) bm_tail = gp(bm)[nbm - 1] >> (nb & 7u);
   // Puts record p (index idx, exponent v) into LDS after checking it: strictly
-  // after its predecessor's index pidx, and inside the tile.
+  // after its predecessor's index pidx, and inside the tile.  The first record
+  // of each block marks the block (records ascend; when they do not, the
+  // order error is reported and the bitmap verdict is unspecified).
+  uint8_t* const s_exb = reinterpret_cast<uint8_t*>(s_ex);
   auto put = [&](uint32_t p, uint32_t idx, uint32_t v, uint32_t pidx) {
     uint32_t e = 0;
     if (p > 0 && pidx >= idx) e |= CIERA_ST_PATCH;
     if (idx < ts || idx >= te) {
       e |= CIERA_ST_PATCH;
     } else {
-      const uint32_t o = (uint32_t)(idx - ts);
-      s_pv[o] = (uint8_t)v;
-      atomicOr(&s_pm[o >> 5], 1u << (o & 31u));
-      const uint32_t bb = (uint32_t)(idx / B - tb0);
-      atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
+      s_exb[idx - ts] = (uint8_t)v;
+      if (p == lo || (pidx >> lb) != (idx >> lb)) {
+        const uint32_t bb = (uint32_t)((idx >> lb) - tb0);
+        atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
+      }
     }
     if (e) report(status_out, e);
   };
@@ -847,14 +861,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
 #pragma unroll
     for (int k = 0; k < 4; ++k) ex[u][k] = cw[u][k];
     if (patched && cnt[u] > 0) {
-      const uint32_t o0 = (uint32_t)u * kDecRow + tid * kEPT;  // 16-aligned: one half-word of s_pm
-      uint32_t pm = (s_pm[o0 >> 5] >> (o0 & 31u)) & 0xFFFFu;
-      while (pm) {
-        const int j = __ffs(pm) - 1;
-        pm &= pm - 1;
-        const uint32_t sh = 8u * (j & 3);
-        ex[u][j >> 2] = (ex[u][j >> 2] & ~(0xFFu << sh)) | ((uint32_t)s_pv[o0 + j] << sh);
-      }
+      const v4u e = *reinterpret_cast<const v4u*>(&s_ex[((uint32_t)u * kDecRow + tid * kEPT) / 4]);
+      ex[u][0] = e.x; ex[u][1] = e.y; ex[u][2] = e.z; ex[u][3] = e.w;
     }
   }
 
