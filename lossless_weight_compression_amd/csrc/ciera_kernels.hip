@@ -34,6 +34,10 @@ __device__ __forceinline__ const G1 T* gp(const T* p) { return (const G1 T*)p; }
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // one 16-byte global access
 __device__ __forceinline__ v4u ldg16(const void* p) { return *gp(reinterpret_cast<const v4u*>(p)); }
 __device__ __forceinline__ void stg16(void* p, v4u v) { *gp(reinterpret_cast<v4u*>(p)) = v; }
+// Non-temporal 16-byte store: for data no later access of this launch reads.
+__device__ __forceinline__ void stg16_nt(void* p, v4u v) {
+  __builtin_nontemporal_store(v, gp(reinterpret_cast<v4u*>(p)));
+}
 
 template <int DT>
 struct Tr;
@@ -218,16 +222,17 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t nbytes, bo
   }
 }
 
-// Stores the first nbytes <= 4*NW bytes of the words w at p (vector stores
-// when complete and allowed).
-template <int NW>
+// Stores the first nbytes <= 4*NW bytes of the words w at p (vector stores,
+// non-temporal if NT, when complete and allowed).
+template <int NW, bool NT = false>
 __device__ __forceinline__ void store_words(uint8_t* p, uint32_t nbytes, bool vec, const uint32_t w[NW]) {
   if (vec && nbytes == NW * 4) {
 #pragma unroll
     for (int q = 0; q < NW / 4; ++q) {
       v4u a;
       a.x = w[4 * q]; a.y = w[4 * q + 1]; a.z = w[4 * q + 2]; a.w = w[4 * q + 3];
-      stg16(p + 16 * q, a);
+      if (NT) stg16_nt(p + 16 * q, a);
+      else stg16(p + 16 * q, a);
     }
   } else {
 #pragma unroll
@@ -892,13 +897,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
       }
     }
     // cache write-back in whole 128-byte lines (8 lanes): scattered partial
-    // lines cost more HBM time than the extra bytes of full lines
+    // lines cost more HBM time than the extra bytes of full lines; the
+    // stores are non-temporal (nothing in this launch reads them again)
     const bool dirty = cnt[u] > 0 && (ex[u][0] != cw[u][0] || ex[u][1] != cw[u][1] ||
                                       ex[u][2] != cw[u][2] || ex[u][3] != cw[u][3]);
     const uint64_t m = patched ? __ballot(dirty) : 0ull;
     if (cnt[u] > 0 && ((m >> (lane & ~7u)) & 0xFFu)) {
       const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
-      store_bytes16(cache + c0, cnt[u], aligned, ex[u]);
+      store_words<4, true>(cache + c0, (uint32_t)cnt[u], aligned, ex[u]);
     }
   }
 }
