@@ -141,6 +141,7 @@ struct BatchImpl {
   uint32_t count, ngroups;
   uint32_t batch_id, tag_base;
   uint32_t launches, any_compress;
+  uint32_t fix_wg, reserved;  // fallback rewrite: workgroups per item
   uint64_t off_flags, off_ctr, off_items;
   Group g[kMaxGroups];
 };
@@ -340,6 +341,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
   reinterpret_cast<uint32_t*>(blob.data())[0] = b->batch_id;
   EncItem* di = reinterpret_cast<EncItem*>(blob.data() + pl.off_items);
   uint32_t any = 0;
+  uint64_t max_bytes = 0;  // largest shard that may need the RAW rewrite
   for (uint32_t j = 0; j < count; ++j) {
     const ciera_encode_item_t& it = items[pl.order[j]];
     uint64_t off, n;
@@ -359,6 +361,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     d.elem_bytes = elem_bytes(it.t.dtype);
     d.batch_id = b->batch_id;
     any |= d.compress;
+    if (d.compress) max_bytes = std::max<uint64_t>(max_bytes, n * d.elem_bytes);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (hipError_t e = upload(scratch, blob.data(), blob.size(), st)) return device_error("descriptor upload", e);
@@ -368,6 +371,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
   b->count = count;
   b->ngroups = (uint32_t)pl.groups.size();
   b->any_compress = any;
+  b->fix_wg = (uint32_t)std::min<uint64_t>(64, std::max<uint64_t>(1, (max_bytes + 65535) / 65536));
   b->off_flags = pl.off_flags;
   b->off_ctr = pl.off_ctr;
   b->off_items = pl.off_items;
@@ -403,7 +407,7 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
     }
   }
   if (b->any_compress) {
-    if (hipError_t e = launch_encode_fixup(items, b->count, flags, ctl + 1, tag, b->batch_id, st)) {
+    if (hipError_t e = launch_encode_fixup(items, b->count, b->fix_wg, flags, ctl + 1, tag, b->batch_id, st)) {
       b->magic = 0;
       return device_error("encode fallback launch", e);
     }

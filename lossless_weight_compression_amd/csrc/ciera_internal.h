@@ -74,7 +74,7 @@ struct EncArgs {
 // descriptor they read belongs to another batch (the scratch was taken over).
 hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
                          uint32_t batch_id, hipStream_t s);
-hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, const uint32_t* raw_flag,
+hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, uint32_t wg_per_item, const uint32_t* raw_flag,
                                const uint32_t* any_raw, uint32_t tag, uint32_t batch_id, hipStream_t s);
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
                          uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,

@@ -587,14 +587,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   }
 }
 
-// Rewrites as RAW the streams whose COMPRESSED form turned out not shorter.
+// Rewrites as RAW the streams whose COMPRESSED form turned out not shorter:
+// gridDim.x workgroups per item, items along y.  Returns at once when the
+// launch flagged no item (the common case).
 __global__ __launch_bounds__(kThreads) void encode_fixup_kernel(const EncItem* __restrict__ items, uint32_t count,
                                                                 const uint32_t* raw_flag, const uint32_t* any_raw,
                                                                 uint32_t tag, uint32_t batch_id) {
   if (*gp(any_raw) != tag) return;
   const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
-  for (uint32_t k = 0; k < count; ++k) {
+  for (uint32_t k = blockIdx.y; k < count; k += gridDim.y) {
     if (gp(raw_flag)[k] != tag) continue;
     const EncItem d = items[k];
     if (d.batch_id != batch_id) return;
@@ -961,10 +963,11 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
   return hipGetLastError();
 }
 
-hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, const uint32_t* raw_flag,
+hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, uint32_t wg_per_item, const uint32_t* raw_flag,
                                const uint32_t* any_raw, uint32_t tag, uint32_t batch_id, hipStream_t s) {
   (void)hipGetLastError();
-  const dim3 grid(64), block(kThreads);
+  if (count == 0 || wg_per_item == 0) return hipSuccess;
+  const dim3 grid(wg_per_item, count < 65535u ? count : 65535u), block(kThreads);
   hipLaunchKernelGGL(encode_fixup_kernel, grid, block, 0, s, items, count, raw_flag, any_raw, tag, batch_id);
   return hipGetLastError();
 }
