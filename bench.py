@@ -17,6 +17,11 @@ state B encodes W0 against the cache of W1 (decode leaves it at W0).
 
 Prints one JSON line (see the keys below).  --gpus above 1 is refused: this
 build runs on one GPU.
+
+--overlap measures instead how much of one step hides behind a concurrent bf16
+GEMM (the compute a rank runs while the next layer's weights are encoded,
+gathered and decoded): the GEMM on one HIP stream, the step on a second one,
+each alone and then both at once, and prints one JSON line of its own.
 """
 from __future__ import annotations
 
@@ -49,6 +54,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy five times (the reference "
                          "kernel for scaling HBM byte counters)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="measure the step alone, a bf16 GEMM alone and both on two streams")
+    ap.add_argument("--gemm", type=int, nargs=3, default=[8192, 8192, 8192], metavar=("M", "N", "K"),
+                    help="GEMM shape of --overlap")
     return ap.parse_args()
 
 
@@ -71,6 +80,96 @@ def main():
         log("bench.py runs on one GPU only: the collective is outside this build; "
             "run with --gpus 1")
         sys.exit(2)
+    if args.overlap:
+        return overlap(args)
+    import torch
+    wl = setup(args)
+    specs, A, Bc, w0, w1, N, n_enc = wl["specs"], wl["A"], wl["Bc"], wl["w0"], wl["w1"], wl["N"], wl["n_enc"]
+    step, stream = wl["step"], torch.cuda.current_stream()
+    dec_bytes, enc_bytes = wl["dec_bytes"], wl["enc_bytes"]
+
+    A.status.zero_()
+    Bc.status.zero_()
+    for k in range(args.warmup):
+        step(k, stream)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, stream, evs[k])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    enc_avg = sum(enc_ms) / len(enc_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    ms_step = t_total * 1e3 / args.steps
+    wl["check"](args.warmup + args.steps - 1)
+    log(f"steps {args.steps}: {ms_step:.4f} ms/step; encode avg {enc_avg * 1e3:.1f} us "
+        f"(p10 {enc_ms[len(enc_ms) // 10] * 1e3:.1f}, p90 {enc_ms[9 * len(enc_ms) // 10] * 1e3:.1f}); "
+        f"decode avg {dec_avg * 1e3:.1f} us (p10 {dec_ms[len(dec_ms) // 10] * 1e3:.1f}, "
+        f"p90 {dec_ms[9 * len(dec_ms) // 10] * 1e3:.1f})")
+
+    logical = 2 * n_enc + 2 * N
+    value = logical / (ms_step * 1e-3) / 1e9
+    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
+    enc_gbps = enc_bytes / (enc_avg * 1e-3) / 1e9
+
+    # HBM traffic of the decode kernel from the committed PMC summary, if it was
+    # taken on the current kernel source
+    traffic = None
+    src = os.path.join(ROOT, "lossless_weight_compression_amd", "csrc", "ciera_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    tf = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if os.path.exists(tf):
+        t = json.load(open(tf))
+        if t.get("kernel_source_sha256") == sha and t.get("workload") == "olmoe_layer_bf16_1pct_uniform" \
+                and not args.clustered and wl["ppm"] == 10000:
+            traffic = t.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(specs, w0, w1, wl["world"], wl["block"], A, args.cpu_seconds)
+
+    out = {
+        "metric": "encode/decode GB/s (bf16 OLMoE MoE layer, 1% exp change) and % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": "olmoe_moe_layer_bf16_" + ("clustered" if args.clustered else "uniform"),
+                   "experts": 64, "tensors": len(specs), "elements": N, "world": wl["world"],
+                   "block_size": wl["block"], "change_frac": args.frac,
+                   "step": "plan(192) + encode(rank 0 shard) + decode(full layer, 16 streams)"},
+        "encode": {"avg_us": round(enc_avg * 1e3, 2), "elements": n_enc,
+                   "logical_GBps": round(2 * n_enc / (enc_avg * 1e-3) / 1e9, 1),
+                   "algorithmic_bytes": enc_bytes, "achieved_GBps": round(enc_gbps, 1),
+                   "hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4)},
+        "decode": {"avg_us": round(dec_avg * 1e3, 2), "elements": N,
+                   "logical_GBps": round(2 * N / (dec_avg * 1e-3) / 1e9, 1),
+                   "algorithmic_bytes": dec_bytes, "achieved_GBps": round(dec_gbps, 1),
+                   "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4)},
+        "compression_ratio": round(wl["raw_bytes"] / wl["stream_bytes"], 4),
+        "changed_exponents": wl["P_total"],
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<bf16,2>",
+                     "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def setup(args):
+    """Inputs, codecs, the other ranks' streams and the step closure of the
+    bench workload, with the round trip checked bit-exact."""
     import torch
 
     from gen import workloads as W
@@ -149,9 +248,8 @@ def main():
     plans_expected = [p.compress for p in A.plans]
     encA = A.prepare_encode(0, shards(w1, 0))
     encB = Bc.prepare_encode(0, shards(w0, 0))
-    stream = torch.cuda.current_stream()
 
-    def step(k, ev=None):
+    def step(k, stream, ev=None):
         codec, enc = (A, encA) if k % 2 == 0 else (Bc, encB)
         # plan: the per-tensor selector (host), consumed by the prepared batch
         for i, t in enumerate(codec.tensors):
@@ -166,85 +264,78 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    A.status.zero_()
-    Bc.status.zero_()
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k, evs[k])
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
-    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    enc_avg = sum(enc_ms) / len(enc_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    ms_step = t_total * 1e3 / args.steps
-    assert A.status.item() == 0 and Bc.status.item() == 0, "decode reported corrupt streams"
-    last = A if (args.warmup + args.steps - 1) % 2 == 0 else Bc
-    want = w1 if last is A else w0
-    for i in range(0, len(specs), 17):
-        assert torch.equal(last.out_view(i).view(torch.int16), want[i].reshape(-1).view(torch.int16)), i
-    log(f"steps {args.steps}: {ms_step:.4f} ms/step; encode avg {enc_avg * 1e3:.1f} us "
-        f"(p10 {enc_ms[len(enc_ms) // 10] * 1e3:.1f}, p90 {enc_ms[9 * len(enc_ms) // 10] * 1e3:.1f}); "
-        f"decode avg {dec_avg * 1e3:.1f} us (p10 {dec_ms[len(dec_ms) // 10] * 1e3:.1f}, "
-        f"p90 {dec_ms[9 * len(dec_ms) // 10] * 1e3:.1f})")
+    def check(last_k):
+        """Decode status clean and the last step's output equal to its input."""
+        assert A.status.item() == 0 and Bc.status.item() == 0, "decode reported corrupt streams"
+        last = A if last_k % 2 == 0 else Bc
+        want = w1 if last is A else w0
+        for i in range(0, len(specs), 17):
+            assert torch.equal(last.out_view(i).view(torch.int16), want[i].reshape(-1).view(torch.int16)), i
 
-    logical = 2 * n_enc + 2 * N
-    value = logical / (ms_step * 1e-3) / 1e9
-    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
-    enc_gbps = enc_bytes / (enc_avg * 1e-3) / 1e9
+    return dict(specs=specs, A=A, Bc=Bc, w0=w0, w1=w1, N=N, n_enc=n_enc, world=world, block=block,
+                ppm=ppm, step=step, check=check, dec_bytes=dec_bytes, enc_bytes=enc_bytes,
+                raw_bytes=raw_bytes, stream_bytes=stream_bytes, P_total=P_total)
 
-    # HBM traffic of the decode kernel from the committed PMC summary, if it was
-    # taken on the current kernel source
-    traffic = None
-    src = os.path.join(ROOT, "lossless_weight_compression_amd", "csrc", "ciera_kernels.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    tf = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    if os.path.exists(tf):
-        t = json.load(open(tf))
-        if t.get("kernel_source_sha256") == sha and t.get("workload") == "olmoe_layer_bf16_1pct_uniform" \
-                and not args.clustered and ppm == 10000:
-            traffic = t.get("hbm_bytes_per_launch")
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(specs, w0, w1, world, block, A, args.cpu_seconds)
+def overlap(args):
+    """The step (plan + encode + decode) on one stream alongside a bf16 GEMM on
+    another: each alone, then both at once.  hidden = (gemm + step - both) /
+    step is the share of the step that the GEMM covers."""
+    import torch
+    wl = setup(args)
+    M, Nn, K = args.gemm
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=gen)
+    b = torch.randn(K, Nn, device="cuda", dtype=torch.bfloat16, generator=gen)
+    c = torch.empty(M, Nn, device="cuda", dtype=torch.bfloat16)
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()  # default priority
+    step = wl["step"]
+    wl["A"].status.zero_()
+    wl["Bc"].status.zero_()
+    k = 0
 
+    def run(gemm, codec):
+        nonlocal k
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s1)
+        s2.wait_event(e0)
+        if gemm:
+            with torch.cuda.stream(s1):
+                torch.mm(a, b, out=c)
+        if codec:
+            step(k, s2)
+            k += 1
+        done = torch.cuda.Event()
+        done.record(s2)
+        s1.wait_event(done)
+        e1.record(s1)
+        return e0, e1
+
+    res = {}
+    for name, g, cd in (("gemm", True, False), ("step", False, True), ("both", True, True)):
+        for _ in range(args.warmup):
+            run(g, cd)
+        torch.cuda.synchronize()
+        evs = [run(g, cd) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        ts = sorted(x.elapsed_time(y) * 1e3 for x, y in evs)
+        res[name] = {"avg_us": round(sum(ts) / len(ts), 2), "p10_us": round(ts[len(ts) // 10], 2),
+                     "p90_us": round(ts[9 * len(ts) // 10], 2)}
+    wl["check"](k - 1)
+    tg, ts_, tb = res["gemm"]["avg_us"], res["step"]["avg_us"], res["both"]["avg_us"]
+    hidden = (tg + ts_ - tb) / ts_
+    flops = 2.0 * M * Nn * K
     out = {
-        "metric": "encode/decode GB/s (bf16 OLMoE MoE layer, 1% exp change) and % of HBM peak",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "u16",
-        "data": "synthetic",
+        "metric": "share of the codec step hidden behind a concurrent bf16 GEMM",
+        "value": round(hidden, 4), "unit": "fraction", "higher_is_better": True, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": "u16+bf16", "data": "synthetic",
         "config": {"workload": "olmoe_moe_layer_bf16_" + ("clustered" if args.clustered else "uniform"),
-                   "experts": 64, "tensors": len(specs), "elements": N, "world": world,
-                   "block_size": block, "change_frac": args.frac,
-                   "step": "plan(192) + encode(rank 0 shard) + decode(full layer, 16 streams)"},
-        "encode": {"avg_us": round(enc_avg * 1e3, 2), "elements": n_enc,
-                   "logical_GBps": round(2 * n_enc / (enc_avg * 1e-3) / 1e9, 1),
-                   "algorithmic_bytes": enc_bytes, "achieved_GBps": round(enc_gbps, 1),
-                   "hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4)},
-        "decode": {"avg_us": round(dec_avg * 1e3, 2), "elements": N,
-                   "logical_GBps": round(2 * N / (dec_avg * 1e-3) / 1e9, 1),
-                   "algorithmic_bytes": dec_bytes, "achieved_GBps": round(dec_gbps, 1),
-                   "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4)},
-        "compression_ratio": round(raw_bytes / stream_bytes, 4),
-        "changed_exponents": P_total,
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel<bf16,2>",
-                     "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
-        "cpu_baseline": cpu,
+                   "change_frac": args.frac, "gemm_mnk": [M, Nn, K],
+                   "streams": "GEMM on one stream, step on a second stream (default priorities)"},
+        "gemm": dict(res["gemm"], tflops=round(flops / (tg * 1e-6) / 1e12, 1)),
+        "step": res["step"], "both": res["both"],
+        "slowdown_vs_longer": round(tb / max(tg, ts_), 4),
     }
     print(json.dumps(out), flush=True)
 
