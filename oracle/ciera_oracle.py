@@ -35,7 +35,12 @@ in the design notes of the repository):
       block b holds at least one changed exponent; the bitmap is omitted when
       nothing changed.
   R4  sign|mantissa bytes: bf16 -> one byte (sign in bit 7, mantissa in bits
-      6..0); fp32 -> three little-endian bytes of (sign << 23 | mantissa).
+      6..0); fp32 -> three little-endian bytes of (sign << 23 | mantissa);
+      fp16 (IEEE binary16: 1 sign, 5 exponent, 10 mantissa bits) -> the 11-bit
+      value (sign << 10 | mantissa) of every element, packed back to back into
+      one bit stream, least significant bit first: value i occupies bits
+      [11i, 11i + 11), so 8 values fill 11 bytes and the section is
+      ceil(11n/8) bytes.  The cache holds the 5-bit fp16 exponent in a byte.
   R5  a 64-byte little-endian header (layout in ``HEADER_FIELDS``).
   R6  the gain subtracts all codec costs; the link term is linear in bytes.
   R7  the plan's change rate is the element change fraction (ppm).
@@ -63,6 +68,7 @@ MAGIC = b"CIER"
 VERSION = 1
 BF16 = 1
 FP32 = 2
+FP16 = 3
 MODE_RAW = 0
 MODE_COMPRESSED = 1
 PATCH_BYTES = 5                    # u32 index + u8 exponent
@@ -84,60 +90,83 @@ HEADER_FIELDS = [
 
 
 def elem_bytes(dtype: int) -> int:
-    """e: bytes per value (16-bit bf16 and 32-bit fp32) [CIERA 3.2: S = N*b/8]."""
-    return {BF16: 2, FP32: 4}[dtype]
+    """e: bytes per value (16-bit bf16 and fp16, 32-bit fp32) [CIERA 3.2: S = N*b/8]."""
+    return {BF16: 2, FP32: 4, FP16: 2}[dtype]
+
+
+def sm_bits(dtype: int) -> int:
+    """Sign|mantissa bits per value (R4): everything but the exponent bits."""
+    return {BF16: 8, FP32: 24, FP16: 11}[dtype]
 
 
 def sm_bytes(dtype: int) -> int:
-    """k: sign|mantissa bytes per value (R4): everything but the 8 exponent bits."""
+    """k: sign|mantissa bytes per value of the byte-aligned types (bf16, fp32)."""
     return {BF16: 1, FP32: 3}[dtype]
 
 
+def sm_section_bytes(n: int, dtype: int) -> int:
+    """Bytes of the sign|mantissa section of n values: ceil(n * bits / 8) (R4)."""
+    return -(-n * sm_bits(dtype) // 8)
+
+
 def int_dtype(dtype: int):
-    return {BF16: np.uint16, FP32: np.uint32}[dtype]
+    return {BF16: np.uint16, FP32: np.uint32, FP16: np.uint16}[dtype]
 
 
 # -------------------------------------------------------- field split / merge
 # [CIERA 3.1] "splits each weight value into exponent bits and sign-plus-mantissa
 # bits".  Bit positions are those of IEEE-754 binary32 and of bfloat16 (binary32
-# with the low 16 mantissa bits dropped): sign | 8 exponent bits | mantissa.
+# with the low 16 mantissa bits dropped): sign | 8 exponent bits | mantissa; and
+# of IEEE-754 binary16: sign | 5 exponent bits | 10 mantissa bits.
+
+# (exponent shift = mantissa bits, exponent mask, sign bit position)
+_LAYOUT = {BF16: (7, 0xFF, 15), FP32: (23, 0xFF, 31), FP16: (10, 0x1F, 15)}
+
 
 def exponent_field(u: np.ndarray, dtype: int) -> np.ndarray:
+    shift, emask, _ = _LAYOUT[dtype]
     u = np.asarray(u).astype(np.uint32)
-    shift = 7 if dtype == BF16 else 23
-    return ((u >> shift) & 0xFF).astype(np.uint8)
+    return ((u >> shift) & emask).astype(np.uint8)
 
 
 def sign_mantissa_field(u: np.ndarray, dtype: int) -> np.ndarray:
-    """bf16 -> sign<<7 | mantissa(7);  fp32 -> sign<<23 | mantissa(23)."""
+    """bf16 -> sign<<7 | mantissa(7);  fp32 -> sign<<23 | mantissa(23);
+    fp16 -> sign<<10 | mantissa(10)."""
+    shift, _, sbit = _LAYOUT[dtype]
     u = np.asarray(u).astype(np.uint32)
-    if dtype == BF16:
-        return ((u >> 15) << 7) | (u & 0x7F)
-    return ((u >> 31) << 23) | (u & 0x7FFFFF)
+    return ((u >> sbit) << shift) | (u & ((1 << shift) - 1))
 
 
 def join_fields(sm: np.ndarray, ex: np.ndarray, dtype: int) -> np.ndarray:
     """Inverse of the split: Merge(exponent, sign|mantissa) [CIERA Alg. 1, receiver]."""
+    shift, _, sbit = _LAYOUT[dtype]
     sm = np.asarray(sm).astype(np.uint32)
     ex = np.asarray(ex).astype(np.uint32)
-    if dtype == BF16:
-        return (((sm >> 7) << 15) | (ex << 7) | (sm & 0x7F)).astype(np.uint16)
-    return (((sm >> 23) << 31) | (ex << 23) | (sm & 0x7FFFFF)).astype(np.uint32)
+    u = ((sm >> shift) << sbit) | (ex << shift) | (sm & ((1 << shift) - 1))
+    return u.astype(int_dtype(dtype))
 
 
 def pack_sm(sm: np.ndarray, dtype: int) -> np.ndarray:
-    """Byte-pack sign|mantissa values: k little-endian bytes each (R4)."""
+    """Pack sign|mantissa values (R4): k little-endian bytes each for bf16 and
+    fp32; for fp16 an LSB-first bit stream of 11-bit values."""
     sm = np.asarray(sm).astype(np.uint32)
     if dtype == BF16:
         return sm.astype(np.uint8)
+    if dtype == FP16:
+        bits = (sm[:, None] >> np.arange(11, dtype=np.uint32)[None, :]) & 1   # bit j of value i
+        return np.packbits(bits.astype(np.uint8).reshape(-1), bitorder="little")
     b = np.stack([sm & 0xFF, (sm >> 8) & 0xFF, (sm >> 16) & 0xFF], axis=1)
     return b.astype(np.uint8).reshape(-1)
 
 
-def unpack_sm(b: np.ndarray, dtype: int) -> np.ndarray:
+def unpack_sm(b: np.ndarray, dtype: int, n: Optional[int] = None) -> np.ndarray:
+    """Inverse of pack_sm; fp16 needs the value count n."""
     b = np.asarray(b, dtype=np.uint8)
     if dtype == BF16:
         return b.astype(np.uint32)
+    if dtype == FP16:
+        bits = np.unpackbits(b, bitorder="little")[:11 * n].reshape(n, 11).astype(np.uint32)
+        return (bits << np.arange(11, dtype=np.uint32)[None, :]).sum(axis=1).astype(np.uint32)
     t = b.reshape(-1, 3).astype(np.uint32)
     return t[:, 0] | (t[:, 1] << 8) | (t[:, 2] << 16)
 
@@ -172,7 +201,7 @@ def raw_len(n: int, dtype: int) -> int:
 
 def comp_len(n: int, n_changed: int, dtype: int, block_size: int) -> int:
     """Header + all sign|mantissa bytes (+ bitmap + 5-byte patches if anything changed)."""
-    base = HEADER_BYTES + n * sm_bytes(dtype)
+    base = HEADER_BYTES + sm_section_bytes(n, dtype)
     if n_changed == 0:
         return base
     return base + bitmap_bytes(n, block_size) + PATCH_BYTES * n_changed
@@ -241,8 +270,8 @@ def encode(x: np.ndarray, cache_slice: np.ndarray, dtype: int, block_size: int,
         return out
     # 4. sign|mantissa bytes of every value
     pos = HEADER_BYTES
-    out[pos:pos + n * sm_bytes(dtype)] = pack_sm(sm, dtype)
-    pos += n * sm_bytes(dtype)
+    out[pos:pos + sm_section_bytes(n, dtype)] = pack_sm(sm, dtype)
+    pos += sm_section_bytes(n, dtype)
     if n_changed == 0:
         return out
     # 5. bitmap: one bit per block of B values that holds a change (R3)
@@ -297,9 +326,9 @@ def decode_stream(s: np.ndarray, dtype: int, block_size: int, n: int, offset: in
         le = np.dtype(int_dtype(dtype)).newbyteorder("<")
         x = s[pos:pos + n * elem_bytes(dtype)].view(le).astype(int_dtype(dtype))
         return x, exponent_field(x, dtype), 0          # R9
-    k = sm_bytes(dtype)
-    sm = unpack_sm(s[pos:pos + n * k], dtype)
-    pos += n * k
+    sms = sm_section_bytes(n, dtype)
+    sm = unpack_sm(s[pos:pos + sms], dtype, n)
+    pos += sms
     ex = np.array(cache_slice, dtype=np.uint8, copy=True)   # previous exponents
     p = h["n_changed"]
     if p > 0:

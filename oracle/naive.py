@@ -10,25 +10,25 @@ from __future__ import annotations
 import struct
 from typing import List, Tuple
 
-BF16, FP32 = 1, 2
+BF16, FP32, FP16 = 1, 2, 3
 
 
-def _sizes(dtype: int) -> Tuple[int, int, int]:
-    """(exponent shift, element bytes, sign|mantissa bytes)."""
-    return (7, 2, 1) if dtype == BF16 else (23, 4, 3)
+def _sizes(dtype: int) -> Tuple[int, int, int, int]:
+    """(mantissa bits, exponent bits, element bytes, sign|mantissa bits)."""
+    return {BF16: (7, 8, 2, 8), FP32: (23, 8, 4, 24), FP16: (10, 5, 2, 11)}[dtype]
 
 
 def split(u: int, dtype: int) -> Tuple[int, int]:
     """(exponent, sign|mantissa) of one bit pattern."""
-    shift, e, _ = _sizes(dtype)
+    shift, ebits, e, _ = _sizes(dtype)
     sign = u >> (8 * e - 1)
-    exp = (u >> shift) & 0xFF
+    exp = (u >> shift) & ((1 << ebits) - 1)
     mant = u & ((1 << shift) - 1)
     return exp, (sign << shift) | mant
 
 
 def merge(exp: int, sm: int, dtype: int) -> int:
-    shift, e, _ = _sizes(dtype)
+    shift, _, e, _ = _sizes(dtype)
     sign = sm >> shift
     mant = sm & ((1 << shift) - 1)
     return (sign << (8 * e - 1)) | (exp << shift) | mant
@@ -36,16 +36,17 @@ def merge(exp: int, sm: int, dtype: int) -> int:
 
 def encode(x: List[int], cache: List[int], dtype: int, block: int, compress: bool,
            offset: int = 0, rank: int = 0, world: int = 1) -> bytes:
-    shift, e, k = _sizes(dtype)
+    shift, _, e, kbits = _sizes(dtype)
     n = len(x)
-    sm_bytes = bytearray()
+    acc, nacc = 0, 0           # sign|mantissa bit stream, least significant bit first
     changed = []
     for i, u in enumerate(x):
         exp, sm = split(u, dtype)
-        for b in range(k):
-            sm_bytes.append((sm >> (8 * b)) & 0xFF)
+        acc |= sm << nacc
+        nacc += kbits
         if exp != cache[i]:
             changed.append((i, exp))
+    sm_bytes = acc.to_bytes((nacc + 7) // 8, "little")
     nblk = (n + block - 1) // block
     nbm = (nblk + 7) // 8
     bitmap = bytearray(nbm)
@@ -66,8 +67,9 @@ def encode(x: List[int], cache: List[int], dtype: int, block: int, compress: boo
 
 def decode(stream: bytes, cache: List[int], dtype: int, block: int) -> Tuple[List[int], List[int]]:
     """Decode one well-formed stream; returns (values, new cache)."""
-    shift, e, k = _sizes(dtype)
+    shift, _, e, kbits = _sizes(dtype)
     (_, _, _, mode, _, _, n, p, total, _, _, _, _) = struct.unpack_from("<4sHBBIIQQQQIIQ", stream, 0)
+    sms = (n * kbits + 7) // 8
     body = stream[64:total]
     if mode == 0:
         xs = [struct.unpack_from("<H" if e == 2 else "<I", body, i * e)[0] for i in range(n)]
@@ -75,14 +77,13 @@ def decode(stream: bytes, cache: List[int], dtype: int, block: int) -> Tuple[Lis
     exps = list(cache)
     if p:
         nbm = ((n + block - 1) // block + 7) // 8
-        base = n * k + nbm
+        base = sms + nbm
         for j in range(p):
             i, v = struct.unpack_from("<IB", body, base + 5 * j)
             exps[i] = v
+    acc = int.from_bytes(body[:sms], "little")
     xs = []
     for i in range(n):
-        sm = 0
-        for b in range(k):
-            sm |= body[i * k + b] << (8 * b)
+        sm = (acc >> (i * kbits)) & ((1 << kbits) - 1)
         xs.append(merge(exps[i], sm, dtype))
     return xs, exps

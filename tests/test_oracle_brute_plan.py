@@ -27,11 +27,11 @@ def test_every_change_mask_small_n():
             assert st == 0 and np.array_equal(out, x) and np.array_equal(c2, exact)
 
 
-@pytest.mark.parametrize("dtype", [O.BF16, O.FP32])
+@pytest.mark.parametrize("dtype", [O.BF16, O.FP32, O.FP16])
 def test_lengths_1_to_130_against_twin(dtype):
     """n in 1..130 with B=64 covers partial blocks and partial bitmap bytes."""
     rng = np.random.default_rng(dtype)
-    bits = 16 if dtype == O.BF16 else 32
+    bits = 32 if dtype == O.FP32 else 16
     for n in range(1, 131):
         x = rng.integers(0, 1 << bits, n, dtype=np.uint64).astype(O.int_dtype(dtype))
         exact = O.exponent_field(x, dtype)
@@ -136,12 +136,23 @@ def test_corruption_classes():
 #   dec  = 5000 + 16*(137723 + 262144 + 262144)*1000 // 5600000 = 5000 + 1891 = 6891
 #   gain = 226518 -> COMPRESS
 # Same tensor, W = 1: save = 0 -> gain = -dec -> RAW.
+# OLMoE gate 2048x1024 fp16 at 1%: n = 131072, raw = 262208, sign|mantissa
+#   ceil(11*131072/8) = 180224; comp = 64 + 180224 + 32 + 6555 = 186875
+#   save = 75333*15000 // 8000 = 141249
+#   dec  = 5000 + 16*(186875 + 262144 + 262144)*1000 // 5600000 = 5000 + 2031 = 7031
+#   gain = 134218 -> COMPRESS
+# RMSNorm 7168 fp16 at 1%: n = 448, raw = 960, sign|mantissa ceil(4928/8) = 616
+#   comp = 64 + 616 + 1 + 25 = 706; save = 254*15000 // 8000 = 476
+#   dec  = 5000 + 16*(706 + 448 + 448 + 896)*1000 // 5600000 = 5000 + 7 = 5007
+#   gain = -4531 -> RAW
 PLAN_TABLE = [
     # rows, cols, dtype, world, ppm, compress, expected bytes, gain
     (7168, 1, O.BF16, 16, 10000, 0, 960, -4215),
     (7168, 256, O.BF16, 16, 10000, 1, 120515, 197579),
     (2048, 1024, O.FP32, 16, 300000, 0, 524352, 0),
     (2048, 1024, O.BF16, 16, 10000, 1, 137723, 226518),
+    (2048, 1024, O.FP16, 16, 10000, 1, 186875, 134218),
+    (7168, 1, O.FP16, 16, 10000, 0, 960, -4531),
 ]
 
 

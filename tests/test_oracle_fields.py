@@ -1,8 +1,8 @@
 """Pins of the oracle's field split/merge against IEEE-754 facts and library routines.
 
 [CIERA 3.1] splits every value into exponent bits and sign-plus-mantissa bits.
-Which bits those are is fixed by IEEE-754 binary32 and bfloat16 (the top 16 bits
-of a binary32).  The pins below check the oracle against ``math.frexp`` /
+Which bits those are is fixed by IEEE-754 binary32, binary16 and bfloat16 (the
+top 16 bits of a binary32).  The pins below check the oracle against ``math.frexp`` /
 ``numpy.frexp`` and against float arithmetic rebuilding each value from its
 fields -- neither of which shares the oracle's bit formulas.
 """
@@ -62,6 +62,37 @@ def test_bf16_sign_mantissa_rebuilds_value_exhaustive():
             rebuilt = (1 + m / 128.0) * 2.0 ** (ex[u] - 127)
         rebuilt = -rebuilt if s else rebuilt
         assert rebuilt == v and math.copysign(1, rebuilt) == math.copysign(1, v), hex(u)
+
+
+def test_fp16_split_join_exhaustive():
+    ex = O.exponent_field(ALL_BF16, O.FP16)
+    sm = O.sign_mantissa_field(ALL_BF16, O.FP16)
+    assert ex.max() == 31 and sm.max() == 0x7FF
+    assert np.array_equal(O.join_fields(sm, ex, O.FP16), ALL_BF16)
+    assert np.unique(ex.astype(np.uint32) << 11 | sm).size == 65536
+    # the 11-bit values survive the bit-stream packing, at every length mod 8
+    for n in (65536, 65535, 65533, 9, 1):
+        assert np.array_equal(O.unpack_sm(O.pack_sm(sm[:n], O.FP16), O.FP16, n), sm[:n])
+        assert O.pack_sm(sm[:n], O.FP16).size == -(-11 * n // 8)
+
+
+def test_fp16_fields_match_numpy_float16_exhaustive():
+    """Exponent field against frexp of numpy's binary16 values; sign|mantissa
+    rebuilds every finite value by float arithmetic."""
+    v = ALL_BF16.view(np.float16).astype(np.float64)
+    ex = O.exponent_field(ALL_BF16, O.FP16).astype(np.int64)
+    sm = O.sign_mantissa_field(ALL_BF16, O.FP16).astype(np.int64)
+    finite = np.isfinite(v)
+    normal = finite & (np.abs(v) >= 2.0 ** -14)
+    _, e = np.frexp(v[normal])
+    assert np.array_equal(ex[normal], e - 1 + 15)
+    assert np.all(ex[~finite] == 31) and np.all(ex[finite & ~normal] == 0)
+    m = sm & 0x3FF
+    mag = np.where(ex == 0, m / 1024.0 * 2.0 ** -14, (1 + m / 1024.0) * np.exp2(ex - 15.0))
+    rebuilt = np.where(sm >> 10 == 1, -mag, mag)
+    assert np.array_equal(rebuilt[finite], v[finite])
+    assert np.array_equal(np.signbit(rebuilt[finite]), np.signbit(v[finite]))   # -0.0 included
+    assert np.all((m[np.isnan(v)] != 0)) and np.all(m[np.isinf(v)] == 0)
 
 
 def fp32_structured():

@@ -17,6 +17,10 @@ PINS = [
     TF.test_known_values,
     TS.test_known_answer_bf16,
     TS.test_known_answer_fp32,
+    TS.test_known_answer_fp16,
+    TS.test_known_answer_fp16_partial_group,
+    TF.test_fp16_fields_match_numpy_float16_exhaustive,
+    TS.test_fp16_lengths_closed_form,
     TS.test_known_answer_fp32_raw_fallback,
     TS.test_known_answer_zero_change_and_plan_raw,
     TS.test_exhaustive_bf16_round_trip,
@@ -38,21 +42,51 @@ def _some_pin_fails():
 
 def _wrong_exp_shift(u, dtype):
     u = np.asarray(u).astype(np.uint32)
-    return ((u >> (8 if dtype == O.BF16 else 23)) & 0xFF).astype(np.uint8)
+    return ((u >> {O.BF16: 8, O.FP32: 23, O.FP16: 10}[dtype]) & (0x1F if dtype == O.FP16 else 0xFF)).astype(np.uint8)
 
 
 def _sm_without_sign(u, dtype):
     u = np.asarray(u).astype(np.uint32)
-    return u & (0x7F if dtype == O.BF16 else 0x7FFFFF)
+    return u & {O.BF16: 0x7F, O.FP32: 0x7FFFFF, O.FP16: 0x3FF}[dtype]
+
+
+def _fp16_exponent_eight_bits(orig):
+    def ef(u, dtype):
+        if dtype != O.FP16:
+            return orig(u, dtype)
+        return ((np.asarray(u).astype(np.uint32) >> 10) & 0xFF).astype(np.uint8)
+    return ef
+
+
+def _fp16_msb_first(orig_pack, orig_unpack):
+    def pack(sm, dtype):
+        if dtype != O.FP16:
+            return orig_pack(sm, dtype)
+        sm = np.asarray(sm).astype(np.uint32)
+        bits = (sm[:, None] >> np.arange(11, dtype=np.uint32)[None, :]) & 1
+        return np.packbits(bits.astype(np.uint8).reshape(-1), bitorder="big")
+
+    def unpack(b, dtype, n=None):
+        if dtype != O.FP16:
+            return orig_unpack(b, dtype, n)
+        bits = np.unpackbits(np.asarray(b, np.uint8), bitorder="big")[:11 * n].reshape(n, 11).astype(np.uint32)
+        return (bits << np.arange(11, dtype=np.uint32)[None, :]).sum(axis=1).astype(np.uint32)
+    return pack, unpack
+
+
+def _fp16_two_bytes_per_value(orig):
+    def smb(n, dtype):
+        return 2 * n if dtype == O.FP16 else orig(n, dtype)
+    return smb
 
 
 def _comp_len_no_bitmap(n, p, dtype, B):
-    base = O.HEADER_BYTES + n * O.sm_bytes(dtype)
+    base = O.HEADER_BYTES + O.sm_section_bytes(n, dtype)
     return base if p == 0 else base + O.PATCH_BYTES * p
 
 
 def _comp_len_always_bitmap(n, p, dtype, B):
-    return O.HEADER_BYTES + n * O.sm_bytes(dtype) + O.bitmap_bytes(n, B) + O.PATCH_BYTES * p
+    return O.HEADER_BYTES + O.sm_section_bytes(n, dtype) + O.bitmap_bytes(n, B) + O.PATCH_BYTES * p
 
 
 def _msb_first_encode(orig):
@@ -61,7 +95,7 @@ def _msb_first_encode(orig):
         h = O.parse_header(s)
         if h["mode"] == O.MODE_COMPRESSED and h["n_changed"]:
             n = h["n"]
-            off = 64 + n * O.sm_bytes(h["dtype"])
+            off = 64 + O.sm_section_bytes(n, h["dtype"])
             nbm = O.bitmap_bytes(n, h["block_size"])
             bm = s[off:off + nbm]
             s = s.copy()
@@ -76,7 +110,7 @@ def _index_plus_one(orig_enc, orig_dec):
         h = O.parse_header(s)
         if h["mode"] == O.MODE_COMPRESSED and h["n_changed"]:
             n, p = h["n"], h["n_changed"]
-            pb = 64 + n * O.sm_bytes(h["dtype"]) + O.bitmap_bytes(n, h["block_size"])
+            pb = 64 + O.sm_section_bytes(n, h["dtype"]) + O.bitmap_bytes(n, h["block_size"])
             rec = s[pb:pb + 5 * p].reshape(p, 5)
             idx = rec[:, :4].copy().view("<u4").reshape(-1) + 1
             rec[:, :4] = idx.astype("<u4").view(np.uint8).reshape(p, 4)
@@ -90,7 +124,7 @@ def _index_plus_one(orig_enc, orig_dec):
             return orig_dec(s, dtype, B, n, off, rank, world, cache_slice)
         if h["magic"] == O.MAGIC and h["mode"] == O.MODE_COMPRESSED and 0 < h["n_changed"] <= n:
             p = h["n_changed"]
-            pb = 64 + n * O.sm_bytes(dtype) + O.bitmap_bytes(n, B)
+            pb = 64 + O.sm_section_bytes(n, dtype) + O.bitmap_bytes(n, B)
             if pb + 5 * p <= s.size:
                 rec = s[pb:pb + 5 * p].reshape(p, 5)
                 idx = rec[:, :4].copy().view("<u4").reshape(-1) - 1
@@ -141,6 +175,11 @@ MUTATIONS = {
     "decode ignores patches": lambda mp: mp.setattr(O, "decode_stream", _decode_skips_patches(O.decode_stream)),
     "plan drops the W factor of decode": lambda mp: mp.setattr(O, "plan", _plan_dec_without_world),
     "tie resolved as compressed": lambda mp: mp.setattr(O, "comp_len", _check_raw_tie_compress(O.comp_len)),
+    "fp16 exponent read as 8 bits": lambda mp: mp.setattr(O, "exponent_field", _fp16_exponent_eight_bits(O.exponent_field)),
+    "fp16 bit stream most-significant bit first (shared)": lambda mp: (
+        lambda pu: (mp.setattr(O, "pack_sm", pu[0]), mp.setattr(O, "unpack_sm", pu[1])))(
+        _fp16_msb_first(O.pack_sm, O.unpack_sm)),
+    "fp16 section sized 2 bytes per value": lambda mp: mp.setattr(O, "sm_section_bytes", _fp16_two_bytes_per_value(O.sm_section_bytes)),
 }
 
 

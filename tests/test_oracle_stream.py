@@ -64,6 +64,57 @@ def kat_fp32():
     return x, cache, want
 
 
+def kat_fp16():
+    """n=16 fp16 values, B=64, rank 0 of 1.  11-bit sign|mantissa values
+    (sign << 10 | mantissa) packed back to back, least significant bit first:
+      x[0] =  1.0    0x3C00 -> sm 0x000, exponent 15
+      x[1] = -2.0    0xC000 -> sm 0x400, exponent 16, cache 15 -> patch (1, 0x10)
+      x[2] =  1.5    0x3E00 -> sm 0x200
+      x[3] =  2^-24  0x0001 -> sm 0x001, exponent 0
+      x[4] = +Inf    0x7C00 -> sm 0x000, exponent 31
+      x[5] =  NaN    0xFE01 -> sm 0x601, exponent 31
+      x[6] = -0.0    0x8000 -> sm 0x400, exponent 0
+      x[7] = 65504   0x7BFF -> sm 0x3FF, exponent 30
+      x[8..15] = 1.0 -> sm 0x000
+    Set bits of the stream: 21 (x1), 31 (x2), 33 (x3), 55, 64, 65 (x5), 76 (x6),
+    77..86 (x7) -> bytes 00 00 20 80 02 00 80 00 03 F0 7F, then 11 zero bytes
+    (176 bits = 22 bytes).  total = 64 + 22 + 1 + 5 = 92 (0x5C) < raw 96."""
+    x = np.array([0x3C00, 0xC000, 0x3E00, 0x0001, 0x7C00, 0xFE01, 0x8000, 0x7BFF] + [0x3C00] * 8,
+                 dtype=np.uint16)
+    cache = np.array([15, 15, 15, 0, 31, 31, 0, 30] + [15] * 8, dtype=np.uint8)
+    want = H("43494552 0100 03 01 40000000 00000000"
+             "1000000000000000 0100000000000000 5C00000000000000 0000000000000000"
+             "00000000 01000000 0000000000000000"
+             "0000208002008000 03F07F" + "00" * 11 +
+             "01"
+             "0100000010")
+    return x, cache, want
+
+
+def test_known_answer_fp16():
+    x, cache, want = kat_fp16()
+    got = O.encode(x, cache, O.FP16, 64, True)
+    assert got.tobytes().hex() == want.tobytes().hex()
+    assert N.encode([int(v) for v in x], [int(v) for v in cache], 3, 64, True) == want.tobytes()
+    out, new_cache, st = O.decode([want], 16, 1, O.FP16, 64, 1, cache)
+    assert st == 0 and np.array_equal(out, x) and new_cache[1] == 16
+
+
+def test_known_answer_fp16_partial_group():
+    """n=3 (33 bits -> 5 bytes), nothing changed, B=512:
+      -0.0 (sm 0x400) -> bit 10; 65504 (sm 0x3FF) -> bits 11..20;
+      NaN 0xFE01 (sm 0x601) -> bits 22, 31, 32  => 00 FC 5F 80 01.
+    total = 64 + 5 = 69 (0x45) < raw 70."""
+    x = np.array([0x8000, 0x7BFF, 0xFE01], dtype=np.uint16)
+    cache = np.array([0, 30, 31], dtype=np.uint8)
+    want = H("43494552 0100 03 01 00020000 00000000"
+             "0300000000000000 0000000000000000 4500000000000000 0000000000000000"
+             "00000000 01000000 0000000000000000"
+             "00FC5F8001")
+    assert O.encode(x, cache, O.FP16, 512, True).tobytes().hex() == want.tobytes().hex()
+    assert N.encode([int(v) for v in x], [int(v) for v in cache], 3, 512, True) == want.tobytes()
+
+
 def test_known_answer_bf16():
     x, cache, want = kat_bf16()
     got = O.encode(x, cache, O.BF16, 64, True, offset=130, rank=1, world=2)
@@ -108,23 +159,29 @@ def test_known_answer_zero_change_and_plan_raw():
 
 # ---------------------------------------------------- closed forms / invariants
 
-@pytest.mark.parametrize("dtype", [O.BF16, O.FP32])
+@pytest.mark.parametrize("dtype", [O.BF16, O.FP32, O.FP16])
 @pytest.mark.parametrize("n", [1, 15, 16, 17, 511, 512, 513, 4096, 10000])
 def test_zero_change_length(dtype, n):
-    """No exponent changed -> exactly n sign|mantissa bytes plus the header."""
+    """No exponent changed -> exactly the sign|mantissa section plus the header:
+    n bytes (bf16), 3n (fp32), ceil(11n/8) (fp16) -- RAW only on a tie with the
+    raw length (one fp16 value: 2 bytes either way)."""
     rng = np.random.default_rng(n)
-    x = rng.integers(0, 1 << (16 if dtype == O.BF16 else 32), n, dtype=np.uint64).astype(O.int_dtype(dtype))
+    x = rng.integers(0, 1 << (32 if dtype == O.FP32 else 16), n, dtype=np.uint64).astype(O.int_dtype(dtype))
     s = O.encode(x, O.exponent_field(x, dtype), dtype, 512, True)
-    assert s.size == 64 + n * O.sm_bytes(dtype)
-    assert O.parse_header(s)["mode"] == O.MODE_COMPRESSED
+    want = 64 + {O.BF16: n, O.FP32: 3 * n, O.FP16: (11 * n + 7) // 8}[dtype]
+    raw = 64 + {O.BF16: 2, O.FP32: 4, O.FP16: 2}[dtype] * n
+    if want < raw:
+        assert s.size == want and O.parse_header(s)["mode"] == O.MODE_COMPRESSED
+    else:
+        assert dtype == O.FP16 and n == 1 and s.size == raw and O.parse_header(s)["mode"] == O.MODE_RAW
 
 
-@pytest.mark.parametrize("dtype", [O.BF16, O.FP32])
+@pytest.mark.parametrize("dtype", [O.BF16, O.FP32, O.FP16])
 def test_all_changed_is_raw(dtype):
     """Every exponent differs: 5 bytes per patch exceed the (e-k) bytes saved -> RAW."""
     rng = np.random.default_rng(5)
     n = 1000
-    x = rng.integers(0, 1 << (16 if dtype == O.BF16 else 32), n, dtype=np.uint64).astype(O.int_dtype(dtype))
+    x = rng.integers(0, 1 << (32 if dtype == O.FP32 else 16), n, dtype=np.uint64).astype(O.int_dtype(dtype))
     cache = O.exponent_field(x, dtype) ^ np.uint8(1)
     s = O.encode(x, cache, dtype, 512, True)
     h = O.parse_header(s)
@@ -172,6 +229,33 @@ def test_exhaustive_bf16_round_trip():
             assert st == 0
             assert np.array_equal(out, x)
             assert np.array_equal(new_cache, exact)          # cache == EXP(x) after decode
+
+
+def test_exhaustive_fp16_round_trip():
+    """decode(encode(x)) == x for all 65,536 fp16 patterns against several
+    caches, in one shard and in shards whose lengths are not multiples of 8."""
+    x = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    rng = np.random.default_rng(8)
+    exact = O.exponent_field(x, O.FP16)
+    for cache in (exact, rng.integers(0, 32, x.size, dtype=np.uint8),
+                  np.where(rng.random(x.size) < 0.01, exact ^ 1, exact).astype(np.uint8)):
+        for rows, cols, world in ((256, 256, 1), (4096, 16, 4), (65536, 1, 7)):
+            streams = [O.encode(x[o:o + n], cache[o:o + n], O.FP16, 512, True, o, r, world)
+                       for r in range(world) for (o, n) in [O.shard(rows, cols, world, r)]]
+            out, new_cache, st = O.decode(streams, rows, cols, O.FP16, 512, world, cache)
+            assert st == 0 and np.array_equal(out, x) and np.array_equal(new_cache, exact)
+
+
+def test_fp16_lengths_closed_form():
+    """fp16 sign|mantissa section: 11 bits per value, ceil(11n/8) bytes; 8 values
+    fill exactly 11 bytes; with no change the stream is 64 + ceil(11n/8)."""
+    for n in range(0, 100):
+        assert O.sm_section_bytes(n, O.FP16) == math.ceil(11 * n / 8)
+        assert O.comp_len(n, 0, O.FP16, 64) == 64 + math.ceil(11 * n / 8)
+    assert O.comp_len(8000, 0, O.FP16, 64) == 64 + 11000
+    # ratio at no change: raw 2 bytes per value vs 11/8
+    n = 1 << 20
+    assert O.raw_len(n, O.FP16) - 64 == 2 * n and O.comp_len(n, 0, O.FP16, 512) - 64 == n * 11 // 8
 
 
 def test_fp32_round_trip_structured():
