@@ -137,12 +137,21 @@ SIGMA_1PCT = 0.0087
 SIGMA_2PCT = 0.0174
 
 
+# (mantissa bits, exponent bits, same-width integer type) of each float format
+_LAYOUT = {torch.bfloat16: (7, 8, torch.int16), torch.float32: (23, 8, torch.int32),
+           torch.float16: (10, 5, torch.int16)}
+
+
+def elem_bytes(dtype: torch.dtype) -> int:
+    return 4 if dtype == torch.float32 else 2
+
+
 def _mantissa_mask(dtype: torch.dtype) -> int:
-    return {torch.bfloat16: 0x7F, torch.float32: 0x7FFFFF}[dtype]
+    return (1 << _LAYOUT[dtype][0]) - 1
 
 
 def _int_view(w: torch.Tensor) -> torch.Tensor:
-    return w.view({torch.bfloat16: torch.int16, torch.float32: torch.int32}[w.dtype])
+    return w.view(_LAYOUT[w.dtype][2])
 
 
 def mask_uniform(numel: int, frac: float, seed: int, device="cpu") -> torch.Tensor:
@@ -189,7 +198,7 @@ def perturb_exact(w0: torch.Tensor, mask: torch.Tensor, seed: int) -> torch.Tens
     for normal numbers away from the range limits, so their binary exponent
     moves by exactly one.  Every position then has its mantissa bits XOR-ed
     with random bits (which never touches the exponent)."""
-    assert w0.dtype in (torch.bfloat16, torch.float32)
+    assert w0.dtype in _LAYOUT
     dev = w0.device
     g = _gen(seed, dev)
     flat = w0.reshape(-1)
@@ -206,12 +215,13 @@ def perturb_exact(w0: torch.Tensor, mask: torch.Tensor, seed: int) -> torch.Tens
     return w1.reshape(w0.shape)
 
 
-_SPECIAL_BF16 = {
-    # class -> (sign, exponent, mantissa kind); kinds: 0 zero, 1 random non-zero
-    "pzero": (0, 0x00, 0), "nzero": (1, 0x00, 0),
-    "psub": (0, 0x00, 1), "nsub": (1, 0x00, 1),
-    "pinf": (0, 0xFF, 0), "ninf": (1, 0xFF, 0),
-    "qnan": (None, 0xFF, 2), "snan": (None, 0xFF, 3),
+_SPECIALS = {
+    # class -> (sign, exponent (0 or all ones), mantissa kind); kinds: 0 zero,
+    # 1 random non-zero, 2 quiet NaN payload, 3 signalling NaN payload
+    "pzero": (0, 0, 0), "nzero": (1, 0, 0),
+    "psub": (0, 0, 1), "nsub": (1, 0, 1),
+    "pinf": (0, 1, 0), "ninf": (1, 1, 0),
+    "qnan": (None, 1, 2), "snan": (None, 1, 3),
 }
 
 
@@ -220,9 +230,10 @@ def inject_specials(w: torch.Tensor, prob: float, seed: int) -> torch.Tensor:
     by a value drawn uniformly from the eight special classes above.
 
     The bit patterns are built from the IEEE-754 / bfloat16 field positions:
-    sign in the top bit, then the exponent (8 bits), then the mantissa (7 bits
-    for bf16, 23 for fp32).  A quiet NaN has the top mantissa bit set; a
-    signalling NaN has it clear and some other mantissa bit set."""
+    sign in the top bit, then the exponent (8 bits; 5 for fp16), then the
+    mantissa (7 bits for bf16, 23 for fp32, 10 for fp16).  A quiet NaN has the
+    top mantissa bit set; a signalling NaN has it clear and some other mantissa
+    bit set."""
     dev = w.device
     g = _gen(seed, dev)
     out = w.clone().reshape(-1)
@@ -232,7 +243,8 @@ def inject_specials(w: torch.Tensor, prob: float, seed: int) -> torch.Tensor:
     m = idx.numel()
     if m == 0:
         return out.reshape(w.shape)
-    mbits = 7 if w.dtype == torch.bfloat16 else 23
+    mbits, ebits, _ = _LAYOUT[w.dtype]
+    emax = (1 << ebits) - 1
     cls = torch.randint(0, 8, (m,), generator=g, device=dev)
     rnd_sign = torch.randint(0, 2, (m,), generator=g, device=dev)
     rnd_mant = torch.randint(1, 1 << mbits, (m,), generator=g, device=dev)
@@ -240,10 +252,10 @@ def inject_specials(w: torch.Tensor, prob: float, seed: int) -> torch.Tensor:
     sign = torch.zeros(m, dtype=torch.int64, device=dev)
     expo = torch.zeros(m, dtype=torch.int64, device=dev)
     mant = torch.zeros(m, dtype=torch.int64, device=dev)
-    for c, (s, e, kind) in enumerate(_SPECIAL_BF16.values()):
+    for c, (s, e, kind) in enumerate(_SPECIALS.values()):
         here = cls == c
         sign = torch.where(here, torch.full_like(sign, s) if s is not None else rnd_sign, sign)
-        expo = torch.where(here, torch.full_like(expo, e), expo)
+        expo = torch.where(here, torch.full_like(expo, e * emax), expo)
         if kind == 1:
             mk = rnd_mant
         elif kind == 2:
@@ -254,12 +266,12 @@ def inject_specials(w: torch.Tensor, prob: float, seed: int) -> torch.Tensor:
         else:
             mk = torch.zeros_like(mant)
         mant = torch.where(here, mk, mant)
-    pattern = (sign << (mbits + 8)) | (expo << mbits) | mant
+    pattern = (sign << (mbits + ebits)) | (expo << mbits) | mant
     iv = _int_view(out)
-    if w.dtype == torch.bfloat16:
-        pattern = torch.where(pattern >= 0x8000, pattern - 0x10000, pattern)
-    else:
+    if w.dtype == torch.float32:
         pattern = torch.where(pattern >= 0x80000000, pattern - 0x100000000, pattern)
+    else:
+        pattern = torch.where(pattern >= 0x8000, pattern - 0x10000, pattern)
     iv[idx] = pattern.to(iv.dtype)
     return out.reshape(w.shape)
 
@@ -286,7 +298,7 @@ def weight_pair(specs: Sequence[TensorSpec], i: int, cfg: PairConfig, device="cp
     ``w_prev`` continues a chain of iterates; otherwise W_prev is the base
     weights (with specials injected if configured)."""
     s = specs[i]
-    eb = 2 if cfg.dtype == torch.bfloat16 else 4
+    eb = elem_bytes(cfg.dtype)
     if w_prev is None:
         w_prev = base_weights(s, tensor_seed(cfg.tag, "base", i), cfg.dtype, device)
         if cfg.specials > 0:
@@ -312,7 +324,7 @@ def weight_pair(specs: Sequence[TensorSpec], i: int, cfg: PairConfig, device="cp
 def layer_windows(specs: Sequence[TensorSpec], cfg: PairConfig, iteration: int = 0) -> Optional[torch.Tensor]:
     if not cfg.clustered:
         return None
-    eb = 2 if cfg.dtype == torch.bfloat16 else 4
+    eb = elem_bytes(cfg.dtype)
     return clustered_windows(specs, cfg.frac, eb, tensor_seed(cfg.tag, "win", iteration))
 
 
@@ -331,6 +343,10 @@ def config(name: str, frac: float = 0.01, clustered: bool = False) -> Tuple[List
     if name == "layer_fp32":
         tag = f"layer32-{frac}-{'c' if clustered else 'u'}"
         return olmoe_layer_specs(), PairConfig(tag, dtype=torch.float32, frac=frac,
+                                               clustered=clustered), 16
+    if name == "layer_fp16":
+        tag = f"layer16-{frac}-{'c' if clustered else 'u'}"
+        return olmoe_layer_specs(), PairConfig(tag, dtype=torch.float16, frac=frac,
                                                clustered=clustered), 16
     if name == "fine":
         return fine_grained_layer_specs(), PairConfig("fine", frac=frac, specials=1e-4), 16

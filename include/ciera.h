@@ -17,12 +17,17 @@
  *     [32,40) total_len  [40,48) element offset of the shard in the tensor
  *     [48,52) rank  [52,56) world  [56,64) 0
  *   COMPRESSED body: n sign|mantissa records (bf16: 1 byte, sign in bit 7 and
- *     the 7 mantissa bits below; fp32: 3 bytes of sign<<23|mantissa), then --
+ *     the 7 mantissa bits below; fp32: 3 bytes of sign<<23|mantissa; fp16:
+ *     the 11-bit values sign<<10|mantissa back to back in one bit stream,
+ *     least significant bit first, ceil(11n/8) bytes -- the exponent of an
+ *     fp16 value is its 5-bit field, cached in a byte), then --
  *     only if n_changed > 0 -- a bitmap of ceil(ceil(n/B)/8) bytes (bit b =
  *     byte b/8, bit b%8: block b of B values holds a changed exponent), then
  *     n_changed records of 5 bytes (u32 shard-local index, u8 exponent) in
  *     strictly ascending index order.
  *   RAW body: the n values as stored (2 or 4 bytes each).
+ *   fp16 extends the pages' bf16/fp32 scope the same way; its layout is this
+ *   library's reading, not a format of the pages.
  *   A stream is COMPRESSED only if the plan asked for it and it is strictly
  *   shorter than the RAW stream (64 + n*element bytes).
  *
@@ -54,7 +59,7 @@ extern "C" {
 #define CIERA_ABI_VERSION 1u
 #define CIERA_HEADER_BYTES 64u
 
-typedef enum { CIERA_BF16 = 1, CIERA_FP32 = 2 } ciera_dtype_t;
+typedef enum { CIERA_BF16 = 1, CIERA_FP32 = 2, CIERA_FP16 = 3 } ciera_dtype_t;
 
 typedef enum {
   CIERA_OK = 0,

@@ -10,7 +10,7 @@ from typing import List, Optional, Sequence, Tuple
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libciera.so")
 
-CIERA_BF16, CIERA_FP32 = 1, 2
+CIERA_BF16, CIERA_FP32, CIERA_FP16 = 1, 2, 3
 CIERA_OK, CIERA_ERR_INVALID_ARG, CIERA_ERR_BUFFER_TOO_SMALL, CIERA_ERR_UNSUPPORTED, CIERA_ERR_DEVICE = range(5)
 CIERA_ST_MAGIC, CIERA_ST_FIELD, CIERA_ST_LENGTH, CIERA_ST_PATCH, CIERA_ST_BITMAP = 1, 2, 4, 8, 16
 HEADER_BYTES = 64

@@ -28,8 +28,10 @@ constexpr uint64_t kEncMagic = 0x434945524145454eull;  // batch kinds
 constexpr uint64_t kDecMagic = 0x4349455241444543ull;
 constexpr int kMaxGroups = 64;
 
-uint32_t elem_bytes(uint32_t dt) { return dt == CIERA_BF16 ? 2u : 4u; }
-uint32_t sm_bytes(uint32_t dt) { return dt == CIERA_BF16 ? 1u : 3u; }
+uint32_t elem_bytes(uint32_t dt) { return dt == CIERA_FP32 ? 4u : 2u; }
+// Sign|mantissa bits per value: bf16 8, fp32 24, fp16 11 (an LSB-first bit
+// stream); the section of n values takes ceil(n * bits / 8) bytes.
+uint32_t sm_bits(uint32_t dt) { return dt == CIERA_BF16 ? 8u : dt == CIERA_FP32 ? 24u : 11u; }
 bool pow2(uint32_t x) { return x && !(x & (x - 1)); }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
@@ -45,7 +47,7 @@ ciera_status_t device_error(const char* what, hipError_t e) {
 
 ciera_status_t check_tensor(const ciera_tensor_t* t) {
   if (!t) return CIERA_ERR_INVALID_ARG;
-  if (t->dtype != CIERA_BF16 && t->dtype != CIERA_FP32) return CIERA_ERR_INVALID_ARG;
+  if (t->dtype != CIERA_BF16 && t->dtype != CIERA_FP32 && t->dtype != CIERA_FP16) return CIERA_ERR_INVALID_ARG;
   if (!pow2(t->block_size) || t->block_size < 64 || t->block_size > 4096) return CIERA_ERR_INVALID_ARG;
   if (t->world == 0) return CIERA_ERR_INVALID_ARG;
   if (t->rows >= kMaxElems || t->cols >= kMaxElems) return CIERA_ERR_UNSUPPORTED;
@@ -281,10 +283,10 @@ ciera_status_t ciera_plan(const ciera_tensor_t* t, uint32_t change_ppm, const ci
   if (c.link_bytes_per_us == 0 || c.hbm_bytes_per_us == 0) return CIERA_ERR_INVALID_ARG;
   uint64_t off, n;
   shard_of(t, 0, &off, &n);
-  const u128 e = elem_bytes(t->dtype), k = sm_bytes(t->dtype), W = t->world;
+  const u128 e = elem_bytes(t->dtype), W = t->world;
   const u128 raw = kHeader + (u128)n * e;
   const u128 P = ((u128)change_ppm * n + 999999u) / 1000000u;
-  const u128 comp = kHeader + (u128)n * k + (P ? bitmap_bytes(n, t->block_size) + 5 * P : 0);
+  const u128 comp = kHeader + ((u128)n * sm_bits(t->dtype) + 7) / 8 + (P ? bitmap_bytes(n, t->block_size) + 5 * P : 0);
   std::memset(out, 0, sizeof(*out));
   out->raw_stream_bytes = (uint64_t)raw;
   out->max_stream_bytes = (uint64_t)raw;

@@ -41,29 +41,50 @@ __device__ __forceinline__ void stg16_nt(void* p, v4u v) {
 
 template <int DT>
 struct Tr;
+// E: bytes per value; SHIFT: mantissa bits; EMASK: exponent field; SMBITS:
+// sign|mantissa bits per value in the stream (bf16 and fp32 whole bytes, fp16
+// an 11-bit LSB-first bit stream: 16 values = 22 bytes).
 template <>
 struct Tr<1> {  // bf16: 1 sign, 8 exponent, 7 mantissa bits
-  static constexpr int E = 2, K = 1, SHIFT = 7;
+  static constexpr int E = 2, SHIFT = 7, SMBITS = 8;
+  static constexpr uint32_t EMASK = 0xFF;
 };
 template <>
 struct Tr<2> {  // fp32: 1 sign, 8 exponent, 23 mantissa bits
-  static constexpr int E = 4, K = 3, SHIFT = 23;
+  static constexpr int E = 4, SHIFT = 23, SMBITS = 24;
+  static constexpr uint32_t EMASK = 0xFF;
 };
+template <>
+struct Tr<3> {  // fp16: 1 sign, 5 exponent, 10 mantissa bits
+  static constexpr int E = 2, SHIFT = 10, SMBITS = 11;
+  static constexpr uint32_t EMASK = 0x1F;
+};
+
+// Bytes of the sign|mantissa section of n values, and the byte offset of value
+// c0 in it (c0 a multiple of 16, so the offset is whole).
+template <int DT>
+__device__ __forceinline__ uint64_t sm_sec(uint64_t n) {
+  return (n * Tr<DT>::SMBITS + 7) / 8;
+}
+template <int DT>
+__device__ __forceinline__ uint64_t sm_off(uint64_t c0) {
+  return c0 * Tr<DT>::SMBITS / 8;
+}
 
 template <int DT>
 __device__ __forceinline__ uint32_t exp_of(uint32_t v) {
-  return (v >> Tr<DT>::SHIFT) & 0xFFu;
+  return (v >> Tr<DT>::SHIFT) & Tr<DT>::EMASK;
 }
-// sign|mantissa: bf16 -> sign<<7 | mantissa(7); fp32 -> sign<<23 | mantissa(23)
+// sign|mantissa: sign << SHIFT | mantissa (bf16 8 bits, fp32 24, fp16 11)
 template <int DT>
 __device__ __forceinline__ uint32_t sm_of(uint32_t v) {
-  if constexpr (DT == 1) return ((v >> 8) & 0x80u) | (v & 0x7Fu);
-  else return ((v >> 8) & 0x800000u) | (v & 0x7FFFFFu);
+  constexpr int S = Tr<DT>::SHIFT, SB = 8 * Tr<DT>::E - 1;
+  return ((v >> SB) << S) | (v & ((1u << S) - 1u));
 }
 template <int DT>
 __device__ __forceinline__ uint32_t join(uint32_t sm, uint32_t ex) {
-  if constexpr (DT == 1) return ((sm & 0x80u) << 8) | (ex << 7) | (sm & 0x7Fu);
-  else return ((sm & 0x800000u) << 8) | (ex << 23) | (sm & 0x7FFFFFu);
+  constexpr int S = Tr<DT>::SHIFT, SB = 8 * Tr<DT>::E - 1;
+  return ((sm >> S) << SB) | (ex << S) | (sm & ((1u << S) - 1u));
 }
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
@@ -78,7 +99,7 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 template <int DT>
 __device__ __forceinline__ void load16(const uint8_t* p, int cnt, uint32_t v[16]) {
   if (cnt == 16) {
-    if constexpr (DT == 1) {
+    if constexpr (Tr<DT>::E == 2) {
       const v4u a = ldg16(p);
       const v4u b = ldg16(p + 16);
       const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -98,7 +119,7 @@ __device__ __forceinline__ void load16(const uint8_t* p, int cnt, uint32_t v[16]
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < cnt) {
-        if constexpr (DT == 1) v[j] = gp(reinterpret_cast<const uint16_t*>(p))[j];
+        if constexpr (Tr<DT>::E == 2) v[j] = gp(reinterpret_cast<const uint16_t*>(p))[j];
         else v[j] = gp(reinterpret_cast<const uint32_t*>(p))[j];
       } else {
         v[j] = 0;
@@ -110,7 +131,7 @@ __device__ __forceinline__ void load16(const uint8_t* p, int cnt, uint32_t v[16]
 template <int DT>
 __device__ __forceinline__ void store16(uint8_t* p, int cnt, const uint32_t v[16], bool vec = true) {
   if (cnt == 16 && vec) {
-    if constexpr (DT == 1) {
+    if constexpr (Tr<DT>::E == 2) {
       v4u a, b;
       a.x = v[0] | (v[1] << 16); a.y = v[2] | (v[3] << 16);
       a.z = v[4] | (v[5] << 16); a.w = v[6] | (v[7] << 16);
@@ -130,7 +151,7 @@ __device__ __forceinline__ void store16(uint8_t* p, int cnt, const uint32_t v[16
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < cnt) {
-        if constexpr (DT == 1) gp(reinterpret_cast<uint16_t*>(p))[j] = (uint16_t)v[j];
+        if constexpr (Tr<DT>::E == 2) gp(reinterpret_cast<uint16_t*>(p))[j] = (uint16_t)v[j];
         else gp(reinterpret_cast<uint32_t*>(p))[j] = v[j];
       }
     }
@@ -166,10 +187,44 @@ __device__ __forceinline__ uint32_t byte_of(const uint32_t c[4], int j) {
   return (c[j >> 2] >> (8 * (j & 3))) & 0xFFu;
 }
 
-// sign|mantissa records of 16 values: bf16 16 bytes, fp32 48 bytes (3 per value, LE).
+// fp16: the 11-bit values of 16 elements as an LSB-first bit stream, in 6
+// words (176 bits; the top half of the last word is zero).
+__device__ __forceinline__ void pack11x16(const uint32_t sm[16], uint32_t o[6]) {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) o[i] = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int b = 11 * j, w = b >> 5, r = b & 31;
+    o[w] |= sm[j] << r;
+    if (r > 21) o[w + 1] |= sm[j] >> (32 - r);
+  }
+}
+
+// sign|mantissa records of 16 values at p: bf16 16 bytes, fp32 48 bytes (3 per
+// value, LE), fp16 22 bytes (p even: the chunk starts at byte 22k of the section).
 template <int DT>
 __device__ __forceinline__ void store_sm16(uint8_t* p, int cnt, const uint32_t sm[16]) {
-  if constexpr (DT == 1) {
+  if constexpr (DT == 3) {
+    uint32_t o[6];
+    pack11x16(sm, o);
+    if (cnt == 16) {
+      if ((reinterpret_cast<uintptr_t>(p) & 3u) == 0) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) gp(reinterpret_cast<uint32_t*>(p))[i] = o[i];
+        gp(reinterpret_cast<uint16_t*>(p + 20))[0] = (uint16_t)o[5];
+      } else {  // p = 4q + 2
+        gp(reinterpret_cast<uint16_t*>(p))[0] = (uint16_t)o[0];
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+          gp(reinterpret_cast<uint32_t*>(p + 2))[i] = (o[i] >> 16) | (o[i + 1] << 16);
+      }
+    } else {
+      const int nb = (11 * cnt + 7) / 8;
+#pragma unroll
+      for (int b = 0; b < 22; ++b)
+        if (b < nb) gp(p)[b] = (uint8_t)(o[b >> 2] >> (8 * (b & 3)));
+    }
+  } else if constexpr (DT == 1) {
     uint32_t c[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -271,10 +326,43 @@ __device__ __forceinline__ uint32_t nonzero_bytes16(const uint32_t d[4]) {
   return m;
 }
 
-// sign|mantissa of value j from the raw words of a 16-value chunk.
+// The sign|mantissa words of the 16-value chunk starting at value c0 of a
+// section (c0 a multiple of 16).  fp16 chunks start on even bytes: a complete
+// chunk is read as the 6 aligned words around it and shifted down by 16 bits
+// when it starts mid-word (the words stay inside the slot, which holds a RAW
+// stream of 2 bytes per value); a partial chunk is read byte by byte.
+template <int DT, int SW>
+__device__ __forceinline__ void load_smw(const uint8_t* sec, uint64_t c0, int cnt, uint32_t w[SW]) {
+  const uint8_t* a = sec + sm_off<DT>(c0);
+  if constexpr (DT == 3) {
+    if (cnt == 16) {
+      const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(a) & 3u);  // 0 or 2
+      const G1 uint32_t* q = gp(reinterpret_cast<const uint32_t*>(a - sh));
+#pragma unroll
+      for (int i = 0; i < 6; ++i) w[i] = q[i];
+      if (sh) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) w[i] = (w[i] >> 16) | (w[i + 1] << 16);
+        w[5] >>= 16;
+      }
+    } else {
+      load_words<SW>(a, (uint32_t)(11 * cnt + 7) / 8, false, w);
+    }
+  } else {
+    load_words<SW>(a, (uint32_t)cnt * Tr<DT>::SMBITS / 8, true, w);
+  }
+}
+
+// sign|mantissa of value j from the raw words of a 16-value chunk (fp16: the
+// chunk's bit stream starting at bit 0 of w[0]).
 template <int DT>
 __device__ __forceinline__ uint32_t sm_from_words(const uint32_t* w, int j) {
-  if constexpr (DT == 1) {
+  if constexpr (DT == 3) {
+    const int b = 11 * j, q = b >> 5, r = b & 31;
+    uint32_t v = w[q] >> r;
+    if (r > 21) v |= w[q + 1] << (32 - r);
+    return v & 0x7FFu;
+  } else if constexpr (DT == 1) {
     return (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
   } else {
     const int q = j >> 2, k = j & 3;
@@ -394,7 +482,7 @@ __device__ uint32_t look_back(uint64_t* sw, uint32_t local, uint32_t tag, uint32
 
 template <int DT, int S>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* ctl, uint32_t batch_id) {
-  constexpr int E = Tr<DT>::E, K = Tr<DT>::K;
+  constexpr int E = Tr<DT>::E;
   constexpr uint32_t T = (uint32_t)kSub * S;
   constexpr int XW = 4 * E;  // words of 16 raw values
   __shared__ uint32_t s_local, s_excl;
@@ -462,13 +550,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
           uint32_t v[16], sm[16];
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            v[j] = xw[s][j];
+            if constexpr (E == 2) v[j] = (xw[s][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            else v[j] = xw[s][j];
             const uint32_t e = exp_of<DT>(v[j]);
             expk[s][j >> 2] |= e << (8 * (j & 3));
             if (j < cnt[s] && e != byte_of(cw[s], j)) mask[s] |= 1u << j;
             sm[j] = sm_of<DT>(v[j]);
           }
-          if (compress) store_sm16<DT>(d.stream + kHeader + c0 * K, cnt[s], sm);
+          if (compress) store_sm16<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], sm);
           else store16<DT>(d.stream + kHeader + c0 * E, cnt[s], v);
         }
         if (mask[s]) {
@@ -532,9 +621,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
     const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
     const uint32_t tbytes = (tblocks + 7) / 8;
     if (tid < tbytes)
-      gp(d.stream)[kHeader + n * K + (base >> (lb + 3)) + tid] = (uint8_t)(s_bm[tid >> 2] >> (8 * (tid & 3)));
+      gp(d.stream)[kHeader + sm_sec<DT>(n) + (base >> (lb + 3)) + tid] = (uint8_t)(s_bm[tid >> 2] >> (8 * (tid & 3)));
     // (index, exponent) records
-    const uint64_t pbase = kHeader + n * K + nbm;
+    const uint64_t pbase = kHeader + sm_sec<DT>(n) + nbm;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       uint32_t m = mask[s];
@@ -559,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   // the item's last tile knows the total and writes the header
   if (local == a.tpi - 1 && tid == 0) {
     const uint64_t P = (uint64_t)excl + agg;
-    const uint64_t comp = kHeader + n * K + (P ? nbm + 5 * P : 0);
+    const uint64_t comp = kHeader + sm_sec<DT>(n) + (P ? nbm + 5 * P : 0);
     const uint64_t raw = kHeader + n * E;
     const bool cmode = compress && comp < raw;
     if (compress && !cmode) {
@@ -617,10 +706,10 @@ template <int DT, int U>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __restrict__ items, uint32_t item0,
                                                           uint32_t tpr, uint32_t world, uint32_t* status_out,
                                                           const uint32_t* ctl, uint32_t batch_id) {
-  constexpr int E = Tr<DT>::E, K = Tr<DT>::K;
+  constexpr int E = Tr<DT>::E;
   constexpr uint32_t T = (uint32_t)kDecRow * U;
   constexpr uint32_t BMW = (T / 64 + 31) / 32;  // words of per-tile block bits (B >= 64)
-  constexpr int SW = 4 * K;                     // words of 16 sign|mantissa records
+  constexpr int SW = (16 * Tr<DT>::SMBITS + 31) / 32;  // words of 16 sign|mantissa records
   __shared__ uint32_t s_hdr[16];
   __shared__ uint32_t s_expbm[BMW];  // blocks of the tile that hold a patch
   __shared__ uint32_t s_ex[T / 4];   // the tile's exponents: cached, then patched in place
@@ -654,7 +743,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
     cnt[u] = c0 < te ? (int)min<uint64_t>(16, te - c0) : 0;
     if (cnt[u] > 0) {
-      load_words<SW>(st + kHeader + c0 * K, (uint32_t)cnt[u] * K, true, sw[u]);
+      load_smw<DT, SW>(st + kHeader, c0, cnt[u], sw[u]);
       load_words<4>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
     }
   }
@@ -691,7 +780,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
              s_hdr[13] != world || h_mode > 1u) {
     bad = CIERA_ST_FIELD;
   } else {
-    const uint64_t want = h_mode == 0 ? kHeader + n * E : kHeader + n * K + (P ? nbm + 5 * P : 0);
+    const uint64_t want = h_mode == 0 ? kHeader + n * E : kHeader + sm_sec<DT>(n) + (P ? nbm + 5 * P : 0);
     if (P > n || h_tot > d.slot || h_tot != want) bad = CIERA_ST_LENGTH;
   }
   if (bad) {
@@ -719,7 +808,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   // 3. COMPRESSED: this tile's patch range [lo, hi).  Every wave finds it on its
   //    own (two searches sharing a first round of 64 probes, then 32 lanes per
   //    key), so the records can be read without a barrier in between.
-  const uint64_t recs = kHeader + n * K + nbm;
+  const uint64_t recs = kHeader + sm_sec<DT>(n) + nbm;
   uint32_t lo = 0, hi = 0;
   if (P > 0) {
     if (tpr == 1) {
@@ -776,7 +865,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   const bool patched = hi > lo;  // uniform
   const uint64_t tb0 = ts >> lb, tb1 = (te + B - 1) >> lb;
   const uint32_t nbt = (uint32_t)(tb1 - tb0);
-  const uint8_t* bm = st + kHeader + n * K;
+  const uint8_t* bm = st + kHeader + sm_sec<DT>(n);
   const bool bm_mine = P > 0 && tid * 32 < nbt;
   Words2 bmw{0, 0, 0};
   uint32_t bm_tail = 0;
@@ -950,7 +1039,7 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
       case 8: CIERA_ENC(1, 8); break;
       default: return hipErrorInvalidValue;
     }
-  } else {
+  } else if (dtype == 2) {
     switch (sub) {
       case 1: CIERA_ENC(2, 1); break;
       case 2: CIERA_ENC(2, 2); break;
@@ -958,6 +1047,16 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
       case 8: CIERA_ENC(2, 8); break;
       default: return hipErrorInvalidValue;
     }
+  } else if (dtype == 3) {
+    switch (sub) {
+      case 1: CIERA_ENC(3, 1); break;
+      case 2: CIERA_ENC(3, 2); break;
+      case 4: CIERA_ENC(3, 4); break;
+      case 8: CIERA_ENC(3, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
   }
 #undef CIERA_ENC
   return hipGetLastError();
@@ -986,13 +1085,22 @@ hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0,
       case 4: CIERA_DEC(1, 4); break;
       default: return hipErrorInvalidValue;
     }
-  } else {
+  } else if (dtype == 2) {
     switch (u) {
       case 1: CIERA_DEC(2, 1); break;
       case 2: CIERA_DEC(2, 2); break;
       case 4: CIERA_DEC(2, 4); break;
       default: return hipErrorInvalidValue;
     }
+  } else if (dtype == 3) {
+    switch (u) {
+      case 1: CIERA_DEC(3, 1); break;
+      case 2: CIERA_DEC(3, 2); break;
+      case 4: CIERA_DEC(3, 4); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
   }
 #undef CIERA_DEC
   return hipGetLastError();
@@ -1006,7 +1114,9 @@ hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint
   (void)hipGetLastError();
   const dim3 grid((uint32_t)blocks), block(kThreads);
   if (dtype == 1) hipLaunchKernelGGL((cache_update_kernel<1>), grid, block, 0, s, w, cache, n);
-  else hipLaunchKernelGGL((cache_update_kernel<2>), grid, block, 0, s, w, cache, n);
+  else if (dtype == 2) hipLaunchKernelGGL((cache_update_kernel<2>), grid, block, 0, s, w, cache, n);
+  else if (dtype == 3) hipLaunchKernelGGL((cache_update_kernel<3>), grid, block, 0, s, w, cache, n);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

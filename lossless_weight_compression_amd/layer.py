@@ -21,8 +21,8 @@ import torch
 
 from . import _binding as B
 
-TORCH_TO_CIERA = {torch.bfloat16: B.CIERA_BF16, torch.float32: B.CIERA_FP32}
-ELEM = {B.CIERA_BF16: 2, B.CIERA_FP32: 4}
+TORCH_TO_CIERA = {torch.bfloat16: B.CIERA_BF16, torch.float32: B.CIERA_FP32, torch.float16: B.CIERA_FP16}
+ELEM = {B.CIERA_BF16: 2, B.CIERA_FP32: 4, B.CIERA_FP16: 2}
 
 
 def _align(x: int, a: int) -> int:

@@ -10,8 +10,8 @@ import torch
 
 from oracle import ciera_oracle as O
 
-DT = {torch.bfloat16: O.BF16, torch.float32: O.FP32}
-IV = {torch.bfloat16: torch.int16, torch.float32: torch.int32}
+DT = {torch.bfloat16: O.BF16, torch.float32: O.FP32, torch.float16: O.FP16}
+IV = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.float16: torch.int16}
 
 
 def say(*a):
@@ -20,9 +20,9 @@ def say(*a):
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:
-    """Integer bit patterns of a bf16/fp32 tensor as numpy uint16/uint32."""
+    """Integer bit patterns of a bf16/fp16/fp32 tensor as numpy uint16/uint32."""
     iv = t.detach().reshape(-1).view(IV[t.dtype]).cpu().numpy()
-    return iv.view(np.uint16 if t.dtype == torch.bfloat16 else np.uint32)
+    return iv.view(np.uint32 if t.dtype == torch.float32 else np.uint16)
 
 
 def header_total(slot: np.ndarray) -> int:

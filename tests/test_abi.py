@@ -49,7 +49,7 @@ def _rand_tensors(seed, count):
     for _ in range(count):
         rows = int(rng.choice([0, 1, 7, 448, 1024, 2048, 7168, int(rng.integers(1, 100000))]))
         cols = int(rng.choice([1, 3, 256, 1024, 2048, int(rng.integers(1, 5000))]))
-        yield (rows, cols, int(rng.choice([1, 2])), int(2 ** rng.integers(6, 13)),
+        yield (rows, cols, int(rng.choice([1, 2, 3])), int(2 ** rng.integers(6, 13)),
                int(rng.choice([1, 2, 4, 8, 16, 64, int(rng.integers(1, 200))])))
 
 
@@ -87,7 +87,7 @@ def test_shard_parity_with_oracle():
 
 
 def test_argument_errors_are_synchronous():
-    bad = [L.Tensor(4, 4, 3, 512, 1), L.Tensor(4, 4, 1, 500, 1), L.Tensor(4, 4, 1, 32, 1),
+    bad = [L.Tensor(4, 4, 4, 512, 1), L.Tensor(4, 4, 0, 512, 1), L.Tensor(4, 4, 1, 500, 1), L.Tensor(4, 4, 1, 32, 1),
            L.Tensor(4, 4, 1, 8192, 1), L.Tensor(4, 4, 1, 512, 0)]
     for t in bad:
         with pytest.raises(L.CieraError) as e:

@@ -20,8 +20,8 @@ if not torch.cuda.is_available():
 from lossless_weight_compression_amd.layer import LayerCodec  # noqa: E402
 from tests.gpu_harness import say, to_np  # noqa: E402
 
-IV = {torch.bfloat16: torch.int16, torch.float32: torch.int32}
-ODT = {torch.bfloat16: O.BF16, torch.float32: O.FP32}
+IV = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.float16: torch.int16}
+ODT = {torch.bfloat16: O.BF16, torch.float32: O.FP32, torch.float16: O.FP16}
 
 
 def exp_field_gpu(w: torch.Tensor) -> torch.Tensor:
@@ -29,6 +29,8 @@ def exp_field_gpu(w: torch.Tensor) -> torch.Tensor:
     (test-side property check, independent of the library)."""
     if w.dtype == torch.bfloat16:
         return ((w.reshape(-1).view(torch.int16).to(torch.int32) >> 7) & 0xFF).to(torch.uint8)
+    if w.dtype == torch.float16:
+        return ((w.reshape(-1).view(torch.int16).to(torch.int32) >> 10) & 0x1F).to(torch.uint8)
     return ((w.reshape(-1).view(torch.int32) >> 23) & 0xFF).to(torch.uint8)
 
 
@@ -126,6 +128,19 @@ def test_olmoe_layer_bf16(frac, clustered):
     say(f"[gpu]   compression ratio {res['ratio']:.4f}")
     # raw/compressed ~ 2 / (1 + 5f) either way (clustered shards with > ~20% changes go RAW)
     assert abs(res["ratio"] - EXPECTED_RATIO[frac]) < (0.01 if not clustered else 0.03)
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.01, 0.1])
+def test_olmoe_layer_fp16(frac):
+    """The 64-expert layer in fp16: 11-bit sign|mantissa stream, raw/compressed
+    ~ 2 / (1.375 + 5f) (still below 2 at 10%; the break-even is 12.5%)."""
+    say(f"[gpu] OLMoE layer fp16 f={frac}")
+    specs, cfg, world, w0, w1 = _layer("layer_fp16", frac)
+    ppm = int(round(frac * 1e6))
+    _, res = run_layer(specs, w0, w1, torch.float16, world, ppm, sample=(0, 97, 191))
+    say(f"[gpu]   compression ratio {res['ratio']:.4f}")
+    want = 2.0 / min(2.0, 1.375 + 5 * frac)
+    assert abs(res["ratio"] - want) < 0.02
 
 
 def test_olmoe_layer_fp32_warmup_and_schedule():

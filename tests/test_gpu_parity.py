@@ -58,6 +58,17 @@ EDGE = [
     (1000, 1000, 16, 512, torch.bfloat16, 0.0),
     (1000, 1000, 16, 512, torch.float32, 0.003),
     (7168, 1, 16, 512, torch.bfloat16, 0.01),   # an RMSNorm vector
+    # fp16: 22-byte sign|mantissa chunks start mid-word at odd chunks; partial
+    # chunks at every shard end that is not a multiple of 16 values
+    (1, 1, 1, 512, torch.float16, 0.5),
+    (17, 1, 16, 64, torch.float16, 0.3),
+    (10, 3, 4, 64, torch.float16, 0.1),
+    (33, 7, 2, 128, torch.float16, 0.05),
+    (1, 4097, 1, 512, torch.float16, 0.01),
+    (2, 8193, 1, 64, torch.float16, 0.002),
+    (64, 1000, 4, 1024, torch.float16, 0.01),
+    (1000, 1000, 16, 512, torch.float16, 0.003),
+    (96, 4096, 2, 4096, torch.float16, 0.0),
 ]
 
 
@@ -74,7 +85,7 @@ def test_edge_shapes(rows, cols, world, B, dtype, frac):
         assert res["status"] == 0 and res["ostatus"] == 0
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
 @pytest.mark.parametrize("frac", [0.0, 0.005, 0.19, 0.3, 1.0])
 def test_change_rates_and_raw_fallback(dtype, frac):
     """Forced compress=1 at every rate: high rates must come out RAW through the
@@ -113,6 +124,24 @@ def test_specials_and_all_bf16_patterns():
     cfg = W.PairConfig("sp-test", frac=0.01, specials=1e-2)
     w0, w1 = _pairs(spec, cfg)
     assert Case([(448, 256)], torch.bfloat16, 16).run(w0, w1)["status"] == 0
+
+
+def test_all_fp16_patterns_and_specials():
+    """Every fp16 bit pattern (+-0, subnormals, Inf, all NaN payloads) survives,
+    against a cache of other exponents, in shards of several sizes."""
+    say("[gpu] all 65536 fp16 patterns")
+    x = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.float16).reshape(256, 256)
+    rng = np.random.default_rng(6)
+    perm = torch.from_numpy(rng.permutation(65536))
+    w0 = [x.reshape(-1)[perm].reshape(256, 256).clone()]
+    w1 = [x.clone()]
+    for world in (1, 4, 16):
+        res = Case([(256, 256)], torch.float16, world).run(w0, w1, compress=[1])
+        assert res["status"] == 0
+    spec = [W.TensorSpec("r", 448, 256)]
+    cfg = W.PairConfig("sp16-test", dtype=torch.float16, frac=0.01, specials=1e-2)
+    w0, w1 = _pairs(spec, cfg)
+    assert Case([(448, 256)], torch.float16, 16).run(w0, w1)["status"] == 0
 
 
 def _corrupt_case(frac=0.01):

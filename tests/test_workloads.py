@@ -74,3 +74,25 @@ def test_specials_present():
     assert np.any((ex == 255) & ((sm & 0x7F) != 0))      # NaN
     assert np.any((ex == 0) & ((sm & 0x7F) != 0))        # subnormal
     assert np.any((ex == 0) & (sm == 0x80))              # -0
+
+
+def test_fp16_exact_rate_and_specials():
+    """fp16 iterates: the exact mask moves the exponent of masked normal values
+    by one (5-bit field), and the special classes land on the fp16 fields."""
+    specs = W.olmoe_expert_specs()
+    cfg = W.PairConfig("t-fp16", dtype=torch.float16, frac=0.01)
+    w0, w1 = W.weight_pair(specs, 0, cfg)
+    assert w0.dtype == torch.float16
+    u0 = w0.reshape(-1).view(torch.int16).numpy().view(np.uint16)
+    u1 = w1.reshape(-1).view(torch.int16).numpy().view(np.uint16)
+    e0, e1 = O.exponent_field(u0, O.FP16).astype(int), O.exponent_field(u1, O.FP16).astype(int)
+    normal = (e0 > 1) & (e0 < 30)
+    moved = e0 != e1
+    assert np.all(np.abs(e0 - e1)[moved & normal] == 1)
+    n = u0.size
+    assert abs(moved.mean() - 0.01) < 5 * np.sqrt(0.01 * 0.99 / n) + 0.004   # fp16 subnormal tail
+    s = W.inject_specials(w0, 0.05, 3).reshape(-1).view(torch.int16).numpy().view(np.uint16)
+    ex = O.exponent_field(s, O.FP16)
+    m = O.sign_mantissa_field(s, O.FP16) & 0x3FF
+    assert np.any((ex == 31) & (m == 0)) and np.any((ex == 31) & (m != 0))
+    assert np.any((ex == 0) & (m != 0)) and np.any(s == 0x8000)
