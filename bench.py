@@ -3,7 +3,8 @@
 
 Workload: a full OLMoE-shaped MoE layer in bf16 -- 64 experts x (2048x1024,
 2048x1024, 1024x2048) = 402,653,184 weights -- row-sharded over 16 ranks, with
-1% of exponents changing per iteration (uniform; --clustered for 4 KiB runs).
+1% of exponents changing per iteration (uniform; --clustered for 4 KiB runs;
+--dtype fp16 / fp32 for the same layer in those formats).
 
 One step is one iteration of the hot path as one rank runs it:
   plan    -- ciera_plan for all 192 tensors (host);
@@ -36,6 +37,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor peak
+# --dtype -> (torch dtype name, bytes per value, same-width integer type name)
+DTYPES = {"bf16": ("bfloat16", 2, "int16"), "fp16": ("float16", 2, "int16"), "fp32": ("float32", 4, "int32")}
+
+
+def workload_name(args):
+    return f"olmoe_moe_layer_{args.dtype}_" + ("clustered" if args.clustered else "uniform")
 
 
 def log(*a):
@@ -49,6 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--frac", type=float, default=0.01)
     ap.add_argument("--clustered", action="store_true")
+    ap.add_argument("--dtype", choices=sorted(DTYPES), default="bf16")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -111,7 +119,8 @@ def main():
         f"decode avg {dec_avg * 1e3:.1f} us (p10 {dec_ms[len(dec_ms) // 10] * 1e3:.1f}, "
         f"p90 {dec_ms[9 * len(dec_ms) // 10] * 1e3:.1f})")
 
-    logical = 2 * n_enc + 2 * N
+    E = wl["E"]
+    logical = E * n_enc + E * N
     value = logical / (ms_step * 1e-3) / 1e9
     dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
     enc_gbps = enc_bytes / (enc_avg * 1e-3) / 1e9
@@ -125,15 +134,16 @@ def main():
     if os.path.exists(tf):
         t = json.load(open(tf))
         if t.get("kernel_source_sha256") == sha and t.get("workload") == "olmoe_layer_bf16_1pct_uniform" \
-                and not args.clustered and wl["ppm"] == 10000:
+                and not args.clustered and wl["ppm"] == 10000 and args.dtype == "bf16":
             traffic = t.get("hbm_bytes_per_launch")
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(specs, w0, w1, wl["world"], wl["block"], A, args.cpu_seconds)
+        cpu = cpu_baseline(specs, w0, w1, wl["world"], wl["block"], A, args.cpu_seconds, args.dtype)
 
     out = {
-        "metric": "encode/decode GB/s (bf16 OLMoE MoE layer, 1% exp change) and % of HBM peak",
+        "metric": f"encode/decode GB/s ({args.dtype} OLMoE MoE layer, {args.frac * 100:g}% exp change) "
+                  "and % of HBM peak",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -143,23 +153,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u16",
+        "dtype": "u32" if E == 4 else "u16",
         "data": "synthetic",
-        "config": {"workload": "olmoe_moe_layer_bf16_" + ("clustered" if args.clustered else "uniform"),
+        "config": {"workload": workload_name(args),
                    "experts": 64, "tensors": len(specs), "elements": N, "world": wl["world"],
                    "block_size": wl["block"], "change_frac": args.frac,
                    "step": "plan(192) + encode(rank 0 shard) + decode(full layer, 16 streams)"},
         "encode": {"avg_us": round(enc_avg * 1e3, 2), "elements": n_enc,
-                   "logical_GBps": round(2 * n_enc / (enc_avg * 1e-3) / 1e9, 1),
+                   "logical_GBps": round(E * n_enc / (enc_avg * 1e-3) / 1e9, 1),
                    "algorithmic_bytes": enc_bytes, "achieved_GBps": round(enc_gbps, 1),
                    "hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4)},
         "decode": {"avg_us": round(dec_avg * 1e3, 2), "elements": N,
-                   "logical_GBps": round(2 * N / (dec_avg * 1e-3) / 1e9, 1),
+                   "logical_GBps": round(E * N / (dec_avg * 1e-3) / 1e9, 1),
                    "algorithmic_bytes": dec_bytes, "achieved_GBps": round(dec_gbps, 1),
                    "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4)},
         "compression_ratio": round(wl["raw_bytes"] / wl["stream_bytes"], 4),
         "changed_exponents": wl["P_total"],
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel<bf16,2>",
+        "roofline": {"bound": "hbm", "kernel": f"decode_kernel<{args.dtype},2>",
                      "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
@@ -179,8 +189,10 @@ def setup(args):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     specs = W.olmoe_layer_specs()
-    cfg = W.PairConfig(f"bench-{args.frac}-{'c' if args.clustered else 'u'}", frac=args.frac,
-                       clustered=args.clustered)
+    tname, E, iname = DTYPES[args.dtype]
+    tdt, idt = getattr(torch, tname), getattr(torch, iname)
+    tag = f"bench-{args.frac}-{'c' if args.clustered else 'u'}" + ("" if args.dtype == "bf16" else "-" + args.dtype)
+    cfg = W.PairConfig(tag, dtype=tdt, frac=args.frac, clustered=args.clustered)
     world, block = 16, 512
     shapes = [(s.rows, s.cols) for s in specs]
     N = sum(s.numel for s in specs)
@@ -197,8 +209,8 @@ def setup(args):
     torch.cuda.synchronize()
     log(f"generated {N} weights in {time.time() - t0:.1f}s")
 
-    A = LayerCodec(shapes, torch.bfloat16, world, block, dev, ppm)
-    Bc = LayerCodec(shapes, torch.bfloat16, world, block, dev, ppm, cache=A.cache)
+    A = LayerCodec(shapes, tdt, world, block, dev, ppm)
+    Bc = LayerCodec(shapes, tdt, world, block, dev, ppm, cache=A.cache)
 
     def shards(ws, r):
         out = []
@@ -218,8 +230,8 @@ def setup(args):
     torch.cuda.synchronize()
     assert stA.item() == 0 and stB.item() == 0, "decode reported corrupt streams"
     for i in range(len(specs)):
-        assert torch.equal(A.out_view(i).view(torch.int16), w1[i].reshape(-1).view(torch.int16)), i
-        assert torch.equal(Bc.out_view(i).view(torch.int16), w0[i].reshape(-1).view(torch.int16)), i
+        assert torch.equal(A.out_view(i).view(idt), w1[i].reshape(-1).view(idt)), i
+        assert torch.equal(Bc.out_view(i).view(idt), w0[i].reshape(-1).view(idt)), i
     log("setup round trip W0 -> W1 -> W0 bit-exact")
 
     # stream accounting from the headers (state A; B moves the same positions)
@@ -234,13 +246,13 @@ def setup(args):
     hA = headers(A)
     P_total = int(hA["n_changed"].sum())
     stream_bytes = int(hA["total_len"].sum())
-    raw_bytes = int((64 + 2 * hA["n"]).sum())
+    raw_bytes = int((64 + E * hA["n"]).sum())
     r0 = [i * world for i in range(len(specs))]  # rank-0 rows in header order
     enc_stream_bytes = int(hA["total_len"][r0].sum())
     n_enc = int(hA["n"][r0].sum())
     assert int(hA["n"].sum()) == N
-    dec_bytes = stream_bytes + N + 2 * N + P_total          # read streams + cache, write values + changed cache
-    enc_bytes = 2 * n_enc + n_enc + enc_stream_bytes       # read shard + cache slice, write streams
+    dec_bytes = stream_bytes + N + E * N + P_total         # read streams + cache, write values + changed cache
+    enc_bytes = E * n_enc + n_enc + enc_stream_bytes       # read shard + cache slice, write streams
     log(f"P={P_total} ({P_total / N:.4%}), streams {stream_bytes} B vs raw {raw_bytes} B "
         f"(ratio {raw_bytes / stream_bytes:.4f}), COMPRESSED streams {int((hA['mode'] == 1).sum())}/{len(hA['mode'])}")
 
@@ -270,9 +282,9 @@ def setup(args):
         last = A if last_k % 2 == 0 else Bc
         want = w1 if last is A else w0
         for i in range(0, len(specs), 17):
-            assert torch.equal(last.out_view(i).view(torch.int16), want[i].reshape(-1).view(torch.int16)), i
+            assert torch.equal(last.out_view(i).view(idt), want[i].reshape(-1).view(idt)), i
 
-    return dict(specs=specs, A=A, Bc=Bc, w0=w0, w1=w1, N=N, n_enc=n_enc, world=world, block=block,
+    return dict(specs=specs, A=A, Bc=Bc, w0=w0, w1=w1, N=N, n_enc=n_enc, world=world, block=block, E=E,
                 ppm=ppm, step=step, check=check, dec_bytes=dec_bytes, enc_bytes=enc_bytes,
                 raw_bytes=raw_bytes, stream_bytes=stream_bytes, P_total=P_total)
 
@@ -330,7 +342,7 @@ def overlap(args):
         "metric": "share of the codec step hidden behind a concurrent bf16 GEMM",
         "value": round(hidden, 4), "unit": "fraction", "higher_is_better": True, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "dtype": "u16+bf16", "data": "synthetic",
-        "config": {"workload": "olmoe_moe_layer_bf16_" + ("clustered" if args.clustered else "uniform"),
+        "config": {"workload": workload_name(args),
                    "change_frac": args.frac, "gemm_mnk": [M, Nn, K],
                    "streams": "GEMM on one stream, step on a second stream (default priorities)"},
         "gemm": dict(res["gemm"], tflops=round(flops / (tg * 1e-6) / 1e12, 1)),
@@ -340,7 +352,7 @@ def overlap(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(specs, w0, w1, world, block, codec, budget_s):
+def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16"):
     """The oracle, as it stands, on a bounded sample of the same workload:
     for whole tensors in layer order, encode rank 0's shard and decode the
     full tensor from all 16 streams, until the CPU time budget is spent.  Its
@@ -350,7 +362,12 @@ def cpu_baseline(specs, w0, w1, world, block, codec, budget_s):
 
     from oracle import ciera_oracle as O
 
+    odt = {"bf16": O.BF16, "fp16": O.FP16, "fp32": O.FP32}[dtype]
+    E = O.elem_bytes(odt)
+
     def bits(t):
+        if E == 4:
+            return t.reshape(-1).view(torch.int32).cpu().numpy().view(np.uint32)
         return t.reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16)
 
     t_enc = t_dec = 0.0
@@ -358,26 +375,26 @@ def cpu_baseline(specs, w0, w1, world, block, codec, budget_s):
     done = 0
     for i, s in enumerate(specs):
         x0, x1 = bits(w0[i]), bits(w1[i])
-        cache = O.cache_update(x0, O.BF16)
+        cache = O.cache_update(x0, odt)
         streams = []
         for r in range(world):
             off, n = O.shard(s.rows, s.cols, world, r)
             if r == 0:
                 t = time.perf_counter()
-            st = O.encode(x1[off:off + n], cache[off:off + n], O.BF16, block, bool(codec.plans[i].compress),
+            st = O.encode(x1[off:off + n], cache[off:off + n], odt, block, bool(codec.plans[i].compress),
                           off, r, world)
             if r == 0:
                 t_enc += time.perf_counter() - t
                 gpu = codec.slot(i, 0)[:st.size].cpu().numpy()
                 if not np.array_equal(gpu, st):
                     raise RuntimeError(f"GPU stream of tensor {i} rank 0 differs from the oracle")
-                logical += 2 * n
+                logical += E * n
             streams.append(st)
         t = time.perf_counter()
-        out, new_cache, status = O.decode(streams, s.rows, s.cols, O.BF16, block, world, cache)
+        out, new_cache, status = O.decode(streams, s.rows, s.cols, odt, block, world, cache)
         t_dec += time.perf_counter() - t
         assert status == 0 and np.array_equal(out, x1)
-        logical += 2 * s.numel
+        logical += E * s.numel
         done += 1
         if t_enc + t_dec >= budget_s:
             break
