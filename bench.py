@@ -16,8 +16,8 @@ between two states so that every step sees exactly the configured change rate:
 state A encodes W1 against the cache of W0 (decode leaves the cache at W1),
 state B encodes W0 against the cache of W1 (decode leaves it at W0).
 
-Prints one JSON line (see the keys below).  --gpus above 1 is refused: this
-build runs on one GPU.
+Prints one JSON line (see the keys below).  --gpus above 1 is refused: the
+collective between GPUs is not part of this library, so it runs on one GPU.
 
 --overlap measures instead how much of one step hides behind a concurrent bf16
 GEMM (the compute a rank runs while the next layer's weights are encoded,
@@ -85,7 +85,7 @@ def main():
     if args.copy_calibration:
         return copy_calibration()
     if args.gpus != 1:
-        log("bench.py runs on one GPU only: the collective is outside this build; "
+        log("bench.py runs on one GPU only: the collective between GPUs is not part of this library; "
             "run with --gpus 1")
         sys.exit(2)
     if args.overlap:
