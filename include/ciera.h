@@ -33,7 +33,8 @@
  *
  * Sharding: a tensor of rows x cols (row-major; a 1-D vector is rows=len,
  * cols=1) is split over W ranks by rows; rank r holds floor(R/W) + [r < R%W]
- * consecutive rows (ZeRO-style even partition).
+ * consecutive rows (ZeRO-style even partition).  Patch indices are u32, so a
+ * shard holds fewer than 2^32 values (larger shards: CIERA_ERR_UNSUPPORTED).
  *
  * Conventions for every device call:
  *   - all pointers are device pointers of the current HIP device unless noted;

@@ -52,6 +52,10 @@ ciera_status_t check_tensor(const ciera_tensor_t* t) {
   if (t->world == 0) return CIERA_ERR_INVALID_ARG;
   if (t->rows >= kMaxElems || t->cols >= kMaxElems) return CIERA_ERR_UNSUPPORTED;
   if ((u128)t->rows * t->cols >= kMaxElems) return CIERA_ERR_UNSUPPORTED;
+  // patch records carry u32 shard-local indices: the largest shard (rank 0's)
+  // must hold fewer than 2^32 values
+  const uint64_t rows0 = t->rows / t->world + (t->rows % t->world ? 1 : 0);
+  if ((u128)rows0 * t->cols >= ((u128)1 << 32)) return CIERA_ERR_UNSUPPORTED;
   return CIERA_OK;
 }
 

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ciera.h"
@@ -1026,8 +1027,12 @@ __global__ __launch_bounds__(kThreads) void cache_update_kernel(const uint8_t* _
 // Each launcher clears the thread's last-error state first, so that the error it
 // returns is the launch's own and not one left by an unrelated earlier call.
 
-hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
-                         uint32_t batch_id, hipStream_t s) {
+// Workgroups per launch: a grid stays well below 2^32 work-items; larger
+// batches are cut into launches of whole items.
+constexpr uint64_t kMaxGrid = (uint64_t)1 << 22;
+
+static hipError_t launch_encode_part(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
+                                     uint32_t batch_id, hipStream_t s) {
   (void)hipGetLastError();
   const dim3 grid(nitems * a.tpi), block(kThreads);
 #define CIERA_ENC(DT, S) hipLaunchKernelGGL((encode_kernel<DT, S>), grid, block, 0, s, a, ctl, batch_id)
@@ -1062,6 +1067,18 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
   return hipGetLastError();
 }
 
+hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
+                         uint32_t batch_id, hipStream_t s) {
+  const uint32_t per = (uint32_t)std::max<uint64_t>(1, kMaxGrid / a.tpi);
+  for (uint32_t i = 0; i < nitems; i += per) {
+    EncArgs c = a;
+    c.item0 = a.item0 + i;
+    c.status = a.status + (uint64_t)i * a.tpi;  // status words are indexed from the group's first item
+    if (hipError_t e = launch_encode_part(dtype, sub, std::min(per, nitems - i), c, ctl, batch_id, s)) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, uint32_t wg_per_item, const uint32_t* raw_flag,
                                const uint32_t* any_raw, uint32_t tag, uint32_t batch_id, hipStream_t s) {
   (void)hipGetLastError();
@@ -1071,9 +1088,9 @@ hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, uint32_t wg
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems, uint32_t tpr,
-                         uint32_t world, uint32_t* status, const uint32_t* ctl, uint32_t batch_id,
-                         hipStream_t s) {
+static hipError_t launch_decode_part(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
+                                     uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,
+                                     uint32_t batch_id, hipStream_t s) {
   (void)hipGetLastError();
   const dim3 grid(nitems * tpr * world), block(kDecThreads);
 #define CIERA_DEC(DT, U) \
@@ -1104,6 +1121,20 @@ hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0,
   }
 #undef CIERA_DEC
   return hipGetLastError();
+}
+
+hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems, uint32_t tpr,
+                         uint32_t world, uint32_t* status, const uint32_t* ctl, uint32_t batch_id,
+                         hipStream_t s) {
+  const uint64_t tpi = (uint64_t)tpr * world;
+  if (tpi * kDecThreads >= ((uint64_t)1 << 32)) return hipErrorInvalidValue;  // one item alone too large
+  const uint32_t per = (uint32_t)std::max<uint64_t>(1, kMaxGrid / tpi);
+  for (uint32_t i = 0; i < nitems; i += per) {
+    if (hipError_t e = launch_decode_part(dtype, u, items, item0 + i, std::min(per, nitems - i), tpr, world, status,
+                                          ctl, batch_id, s))
+      return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n, hipStream_t s) {

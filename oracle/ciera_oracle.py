@@ -247,6 +247,8 @@ def encode(x: np.ndarray, cache_slice: np.ndarray, dtype: int, block_size: int,
     n = x.size
     if cache_slice.size != n:
         raise ValueError("cache slice and shard differ in length")
+    if n >= 1 << 32:
+        raise ValueError("a shard holds fewer than 2^32 values (u32 patch indices)")
     # 1. split
     ex = exponent_field(x, dtype)
     sm = sign_mantissa_field(x, dtype)

@@ -95,6 +95,13 @@ def test_argument_errors_are_synchronous():
         assert e.value.code == 1
     with pytest.raises(L.CieraError):
         L.ciera_plan(L.Tensor(4, 4, 1, 512, 1), 1_000_001)
+    # u32 patch indices: the largest shard must hold fewer than 2^32 values
+    for t in (L.Tensor(1 << 20, 1 << 12, 1, 512, 1), L.Tensor((1 << 21) + 1, 1 << 12, 1, 512, 2)):
+        with pytest.raises(L.CieraError) as e:
+            L.ciera_plan(t, 100)
+        assert e.value.code == 3
+    assert L.ciera_plan(L.Tensor((1 << 20) - 1, 1 << 12, 1, 512, 1), 100).raw_stream_bytes == \
+        64 + 2 * ((1 << 20) - 1) * (1 << 12)
     with pytest.raises(L.CieraError) as e:
         L.ciera_shard(L.Tensor(4, 4, 1, 512, 2), 2)
     assert e.value.code == 1
