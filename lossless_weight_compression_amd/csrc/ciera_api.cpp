@@ -345,6 +345,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
   b->tag_base = next_id();
   std::vector<uint8_t> blob(pl.upload, 0);
   reinterpret_cast<uint32_t*>(blob.data())[0] = b->batch_id;
+  reinterpret_cast<uint32_t*>(blob.data())[kCtlEpoch] = 1u + b->tag_base % 0x3FFFFFFEu;  // first launch's tag
   EncItem* di = reinterpret_cast<EncItem*>(blob.data() + pl.off_items);
   uint32_t any = 0;
   uint64_t max_bytes = 0;  // largest shard that may need the RAW rewrite
@@ -391,7 +392,6 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
   if (b->magic != kEncMagic) return CIERA_ERR_INVALID_ARG;
   if (b->count == 0) return CIERA_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t tag = 1u + (b->tag_base + b->launches) % 0x3FFFFFFEu;
   uint32_t* ctl = reinterpret_cast<uint32_t*>(b->scratch);
   const EncItem* items = reinterpret_cast<const EncItem*>(b->scratch + b->off_items);
   uint32_t* flags = reinterpret_cast<uint32_t*>(b->scratch + b->off_flags);
@@ -402,8 +402,6 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
     a.item0 = g.item0;
     a.tpi = g.tpi;
     a.ctr = reinterpret_cast<uint32_t*>(b->scratch + b->off_ctr);
-    a.launch = b->launches;
-    a.tag = tag;
     a.status = reinterpret_cast<uint64_t*>(b->scratch + g.status_off);
     a.raw_flag = flags;
     a.any_raw = ctl + 1;
@@ -412,11 +410,10 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
       return device_error("encode launch", e);
     }
   }
-  if (b->any_compress) {
-    if (hipError_t e = launch_encode_fixup(items, b->count, b->fix_wg, flags, ctl + 1, tag, b->batch_id, st)) {
-      b->magic = 0;
-      return device_error("encode fallback launch", e);
-    }
+  // always: besides the RAW rewrite it advances the device-side epoch
+  if (hipError_t e = launch_encode_fixup(items, b->count, b->fix_wg, flags, ctl, b->batch_id, st)) {
+    b->magic = 0;
+    return device_error("encode fallback launch", e);
   }
   b->launches += 1;
   return CIERA_OK;

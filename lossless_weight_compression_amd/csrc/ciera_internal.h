@@ -52,18 +52,21 @@ struct DecItem {
 };
 
 // Encode scratch layout (offsets in bytes from the scratch base):
-//   ctl      : u32 [batch id, any_raw, error] (+ padding to 256 B)
+//   ctl      : u32 [batch id, any_raw, error, epoch, tag] (+ padding to 256 B);
+//              epoch is the tag of the next launch and lives on the device (the
+//              fallback kernel advances it), tag is the running launch's, so a
+//              launch's kernel arguments never change and it can be replayed
+//              from a captured graph
 //   raw_flag : u32 per item -- equals the launch tag if the item must be rewritten RAW
-//   ctr      : u32 per item -- dynamic tile counter, grows by tiles-per-item per launch
+//   ctr      : u32 per item -- dynamic tile counter, back at 0 after every launch
 //   items    : EncItem per item, ordered by group
 //   status   : u64 per tile, look-back words tagged with the launch tag
+constexpr int kCtlAnyRaw = 1, kCtlError = 2, kCtlEpoch = 3, kCtlTag = 4;
 struct EncArgs {
   const EncItem* items;
   uint32_t item0;      // first item of the group
   uint32_t tpi;        // tiles per item in the group
   uint32_t* ctr;       // per-item counters (indexed by absolute item)
-  uint32_t launch;     // launches of this batch so far
-  uint32_t tag;        // launch tag, never 0
   uint64_t* status;    // group's status words, (item - item0) * tpi + tile
   uint32_t* raw_flag;  // per absolute item
   uint32_t* any_raw;
@@ -75,7 +78,7 @@ struct EncArgs {
 hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
                          uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, uint32_t wg_per_item, const uint32_t* raw_flag,
-                               const uint32_t* any_raw, uint32_t tag, uint32_t batch_id, hipStream_t s);
+                               uint32_t* ctl, uint32_t batch_id, hipStream_t s);
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
                          uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,
                          uint32_t batch_id, hipStream_t s);

@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   constexpr int E = Tr<DT>::E;
   constexpr uint32_t T = (uint32_t)kSub * S;
   constexpr int XW = 4 * E;  // words of 16 raw values
-  __shared__ uint32_t s_local, s_excl;
+  __shared__ uint32_t s_local, s_excl, s_tag;
   __shared__ uint32_t s_wtot[4 * S];
   __shared__ uint32_t s_bm[2 * S];  // one bit per block of the tile: T/B <= T/64 = 64*S bits
 
@@ -494,13 +494,19 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   const uint32_t item = a.item0 + blockIdx.x / a.tpi;
   const EncItem d = a.items[item];
   if (d.batch_id != batch_id) return;  // the scratch holds another batch (uniform)
-  if (tid == 0)
-    s_local = __hip_atomic_fetch_add(gp(a.ctr + item), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-              a.launch * a.tpi;
+  if (tid == 0) {
+    const uint32_t got = __hip_atomic_fetch_add(gp(a.ctr + item), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the item's last tile to take an id: every tile has taken one, so the
+    // counter goes back to 0 for the next launch
+    if (got == a.tpi - 1) __hip_atomic_store(gp(a.ctr + item), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_local = got;
+    s_tag = *gp(ctl + kCtlEpoch);  // written before this launch, fixed during it
+  }
   if (tid < 2 * S) s_bm[tid] = 0;
   __syncthreads();
-  const uint32_t local = s_local;
+  const uint32_t local = s_local, tag = s_tag;
   if (local >= a.tpi) return;  // uniform; cannot happen while counters match launches
+  if (local == 0 && tid == 0) *gp(ctl + kCtlTag) = tag;  // for the fallback kernel
   const uint64_t base = (uint64_t)local * T;
   const uint64_t n = d.n;
   const uint32_t B = d.block_size;
@@ -603,11 +609,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   if (wave == 0) {
     uint32_t excl = 0;
     if (local == 0) {
-      if (lane == 0) publish(sw, pack_status(kFlagIncl, a.tag, agg));
+      if (lane == 0) publish(sw, pack_status(kFlagIncl, tag, agg));
     } else {
-      if (lane == 0) publish(sw + local, pack_status(kFlagAgg, a.tag, agg));
-      excl = look_back(sw, local, a.tag, ctl + 2);
-      if (lane == 0) publish(sw + local, pack_status(kFlagIncl, a.tag, excl + agg));
+      if (lane == 0) publish(sw + local, pack_status(kFlagAgg, tag, agg));
+      excl = look_back(sw, local, tag, ctl + kCtlError);
+      if (lane == 0) publish(sw + local, pack_status(kFlagIncl, tag, excl + agg));
     }
     if (lane == 0) s_excl = excl;
   }
@@ -653,8 +659,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
     const uint64_t raw = kHeader + n * E;
     const bool cmode = compress && comp < raw;
     if (compress && !cmode) {
-      gp(a.raw_flag)[item] = a.tag;
-      *gp(a.any_raw) = a.tag;
+      gp(a.raw_flag)[item] = tag;
+      *gp(a.any_raw) = tag;
     }
     uint32_t h[16];
     h[0] = 0x52454943u;  // "CIER"
@@ -679,11 +685,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
 
 // Rewrites as RAW the streams whose COMPRESSED form turned out not shorter:
 // gridDim.x workgroups per item, items along y.  Returns at once when the
-// launch flagged no item (the common case).
+// launch flagged no item (the common case).  It runs after every encode launch
+// and advances the epoch: the next launch's tag.
 __global__ __launch_bounds__(kThreads) void encode_fixup_kernel(const EncItem* __restrict__ items, uint32_t count,
-                                                                const uint32_t* raw_flag, const uint32_t* any_raw,
-                                                                uint32_t tag, uint32_t batch_id) {
-  if (*gp(any_raw) != tag) return;
+                                                                const uint32_t* raw_flag, uint32_t* ctl,
+                                                                uint32_t batch_id) {
+  const uint32_t tag = *gp(ctl + kCtlTag);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    *gp(ctl + kCtlEpoch) = 1u + tag % 0x3FFFFFFEu;  // never 0; no other block reads the epoch
+  if (*gp(ctl + kCtlAnyRaw) != tag) return;
   const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
   for (uint32_t k = blockIdx.y; k < count; k += gridDim.y) {
@@ -1080,11 +1090,11 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
 }
 
 hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, uint32_t wg_per_item, const uint32_t* raw_flag,
-                               const uint32_t* any_raw, uint32_t tag, uint32_t batch_id, hipStream_t s) {
+                               uint32_t* ctl, uint32_t batch_id, hipStream_t s) {
   (void)hipGetLastError();
   if (count == 0 || wg_per_item == 0) return hipSuccess;
   const dim3 grid(wg_per_item, count < 65535u ? count : 65535u), block(kThreads);
-  hipLaunchKernelGGL(encode_fixup_kernel, grid, block, 0, s, items, count, raw_flag, any_raw, tag, batch_id);
+  hipLaunchKernelGGL(encode_fixup_kernel, grid, block, 0, s, items, count, raw_flag, ctl, batch_id);
   return hipGetLastError();
 }
 
