@@ -137,7 +137,7 @@ struct Group {
   uint32_t tpi;          // encode: tiles per item
   uint32_t tpr, world;   // decode: tiles per rank, world
   uint32_t pad;
-  uint64_t status_off;   // encode: byte offset of the group's look-back words
+  uint64_t tile0;        // encode: the group's first tile in the batch's count array
 };
 struct BatchImpl {
   uint64_t magic;
@@ -145,10 +145,10 @@ struct BatchImpl {
   uint64_t scratch_bytes;
   uint32_t* status_dev;
   uint32_t count, ngroups;
-  uint32_t batch_id, tag_base;
+  uint32_t batch_id, reserved0;
   uint32_t launches, any_compress;
-  uint32_t fix_wg, reserved;  // fallback rewrite: workgroups per item
-  uint64_t off_flags, off_ctr, off_items;
+  uint32_t fin_wg, reserved1;  // encode finishing kernel: workgroups per item
+  uint64_t off_counts, off_stash, off_items;
   Group g[kMaxGroups];
 };
 static_assert(sizeof(BatchImpl) <= sizeof(ciera_batch_t), "batch handle too small");
@@ -164,10 +164,15 @@ uint32_t enc_sub(uint32_t B, uint64_t n) {
 }
 uint32_t dec_unit(uint64_t n0) { return n0 > (uint64_t)kDecRow ? 2u : 1u; }
 
+// A tile's stash holds up to T/8 changes (12.5% of its values); a tile with
+// more has them derived again by the finishing kernel.
+constexpr uint32_t kStashDiv = 8;
+
 struct EncPlan {
   std::vector<uint32_t> order;  // items in group order
   std::vector<Group> groups;
-  uint64_t off_flags = 0, off_ctr = 0, off_items = 0, upload = 0, total = 0;
+  std::vector<uint64_t> tile0, stash;  // per item in group order
+  uint64_t off_items = 0, off_counts = 0, off_stash = 0, upload = 0, total = 0;
 };
 
 ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncPlan* pl) {
@@ -187,7 +192,7 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     by[std::make_tuple(it.t.dtype, S, (uint32_t)tpi)].push_back(i);
   }
   if (by.size() > (size_t)kMaxGroups) return CIERA_ERR_UNSUPPORTED;
-  uint64_t tiles = 0;
+  uint64_t tiles = 0, words = 0;
   for (auto& kv : by) {
     Group g{};
     g.dtype = std::get<0>(kv.first);
@@ -196,18 +201,22 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     g.item0 = (uint32_t)pl->order.size();
     g.nitems = (uint32_t)kv.second.size();
     if ((uint64_t)g.nitems * g.tpi >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
-    g.status_off = tiles;  // in words for now
-    tiles += (uint64_t)g.nitems * g.tpi;
+    g.tile0 = tiles;
+    const uint64_t cap = (uint64_t)kSub * g.unit / kStashDiv;
+    for (uint32_t k = 0; k < g.nitems; ++k) {
+      pl->tile0.push_back(tiles);
+      pl->stash.push_back(words);
+      tiles += g.tpi;
+      words += g.tpi * cap;
+    }
     pl->order.insert(pl->order.end(), kv.second.begin(), kv.second.end());
     pl->groups.push_back(g);
   }
-  pl->off_flags = 256;
-  pl->off_ctr = align_up(pl->off_flags + 4ull * count, 64);
-  pl->off_items = align_up(pl->off_ctr + 4ull * count, 64);
+  pl->off_items = 256;
   pl->upload = pl->off_items + sizeof(EncItem) * (uint64_t)count;
-  const uint64_t st = align_up(pl->upload, 256);
-  for (Group& g : pl->groups) g.status_off = st + 8 * g.status_off;
-  pl->total = align_up(st + 8 * tiles, 256);
+  pl->off_counts = align_up(pl->upload, 256);
+  pl->off_stash = align_up(pl->off_counts + 4 * tiles, 256);
+  pl->total = align_up(pl->off_stash + 4 * words, 256);
   return CIERA_OK;
 }
 
@@ -342,10 +351,8 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
   }
   BatchImpl* b = impl(batch);
   b->batch_id = next_id();
-  b->tag_base = next_id();
   std::vector<uint8_t> blob(pl.upload, 0);
   reinterpret_cast<uint32_t*>(blob.data())[0] = b->batch_id;
-  reinterpret_cast<uint32_t*>(blob.data())[kCtlEpoch] = 1u + b->tag_base % 0x3FFFFFFEu;  // first launch's tag
   EncItem* di = reinterpret_cast<EncItem*>(blob.data() + pl.off_items);
   uint32_t any = 0;
   uint64_t max_bytes = 0;  // largest shard that may need the RAW rewrite
@@ -360,6 +367,12 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     d.n = n;
     d.off = off;
     d.capacity = it.stream_capacity;
+    const uint32_t S = enc_sub(it.t.block_size, n);
+    d.tile0 = pl.tile0[j];
+    d.stash = pl.stash[j];
+    d.tvals = (uint32_t)kSub * S;
+    d.tpi = (uint32_t)std::max<uint64_t>(1, (n + d.tvals - 1) / d.tvals);
+    d.cap = d.tvals / kStashDiv;
     d.rank = it.rank;
     d.world = it.t.world;
     d.block_size = it.t.block_size;
@@ -378,9 +391,9 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
   b->count = count;
   b->ngroups = (uint32_t)pl.groups.size();
   b->any_compress = any;
-  b->fix_wg = (uint32_t)std::min<uint64_t>(64, std::max<uint64_t>(1, (max_bytes + 65535) / 65536));
-  b->off_flags = pl.off_flags;
-  b->off_ctr = pl.off_ctr;
+  b->fin_wg = (uint32_t)std::min<uint64_t>(64, std::max<uint64_t>(1, (max_bytes + 65535) / 65536));
+  b->off_counts = pl.off_counts;
+  b->off_stash = pl.off_stash;
   b->off_items = pl.off_items;
   for (size_t g = 0; g < pl.groups.size(); ++g) b->g[g] = pl.groups[g];
   return CIERA_OK;
@@ -392,28 +405,30 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
   if (b->magic != kEncMagic) return CIERA_ERR_INVALID_ARG;
   if (b->count == 0) return CIERA_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* ctl = reinterpret_cast<uint32_t*>(b->scratch);
   const EncItem* items = reinterpret_cast<const EncItem*>(b->scratch + b->off_items);
-  uint32_t* flags = reinterpret_cast<uint32_t*>(b->scratch + b->off_flags);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(b->scratch + b->off_counts);
+  uint32_t* stash = reinterpret_cast<uint32_t*>(b->scratch + b->off_stash);
   for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
     const Group& g = b->g[gi];
     EncArgs a;
     a.items = items;
     a.item0 = g.item0;
     a.tpi = g.tpi;
-    a.ctr = reinterpret_cast<uint32_t*>(b->scratch + b->off_ctr);
-    a.status = reinterpret_cast<uint64_t*>(b->scratch + g.status_off);
-    a.raw_flag = flags;
-    a.any_raw = ctl + 1;
-    if (hipError_t e = launch_encode(g.dtype, g.unit, g.nitems, a, ctl, b->batch_id, st)) {
-      b->magic = 0;  // counters may be out of step now: the batch must be prepared again
+    a.counts = counts;
+    a.stash = stash;
+    if (hipError_t e = launch_encode(g.dtype, g.unit, g.nitems, a, b->batch_id, st))
       return device_error("encode launch", e);
-    }
   }
-  // always: besides the RAW rewrite it advances the device-side epoch
-  if (hipError_t e = launch_encode_fixup(items, b->count, b->fix_wg, flags, ctl, b->batch_id, st)) {
-    b->magic = 0;
-    return device_error("encode fallback launch", e);
+  // one finishing launch per dtype: groups are ordered by dtype first, so the
+  // items of one dtype are contiguous
+  for (uint32_t gi = 0; gi < b->ngroups;) {
+    uint32_t gj = gi;
+    uint32_t nitems = 0;
+    while (gj < b->ngroups && b->g[gj].dtype == b->g[gi].dtype) nitems += b->g[gj++].nitems;
+    if (hipError_t e = launch_encode_finish(b->g[gi].dtype, items, b->g[gi].item0, nitems, b->fin_wg, counts, stash,
+                                            b->batch_id, st))
+      return device_error("encode finish launch", e);
+    gi = gj;
   }
   b->launches += 1;
   return CIERA_OK;

@@ -28,13 +28,17 @@ struct EncItem {
   uint64_t n;
   uint64_t off;
   uint64_t capacity;
+  uint64_t tile0;          // the item's first tile in the batch's per-tile count array
+  uint64_t stash;          // word offset of the item's first tile stash in the batch's stash array
+  uint32_t tpi;            // tiles of the item
+  uint32_t tvals;          // values per tile (a multiple of 4096)
+  uint32_t cap;            // records a tile stash holds
   uint32_t rank, world;
   uint32_t block_size;
   uint32_t compress;
   uint32_t cache_aligned;  // (cache_full + off) is 16-byte aligned
-  uint32_t elem_bytes;     // 2 (bf16) or 4 (fp32)
+  uint32_t elem_bytes;     // 2 (bf16, fp16) or 4 (fp32)
   uint32_t batch_id;       // the batch that wrote this descriptor
-  uint32_t pad;
 };
 
 // One decode item: a tensor and its W receive slots.
@@ -52,33 +56,26 @@ struct DecItem {
 };
 
 // Encode scratch layout (offsets in bytes from the scratch base):
-//   ctl      : u32 [batch id, any_raw, error, epoch, tag] (+ padding to 256 B);
-//              epoch is the tag of the next launch and lives on the device (the
-//              fallback kernel advances it), tag is the running launch's, so a
-//              launch's kernel arguments never change and it can be replayed
-//              from a captured graph
-//   raw_flag : u32 per item -- equals the launch tag if the item must be rewritten RAW
-//   ctr      : u32 per item -- dynamic tile counter, back at 0 after every launch
-//   items    : EncItem per item, ordered by group
-//   status   : u64 per tile, look-back words tagged with the launch tag
-constexpr int kCtlAnyRaw = 1, kCtlError = 2, kCtlEpoch = 3, kCtlTag = 4;
+//   ctl    : u32 [batch id] (+ padding to 256 B)
+//   items  : EncItem per item, ordered by group
+//   counts : u32 per tile -- changed values of the tile, written by the split kernel
+//   stash  : u32 x cap per tile -- the tile's first cap changes in ascending order,
+//            (value index in the tile) | exponent << 16; the finishing kernel moves
+//            them to their places in the stream
 struct EncArgs {
   const EncItem* items;
   uint32_t item0;      // first item of the group
   uint32_t tpi;        // tiles per item in the group
-  uint32_t* ctr;       // per-item counters (indexed by absolute item)
-  uint64_t* status;    // group's status words, (item - item0) * tpi + tile
-  uint32_t* raw_flag;  // per absolute item
-  uint32_t* any_raw;
+  uint32_t* counts;    // the batch's per-tile counts
+  uint32_t* stash;     // the batch's stash words
 };
 
 // ctl: the control words at the start of a batch's scratch.  Every descriptor
 // carries the id of the batch that wrote it; kernels exit at once when the
 // descriptor they read belongs to another batch (the scratch was taken over).
-hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
-                         uint32_t batch_id, hipStream_t s);
-hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, uint32_t wg_per_item, const uint32_t* raw_flag,
-                               uint32_t* ctl, uint32_t batch_id, hipStream_t s);
+hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t batch_id, hipStream_t s);
+hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0, uint32_t nitems, uint32_t wg_per_item,
+                                const uint32_t* counts, const uint32_t* stash, uint32_t batch_id, hipStream_t s);
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
                          uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,
                          uint32_t batch_id, hipStream_t s);

@@ -419,94 +419,134 @@ __device__ __forceinline__ void report(uint32_t* status, uint32_t bits) {
     __hip_atomic_fetch_or(gp(status), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ------------------------------------------------------- decoupled look-back
-// One 64-bit word per tile: [63:62] flag, [61:32] launch tag, [31:0] count.
-// Words of earlier launches carry another tag and read as "not ready", so the
-// array is never cleared.
-constexpr uint64_t kFlagAgg = 1, kFlagIncl = 2;
-constexpr uint32_t kSpinCap = 1u << 22;  // only reached if the scratch was tampered with
-
-__device__ __forceinline__ uint64_t pack_status(uint64_t flag, uint32_t tag, uint32_t v) {
-  return (flag << 62) | ((uint64_t)(tag & 0x3FFFFFFFu) << 32) | v;
-}
-__device__ __forceinline__ void publish(uint64_t* w, uint64_t val) {
-  __hip_atomic_store(gp(w), val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t peek(uint64_t* w) {
-  return __hip_atomic_load(gp(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Exclusive prefix of tile `local`'s count among the tiles of its item
-// (status words sw[0..local)).  Wave-wide.  Every tile read holds a smaller
-// dynamic id of the same item, so its workgroup is already running and its
-// word arrives; the spin cap only guards against a corrupted scratch.
-__device__ uint32_t look_back(uint64_t* sw, uint32_t local, uint32_t tag, uint32_t* err) {
-  const uint32_t lane = lane_id();
-  uint32_t excl = 0;
-  int64_t hi = (int64_t)local - 1;
-  while (true) {
-    const int64_t j = hi - (int64_t)lane;
-    const bool valid = j >= 0;
-    uint64_t w;
-    uint32_t spins = 0;
-    while (true) {
-      w = valid ? peek(sw + j) : pack_status(kFlagIncl, tag, 0u);
-      const bool ready = ((w >> 62) != 0) && (((uint32_t)(w >> 32) & 0x3FFFFFFFu) == (tag & 0x3FFFFFFFu));
-      if (__all(ready)) break;
-      if (++spins >= kSpinCap) {
-        if (lane == 0) __hip_atomic_fetch_or(gp(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        w = ready ? w : pack_status(kFlagIncl, tag, 0u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    const uint64_t incl = __ballot((w >> 62) == kFlagIncl);
-    uint32_t mine = (uint32_t)w;
-    if (incl) {
-      const uint32_t stop = (uint32_t)__ffsll((unsigned long long)incl) - 1u;  // nearest inclusive
-      if (lane > stop) mine = 0;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o);
-    excl += mine;
-    if (incl) break;
-    hi -= 64;
-  }
-  return excl;
-}
-
 // --------------------------------------------------------------------- encode
-// One workgroup per tile of S*4096 values of one item; items of a group share a
-// tile count, so the item is blockIdx / tpi and only the tile's place inside the
-// item is taken dynamically (per-item counter), which keeps the look-back free
-// of deadlock without a global hot counter.
+// Two kernels, and no workgroup ever waits on another.
+//
+// encode_kernel: one workgroup per tile of S*4096 values of one item.  Split,
+// compare, the sign|mantissa (or RAW) stores, the tile's bitmap bytes, its
+// change count, and its first `cap` changes as (index in tile, exponent) words
+// in the tile's stash in scratch.
+//
+// encode_finish_kernel: per item, the sum of its tile counts decides the mode;
+// the header is written, the stashed changes go to their places in the patch
+// list (a tile whose changes overflowed its stash derives them again from the
+// shard and the cache), or the stream is rewritten RAW when the compressed
+// form turned out not shorter.
+
+// Exponent bytes (four words) and change mask of one 16-value chunk, given its
+// raw value words xw and cached exponent words cw; only the cnt values present
+// count (all 16 when FULL).
+template <int DT, bool FULL>
+__device__ __forceinline__ uint32_t chunk_exps(const uint32_t* xw, const uint32_t cw[4], int cnt, uint32_t expk[4]) {
+  uint32_t mask = 0;
+  expk[0] = expk[1] = expk[2] = expk[3] = 0;
+  if constexpr (DT == 1) {
+    uint32_t dif[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      expk[q] = bf16x4_exp(xw[2 * q], xw[2 * q + 1]);
+      dif[q] = expk[q] ^ cw[q];
+      if (!FULL) {  // only the cnt values present
+        const int nv = cnt - 4 * q;
+        dif[q] &= nv >= 4 ? 0xFFFFFFFFu : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
+      }
+    }
+    if (dif[0] | dif[1] | dif[2] | dif[3]) mask = nonzero_bytes16(dif);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint32_t v;
+      if constexpr (Tr<DT>::E == 2) v = (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      else v = xw[j];
+      const uint32_t e = exp_of<DT>(v);
+      expk[j >> 2] |= e << (8 * (j & 3));
+      if ((FULL || j < cnt) && e != byte_of(cw, j)) mask |= 1u << j;
+    }
+  }
+  return mask;
+}
+
+// Stores the chunk's sign|mantissa records (compress) or its raw values.
+template <int DT>
+__device__ __forceinline__ void chunk_store(uint8_t* stream, uint64_t c0, int cnt, const uint32_t* xw, bool compress) {
+  constexpr int E = Tr<DT>::E;
+  if constexpr (DT == 1) {
+    if (compress) {
+      uint32_t smw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) smw[q] = bf16x4_sm(xw[2 * q], xw[2 * q + 1]);
+      store_words<4>(stream + kHeader + c0, (uint32_t)cnt, true, smw);
+    } else {
+      store_words<4 * E>(stream + kHeader + c0 * E, (uint32_t)cnt * E, true, xw);
+    }
+  } else {
+    uint32_t v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (E == 2) v[j] = (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      else v[j] = xw[j];
+    }
+    if (compress) {
+      uint32_t sm[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sm[j] = sm_of<DT>(v[j]);
+      store_sm16<DT>(stream + kHeader + sm_off<DT>(c0), cnt, sm);
+    } else {
+      store16<DT>(stream + kHeader + c0 * E, cnt, v);
+    }
+  }
+}
+
+// Exclusive prefix of v over the workgroup's threads in thread order, and the
+// total.  Contains one barrier; s_red (4 words) must not be in use by another
+// call until every thread has passed a later barrier.
+template <class V>
+__device__ __forceinline__ V block_scan(V v, V* s_red, V& total) {
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  V incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const V t = __shfl_up(incl, o);
+    if (lane >= (uint32_t)o) incl += t;
+  }
+  if (lane == 63) s_red[wave] = incl;
+  __syncthreads();
+  V before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    const V t = s_red[w];
+    if (w < (int)wave) before += t;
+    tot += t;
+  }
+  total = tot;
+  return before + incl - v;
+}
+
+// One 5-byte patch record (u32 index, u8 exponent, little-endian) at byte pos
+// of the stream, if it lies inside the stream's capacity.
+__device__ __forceinline__ void put_record(uint8_t* stream, uint64_t capacity, uint64_t pos, uint32_t idx, uint32_t ex) {
+  if (pos + 5 <= capacity) {
+    G1 uint8_t* q = gp(stream + pos);
+    q[0] = (uint8_t)idx; q[1] = (uint8_t)(idx >> 8);
+    q[2] = (uint8_t)(idx >> 16); q[3] = (uint8_t)(idx >> 24);
+    q[4] = (uint8_t)ex;
+  }
+}
 
 template <int DT, int S>
-__global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* ctl, uint32_t batch_id) {
+__global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t batch_id) {
   constexpr int E = Tr<DT>::E;
   constexpr uint32_t T = (uint32_t)kSub * S;
   constexpr int XW = 4 * E;  // words of 16 raw values
-  __shared__ uint32_t s_local, s_excl, s_tag;
   __shared__ uint32_t s_wtot[4 * S];
-  __shared__ uint32_t s_bm[2 * S];  // one bit per block of the tile: T/B <= T/64 = 64*S bits
+  __shared__ uint64_t s_chg[4 * S];  // one bit per 16-value chunk of the tile, in value order
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const uint32_t item = a.item0 + blockIdx.x / a.tpi;
+  const uint32_t rel_item = blockIdx.x / a.tpi;
+  const uint32_t item = a.item0 + rel_item;
+  const uint32_t local = blockIdx.x - rel_item * a.tpi;
   const EncItem d = a.items[item];
   if (d.batch_id != batch_id) return;  // the scratch holds another batch (uniform)
-  if (tid == 0) {
-    const uint32_t got = __hip_atomic_fetch_add(gp(a.ctr + item), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // the item's last tile to take an id: every tile has taken one, so the
-    // counter goes back to 0 for the next launch
-    if (got == a.tpi - 1) __hip_atomic_store(gp(a.ctr + item), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_local = got;
-    s_tag = *gp(ctl + kCtlEpoch);  // written before this launch, fixed during it
-  }
-  if (tid < 2 * S) s_bm[tid] = 0;
-  __syncthreads();
-  const uint32_t local = s_local, tag = s_tag;
-  if (local >= a.tpi) return;  // uniform; cannot happen while counters match launches
-  if (local == 0 && tid == 0) *gp(ctl + kCtlTag) = tag;  // for the fallback kernel
   const uint64_t base = (uint64_t)local * T;
   const uint64_t n = d.n;
   const uint32_t B = d.block_size;
@@ -514,9 +554,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
   const bool compress = d.compress != 0;
   const bool caligned = d.cache_aligned != 0;
 
-  // Loads, split and compare, sign|mantissa (or RAW) stores, bitmap bits in
-  // LDS.  A tile wholly inside its item with an aligned cache takes a
-  // straight-line copy of this code (FULL: every chunk has 16 values).
+  // Loads, split and compare, sign|mantissa (or RAW) stores.  A tile wholly
+  // inside its item with an aligned cache takes a straight-line copy of this
+  // code (FULL: every chunk has 16 values).
   uint32_t mask[S];
   uint32_t expk[S][4];
   auto split_tile = [&](auto full_c) {
@@ -538,49 +578,20 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
       mask[s] = 0;
       expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
       if (cnt[s] > 0) {
-        if constexpr (DT == 1) {
-          uint32_t smw[4], dif[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            expk[s][q] = bf16x4_exp(xw[s][2 * q], xw[s][2 * q + 1]);
-            smw[q] = bf16x4_sm(xw[s][2 * q], xw[s][2 * q + 1]);
-            dif[q] = expk[s][q] ^ cw[s][q];
-            if (!FULL) {  // only the cnt values present
-              const int nv = cnt[s] - 4 * q;
-              dif[q] &= nv >= 4 ? 0xFFFFFFFFu : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
-            }
-          }
-          if (dif[0] | dif[1] | dif[2] | dif[3]) mask[s] = nonzero_bytes16(dif);
-          if (compress) store_words<4>(d.stream + kHeader + c0, (uint32_t)cnt[s], true, smw);
-          else store_words<XW>(d.stream + kHeader + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
-        } else {
-          uint32_t v[16], sm[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            if constexpr (E == 2) v[j] = (xw[s][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-            else v[j] = xw[s][j];
-            const uint32_t e = exp_of<DT>(v[j]);
-            expk[s][j >> 2] |= e << (8 * (j & 3));
-            if (j < cnt[s] && e != byte_of(cw[s], j)) mask[s] |= 1u << j;
-            sm[j] = sm_of<DT>(v[j]);
-          }
-          if (compress) store_sm16<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], sm);
-          else store16<DT>(d.stream + kHeader + c0 * E, cnt[s], v);
-        }
-        if (mask[s]) {
-          const uint32_t rel = ((uint32_t)s * kSub + tid * kEPT) >> lb;
-          atomicOr(&s_bm[rel >> 5], 1u << (rel & 31u));
-        }
+        mask[s] = chunk_exps<DT, FULL>(xw[s], cw[s], cnt[s], expk[s]);
+        chunk_store<DT>(d.stream, c0, cnt[s], xw[s], compress);
       }
     }
   };
   if (caligned && base + T <= n) split_tile(std::true_type{});  // uniform
   else split_tile(std::false_type{});
 
-  // block-wide exclusive scan of the per-thread change counts, chunk-row major
+  // chunk change flags for the bitmap; block-wide exclusive scan of the
+  // per-thread change counts, chunk-row major (= ascending value index)
   uint32_t lpre[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
+    const uint64_t chg = __ballot(mask[s] != 0);
     const uint32_t c = (uint32_t)__popc(mask[s]);
     uint32_t pre = 0, tot = 0;
 #pragma unroll
@@ -590,7 +601,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
       tot += (uint32_t)__popcll(m) << b;
     }
     lpre[s] = pre;
-    if (lane == 0) s_wtot[s * 4 + wave] = tot;
+    if (lane == 0) {
+      s_wtot[s * 4 + wave] = tot;
+      s_chg[s * 4 + wave] = chg;
+    }
   }
   __syncthreads();
   uint32_t agg = 0;
@@ -604,107 +618,221 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t* c
       agg += t;
     }
   }
+  if (tid == 0) gp(a.counts)[d.tile0 + local] = agg;
+  if (!compress) return;
 
-  uint64_t* sw = a.status + (uint64_t)(item - a.item0) * a.tpi;
-  if (wave == 0) {
-    uint32_t excl = 0;
-    if (local == 0) {
-      if (lane == 0) publish(sw, pack_status(kFlagIncl, tag, agg));
-    } else {
-      if (lane == 0) publish(sw + local, pack_status(kFlagAgg, tag, agg));
-      excl = look_back(sw, local, tag, ctl + kCtlError);
-      if (lane == 0) publish(sw + local, pack_status(kFlagIncl, tag, excl + agg));
-    }
-    if (lane == 0) s_excl = excl;
-  }
-  __syncthreads();
-  const uint32_t excl = s_excl;
-
+  // bitmap bytes of this tile's blocks (a tile spans whole bitmap bytes), when
+  // a stream with a change can be COMPRESSED at all (otherwise it is never read)
   const uint64_t nb = (n + B - 1) >> lb;
   const uint64_t nbm = (nb + 7) / 8;
-  if (compress) {
-    // bitmap bytes of this tile's blocks (a tile spans whole bitmap bytes)
+  const uint64_t smsec = sm_sec<DT>(n);
+  if (smsec + nbm + 5 <= n * E) {
     const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
     const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
     const uint32_t tbytes = (tblocks + 7) / 8;
-    if (tid < tbytes)
-      gp(d.stream)[kHeader + sm_sec<DT>(n) + (base >> (lb + 3)) + tid] = (uint8_t)(s_bm[tid >> 2] >> (8 * (tid & 3)));
-    // (index, exponent) records
-    const uint64_t pbase = kHeader + sm_sec<DT>(n) + nbm;
+    if (tid < tbytes) {
+      const uint32_t L = B >> 4;  // chunks per block, >= 4
+      uint32_t byte = 0;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      uint32_t m = mask[s];
-      uint64_t g = (uint64_t)excl + before[s] + lpre[s];
-      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-      while (m) {
-        const int j = __ffs(m) - 1;
-        m &= m - 1;
-        const uint64_t pos = pbase + 5 * g;
-        if (pos + 5 <= d.capacity) {
-          const uint32_t idx = (uint32_t)(c0 + j);
-          G1 uint8_t* q = gp(d.stream + pos);
-          q[0] = (uint8_t)idx; q[1] = (uint8_t)(idx >> 8);
-          q[2] = (uint8_t)(idx >> 16); q[3] = (uint8_t)(idx >> 24);
-          q[4] = (uint8_t)byte_of(expk[s], j);
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t blk = tid * 8 + (uint32_t)k;
+        if (blk < tblocks) {
+          const uint32_t first = blk * L;
+          uint64_t any;
+          if (L < 64) {
+            any = (s_chg[first >> 6] >> (first & 63u)) & ((1ull << L) - 1ull);
+          } else {
+            any = 0;
+            for (uint32_t u = 0; u < L / 64; ++u) any |= s_chg[(first >> 6) + u];
+          }
+          if (any) byte |= 1u << k;
         }
-        ++g;
       }
+      gp(d.stream)[kHeader + smsec + (base >> (lb + 3)) + tid] = (uint8_t)byte;
     }
   }
 
-  // the item's last tile knows the total and writes the header
-  if (local == a.tpi - 1 && tid == 0) {
-    const uint64_t P = (uint64_t)excl + agg;
-    const uint64_t comp = kHeader + sm_sec<DT>(n) + (P ? nbm + 5 * P : 0);
-    const uint64_t raw = kHeader + n * E;
-    const bool cmode = compress && comp < raw;
-    if (compress && !cmode) {
-      gp(a.raw_flag)[item] = tag;
-      *gp(a.any_raw) = tag;
-    }
-    uint32_t h[16];
-    h[0] = 0x52454943u;  // "CIER"
-    h[1] = 1u | ((uint32_t)DT << 16) | ((cmode ? 1u : 0u) << 24);
-    h[2] = B;
-    h[3] = 0;
-    h[4] = (uint32_t)n; h[5] = (uint32_t)(n >> 32);
-    h[6] = (uint32_t)P; h[7] = (uint32_t)(P >> 32);
-    const uint64_t tot = cmode ? comp : raw;
-    h[8] = (uint32_t)tot; h[9] = (uint32_t)(tot >> 32);
-    h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
-    h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
-
+  // the tile's first cap changes, ascending, into its stash
+  G1 uint32_t* st = gp(a.stash + d.stash + (uint64_t)local * d.cap);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v4u o;
-      o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
-      stg16(d.stream + 16 * q, o);
+  for (int s = 0; s < S; ++s) {
+    uint32_t m = mask[s];
+    uint32_t g = before[s] + lpre[s];
+    const uint32_t rel0 = (uint32_t)s * kSub + tid * kEPT;
+    while (m) {
+      const int j = __ffs(m) - 1;
+      m &= m - 1;
+      if (g < d.cap) st[g] = (rel0 + (uint32_t)j) | (byte_of(expk[s], j) << 16);
+      ++g;
     }
   }
 }
 
-// Rewrites as RAW the streams whose COMPRESSED form turned out not shorter:
-// gridDim.x workgroups per item, items along y.  Returns at once when the
-// launch flagged no item (the common case).  It runs after every encode launch
-// and advances the epoch: the next launch's tag.
-__global__ __launch_bounds__(kThreads) void encode_fixup_kernel(const EncItem* __restrict__ items, uint32_t count,
-                                                                const uint32_t* raw_flag, uint32_t* ctl,
-                                                                uint32_t batch_id) {
-  const uint32_t tag = *gp(ctl + kCtlTag);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
-    *gp(ctl + kCtlEpoch) = 1u + tag % 0x3FFFFFFEu;  // never 0; no other block reads the epoch
-  if (*gp(ctl + kCtlAnyRaw) != tag) return;
-  const uint64_t gtid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint64_t gsz = (uint64_t)gridDim.x * blockDim.x;
-  for (uint32_t k = blockIdx.y; k < count; k += gridDim.y) {
-    if (gp(raw_flag)[k] != tag) continue;
-    const EncItem d = items[k];
-    if (d.batch_id != batch_id) return;
-    if (d.stream == nullptr) continue;
-    const uint64_t bytes = d.n * d.elem_bytes;
-    const uint64_t vec = bytes / 16;
-    for (uint64_t i = gtid; i < vec; i += gsz) stg16(d.stream + kHeader + 16 * i, ldg16(d.x + 16 * i));
-    for (uint64_t i = vec * 16 + gtid; i < bytes; i += gsz) gp(d.stream)[kHeader + i] = gp(d.x)[i];
+// Tiles per window of the finishing kernel: counts are scanned in LDS a window
+// at a time.
+constexpr uint32_t kWin = 1024;
+
+// Writes the patch records of tile j of item d (tvals values) again from the
+// shard and the cache, the first one as record number r0.  Workgroup-wide.
+template <int DT>
+__device__ void rederive_tile(const EncItem& d, uint64_t j, uint32_t r0, uint64_t pbase, uint32_t* s_red) {
+  constexpr int E = Tr<DT>::E;
+  constexpr int XW = 4 * E;
+  const uint32_t tid = threadIdx.x;
+  uint32_t run = r0;
+  for (uint32_t row = 0; row < d.tvals / kSub; ++row) {  // uniform
+    const uint64_t c0 = j * d.tvals + (uint64_t)row * kSub + (uint64_t)tid * kEPT;
+    const int cnt = c0 < d.n ? (int)min<uint64_t>(16, d.n - c0) : 0;
+    uint32_t xw[XW], cw[4], expk[4], mask = 0;
+    if (cnt > 0) {
+      load_words<XW>(d.x + c0 * E, (uint32_t)cnt * E, true, xw);
+      load_words<4>(d.cache + c0, (uint32_t)cnt, d.cache_aligned != 0, cw);
+      mask = chunk_exps<DT, false>(xw, cw, cnt, expk);
+    }
+    uint32_t tot;
+    uint32_t g = run + block_scan<uint32_t>((uint32_t)__popc(mask), s_red, tot);
+    while (mask) {
+      const int k = __ffs(mask) - 1;
+      mask &= mask - 1;
+      put_record(d.stream, d.capacity, pbase + 5ull * g, (uint32_t)(c0 + k), byte_of(expk, k));
+      ++g;
+    }
+    run += tot;
+    __syncthreads();  // s_red is read before it is written again
+  }
+}
+
+// gridDim.x workgroups per item, items along y.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncItem* __restrict__ items, uint32_t item0,
+                                                                 uint32_t nitems, const uint32_t* counts,
+                                                                 const uint32_t* stash, uint32_t batch_id) {
+  constexpr int E = Tr<DT>::E;
+  __shared__ uint32_t s_pre[kWin + 1];  // exclusive prefix of the window's tile counts, then its total
+  __shared__ uint32_t s_ovf[kWin];      // window tiles whose changes overflowed their stash
+  __shared__ uint64_t s_red64[kThreads / 64];
+  __shared__ uint32_t s_red[kThreads / 64];
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t G = gridDim.x, g = blockIdx.x;
+  for (uint32_t it = blockIdx.y; it < nitems; it += gridDim.y) {
+    __syncthreads();  // LDS of the previous item is no longer read
+    const EncItem d = items[item0 + it];
+    if (d.batch_id != batch_id) return;  // uniform
+    const uint32_t tpi = d.tpi;
+    const G1 uint32_t* cnts = gp(counts + d.tile0);
+
+    // Scans one window of tile counts into s_pre (and its overflowing tiles
+    // into s_ovf); returns the window total and the number of overflowing
+    // tiles.  `rest` adds the counts past the first window (first call only).
+    auto scan_window = [&](uint32_t w0, bool with_rest, uint32_t& novf, uint32_t& rest_total) -> uint32_t {
+      const uint32_t nw = min(kWin, tpi - w0);
+      uint32_t c4[4], sum = 0, nov = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t i = tid * 4 + (uint32_t)k;
+        c4[k] = i < nw ? cnts[w0 + i] : 0u;
+        sum += c4[k];
+        nov += c4[k] > d.cap ? 1u : 0u;
+      }
+      uint32_t rest = 0;
+      if (with_rest)
+        for (uint32_t i = kWin + tid; i < tpi; i += kThreads) rest += cnts[i];
+      uint64_t tot64;
+      const uint64_t ex = block_scan<uint64_t>((uint64_t)sum | ((uint64_t)nov << 32), s_red64, tot64);
+      uint32_t rt = 0;
+      if (with_rest && tpi > kWin) (void)block_scan<uint32_t>(rest, s_red, rt);
+      uint32_t pre = (uint32_t)ex, o = (uint32_t)(ex >> 32);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t i = tid * 4 + (uint32_t)k;
+        if (i < nw) {
+          s_pre[i] = pre;
+          if (c4[k] > d.cap) s_ovf[o++] = i;
+        }
+        pre += c4[k];
+      }
+      if (tid == 0) s_pre[nw] = (uint32_t)tot64;
+      __syncthreads();
+      novf = (uint32_t)(tot64 >> 32);
+      rest_total = rt;
+      return (uint32_t)tot64;
+    };
+
+    uint32_t novf, rest;
+    const uint32_t wtot0 = scan_window(0, true, novf, rest);
+    const uint64_t P = (uint64_t)wtot0 + rest;
+    const uint64_t n = d.n;
+    const uint32_t B = d.block_size;
+    const uint32_t lb = (uint32_t)__ffs(B) - 1u;
+    const uint64_t nbm = (((n + B - 1) >> lb) + 7) / 8;
+    const uint64_t smsec = sm_sec<DT>(n);
+    const uint64_t comp = kHeader + smsec + (P ? nbm + 5 * P : 0);
+    const uint64_t raw = kHeader + n * E;
+    const bool cmode = d.compress != 0 && comp < raw;
+
+    if (g == 0 && tid == 0) {
+      uint32_t h[16];
+      h[0] = 0x52454943u;  // "CIER"
+      h[1] = 1u | ((uint32_t)DT << 16) | ((cmode ? 1u : 0u) << 24);
+      h[2] = B;
+      h[3] = 0;
+      h[4] = (uint32_t)n; h[5] = (uint32_t)(n >> 32);
+      h[6] = (uint32_t)P; h[7] = (uint32_t)(P >> 32);
+      const uint64_t tot = cmode ? comp : raw;
+      h[8] = (uint32_t)tot; h[9] = (uint32_t)(tot >> 32);
+      h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
+      h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v4u o;
+        o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
+        stg16(d.stream + 16 * q, o);
+      }
+    }
+    if (d.compress != 0 && !cmode) {  // the compressed form is not shorter: RAW
+      const uint64_t bytes = n * E;
+      const uint64_t vec = bytes / 16;
+      const uint64_t gt = (uint64_t)g * kThreads + tid, gs = (uint64_t)G * kThreads;
+      for (uint64_t i = gt; i < vec; i += gs) stg16(d.stream + kHeader + 16 * i, ldg16(d.x + 16 * i));
+      for (uint64_t i = vec * 16 + gt; i < bytes; i += gs) gp(d.stream)[kHeader + i] = gp(d.x)[i];
+      continue;
+    }
+    if (!cmode || P == 0) continue;  // RAW as planned (written by encode_kernel), or no patches
+
+    const uint64_t pbase = kHeader + smsec + nbm;
+    uint32_t run = 0;  // records before the window
+    for (uint32_t w0 = 0; w0 < tpi; w0 += kWin) {  // uniform
+      uint32_t wtot = wtot0;
+      if (w0 > 0) {
+        __syncthreads();  // the previous window's LDS is no longer read
+        wtot = scan_window(w0, false, novf, rest);
+      }
+      const uint32_t nw = min(kWin, tpi - w0);
+      for (uint32_t r0 = g * kThreads; r0 < wtot; r0 += G * kThreads) {
+        const uint32_t r = r0 + tid;
+        if (r < wtot) {
+          uint32_t lo = 0, hi = nw;  // s_pre[lo] <= r < s_pre[hi]
+          while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (s_pre[mid] <= r) lo = mid;
+            else hi = mid;
+          }
+          const uint32_t k = r - s_pre[lo];
+          if (s_pre[lo + 1] - s_pre[lo] <= d.cap) {
+            const uint64_t j = (uint64_t)w0 + lo;
+            const uint32_t v = gp(stash)[d.stash + j * d.cap + k];
+            put_record(d.stream, d.capacity, pbase + 5ull * (run + r), (uint32_t)(j * d.tvals + (v & 0xFFFFu)),
+                       v >> 16);
+          }
+        }
+      }
+      for (uint32_t u = 0; u < novf; ++u) {  // uniform
+        const uint32_t i = s_ovf[u];
+        if ((w0 + i) % G == g) rederive_tile<DT>(d, (uint64_t)w0 + i, run + s_pre[i], pbase, s_red);
+      }
+      run += wtot;
+    }
   }
 }
 
@@ -1041,60 +1169,52 @@ __global__ __launch_bounds__(kThreads) void cache_update_kernel(const uint8_t* _
 // batches are cut into launches of whole items.
 constexpr uint64_t kMaxGrid = (uint64_t)1 << 22;
 
-static hipError_t launch_encode_part(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
-                                     uint32_t batch_id, hipStream_t s) {
+static hipError_t launch_encode_part(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t batch_id,
+                                     hipStream_t s) {
   (void)hipGetLastError();
   const dim3 grid(nitems * a.tpi), block(kThreads);
-#define CIERA_ENC(DT, S) hipLaunchKernelGGL((encode_kernel<DT, S>), grid, block, 0, s, a, ctl, batch_id)
+#define CIERA_ENC(DT, S) hipLaunchKernelGGL((encode_kernel<DT, S>), grid, block, 0, s, a, batch_id)
+#define CIERA_ENC_DT(DT)                  \
+  switch (sub) {                          \
+    case 1: CIERA_ENC(DT, 1); break;      \
+    case 2: CIERA_ENC(DT, 2); break;      \
+    case 4: CIERA_ENC(DT, 4); break;      \
+    case 8: CIERA_ENC(DT, 8); break;      \
+    default: return hipErrorInvalidValue; \
+  }
   if (dtype == 1) {
-    switch (sub) {
-      case 1: CIERA_ENC(1, 1); break;
-      case 2: CIERA_ENC(1, 2); break;
-      case 4: CIERA_ENC(1, 4); break;
-      case 8: CIERA_ENC(1, 8); break;
-      default: return hipErrorInvalidValue;
-    }
+    CIERA_ENC_DT(1)
   } else if (dtype == 2) {
-    switch (sub) {
-      case 1: CIERA_ENC(2, 1); break;
-      case 2: CIERA_ENC(2, 2); break;
-      case 4: CIERA_ENC(2, 4); break;
-      case 8: CIERA_ENC(2, 8); break;
-      default: return hipErrorInvalidValue;
-    }
+    CIERA_ENC_DT(2)
   } else if (dtype == 3) {
-    switch (sub) {
-      case 1: CIERA_ENC(3, 1); break;
-      case 2: CIERA_ENC(3, 2); break;
-      case 4: CIERA_ENC(3, 4); break;
-      case 8: CIERA_ENC(3, 8); break;
-      default: return hipErrorInvalidValue;
-    }
+    CIERA_ENC_DT(3)
   } else {
     return hipErrorInvalidValue;
   }
+#undef CIERA_ENC_DT
 #undef CIERA_ENC
   return hipGetLastError();
 }
 
-hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t* ctl,
-                         uint32_t batch_id, hipStream_t s) {
+hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t batch_id, hipStream_t s) {
   const uint32_t per = (uint32_t)std::max<uint64_t>(1, kMaxGrid / a.tpi);
   for (uint32_t i = 0; i < nitems; i += per) {
     EncArgs c = a;
     c.item0 = a.item0 + i;
-    c.status = a.status + (uint64_t)i * a.tpi;  // status words are indexed from the group's first item
-    if (hipError_t e = launch_encode_part(dtype, sub, std::min(per, nitems - i), c, ctl, batch_id, s)) return e;
+    if (hipError_t e = launch_encode_part(dtype, sub, std::min(per, nitems - i), c, batch_id, s)) return e;
   }
   return hipSuccess;
 }
 
-hipError_t launch_encode_fixup(const EncItem* items, uint32_t count, uint32_t wg_per_item, const uint32_t* raw_flag,
-                               uint32_t* ctl, uint32_t batch_id, hipStream_t s) {
+hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0, uint32_t nitems, uint32_t wg_per_item,
+                                const uint32_t* counts, const uint32_t* stash, uint32_t batch_id, hipStream_t s) {
   (void)hipGetLastError();
-  if (count == 0 || wg_per_item == 0) return hipSuccess;
-  const dim3 grid(wg_per_item, count < 65535u ? count : 65535u), block(kThreads);
-  hipLaunchKernelGGL(encode_fixup_kernel, grid, block, 0, s, items, count, raw_flag, ctl, batch_id);
+  if (nitems == 0 || wg_per_item == 0) return hipSuccess;
+  const dim3 grid(wg_per_item, nitems < 65535u ? nitems : 65535u), block(kThreads);
+  if (dtype == 1) hipLaunchKernelGGL((encode_finish_kernel<1>), grid, block, 0, s, items, item0, nitems, counts, stash, batch_id);
+  else if (dtype == 2) hipLaunchKernelGGL((encode_finish_kernel<2>), grid, block, 0, s, items, item0, nitems, counts, stash, batch_id);
+  else if (dtype == 3) hipLaunchKernelGGL((encode_finish_kernel<3>), grid, block, 0, s, items, item0, nitems, counts, stash, batch_id);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
