@@ -137,6 +137,8 @@ def main():
                 and not args.clustered and wl["ppm"] == 10000 and args.dtype == "bf16":
             traffic = t.get("hbm_bytes_per_launch")
 
+    iso = isolated(wl, stream, args.warmup + args.steps, max(10, args.steps // 2))
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(specs, w0, w1, wl["world"], wl["block"], A, args.cpu_seconds, args.dtype)
@@ -167,6 +169,12 @@ def main():
                    "logical_GBps": round(E * N / (dec_avg * 1e-3) / 1e9, 1),
                    "algorithmic_bytes": dec_bytes, "achieved_GBps": round(dec_gbps, 1),
                    "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4)},
+        "isolated": {
+            "encode_us": iso["encode_us"], "decode_us": iso["decode_us"],
+            "encode_hbm_frac": round(enc_bytes / (iso["encode_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "decode_hbm_frac": round(dec_bytes / (iso["decode_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "condition": "each launch alone, after a 1 GiB read of other data (Infinity Cache clean, "
+                         "inputs in HBM)"},
         "compression_ratio": round(wl["raw_bytes"] / wl["stream_bytes"], 4),
         "changed_exponents": wl["P_total"],
         "roofline": {"bound": "hbm", "kernel": f"decode_kernel<{args.dtype},2>",
@@ -175,6 +183,36 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def isolated(wl, stream, k0, reps):
+    """Each kernel alone.  Inside a step the encode follows a decode that wrote
+    ~1.1 GB, so it starts with the 256 MB Infinity Cache full of dirty lines
+    and pays for their write-back.  Here a read of 1 GiB of other data before
+    every launch writes those back and leaves the cache holding clean,
+    unrelated lines: the launch reads its inputs from HBM and writes back only
+    its own data.  Returns the mean event-timed duration of each launch (us)."""
+    import torch
+    flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda")  # 1 GiB
+    enc, dec = [], []
+    for k in range(k0, k0 + reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        flush.sum()
+        e[0].record(stream)
+        wl["encode_only"](k, stream)
+        e[1].record(stream)
+        flush.sum()
+        e[2].record(stream)
+        wl["decode_only"](k, stream)
+        e[3].record(stream)
+        enc.append(e)
+        dec.append(e)
+    torch.cuda.synchronize()
+    wl["check"](k0 + reps - 1)
+    ue = [x[0].elapsed_time(x[1]) * 1e3 for x in enc]
+    ud = [x[2].elapsed_time(x[3]) * 1e3 for x in dec]
+    del flush
+    return {"encode_us": round(sum(ue) / len(ue), 2), "decode_us": round(sum(ud) / len(ud), 2)}
 
 
 def setup(args):
@@ -284,8 +322,14 @@ def setup(args):
         for i in range(0, len(specs), 17):
             assert torch.equal(last.out_view(i).view(idt), want[i].reshape(-1).view(idt)), i
 
+    def encode_only(k, stream):
+        (encA if k % 2 == 0 else encB).launch(stream)
+
+    def decode_only(k, stream):
+        (A if k % 2 == 0 else Bc).decode(stream, zero_status=False)
+
     return dict(specs=specs, A=A, Bc=Bc, w0=w0, w1=w1, N=N, n_enc=n_enc, world=world, block=block, E=E,
-                ppm=ppm, step=step, check=check, dec_bytes=dec_bytes, enc_bytes=enc_bytes,
+                ppm=ppm, step=step, check=check, encode_only=encode_only, decode_only=decode_only, dec_bytes=dec_bytes, enc_bytes=enc_bytes,
                 raw_bytes=raw_bytes, stream_bytes=stream_bytes, P_total=P_total)
 
 

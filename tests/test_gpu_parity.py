@@ -109,6 +109,30 @@ def test_change_rates_and_raw_fallback(dtype, frac):
         assert modes == {O.MODE_COMPRESSED}
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_many_tiles_windows_and_stash_overflow(dtype):
+    """One shard of 1051 encode tiles (8192 values each, the last one half
+    full): the finishing kernel scans tile counts in windows of 1024, and tiles
+    with more changes than their stash holds (1/8 of the tile) -- in the first
+    window, in the second and in the partial last tile -- have their records
+    derived again.  The rest changes at 1%, so the stream stays COMPRESSED."""
+    rows, cols, T = 2101, 4096, 8192
+    say(f"[gpu] many tiles {rows}x{cols} {dtype}")
+    spec = W.TensorSpec("big", rows, cols)
+    w0 = W.base_weights(spec, W.tensor_seed("many", rows), dtype)
+    mask = W.mask_uniform(rows * cols, 0.01, W.tensor_seed("many-m", rows))
+    dense = W.mask_uniform(rows * cols, 0.6, W.tensor_seed("many-d", rows))
+    for t in (3, 1030, 1050):
+        lo, hi = t * T, min(rows * cols, (t + 1) * T)
+        mask[lo:hi] |= dense[lo:hi]
+    w1 = W.perturb_exact(w0, mask, W.tensor_seed("many-p", rows))
+    case = Case([(rows, cols)], dtype, 1)
+    res = case.run([w0], [w1], compress=[1])
+    assert res["status"] == 0 and res["ostatus"] == 0
+    h = O.parse_header(case.codec.slot(0, 0).cpu().numpy())
+    assert h["mode"] == O.MODE_COMPRESSED and h["n_changed"] > 0
+
+
 def test_specials_and_all_bf16_patterns():
     """Every bf16 bit pattern (+-0, subnormals, Inf, all NaN payloads) survives."""
     say("[gpu] all 65536 bf16 patterns")
