@@ -34,6 +34,11 @@ __device__ __forceinline__ const G1 T* gp(const T* p) { return (const G1 T*)p; }
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // one 16-byte global access
 __device__ __forceinline__ v4u ldg16(const void* p) { return *gp(reinterpret_cast<const v4u*>(p)); }
+// Non-temporal 16-byte load: for data read once (the bulk streams), which
+// then does not displace reused lines.
+__device__ __forceinline__ v4u ldg16_nt(const void* p) {
+  return __builtin_nontemporal_load(gp(reinterpret_cast<const v4u*>(p)));
+}
 __device__ __forceinline__ void stg16(void* p, v4u v) { *gp(reinterpret_cast<v4u*>(p)) = v; }
 // Non-temporal 16-byte store: for data no later access of this launch reads.
 __device__ __forceinline__ void stg16_nt(void* p, v4u v) {
@@ -260,13 +265,14 @@ __device__ __forceinline__ void store_sm16(uint8_t* p, int cnt, const uint32_t s
   }
 }
 
-// Raw 32-bit words of nbytes <= 4*NW bytes at p (vector loads when complete and allowed).
-template <int NW>
+// Raw 32-bit words of nbytes <= 4*NW bytes at p (vector loads, non-temporal
+// if NT, when complete and allowed).
+template <int NW, bool NT = false>
 __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t nbytes, bool vec, uint32_t w[NW]) {
   if (vec && nbytes == NW * 4) {
 #pragma unroll
     for (int q = 0; q < NW / 4; ++q) {
-      const v4u a = ldg16(p + 16 * q);
+      const v4u a = NT ? ldg16_nt(p + 16 * q) : ldg16(p + 16 * q);
       w[4 * q] = a.x; w[4 * q + 1] = a.y; w[4 * q + 2] = a.z; w[4 * q + 3] = a.w;
     }
   } else {
@@ -350,7 +356,7 @@ __device__ __forceinline__ void load_smw(const uint8_t* sec, uint64_t c0, int cn
       load_words<SW>(a, (uint32_t)(11 * cnt + 7) / 8, false, w);
     }
   } else {
-    load_words<SW>(a, (uint32_t)cnt * Tr<DT>::SMBITS / 8, true, w);
+    load_words<SW, true>(a, (uint32_t)cnt * Tr<DT>::SMBITS / 8, true, w);
   }
 }
 
@@ -568,8 +574,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
       const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
       cnt[s] = FULL ? 16 : (c0 < n ? (int)min<uint64_t>(16, n - c0) : 0);
       if (cnt[s] > 0) {
-        load_words<XW>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
-        load_words<4>(d.cache + c0, (uint32_t)cnt[s], FULL || caligned, cw[s]);
+        load_words<XW, true>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
+        load_words<4, true>(d.cache + c0, (uint32_t)cnt[s], FULL || caligned, cw[s]);
       }
     }
 #pragma unroll
@@ -883,7 +889,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     cnt[u] = c0 < te ? (int)min<uint64_t>(16, te - c0) : 0;
     if (cnt[u] > 0) {
       load_smw<DT, SW>(st + kHeader, c0, cnt[u], sw[u]);
-      load_words<4>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
+      load_words<4, true>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
     }
   }
   const uint64_t nb = (n + B - 1) >> lb;
