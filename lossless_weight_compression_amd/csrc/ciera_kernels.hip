@@ -708,137 +708,150 @@ __device__ void rederive_tile(const EncItem& d, uint64_t j, uint32_t r0, uint64_
   }
 }
 
+// LDS of one item's finishing work.
+struct FinLds {
+  uint32_t pre[kWin + 1];  // exclusive prefix of the window's tile counts, then its total
+  uint32_t ovf[kWin];      // window tiles whose changes overflowed their stash
+  uint64_t red64[kThreads / 64];
+  uint32_t red[kThreads / 64];
+};
+
+// Finishing work of item d by workgroup g of G: the sum of its tile counts
+// decides the mode; workgroup 0 writes the header; the stashed changes go to
+// their places in the patch list (tiles that overflowed their stash derive
+// theirs again), or the stream is rewritten RAW.  Workgroup-wide.
+template <int DT>
+__device__ void finish_item(const EncItem& d, const uint32_t* counts, const uint32_t* stash, uint32_t G, uint32_t g,
+                            FinLds& L) {
+  constexpr int E = Tr<DT>::E;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t tpi = d.tpi;
+  const G1 uint32_t* cnts = gp(counts + d.tile0);
+
+  // Scans one window of tile counts into L.pre (and its overflowing tiles
+  // into L.ovf); returns the window total and the number of overflowing
+  // tiles.  `rest` adds the counts past the first window (first call only).
+  auto scan_window = [&](uint32_t w0, bool with_rest, uint32_t& novf, uint32_t& rest_total) -> uint32_t {
+    const uint32_t nw = min(kWin, tpi - w0);
+    uint32_t c4[4], sum = 0, nov = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t i = tid * 4 + (uint32_t)k;
+      c4[k] = i < nw ? cnts[w0 + i] : 0u;
+      sum += c4[k];
+      nov += c4[k] > d.cap ? 1u : 0u;
+    }
+    uint32_t rest = 0;
+    if (with_rest)
+      for (uint32_t i = kWin + tid; i < tpi; i += kThreads) rest += cnts[i];
+    uint64_t tot64;
+    const uint64_t ex = block_scan<uint64_t>((uint64_t)sum | ((uint64_t)nov << 32), L.red64, tot64);
+    uint32_t rt = 0;
+    if (with_rest && tpi > kWin) (void)block_scan<uint32_t>(rest, L.red, rt);
+    uint32_t pre = (uint32_t)ex, o = (uint32_t)(ex >> 32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t i = tid * 4 + (uint32_t)k;
+      if (i < nw) {
+        L.pre[i] = pre;
+        if (c4[k] > d.cap) L.ovf[o++] = i;
+      }
+      pre += c4[k];
+    }
+    if (tid == 0) L.pre[nw] = (uint32_t)tot64;
+    __syncthreads();
+    novf = (uint32_t)(tot64 >> 32);
+    rest_total = rt;
+    return (uint32_t)tot64;
+  };
+
+  uint32_t novf, rest;
+  const uint32_t wtot0 = scan_window(0, true, novf, rest);
+  const uint64_t P = (uint64_t)wtot0 + rest;
+  const uint64_t n = d.n;
+  const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;
+  const uint64_t nbm = (((n + B - 1) >> lb) + 7) / 8;
+  const uint64_t smsec = sm_sec<DT>(n);
+  const uint64_t comp = kHeader + smsec + (P ? nbm + 5 * P : 0);
+  const uint64_t raw = kHeader + n * E;
+  const bool cmode = d.compress != 0 && comp < raw;
+
+  if (g == 0 && tid == 0) {
+    uint32_t h[16];
+    h[0] = 0x52454943u;  // "CIER"
+    h[1] = 1u | ((uint32_t)DT << 16) | ((cmode ? 1u : 0u) << 24);
+    h[2] = B;
+    h[3] = 0;
+    h[4] = (uint32_t)n; h[5] = (uint32_t)(n >> 32);
+    h[6] = (uint32_t)P; h[7] = (uint32_t)(P >> 32);
+    const uint64_t tot = cmode ? comp : raw;
+    h[8] = (uint32_t)tot; h[9] = (uint32_t)(tot >> 32);
+    h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
+    h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v4u o;
+      o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
+      stg16(d.stream + 16 * q, o);
+    }
+  }
+  if (d.compress != 0 && !cmode) {  // the compressed form is not shorter: RAW
+    const uint64_t bytes = n * E;
+    const uint64_t vec = bytes / 16;
+    const uint64_t gt = (uint64_t)g * kThreads + tid, gs = (uint64_t)G * kThreads;
+    for (uint64_t i = gt; i < vec; i += gs) stg16(d.stream + kHeader + 16 * i, ldg16(d.x + 16 * i));
+    for (uint64_t i = vec * 16 + gt; i < bytes; i += gs) gp(d.stream)[kHeader + i] = gp(d.x)[i];
+    return;
+  }
+  if (!cmode || P == 0) return;  // RAW as planned (written by encode_kernel), or no patches
+
+  const uint64_t pbase = kHeader + smsec + nbm;
+  uint32_t run = 0;  // records before the window
+  for (uint32_t w0 = 0; w0 < tpi; w0 += kWin) {  // uniform
+    uint32_t wtot = wtot0;
+    if (w0 > 0) {
+      __syncthreads();  // the previous window's LDS is no longer read
+      wtot = scan_window(w0, false, novf, rest);
+    }
+    const uint32_t nw = min(kWin, tpi - w0);
+    for (uint32_t r0 = g * kThreads; r0 < wtot; r0 += G * kThreads) {
+      const uint32_t r = r0 + tid;
+      if (r < wtot) {
+        uint32_t lo = 0, hi = nw;  // L.pre[lo] <= r < L.pre[hi]
+        while (hi - lo > 1) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (L.pre[mid] <= r) lo = mid;
+          else hi = mid;
+        }
+        const uint32_t k = r - L.pre[lo];
+        if (L.pre[lo + 1] - L.pre[lo] <= d.cap) {
+          const uint64_t j = (uint64_t)w0 + lo;
+          const uint32_t v = gp(stash)[d.stash + j * d.cap + k];
+          put_record(d.stream, d.capacity, pbase + 5ull * (run + r), (uint32_t)(j * d.tvals + (v & 0xFFFFu)),
+                     v >> 16);
+        }
+      }
+    }
+    for (uint32_t u = 0; u < novf; ++u) {  // uniform
+      const uint32_t i = L.ovf[u];
+      if ((w0 + i) % G == g) rederive_tile<DT>(d, (uint64_t)w0 + i, run + L.pre[i], pbase, L.red);
+    }
+    run += wtot;
+  }
+}
+
 // gridDim.x workgroups per item, items along y.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncItem* __restrict__ items, uint32_t item0,
                                                                  uint32_t nitems, const uint32_t* counts,
                                                                  const uint32_t* stash, uint32_t batch_id) {
-  constexpr int E = Tr<DT>::E;
-  __shared__ uint32_t s_pre[kWin + 1];  // exclusive prefix of the window's tile counts, then its total
-  __shared__ uint32_t s_ovf[kWin];      // window tiles whose changes overflowed their stash
-  __shared__ uint64_t s_red64[kThreads / 64];
-  __shared__ uint32_t s_red[kThreads / 64];
-
-  const uint32_t tid = threadIdx.x;
-  const uint32_t G = gridDim.x, g = blockIdx.x;
+  __shared__ FinLds s_fin;
   for (uint32_t it = blockIdx.y; it < nitems; it += gridDim.y) {
     __syncthreads();  // LDS of the previous item is no longer read
     const EncItem d = items[item0 + it];
     if (d.batch_id != batch_id) return;  // uniform
-    const uint32_t tpi = d.tpi;
-    const G1 uint32_t* cnts = gp(counts + d.tile0);
-
-    // Scans one window of tile counts into s_pre (and its overflowing tiles
-    // into s_ovf); returns the window total and the number of overflowing
-    // tiles.  `rest` adds the counts past the first window (first call only).
-    auto scan_window = [&](uint32_t w0, bool with_rest, uint32_t& novf, uint32_t& rest_total) -> uint32_t {
-      const uint32_t nw = min(kWin, tpi - w0);
-      uint32_t c4[4], sum = 0, nov = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t i = tid * 4 + (uint32_t)k;
-        c4[k] = i < nw ? cnts[w0 + i] : 0u;
-        sum += c4[k];
-        nov += c4[k] > d.cap ? 1u : 0u;
-      }
-      uint32_t rest = 0;
-      if (with_rest)
-        for (uint32_t i = kWin + tid; i < tpi; i += kThreads) rest += cnts[i];
-      uint64_t tot64;
-      const uint64_t ex = block_scan<uint64_t>((uint64_t)sum | ((uint64_t)nov << 32), s_red64, tot64);
-      uint32_t rt = 0;
-      if (with_rest && tpi > kWin) (void)block_scan<uint32_t>(rest, s_red, rt);
-      uint32_t pre = (uint32_t)ex, o = (uint32_t)(ex >> 32);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t i = tid * 4 + (uint32_t)k;
-        if (i < nw) {
-          s_pre[i] = pre;
-          if (c4[k] > d.cap) s_ovf[o++] = i;
-        }
-        pre += c4[k];
-      }
-      if (tid == 0) s_pre[nw] = (uint32_t)tot64;
-      __syncthreads();
-      novf = (uint32_t)(tot64 >> 32);
-      rest_total = rt;
-      return (uint32_t)tot64;
-    };
-
-    uint32_t novf, rest;
-    const uint32_t wtot0 = scan_window(0, true, novf, rest);
-    const uint64_t P = (uint64_t)wtot0 + rest;
-    const uint64_t n = d.n;
-    const uint32_t B = d.block_size;
-    const uint32_t lb = (uint32_t)__ffs(B) - 1u;
-    const uint64_t nbm = (((n + B - 1) >> lb) + 7) / 8;
-    const uint64_t smsec = sm_sec<DT>(n);
-    const uint64_t comp = kHeader + smsec + (P ? nbm + 5 * P : 0);
-    const uint64_t raw = kHeader + n * E;
-    const bool cmode = d.compress != 0 && comp < raw;
-
-    if (g == 0 && tid == 0) {
-      uint32_t h[16];
-      h[0] = 0x52454943u;  // "CIER"
-      h[1] = 1u | ((uint32_t)DT << 16) | ((cmode ? 1u : 0u) << 24);
-      h[2] = B;
-      h[3] = 0;
-      h[4] = (uint32_t)n; h[5] = (uint32_t)(n >> 32);
-      h[6] = (uint32_t)P; h[7] = (uint32_t)(P >> 32);
-      const uint64_t tot = cmode ? comp : raw;
-      h[8] = (uint32_t)tot; h[9] = (uint32_t)(tot >> 32);
-      h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
-      h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v4u o;
-        o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
-        stg16(d.stream + 16 * q, o);
-      }
-    }
-    if (d.compress != 0 && !cmode) {  // the compressed form is not shorter: RAW
-      const uint64_t bytes = n * E;
-      const uint64_t vec = bytes / 16;
-      const uint64_t gt = (uint64_t)g * kThreads + tid, gs = (uint64_t)G * kThreads;
-      for (uint64_t i = gt; i < vec; i += gs) stg16(d.stream + kHeader + 16 * i, ldg16(d.x + 16 * i));
-      for (uint64_t i = vec * 16 + gt; i < bytes; i += gs) gp(d.stream)[kHeader + i] = gp(d.x)[i];
-      continue;
-    }
-    if (!cmode || P == 0) continue;  // RAW as planned (written by encode_kernel), or no patches
-
-    const uint64_t pbase = kHeader + smsec + nbm;
-    uint32_t run = 0;  // records before the window
-    for (uint32_t w0 = 0; w0 < tpi; w0 += kWin) {  // uniform
-      uint32_t wtot = wtot0;
-      if (w0 > 0) {
-        __syncthreads();  // the previous window's LDS is no longer read
-        wtot = scan_window(w0, false, novf, rest);
-      }
-      const uint32_t nw = min(kWin, tpi - w0);
-      for (uint32_t r0 = g * kThreads; r0 < wtot; r0 += G * kThreads) {
-        const uint32_t r = r0 + tid;
-        if (r < wtot) {
-          uint32_t lo = 0, hi = nw;  // s_pre[lo] <= r < s_pre[hi]
-          while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (s_pre[mid] <= r) lo = mid;
-            else hi = mid;
-          }
-          const uint32_t k = r - s_pre[lo];
-          if (s_pre[lo + 1] - s_pre[lo] <= d.cap) {
-            const uint64_t j = (uint64_t)w0 + lo;
-            const uint32_t v = gp(stash)[d.stash + j * d.cap + k];
-            put_record(d.stream, d.capacity, pbase + 5ull * (run + r), (uint32_t)(j * d.tvals + (v & 0xFFFFu)),
-                       v >> 16);
-          }
-        }
-      }
-      for (uint32_t u = 0; u < novf; ++u) {  // uniform
-        const uint32_t i = s_ovf[u];
-        if ((w0 + i) % G == g) rederive_tile<DT>(d, (uint64_t)w0 + i, run + s_pre[i], pbase, s_red);
-      }
-      run += wtot;
-    }
+    finish_item<DT>(d, counts, stash, gridDim.x, blockIdx.x, s_fin);
   }
 }
 
