@@ -122,7 +122,7 @@ hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) 
   return hipSuccess;
 }
 
-// Batch ids and launch tags: distinct per prepare / per launch, never 0.
+// Batch ids: distinct per prepare, never 0.
 std::atomic<uint32_t> g_ids{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u};
 uint32_t next_id() {
   uint32_t v;

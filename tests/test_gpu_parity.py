@@ -250,7 +250,7 @@ def test_patch_record_order_errors_at_many_positions(frac):
 
 
 def test_encode_is_deterministic():
-    """Two encodes of the same inputs give identical bytes (look-back race check)."""
+    """Two encodes of the same inputs give identical bytes (no order dependence between workgroups)."""
     specs = W.olmoe_expert_specs()
     cfg = W.PairConfig("det", frac=0.01)
     w0, w1 = _pairs(specs, cfg)
