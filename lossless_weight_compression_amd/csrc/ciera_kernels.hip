@@ -35,7 +35,13 @@ __device__ __forceinline__ const G1 T* gp(const T* p) { return (const G1 T*)p; }
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // one 16-byte global access
 __device__ __forceinline__ v4u ldg16(const void* p) { return *gp(reinterpret_cast<const v4u*>(p)); }
 // Non-temporal 16-byte load: for data read once (the bulk streams), which
-// then does not displace reused lines.
+// then does not displace reused lines.  Used where a wave's 16-byte loads of
+// a chunk row cover whole 128-byte lines between them with at most two loads
+// per thread (bf16, fp16: 16 or 32 bytes per thread).  fp32 threads read 48 or
+// 64 contiguous bytes with three or four strided loads; non-temporal there
+// measured 15% slower (decode) and 19% slower (encode), so fp32 loads normally.
+template <int DT>
+constexpr bool kNtBulk = DT != 2;
 __device__ __forceinline__ v4u ldg16_nt(const void* p) {
   return __builtin_nontemporal_load(gp(reinterpret_cast<const v4u*>(p)));
 }
@@ -356,7 +362,7 @@ __device__ __forceinline__ void load_smw(const uint8_t* sec, uint64_t c0, int cn
       load_words<SW>(a, (uint32_t)(11 * cnt + 7) / 8, false, w);
     }
   } else {
-    load_words<SW, true>(a, (uint32_t)cnt * Tr<DT>::SMBITS / 8, true, w);
+    load_words<SW, kNtBulk<DT>>(a, (uint32_t)cnt * Tr<DT>::SMBITS / 8, true, w);
   }
 }
 
@@ -574,8 +580,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
       const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
       cnt[s] = FULL ? 16 : (c0 < n ? (int)min<uint64_t>(16, n - c0) : 0);
       if (cnt[s] > 0) {
-        load_words<XW, true>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
-        load_words<4, true>(d.cache + c0, (uint32_t)cnt[s], FULL || caligned, cw[s]);
+        load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
+        load_words<4, kNtBulk<DT>>(d.cache + c0, (uint32_t)cnt[s], FULL || caligned, cw[s]);
       }
     }
 #pragma unroll
@@ -902,7 +908,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     cnt[u] = c0 < te ? (int)min<uint64_t>(16, te - c0) : 0;
     if (cnt[u] > 0) {
       load_smw<DT, SW>(st + kHeader, c0, cnt[u], sw[u]);
-      load_words<4, true>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
+      load_words<4, kNtBulk<DT>>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
     }
   }
   const uint64_t nb = (n + B - 1) >> lb;
