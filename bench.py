@@ -127,7 +127,7 @@ def main():
 
     # HBM traffic of the decode kernel from the committed PMC summary, if it was
     # taken on the current kernel source
-    traffic = None
+    traffic = enc_traffic = None
     src = os.path.join(ROOT, "lossless_weight_compression_amd", "csrc", "ciera_kernels.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     tf = os.path.join(ROOT, "profiles", "decode_traffic.json")
@@ -136,6 +136,7 @@ def main():
         if t.get("kernel_source_sha256") == sha and t.get("workload") == "olmoe_layer_bf16_1pct_uniform" \
                 and not args.clustered and wl["ppm"] == 10000 and args.dtype == "bf16":
             traffic = t.get("hbm_bytes_per_launch")
+            enc_traffic = t.get("encode_kernel_bytes_per_launch", 0) + t.get("encode_finish_kernel_bytes_per_launch", 0)
 
     iso = isolated(wl, stream, args.warmup + args.steps, max(10, args.steps // 2))
 
@@ -164,7 +165,10 @@ def main():
         "encode": {"avg_us": round(enc_avg * 1e3, 2), "elements": n_enc,
                    "logical_GBps": round(E * n_enc / (enc_avg * 1e-3) / 1e9, 1),
                    "algorithmic_bytes": enc_bytes, "achieved_GBps": round(enc_gbps, 1),
-                   "hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4)},
+                   "hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
+                   "traffic_bytes": enc_traffic,
+                   "traffic_frac": None if enc_traffic is None
+                   else round(enc_traffic / (enc_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "decode": {"avg_us": round(dec_avg * 1e3, 2), "elements": N,
                    "logical_GBps": round(E * N / (dec_avg * 1e-3) / 1e9, 1),
                    "algorithmic_bytes": dec_bytes, "achieved_GBps": round(dec_gbps, 1),
@@ -179,7 +183,11 @@ def main():
         "changed_exponents": wl["P_total"],
         "roofline": {"bound": "hbm", "kernel": f"decode_kernel<{args.dtype},2>",
                      "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     # the same launch on the HBM bytes it actually moves (rocprofv3 counters)
+                     "traffic_GBps": None if traffic is None else round(traffic / (dec_avg * 1e-3) / 1e9, 1),
+                     "traffic_frac": None if traffic is None
+                     else round(traffic / (dec_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
