@@ -120,6 +120,19 @@ typedef struct {
 ciera_status_t ciera_plan(const ciera_tensor_t* t, uint32_t change_ppm,
                           const ciera_cost_model_t* cm, ciera_plan_t* out);
 
+/* ciera_select -- benefit-driven selection under a cache budget [CIERA 3.2]:
+ * among the tensors whose plan has a positive gain (plans[i].gain_ns > 0), rank
+ * them by gain per byte of exponent cache, gain_ns / cache_bytes, descending
+ * (exact integer cross-multiplication; equal ratios keep the input order; a
+ * tensor with no cache ranks first), then take them in that order while the
+ * running total of cache_bytes stays <= cache_budget_bytes, stopping at the
+ * first one that does not fit.  compress_out[i] = 1 for the selected tensors,
+ * 0 for all others.  plans: count host plans from ciera_plan; compress_out:
+ * count host words, caller-owned.  Host only, pure.  Errors: INVALID_ARG when
+ * count > 0 and plans or compress_out is NULL. */
+ciera_status_t ciera_select(const ciera_plan_t* plans, uint32_t count, uint64_t cache_budget_bytes,
+                            uint32_t* compress_out);
+
 /* ciera_shard -- element offset and count of rank's row shard.  Host only. */
 ciera_status_t ciera_shard(const ciera_tensor_t* t, uint32_t rank, uint64_t* offset,
                            uint64_t* n);

@@ -1,6 +1,6 @@
 """CIERA exponent-reuse codec for MI355X (gfx950).
 
-``_binding`` mirrors include/ciera.h (ciera_plan, ciera_shard, ciera_encode,
+``_binding`` mirrors include/ciera.h (ciera_plan, ciera_select, ciera_shard, ciera_encode,
 ciera_decode, ciera_cache_update, ...) over the in-tree libciera.so; ``layer``
 holds a layer's caches, receive slots and outputs in flat device buffers.
 Importing fails loudly when the library has not been built.
@@ -10,4 +10,4 @@ from ._binding import (Batch, CieraError, CostModel, DecodeItem, EncodeItem, Pla
                        ciera_abi_version, ciera_cache_update, ciera_decode, ciera_decode_launch,
                        ciera_decode_prepare, ciera_decode_scratch_bytes, ciera_encode,
                        ciera_encode_launch, ciera_encode_prepare, ciera_encode_scratch_bytes,
-                       ciera_plan, ciera_shard, ciera_status_str, decode_item, encode_item)
+                       ciera_plan, ciera_select, ciera_shard, ciera_status_str, decode_item, encode_item)

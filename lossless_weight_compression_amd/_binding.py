@@ -16,7 +16,7 @@ CIERA_ST_MAGIC, CIERA_ST_FIELD, CIERA_ST_LENGTH, CIERA_ST_PATCH, CIERA_ST_BITMAP
 HEADER_BYTES = 64
 
 # every symbol include/ciera.h declares
-EXPORTS = ["ciera_plan", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
+EXPORTS = ["ciera_plan", "ciera_select", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
            "ciera_encode_prepare", "ciera_encode_launch", "ciera_decode_scratch_bytes",
            "ciera_decode", "ciera_decode_prepare", "ciera_decode_launch", "ciera_cache_update",
            "ciera_status_str", "ciera_abi_version", "ciera_last_error"]
@@ -93,6 +93,7 @@ def _load() -> ctypes.CDLL:
         raise ImportError(f"two HIP runtimes are mapped into this process: {sorted(runtimes)}")
     sig = {
         "ciera_plan": (c_int, [POINTER(Tensor), c_uint32, POINTER(CostModel), POINTER(Plan)]),
+        "ciera_select": (c_int, [POINTER(Plan), c_uint32, c_uint64, POINTER(c_uint32)]),
         "ciera_shard": (c_int, [POINTER(Tensor), c_uint32, POINTER(c_uint64), POINTER(c_uint64)]),
         "ciera_encode_scratch_bytes": (c_int, [POINTER(EncodeItem), c_uint32, POINTER(c_uint64)]),
         "ciera_encode": (c_int, [POINTER(EncodeItem), c_uint32, c_void_p, c_uint64, c_void_p]),
@@ -163,6 +164,16 @@ def ciera_plan(t: Tensor, change_ppm: int, cost: Optional[CostModel] = None) -> 
     _check(_lib.ciera_plan(byref(t), change_ppm, byref(cost) if cost is not None else None,
                            byref(out)), "ciera_plan")
     return out
+
+
+def ciera_select(plans: Sequence[Plan], cache_budget_bytes: int) -> List[int]:
+    """Benefit-driven selection: compress flag per plan under a cache budget."""
+    arr = (Plan * max(len(plans), 1))()
+    for i, p in enumerate(plans):
+        arr[i] = p
+    out = (c_uint32 * max(len(plans), 1))()
+    _check(_lib.ciera_select(arr, len(plans), cache_budget_bytes, out), "ciera_select")
+    return [int(out[i]) for i in range(len(plans))]
 
 
 def ciera_shard(t: Tensor, rank: int) -> Tuple[int, int]:

@@ -321,6 +321,28 @@ ciera_status_t ciera_plan(const ciera_tensor_t* t, uint32_t change_ppm, const ci
   return CIERA_OK;
 }
 
+ciera_status_t ciera_select(const ciera_plan_t* plans, uint32_t count, uint64_t cache_budget_bytes,
+                            uint32_t* compress_out) {
+  if (count && (!plans || !compress_out)) return CIERA_ERR_INVALID_ARG;
+  std::vector<uint32_t> cand;
+  for (uint32_t i = 0; i < count; ++i) {
+    compress_out[i] = 0;
+    if (plans[i].gain_ns > 0) cand.push_back(i);
+  }
+  // a before b when g_a / M_a > g_b / M_b, i.e. g_a * M_b > g_b * M_a (g > 0)
+  std::stable_sort(cand.begin(), cand.end(), [plans](uint32_t a, uint32_t b) {
+    return (u128)(uint64_t)plans[a].gain_ns * plans[b].cache_bytes >
+           (u128)(uint64_t)plans[b].gain_ns * plans[a].cache_bytes;
+  });
+  u128 used = 0;
+  for (uint32_t i : cand) {
+    if (used + plans[i].cache_bytes > cache_budget_bytes) break;
+    compress_out[i] = 1;
+    used += plans[i].cache_bytes;
+  }
+  return CIERA_OK;
+}
+
 // ------------------------------------------------------------------ encode
 
 ciera_status_t ciera_encode_scratch_bytes(const ciera_encode_item_t* items, uint32_t count, uint64_t* bytes) {

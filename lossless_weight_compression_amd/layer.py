@@ -33,7 +33,7 @@ class LayerCodec:
     def __init__(self, shapes: Sequence[Tuple[int, int]], dtype: torch.dtype, world: int,
                  block_size: int = 512, device="cuda", change_ppm: int = 10_000,
                  cost: Optional[B.CostModel] = None, with_out: bool = True,
-                 cache: Optional[torch.Tensor] = None):
+                 cache: Optional[torch.Tensor] = None, cache_budget: Optional[int] = None):
         self.dtype = dtype
         self.cdtype = TORCH_TO_CIERA[dtype]
         self.e = ELEM[self.cdtype]
@@ -42,6 +42,9 @@ class LayerCodec:
         self.tensors = [B.Tensor(r, c, self.cdtype, block_size, world) for r, c in shapes]
         self.numel = [r * c for r, c in shapes]
         self.plans = [B.ciera_plan(t, change_ppm, cost) for t in self.tensors]
+        if cache_budget is not None:  # benefit-driven selection: the rest is sent RAW
+            for p, c in zip(self.plans, B.ciera_select(self.plans, cache_budget)):
+                p.compress = c
         self.slot_bytes = [_align(p.max_stream_bytes, 16) for p in self.plans]
         # flat buffers with 256-byte aligned per-tensor regions
         self.cache_off, self.stream_off, self.out_off = [], [], []

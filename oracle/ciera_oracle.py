@@ -413,3 +413,32 @@ def plan(rows: int, cols: int, dtype: int, block_size: int, world: int,
     compress = 1 if gain > 0 else 0
     res.update(compress=compress, expected_stream_bytes=comp if compress else raw, gain_ns=gain)
     return res
+
+
+# ------------------------------------------------------------------ selection
+# [CIERA 3.2] Among the shards with a positive gain g_i, rank them by g_i / M_i
+# (gain per byte of exponent cache) in descending order and select them until
+# the cache budget is exhausted.  Readings: M_i is the cache this design holds
+# for the tensor (one byte per value of the full tensor, the plan's
+# cache_bytes); equal ratios keep the input order; the selection stops at the
+# first ranked shard whose cache no longer fits in what is left (R25).
+
+def select(gains: Sequence[int], cache_bytes: Sequence[int], budget: int) -> List[int]:
+    """compress flags (0/1) per tensor: the benefit-driven selection."""
+    from fractions import Fraction
+    cand = [i for i in range(len(gains)) if gains[i] > 0]
+
+    def ratio(i):  # a shard with no cache costs nothing: it ranks first
+        return Fraction(gains[i], cache_bytes[i]) if cache_bytes[i] > 0 else float("inf")
+
+    ranked = sorted(cand, key=lambda i: ratio(i), reverse=True)  # sorted() is stable
+    # reverse=True keeps equal keys in their input order as well
+    out = [0] * len(gains)
+    used = 0
+    for i in ranked:
+        if used + cache_bytes[i] > budget:
+            break
+        out[i] = 1
+        used += cache_bytes[i]
+    return out
+

@@ -18,7 +18,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 from lossless_weight_compression_amd.layer import LayerCodec  # noqa: E402
-from tests.gpu_harness import say, to_np  # noqa: E402
+from tests.gpu_harness import Case, say, to_np  # noqa: E402
 
 IV = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.float16: torch.int16}
 ODT = {torch.bfloat16: O.BF16, torch.float32: O.FP32, torch.float16: O.FP16}
@@ -237,3 +237,30 @@ def test_prepared_batch_rejects_foreign_scratch():
     L.ciera_encode_launch(b)
     torch.cuda.synchronize()
     assert int(codec.streams.count_nonzero()) > 0
+
+
+def test_layer_under_cache_budget():
+    """ciera_select inside LayerCodec: with a cache budget of two expert
+    tensors, the norm (no gain), the router and one expert go RAW, the two
+    other experts COMPRESSED; the round trip stays bit-exact and the streams
+    equal the oracle's for those decisions."""
+    shapes = [(7168, 1), (7168, 256), (2048, 1024), (2048, 1024), (1024, 2048)]
+    say(f"[gpu] cache budget {shapes}")
+    budget = 2 * 2048 * 1024
+    codec = LayerCodec(shapes, torch.bfloat16, 16, change_ppm=10_000, cache_budget=budget)
+    want = O.select([p.gain_ns for p in codec.plans], [p.cache_bytes for p in codec.plans], budget)
+    got = [p.compress for p in codec.plans]
+    assert got == want and sum(got) == 2, got
+    w0, w1 = [], []
+    for i, (r, c) in enumerate(shapes):
+        spec = W.TensorSpec(f"t{i}", r, c)
+        a = W.base_weights(spec, W.tensor_seed("budget", i), torch.bfloat16)
+        m = W.mask_uniform(r * c, 0.01, W.tensor_seed("budget-m", i))
+        w0.append(a)
+        w1.append(W.perturb_exact(a, m, W.tensor_seed("budget-p", i)))
+    case = Case(shapes, torch.bfloat16, 16)
+    res = case.run(w0, w1, compress=got)
+    assert res["status"] == 0 and res["ostatus"] == 0
+    modes = [int(O.parse_header(case.codec.slot(i, 0).cpu().numpy())["mode"]) for i in range(len(shapes))]
+    assert modes == [O.MODE_COMPRESSED if g else O.MODE_RAW for g in got]
+

@@ -10,6 +10,7 @@ from oracle import ciera_oracle as O
 from tests import test_oracle_brute_plan as TB
 from tests import test_oracle_fields as TF
 from tests import test_oracle_stream as TS
+from tests import test_select as TSel
 
 PINS = [
     TF.test_bf16_exponent_matches_frexp_exhaustive,
@@ -28,6 +29,8 @@ PINS = [
     TS.test_payload_model_matches_pages,
     lambda: [TB.test_plan_decision_table(r) for r in TB.PLAN_TABLE],
     TB.test_corruption_classes,
+    lambda: [TSel.test_select_table(r) for r in TSel.SELECT_TABLE],
+    TSel.test_low_change_shards_rank_first,
 ]
 
 
@@ -163,6 +166,30 @@ def _check_raw_tie_compress(orig):
     return cl
 
 
+def _select_variant(ascending=False, by_gain=False, skip_misfits=False, ties_reversed=False):
+    """The selection with one plausible slip."""
+    def sel(gains, cache, budget):
+        from fractions import Fraction
+        cand = [i for i in range(len(gains)) if gains[i] > 0]
+        if ties_reversed:
+            cand = cand[::-1]
+
+        def key(i):
+            if by_gain:
+                return gains[i]
+            return Fraction(gains[i], cache[i]) if cache[i] > 0 else float("inf")
+        ranked = sorted(cand, key=key, reverse=not ascending)
+        out, used = [0] * len(gains), 0
+        for i in ranked:
+            if used + cache[i] > budget:
+                if skip_misfits:
+                    continue
+                break
+            out[i], used = 1, used + cache[i]
+        return out
+    return sel
+
+
 MUTATIONS = {
     "exponent shift off by one bit": lambda mp: mp.setattr(O, "exponent_field", _wrong_exp_shift),
     "sign bit dropped": lambda mp: mp.setattr(O, "sign_mantissa_field", _sm_without_sign),
@@ -180,6 +207,10 @@ MUTATIONS = {
         lambda pu: (mp.setattr(O, "pack_sm", pu[0]), mp.setattr(O, "unpack_sm", pu[1])))(
         _fp16_msb_first(O.pack_sm, O.unpack_sm)),
     "fp16 section sized 2 bytes per value": lambda mp: mp.setattr(O, "sm_section_bytes", _fp16_two_bytes_per_value(O.sm_section_bytes)),
+    "selection ranked ascending": lambda mp: mp.setattr(O, "select", _select_variant(ascending=True)),
+    "selection ranked by gain alone": lambda mp: mp.setattr(O, "select", _select_variant(by_gain=True)),
+    "selection skips a misfit and goes on": lambda mp: mp.setattr(O, "select", _select_variant(skip_misfits=True)),
+    "selection breaks ties against input order": lambda mp: mp.setattr(O, "select", _select_variant(ties_reversed=True)),
 }
 
 

@@ -1,0 +1,139 @@
+"""Benefit-driven selection under a cache budget [CIERA 3.2], CPU only.
+
+The pages rank the shards with a positive gain g_i by g_i / M_i (gain per byte
+of exponent cache), descending, and select them until the cache budget is
+exhausted.  Pinned here by a hand-worked table and by properties that follow
+from that sentence; the C-ABI ciera_select is then compared with the oracle
+on plans from ciera_plan and on random gains."""
+import numpy as np
+import pytest
+
+from oracle import ciera_oracle as O
+
+# (gain_ns, cache_bytes) of six tensors.  Ratios: 0 -> 2, 1 -> 3, 2 -> gain < 0
+# (never a candidate), 3 -> 3 (ties with 1, which comes first in the input),
+# 4 -> 1, 5 -> gain 0 (never a candidate).  Ranked: 1, 3, 0, 4 with running
+# cache totals 100, 130, 180, 220.
+SELECT_GAINS = [100, 300, -5, 90, 40, 0]
+SELECT_CACHE = [50, 100, 10, 30, 40, 10]
+SELECT_TABLE = [
+    # budget, expected flags
+    (10**9, [1, 1, 0, 1, 1, 0]),  # everything with a positive gain
+    (220, [1, 1, 0, 1, 1, 0]),    # exactly the total of the four candidates
+    (219, [1, 1, 0, 1, 0, 0]),    # tensor 4 no longer fits
+    (180, [1, 1, 0, 1, 0, 0]),
+    (179, [0, 1, 0, 1, 0, 0]),    # tensor 0 does not fit: stop, although 4 (40) would
+    (130, [0, 1, 0, 1, 0, 0]),
+    (129, [0, 1, 0, 0, 0, 0]),    # the tie: 1 before 3
+    (99, [0, 0, 0, 0, 0, 0]),     # the best-ranked tensor does not fit
+    (0, [0, 0, 0, 0, 0, 0]),
+]
+
+
+@pytest.mark.parametrize("row", SELECT_TABLE)
+def test_select_table(row):
+    budget, want = row
+    assert O.select(SELECT_GAINS, SELECT_CACHE, budget) == want
+
+
+def _ranked(gains, cache):
+    """Candidates in the pages' order, by exact cross-multiplication."""
+    import functools
+
+    def cmp(a, b):
+        x, y = gains[a] * cache[b], gains[b] * cache[a]
+        return -1 if x > y else (1 if x < y else (a - b))
+    return sorted([i for i in range(len(gains)) if gains[i] > 0], key=functools.cmp_to_key(cmp))
+
+
+def test_select_properties_random():
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        k = int(rng.integers(0, 12))
+        gains = [int(v) for v in rng.integers(-50, 200, k)]
+        cache = [int(v) for v in rng.integers(0, 100, k)]
+        total = sum(cache[i] for i in range(k) if gains[i] > 0)
+        budget = int(rng.integers(0, total + 2))
+        out = O.select(gains, cache, budget)
+        ranked = _ranked(gains, cache)
+        chosen = [i for i in ranked if out[i]]
+        # the selection is a prefix of the ranking, within budget, and maximal
+        assert chosen == ranked[:len(chosen)]
+        assert sum(cache[i] for i in chosen) <= budget
+        if len(chosen) < len(ranked):
+            assert sum(cache[i] for i in chosen) + cache[ranked[len(chosen)]] > budget
+        assert all(out[i] == 0 for i in range(k) if gains[i] <= 0)
+        # an unlimited budget takes every candidate
+        assert O.select(gains, cache, total) == [1 if g > 0 else 0 for g in gains]
+
+
+def test_low_change_shards_rank_first():
+    """The pages: the selection favours shards with low change rates and skips
+    those whose high change rate leaves no gain.  The same OLMoE-expert shape
+    at rising rates ranks in the same order; 30% has no gain at all."""
+    rates = [300_000, 100, 10_000, 1_000, 50_000]
+    plans = [O.plan(2048, 1024, O.BF16, 512, 16, r) for r in rates]
+    gains = [p["gain_ns"] for p in plans]
+    cache = [p["cache_bytes"] for p in plans]
+    assert plans[0]["compress"] == 0
+    order = _ranked(gains, cache)
+    assert [rates[i] for i in order] == [100, 1_000, 10_000, 50_000]
+    # a budget of two tensors' caches takes the two lowest rates
+    assert O.select(gains, cache, 2 * 2048 * 1024) == [0, 1, 0, 1, 0]
+
+
+L = pytest.importorskip("lossless_weight_compression_amd")
+
+
+def _c_plans(plan_dicts):
+    out = []
+    for d in plan_dicts:
+        p = L.Plan()
+        p.gain_ns = d["gain_ns"]
+        p.cache_bytes = d["cache_bytes"]
+        p.compress = 1 if d["gain_ns"] > 0 else 0
+        out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("row", SELECT_TABLE)
+def test_c_select_table(row):
+    budget, want = row
+    plans = _c_plans([dict(gain_ns=g, cache_bytes=m) for g, m in zip(SELECT_GAINS, SELECT_CACHE)])
+    assert L.ciera_select(plans, budget) == want
+
+
+def test_c_select_matches_oracle_on_plans():
+    rng = np.random.default_rng(5)
+    shapes = [(2048, 1024), (1024, 2048), (7168, 256), (7168, 1), (448, 2048), (333, 77), (1, 1)]
+    for _ in range(200):
+        ts, plans = [], []
+        for _ in range(int(rng.integers(0, 24))):
+            r, c = shapes[int(rng.integers(0, len(shapes)))]
+            W = int(rng.choice([1, 2, 8, 16]))
+            ppm = int(rng.choice([0, 100, 1000, 10_000, 100_000, 300_000]))
+            t = L.Tensor(r, c, int(rng.choice([1, 2, 3])), 512, W)
+            ts.append(t)
+            plans.append(L.ciera_plan(t, ppm))
+        total = sum(p.cache_bytes for p in plans)
+        budget = int(rng.integers(0, total + 2)) if total else 0
+        want = O.select([p.gain_ns for p in plans], [p.cache_bytes for p in plans], budget)
+        assert L.ciera_select(plans, budget) == want
+
+
+def test_c_select_matches_oracle_random_gains():
+    rng = np.random.default_rng(9)
+    for _ in range(500):
+        k = int(rng.integers(0, 16))
+        d = [dict(gain_ns=int(rng.integers(-10**6, 10**9)), cache_bytes=int(rng.choice(
+            [0, int(rng.integers(1, 1000)), int(rng.integers(1, 2**40))]))) for _ in range(k)]
+        budget = int(rng.integers(0, 2**41))
+        want = O.select([x["gain_ns"] for x in d], [x["cache_bytes"] for x in d], budget)
+        assert L.ciera_select(_c_plans(d), budget) == want
+
+
+def test_c_select_rejects_null():
+    import ctypes
+    lib = L._binding._lib
+    assert lib.ciera_select(None, 0, 0, None) == 0
+    assert lib.ciera_select(None, 1, 0, None) == L._binding.CIERA_ERR_INVALID_ARG
