@@ -138,6 +138,7 @@ struct Group {
   uint32_t tpr, world;   // decode: tiles per rank, world
   uint32_t pad;
   uint64_t tile0;        // encode: the group's first tile in the batch's count array
+  uint64_t stash0;       // encode: word offset of the group's first tile stash
 };
 struct BatchImpl {
   uint64_t magic;
@@ -164,9 +165,9 @@ uint32_t enc_sub(uint32_t B, uint64_t n) {
 }
 uint32_t dec_unit(uint64_t n0) { return n0 > (uint64_t)kDecRow ? 2u : 1u; }
 
-// A tile's stash holds up to T/8 changes (12.5% of its values); a tile with
+// A tile's stash holds up to T/4 changes (25% of its values); a tile with
 // more has them derived again by the finishing kernel.
-constexpr uint32_t kStashDiv = 8;
+constexpr uint32_t kStashDiv = 4;
 
 struct EncPlan {
   std::vector<uint32_t> order;  // items in group order
@@ -202,6 +203,7 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     g.nitems = (uint32_t)kv.second.size();
     if ((uint64_t)g.nitems * g.tpi >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
     g.tile0 = tiles;
+    g.stash0 = words;
     const uint64_t cap = (uint64_t)kSub * g.unit / kStashDiv;
     for (uint32_t k = 0; k < g.nitems; ++k) {
       pl->tile0.push_back(tiles);
@@ -441,16 +443,27 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
     if (hipError_t e = launch_encode(g.dtype, g.unit, g.nitems, a, b->batch_id, st))
       return device_error("encode launch", e);
   }
-  // one finishing launch per dtype: groups are ordered by dtype first, so the
-  // items of one dtype are contiguous
-  for (uint32_t gi = 0; gi < b->ngroups;) {
-    uint32_t gj = gi;
-    uint32_t nitems = 0;
-    while (gj < b->ngroups && b->g[gj].dtype == b->g[gi].dtype) nitems += b->g[gj++].nitems;
-    if (hipError_t e = launch_encode_finish(b->g[gi].dtype, items, b->g[gi].item0, nitems, b->fin_wg, counts, stash,
-                                            b->batch_id, st))
-      return device_error("encode finish launch", e);
-    gi = gj;
+  // finishing kernels: one workgroup per tile for groups of at most kThreads
+  // tiles per item (overflowing tiles are then derived again in parallel);
+  // per item, over windows of tiles, for larger items
+  for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
+    const Group& g = b->g[gi];
+    hipError_t e;
+    if (g.tpi <= (uint32_t)kThreads) {
+      FinArgs f{};
+      f.items = items;
+      f.counts = counts;
+      f.stash = stash;
+      f.tile0 = g.tile0;
+      f.stash0 = g.stash0;
+      f.item0 = g.item0;
+      f.tpi = g.tpi;
+      f.cap = (uint32_t)kSub * g.unit / kStashDiv;
+      e = launch_encode_finish_tiles(g.dtype, g.nitems, f, b->batch_id, st);
+    } else {
+      e = launch_encode_finish(g.dtype, items, g.item0, g.nitems, b->fin_wg, counts, stash, b->batch_id, st);
+    }
+    if (e) return device_error("encode finish launch", e);
   }
   b->launches += 1;
   return CIERA_OK;

@@ -70,12 +70,24 @@ struct EncArgs {
   uint32_t* stash;     // the batch's stash words
 };
 
+// The per-tile finishing kernel of one group (at most kThreads tiles per
+// item); the group's counts and stashes are contiguous, item by item.
+struct FinArgs {
+  const EncItem* items;
+  const uint32_t* counts;
+  const uint32_t* stash;
+  uint64_t tile0;   // the group's first tile (index into counts)
+  uint64_t stash0;  // word offset of the group's first tile stash
+  uint32_t item0, tpi, cap, pad;
+};
+
 // ctl: the control words at the start of a batch's scratch.  Every descriptor
 // carries the id of the batch that wrote it; kernels exit at once when the
 // descriptor they read belongs to another batch (the scratch was taken over).
 hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0, uint32_t nitems, uint32_t wg_per_item,
                                 const uint32_t* counts, const uint32_t* stash, uint32_t batch_id, hipStream_t s);
+hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s);
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
                          uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,
                          uint32_t batch_id, hipStream_t s);

@@ -714,6 +714,36 @@ __device__ void rederive_tile(const EncItem& d, uint64_t j, uint32_t r0, uint64_
   }
 }
 
+// The 64-byte stream header (little-endian): "CIER", version 1, dtype, mode,
+// block size, n, changed values P, total length, offset, rank, world.
+template <int DT>
+__device__ __forceinline__ void write_header(const EncItem& d, uint64_t P, bool cmode, uint64_t total) {
+  uint32_t h[16];
+  h[0] = 0x52454943u;  // "CIER"
+  h[1] = 1u | ((uint32_t)DT << 16) | ((cmode ? 1u : 0u) << 24);
+  h[2] = d.block_size;
+  h[3] = 0;
+  h[4] = (uint32_t)d.n; h[5] = (uint32_t)(d.n >> 32);
+  h[6] = (uint32_t)P; h[7] = (uint32_t)(P >> 32);
+  h[8] = (uint32_t)total; h[9] = (uint32_t)(total >> 32);
+  h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
+  h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v4u o;
+    o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
+    stg16(d.stream + 16 * q, o);
+  }
+}
+
+// Raw body bytes [b0, b1) of the shard copied into the stream (b0 a multiple
+// of 16); this is thread gt of gs copying.
+__device__ __forceinline__ void raw_copy(const EncItem& d, uint64_t b0, uint64_t b1, uint64_t gt, uint64_t gs) {
+  const uint64_t v1 = b0 + (b1 - b0) / 16 * 16;
+  for (uint64_t i = b0 + 16 * gt; i < v1; i += 16 * gs) stg16(d.stream + kHeader + i, ldg16(d.x + i));
+  for (uint64_t i = v1 + gt; i < b1; i += gs) gp(d.stream)[kHeader + i] = gp(d.x)[i];
+}
+
 // LDS of one item's finishing work.
 struct FinLds {
   uint32_t pre[kWin + 1];  // exclusive prefix of the window's tile counts, then its total
@@ -783,31 +813,9 @@ __device__ void finish_item(const EncItem& d, const uint32_t* counts, const uint
   const uint64_t raw = kHeader + n * E;
   const bool cmode = d.compress != 0 && comp < raw;
 
-  if (g == 0 && tid == 0) {
-    uint32_t h[16];
-    h[0] = 0x52454943u;  // "CIER"
-    h[1] = 1u | ((uint32_t)DT << 16) | ((cmode ? 1u : 0u) << 24);
-    h[2] = B;
-    h[3] = 0;
-    h[4] = (uint32_t)n; h[5] = (uint32_t)(n >> 32);
-    h[6] = (uint32_t)P; h[7] = (uint32_t)(P >> 32);
-    const uint64_t tot = cmode ? comp : raw;
-    h[8] = (uint32_t)tot; h[9] = (uint32_t)(tot >> 32);
-    h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
-    h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v4u o;
-      o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
-      stg16(d.stream + 16 * q, o);
-    }
-  }
+  if (g == 0 && tid == 0) write_header<DT>(d, P, cmode, cmode ? comp : raw);
   if (d.compress != 0 && !cmode) {  // the compressed form is not shorter: RAW
-    const uint64_t bytes = n * E;
-    const uint64_t vec = bytes / 16;
-    const uint64_t gt = (uint64_t)g * kThreads + tid, gs = (uint64_t)G * kThreads;
-    for (uint64_t i = gt; i < vec; i += gs) stg16(d.stream + kHeader + 16 * i, ldg16(d.x + 16 * i));
-    for (uint64_t i = vec * 16 + gt; i < bytes; i += gs) gp(d.stream)[kHeader + i] = gp(d.x)[i];
+    raw_copy(d, 0, n * E, (uint64_t)g * kThreads + tid, (uint64_t)G * kThreads);
     return;
   }
   if (!cmode || P == 0) return;  // RAW as planned (written by encode_kernel), or no patches
@@ -858,6 +866,68 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncItem* 
     const EncItem d = items[item0 + it];
     if (d.batch_id != batch_id) return;  // uniform
     finish_item<DT>(d, counts, stash, gridDim.x, blockIdx.x, s_fin);
+  }
+}
+
+// Finishing kernel for groups of at most kThreads tiles per item: one
+// workgroup per tile, so tiles whose changes overflowed their stash are
+// derived again in parallel.  The item's tile counts, the tile's first
+// kThreads stash words and the descriptor are requested together; then the
+// tile's records go to their places, or its part of the shard is copied RAW.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void encode_finish_tile_kernel(FinArgs f, uint32_t batch_id) {
+  constexpr int E = Tr<DT>::E;
+  __shared__ uint64_t s_red64[kThreads / 64];
+  __shared__ uint32_t s_red[kThreads / 64];
+
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t rel = blockIdx.x / f.tpi;
+  const uint32_t local = blockIdx.x - rel * f.tpi;
+  const uint64_t t0 = f.tile0 + (uint64_t)rel * f.tpi;                // the item's first tile
+  const uint64_t sbase = f.stash0 + (t0 - f.tile0 + local) * f.cap;  // this tile's stash
+  const uint32_t c_t = tid < f.tpi ? gp(f.counts)[t0 + tid] : 0u;
+  const uint32_t mine = gp(f.counts)[t0 + local];
+  const uint32_t sv = gp(f.stash)[sbase + tid];  // cap >= kThreads: inside the stash
+  const EncItem d = f.items[f.item0 + rel];
+  if (d.batch_id != batch_id) return;  // uniform
+
+  // total and exclusive prefix of the item's tile counts, in one reduction
+  uint64_t v = (uint64_t)c_t | ((uint64_t)(tid < local ? c_t : 0u) << 32);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if (lane == 0) s_red64[wave] = v;
+  __syncthreads();
+  uint64_t sum = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) sum += s_red64[w];
+  const uint64_t P = (uint32_t)sum;
+  const uint32_t excl = (uint32_t)(sum >> 32);
+
+  const uint64_t n = d.n;
+  const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;
+  const uint64_t nbm = (((n + B - 1) >> lb) + 7) / 8;
+  const uint64_t smsec = sm_sec<DT>(n);
+  const uint64_t comp = kHeader + smsec + (P ? nbm + 5 * P : 0);
+  const uint64_t raw = kHeader + n * E;
+  const bool cmode = d.compress != 0 && comp < raw;
+  if (local == 0 && tid == 0) write_header<DT>(d, P, cmode, cmode ? comp : raw);
+  if (d.compress != 0 && !cmode) {  // the compressed form is not shorter: this tile's part RAW
+    const uint64_t v0 = (uint64_t)local * d.tvals;
+    const uint64_t v1 = min<uint64_t>(n, v0 + d.tvals);
+    if (v0 < v1) raw_copy(d, v0 * E, v1 * E, tid, kThreads);
+    return;
+  }
+  if (!cmode || mine == 0) return;
+  const uint64_t pbase = kHeader + smsec + nbm;
+  if (mine <= d.cap) {
+    const uint64_t tb = (uint64_t)local * d.tvals;
+    for (uint32_t r = tid; r < mine; r += kThreads) {
+      const uint32_t w = r < kThreads ? sv : gp(f.stash)[sbase + r];
+      put_record(d.stream, d.capacity, pbase + 5ull * (excl + r), (uint32_t)(tb + (w & 0xFFFFu)), w >> 16);
+    }
+  } else {
+    rederive_tile<DT>(d, local, excl, pbase, s_red);
   }
 }
 
@@ -1241,6 +1311,25 @@ hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0,
   else if (dtype == 3) hipLaunchKernelGGL((encode_finish_kernel<3>), grid, block, 0, s, items, item0, nitems, counts, stash, batch_id);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s) {
+  if (nitems == 0) return hipSuccess;
+  const uint32_t per = (uint32_t)std::max<uint64_t>(1, kMaxGrid / f.tpi);
+  for (uint32_t i = 0; i < nitems; i += per) {
+    (void)hipGetLastError();
+    FinArgs c = f;
+    c.item0 = f.item0 + i;
+    c.tile0 = f.tile0 + (uint64_t)i * f.tpi;
+    c.stash0 = f.stash0 + (uint64_t)i * f.tpi * f.cap;
+    const dim3 grid(std::min(per, nitems - i) * f.tpi), block(kThreads);
+    if (dtype == 1) hipLaunchKernelGGL((encode_finish_tile_kernel<1>), grid, block, 0, s, c, batch_id);
+    else if (dtype == 2) hipLaunchKernelGGL((encode_finish_tile_kernel<2>), grid, block, 0, s, c, batch_id);
+    else if (dtype == 3) hipLaunchKernelGGL((encode_finish_tile_kernel<3>), grid, block, 0, s, c, batch_id);
+    else return hipErrorInvalidValue;
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
 }
 
 static hipError_t launch_decode_part(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,

@@ -109,23 +109,34 @@ def test_change_rates_and_raw_fallback(dtype, frac):
         assert modes == {O.MODE_COMPRESSED}
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_many_tiles_windows_and_stash_overflow(dtype):
-    """One shard of 1051 encode tiles (8192 values each, the last one half
-    full): the finishing kernel scans tile counts in windows of 1024, and tiles
-    with more changes than their stash holds (1/8 of the tile) -- in the first
-    window, in the second and in the partial last tile -- have their records
-    derived again.  The rest changes at 1%, so the stream stays COMPRESSED."""
-    rows, cols, T = 2101, 4096, 8192
-    say(f"[gpu] many tiles {rows}x{cols} {dtype}")
+# (rows, cols, dtype, dense tiles): 1051 encode tiles of 8192 values (the last
+# half full) go through the finishing kernel that scans tile counts in windows
+# of 1024; 256 tiles go through the one-workgroup-per-tile finishing kernel.
+MANY_TILES = [
+    (2101, 4096, torch.bfloat16, (3, 1030, 1050)),
+    (2101, 4096, torch.float16, (3, 1030, 1050)),
+    (2048, 1024, torch.bfloat16, (0, 5, 255)),
+    (2047, 1024, torch.float32, (1, 254, 255)),
+]
+
+
+@pytest.mark.parametrize("rows,cols,dtype,dense", MANY_TILES)
+def test_many_tiles_and_stash_overflow(rows, cols, dtype, dense):
+    """One shard of many encode tiles (8192 values each).  Tiles with more
+    changes than their stash holds (a quarter of the tile) -- here 60% in a few
+    tiles, among them the last, partial one -- have their records derived again
+    from the shard and the cache.  The rest changes at 1%, so the stream stays
+    COMPRESSED."""
+    T = 8192
+    say(f"[gpu] many tiles {rows}x{cols} {dtype} dense {dense}")
     spec = W.TensorSpec("big", rows, cols)
-    w0 = W.base_weights(spec, W.tensor_seed("many", rows), dtype)
-    mask = W.mask_uniform(rows * cols, 0.01, W.tensor_seed("many-m", rows))
-    dense = W.mask_uniform(rows * cols, 0.6, W.tensor_seed("many-d", rows))
-    for t in (3, 1030, 1050):
+    w0 = W.base_weights(spec, W.tensor_seed("many", rows, cols), dtype)
+    mask = W.mask_uniform(rows * cols, 0.01, W.tensor_seed("many-m", rows, cols))
+    dense_m = W.mask_uniform(rows * cols, 0.6, W.tensor_seed("many-d", rows, cols))
+    for t in dense:
         lo, hi = t * T, min(rows * cols, (t + 1) * T)
-        mask[lo:hi] |= dense[lo:hi]
-    w1 = W.perturb_exact(w0, mask, W.tensor_seed("many-p", rows))
+        mask[lo:hi] |= dense_m[lo:hi]
+    w1 = W.perturb_exact(w0, mask, W.tensor_seed("many-p", rows, cols))
     case = Case([(rows, cols)], dtype, 1)
     res = case.run([w0], [w1], compress=[1])
     assert res["status"] == 0 and res["ostatus"] == 0
