@@ -65,7 +65,10 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="measure the step alone, a bf16 GEMM alone and both on two streams")
     ap.add_argument("--gemm", type=int, nargs=3, default=[8192, 8192, 8192], metavar=("M", "N", "K"),
-                    help="GEMM shape of --overlap")
+                    help="GEMM shape of --overlap and --pipeline")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="consecutive layers: encode of the next layer on its own stream beside the decode "
+                         "of this one and a bf16 GEMM that waits only on that decode, against all in order")
     return ap.parse_args()
 
 
@@ -90,6 +93,8 @@ def main():
         sys.exit(2)
     if args.overlap:
         return overlap(args)
+    if args.pipeline:
+        return pipeline(args)
     import torch
     wl = setup(args)
     specs, A, Bc, w0, w1, N, n_enc = wl["specs"], wl["A"], wl["Bc"], wl["w0"], wl["w1"], wl["N"], wl["n_enc"]
@@ -400,6 +405,97 @@ def overlap(args):
         "gemm": dict(res["gemm"], tflops=round(flops / (tg * 1e-6) / 1e12, 1)),
         "step": res["step"], "both": res["both"],
         "slowdown_vs_longer": round(tb / max(tg, ts_), 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def pipeline(args):
+    """Consecutive layers, as a rank runs them [CIERA 3.3, Figure 7]: layer j's
+    encode on a sender stream, its decode on a receiver stream once the encode
+    is done (the Allgather would sit there), and the layer's compute -- a bf16
+    GEMM -- on a compute stream once the decode is done.  The next layer's
+    encode is free to run beside this layer's decode and GEMM.  Two layers of
+    the same shapes with their own buffers and caches alternate; a layer's
+    next encode waits for its last decode (the cache), its next decode for its
+    last GEMM (the output).  Compared with the same work in order on one
+    stream, with the GEMMs alone and with the codec alone."""
+    import torch
+    layers = [setup(args), setup(args)]
+    for L in layers:
+        L["A"].status.zero_()
+        L["Bc"].status.zero_()
+    M, Nn, K = args.gemm
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=gen)
+    b = torch.randn(K, Nn, device="cuda", dtype=torch.bfloat16, generator=gen)
+    c = torch.empty(M, Nn, device="cuda", dtype=torch.bfloat16)
+    cur = torch.cuda.current_stream()
+    side = [torch.cuda.Stream() for _ in range(3)]  # default priorities
+    ks = [0, 0]
+
+    def run(J, mode):
+        """mode: 'pipe', 'seq', 'gemm' or 'codec'; returns elapsed us."""
+        send, recv, comp = side if mode == "pipe" else (cur, cur, cur)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for s in side:
+            s.wait_event(e0)
+        enc_done, dec_done, gemm_done = [], [], []
+        for j in range(J):
+            L = layers[j % 2]
+            if mode != "gemm":  # each layer's states alternate with its codec steps
+                k = ks[j % 2]
+                ks[j % 2] += 1
+                if j >= 2:
+                    send.wait_event(dec_done[j - 2])
+                L["encode_only"](k, send)
+                ev = torch.cuda.Event()
+                ev.record(send)
+                enc_done.append(ev)
+                recv.wait_event(ev)
+                if j >= 2 and gemm_done:
+                    recv.wait_event(gemm_done[j - 2])
+                L["decode_only"](k, recv)
+                ev = torch.cuda.Event()
+                ev.record(recv)
+                dec_done.append(ev)
+            if mode != "codec":
+                if dec_done:
+                    comp.wait_event(dec_done[j])
+                with torch.cuda.stream(comp):
+                    torch.mm(a, b, out=c)
+                ev = torch.cuda.Event()
+                ev.record(comp)
+                gemm_done.append(ev)
+        for evs in (enc_done, dec_done, gemm_done):
+            if evs:
+                cur.wait_event(evs[-1])
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    J = max(4, args.steps)
+    res = {}
+    for mode in ("gemm", "codec", "seq", "pipe"):
+        run(max(4, args.warmup), mode)
+        ts = sorted(run(J, mode) / J for _ in range(3))
+        res[mode] = round(ts[1], 2)  # median of three runs, per layer
+    for i, L in enumerate(layers):
+        L["check"](ks[i] - 1)
+    flops = 2.0 * M * Nn * K
+    out = {
+        "metric": "time per layer: codec pipelined beside a bf16 GEMM (encode of the next layer on its own stream)",
+        "value": res["pipe"], "unit": "us", "higher_is_better": False, "n_gpus": 1,
+        "steps": J, "warmup": args.warmup, "dtype": f"{'u32' if layers[0]['E'] == 4 else 'u16'}+bf16",
+        "data": "synthetic",
+        "config": {"workload": workload_name(args), "change_frac": args.frac, "gemm_mnk": [M, Nn, K],
+                   "layers": "two OLMoE-shaped layers alternating, own buffers and caches",
+                   "streams": "sender, receiver, compute (default priorities)"},
+        "per_layer_us": {"gemm_alone": res["gemm"], "codec_alone": res["codec"],
+                         "in_order_one_stream": res["seq"], "pipelined": res["pipe"]},
+        "gemm_tflops": round(flops / (res["gemm"] * 1e-6) / 1e12, 1),
+        "codec_hidden": round((res["seq"] - res["pipe"]) / res["codec"], 4),
+        "pipelined_over_gemm": round(res["pipe"] / res["gemm"], 4),
     }
     print(json.dumps(out), flush=True)
 
