@@ -545,12 +545,11 @@ ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream) {
   BatchImpl* b = impl(batch);
   if (b->magic != kDecMagic) return CIERA_ERR_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t* ctl = reinterpret_cast<const uint32_t*>(b->scratch);
   const DecItem* items = reinterpret_cast<const DecItem*>(b->scratch + b->off_items);
   for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
     const Group& g = b->g[gi];
     if (hipError_t e = launch_decode(g.dtype, g.unit, items, g.item0, g.nitems, g.tpr, g.world, b->status_dev,
-                                     ctl, b->batch_id, st))
+                                     b->batch_id, st))
       return device_error("decode launch", e);
   }
   b->launches += 1;

@@ -56,7 +56,7 @@ struct DecItem {
 };
 
 // Encode scratch layout (offsets in bytes from the scratch base):
-//   ctl    : u32 [batch id] (+ padding to 256 B)
+//   head   : u32 batch id (+ padding to 256 B)
 //   items  : EncItem per item, ordered by group
 //   counts : u32 per tile -- changed values of the tile, written by the split kernel
 //   stash  : u32 x cap per tile -- the tile's first cap changes in ascending order,
@@ -81,16 +81,16 @@ struct FinArgs {
   uint32_t item0, tpi, cap, pad;
 };
 
-// ctl: the control words at the start of a batch's scratch.  Every descriptor
-// carries the id of the batch that wrote it; kernels exit at once when the
-// descriptor they read belongs to another batch (the scratch was taken over).
+// The first 256 bytes of a batch's scratch hold its batch id.  Every descriptor
+// carries the id of the batch that wrote it, and every kernel takes its batch's
+// id as an argument: a descriptor of another batch (the scratch was prepared
+// anew for another batch) is skipped.
 hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0, uint32_t nitems, uint32_t wg_per_item,
                                 const uint32_t* counts, const uint32_t* stash, uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s);
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
-                         uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,
-                         uint32_t batch_id, hipStream_t s);
+                         uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id, hipStream_t s);
 hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n, hipStream_t s);
 
 }  // namespace ciera

@@ -170,19 +170,7 @@ __device__ __forceinline__ void store16(uint8_t* p, int cnt, const uint32_t v[16
   }
 }
 
-// 16 bytes (cache exponents) as four little-endian words.
-__device__ __forceinline__ void load_bytes16(const uint8_t* p, int cnt, bool aligned, uint32_t c[4]) {
-  if (cnt == 16 && aligned) {
-    const v4u a = ldg16(p);
-    c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
-  } else {
-    c[0] = c[1] = c[2] = c[3] = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < cnt) c[j >> 2] |= (uint32_t)gp(p)[j] << (8 * (j & 3));
-  }
-}
-
+// 16 bytes (cache exponents) stored from four little-endian words.
 __device__ __forceinline__ void store_bytes16(uint8_t* p, int cnt, bool aligned, const uint32_t c[4]) {
   if (cnt == 16 && aligned) {
     v4u a;
@@ -939,7 +927,7 @@ __global__ __launch_bounds__(kThreads) void encode_finish_tile_kernel(FinArgs f,
 template <int DT, int U>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __restrict__ items, uint32_t item0,
                                                           uint32_t tpr, uint32_t world, uint32_t* status_out,
-                                                          const uint32_t* ctl, uint32_t batch_id) {
+                                                          uint32_t batch_id) {
   constexpr int E = Tr<DT>::E;
   constexpr uint32_t T = (uint32_t)kDecRow * U;
   constexpr uint32_t BMW = (T / 64 + 31) / 32;  // words of per-tile block bits (B >= 64)
@@ -1333,12 +1321,12 @@ hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs&
 }
 
 static hipError_t launch_decode_part(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
-                                     uint32_t tpr, uint32_t world, uint32_t* status, const uint32_t* ctl,
-                                     uint32_t batch_id, hipStream_t s) {
+                                     uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id,
+                                     hipStream_t s) {
   (void)hipGetLastError();
   const dim3 grid(nitems * tpr * world), block(kDecThreads);
 #define CIERA_DEC(DT, U) \
-  hipLaunchKernelGGL((decode_kernel<DT, U>), grid, block, 0, s, items, item0, tpr, world, status, ctl, batch_id)
+  hipLaunchKernelGGL((decode_kernel<DT, U>), grid, block, 0, s, items, item0, tpr, world, status, batch_id)
   if (dtype == 1) {
     switch (u) {
       case 1: CIERA_DEC(1, 1); break;
@@ -1368,14 +1356,14 @@ static hipError_t launch_decode_part(int dtype, int u, const DecItem* items, uin
 }
 
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems, uint32_t tpr,
-                         uint32_t world, uint32_t* status, const uint32_t* ctl, uint32_t batch_id,
+                         uint32_t world, uint32_t* status, uint32_t batch_id,
                          hipStream_t s) {
   const uint64_t tpi = (uint64_t)tpr * world;
   if (tpi * kDecThreads >= ((uint64_t)1 << 32)) return hipErrorInvalidValue;  // one item alone too large
   const uint32_t per = (uint32_t)std::max<uint64_t>(1, kMaxGrid / tpi);
   for (uint32_t i = 0; i < nitems; i += per) {
     if (hipError_t e = launch_decode_part(dtype, u, items, item0 + i, std::min(per, nitems - i), tpr, world, status,
-                                          ctl, batch_id, s))
+                                          batch_id, s))
       return e;
   }
   return hipSuccess;
