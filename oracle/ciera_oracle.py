@@ -71,6 +71,7 @@ FP32 = 2
 FP16 = 3
 MODE_RAW = 0
 MODE_COMPRESSED = 1
+MODE_BLOCK = 2                     # the block-hash variant (R26-R28)
 PATCH_BYTES = 5                    # u32 index + u8 exponent
 
 # decode status bits
@@ -78,7 +79,8 @@ ST_MAGIC = 1       # bad magic or version
 ST_FIELD = 2       # dtype / block size / n / offset / rank / world / mode mismatch
 ST_LENGTH = 4      # total_len or n_changed inconsistent, or larger than the slot
 ST_PATCH = 8       # a patch index >= n, or indices not strictly ascending
-ST_BITMAP = 16     # bitmap disagrees with the patch list (unspecified if ST_PATCH)
+ST_BITMAP = 16     # bitmap disagrees with the patch list (unspecified if ST_PATCH), or
+                   # (block variant) its set bits are not n_changed or a tail bit is set
 
 # (name, byte offset, struct code) -- little-endian
 HEADER_FIELDS = [
@@ -303,12 +305,17 @@ def _check_header(s: np.ndarray, dtype: int, block_size: int, n: int, offset: in
         return ST_MAGIC, None
     if (h["dtype"] != dtype or h["block_size"] != block_size or h["n"] != n
             or h["offset"] != offset or h["rank"] != rank or h["world"] != world
-            or h["mode"] not in (MODE_RAW, MODE_COMPRESSED)):
+            or h["mode"] not in (MODE_RAW, MODE_COMPRESSED, MODE_BLOCK)):
         return ST_FIELD, None
     p = h["n_changed"]
-    if p > n or h["total_len"] > s.size:
+    if p > (n_blocks(n, block_size) if h["mode"] == MODE_BLOCK else n) or h["total_len"] > s.size:
         return ST_LENGTH, None
-    want = raw_len(n, dtype) if h["mode"] == MODE_RAW else comp_len(n, p, dtype, block_size)
+    if h["mode"] == MODE_RAW:
+        want = raw_len(n, dtype)
+    elif h["mode"] == MODE_COMPRESSED:
+        want = comp_len(n, p, dtype, block_size)
+    else:
+        want = block_comp_len(n, p, dtype, block_size)
     if h["total_len"] != want:
         return ST_LENGTH, None
     return 0, h
@@ -332,6 +339,8 @@ def decode_stream(s: np.ndarray, dtype: int, block_size: int, n: int, offset: in
     sm = unpack_sm(s[pos:pos + sms], dtype, n)
     pos += sms
     ex = np.array(cache_slice, dtype=np.uint8, copy=True)   # previous exponents
+    if h["mode"] == MODE_BLOCK:
+        return _decode_blocks(s, pos, h["n_changed"], n, block_size, sm, ex, dtype)
     p = h["n_changed"]
     if p > 0:
         nbm = bitmap_bytes(n, block_size)
@@ -441,4 +450,138 @@ def select(gains: Sequence[int], cache_bytes: Sequence[int], budget: int) -> Lis
         out[i] = 1
         used += cache_bytes[i]
     return out
+
+
+# ------------------------------------------------------- block-hash variant
+# [CIERA 3.1; Appendix A, Algorithm 1] as the pages publish it: the sender
+# keeps a 128-bit hash of every block's exponents (HashCache, 16 bytes per
+# block instead of the exponents themselves), built from two independent
+# 64-bit SplitMix64 hashes [ref. 22 of the page]; a block whose hash differs
+# from the cached one is marked in the bitmap, its hash replaces the cached
+# one, and its exponents travel whole.  Readings:
+#   R26 the 64-bit hash of a block: its exponent bytes (one per value) as
+#       little-endian 8-byte words w_j, the last one zero-padded;
+#       H_s = mix64((sum_j mix64(w_j ^ (s + (j + 1) * GAMMA)) + L) mod 2^64)
+#       with L the block's byte length, mix64 SplitMix64's output function and
+#       GAMMA its increment; the position-keyed sum can be formed in parallel
+#       over a block's words (the word-wise hashing of the page's ref. [23]).
+#       The two halves use the seeds HASH_SEEDS.
+#   R27 the payload (the pages ANS-code it with a closed library): the
+#       exponent bytes of each changed block, in block order, B bytes per
+#       block, the last block zero-padded to B.  The stream is
+#       header (mode 2, n_changed = changed blocks) | sign|mantissa |
+#       [bitmap | payload] if any block changed; BLOCK only when strictly
+#       shorter than RAW (R8).
+#   R28 the receiver: cached exponents, the changed blocks replaced from the
+#       payload, merged with the sign|mantissa bits; bitmap set bits other
+#       than n_changed, or a set bit past the last block, is ST_BITMAP.
+# Parity unpinned against the pages: the hash's constants and word layout
+# (the pages name SplitMix64 but give no construction); the hash is sender
+# state and never travels, and the pins check that it marks exactly the blocks
+# whose exponents changed.
+
+MASK64 = (1 << 64) - 1
+GAMMA = 0x9E3779B97F4A7C15                           # SplitMix64 increment
+HASH_SEEDS = (0x243F6A8885A308D3, 0x13198A2E03707344)  # digits of pi, for two independent halves
+
+
+def mix64(z: int) -> int:
+    """SplitMix64's output function (Steele, Lea and Flood; 64-bit variant)."""
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+    return z ^ (z >> 31)
+
+
+def block_hash64(b: bytes, seed: int) -> int:
+    """R26: one 64-bit hash of a block's exponent bytes."""
+    L = len(b)
+    padded = bytes(b) + bytes(-L % 8)
+    acc = 0
+    for j in range(len(padded) // 8):
+        w = int.from_bytes(padded[8 * j:8 * j + 8], "little")
+        acc = (acc + mix64(w ^ ((seed + (j + 1) * GAMMA) & MASK64))) & MASK64
+    return mix64((acc + L) & MASK64)
+
+
+def block_hashes(ex: np.ndarray, block_size: int) -> np.ndarray:
+    """The 128-bit hash of every block of an exponent array: (blocks, 2) uint64."""
+    ex = np.asarray(ex, dtype=np.uint8).reshape(-1)
+    nb = n_blocks(ex.size, block_size)
+    out = np.zeros((nb, 2), dtype=np.uint64)
+    for k in range(nb):
+        b = ex[k * block_size:(k + 1) * block_size].tobytes()
+        out[k, 0] = block_hash64(b, HASH_SEEDS[0])
+        out[k, 1] = block_hash64(b, HASH_SEEDS[1])
+    return out
+
+
+def hash_seed(x: np.ndarray, dtype: int, block_size: int) -> np.ndarray:
+    """HashCache of a shard: the hash of each block's exponents (after warmup)."""
+    return block_hashes(exponent_field(np.asarray(x).reshape(-1), dtype), block_size)
+
+
+def block_comp_len(n: int, n_changed_blocks: int, dtype: int, block_size: int) -> int:
+    """Header + sign|mantissa (+ bitmap + B bytes per changed block)."""
+    base = HEADER_BYTES + sm_section_bytes(n, dtype)
+    if n_changed_blocks == 0:
+        return base
+    return base + bitmap_bytes(n, block_size) + n_changed_blocks * block_size
+
+
+def encode_block(x: np.ndarray, hashes: np.ndarray, dtype: int, block_size: int, compress: bool,
+                 offset: int = 0, rank: int = 0, world: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Sender side of the block-hash variant [CIERA Alg. 1 sender]: returns the
+    stream and the updated HashCache of the shard."""
+    x = np.ascontiguousarray(np.asarray(x).reshape(-1)).astype(int_dtype(dtype))
+    n = x.size
+    nb = n_blocks(n, block_size)
+    hashes = np.asarray(hashes, dtype=np.uint64).reshape(nb, 2)
+    ex = exponent_field(x, dtype)
+    sm = sign_mantissa_field(x, dtype)
+    new = block_hashes(ex, block_size)
+    changed = np.nonzero(np.any(new != hashes, axis=1))[0]
+    c = int(changed.size)
+    c_len = block_comp_len(n, c, dtype, block_size)
+    r_len = raw_len(n, dtype)
+    mode = MODE_BLOCK if (compress and c_len < r_len) else MODE_RAW
+    total = c_len if mode == MODE_BLOCK else r_len
+    hdr = pack_header(version=VERSION, dtype=dtype, mode=mode, block_size=block_size,
+                      n=n, n_changed=c, total_len=total, offset=offset, rank=rank, world=world)
+    out = np.zeros(total, dtype=np.uint8)
+    out[:HEADER_BYTES] = np.frombuffer(hdr, dtype=np.uint8)
+    if mode == MODE_RAW:
+        le = np.dtype(int_dtype(dtype)).newbyteorder("<")
+        out[HEADER_BYTES:] = x.astype(le).view(np.uint8)
+        return out, new
+    pos = HEADER_BYTES
+    out[pos:pos + sm_section_bytes(n, dtype)] = pack_sm(sm, dtype)
+    pos += sm_section_bytes(n, dtype)
+    if c == 0:
+        return out, new
+    nbm = bitmap_bytes(n, block_size)
+    bm = np.zeros(nbm, dtype=np.uint8)
+    np.bitwise_or.at(bm, changed // 8, (1 << (changed % 8)).astype(np.uint8))
+    out[pos:pos + nbm] = bm
+    pos += nbm
+    for j, k in enumerate(changed):          # whole blocks, the last zero-padded (R27)
+        blk = ex[k * block_size:(k + 1) * block_size]
+        out[pos + j * block_size:pos + j * block_size + blk.size] = blk
+    return out, new
+
+
+def _decode_blocks(s, pos, c, n, block_size, sm, ex, dtype):
+    """R28: replace the changed blocks of the cached exponents and merge."""
+    st = 0
+    if c > 0:
+        nb = n_blocks(n, block_size)
+        nbm = bitmap_bytes(n, block_size)
+        bm = s[pos:pos + nbm]
+        payload = s[pos + nbm:pos + nbm + c * block_size]
+        bits = np.unpackbits(bm, bitorder="little")
+        if np.any(bits[nb:]) or int(bits[:nb].sum()) != c:
+            st |= ST_BITMAP
+        for j, k in enumerate(np.nonzero(bits[:nb])[0][:c]):
+            L = min(block_size, n - k * block_size)
+            ex[k * block_size:k * block_size + L] = payload[j * block_size:j * block_size + L]
+    return join_fields(sm, ex, dtype), ex, st
 

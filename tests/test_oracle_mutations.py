@@ -10,6 +10,7 @@ from oracle import ciera_oracle as O
 from tests import test_oracle_brute_plan as TB
 from tests import test_oracle_fields as TF
 from tests import test_oracle_stream as TS
+from tests import test_oracle_block as TBk
 from tests import test_select as TSel
 
 PINS = [
@@ -31,6 +32,11 @@ PINS = [
     TB.test_corruption_classes,
     lambda: [TSel.test_select_table(r) for r in TSel.SELECT_TABLE],
     TSel.test_low_change_shards_rank_first,
+    TBk.test_splitmix64_published_outputs,
+    TBk.test_block_hash_position_length_and_avalanche,
+    TBk.test_known_answer_block_stream,
+    TBk.test_block_round_trip_all_bf16_patterns,
+    TBk.test_block_decode_status_classes,
 ]
 
 
@@ -190,6 +196,35 @@ def _select_variant(ascending=False, by_gain=False, skip_misfits=False, ties_rev
     return sel
 
 
+def _hash_without_position(b, seed):
+    L = len(b)
+    padded = bytes(b) + bytes(-L % 8)
+    acc = 0
+    for j in range(len(padded) // 8):
+        w = int.from_bytes(padded[8 * j:8 * j + 8], "little")
+        acc = (acc + O.mix64(w ^ seed)) & O.MASK64
+    return O.mix64((acc + L) & O.MASK64)
+
+
+def _mix64_wrong_shift(z):
+    z = ((z ^ (z >> 31)) * 0xBF58476D1CE4E5B9) & O.MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & O.MASK64
+    return z ^ (z >> 31)
+
+
+def _block_len_unpadded(orig):
+    def bl(n, c, dtype, B):
+        full = orig(n, c, dtype, B)
+        return full - (B - (n % B)) if c and n % B else full
+    return bl
+
+
+def _decode_blocks_ignores_payload(orig):
+    def dec(s, pos, c, n, B, sm, ex, dtype):
+        return O.join_fields(sm, ex, dtype), ex, 0
+    return dec
+
+
 MUTATIONS = {
     "exponent shift off by one bit": lambda mp: mp.setattr(O, "exponent_field", _wrong_exp_shift),
     "sign bit dropped": lambda mp: mp.setattr(O, "sign_mantissa_field", _sm_without_sign),
@@ -211,6 +246,10 @@ MUTATIONS = {
     "selection ranked by gain alone": lambda mp: mp.setattr(O, "select", _select_variant(by_gain=True)),
     "selection skips a misfit and goes on": lambda mp: mp.setattr(O, "select", _select_variant(skip_misfits=True)),
     "selection breaks ties against input order": lambda mp: mp.setattr(O, "select", _select_variant(ties_reversed=True)),
+    "block hash without position key": lambda mp: mp.setattr(O, "block_hash64", _hash_without_position),
+    "SplitMix64 mix with a wrong shift": lambda mp: mp.setattr(O, "mix64", _mix64_wrong_shift),
+    "block payload last block unpadded": lambda mp: mp.setattr(O, "block_comp_len", _block_len_unpadded(O.block_comp_len)),
+    "block decode ignores the payload": lambda mp: mp.setattr(O, "_decode_blocks", _decode_blocks_ignores_payload(O._decode_blocks)),
 }
 
 
