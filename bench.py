@@ -42,7 +42,8 @@ DTYPES = {"bf16": ("bfloat16", 2, "int16"), "fp16": ("float16", 2, "int16"), "fp
 
 
 def workload_name(args):
-    return f"olmoe_moe_layer_{args.dtype}_" + ("clustered" if args.clustered else "uniform")
+    return (f"olmoe_moe_layer_{args.dtype}_" + ("clustered" if args.clustered else "uniform")
+            + ("_blockhash" if getattr(args, "variant", "patches") == "block" else ""))
 
 
 def log(*a):
@@ -57,6 +58,9 @@ def parse():
     ap.add_argument("--frac", type=float, default=0.01)
     ap.add_argument("--clustered", action="store_true")
     ap.add_argument("--dtype", choices=sorted(DTYPES), default="bf16")
+    ap.add_argument("--variant", choices=["patches", "block"], default="patches",
+                    help="patches: per-value (index, exponent) records, as planned; block: the pages' "
+                         "block-hash variant for every tensor")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -147,7 +151,8 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(specs, w0, w1, wl["world"], wl["block"], A, args.cpu_seconds, args.dtype)
+        cpu = cpu_baseline(specs, w0, w1, wl["world"], wl["block"], A, args.cpu_seconds, args.dtype,
+                           wl["variant"] == "block")
 
     out = {
         "metric": f"encode/decode GB/s ({args.dtype} OLMoE MoE layer, {args.frac * 100:g}% exp change) "
@@ -185,7 +190,7 @@ def main():
             "condition": "each launch alone, after a 1 GiB read of other data (Infinity Cache clean, "
                          "inputs in HBM)"},
         "compression_ratio": round(wl["raw_bytes"] / wl["stream_bytes"], 4),
-        "changed_exponents": wl["P_total"],
+        ("changed_blocks" if wl["variant"] == "block" else "changed_exponents"): wl["P_total"],
         "roofline": {"bound": "hbm", "kernel": f"decode_kernel<{args.dtype},2>",
                      "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -244,7 +249,7 @@ def setup(args):
     tdt, idt = getattr(torch, tname), getattr(torch, iname)
     tag = f"bench-{args.frac}-{'c' if args.clustered else 'u'}" + ("" if args.dtype == "bf16" else "-" + args.dtype)
     cfg = W.PairConfig(tag, dtype=tdt, frac=args.frac, clustered=args.clustered)
-    world, block = 16, 512
+    world, blk = 16, 512
     shapes = [(s.rows, s.cols) for s in specs]
     N = sum(s.numel for s in specs)
     ppm = int(round(args.frac * 1e6))
@@ -260,8 +265,8 @@ def setup(args):
     torch.cuda.synchronize()
     log(f"generated {N} weights in {time.time() - t0:.1f}s")
 
-    A = LayerCodec(shapes, tdt, world, block, dev, ppm)
-    Bc = LayerCodec(shapes, tdt, world, block, dev, ppm, cache=A.cache)
+    A = LayerCodec(shapes, tdt, world, blk, dev, ppm)
+    Bc = LayerCodec(shapes, tdt, world, blk, dev, ppm, cache=A.cache)
 
     def shards(ws, r):
         out = []
@@ -270,13 +275,21 @@ def setup(args):
             out.append(ws[i].reshape(-1)[off:off + n])
         return out
 
-    # cache <- exp(W0); state A streams (W1 vs exp(W0)) for all ranks
+    # cache <- exp(W0); state A streams (W1 vs exp(W0)) for all ranks.  The
+    # block variant keeps per-rank hash caches instead, seeded from W0 and
+    # shared by both states like the exponent cache.
+    block = args.variant == "block"
+    comp = [L.BLOCK] * len(specs) if block else None
     A.seed_cache(w0)
+    if block:
+        Bc.share_hash_caches(A)
+        for r in range(world):
+            A.seed_hashes(r, shards(w0, r))
     for r in range(world):
-        A.encode(r, shards(w1, r))
+        A.encode(r, shards(w1, r), compress=comp)
     stA = A.decode()
     for r in range(world):
-        Bc.encode(r, shards(w0, r))
+        Bc.encode(r, shards(w0, r), compress=comp)
     stB = Bc.decode()
     torch.cuda.synchronize()
     assert stA.item() == 0 and stB.item() == 0, "decode reported corrupt streams"
@@ -294,6 +307,7 @@ def setup(args):
         q = h.view(torch.int64)  # 8 little-endian u64 per header
         return {"n": q[:, 2], "n_changed": q[:, 3], "total_len": q[:, 4], "mode": h[:, 7]}
 
+
     hA = headers(A)
     P_total = int(hA["n_changed"].sum())
     stream_bytes = int(hA["total_len"].sum())
@@ -302,15 +316,21 @@ def setup(args):
     enc_stream_bytes = int(hA["total_len"][r0].sum())
     n_enc = int(hA["n"][r0].sum())
     assert int(hA["n"].sum()) == N
-    dec_bytes = stream_bytes + N + E * N + P_total         # read streams + cache, write values + changed cache
-    enc_bytes = E * n_enc + n_enc + enc_stream_bytes       # read shard + cache slice, write streams
+    if block:  # n_changed counts changed blocks, each rewriting B cached exponents
+        nb_enc = sum(-(-int(n) // blk) for n in hA["n"][r0])
+        dec_bytes = stream_bytes + N + E * N + P_total * blk
+        enc_bytes = E * n_enc + 16 * nb_enc + int(hA["n_changed"][r0].sum()) * 16 + enc_stream_bytes
+    else:
+        dec_bytes = stream_bytes + N + E * N + P_total     # read streams + cache, write values + changed cache
+        enc_bytes = E * n_enc + n_enc + enc_stream_bytes   # read shard + cache slice, write streams
     log(f"P={P_total} ({P_total / N:.4%}), streams {stream_bytes} B vs raw {raw_bytes} B "
-        f"(ratio {raw_bytes / stream_bytes:.4f}), COMPRESSED streams {int((hA['mode'] == 1).sum())}/{len(hA['mode'])}")
+        f"(ratio {raw_bytes / stream_bytes:.4f}), {'BLOCK' if block else 'COMPRESSED'} streams "
+        f"{int((hA['mode'] != 0).sum())}/{len(hA['mode'])}")
 
     # prepared launches (tables uploaded once)
     plans_expected = [p.compress for p in A.plans]
-    encA = A.prepare_encode(0, shards(w1, 0))
-    encB = Bc.prepare_encode(0, shards(w0, 0))
+    encA = A.prepare_encode(0, shards(w1, 0), compress=comp)
+    encB = Bc.prepare_encode(0, shards(w0, 0), compress=comp)
 
     def step(k, stream, ev=None):
         codec, enc = (A, encA) if k % 2 == 0 else (Bc, encB)
@@ -341,7 +361,8 @@ def setup(args):
     def decode_only(k, stream):
         (A if k % 2 == 0 else Bc).decode(stream, zero_status=False)
 
-    return dict(specs=specs, A=A, Bc=Bc, w0=w0, w1=w1, N=N, n_enc=n_enc, world=world, block=block, E=E,
+    return dict(specs=specs, A=A, Bc=Bc, w0=w0, w1=w1, N=N, n_enc=n_enc, world=world, block=blk, E=E,
+                variant=args.variant,
                 ppm=ppm, step=step, check=check, encode_only=encode_only, decode_only=decode_only, dec_bytes=dec_bytes, enc_bytes=enc_bytes,
                 raw_bytes=raw_bytes, stream_bytes=stream_bytes, P_total=P_total)
 
@@ -500,7 +521,7 @@ def pipeline(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16"):
+def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16", block_variant=False):
     """The oracle, as it stands, on a bounded sample of the same workload:
     for whole tensors in layer order, encode rank 0's shard and decode the
     full tensor from all 16 streams, until the CPU time budget is spent.  Its
@@ -527,10 +548,14 @@ def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16"):
         streams = []
         for r in range(world):
             off, n = O.shard(s.rows, s.cols, world, r)
+            h0 = O.hash_seed(x0[off:off + n], odt, block) if block_variant else None  # sender state, untimed
             if r == 0:
                 t = time.perf_counter()
-            st = O.encode(x1[off:off + n], cache[off:off + n], odt, block, bool(codec.plans[i].compress),
-                          off, r, world)
+            if block_variant:
+                st, _ = O.encode_block(x1[off:off + n], h0, odt, block, True, off, r, world)
+            else:
+                st = O.encode(x1[off:off + n], cache[off:off + n], odt, block, bool(codec.plans[i].compress),
+                              off, r, world)
             if r == 0:
                 t_enc += time.perf_counter() - t
                 gpu = codec.slot(i, 0)[:st.size].cpu().numpy()

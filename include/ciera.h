@@ -12,7 +12,7 @@
  *
  * Stream format (one stream per (tensor, rank); all integers little-endian):
  *   header, 64 bytes:
- *     [0,4) "CIER"  [4,6) version=1  [6] dtype  [7] mode (0 RAW, 1 COMPRESSED)
+ *     [0,4) "CIER"  [4,6) version=1  [6] dtype  [7] mode (0 RAW, 1 COMPRESSED, 2 BLOCK)
  *     [8,12) block size B  [12,16) 0  [16,24) n  [24,32) n_changed
  *     [32,40) total_len  [40,48) element offset of the shard in the tensor
  *     [48,52) rank  [52,56) world  [56,64) 0
@@ -25,11 +25,16 @@
  *     byte b/8, bit b%8: block b of B values holds a changed exponent), then
  *     n_changed records of 5 bytes (u32 shard-local index, u8 exponent) in
  *     strictly ascending index order.
+ *   BLOCK body (the block-hash variant, the pages' own change detection): the
+ *     n sign|mantissa records as above, then -- only if n_changed > 0, which
+ *     here counts changed blocks -- the bitmap (bit b: block b's exponents
+ *     changed) and the exponent bytes of every changed block, B bytes each in
+ *     block order, the last block zero-padded to B.
  *   RAW body: the n values as stored (2 or 4 bytes each).
  *   fp16 extends the pages' bf16/fp32 scope the same way; its layout is this
  *   library's reading, not a format of the pages.
- *   A stream is COMPRESSED only if the plan asked for it and it is strictly
- *   shorter than the RAW stream (64 + n*element bytes).
+ *   A stream is COMPRESSED (BLOCK) only if the caller asked for it and it is
+ *   strictly shorter than the RAW stream (64 + n*element bytes).
  *
  * Sharding: a tensor of rows x cols (row-major; a 1-D vector is rows=len,
  * cols=1) is split over W ranks by rows; rank r holds floor(R/W) + [r < R%W]
@@ -57,7 +62,7 @@
 extern "C" {
 #endif
 
-#define CIERA_ABI_VERSION 1u
+#define CIERA_ABI_VERSION 2u
 #define CIERA_HEADER_BYTES 64u
 
 typedef enum { CIERA_BF16 = 1, CIERA_FP32 = 2, CIERA_FP16 = 3 } ciera_dtype_t;
@@ -75,7 +80,8 @@ typedef enum {
 #define CIERA_ST_FIELD 2u  /* dtype, B, n, offset, rank, world or mode mismatch */
 #define CIERA_ST_LENGTH 4u /* total_len / n_changed inconsistent or beyond the slot */
 #define CIERA_ST_PATCH 8u  /* a patch index >= n, or indices not strictly ascending */
-#define CIERA_ST_BITMAP 16u /* bitmap disagrees with the patches (unspecified with ST_PATCH) */
+#define CIERA_ST_BITMAP 16u /* bitmap disagrees with the patches (unspecified with ST_PATCH); BLOCK:
+                               set bits other than n_changed, or a set bit past the last block */
 
 /* One logical tensor and how it is sharded.  block_size is B, a power of two in
  * [64, 4096] (the pages sweep 256..4096 and default to 512 [CIERA 4.1, 4.5]). */
@@ -141,9 +147,13 @@ ciera_status_t ciera_shard(const ciera_tensor_t* t, uint32_t rank, uint64_t* off
 typedef struct {
   ciera_tensor_t t;
   uint32_t rank;              /* < t.world */
-  uint32_t compress;          /* the plan's decision; 0 always writes RAW */
+  uint32_t compress;          /* 0 always RAW; 1 COMPRESSED (the plan's decision); 2 the
+                                 block-hash variant (BLOCK); each subject to the length rule */
   const void* shard;          /* n_r values of t.dtype; 16-byte aligned */
-  const uint8_t* cache_full;  /* N = rows*cols cached exponents; [off_r, off_r+n_r) is read */
+  const uint8_t* cache_full;  /* compress 0/1: N = rows*cols cached exponents; [off_r, off_r+n_r)
+                                 is read.  compress 2: the shard's hash cache instead --
+                                 16 bytes per block of B values (two little-endian u64),
+                                 16-byte aligned -- read and updated in place */
   uint8_t* stream;            /* output; 16-byte aligned */
   uint64_t stream_capacity;   /* >= 64 + n_r*e (the RAW length) */
 } ciera_encode_item_t;
@@ -220,6 +230,20 @@ ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t c
                                     uint32_t* status_dev, void* scratch, uint64_t scratch_bytes,
                                     ciera_batch_t* batch, void* stream);
 ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream);
+
+/* ciera_hash_update -- the block-hash variant's sender state [CIERA 3.1;
+ * Algorithm 1 (HashCache)]: for rank's shard of t (n_r values), hash_cache
+ * receives the 128-bit hash of every block's exponents, 16 bytes per block
+ * (ceil(n_r/B) blocks): two 64-bit halves, each
+ *   mix64((sum_j mix64(w_j ^ (seed + (j+1)*0x9E3779B97F4A7C15)) + L) mod 2^64)
+ * over the block's exponent bytes as little-endian 8-byte words w_j (the last
+ * zero-padded), L the block's length in bytes, mix64 the SplitMix64 output
+ * function, seeds 0x243F6A8885A308D3 and 0x13198A2E03707344.  Seeds the cache
+ * when reuse is switched on; encode with compress = 2 keeps it current.
+ * shard and hash_cache 16-byte aligned.  Errors: INVALID_ARG for a bad tensor,
+ * rank or pointer. */
+ciera_status_t ciera_hash_update(const ciera_tensor_t* t, uint32_t rank, const void* shard,
+                                 uint8_t* hash_cache, void* stream);
 
 /* ciera_cache_update -- cache_full[i] = exponent of weights_full[i] for the
  * whole tensor: seeds the cache when exponent reuse is switched on after

@@ -11,6 +11,7 @@ from typing import List, Optional, Sequence, Tuple
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libciera.so")
 
 CIERA_BF16, CIERA_FP32, CIERA_FP16 = 1, 2, 3
+RAW, COMPRESSED, BLOCK = 0, 1, 2  # encode item `compress` values and stream modes
 CIERA_OK, CIERA_ERR_INVALID_ARG, CIERA_ERR_BUFFER_TOO_SMALL, CIERA_ERR_UNSUPPORTED, CIERA_ERR_DEVICE = range(5)
 CIERA_ST_MAGIC, CIERA_ST_FIELD, CIERA_ST_LENGTH, CIERA_ST_PATCH, CIERA_ST_BITMAP = 1, 2, 4, 8, 16
 HEADER_BYTES = 64
@@ -19,6 +20,7 @@ HEADER_BYTES = 64
 EXPORTS = ["ciera_plan", "ciera_select", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
            "ciera_encode_prepare", "ciera_encode_launch", "ciera_decode_scratch_bytes",
            "ciera_decode", "ciera_decode_prepare", "ciera_decode_launch", "ciera_cache_update",
+           "ciera_hash_update",
            "ciera_status_str", "ciera_abi_version", "ciera_last_error"]
 
 
@@ -106,6 +108,7 @@ def _load() -> ctypes.CDLL:
                                          POINTER(Batch), c_void_p]),
         "ciera_decode_launch": (c_int, [POINTER(Batch), c_void_p]),
         "ciera_cache_update": (c_int, [POINTER(Tensor), c_void_p, c_void_p, c_void_p]),
+        "ciera_hash_update": (c_int, [POINTER(Tensor), c_uint32, c_void_p, c_void_p, c_void_p]),
         "ciera_status_str": (c_char_p, [c_int]),
         "ciera_abi_version": (c_uint32, []),
         "ciera_last_error": (c_char_p, []),
@@ -201,7 +204,7 @@ def ciera_decode_scratch_bytes(items: Sequence[DecodeItem]) -> int:
 def encode_item(t: Tensor, rank: int, compress: int, shard, cache_full, stream_buf,
                 capacity: Optional[int] = None) -> EncodeItem:
     cap = capacity if capacity is not None else stream_buf.numel() * stream_buf.element_size()
-    return EncodeItem(t, rank, 1 if compress else 0, _ptr(shard), _ptr(cache_full), _ptr(stream_buf), cap)
+    return EncodeItem(t, rank, int(compress), _ptr(shard), _ptr(cache_full), _ptr(stream_buf), cap)
 
 
 def decode_item(t: Tensor, streams, slot_bytes: int, out_full, cache_full) -> DecodeItem:
@@ -225,6 +228,11 @@ def ciera_decode(items: Sequence[DecodeItem], status, scratch, scratch_bytes: Op
 def ciera_cache_update(t: Tensor, weights_full, cache_full, stream=None) -> None:
     _check(_lib.ciera_cache_update(byref(t), _ptr(weights_full), _ptr(cache_full), _stream(stream)),
            "ciera_cache_update")
+
+
+def ciera_hash_update(t: Tensor, rank: int, shard, hash_cache, stream=None) -> None:
+    _check(_lib.ciera_hash_update(byref(t), rank, _ptr(shard), _ptr(hash_cache), _stream(stream)),
+           "ciera_hash_update")
 
 
 def ciera_encode_prepare(items: Sequence[EncodeItem], scratch, scratch_bytes: Optional[int] = None,

@@ -369,7 +369,9 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     const ciera_encode_item_t& it = items[i];
     uint64_t off, n;
     shard_of(&it.t, it.rank, &off, &n);
+    if (it.compress > kBlockVariant) return CIERA_ERR_INVALID_ARG;
     if (n && (!it.shard || !aligned(it.shard, 16) || !it.cache_full)) return CIERA_ERR_INVALID_ARG;
+    if (n && it.compress == kBlockVariant && !aligned(it.cache_full, 16)) return CIERA_ERR_INVALID_ARG;
     if (!it.stream || !aligned(it.stream, 16)) return CIERA_ERR_INVALID_ARG;
     if (it.stream_capacity < kHeader + n * elem_bytes(it.t.dtype)) return CIERA_ERR_BUFFER_TOO_SMALL;
   }
@@ -386,7 +388,10 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     shard_of(&it.t, it.rank, &off, &n);
     EncItem& d = di[j];
     d.x = static_cast<const uint8_t*>(it.shard);
-    d.cache = it.cache_full + off;
+    const bool blocks = it.compress == kBlockVariant;
+    // the block-hash variant reads and updates the shard's hash cache instead
+    d.cache = blocks ? nullptr : it.cache_full + off;
+    d.hashes = blocks ? const_cast<uint8_t*>(it.cache_full) : nullptr;
     d.stream = it.stream;
     d.n = n;
     d.off = off;
@@ -400,11 +405,11 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     d.rank = it.rank;
     d.world = it.t.world;
     d.block_size = it.t.block_size;
-    d.compress = it.compress ? 1u : 0u;
-    d.cache_aligned = aligned(d.cache, 16) ? 1u : 0u;
+    d.compress = blocks ? kBlockVariant : it.compress ? 1u : 0u;
+    d.cache_aligned = !blocks && aligned(d.cache, 16) ? 1u : 0u;
     d.elem_bytes = elem_bytes(it.t.dtype);
     d.batch_id = b->batch_id;
-    any |= d.compress;
+    any |= d.compress != 0;
     if (d.compress) max_bytes = std::max<uint64_t>(max_bytes, n * d.elem_bytes);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -563,6 +568,21 @@ ciera_status_t ciera_decode(const ciera_decode_item_t* items, uint32_t count, ui
   ciera_status_t s = ciera_decode_prepare(items, count, status_dev, scratch, scratch_bytes, &b, stream);
   if (s) return s;
   return ciera_decode_launch(&b, stream);
+}
+
+ciera_status_t ciera_hash_update(const ciera_tensor_t* t, uint32_t rank, const void* shard, uint8_t* hash_cache,
+                                 void* stream) {
+  ciera_status_t s = check_tensor(t);
+  if (s) return s;
+  if (rank >= t->world) return CIERA_ERR_INVALID_ARG;
+  uint64_t off, n;
+  shard_of(t, rank, &off, &n);
+  if (n == 0) return CIERA_OK;
+  if (!shard || !aligned(shard, 16) || !hash_cache || !aligned(hash_cache, 16)) return CIERA_ERR_INVALID_ARG;
+  if (hipError_t e = launch_hash_seed(t->dtype, static_cast<const uint8_t*>(shard), hash_cache, n, t->block_size,
+                                      reinterpret_cast<hipStream_t>(stream)))
+    return device_error("hash update launch", e);
+  return CIERA_OK;
 }
 
 ciera_status_t ciera_cache_update(const ciera_tensor_t* t, const void* weights_full, uint8_t* cache_full,

@@ -11,6 +11,7 @@ constexpr int kThreads = 256;          // one workgroup = 4 wave64
 constexpr int kEPT = 16;               // values per thread per chunk
 constexpr int kSub = kThreads * kEPT;  // 4096 values per chunk row of a tile
 constexpr uint64_t kHeader = 64;
+constexpr uint32_t kBlockVariant = 2;  // EncItem::compress of the block-hash variant; stream mode 2
 
 // Decode workgroups: kDecThreads threads, 16 values each per chunk row; a tile
 // is U chunk rows.  (512- and 1024-thread groups, which put more data behind
@@ -23,7 +24,8 @@ constexpr int kRecWords = (3 + 5 * kRecBatch + 3) / 4;  // aligned words that co
 // One encode item as the kernels see it.
 struct EncItem {
   const uint8_t* x;      // shard values
-  const uint8_t* cache;  // cache_full + offset of the shard
+  const uint8_t* cache;  // cache_full + offset of the shard (element variant)
+  uint8_t* hashes;       // the shard's hash cache, 16 bytes per block (block-hash variant)
   uint8_t* stream;
   uint64_t n;
   uint64_t off;
@@ -35,7 +37,7 @@ struct EncItem {
   uint32_t cap;            // records a tile stash holds
   uint32_t rank, world;
   uint32_t block_size;
-  uint32_t compress;
+  uint32_t compress;       // 0 RAW, 1 element patches, kBlockVariant the block-hash variant
   uint32_t cache_aligned;  // (cache_full + off) is 16-byte aligned
   uint32_t elem_bytes;     // 2 (bf16, fp16) or 4 (fp32)
   uint32_t batch_id;       // the batch that wrote this descriptor
@@ -92,5 +94,6 @@ hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs&
 hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
                          uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id, hipStream_t s);
 hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n, hipStream_t s);
+hipError_t launch_hash_seed(int dtype, const uint8_t* x, uint8_t* hashes, uint64_t n, uint32_t block_size, hipStream_t s);
 
 }  // namespace ciera

@@ -411,6 +411,25 @@ __device__ __forceinline__ void read_rec(const uint8_t* st, uint64_t recs, uint6
   rec_fields(load_rec(st, recs, p), idx, ex);
 }
 
+// 16 bytes at any alignment, as the aligned words that cover them: every word
+// read starts at or before the 16th byte, so it stays inside a buffer whose
+// end is 16-byte aligned.
+__device__ __forceinline__ v4u load16_any(const uint8_t* p) {
+  const uint32_t a = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 3u);
+  const G1 uint32_t* w = gp(reinterpret_cast<const uint32_t*>(p - a));
+  v4u v;
+  if (a == 0) {
+    v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+  } else {
+    const uint32_t x0 = w[0], x1 = w[1], x2 = w[2], x3 = w[3], x4 = w[4], sh = 8 * a;
+    v.x = (x0 >> sh) | (x1 << (32 - sh));
+    v.y = (x1 >> sh) | (x2 << (32 - sh));
+    v.z = (x2 >> sh) | (x3 << (32 - sh));
+    v.w = (x3 >> sh) | (x4 << (32 - sh));
+  }
+  return v;
+}
+
 // ORs decode status bits into the caller's word; a plain read first keeps a
 // stream of identical errors (every tile of a corrupt batch) from serializing
 // on one address.
@@ -533,6 +552,234 @@ __device__ __forceinline__ void put_record(uint8_t* stream, uint64_t capacity, u
   }
 }
 
+// ----------------------------------------------- block-hash variant (encode)
+// [CIERA 3.1; Algorithm 1] as published: a 128-bit hash per block of B values
+// (two 64-bit halves from SplitMix64's output function), compared with the
+// sender's cached hash; changed blocks travel whole.  The hash of a block's
+// exponent bytes, as little-endian 8-byte words w_j (zero-padded), L bytes:
+//   H_s = mix64((sum_j mix64(w_j ^ (s + (j + 1) * GAMMA)) + L) mod 2^64),
+// position-keyed so that the words of a block can be summed in parallel.
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;  // SplitMix64 increment
+constexpr uint64_t kSeedA = 0x243F6A8885A308D3ull, kSeedB = 0x13198A2E03707344ull;
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {  // SplitMix64 output function
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// The terms of one chunk's 16 exponent bytes (words 2*lc and 2*lc + 1 of its
+// block), of which the first `valid` bytes belong to the block.
+__device__ __forceinline__ void chunk_hash_terms(const uint32_t ex[4], uint32_t lc, uint32_t valid, uint64_t& ta,
+                                                 uint64_t& tb) {
+  const uint64_t w0 = ex[0] | ((uint64_t)ex[1] << 32), w1 = ex[2] | ((uint64_t)ex[3] << 32);
+  const uint64_t k0 = (uint64_t)(2 * lc + 1) * kGamma, k1 = (uint64_t)(2 * lc + 2) * kGamma;
+  ta = tb = 0;
+  if (valid > 0) {
+    ta += mix64(w0 ^ (kSeedA + k0));
+    tb += mix64(w0 ^ (kSeedB + k0));
+  }
+  if (valid > 8) {
+    ta += mix64(w1 ^ (kSeedA + k1));
+    tb += mix64(w1 ^ (kSeedB + k1));
+  }
+}
+
+// Sum over aligned groups of g lanes (g a power of two <= 64, uniform).
+__device__ __forceinline__ uint64_t group_sum(uint64_t v, uint32_t g) {
+  for (uint32_t o = 1; o < g; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// The 128-bit hashes of the blocks of one tile (S rows of 4096 values; ex[s]
+// are the exponent bytes of this thread's 16-value chunk of row s, zero past
+// n).  Afterwards the first thread of each block that starts before n has
+// lead[s] set and the block's hash in ha[s], hb[s].  Contains one barrier when
+// a block is wider than a wave (B > 1024); s_hp: 8 * S words of LDS.
+template <int S>
+__device__ __forceinline__ void tile_block_hashes(const uint32_t (&ex)[S][4], uint64_t base, uint64_t n, uint32_t B,
+                                                  uint64_t* s_hp, bool (&lead)[S], uint64_t (&ha)[S],
+                                                  uint64_t (&hb)[S]) {
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t cpb = B >> 4;  // chunks per block, 4 .. 256: the block lies inside one row
+  const uint32_t g = min(cpb, 64u);
+  uint64_t L[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+    const uint64_t b0 = c0 & ~(uint64_t)(B - 1);  // the block's first value
+    const uint32_t lc = (uint32_t)((c0 - b0) >> 4);
+    L[s] = b0 < n ? min<uint64_t>(B, n - b0) : 0;
+    const uint32_t valid = L[s] > 16ull * lc ? (uint32_t)min<uint64_t>(16, L[s] - 16ull * lc) : 0u;
+    uint64_t ta, tb;
+    chunk_hash_terms(ex[s], lc, valid, ta, tb);
+    ha[s] = group_sum(ta, g);
+    hb[s] = group_sum(tb, g);
+    lead[s] = lc == 0 && L[s] > 0;
+    if (cpb > 64 && lane == 0) {
+      s_hp[2 * (s * 4 + wave)] = ha[s];
+      s_hp[2 * (s * 4 + wave) + 1] = hb[s];
+    }
+  }
+  if (cpb > 64) {  // uniform: the waves of a block meet in LDS
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (lead[s]) {
+        ha[s] = hb[s] = 0;
+        for (uint32_t w = wave; w < wave + (cpb >> 6); ++w) {
+          ha[s] += s_hp[2 * (s * 4 + w)];
+          hb[s] += s_hp[2 * (s * 4 + w) + 1];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (lead[s]) {
+      ha[s] = mix64(ha[s] + L[s]);
+      hb[s] = mix64(hb[s] + L[s]);
+    }
+  }
+}
+
+// One tile of the split kernel for an item of the block-hash variant: the
+// sign|mantissa stores, the blocks' hashes against the cached ones (d.hashes
+// is the shard's hash cache, 16 bytes per block, updated in place), the tile's
+// bitmap bytes, its count of changed blocks, and the exponent bytes of its
+// changed blocks, B per block in block order, into its stash (T bytes: every
+// block fits).
+template <int DT, int S>
+__device__ void split_tile_block(const EncItem& d, uint32_t local, const EncArgs& a) {
+  constexpr int E = Tr<DT>::E;
+  constexpr uint32_t T = (uint32_t)kSub * S;
+  constexpr int XW = 4 * E;
+  __shared__ uint64_t s_hp[8 * S];
+  __shared__ uint32_t s_flag[T / 64];  // changed flag per block of the tile (B >= 64)
+  const uint32_t tid = threadIdx.x;
+  const uint64_t base = (uint64_t)local * T;
+  const uint64_t n = d.n;
+  const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;
+
+  uint32_t xw[S][XW], expk[S][4];
+  int cnt[S];
+  uint64_t ch[S][2];  // cached hash of the block this thread leads
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+    cnt[s] = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
+    if (cnt[s] > 0) load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
+    ch[s][0] = ch[s][1] = 0;
+    if ((c0 & (B - 1)) == 0 && c0 < n) {
+      const v4u h = ldg16(d.hashes + 16 * (c0 >> lb));
+      ch[s][0] = h.x | ((uint64_t)h.y << 32);
+      ch[s][1] = h.z | ((uint64_t)h.w << 32);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+    expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
+    if (cnt[s] > 0) {
+      const uint32_t none[4] = {0, 0, 0, 0};
+      (void)chunk_exps<DT, false>(xw[s], none, cnt[s], expk[s]);
+      chunk_store<DT>(d.stream, c0, cnt[s], xw[s], true);
+    }
+  }
+  bool lead[S];
+  uint64_t ha[S], hb[S];
+  tile_block_hashes<S>(expk, base, n, B, s_hp, lead, ha, hb);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (lead[s]) {
+      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+      const bool changed = ha[s] != ch[s][0] || hb[s] != ch[s][1];
+      if (changed) {
+        v4u h;
+        h.x = (uint32_t)ha[s]; h.y = (uint32_t)(ha[s] >> 32);
+        h.z = (uint32_t)hb[s]; h.w = (uint32_t)(hb[s] >> 32);
+        stg16(d.hashes + 16 * (c0 >> lb), h);
+      }
+      s_flag[(uint32_t)(c0 - base) >> lb] = changed ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
+  const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
+  if (tid == 0) {
+    uint32_t c = 0;
+    for (uint32_t k = 0; k < tblocks; ++k) c += s_flag[k];
+    gp(a.counts)[d.tile0 + local] = c;
+  }
+  // bitmap bytes, when a stream with a changed block can be BLOCK at all
+  const uint64_t nb = (n + B - 1) >> lb;
+  const uint64_t nbm = (nb + 7) / 8;
+  const uint64_t smsec = sm_sec<DT>(n);
+  if (smsec + nbm + B < n * E) {
+    const uint32_t tbytes = (tblocks + 7) / 8;
+    if (tid < tbytes) {
+      uint32_t byte = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (tid * 8 + (uint32_t)k < tblocks && s_flag[tid * 8 + k]) byte |= 1u << k;
+      gp(d.stream)[kHeader + smsec + (base >> (lb + 3)) + tid] = (uint8_t)byte;
+    }
+  }
+  // the exponent bytes of the changed blocks into the stash, compacted
+  uint8_t* st = reinterpret_cast<uint8_t*>(a.stash + d.stash + (uint64_t)local * d.cap);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+    const uint32_t blk = (uint32_t)(c0 - base) >> lb;
+    if (blk < tblocks && s_flag[blk]) {
+      uint32_t rank = 0;
+      for (uint32_t k = 0; k < blk; ++k) rank += s_flag[k];
+      v4u e;
+      e.x = expk[s][0]; e.y = expk[s][1]; e.z = expk[s][2]; e.w = expk[s][3];
+      stg16(st + (uint64_t)rank * B + ((uint32_t)(c0 - base) & (B - 1)), e);
+    }
+  }
+}
+
+// The hash cache of one shard (hash_update): every block's hash, one
+// workgroup per tile of S rows.
+template <int DT, int S>
+__global__ __launch_bounds__(kThreads) void hash_seed_kernel(const uint8_t* __restrict__ x, uint8_t* hashes, uint64_t n,
+                                                             uint32_t B) {
+  constexpr int E = Tr<DT>::E;
+  constexpr int XW = 4 * E;
+  __shared__ uint64_t s_hp[8 * S];
+  const uint32_t tid = threadIdx.x;
+  const uint64_t base = (uint64_t)blockIdx.x * kSub * S;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;
+  uint32_t xw[S][XW], expk[S][4];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+    const int cnt = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
+    expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
+    if (cnt > 0) {
+      load_words<XW>(x + c0 * E, (uint32_t)cnt * E, true, xw[s]);
+      const uint32_t none[4] = {0, 0, 0, 0};
+      (void)chunk_exps<DT, false>(xw[s], none, cnt, expk[s]);
+    }
+  }
+  bool lead[S];
+  uint64_t ha[S], hb[S];
+  tile_block_hashes<S>(expk, base, n, B, s_hp, lead, ha, hb);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    if (lead[s]) {
+      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+      v4u h;
+      h.x = (uint32_t)ha[s]; h.y = (uint32_t)(ha[s] >> 32);
+      h.z = (uint32_t)hb[s]; h.w = (uint32_t)(hb[s] >> 32);
+      stg16(hashes + 16 * (c0 >> lb), h);
+    }
+  }
+}
+
 template <int DT, int S>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t batch_id) {
   constexpr int E = Tr<DT>::E;
@@ -547,6 +794,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
   const uint32_t local = blockIdx.x - rel_item * a.tpi;
   const EncItem d = a.items[item];
   if (d.batch_id != batch_id) return;  // the scratch holds another batch (uniform)
+  if (d.compress == kBlockVariant) {   // uniform
+    split_tile_block<DT, S>(d, local, a);
+    return;
+  }
   const uint64_t base = (uint64_t)local * T;
   const uint64_t n = d.n;
   const uint32_t B = d.block_size;
@@ -702,13 +953,14 @@ __device__ void rederive_tile(const EncItem& d, uint64_t j, uint32_t r0, uint64_
   }
 }
 
-// The 64-byte stream header (little-endian): "CIER", version 1, dtype, mode,
-// block size, n, changed values P, total length, offset, rank, world.
+// The 64-byte stream header (little-endian): "CIER", version 1, dtype, mode
+// (0 RAW, 1 COMPRESSED, 2 BLOCK), block size, n, changed values (blocks for
+// BLOCK) P, total length, offset, rank, world.
 template <int DT>
-__device__ __forceinline__ void write_header(const EncItem& d, uint64_t P, bool cmode, uint64_t total) {
+__device__ __forceinline__ void write_header(const EncItem& d, uint64_t P, uint32_t mode, uint64_t total) {
   uint32_t h[16];
   h[0] = 0x52454943u;  // "CIER"
-  h[1] = 1u | ((uint32_t)DT << 16) | ((cmode ? 1u : 0u) << 24);
+  h[1] = 1u | ((uint32_t)DT << 16) | (mode << 24);
   h[2] = d.block_size;
   h[3] = 0;
   h[4] = (uint32_t)d.n; h[5] = (uint32_t)(d.n >> 32);
@@ -730,6 +982,27 @@ __device__ __forceinline__ void raw_copy(const EncItem& d, uint64_t b0, uint64_t
   const uint64_t v1 = b0 + (b1 - b0) / 16 * 16;
   for (uint64_t i = b0 + 16 * gt; i < v1; i += 16 * gs) stg16(d.stream + kHeader + i, ldg16(d.x + i));
   for (uint64_t i = v1 + gt; i < b1; i += gs) gp(d.stream)[kHeader + i] = gp(d.x)[i];
+}
+
+// len bytes (a multiple of 16) from a 16-byte aligned source to dst at any
+// alignment; thread gt of gs.
+__device__ __forceinline__ void copy_to_stream(uint8_t* dst, const uint8_t* src, uint64_t len, uint64_t gt,
+                                               uint64_t gs) {
+  const uint32_t a = (uint32_t)(reinterpret_cast<uintptr_t>(dst) & 15u);
+  for (uint64_t i = gt; i < len / 16; i += gs) {
+    const v4u v = ldg16(src + 16 * i);
+    uint8_t* q = dst + 16 * i;
+    if (a == 0) {
+      stg16(q, v);
+    } else if ((a & 3u) == 0) {
+      G1 uint32_t* w = gp(reinterpret_cast<uint32_t*>(q));
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+      const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int b = 0; b < 16; ++b) gp(q)[b] = (uint8_t)(x[b >> 2] >> (8 * (b & 3)));
+    }
+  }
 }
 
 // LDS of one item's finishing work.
@@ -801,7 +1074,34 @@ __device__ void finish_item(const EncItem& d, const uint32_t* counts, const uint
   const uint64_t raw = kHeader + n * E;
   const bool cmode = d.compress != 0 && comp < raw;
 
-  if (g == 0 && tid == 0) write_header<DT>(d, P, cmode, cmode ? comp : raw);
+  if (d.compress == kBlockVariant) {  // uniform: block-hash variant, counts are changed blocks
+    const uint64_t bcomp = kHeader + smsec + (P ? nbm + P * B : 0);
+    const bool bmode = bcomp < raw;
+    if (g == 0 && tid == 0) write_header<DT>(d, P, bmode ? kBlockVariant : 0u, bmode ? bcomp : raw);
+    if (!bmode) {
+      raw_copy(d, 0, n * E, (uint64_t)g * kThreads + tid, (uint64_t)G * kThreads);
+      return;
+    }
+    uint32_t run = 0;  // changed blocks before the window
+    for (uint32_t w0 = 0; P > 0 && w0 < tpi; w0 += kWin) {  // uniform
+      uint32_t wtot = wtot0;
+      if (w0 > 0) {
+        __syncthreads();  // the previous window's LDS is no longer read
+        wtot = scan_window(w0, false, novf, rest);
+      }
+      const uint32_t nw = min(kWin, tpi - w0);
+      for (uint32_t i = g; i < nw; i += G) {  // this workgroup's tiles of the window
+        const uint32_t c = L.pre[i + 1] - L.pre[i];
+        if (c)
+          copy_to_stream(d.stream + kHeader + smsec + nbm + (uint64_t)(run + L.pre[i]) * B,
+                         reinterpret_cast<const uint8_t*>(stash + d.stash + ((uint64_t)w0 + i) * d.cap), (uint64_t)c * B,
+                         tid, kThreads);
+      }
+      run += wtot;
+    }
+    return;
+  }
+  if (g == 0 && tid == 0) write_header<DT>(d, P, cmode ? 1u : 0u, cmode ? comp : raw);
   if (d.compress != 0 && !cmode) {  // the compressed form is not shorter: RAW
     raw_copy(d, 0, n * E, (uint64_t)g * kThreads + tid, (uint64_t)G * kThreads);
     return;
@@ -899,7 +1199,21 @@ __global__ __launch_bounds__(kThreads) void encode_finish_tile_kernel(FinArgs f,
   const uint64_t comp = kHeader + smsec + (P ? nbm + 5 * P : 0);
   const uint64_t raw = kHeader + n * E;
   const bool cmode = d.compress != 0 && comp < raw;
-  if (local == 0 && tid == 0) write_header<DT>(d, P, cmode, cmode ? comp : raw);
+  if (d.compress == kBlockVariant) {  // uniform: block-hash variant
+    const uint64_t bcomp = kHeader + smsec + (P ? nbm + P * d.block_size : 0);
+    const bool bmode = bcomp < raw;
+    if (local == 0 && tid == 0) write_header<DT>(d, P, bmode ? kBlockVariant : 0u, bmode ? bcomp : raw);
+    if (!bmode) {
+      const uint64_t v0 = (uint64_t)local * d.tvals;
+      const uint64_t v1 = min<uint64_t>(n, v0 + d.tvals);
+      if (v0 < v1) raw_copy(d, v0 * E, v1 * E, tid, kThreads);
+    } else if (mine > 0) {
+      copy_to_stream(d.stream + kHeader + smsec + nbm + (uint64_t)excl * d.block_size,
+                     reinterpret_cast<const uint8_t*>(f.stash + sbase), (uint64_t)mine * d.block_size, tid, kThreads);
+    }
+    return;
+  }
+  if (local == 0 && tid == 0) write_header<DT>(d, P, cmode ? 1u : 0u, cmode ? comp : raw);
   if (d.compress != 0 && !cmode) {  // the compressed form is not shorter: this tile's part RAW
     const uint64_t v0 = (uint64_t)local * d.tvals;
     const uint64_t v1 = min<uint64_t>(n, v0 + d.tvals);
@@ -935,6 +1249,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   __shared__ uint32_t s_hdr[16];
   __shared__ uint32_t s_expbm[BMW];  // blocks of the tile that hold a patch
   __shared__ uint32_t s_ex[T / 4];   // the tile's exponents: cached, then patched in place
+  __shared__ uint32_t s_sum[kDecThreads / 64];
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t tpi = tpr * world;
@@ -999,11 +1314,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   if (s_hdr[0] != 0x52454943u || (s_hdr[1] & 0xFFFFu) != 1u) {
     bad = CIERA_ST_MAGIC;
   } else if (h_dtype != (uint32_t)DT || s_hdr[2] != B || h_n != n || h_off != off || s_hdr[12] != r ||
-             s_hdr[13] != world || h_mode > 1u) {
+             s_hdr[13] != world || h_mode > 2u) {
     bad = CIERA_ST_FIELD;
   } else {
-    const uint64_t want = h_mode == 0 ? kHeader + n * E : kHeader + sm_sec<DT>(n) + (P ? nbm + 5 * P : 0);
-    if (P > n || h_tot > d.slot || h_tot != want) bad = CIERA_ST_LENGTH;
+    const uint64_t want = h_mode == 0   ? kHeader + n * E
+                          : h_mode == 1 ? kHeader + sm_sec<DT>(n) + (P ? nbm + 5 * P : 0)
+                                        : kHeader + sm_sec<DT>(n) + (P ? nbm + P * B : 0);
+    if (P > (h_mode == 2 ? nb : n) || h_tot > d.slot || h_tot != want) bad = CIERA_ST_LENGTH;
   }
   if (bad) {
     if (t_in == 0 && tid == 0) report(status_out, bad);
@@ -1027,6 +1344,54 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     return;
   }
 
+  bool patched = false;  // uniform: some exponent of the tile comes from the stream
+  if (h_mode == kBlockVariant) {
+    // 3b. BLOCK: the tile's changed blocks come whole from the payload.  The
+    //     bitmap bits before the tile give the first one's place (their count,
+    //     summed over the workgroup); the tile's own bits go to LDS.
+    const uint64_t tb0 = ts >> lb, tb1 = (te + B - 1) >> lb;
+    const uint32_t nbt = (uint32_t)(tb1 - tb0);
+    const uint8_t* bm = st + kHeader + sm_sec<DT>(n);
+    const uint64_t pbase = kHeader + sm_sec<DT>(n) + nbm;
+    uint32_t before = 0, e = 0;
+    if (tid < BMW) s_expbm[tid] = 0;
+    if (P > 0) {  // the payload follows the bitmap: the bit-word loads stay inside the stream
+      for (uint64_t b = (uint64_t)tid * 32; b < tb0; b += 32ull * kDecThreads)
+        before += (uint32_t)__popc(bits_of(load_bits_w(bm, b), (uint32_t)min<uint64_t>(32, tb0 - b)));
+      if (tid * 32 < nbt) s_expbm[tid] = bits_of(load_bits_w(bm, tb0 + tid * 32), min(32u, nbt - tid * 32));
+      if (te == n && tid == 0 && (nb & 7u) != 0 && (gp(bm)[nbm - 1] >> (nb & 7u)) != 0) e |= CIERA_ST_BITMAP;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o);
+    if (lane == 0) s_sum[wave] = before;
+    __syncthreads();
+    uint32_t prefix = 0, mine = 0;
+#pragma unroll
+    for (int w = 0; w < kDecThreads / 64; ++w) prefix += s_sum[w];
+#pragma unroll
+    for (int w = 0; w < (int)BMW; ++w) mine += (uint32_t)__popc(s_expbm[w]);
+    if (te == n && tid == 0 && P > 0 && prefix + mine != P) e |= CIERA_ST_BITMAP;
+    if (e) report(status_out, e);
+    patched = mine > 0;
+    if (patched) {
+      uint8_t* const s_exb = reinterpret_cast<uint8_t*>(s_ex);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t vo = (uint32_t)u * kDecRow + tid * kEPT;  // value offset in the tile
+        const uint32_t bt = vo >> lb;
+        if (bt < nbt && ((s_expbm[bt >> 5] >> (bt & 31u)) & 1u)) {
+          uint32_t r = prefix;
+          for (uint32_t w = 0; w < (bt >> 5); ++w) r += (uint32_t)__popc(s_expbm[w]);
+          r += (uint32_t)__popc(s_expbm[bt >> 5] & ((1u << (bt & 31u)) - 1u));
+          if (r < P) {  // more set bits than n_changed: reported above, read nothing past the payload
+            const v4u v = load16_any(st + pbase + (uint64_t)r * B + (vo & (B - 1)));
+            *reinterpret_cast<v4u*>(s_exb + vo) = v;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  } else {
   // 3. COMPRESSED: this tile's patch range [lo, hi).  Every wave finds it on its
   //    own (two searches sharing a first round of 64 probes, then 32 lanes per
   //    key), so the records can be read without a barrier in between.
@@ -1084,7 +1449,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   //    the tile's bitmap bits.  A record's predecessor, for the ascending-order
   //    check, is the thread's previous record or the last one of the lane
   //    below (lane 0 reads it).
-  const bool patched = hi > lo;  // uniform
+  patched = hi > lo;
   const uint64_t tb0 = ts >> lb, tb1 = (te + B - 1) >> lb;
   const uint32_t nbt = (uint32_t)(tb1 - tb0);
   const uint8_t* bm = st + kHeader + sm_sec<DT>(n);
@@ -1173,6 +1538,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     }
   }
   if (P > 0) __syncthreads();
+
+  // 5. bitmap check: the tile's bits mark exactly the blocks that hold patches
+  if (P > 0) {
+    uint32_t e = 0;
+    if (bm_mine && bm_got != s_expbm[tid]) e |= CIERA_ST_BITMAP;
+    if (bm_tail != 0) e |= CIERA_ST_BITMAP;
+    if (e) report(status_out, e);
+  }
+  }  // COMPRESSED
+
   uint32_t ex[U][4];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -1182,14 +1557,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
       const v4u e = *reinterpret_cast<const v4u*>(&s_ex[((uint32_t)u * kDecRow + tid * kEPT) / 4]);
       ex[u][0] = e.x; ex[u][1] = e.y; ex[u][2] = e.z; ex[u][3] = e.w;
     }
-  }
-
-  // 5. bitmap check: the tile's bits mark exactly the blocks that hold patches
-  if (P > 0) {
-    uint32_t e = 0;
-    if (bm_mine && bm_got != s_expbm[tid]) e |= CIERA_ST_BITMAP;
-    if (bm_tail != 0) e |= CIERA_ST_BITMAP;
-    if (e) report(status_out, e);
   }
 
   // 6. merge and store; write back the cache lines that changed
@@ -1367,6 +1734,20 @@ hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0,
       return e;
   }
   return hipSuccess;
+}
+
+// One workgroup per row of 4096 values: a block (B <= 4096) lies inside one row.
+hipError_t launch_hash_seed(int dtype, const uint8_t* x, uint8_t* hashes, uint64_t n, uint32_t block_size, hipStream_t s) {
+  const uint64_t tiles = (n + kSub - 1) / kSub;
+  if (tiles == 0) return hipSuccess;
+  if (tiles >= ((uint64_t)1 << 31)) return hipErrorInvalidValue;
+  (void)hipGetLastError();
+  const dim3 grid((uint32_t)tiles), block(kThreads);
+  if (dtype == 1) hipLaunchKernelGGL((hash_seed_kernel<1, 1>), grid, block, 0, s, x, hashes, n, block_size);
+  else if (dtype == 2) hipLaunchKernelGGL((hash_seed_kernel<2, 1>), grid, block, 0, s, x, hashes, n, block_size);
+  else if (dtype == 3) hipLaunchKernelGGL((hash_seed_kernel<3, 1>), grid, block, 0, s, x, hashes, n, block_size);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n, hipStream_t s) {

@@ -73,6 +73,7 @@ class LayerCodec:
                                        dtype=torch.uint8, device=self.device)
         self._dec_batch = None
         self._enc_scratch = None
+        self._hashes = None
 
     # ------------------------------------------------------------------ views
     def shard(self, i: int, rank: int) -> Tuple[int, int]:
@@ -95,14 +96,44 @@ class LayerCodec:
         for i, w in enumerate(weights):
             B.ciera_cache_update(self.tensors[i], w, self.cache.data_ptr() + self.cache_off[i], stream)
 
+    def hash_cache(self, i: int, rank: int) -> torch.Tensor:
+        """Sender state of the block-hash variant for (tensor i, rank): 16 bytes
+        per block of the shard (allocated on first use)."""
+        if self._hashes is None:
+            self._hash_off, h = {}, 0
+            for j, t in enumerate(self.tensors):
+                for r in range(self.world):
+                    _, n = self.shard(j, r)
+                    self._hash_off[(j, r)] = h
+                    h += _align(16 * (-(-n // t.block_size)), 256)
+            self._hashes = torch.zeros(max(h, 256), dtype=torch.uint8, device=self.device)
+        _, n = self.shard(i, rank)
+        o = self._hash_off[(i, rank)]
+        return self._hashes[o:o + 16 * (-(-n // self.tensors[i].block_size))]
+
+    def share_hash_caches(self, other: "LayerCodec") -> None:
+        """Use other's block-variant hash caches (same shapes), as `cache=` shares
+        the exponent cache: two codecs that alternate iterations of one layer."""
+        other.hash_cache(0, 0)
+        self._hashes, self._hash_off = other._hashes, other._hash_off
+
+    def seed_hashes(self, rank: int, shards: Sequence[torch.Tensor], stream=None) -> None:
+        """The block-hash variant's hash caches of rank's shards (reuse switched on)."""
+        for i, t in enumerate(self.tensors):
+            B.ciera_hash_update(t, rank, shards[i], self.hash_cache(i, rank).data_ptr(), stream)
+
     def encode_items(self, rank: int, shards: Sequence[torch.Tensor],
                      compress: Optional[Sequence[int]] = None) -> List[B.EncodeItem]:
+        """compress[i]: 0 RAW, 1 COMPRESSED (default: the plan's), 2 the block-hash
+        variant, which reads and updates rank's hash cache of tensor i."""
         items = []
         for i, t in enumerate(self.tensors):
             c = self.plans[i].compress if compress is None else compress[i]
             a = self.stream_off[i] + rank * self.slot_bytes[i]
-            items.append(B.encode_item(t, rank, c, shards[i], self.cache.data_ptr() + self.cache_off[i],
-                                       self.streams.data_ptr() + a, self.slot_bytes[i]))
+            state = (self.hash_cache(i, rank).data_ptr() if c == B.BLOCK
+                     else self.cache.data_ptr() + self.cache_off[i])
+            items.append(B.EncodeItem(t, rank, c, B._ptr(shards[i]), state,
+                                      self.streams.data_ptr() + a, self.slot_bytes[i]))
         return items
 
     def encode_scratch(self, items: Sequence[B.EncodeItem]) -> torch.Tensor:

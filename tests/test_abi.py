@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert L.ciera_abi_version() == 1
+    assert L.ciera_abi_version() == 2
     assert L.ciera_status_str(0) == "ok"
     assert "buffer" in L.ciera_status_str(2)
 

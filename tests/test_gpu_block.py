@@ -1,0 +1,173 @@
+"""GPU parity of the block-hash variant (the pages' own change detection,
+[CIERA 3.1; Appendix A, Algorithm 1]) against the oracle, byte for byte: hash
+caches after seeding and after encode, streams, rebuilt values, exponent
+caches and decode status."""
+import numpy as np
+import pytest
+import torch
+
+from gen import workloads as W
+from oracle import ciera_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from lossless_weight_compression_amd import _binding as B  # noqa: E402
+from lossless_weight_compression_amd.layer import LayerCodec  # noqa: E402
+from tests.gpu_harness import DT, say, to_np  # noqa: E402
+
+
+def _hashes_np(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view("<u8").reshape(-1, 2)
+
+
+def run_block(shapes, dtype, world, block, w0, w1, edits=None, variant=None):
+    """Seed exponent and hash caches from w0, encode w1 for every rank with the
+    block variant (or `variant` per tensor), optionally edit stream bytes, decode;
+    compare everything with the oracle.  Returns (gpu status, oracle status)."""
+    odt = DT[dtype]
+    codec = LayerCodec(shapes, dtype, world, block, "cuda", 10_000)
+    d0 = [x.to("cuda").contiguous() for x in w0]
+    d1 = [x.to("cuda").contiguous() for x in w1]
+    codec.seed_cache(d0)
+    variant = variant or [B.BLOCK] * len(shapes)
+
+    def shards(ws, r):
+        return [ws[i].reshape(-1)[slice(*(lambda o, n: (o, o + n))(*codec.shard(i, r)))].clone()
+                for i in range(len(shapes))]
+
+    o_hash = {}
+    for r in range(world):
+        codec.seed_hashes(r, shards(d0, r))
+    torch.cuda.synchronize()
+    for i, (rows, cols) in enumerate(shapes):
+        x0 = to_np(w0[i])
+        for r in range(world):
+            off, n = O.shard(rows, cols, world, r)
+            o_hash[(i, r)] = O.hash_seed(x0[off:off + n], odt, block)
+            assert np.array_equal(_hashes_np(codec.hash_cache(i, r)), o_hash[(i, r)]), f"hash seed {i} {r}"
+    for r in range(world):
+        codec.encode(r, shards(d1, r), compress=variant)
+    torch.cuda.synchronize()
+    for (i, r, o, b) in edits or []:
+        codec.slot(i, r)[o:o + len(b)] = torch.tensor(list(b), dtype=torch.uint8, device="cuda")
+    slots = [[codec.slot(i, r).cpu().numpy().copy() for r in range(world)] for i in range(len(shapes))]
+    st = codec.decode()
+    torch.cuda.synchronize()
+    g_status, o_status = int(st.item()), 0
+    for i, (rows, cols) in enumerate(shapes):
+        x1 = to_np(w1[i])
+        cache0 = O.cache_update(to_np(w0[i]), odt)
+        o_slots = []
+        for r in range(world):
+            off, n = O.shard(rows, cols, world, r)
+            if variant[i] == B.BLOCK:
+                s, h1 = O.encode_block(x1[off:off + n], o_hash[(i, r)], odt, block, True, off, r, world)
+                assert np.array_equal(_hashes_np(codec.hash_cache(i, r)), h1), f"hash cache {i} {r}"
+            else:
+                s = O.encode(x1[off:off + n], cache0[off:off + n], odt, block, bool(variant[i]), off, r, world)
+            if not edits:
+                got = slots[i][r][:s.size]
+                bad = np.nonzero(got != s)[0]
+                assert bad.size == 0, (i, r, bad[:8].tolist(), got[bad[:8]].tolist(), s[bad[:8]].tolist(), s.size)
+            pad = np.zeros(codec.slot_bytes[i], dtype=np.uint8)
+            pad[:s.size] = s
+            o_slots.append(pad)
+        for (ei, er, o, b) in edits or []:
+            if ei == i:
+                o_slots[er][o:o + len(b)] = np.frombuffer(bytes(b), dtype=np.uint8)
+        o_out, o_cache, ost = O.decode(o_slots, rows, cols, odt, block, world, cache0)
+        o_status |= ost
+        if not edits:
+            assert np.array_equal(to_np(codec.out_view(i)), x1), f"tensor {i}: decode(encode(x)) != x"
+            assert np.array_equal(codec.cache_view(i).cpu().numpy(), o_cache), f"tensor {i}: caches differ"
+    return g_status, o_status
+
+
+BLOCK_EDGE = [
+    # rows, cols, world, B, dtype, frac of values changing
+    (1, 1, 1, 512, torch.bfloat16, 1.0),
+    (17, 1, 16, 64, torch.bfloat16, 0.3),
+    (3, 5, 8, 512, torch.bfloat16, 0.2),          # ranks 3..7 hold no rows
+    (10, 3, 4, 64, torch.bfloat16, 0.05),         # shard offsets not 16-aligned
+    (10, 3, 4, 64, torch.float32, 0.05),
+    (33, 7, 2, 128, torch.float16, 0.02),
+    (1, 4097, 1, 512, torch.bfloat16, 0.001),     # one value past a tile
+    (2, 8193, 1, 64, torch.bfloat16, 0.0005),
+    (64, 1000, 4, 1024, torch.bfloat16, 0.0002),  # blocks wider than a wave
+    (64, 1000, 4, 2048, torch.float32, 0.0001),
+    (96, 4096, 2, 4096, torch.bfloat16, 0.00005),
+    (96, 4096, 2, 4096, torch.float16, 0.0),
+    (1000, 1000, 16, 512, torch.bfloat16, 0.0005),
+    (7168, 1, 16, 512, torch.bfloat16, 0.001),
+    (2101, 4096, 1, 512, torch.bfloat16, 0.00002),  # 1051 tiles: the windowed finishing kernel
+]
+
+
+@pytest.mark.parametrize("rows,cols,world,Bk,dtype,frac", BLOCK_EDGE)
+def test_block_variant_edge_shapes(rows, cols, world, Bk, dtype, frac):
+    say(f"[gpu] block variant {rows}x{cols} W={world} B={Bk} {dtype} f={frac}")
+    spec = W.TensorSpec("b", rows, cols)
+    w0 = [W.base_weights(spec, W.tensor_seed("blk", rows, cols, Bk), dtype)]
+    mask = W.mask_uniform(rows * cols, frac, W.tensor_seed("blk-m", rows, cols, Bk))
+    w1 = [W.perturb_exact(w0[0], mask, W.tensor_seed("blk-p", rows, cols, Bk))]
+    g, o = run_block([(rows, cols)], dtype, world, Bk, w0, w1)
+    assert g == 0 and o == 0
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.0001, 0.001, 0.01])
+def test_block_variant_olmoe_expert_mixed_with_patches(frac):
+    """One OLMoE expert, 16 ranks: gate and down in the block variant, up with
+    element patches, in one batch."""
+    specs = W.olmoe_expert_specs()
+    say(f"[gpu] block variant expert f={frac}")
+    w0, w1 = [], []
+    for i, s in enumerate(specs):
+        a = W.base_weights(s, W.tensor_seed("blkx", i), torch.bfloat16)
+        m = W.mask_uniform(s.numel, frac, W.tensor_seed("blkx-m", i, frac))
+        w0.append(a)
+        w1.append(W.perturb_exact(a, m, W.tensor_seed("blkx-p", i, frac)))
+    g, o = run_block([(s.rows, s.cols) for s in specs], torch.bfloat16, 16, 512, w0, w1,
+                     variant=[B.BLOCK, B.COMPRESSED, B.BLOCK])
+    assert g == 0 and o == 0
+
+
+def test_block_variant_decode_status_classes():
+    rows, cols, world, Bk = 64, 900, 4, 64
+    spec = W.TensorSpec("c", rows, cols)
+    w0 = [W.base_weights(spec, W.tensor_seed("blkc"), torch.bfloat16)]
+    m = W.mask_uniform(rows * cols, 0.0005, W.tensor_seed("blkc-m"))
+    w1 = [W.perturb_exact(w0[0], m, W.tensor_seed("blkc-p"))]
+    n = 16 * cols
+    nb, nbm = O.n_blocks(n, Bk), O.bitmap_bytes(n, Bk)
+    assert nb % 8 != 0
+    # the unedited run, to read rank 1's header and bitmap
+    codec = LayerCodec([(rows, cols)], torch.bfloat16, world, Bk, "cuda", 10_000)
+    d0, d1 = w0[0].cuda(), w1[0].cuda()
+    codec.seed_cache([d0])
+    for r in range(world):
+        off, nn = codec.shard(0, r)
+        codec.seed_hashes(r, [d0.reshape(-1)[off:off + nn].clone()])
+        codec.encode(r, [d1.reshape(-1)[off:off + nn].clone()], compress=[B.BLOCK])
+    torch.cuda.synchronize()
+    s = codec.slot(0, 1).cpu().numpy()
+    h = O.parse_header(s)
+    assert h["mode"] == O.MODE_BLOCK and h["n_changed"] >= 2
+    bm0 = 64 + n
+    bm = s[bm0:bm0 + nbm]
+    k = int(np.nonzero(np.unpackbits(bm, bitorder="little")[:nb] == 0)[0][0])  # a clear bit
+    j = int(np.nonzero(np.unpackbits(bm, bitorder="little")[:nb])[0][0])       # a set bit
+    edits = {
+        "extra set bit": [(0, 1, bm0 + k // 8, bytes([int(bm[k // 8]) | (1 << (k % 8))]))],
+        "cleared bit": [(0, 1, bm0 + j // 8, bytes([int(bm[j // 8]) & ~(1 << (j % 8)) & 0xFF]))],
+        "tail bit": [(0, 1, bm0 + nbm - 1, bytes([int(bm[-1]) | 0x80]))],
+        "n_changed > blocks": [(0, 1, 24, (nb + 1).to_bytes(8, "little"))],
+        "total_len": [(0, 1, 32, (int(h["total_len"]) + 1).to_bytes(8, "little"))],
+        "mode 3": [(0, 1, 7, b"\x03")],
+    }
+    for name, e in edits.items():
+        say(f"[gpu] block corruption {name}")
+        g, o = run_block([(rows, cols)], torch.bfloat16, world, Bk, w0, w1, edits=e)
+        assert o != 0 and g == o, (name, g, o)
