@@ -503,15 +503,37 @@ def block_hash64(b: bytes, seed: int) -> int:
     return mix64((acc + L) & MASK64)
 
 
+def _mix64_np(z: np.ndarray) -> np.ndarray:
+    """mix64 elementwise on uint64 arrays (numpy's uint64 products wrap mod 2^64)."""
+    z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+    z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
 def block_hashes(ex: np.ndarray, block_size: int) -> np.ndarray:
-    """The 128-bit hash of every block of an exponent array: (blocks, 2) uint64."""
+    """The 128-bit hash of every block of an exponent array: (blocks, 2) uint64;
+    block_hash64 of each block, evaluated for all blocks at once."""
     ex = np.asarray(ex, dtype=np.uint8).reshape(-1)
-    nb = n_blocks(ex.size, block_size)
+    n = ex.size
+    nb = n_blocks(n, block_size)
     out = np.zeros((nb, 2), dtype=np.uint64)
-    for k in range(nb):
-        b = ex[k * block_size:(k + 1) * block_size].tobytes()
-        out[k, 0] = block_hash64(b, HASH_SEEDS[0])
-        out[k, 1] = block_hash64(b, HASH_SEEDS[1])
+    if nb == 0:
+        return out
+    wpb = block_size // 8                           # words per block (B >= 64)
+    padded = np.zeros(nb * block_size, dtype=np.uint8)
+    padded[:n] = ex
+    words = padded.view("<u8").reshape(nb, wpb).astype(np.uint64)
+    L = np.full(nb, block_size, dtype=np.uint64)
+    L[-1] = n - (nb - 1) * block_size
+    nwords = (L + np.uint64(7)) // np.uint64(8)      # words that belong to each block
+    j1 = np.arange(1, wpb + 1, dtype=np.uint64)      # j + 1
+    valid = np.arange(wpb)[None, :] < nwords[:, None].astype(np.int64)
+    with np.errstate(over="ignore"):
+        for h, seed in enumerate(HASH_SEEDS):
+            keys = np.uint64(seed) + j1 * np.uint64(GAMMA)
+            terms = np.where(valid, _mix64_np(words ^ keys[None, :]), np.uint64(0))
+            acc = terms.sum(axis=1, dtype=np.uint64)
+            out[:, h] = _mix64_np(acc + L)
     return out
 
 

@@ -67,6 +67,17 @@ def test_block_hash_position_length_and_avalanche():
     assert 31.0 < float(np.mean(flips)) < 33.0 and min(flips) > 8
 
 
+@pytest.mark.parametrize("n,B", [(1, 64), (64, 64), (65, 64), (1000, 64), (4096, 512), (5000, 4096), (9, 128)])
+def test_block_hashes_equal_the_scalar_definition(n, B):
+    """block_hashes (all blocks at once) against block_hash64 block by block."""
+    ex = np.random.default_rng(n).integers(0, 256, n).astype(np.uint8)
+    h = O.block_hashes(ex, B)
+    for k in range(O.n_blocks(n, B)):
+        b = ex[k * B:(k + 1) * B].tobytes()
+        assert int(h[k, 0]) == O.block_hash64(b, O.HASH_SEEDS[0])
+        assert int(h[k, 1]) == O.block_hash64(b, O.HASH_SEEDS[1])
+
+
 @pytest.mark.parametrize("dtype", [O.BF16, O.FP32, O.FP16])
 @pytest.mark.parametrize("B", [64, 512])
 def test_changed_blocks_match_exact_compare(dtype, B):
