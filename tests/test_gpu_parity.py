@@ -144,6 +144,41 @@ def test_many_tiles_and_stash_overflow(rows, cols, dtype, dense):
     assert h["mode"] == O.MODE_COMPRESSED and h["n_changed"] > 0
 
 
+# Decode searches of long patch lists (more than 2048 records in a stream),
+# whose first round probes around the place an even spread predicts: shards of
+# 256 decode tiles (2048 x 1024 at one rank) whose changes are spread evenly,
+# or sit far from where an even spread puts them.  (name, uniform rate,
+# (first tile, last tile, rate) of denser regions in 8192-value tiles)
+LONG_LISTS = [
+    ("even-10pct", 0.10, ()),
+    ("even-1.5pct", 0.015, ()),
+    ("first-tiles-only", 0.0, ((0, 1, 0.6),)),
+    ("last-tile-only", 0.0, ((255, 255, 0.6),)),
+    ("middle-cluster", 0.0005, ((100, 103, 0.6),)),
+    ("every-eighth-tile", 0.0, tuple((t, t, 0.3) for t in range(3, 256, 8))),
+    ("two-ends", 0.0, ((0, 0, 0.5), (250, 255, 0.2))),
+]
+
+
+@pytest.mark.parametrize("name,frac,dense", LONG_LISTS)
+def test_long_patch_lists(name, frac, dense):
+    T = 8192
+    rows, cols = 2048, 1024
+    say(f"[gpu] long patch list {name}")
+    spec = W.TensorSpec("long", rows, cols)
+    w0 = W.base_weights(spec, W.tensor_seed("long", name), torch.bfloat16)
+    mask = W.mask_uniform(rows * cols, frac, W.tensor_seed("long-m", name))
+    for k, (t0, t1, f) in enumerate(dense):
+        lo, hi = t0 * T, min(rows * cols, (t1 + 1) * T)
+        mask[lo:hi] |= W.mask_uniform(hi - lo, f, W.tensor_seed("long-d", name, k))
+    w1 = W.perturb_exact(w0, mask, W.tensor_seed("long-p", name))
+    case = Case([(rows, cols)], torch.bfloat16, 1)
+    res = case.run([w0], [w1], compress=[1])
+    assert res["status"] == 0 and res["ostatus"] == 0
+    h = O.parse_header(case.codec.slot(0, 0).cpu().numpy())
+    assert h["mode"] == O.MODE_COMPRESSED and h["n_changed"] > 2048
+
+
 def test_specials_and_all_bf16_patterns():
     """Every bf16 bit pattern (+-0, subnormals, Inf, all NaN payloads) survives."""
     say("[gpu] all 65536 bf16 patterns")
