@@ -305,11 +305,16 @@ def _check_header(s: np.ndarray, dtype: int, block_size: int, n: int, offset: in
         return ST_MAGIC, None
     if (h["dtype"] != dtype or h["block_size"] != block_size or h["n"] != n
             or h["offset"] != offset or h["rank"] != rank or h["world"] != world
-            or h["mode"] not in (MODE_RAW, MODE_COMPRESSED, MODE_BLOCK)):
+            or h["mode"] not in (MODE_RAW, MODE_COMPRESSED, MODE_BLOCK, MODE_CODED)):
         return ST_FIELD, None
     p = h["n_changed"]
     if p > (n_blocks(n, block_size) if h["mode"] == MODE_BLOCK else n) or h["total_len"] > s.size:
         return ST_LENGTH, None
+    if h["mode"] == MODE_CODED:  # R33: the chunk table gives the length, checked per chunk
+        base = HEADER_BYTES + sm_section_bytes(n, dtype)
+        ok = (h["total_len"] == base if p == 0
+              else h["total_len"] >= coded_comp_len(n, p, dtype, block_size, 0))
+        return (0, h) if ok else (ST_LENGTH, None)
     if h["mode"] == MODE_RAW:
         want = raw_len(n, dtype)
     elif h["mode"] == MODE_COMPRESSED:
@@ -341,6 +346,8 @@ def decode_stream(s: np.ndarray, dtype: int, block_size: int, n: int, offset: in
     ex = np.array(cache_slice, dtype=np.uint8, copy=True)   # previous exponents
     if h["mode"] == MODE_BLOCK:
         return _decode_blocks(s, pos, h["n_changed"], n, block_size, sm, ex, dtype)
+    if h["mode"] == MODE_CODED:
+        return _decode_coded(s, pos, h, n, block_size, sm, ex, dtype)
     p = h["n_changed"]
     if p > 0:
         nbm = bitmap_bytes(n, block_size)
@@ -607,3 +614,381 @@ def _decode_blocks(s, pos, c, n, block_size, sm, ex, dtype):
             ex[k * block_size:k * block_size + L] = payload[j * block_size:j * block_size + L]
     return join_fields(sm, ex, dtype), ex, st
 
+
+
+# ---------------------------------------- entropy-coded patches (mode 3)
+# [CIERA 3.1] the sender compresses the changed exponents with ANS; [CIERA
+# Alg. 1] ANS-encode on the sender, ANS-decode on the receiver.  The pages
+# name the coder (ANS, through a vendor library) but not its model or layout;
+# this mode codes each element patch -- the gap since the previous change and
+# the new exponent relative to the cached one -- with range ANS (Duda,
+# "Asymmetric numeral systems", 2009/2013), interleaved over several coder
+# states (Giesen, "Interleaved entropy coders", 2014).  Readings:
+#   R29 the shard is cut into chunks of 4096 values from value 0 (the last may
+#       be shorter); each chunk is coded on its own, so chunks decode in
+#       parallel.
+#   R30 a chunk with c changes is sent as rANS data when c <= 1024 and the
+#       data is shorter than the dense form, else dense: the chunk's new
+#       exponent bytes, zero-padded to a multiple of 4.  A chunk without
+#       changes sends nothing.
+#   R31 rANS data: L = min(64, ceil(c/8)) coder states; change j (in index
+#       order) goes to state j mod L.  Per change four symbols, in decode
+#       order: the gap bucket b = bit length of (gap + 1), where gap = index
+#       minus previous index minus 1 (the first change of a chunk counts from
+#       the chunk start, previous index -1); the b - 1 bits of gap + 1 below
+#       its leading one, as a uniform symbol; the exponent class (+1, -1, +2,
+#       -2, ..., +7, -7 modulo 256, or escape); for an escape the new exponent
+#       itself as a uniform 8-bit symbol.  Gap buckets use the frequencies of
+#       a geometric gap distribution with p = c / chunk length, computed in
+#       32-bit fixed point (``gap_bucket_freqs``); exponent classes use a
+#       fixed table (``DELTA_FREQ``).  Both sum to 2^12.
+#   R32 32-bit states kept in [2^16, 2^32), renormalized by 16-bit words.  The
+#       decoder goes through the changes L at a time and through the four
+#       symbols of each change as four sub-steps; after each sub-step every
+#       state below 2^16, in state order, takes the next word.  The encoder
+#       runs the same sub-steps backwards, each state starting at 2^16, and
+#       its final states open the chunk data: states (u32 each) | words (u16
+#       each) | a zero word when their number is odd.
+#   R33 stream (mode 3): header | sign|mantissa | [bitmap | zero bytes to a
+#       multiple of 4 from the stream start | chunk table | chunk data] if
+#       anything changed.  Chunk table: per chunk, two u32 -- the changes and
+#       the data bytes of this and all earlier chunks.  Mode 3 only when
+#       strictly shorter than RAW (R8).
+#   R34 decode checks: a chunk table entry that goes backwards, exceeds the
+#       chunk length or the data, has a byte count not a multiple of 4, data
+#       without changes or changes without data, rANS data shorter than its
+#       states, or a last entry other than (n_changed, data bytes) is
+#       ST_LENGTH and the chunk is not decoded.  Within a chunk, a change past
+#       its end, an exponent wider than the field, words missing or left
+#       over, a final state other than 2^16, or dense data whose differences
+#       from the cache number other than c, is ST_PATCH.  The bitmap verdict
+#       is unspecified alongside ST_LENGTH or ST_PATCH.
+# Parity unpinned against the pages (they fix no ANS model or layout); the
+# pins are the rANS definition's closed forms, its entropy bound, per-state
+# independence, and round trips.
+
+MODE_CODED = 3
+CHUNK = 4096
+CODED_MAX_PATCHES = 1024
+RANS_LOW = 1 << 16
+RANS_SCALE = 12
+GAP_BUCKETS = 13
+DELTA_FREQ = (2032, 2032) + (2,) * 12 + (8,)
+DELTA_ESCAPE = 14
+
+
+def pad4(v: int) -> int:
+    return (v + 3) & ~3
+
+
+def n_chunks(n: int) -> int:
+    return (n + CHUNK - 1) // CHUNK
+
+
+def chunk_length(n: int, k: int) -> int:
+    return min(CHUNK, n - k * CHUNK)
+
+
+def rans_lanes(c: int) -> int:
+    return min(64, (c + 7) // 8)
+
+
+def gap_bucket_freqs(c: int, length: int) -> List[int]:
+    """R31: frequencies (sum 2^12) of gap buckets 1..13 for a chunk of
+    `length` values holding c changes.  With q = 1 - c/length in 32-bit fixed
+    point, S[i] ~ q^(2^i - 1) is the chance that a gap is at least 2^i - 1;
+    bucket b (gaps 2^(b-1) - 1 .. 2^b - 2) gets S[b-1] - S[b], the last bucket
+    the rest.  Each frequency is that share of 2^12, at least 1; the largest
+    (first of equals) absorbs the rounding."""
+    q = ((length - c) << 32) // length
+    Q = [q]
+    for _ in range(GAP_BUCKETS - 2):
+        Q.append((Q[-1] * Q[-1]) >> 32)           # q^(2^i)
+    S = [1 << 32]
+    for i in range(GAP_BUCKETS - 1):
+        S.append((S[-1] * Q[i]) >> 32)            # q^(2^(i+1) - 1)
+    share = [S[b - 1] - S[b] for b in range(1, GAP_BUCKETS)] + [S[GAP_BUCKETS - 1]]
+    f = [max(1, v >> (32 - RANS_SCALE)) for v in share]
+    top = f.index(max(f))
+    f[top] += (1 << RANS_SCALE) - sum(f)
+    return f
+
+
+def _cum(freqs: Sequence[int]) -> List[int]:
+    out, t = [], 0
+    for v in freqs:
+        out.append(t)
+        t += v
+    return out
+
+
+def delta_class(old: int, new: int) -> int:
+    """R31: +1 -> 0, -1 -> 1, +2 -> 2, -2 -> 3, ..., +7 -> 12, -7 -> 13 (mod 256), else escape (14)."""
+    d = (new - old) & 0xFF
+    for k in range(1, 8):
+        if d == k:
+            return 2 * (k - 1)
+        if d == 256 - k:
+            return 2 * (k - 1) + 1
+    return DELTA_ESCAPE
+
+
+def class_delta(cls: int) -> int:
+    k = cls // 2 + 1
+    return k if cls % 2 == 0 else 256 - k
+
+
+def rans_encode(substeps: Sequence[Sequence[Tuple[int, int, int, int]]], lanes: int):
+    """rANS encoder over interleaved states (R32).  substeps lists, in decode
+    order, the symbols of each sub-step as (state, start, frequency, scale
+    bits), the frequencies of a symbol set summing to 2^scale.  The encoder
+    visits them backwards; before coding symbol s into state x it writes the
+    low 16 bits of x out while x >= f_s * 2^(32 - scale), then
+    x <- floor(x / f_s) * 2^scale + (x mod f_s) + start_s.  Returns the final
+    states and the words in the order the decoder reads them."""
+    x = [RANS_LOW] * lanes
+    emitted = []
+    for sub in reversed(substeps):
+        out = []
+        for lane, start, freq, scale in sub:
+            if x[lane] >= freq << (32 - scale):
+                out.append((lane, x[lane] & 0xFFFF))
+                x[lane] >>= 16
+            x[lane] = ((x[lane] // freq) << scale) + x[lane] % freq + start
+        emitted.append([w for _, w in sorted(out)])   # read in state order
+    words = [w for sub in reversed(emitted) for w in sub]
+    return x, words
+
+
+def _chunk_symbols(offs: Sequence[int], olds: Sequence[int], news: Sequence[int], length: int):
+    """R31: the chunk's changes as four sub-steps per round of L changes."""
+    c = len(offs)
+    L = rans_lanes(c)
+    gf = gap_bucket_freqs(c, length)
+    gc, dc = _cum(gf), _cum(DELTA_FREQ)
+    subs = []
+    prev = -1
+    for t in range((c + L - 1) // L):
+        A, Bs, C, D = [], [], [], []
+        for lane in range(L):
+            j = t * L + lane
+            if j >= c:
+                break
+            g = offs[j] - prev - 1
+            prev = offs[j]
+            b = (g + 1).bit_length()
+            A.append((lane, gc[b - 1], gf[b - 1], RANS_SCALE))
+            if b > 1:
+                Bs.append((lane, (g + 1) - (1 << (b - 1)), 1, b - 1))
+            cls = delta_class(olds[j], news[j])
+            C.append((lane, dc[cls], DELTA_FREQ[cls], RANS_SCALE))
+            if cls == DELTA_ESCAPE:
+                D.append((lane, news[j], 1, 8))
+        subs += [A, Bs, C, D]
+    return subs, L
+
+
+def encode_chunk(ex_chunk: np.ndarray, cache_chunk: np.ndarray) -> bytes:
+    """R30-R32: the data of one chunk (new exponents and cached ones)."""
+    ex_chunk = np.asarray(ex_chunk, dtype=np.uint8)
+    cache_chunk = np.asarray(cache_chunk, dtype=np.uint8)
+    length = int(ex_chunk.size)
+    offs = np.nonzero(ex_chunk != cache_chunk)[0]
+    c = int(offs.size)
+    if c == 0:
+        return b""
+    dense = bytes(ex_chunk) + bytes(pad4(length) - length)
+    if c > CODED_MAX_PATCHES:
+        return dense
+    subs, L = _chunk_symbols([int(v) for v in offs], [int(cache_chunk[v]) for v in offs],
+                             [int(ex_chunk[v]) for v in offs], length)
+    states, words = rans_encode(subs, L)
+    data = struct.pack(f"<{L}I", *states) + struct.pack(f"<{len(words)}H", *words)
+    if len(words) % 2:
+        data += bytes(2)
+    return data if len(data) < len(dense) else dense
+
+
+def coded_comp_len(n: int, n_changed: int, dtype: int, block_size: int, data_bytes: int) -> int:
+    """R33: header + sign|mantissa (+ bitmap, padding, chunk table and data)."""
+    base = HEADER_BYTES + sm_section_bytes(n, dtype)
+    if n_changed == 0:
+        return base
+    return pad4(base + bitmap_bytes(n, block_size)) + 8 * n_chunks(n) + data_bytes
+
+
+def encode_coded(x: np.ndarray, cache_slice: np.ndarray, dtype: int, block_size: int,
+                 compress: bool, offset: int = 0, rank: int = 0, world: int = 1) -> np.ndarray:
+    """Sender side with entropy-coded patches [CIERA 3.1 ANS-encode; R29-R33]."""
+    x = np.ascontiguousarray(np.asarray(x).reshape(-1)).astype(int_dtype(dtype))
+    cache_slice = np.asarray(cache_slice, dtype=np.uint8).reshape(-1)
+    n = x.size
+    if cache_slice.size != n:
+        raise ValueError("cache slice and shard differ in length")
+    ex = exponent_field(x, dtype)
+    sm = sign_mantissa_field(x, dtype)
+    changed = ex != cache_slice
+    P = int(np.count_nonzero(changed))
+    chunks = [encode_chunk(ex[k * CHUNK:k * CHUNK + chunk_length(n, k)],
+                           cache_slice[k * CHUNK:k * CHUNK + chunk_length(n, k)]) for k in range(n_chunks(n))] if P else []
+    c_len = coded_comp_len(n, P, dtype, block_size, sum(len(d) for d in chunks))
+    r_len = raw_len(n, dtype)
+    mode = MODE_CODED if (compress and c_len < r_len) else MODE_RAW
+    total = c_len if mode == MODE_CODED else r_len
+    hdr = pack_header(version=VERSION, dtype=dtype, mode=mode, block_size=block_size,
+                      n=n, n_changed=P, total_len=total, offset=offset, rank=rank, world=world)
+    out = np.zeros(total, dtype=np.uint8)
+    out[:HEADER_BYTES] = np.frombuffer(hdr, dtype=np.uint8)
+    if mode == MODE_RAW:
+        le = np.dtype(int_dtype(dtype)).newbyteorder("<")
+        out[HEADER_BYTES:] = x.astype(le).view(np.uint8)
+        return out
+    pos = HEADER_BYTES
+    out[pos:pos + sm_section_bytes(n, dtype)] = pack_sm(sm, dtype)
+    pos += sm_section_bytes(n, dtype)
+    if P == 0:
+        return out
+    nbm = bitmap_bytes(n, block_size)
+    blocks = np.unique(np.nonzero(changed)[0] // block_size)
+    bm = np.zeros(nbm, dtype=np.uint8)
+    np.bitwise_or.at(bm, blocks // 8, (1 << (blocks % 8)).astype(np.uint8))
+    out[pos:pos + nbm] = bm
+    pos = pad4(pos + nbm)
+    cc = cb = 0
+    table = bytearray()
+    for k, d in enumerate(chunks):
+        cc += int(np.count_nonzero(changed[k * CHUNK:k * CHUNK + chunk_length(n, k)]))
+        cb += len(d)
+        table += struct.pack("<II", cc, cb)
+    out[pos:pos + len(table)] = np.frombuffer(bytes(table), dtype=np.uint8)
+    pos += len(table)
+    data = b"".join(chunks)
+    out[pos:pos + len(data)] = np.frombuffer(data, dtype=np.uint8)
+    return out
+
+
+def rans_decode_chunk(data: bytes, c: int, length: int, cache_chunk: np.ndarray, emask: int):
+    """R31-R32, R34: decode one chunk's rANS data.  Returns (offsets, new
+    exponents, status); changes past the chunk or with an exponent wider than
+    the field are flagged and left out."""
+    L = rans_lanes(c)
+    x = list(struct.unpack_from(f"<{L}I", data, 0))
+    nw = (len(data) - 4 * L) // 2
+    words = struct.unpack_from(f"<{nw}H", data, 4 * L)
+    st = 0
+    ptr = 0
+    gf = gap_bucket_freqs(c, length)
+    gc, dc = _cum(gf), _cum(DELTA_FREQ)
+
+    def find(cum, freqs, slot):
+        s = 0
+        while s + 1 < len(cum) and cum[s + 1] <= slot:
+            s += 1
+        return s
+
+    def renorm():
+        nonlocal ptr, st
+        for lane in range(L):
+            if x[lane] < RANS_LOW:
+                if ptr < nw:
+                    w = words[ptr]
+                else:
+                    w = 0
+                    st |= ST_PATCH
+                ptr += 1
+                x[lane] = ((x[lane] << 16) | w) & 0xFFFFFFFF
+
+    offs, news = [], []
+    prev = -1
+    for t in range((c + L - 1) // L):
+        act = [lane for lane in range(L) if t * L + lane < c]
+        b, g, cls, esc = {}, {}, {}, {}
+        for lane in act:                      # gap bucket
+            slot = x[lane] & ((1 << RANS_SCALE) - 1)
+            s = find(gc, gf, slot)
+            x[lane] = gf[s] * (x[lane] >> RANS_SCALE) + slot - gc[s]
+            b[lane] = s + 1
+        renorm()
+        for lane in act:                      # bits of gap + 1 below the leading one
+            k = b[lane] - 1
+            v = x[lane] & ((1 << k) - 1)
+            x[lane] >>= k
+            g[lane] = (1 << k) + v - 1
+        renorm()
+        for lane in act:                      # exponent class
+            slot = x[lane] & ((1 << RANS_SCALE) - 1)
+            s = find(dc, DELTA_FREQ, slot)
+            x[lane] = DELTA_FREQ[s] * (x[lane] >> RANS_SCALE) + slot - dc[s]
+            cls[lane] = s
+        renorm()
+        for lane in act:                      # escaped exponent
+            if cls[lane] == DELTA_ESCAPE:
+                esc[lane] = x[lane] & 0xFF
+                x[lane] >>= 8
+        renorm()
+        for lane in act:                      # indices in change order
+            idx = prev + g[lane] + 1
+            prev = idx
+            if idx >= length:
+                st |= ST_PATCH
+                continue
+            new = esc[lane] if cls[lane] == DELTA_ESCAPE else (int(cache_chunk[idx]) + class_delta(cls[lane])) & 0xFF
+            if new > emask:
+                st |= ST_PATCH
+                continue
+            offs.append(idx)
+            news.append(new)
+    if ptr + (ptr & 1) != nw or any(v != RANS_LOW for v in x):
+        st |= ST_PATCH
+    return offs, news, st
+
+
+def _decode_coded(s, pos, h, n, block_size, sm, ex, dtype):
+    """R33-R34: receiver side of mode 3 (ex holds the cached exponents)."""
+    P = h["n_changed"]
+    st = 0
+    if P == 0:
+        return join_fields(sm, ex, dtype), ex, st
+    emask = _LAYOUT[dtype][1]
+    nbm = bitmap_bytes(n, block_size)
+    bm = s[pos:pos + nbm]
+    tpos = pad4(pos + nbm)
+    nch = n_chunks(n)
+    dpos = tpos + 8 * nch
+    D = h["total_len"] - dpos
+    table = struct.unpack_from(f"<{2 * nch}I", bytes(s[tpos:dpos]))
+    touched = np.zeros(n, dtype=bool)
+    pc = pb = 0
+    for k in range(nch):
+        cc, cb = table[2 * k], table[2 * k + 1]
+        length = chunk_length(n, k)
+        c, nbytes = cc - pc, cb - pb
+        bad = (cc < pc or cb < pb or cb > D or c > length or nbytes % 4 != 0 or (c == 0) != (nbytes == 0)
+               or (k == nch - 1 and (cc != P or cb != D)))
+        if not bad and c > 0 and nbytes != pad4(length) and nbytes < 4 * rans_lanes(c):
+            bad = True
+        if bad:
+            st |= ST_LENGTH
+        elif c > 0:
+            data = bytes(s[dpos + pb:dpos + cb])
+            base = k * CHUNK
+            old = ex[base:base + length].copy()
+            if nbytes == pad4(length):          # dense
+                new = np.frombuffer(data[:length], dtype=np.uint8)
+                if np.any(new > emask) or int(np.count_nonzero(new != old)) != c:
+                    st |= ST_PATCH
+                touched[base:base + length] = new != old
+                ex[base:base + length] = new
+            else:
+                offs, news, e = rans_decode_chunk(data, c, length, old, emask)
+                st |= e
+                for o, v in zip(offs, news):
+                    touched[base + o] = True
+                    ex[base + o] = v
+        pc, pb = cc, cb                         # the next chunk starts where this entry says
+    want = np.zeros(nbm, dtype=np.uint8)
+    blocks = np.unique(np.nonzero(touched)[0] // block_size)
+    np.bitwise_or.at(want, blocks // 8, (1 << (blocks % 8)).astype(np.uint8))
+    if not np.array_equal(want, bm):
+        st |= ST_BITMAP
+    return join_fields(sm, ex, dtype), ex, st

@@ -165,7 +165,7 @@ def test_block_variant_decode_status_classes():
         "tail bit": [(0, 1, bm0 + nbm - 1, bytes([int(bm[-1]) | 0x80]))],
         "n_changed > blocks": [(0, 1, 24, (nb + 1).to_bytes(8, "little"))],
         "total_len": [(0, 1, 32, (int(h["total_len"]) + 1).to_bytes(8, "little"))],
-        "mode 3": [(0, 1, 7, b"\x03")],
+        "mode 7": [(0, 1, 7, b"\x07")],
     }
     for name, e in edits.items():
         say(f"[gpu] block corruption {name}")

@@ -181,7 +181,7 @@ def test_block_decode_status_classes():
     assert st(lambda t: t.__setitem__(bm0 + nbm - 1, t[bm0 + nbm - 1] | 0x80)) == O.ST_BITMAP  # past the last block
     assert st(lambda t: t.__setitem__(slice(24, 32), np.frombuffer((17).to_bytes(8, "little"), np.uint8))) == O.ST_LENGTH
     assert st(lambda t: t.__setitem__(slice(32, 40), np.frombuffer((s.size + 1).to_bytes(8, "little"), np.uint8))) == O.ST_LENGTH
-    assert st(lambda t: t.__setitem__(7, 3)) == O.ST_FIELD
+    assert st(lambda t: t.__setitem__(7, 9)) == O.ST_FIELD
 
 
 def test_block_multi_iteration_carry():

@@ -12,6 +12,7 @@ from tests import test_oracle_fields as TF
 from tests import test_oracle_stream as TS
 from tests import test_oracle_block as TBk
 from tests import test_select as TSel
+from tests import test_oracle_coded as TC
 
 PINS = [
     TF.test_bf16_exponent_matches_frexp_exhaustive,
@@ -37,6 +38,19 @@ PINS = [
     TBk.test_known_answer_block_stream,
     TBk.test_block_round_trip_all_bf16_patterns,
     TBk.test_block_decode_status_classes,
+    TC.test_rans_worked_example,
+    TC.test_rans_uniform_symbols_exact_length,
+    TC.test_rans_table_symbols_entropy_bound,
+    TC.test_interleaved_states_match_single_state_coding,
+    TC.test_lane_counts,
+    TC.test_chunk_symbols_worked_by_hand,
+    TC.test_delta_classes,
+    lambda: [TC.test_gap_buckets_follow_the_geometric_model(c, L) for c, L in ((41, 4096), (3, 100), (2000, 3000))],
+    TC.test_gap_buckets_all_changed,
+    TC.test_known_answer_stream_layout,
+    TC.test_known_answer_padding_and_no_change,
+    TC.test_dense_threshold,
+    TC.test_round_trip_random_chunks_and_specials,
 ]
 
 
@@ -225,6 +239,88 @@ def _decode_blocks_ignores_payload(orig):
     return dec
 
 
+def _rans_without_start(subs, lanes):
+    x = [O.RANS_LOW] * lanes
+    em = []
+    for sub in reversed(subs):
+        out = []
+        for lane, start, f, k in sub:
+            if x[lane] >= f << (32 - k):
+                out.append((lane, x[lane] & 0xFFFF))
+                x[lane] >>= 16
+            x[lane] = ((x[lane] // f) << k) + x[lane] % f
+        em.append([w for _, w in sorted(out)])
+    return x, [w for sub in reversed(em) for w in sub]
+
+
+def _rans_words_in_emission_order(orig):
+    def enc(subs, lanes):
+        x, w = orig(subs, lanes)
+        return x, w[::-1]
+    return enc
+
+
+def _symbols_gap_without_minus_one(orig):
+    def sym(offs, olds, news, length):
+        subs, L = orig(offs, olds, news, length)
+        gf = O.gap_bucket_freqs(len(offs), length)
+        gc = [sum(gf[:i]) for i in range(13)]
+        prev = 0  # gaps counted from the previous index itself
+        out = []
+        for t in range(len(subs) // 4):
+            A, B = [], []
+            for lane, *_ in subs[4 * t]:
+                j = t * L + lane
+                g = offs[j] - prev
+                prev = offs[j]
+                b = (g + 1).bit_length()
+                A.append((lane, gc[b - 1], gf[b - 1], 12))
+                if b > 1:
+                    B.append((lane, (g + 1) - (1 << (b - 1)), 1, b - 1))
+            out += [A, B, subs[4 * t + 2], subs[4 * t + 3]]
+        return out, L
+    return sym
+
+
+def _symbols_escape_sends_step(orig):
+    def sym(offs, olds, news, length):
+        subs, L = orig(offs, olds, news, length)
+        for t in range(len(subs) // 4):
+            subs[4 * t + 3] = [(lane, (news[t * L + lane] - olds[t * L + lane]) & 0xFF, 1, 8)
+                               for lane, *_ in subs[4 * t + 3]]
+        return subs, L
+    return sym
+
+
+def _gap_freqs_unfixed(c, length):
+    q = ((length - c) << 32) // length
+    Q = [q]
+    for _ in range(11):
+        Q.append((Q[-1] * Q[-1]) >> 32)
+    S = [1 << 32]
+    for i in range(12):
+        S.append((S[-1] * Q[i]) >> 32)
+    share = [S[b - 1] - S[b] for b in range(1, 13)] + [S[12]]
+    return [max(1, v >> 20) for v in share]
+
+
+def _gap_freqs_shifted(orig):
+    def gf(c, length):
+        f = orig(c, length)
+        return f[1:] + f[:1]
+    return gf
+
+
+def _delta_signs_swapped(orig_cls, orig_delta):
+    def cls(old, new):
+        k = orig_cls(old, new)
+        return k ^ 1 if k < 14 else k
+
+    def delta(k):
+        return orig_delta(k ^ 1)
+    return cls, delta
+
+
 MUTATIONS = {
     "exponent shift off by one bit": lambda mp: mp.setattr(O, "exponent_field", _wrong_exp_shift),
     "sign bit dropped": lambda mp: mp.setattr(O, "sign_mantissa_field", _sm_without_sign),
@@ -250,6 +346,18 @@ MUTATIONS = {
     "SplitMix64 mix with a wrong shift": lambda mp: mp.setattr(O, "mix64", _mix64_wrong_shift),
     "block payload last block unpadded": lambda mp: mp.setattr(O, "block_comp_len", _block_len_unpadded(O.block_comp_len)),
     "block decode ignores the payload": lambda mp: mp.setattr(O, "_decode_blocks", _decode_blocks_ignores_payload(O._decode_blocks)),
+    "rANS symbol start dropped": lambda mp: mp.setattr(O, "rans_encode", _rans_without_start),
+    "rANS words in emission order": lambda mp: mp.setattr(O, "rans_encode", _rans_words_in_emission_order(O.rans_encode)),
+    "gap counted without the minus one": lambda mp: mp.setattr(O, "_chunk_symbols", _symbols_gap_without_minus_one(O._chunk_symbols)),
+    "escape carries the step, not the exponent": lambda mp: mp.setattr(O, "_chunk_symbols", _symbols_escape_sends_step(O._chunk_symbols)),
+    "coded padding dropped (shared)": lambda mp: mp.setattr(O, "pad4", lambda v: v),
+    "gap table rounding not fixed": lambda mp: mp.setattr(O, "gap_bucket_freqs", _gap_freqs_unfixed),
+    "gap table shifted one bucket": lambda mp: mp.setattr(O, "gap_bucket_freqs", _gap_freqs_shifted(O.gap_bucket_freqs)),
+    "one state per 16 changes": lambda mp: mp.setattr(O, "rans_lanes", lambda c: min(64, (c + 15) // 16)),
+    "dense from 1024 changes on": lambda mp: mp.setattr(O, "CODED_MAX_PATCHES", 1023),
+    "exponent step signs swapped (shared)": lambda mp: (
+        lambda cd: (mp.setattr(O, "delta_class", cd[0]), mp.setattr(O, "class_delta", cd[1])))(
+        _delta_signs_swapped(O.delta_class, O.class_delta)),
 }
 
 
