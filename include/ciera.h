@@ -12,7 +12,7 @@
  *
  * Stream format (one stream per (tensor, rank); all integers little-endian):
  *   header, 64 bytes:
- *     [0,4) "CIER"  [4,6) version=1  [6] dtype  [7] mode (0 RAW, 1 COMPRESSED, 2 BLOCK)
+ *     [0,4) "CIER"  [4,6) version=1  [6] dtype  [7] mode (0 RAW, 1 COMPRESSED, 2 BLOCK, 3 CODED)
  *     [8,12) block size B  [12,16) 0  [16,24) n  [24,32) n_changed
  *     [32,40) total_len  [40,48) element offset of the shard in the tensor
  *     [48,52) rank  [52,56) world  [56,64) 0
@@ -30,11 +30,32 @@
  *     here counts changed blocks -- the bitmap (bit b: block b's exponents
  *     changed) and the exponent bytes of every changed block, B bytes each in
  *     block order, the last block zero-padded to B.
+ *   CODED body (entropy-coded patches [CIERA 3.1: changed exponents ANS-coded]):
+ *     the n sign|mantissa records, then -- only if n_changed > 0 -- the bitmap,
+ *     zero bytes up to a multiple of 4 from the stream start, a chunk table and
+ *     the chunks' data.  The shard is cut into chunks of 4096 values from value
+ *     0; the table holds two u32 per chunk: the changed values and the data
+ *     bytes of this and all earlier chunks.  A chunk's data is dense -- its
+ *     exponent bytes, zero-padded to a multiple of 4 -- when that is what its
+ *     byte count says, else range-ANS data: L = min(64, ceil(c/8)) final coder
+ *     states (u32), 16-bit words, a zero word when their number is odd.  Change
+ *     j of the chunk (index order) belongs to state j mod L and is four
+ *     symbols: its gap bucket b = bit length of (gap + 1), gap = index -
+ *     previous index - 1 (previous -1 at the chunk start), coded with the
+ *     frequencies (sum 4096) of a geometric gap model with p = c / chunk
+ *     length in 32-bit fixed point; the b - 1 bits of gap + 1 below its
+ *     leading one; its exponent class (+1, -1, +2, -2, ..., +7, -7 modulo 256,
+ *     else escape; frequencies 2032, 2032, twelve of 2, 8); for an escape the
+ *     new exponent as 8 bits.  States stay in [2^16, 2^32); decoding takes the
+ *     changes L at a time and their four symbols as four sub-steps, after each
+ *     of which every state below 2^16, in state order, reads the next word.
+ *     The encoder sends a chunk dense when it has more than 1024 changes or
+ *     when the coded data would not be shorter.
  *   RAW body: the n values as stored (2 or 4 bytes each).
  *   fp16 extends the pages' bf16/fp32 scope the same way; its layout is this
  *   library's reading, not a format of the pages.
- *   A stream is COMPRESSED (BLOCK) only if the caller asked for it and it is
- *   strictly shorter than the RAW stream (64 + n*element bytes).
+ *   A stream is COMPRESSED (BLOCK, CODED) only if the caller asked for it and
+ *   it is strictly shorter than the RAW stream (64 + n*element bytes).
  *
  * Sharding: a tensor of rows x cols (row-major; a 1-D vector is rows=len,
  * cols=1) is split over W ranks by rows; rank r holds floor(R/W) + [r < R%W]
@@ -62,7 +83,7 @@
 extern "C" {
 #endif
 
-#define CIERA_ABI_VERSION 2u
+#define CIERA_ABI_VERSION 3u
 #define CIERA_HEADER_BYTES 64u
 
 typedef enum { CIERA_BF16 = 1, CIERA_FP32 = 2, CIERA_FP16 = 3 } ciera_dtype_t;
@@ -71,26 +92,38 @@ typedef enum {
   CIERA_OK = 0,
   CIERA_ERR_INVALID_ARG = 1,      /* null / misaligned pointer, bad dtype, B, world, rank */
   CIERA_ERR_BUFFER_TOO_SMALL = 2, /* stream capacity, slot or scratch too small */
-  CIERA_ERR_UNSUPPORTED = 3,      /* a shard of >= 2^32 values, or sizes beyond 2^48 */
+  CIERA_ERR_UNSUPPORTED = 3,      /* a shard of >= 2^32 values, sizes beyond 2^48, or a CODED
+                                     shard of more than 256 encode tiles */
   CIERA_ERR_DEVICE = 4            /* a HIP runtime call failed */
 } ciera_status_t;
 
 /* Bits OR-ed into *status_dev by ciera_decode (the caller zeroes it first). */
 #define CIERA_ST_MAGIC 1u  /* bad magic or version */
 #define CIERA_ST_FIELD 2u  /* dtype, B, n, offset, rank, world or mode mismatch */
-#define CIERA_ST_LENGTH 4u /* total_len / n_changed inconsistent or beyond the slot */
-#define CIERA_ST_PATCH 8u  /* a patch index >= n, or indices not strictly ascending */
-#define CIERA_ST_BITMAP 16u /* bitmap disagrees with the patches (unspecified with ST_PATCH); BLOCK:
-                               set bits other than n_changed, or a set bit past the last block */
+#define CIERA_ST_LENGTH 4u /* total_len / n_changed inconsistent or beyond the slot; CODED: a
+                              chunk table entry out of order or range (that chunk is skipped) */
+#define CIERA_ST_PATCH 8u  /* a patch index >= n, or indices not strictly ascending; CODED: a
+                              change past its chunk, an exponent wider than the field, words
+                              missing or left over, a final state other than 2^16, or dense
+                              data whose differences from the cache number other than the
+                              chunk's count */
+#define CIERA_ST_BITMAP 16u /* bitmap disagrees with the patches (unspecified with ST_PATCH, and
+                               for CODED with ST_LENGTH); BLOCK: set bits other than n_changed,
+                               or a set bit past the last block */
 
 /* One logical tensor and how it is sharded.  block_size is B, a power of two in
- * [64, 4096] (the pages sweep 256..4096 and default to 512 [CIERA 4.1, 4.5]). */
+ * [64, 4096] (the pages sweep 256..4096 and default to 512 [CIERA 4.1, 4.5]).
+ * flags: 0, or CIERA_TENSOR_CODED when the tensor's streams may be CODED --
+ * required to encode with compress = 3 and to decode CODED streams (the
+ * decode of such tensors runs a kernel with the rANS decoder; without the
+ * flag a CODED stream is a mode mismatch, CIERA_ST_FIELD). */
+#define CIERA_TENSOR_CODED 1u
 typedef struct {
   uint64_t rows, cols;
   uint32_t dtype;      /* ciera_dtype_t */
   uint32_t block_size; /* B */
   uint32_t world;      /* W >= 1 */
-  uint32_t reserved;   /* 0 */
+  uint32_t flags;      /* 0 or CIERA_TENSOR_CODED */
 } ciera_tensor_t;
 
 /* Cost model of the selector: bytes per microsecond of the Allgather bus and of
@@ -148,9 +181,12 @@ typedef struct {
   ciera_tensor_t t;
   uint32_t rank;              /* < t.world */
   uint32_t compress;          /* 0 always RAW; 1 COMPRESSED (the plan's decision); 2 the
-                                 block-hash variant (BLOCK); each subject to the length rule */
+                                 block-hash variant (BLOCK); 3 CODED (t.flags must hold
+                                 CIERA_TENSOR_CODED; shards of at most 256 encode tiles,
+                                 e.g. 2^21 values at B <= 1024); each subject to the
+                                 length rule */
   const void* shard;          /* n_r values of t.dtype; 16-byte aligned */
-  const uint8_t* cache_full;  /* compress 0/1: N = rows*cols cached exponents; [off_r, off_r+n_r)
+  const uint8_t* cache_full;  /* compress 0/1/3: N = rows*cols cached exponents; [off_r, off_r+n_r)
                                  is read.  compress 2: the shard's hash cache instead --
                                  16 bytes per block of B values (two little-endian u64),
                                  16-byte aligned -- read and updated in place */

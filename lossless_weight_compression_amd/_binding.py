@@ -11,7 +11,8 @@ from typing import List, Optional, Sequence, Tuple
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libciera.so")
 
 CIERA_BF16, CIERA_FP32, CIERA_FP16 = 1, 2, 3
-RAW, COMPRESSED, BLOCK = 0, 1, 2  # encode item `compress` values and stream modes
+RAW, COMPRESSED, BLOCK, CODED = 0, 1, 2, 3  # encode item `compress` values and stream modes
+CIERA_TENSOR_CODED = 1  # Tensor.flags: the tensor's streams may be CODED
 CIERA_OK, CIERA_ERR_INVALID_ARG, CIERA_ERR_BUFFER_TOO_SMALL, CIERA_ERR_UNSUPPORTED, CIERA_ERR_DEVICE = range(5)
 CIERA_ST_MAGIC, CIERA_ST_FIELD, CIERA_ST_LENGTH, CIERA_ST_PATCH, CIERA_ST_BITMAP = 1, 2, 4, 8, 16
 HEADER_BYTES = 64
@@ -33,10 +34,10 @@ class CieraError(RuntimeError):
 
 class Tensor(ctypes.Structure):
     _fields_ = [("rows", c_uint64), ("cols", c_uint64), ("dtype", c_uint32),
-                ("block_size", c_uint32), ("world", c_uint32), ("reserved", c_uint32)]
+                ("block_size", c_uint32), ("world", c_uint32), ("flags", c_uint32)]
 
-    def __init__(self, rows=0, cols=1, dtype=CIERA_BF16, block_size=512, world=1):
-        super().__init__(rows, cols, dtype, block_size, world, 0)
+    def __init__(self, rows=0, cols=1, dtype=CIERA_BF16, block_size=512, world=1, flags=0):
+        super().__init__(rows, cols, dtype, block_size, world, flags)
 
 
 class CostModel(ctypes.Structure):

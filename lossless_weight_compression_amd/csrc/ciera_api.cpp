@@ -50,6 +50,7 @@ ciera_status_t check_tensor(const ciera_tensor_t* t) {
   if (t->dtype != CIERA_BF16 && t->dtype != CIERA_FP32 && t->dtype != CIERA_FP16) return CIERA_ERR_INVALID_ARG;
   if (!pow2(t->block_size) || t->block_size < 64 || t->block_size > 4096) return CIERA_ERR_INVALID_ARG;
   if (t->world == 0) return CIERA_ERR_INVALID_ARG;
+  if (t->flags & ~CIERA_TENSOR_CODED) return CIERA_ERR_INVALID_ARG;
   if (t->rows >= kMaxElems || t->cols >= kMaxElems) return CIERA_ERR_UNSUPPORTED;
   if ((u128)t->rows * t->cols >= kMaxElems) return CIERA_ERR_UNSUPPORTED;
   // patch records carry u32 shard-local indices: the largest shard (rank 0's)
@@ -136,7 +137,7 @@ struct Group {
   uint32_t item0, nitems;
   uint32_t tpi;          // encode: tiles per item
   uint32_t tpr, world;   // decode: tiles per rank, world
-  uint32_t pad;
+  uint32_t coded;        // items with coded patches (encode) / tensors flagged coded (decode)
   uint64_t tile0;        // encode: the group's first tile in the batch's count array
   uint64_t stash0;       // encode: word offset of the group's first tile stash
 };
@@ -169,6 +170,12 @@ uint32_t dec_unit(uint64_t n0) { return n0 > (uint64_t)kDecRow ? 2u : 1u; }
 // more has them derived again by the finishing kernel.
 constexpr uint32_t kStashDiv = 4;
 
+// Stash words per tile: T/4; for coded patches T bytes of chunk data (a
+// 4096-byte region per row) and kCodedInfo info words.
+uint32_t stash_cap(uint32_t S, bool coded) {
+  return (uint32_t)kSub * S / kStashDiv + (coded ? kCodedInfo : 0u);
+}
+
 struct EncPlan {
   std::vector<uint32_t> order;  // items in group order
   std::vector<Group> groups;
@@ -178,7 +185,7 @@ struct EncPlan {
 
 ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncPlan* pl) {
   if (count && !items) return CIERA_ERR_INVALID_ARG;
-  std::map<std::tuple<uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
+  std::map<std::tuple<uint32_t, uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
   for (uint32_t i = 0; i < count; ++i) {
     const ciera_encode_item_t& it = items[i];
     ciera_status_t s = check_tensor(&it.t);
@@ -190,7 +197,10 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     const uint32_t S = enc_sub(it.t.block_size, n);
     const uint64_t T = (uint64_t)kSub * S;
     const uint64_t tpi = std::max<uint64_t>(1, (n + T - 1) / T);
-    by[std::make_tuple(it.t.dtype, S, (uint32_t)tpi)].push_back(i);
+    const uint32_t coded = it.compress == kCoded ? 1u : 0u;
+    // coded patches are finished one workgroup per tile, kThreads tiles per item at most
+    if (coded && tpi > (uint64_t)kThreads) return CIERA_ERR_UNSUPPORTED;
+    by[std::make_tuple(it.t.dtype, S, (uint32_t)tpi, coded)].push_back(i);
   }
   if (by.size() > (size_t)kMaxGroups) return CIERA_ERR_UNSUPPORTED;
   uint64_t tiles = 0, words = 0;
@@ -199,12 +209,13 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     g.dtype = std::get<0>(kv.first);
     g.unit = std::get<1>(kv.first);
     g.tpi = std::get<2>(kv.first);
+    g.coded = std::get<3>(kv.first);
     g.item0 = (uint32_t)pl->order.size();
     g.nitems = (uint32_t)kv.second.size();
     if ((uint64_t)g.nitems * g.tpi >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
     g.tile0 = tiles;
     g.stash0 = words;
-    const uint64_t cap = (uint64_t)kSub * g.unit / kStashDiv;
+    const uint64_t cap = stash_cap(g.unit, g.coded != 0);
     for (uint32_t k = 0; k < g.nitems; ++k) {
       pl->tile0.push_back(tiles);
       pl->stash.push_back(words);
@@ -230,7 +241,7 @@ struct DecPlan {
 
 ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count, DecPlan* pl) {
   if (count && !items) return CIERA_ERR_INVALID_ARG;
-  std::map<std::tuple<uint32_t, uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
+  std::map<std::tuple<uint32_t, uint32_t, uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
   for (uint32_t i = 0; i < count; ++i) {
     const ciera_decode_item_t& it = items[i];
     ciera_status_t s = check_tensor(&it.t);
@@ -241,7 +252,7 @@ ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count, DecP
     const uint32_t U = dec_unit(n0);
     const uint64_t T = (uint64_t)kDecRow * U;
     const uint64_t tpr = std::max<uint64_t>(1, (n0 + T - 1) / T);
-    by[std::make_tuple(it.t.dtype, U, (uint32_t)tpr, it.t.world)].push_back(i);
+    by[std::make_tuple(it.t.dtype, U, (uint32_t)tpr, it.t.world, it.t.flags & CIERA_TENSOR_CODED)].push_back(i);
   }
   if (by.size() > (size_t)kMaxGroups) return CIERA_ERR_UNSUPPORTED;
   for (auto& kv : by) {
@@ -250,6 +261,7 @@ ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count, DecP
     g.unit = std::get<1>(kv.first);
     g.tpr = std::get<2>(kv.first);
     g.world = std::get<3>(kv.first);
+    g.coded = std::get<4>(kv.first);
     g.item0 = (uint32_t)pl->order.size();
     g.nitems = (uint32_t)kv.second.size();
     if ((u128)g.nitems * g.tpr * g.world >= ((u128)1 << 31)) return CIERA_ERR_UNSUPPORTED;
@@ -369,7 +381,8 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     const ciera_encode_item_t& it = items[i];
     uint64_t off, n;
     shard_of(&it.t, it.rank, &off, &n);
-    if (it.compress > kBlockVariant) return CIERA_ERR_INVALID_ARG;
+    if (it.compress > kCoded) return CIERA_ERR_INVALID_ARG;
+    if (it.compress == kCoded && !(it.t.flags & CIERA_TENSOR_CODED)) return CIERA_ERR_INVALID_ARG;
     if (n && (!it.shard || !aligned(it.shard, 16) || !it.cache_full)) return CIERA_ERR_INVALID_ARG;
     if (n && it.compress == kBlockVariant && !aligned(it.cache_full, 16)) return CIERA_ERR_INVALID_ARG;
     if (!it.stream || !aligned(it.stream, 16)) return CIERA_ERR_INVALID_ARG;
@@ -401,11 +414,11 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     d.stash = pl.stash[j];
     d.tvals = (uint32_t)kSub * S;
     d.tpi = (uint32_t)std::max<uint64_t>(1, (n + d.tvals - 1) / d.tvals);
-    d.cap = d.tvals / kStashDiv;
+    d.cap = stash_cap(S, it.compress == kCoded);
     d.rank = it.rank;
     d.world = it.t.world;
     d.block_size = it.t.block_size;
-    d.compress = blocks ? kBlockVariant : it.compress ? 1u : 0u;
+    d.compress = it.compress;
     d.cache_aligned = !blocks && aligned(d.cache, 16) ? 1u : 0u;
     d.elem_bytes = elem_bytes(it.t.dtype);
     d.batch_id = b->batch_id;
@@ -463,7 +476,7 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
       f.stash0 = g.stash0;
       f.item0 = g.item0;
       f.tpi = g.tpi;
-      f.cap = (uint32_t)kSub * g.unit / kStashDiv;
+      f.cap = stash_cap(g.unit, g.coded != 0);
       e = launch_encode_finish_tiles(g.dtype, g.nitems, f, b->batch_id, st);
     } else {
       e = launch_encode_finish(g.dtype, items, g.item0, g.nitems, b->fin_wg, counts, stash, b->batch_id, st);
@@ -553,7 +566,7 @@ ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream) {
   const DecItem* items = reinterpret_cast<const DecItem*>(b->scratch + b->off_items);
   for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
     const Group& g = b->g[gi];
-    if (hipError_t e = launch_decode(g.dtype, g.unit, items, g.item0, g.nitems, g.tpr, g.world, b->status_dev,
+    if (hipError_t e = launch_decode(g.dtype, g.unit, g.coded != 0, items, g.item0, g.nitems, g.tpr, g.world, b->status_dev,
                                      b->batch_id, st))
       return device_error("decode launch", e);
   }

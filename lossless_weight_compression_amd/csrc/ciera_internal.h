@@ -12,6 +12,8 @@ constexpr int kEPT = 16;               // values per thread per chunk
 constexpr int kSub = kThreads * kEPT;  // 4096 values per chunk row of a tile
 constexpr uint64_t kHeader = 64;
 constexpr uint32_t kBlockVariant = 2;  // EncItem::compress of the block-hash variant; stream mode 2
+constexpr uint32_t kCoded = 3;         // EncItem::compress of entropy-coded patches; stream mode 3
+constexpr uint32_t kCodedInfo = 8;     // words after a coded tile's stash data: one per chunk row
 
 // Decode workgroups: kDecThreads threads, 16 values each per chunk row; a tile
 // is U chunk rows.  (512- and 1024-thread groups, which put more data behind
@@ -37,7 +39,7 @@ struct EncItem {
   uint32_t cap;            // records a tile stash holds
   uint32_t rank, world;
   uint32_t block_size;
-  uint32_t compress;       // 0 RAW, 1 element patches, kBlockVariant the block-hash variant
+  uint32_t compress;       // 0 RAW, 1 element patches, kBlockVariant the block-hash variant, kCoded coded patches
   uint32_t cache_aligned;  // (cache_full + off) is 16-byte aligned
   uint32_t elem_bytes;     // 2 (bf16, fp16) or 4 (fp32)
   uint32_t batch_id;       // the batch that wrote this descriptor
@@ -63,7 +65,10 @@ struct DecItem {
 //   counts : u32 per tile -- changed values of the tile, written by the split kernel
 //   stash  : u32 x cap per tile -- the tile's first cap changes in ascending order,
 //            (value index in the tile) | exponent << 16; the finishing kernel moves
-//            them to their places in the stream
+//            them to their places in the stream.  Coded items: per chunk row of
+//            the tile a 4096-byte region (its coded or dense data), then
+//            kCodedInfo words, one per row: changes | words << 13 | dense << 26;
+//            the tile's count is then data bytes | changes << 16
 struct EncArgs {
   const EncItem* items;
   uint32_t item0;      // first item of the group
@@ -91,7 +96,7 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
 hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0, uint32_t nitems, uint32_t wg_per_item,
                                 const uint32_t* counts, const uint32_t* stash, uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s);
-hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
+hipError_t launch_decode(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems,
                          uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id, hipStream_t s);
 hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n, hipStream_t s);
 hipError_t launch_hash_seed(int dtype, const uint8_t* x, uint8_t* hashes, uint64_t n, uint32_t block_size, hipStream_t s);

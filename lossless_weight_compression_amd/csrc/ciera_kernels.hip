@@ -780,6 +780,284 @@ __global__ __launch_bounds__(kThreads) void hash_seed_kernel(const uint8_t* __re
   }
 }
 
+// ------------------------------------------- entropy-coded patches (encode)
+// [CIERA 3.1; Algorithm 1] the changed exponents travel ANS-coded.  Each chunk
+// of 4096 values (a row of a tile, from the shard's first value) codes its c
+// changes with range ANS over L = min(64, ceil(c/8)) interleaved 32-bit
+// states, one per lane of one wave; change j goes to state j mod L.  Per
+// change four symbols, in decode order: the gap bucket b = bit length of
+// (gap + 1), gap = index - previous index - 1 (previous = -1 at the chunk
+// start), with geometric-model frequencies for p = c / chunk length; the
+// b - 1 bits of gap + 1 below its leading one; the exponent class (+1, -1,
+// ..., +7, -7 modulo 256, or escape) from a fixed table; for an escape, the
+// new exponent as 8 bits.  States stay in [2^16, 2^32) and trade 16-bit
+// words: the decoder takes the changes L at a time and the four symbols as
+// four sub-steps, after each of which every state below 2^16, in state
+// order, takes the next word; the encoder runs the same sub-steps backwards
+// from states of 2^16.  Chunk data = final states (u32) | words (u16) | a zero
+// word when their number is odd.  A chunk with more than 1024 changes, or
+// whose coded data is not shorter, goes dense: its exponent bytes, zero-padded
+// to a multiple of 4.
+
+constexpr uint32_t kChunkMaxChanges = 1024;
+constexpr uint32_t kRansLow = 1u << 16;
+
+__device__ __forceinline__ uint32_t pad4u(uint32_t v) { return (v + 3u) & ~3u; }
+__device__ __forceinline__ uint32_t rans_lanes(uint32_t c) { return min(64u, (c + 7u) / 8u); }
+
+// Bytes of a chunk's data from its changes, words and form.
+__device__ __forceinline__ uint32_t coded_bytes(uint32_t c, uint32_t words, bool dense, uint32_t len) {
+  if (c == 0) return 0;
+  return dense ? pad4u(len) : 4u * rans_lanes(c) + 2u * words + 2u * (words & 1u);
+}
+
+// Gap-bucket frequencies (sum 2^12) for c changes among len values; lane i < 13
+// gets bucket i+1's frequency f and start cum.  q = 1 - c/len in 32-bit fixed
+// point; S_i = q^(2^i - 1) by repeated squaring (S_i = S_{i-1} * q^(2^(i-1)));
+// bucket b takes S_{b-1} - S_b (the last, S_12) as a share of 2^12, at least
+// 1; the largest, first of equals, absorbs the rounding.  Wave-wide.
+__device__ __forceinline__ void gap_table(uint32_t c, uint32_t len, uint32_t& f, uint32_t& cum) {
+  const uint32_t lane = lane_id();
+  const uint32_t i = min(lane, 12u);
+  uint64_t Q = ((uint64_t)(len - c) << 32) / len, S = 1ull << 32;
+  for (uint32_t k = 0; k < i; ++k) {
+    S = (S * Q) >> 32;
+    Q = (Q * Q) >> 32;
+  }
+  const uint64_t share = i < 12u ? S - ((S * Q) >> 32) : S;
+  uint32_t fv = lane < 13u ? max(1u, (uint32_t)(share >> 20)) : 0u;
+  uint32_t tot = fv, mx = fv;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    tot += __shfl_xor(tot, o);
+    mx = max(mx, __shfl_xor(mx, o));
+  }
+  const uint64_t tops = __ballot(lane < 13u && fv == mx);
+  if (lane == (uint32_t)__ffsll((unsigned long long)tops) - 1u) fv = fv + 4096u - tot;
+  uint32_t incl = fv;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o);
+    if (lane >= (uint32_t)o) incl += t;
+  }
+  f = fv;
+  cum = incl - fv;
+}
+
+// Exponent classes: +1 -> 0, -1 -> 1, +2 -> 2, ..., +7 -> 12, -7 -> 13 (mod
+// 256), 14 escape; frequencies 2032, 2032, twelve of 2, 8 (sum 2^12).
+__device__ __forceinline__ uint32_t delta_class(uint32_t oldv, uint32_t newv) {
+  const uint32_t d = (newv - oldv) & 0xFFu;
+  if (d >= 1u && d <= 7u) return 2u * (d - 1u);
+  if (d >= 249u) return 2u * (255u - d) + 1u;
+  return 14u;
+}
+__device__ __forceinline__ uint32_t class_step(uint32_t cls) {
+  const uint32_t k = cls / 2u + 1u;
+  return (cls & 1u) ? 256u - k : k;
+}
+__device__ __forceinline__ uint32_t class_freq(uint32_t cls) { return cls < 2u ? 2032u : (cls < 14u ? 2u : 8u); }
+__device__ __forceinline__ uint32_t class_start(uint32_t cls) {
+  return cls < 2u ? 2032u * cls : (cls < 14u ? 4064u + 2u * (cls - 2u) : 4088u);
+}
+__device__ __forceinline__ uint32_t class_of_slot(uint32_t slot) {
+  return slot < 2032u ? 0u : slot < 4064u ? 1u : slot < 4088u ? 2u + ((slot - 4064u) >> 1) : 14u;
+}
+
+// rANS-codes one chunk's c (1..1024) changes, listed in LDS in index order as
+// offset | old exponent << 12 | new exponent << 20, with one wave, and returns
+// the number of words.  With region_end (the end of the chunk's 4096-byte
+// stash region) the words go backwards from it, so they lie in decode order,
+// and the final states just below them when the data fits the region;
+// nothing is written below region_end - 4096.  Without it nothing is written.
+__device__ uint32_t rans_encode_chunk(const uint32_t* list, uint32_t c, uint32_t len, uint8_t* region_end) {
+  const uint32_t lane = lane_id();
+  const uint32_t L = rans_lanes(c);
+  uint32_t gf, gcum;
+  gap_table(c, len, gf, gcum);
+  uint32_t x = kRansLow;
+  uint32_t R = 0;  // words written so far, counted from the end (uniform)
+  // One sub-step, backwards: states about to code a symbol of frequency f
+  // (scale s) write their low word first when x >= f * 2^(32 - s).
+  auto step = [&](bool act, uint32_t start, uint32_t f, uint32_t sc, bool raw) {
+    const bool emit = act && (uint64_t)x >= ((uint64_t)f << (32u - sc));
+    const uint64_t m = __ballot(emit);
+    const uint32_t cnt = (uint32_t)__popcll(m);
+    if (emit) {
+      const uint32_t pos = R + cnt - lanes_below(m);  // words from the end, lower lanes first in decode order
+      if (region_end && 2u * pos <= 4096u) gp(reinterpret_cast<uint16_t*>(region_end - 2u * pos))[0] = (uint16_t)x;
+      x >>= 16;
+    }
+    R += cnt;
+    if (act) x = raw ? ((x << sc) | start) : ((x / f) << sc) + (x % f) + start;
+  };
+  const uint32_t steps = (c + L - 1u) / L;
+  for (int t = (int)steps - 1; t >= 0; --t) {  // uniform
+    const uint32_t j = (uint32_t)t * L + lane;
+    const bool act = lane < L && j < c;
+    uint32_t e = 0, prev = 0xFFFFFFFFu;  // previous offset, -1 at the chunk start
+    if (act) {
+      e = list[j];
+      if (j > 0) prev = list[j - 1] & 0xFFFu;
+    }
+    const uint32_t g1 = (e & 0xFFFu) - prev;  // gap + 1
+    const uint32_t b = act ? 32u - (uint32_t)__clz(g1) : 1u;
+    const uint32_t oldv = (e >> 12) & 0xFFu, newv = (e >> 20) & 0xFFu;
+    const uint32_t cls = delta_class(oldv, newv);
+    const uint32_t fb = __shfl(gf, (int)(b - 1u)), cb = __shfl(gcum, (int)(b - 1u));
+    step(act && cls == 14u, newv, 1u, 8u, true);
+    step(act, class_start(cls), class_freq(cls), 12u, false);
+    step(act && b > 1u, g1 - (1u << (b - 1u)), 1u, b - 1u, true);
+    step(act, cb, fb, 12u, false);
+  }
+  if (region_end && lane < L && 4u * L + 2u * R <= 4096u) {
+    G1 uint16_t* q = gp(reinterpret_cast<uint16_t*>(region_end - 2u * R - 4u * L + 4u * lane));
+    q[0] = (uint16_t)x;
+    q[1] = (uint16_t)(x >> 16);
+  }
+  return R;
+}
+
+// One tile of the split kernel for an item with coded patches: sign|mantissa
+// stores, the bitmap bytes, and per chunk row its data (coded by one wave, two
+// rows at a time, or dense) in the row's stash region, its info word after
+// the regions, and the tile's count (data bytes | changes << 16).
+template <int DT, int S>
+__device__ void split_tile_coded(const EncItem& d, uint32_t local, const EncArgs& a) {
+  constexpr int E = Tr<DT>::E;
+  constexpr uint32_t T = (uint32_t)kSub * S;
+  constexpr int XW = 4 * E;
+  constexpr int P2 = S < 2 ? S : 2;  // rows coded at a time, one wave each
+  __shared__ uint32_t s_list[P2][kChunkMaxChanges];
+  __shared__ uint32_t s_wtot[4 * P2];
+  __shared__ uint64_t s_chg[4 * S];
+  __shared__ uint32_t s_info[S];
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint64_t base = (uint64_t)local * T;
+  const uint64_t n = d.n;
+  const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;
+  const bool caligned = d.cache_aligned != 0;
+  uint8_t* const regions = reinterpret_cast<uint8_t*>(a.stash + d.stash + (uint64_t)local * d.cap);
+
+  for (int s0 = 0; s0 < S; s0 += P2) {  // uniform
+    uint32_t expk[P2][4], cw[P2][4], mask[P2], pre[P2];
+#pragma unroll
+    for (int r = 0; r < P2; ++r) {
+      const uint64_t c0 = base + (uint64_t)(s0 + r) * kSub + (uint64_t)tid * kEPT;
+      const int cnt = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
+      uint32_t xw[XW];
+      mask[r] = 0;
+      expk[r][0] = expk[r][1] = expk[r][2] = expk[r][3] = 0;
+      cw[r][0] = cw[r][1] = cw[r][2] = cw[r][3] = 0;
+      if (cnt > 0) {
+        load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt * E, true, xw);
+        load_words<4, kNtBulk<DT>>(d.cache + c0, (uint32_t)cnt, caligned, cw[r]);
+        mask[r] = chunk_exps<DT, false>(xw, cw[r], cnt, expk[r]);
+        chunk_store<DT>(d.stream, c0, cnt, xw, true);
+      }
+      // exclusive prefix of the change counts over the workgroup, row by row
+      const uint32_t cc = (uint32_t)__popc(mask[r]);
+      uint32_t p = 0, tot = 0;
+#pragma unroll
+      for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t m = __ballot((cc >> bit) & 1u);
+        p += lanes_below(m) << bit;
+        tot += (uint32_t)__popcll(m) << bit;
+      }
+      pre[r] = p;
+      const uint64_t chg = __ballot(mask[r] != 0);
+      if (lane == 0) {
+        s_wtot[r * 4 + wave] = tot;
+        s_chg[(s0 + r) * 4 + wave] = chg;
+      }
+    }
+    __syncthreads();
+    uint32_t c[P2];
+#pragma unroll
+    for (int r = 0; r < P2; ++r) {
+      c[r] = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (w < (int)wave) pre[r] += s_wtot[r * 4 + w];
+        c[r] += s_wtot[r * 4 + w];
+      }
+      if (c[r] <= kChunkMaxChanges) {  // list the row's changes for its coding wave
+        uint32_t m = mask[r], g = pre[r];
+        while (m) {
+          const int k = __ffs(m) - 1;
+          m &= m - 1;
+          s_list[r][g++] = (tid * kEPT + (uint32_t)k) | (byte_of(cw[r], k) << 12) | (byte_of(expk[r], k) << 20);
+        }
+      }
+    }
+    __syncthreads();
+    if ((int)wave < P2) {  // uniform per wave: wave r codes row s0 + r
+      const int r = (int)wave;
+      const uint64_t r0 = base + (uint64_t)(s0 + r) * kSub;
+      const uint32_t len = r0 < n ? (uint32_t)min<uint64_t>(kSub, n - r0) : 0u;
+      uint32_t words = 0;
+      bool dense = c[r] > kChunkMaxChanges;
+      if (c[r] > 0 && !dense) {  // measure, then write only coded data that is shorter than dense
+        words = rans_encode_chunk(s_list[r], c[r], len, nullptr);
+        dense = coded_bytes(c[r], words, false, len) >= pad4u(len);
+        if (!dense) (void)rans_encode_chunk(s_list[r], c[r], len, regions + (uint32_t)(s0 + r + 1) * kSub);
+      }
+      if (lane == 0) s_info[s0 + r] = c[r] | (dense ? 0u : words << 13) | ((dense ? 1u : 0u) << 26);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < P2; ++r) {  // dense rows: their exponent bytes (zero past the shard)
+      if ((s_info[s0 + r] >> 26) & 1u) {
+        v4u e;
+        e.x = expk[r][0]; e.y = expk[r][1]; e.z = expk[r][2]; e.w = expk[r][3];
+        stg16(regions + (uint32_t)(s0 + r) * kSub + tid * kEPT, e);
+      }
+    }
+    __syncthreads();  // s_list and s_wtot are rewritten by the next rows
+  }
+
+  // bitmap bytes of the tile's blocks (a tile spans whole bitmap bytes), when
+  // they lie inside the RAW length (otherwise the stream cannot be coded)
+  const uint64_t smsec = sm_sec<DT>(n);
+  const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
+  const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
+  const uint64_t nbm = (((n + B - 1) >> lb) + 7) / 8;
+  if (smsec + nbm <= n * E && tid < (tblocks + 7) / 8) {
+    const uint32_t Lc = B >> 4;  // 16-value groups per block, >= 4
+    uint32_t byte = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t blk = tid * 8 + (uint32_t)k;
+      if (blk < tblocks) {
+        const uint32_t first = blk * Lc;
+        uint64_t any;
+        if (Lc < 64) {
+          any = (s_chg[first >> 6] >> (first & 63u)) & ((1ull << Lc) - 1ull);
+        } else {
+          any = 0;
+          for (uint32_t u = 0; u < Lc / 64; ++u) any |= s_chg[(first >> 6) + u];
+        }
+        if (any) byte |= 1u << k;
+      }
+    }
+    gp(d.stream)[kHeader + smsec + (base >> (lb + 3)) + tid] = (uint8_t)byte;
+  }
+  if (tid < (uint32_t)S) gp(reinterpret_cast<uint32_t*>(regions + T))[tid] = s_info[tid];
+  if (tid == 0) {
+    uint32_t bytes = 0, chg = 0;
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+      const uint64_t r0 = base + (uint64_t)r * kSub;
+      const uint32_t len = r0 < n ? (uint32_t)min<uint64_t>(kSub, n - r0) : 0u;
+      const uint32_t w = s_info[r];
+      bytes += coded_bytes(w & 0x1FFFu, (w >> 13) & 0x1FFFu, (w >> 26) & 1u, len);
+      chg += w & 0x1FFFu;
+    }
+    gp(a.counts)[d.tile0 + local] = bytes | (chg << 16);
+  }
+}
+
 template <int DT, int S>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t batch_id) {
   constexpr int E = Tr<DT>::E;
@@ -796,6 +1074,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
   if (d.batch_id != batch_id) return;  // the scratch holds another batch (uniform)
   if (d.compress == kBlockVariant) {   // uniform
     split_tile_block<DT, S>(d, local, a);
+    return;
+  }
+  if (d.compress == kCoded) {  // uniform
+    split_tile_coded<DT, S>(d, local, a);
     return;
   }
   const uint64_t base = (uint64_t)local * T;
@@ -1158,6 +1440,92 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncItem* 
   }
 }
 
+// Finishing work of one tile of an item with coded patches (at most kThreads
+// tiles per item): the item's totals and this tile's prefix of data bytes and
+// changes decide the mode and the places; the tile writes its chunks' table
+// entries (changes and data bytes of this and all earlier chunks) and copies
+// its chunks' data (coded data from the end of each stash region, a zero word
+// after an odd number of words; dense data from its start), or its part of
+// the shard RAW.  Workgroup-wide.
+template <int DT>
+__device__ void finish_tile_coded(const FinArgs& f, const EncItem& d, uint32_t local, uint64_t t0, uint64_t sbase) {
+  constexpr int E = Tr<DT>::E;
+  __shared__ uint64_t s_r[2 * (kThreads / 64)];
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t c_t = tid < f.tpi ? gp(f.counts)[t0 + tid] : 0u;
+  const uint32_t by = c_t & 0xFFFFu, ch = c_t >> 16;
+  uint64_t vb = by | ((uint64_t)(tid < local ? by : 0u) << 32);
+  uint64_t vc = ch | ((uint64_t)(tid < local ? ch : 0u) << 32);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    vb += __shfl_xor(vb, o);
+    vc += __shfl_xor(vc, o);
+  }
+  if (lane == 0) {
+    s_r[wave] = vb;
+    s_r[kThreads / 64 + wave] = vc;
+  }
+  __syncthreads();
+  uint64_t sb = 0, sc = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    sb += s_r[w];
+    sc += s_r[kThreads / 64 + w];
+  }
+  const uint64_t Dtot = (uint32_t)sb, P = (uint32_t)sc;
+  const uint64_t n = d.n;
+  const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;
+  const uint64_t nbm = (((n + B - 1) >> lb) + 7) / 8;
+  const uint64_t smsec = sm_sec<DT>(n);
+  const uint64_t nch = (n + kSub - 1) / kSub;
+  const uint64_t bm_end = kHeader + smsec + nbm;
+  const uint64_t tpos = (bm_end + 3) & ~3ull, dpos = tpos + 8 * nch;
+  const uint64_t comp = P ? dpos + Dtot : kHeader + smsec;
+  const uint64_t raw = kHeader + n * E;
+  const bool coded = comp < raw;
+  if (local == 0 && tid == 0) write_header<DT>(d, P, coded ? kCoded : 0u, coded ? comp : raw);
+  if (!coded) {  // the coded form is not shorter: this tile's part RAW
+    const uint64_t v0 = (uint64_t)local * d.tvals;
+    const uint64_t v1 = min<uint64_t>(n, v0 + d.tvals);
+    if (v0 < v1) raw_copy(d, v0 * E, v1 * E, tid, kThreads);
+    return;
+  }
+  if (P == 0) return;
+  if (local == 0 && bm_end + tid < tpos) gp(d.stream)[bm_end + tid] = 0;
+  const uint32_t S = d.tvals / kSub;
+  const uint8_t* regions = reinterpret_cast<const uint8_t*>(f.stash + sbase);
+  const G1 uint32_t* info = gp(reinterpret_cast<const uint32_t*>(regions + d.tvals));
+  uint64_t cc = sc >> 32, cb = sb >> 32;  // changes and bytes before the chunk
+  for (uint32_t r = 0; r < S; ++r) {  // uniform
+    const uint64_t k = (uint64_t)local * S + r;
+    if (k >= nch) break;
+    const uint32_t w = info[r];
+    const uint32_t c = w & 0x1FFFu, words = (w >> 13) & 0x1FFFu;
+    const bool dense = (w >> 26) & 1u;
+    const uint32_t len = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
+    const uint32_t bytes = coded_bytes(c, words, dense, len);
+    uint8_t* dst = d.stream + dpos + cb;
+    if (bytes > 0 && dense) {
+      for (uint32_t i = tid; i < bytes / 4; i += kThreads)
+        gp(reinterpret_cast<uint32_t*>(dst))[i] = gp(reinterpret_cast<const uint32_t*>(regions + r * kSub))[i];
+    } else if (bytes > 0) {
+      const uint32_t h = 2u * rans_lanes(c) + words;  // u16 of states and words
+      const uint8_t* src = regions + (r + 1) * kSub - 2u * h;
+      for (uint32_t i = tid; i < h; i += kThreads)
+        gp(reinterpret_cast<uint16_t*>(dst))[i] = gp(reinterpret_cast<const uint16_t*>(src))[i];
+      if (tid == 0 && (words & 1u)) gp(reinterpret_cast<uint16_t*>(dst))[h] = 0;
+    }
+    cc += c;
+    cb += bytes;
+    if (tid == 0) {
+      G1 uint32_t* e = gp(reinterpret_cast<uint32_t*>(d.stream + tpos + 8 * k));
+      e[0] = (uint32_t)cc;
+      e[1] = (uint32_t)cb;
+    }
+  }
+}
+
 // Finishing kernel for groups of at most kThreads tiles per item: one
 // workgroup per tile, so tiles whose changes overflowed their stash are
 // derived again in parallel.  The item's tile counts, the tile's first
@@ -1179,6 +1547,10 @@ __global__ __launch_bounds__(kThreads) void encode_finish_tile_kernel(FinArgs f,
   const uint32_t sv = gp(f.stash)[sbase + tid];  // cap >= kThreads: inside the stash
   const EncItem d = f.items[f.item0 + rel];
   if (d.batch_id != batch_id) return;  // uniform
+  if (d.compress == kCoded) {          // uniform
+    finish_tile_coded<DT>(f, d, local, t0, sbase);
+    return;
+  }
 
   // total and exclusive prefix of the item's tile counts, in one reduction
   uint64_t v = (uint64_t)c_t | ((uint64_t)(tid < local ? c_t : 0u) << 32);
@@ -1239,7 +1611,7 @@ __global__ __launch_bounds__(kThreads) void encode_finish_tile_kernel(FinArgs f,
 // (sign|mantissa bytes and cached exponents) are issued before the header and
 // the patch range are known, so their latency overlaps that chain.
 
-template <int DT, int U>
+template <int DT, int U, bool CODED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __restrict__ items, uint32_t item0,
                                                           uint32_t tpr, uint32_t world, uint32_t* status_out,
                                                           uint32_t batch_id) {
@@ -1251,6 +1623,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   __shared__ uint32_t s_expbm[BMW];  // blocks of the tile that hold a patch
   __shared__ uint32_t s_ex[T / 4];   // the tile's exponents: cached, then patched in place
   __shared__ uint32_t s_sum[kDecThreads / 64];
+  // coded patches (the tensor's streams may be CODED): each row's chunk data
+  // and gap-bucket starts
+  __shared__ uint32_t s_win[CODED ? U : 1][CODED ? kSub / 4 : 1];
+  __shared__ uint32_t s_cum[CODED ? U : 1][16];
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t tpi = tpr * world;
@@ -1315,8 +1691,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   if (s_hdr[0] != 0x52454943u || (s_hdr[1] & 0xFFFFu) != 1u) {
     bad = CIERA_ST_MAGIC;
   } else if (h_dtype != (uint32_t)DT || s_hdr[2] != B || h_n != n || h_off != off || s_hdr[12] != r ||
-             s_hdr[13] != world || h_mode > 2u) {
+             s_hdr[13] != world || h_mode > (CODED ? kCoded : kBlockVariant)) {
     bad = CIERA_ST_FIELD;
+  } else if (h_mode == kCoded) {  // the chunk table gives the length; checked per chunk
+    const uint64_t dpos = ((kHeader + sm_sec<DT>(n) + nbm + 3) & ~3ull) + 8 * ((n + kSub - 1) / kSub);
+    if (P > n || h_tot > d.slot || (P ? h_tot < dpos : h_tot != kHeader + sm_sec<DT>(n))) bad = CIERA_ST_LENGTH;
   } else {
     const uint64_t want = h_mode == 0   ? kHeader + n * E
                           : h_mode == 1 ? kHeader + sm_sec<DT>(n) + (P ? nbm + 5 * P : 0)
@@ -1391,6 +1770,181 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
         }
       }
       __syncthreads();
+    }
+  } else if (h_mode == kCoded) {
+    if constexpr (CODED) {  // (without CODED the header check rejects mode 3)
+      // 3c. CODED: chunk row u of the tile is chunk t_in * U + u.  Its table
+      //     entry (and the one before) gives its changes and data; dense data
+      //     replaces the row's cached exponents (every thread its 16), coded
+      //     data goes to LDS and wave u decodes it.  Each patched value marks
+      //     its block; the tile's bitmap bits are compared at the end.
+      patched = P > 0;
+      if (P > 0) {
+        const uint64_t nch = (n + kSub - 1) / kSub;
+        const uint64_t bm_end = kHeader + sm_sec<DT>(n) + nbm;
+        const uint64_t tpos = (bm_end + 3) & ~3ull, dpos = tpos + 8 * nch;
+        const uint64_t D = h_tot - dpos;
+        const uint64_t tb0 = ts >> lb, tb1 = (te + B - 1) >> lb;
+        const uint32_t nbt = (uint32_t)(tb1 - tb0);
+        const uint8_t* bm = st + kHeader + sm_sec<DT>(n);
+        uint32_t bm_got = 0, bm_tail = 0;
+        if (tid * 32 < nbt) bm_got = bits_of(load_bits_w(bm, tb0 + tid * 32), min(32u, nbt - tid * 32));
+        if (te == n && tid == 0 && (nb & 7u) != 0) bm_tail = gp(bm)[nbm - 1] >> (nb & 7u);
+        uint32_t c[U], nbytes[U], start[U], len[U];
+        bool dense[U], coded[U];
+        uint32_t e = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint64_t k = (uint64_t)t_in * U + (uint64_t)u;
+          c[u] = nbytes[u] = start[u] = len[u] = 0;
+          dense[u] = coded[u] = false;
+          if (k >= nch) continue;
+          const G1 uint32_t* ent = gp(reinterpret_cast<const uint32_t*>(st + tpos + 8 * k));
+          const uint32_t cc = ent[0], cb = ent[1];
+          const uint32_t pc = k > 0 ? ent[-2] : 0u, pb = k > 0 ? ent[-1] : 0u;
+          len[u] = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
+          const uint32_t cu = cc - pc, bu = cb - pb;
+          bool badk = cc < pc || cb < pb || cb > D || cu > len[u] || (bu & 3u) != 0 || ((cu == 0) != (bu == 0)) ||
+                      (k == nch - 1 && (cc != P || cb != D));
+          if (!badk && cu > 0 && bu != pad4u(len[u]) && (bu < 4u * rans_lanes(cu) || bu > pad4u(len[u])))
+            badk = true;  // coded data holds its states and is shorter than the dense form
+          if (badk) {
+            e |= CIERA_ST_LENGTH;
+            continue;
+          }
+          c[u] = cu;
+          nbytes[u] = bu;
+          start[u] = pb;
+          dense[u] = cu > 0 && bu == pad4u(len[u]);
+          coded[u] = cu > 0 && !dense[u];
+        }
+        if (tid == 0 && e) report(status_out, e);
+        if (tid < (uint32_t)U) s_sum[tid] = 0;  // differences per dense row (s_expbm is clear already)
+        __syncthreads();
+        uint8_t* const s_exb = reinterpret_cast<uint8_t*>(s_ex);
+        auto mark = [&](uint32_t v) {  // value v of the tile was patched
+          const uint32_t bb = (uint32_t)(((ts + v) >> lb) - tb0);
+          atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
+        };
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t vo = (uint32_t)u * kDecRow + tid * kEPT;
+          const G1 uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st + dpos + start[u]));
+          if (coded[u] && tid * 4 < nbytes[u] / 4) {  // coded data to LDS, 16 bytes per thread
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (tid * 4 + (uint32_t)q < nbytes[u] / 4) s_win[u][tid * 4 + q] = src[tid * 4 + q];
+          }
+          if (dense[u] && cnt[u] > 0) {  // this thread's 16 values of a dense row
+            uint32_t dw[4];
+            load_words<4>(st + dpos + start[u] + tid * kEPT, (uint32_t)cnt[u], false, dw);
+            uint32_t diff = 0, wide = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const uint32_t a = byte_of(dw, j), o = byte_of(cw[u], j);
+              if (j < cnt[u]) {
+                diff += a != o ? 1u : 0u;
+                wide |= a > Tr<DT>::EMASK ? 1u : 0u;
+              }
+            }
+            v4u nv;
+            nv.x = dw[0]; nv.y = dw[1]; nv.z = dw[2]; nv.w = dw[3];
+            *reinterpret_cast<v4u*>(s_exb + vo) = nv;
+            if (diff) mark(vo);  // 16 values lie in one block (B >= 64)
+            if (wide) report(status_out, CIERA_ST_PATCH);
+            atomicAdd(&s_sum[u], diff);
+          }
+        }
+        __syncthreads();
+        if ((int)wave < U && coded[wave]) {  // uniform per wave
+          const uint32_t u = wave, cu = c[u], Lr = rans_lanes(cu);
+          const uint32_t navail = (nbytes[u] - 4u * Lr) / 2u;
+          const uint16_t* words = reinterpret_cast<const uint16_t*>(&s_win[u][Lr]);
+          uint32_t gf, gcum;
+          gap_table(cu, len[u], gf, gcum);
+          // bucket starts in LDS (lanes 13-15: 4096, above every slot), read back
+          // as broadcasts for each bucket decode
+          if (lane < 16u) s_cum[u][lane] = lane < 13u ? gcum : 4096u;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // other lanes read them below
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          uint32_t x = lane < Lr ? s_win[u][lane] : kRansLow;
+          uint32_t ptr = 0, run = 0, err = 0;
+          auto renorm = [&]() {
+            const bool need = lane < Lr && x < kRansLow;
+            const uint64_t m = __ballot(need);
+            if (need) {
+              const uint32_t pos = ptr + lanes_below(m);
+              uint32_t w = 0;
+              if (pos < navail) w = words[pos];
+              else err |= CIERA_ST_PATCH;
+              x = (x << 16) | w;
+            }
+            ptr += (uint32_t)__popcll(m);
+          };
+          uint8_t* const rowex = s_exb + u * kDecRow;
+          const uint32_t steps = (cu + Lr - 1u) / Lr;
+          for (uint32_t t = 0; t < steps; ++t) {  // uniform
+            const bool act = lane < Lr && t * Lr + lane < cu;
+            uint32_t slot = x & 4095u, bk = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const v4u cq = *reinterpret_cast<const v4u*>(&s_cum[u][4 * q]);
+              bk += (cq.x <= slot ? 1u : 0u) + (cq.y <= slot ? 1u : 0u) + (cq.z <= slot ? 1u : 0u) +
+                    (cq.w <= slot ? 1u : 0u);
+            }
+            const uint32_t fb = __shfl(gf, (int)(bk - 1u)), cb = __shfl(gcum, (int)(bk - 1u));
+            if (act) x = fb * (x >> 12) + slot - cb;
+            renorm();
+            uint32_t g1 = 1;
+            if (act) {
+              const uint32_t kb = bk - 1u;
+              g1 = (1u << kb) | (x & ((1u << kb) - 1u));
+              x >>= kb;
+            }
+            renorm();
+            slot = x & 4095u;
+            const uint32_t cls = class_of_slot(slot);
+            if (act) x = class_freq(cls) * (x >> 12) + slot - class_start(cls);
+            renorm();
+            uint32_t esc = 0;
+            if (act && cls == 14u) {
+              esc = x & 0xFFu;
+              x >>= 8;
+            }
+            renorm();
+            uint32_t incl = act ? g1 : 0u;  // indices: running sum of gap + 1 in change order
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+              const uint32_t tt = __shfl_up(incl, o);
+              if (lane >= (uint32_t)o) incl += tt;
+            }
+            const uint32_t idx = run + incl - 1u;
+            run += __shfl(incl, 63);
+            if (act) {
+              if (idx >= len[u]) {
+                err |= CIERA_ST_PATCH;
+              } else {
+                const uint32_t nv = cls == 14u ? esc : (rowex[idx] + class_step(cls)) & 0xFFu;
+                if (nv > Tr<DT>::EMASK) {
+                  err |= CIERA_ST_PATCH;
+                } else {
+                  rowex[idx] = (uint8_t)nv;
+                  mark(u * kDecRow + idx);
+                }
+              }
+            }
+          }
+          if (ptr + (ptr & 1u) != navail || (lane < Lr && x != kRansLow)) err |= CIERA_ST_PATCH;
+          if (err) report(status_out, err);
+        }
+        __syncthreads();
+        uint32_t eb = 0;
+        if (tid * 32 < nbt && bm_got != s_expbm[tid]) eb |= CIERA_ST_BITMAP;
+        if (bm_tail != 0) eb |= CIERA_ST_BITMAP;
+        if (tid < (uint32_t)U && dense[tid] && s_sum[tid] != c[tid]) eb |= CIERA_ST_PATCH;
+        if (eb) report(status_out, eb);
+      }
     }
   } else {
   // 3. COMPRESSED: this tile's patch range [lo, hi).  Every wave finds it on its
@@ -1739,13 +2293,20 @@ hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs&
   return hipSuccess;
 }
 
-static hipError_t launch_decode_part(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems,
+static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems,
                                      uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id,
                                      hipStream_t s) {
   (void)hipGetLastError();
   const dim3 grid(nitems * tpr * world), block(kDecThreads);
-#define CIERA_DEC(DT, U) \
-  hipLaunchKernelGGL((decode_kernel<DT, U>), grid, block, 0, s, items, item0, tpr, world, status, batch_id)
+#define CIERA_DEC(DT, U)                                                                                   \
+  do {                                                                                                     \
+    if (coded)                                                                                             \
+      hipLaunchKernelGGL((decode_kernel<DT, U, true>), grid, block, 0, s, items, item0, tpr, world, status, \
+                         batch_id);                                                                        \
+    else                                                                                                   \
+      hipLaunchKernelGGL((decode_kernel<DT, U, false>), grid, block, 0, s, items, item0, tpr, world,       \
+                         status, batch_id);                                                                \
+  } while (0)
   if (dtype == 1) {
     switch (u) {
       case 1: CIERA_DEC(1, 1); break;
@@ -1774,14 +2335,14 @@ static hipError_t launch_decode_part(int dtype, int u, const DecItem* items, uin
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int dtype, int u, const DecItem* items, uint32_t item0, uint32_t nitems, uint32_t tpr,
+hipError_t launch_decode(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems, uint32_t tpr,
                          uint32_t world, uint32_t* status, uint32_t batch_id,
                          hipStream_t s) {
   const uint64_t tpi = (uint64_t)tpr * world;
   if (tpi * kDecThreads >= ((uint64_t)1 << 32)) return hipErrorInvalidValue;  // one item alone too large
   const uint32_t per = (uint32_t)std::max<uint64_t>(1, kMaxGrid / tpi);
   for (uint32_t i = 0; i < nitems; i += per) {
-    if (hipError_t e = launch_decode_part(dtype, u, items, item0 + i, std::min(per, nitems - i), tpr, world, status,
+    if (hipError_t e = launch_decode_part(dtype, u, coded, items, item0 + i, std::min(per, nitems - i), tpr, world, status,
                                           batch_id, s))
       return e;
   }

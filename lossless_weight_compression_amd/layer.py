@@ -33,13 +33,16 @@ class LayerCodec:
     def __init__(self, shapes: Sequence[Tuple[int, int]], dtype: torch.dtype, world: int,
                  block_size: int = 512, device="cuda", change_ppm: int = 10_000,
                  cost: Optional[B.CostModel] = None, with_out: bool = True,
-                 cache: Optional[torch.Tensor] = None, cache_budget: Optional[int] = None):
+                 cache: Optional[torch.Tensor] = None, cache_budget: Optional[int] = None,
+                 coded: Optional[Sequence[bool]] = None):
         self.dtype = dtype
         self.cdtype = TORCH_TO_CIERA[dtype]
         self.e = ELEM[self.cdtype]
         self.world = world
         self.device = torch.device(device)
-        self.tensors = [B.Tensor(r, c, self.cdtype, block_size, world) for r, c in shapes]
+        coded = coded or [False] * len(shapes)  # tensors whose streams may be CODED
+        self.tensors = [B.Tensor(r, c, self.cdtype, block_size, world, B.CIERA_TENSOR_CODED if k else 0)
+                        for (r, c), k in zip(shapes, coded)]
         self.numel = [r * c for r, c in shapes]
         self.plans = [B.ciera_plan(t, change_ppm, cost) for t in self.tensors]
         if cache_budget is not None:  # benefit-driven selection: the rest is sent RAW
@@ -125,7 +128,8 @@ class LayerCodec:
     def encode_items(self, rank: int, shards: Sequence[torch.Tensor],
                      compress: Optional[Sequence[int]] = None) -> List[B.EncodeItem]:
         """compress[i]: 0 RAW, 1 COMPRESSED (default: the plan's), 2 the block-hash
-        variant, which reads and updates rank's hash cache of tensor i."""
+        variant, which reads and updates rank's hash cache of tensor i, 3
+        entropy-coded patches (shards of at most 256 encode tiles)."""
         items = []
         for i, t in enumerate(self.tensors):
             c = self.plans[i].compress if compress is None else compress[i]

@@ -296,8 +296,9 @@ def encode(x: np.ndarray, cache_slice: np.ndarray, dtype: int, block_size: int,
 # -------------------------------------------------------------------- decode
 
 def _check_header(s: np.ndarray, dtype: int, block_size: int, n: int, offset: int,
-                  rank: int, world: int) -> Tuple[int, Optional[dict]]:
-    """Header and length validation of one received stream; (status bits, header)."""
+                  rank: int, world: int, coded: bool = False) -> Tuple[int, Optional[dict]]:
+    """Header and length validation of one received stream; (status bits,
+    header).  Mode 3 is accepted only for a tensor declared coded (R35)."""
     if s.size < HEADER_BYTES:
         return ST_LENGTH, None
     h = parse_header(s)
@@ -305,7 +306,8 @@ def _check_header(s: np.ndarray, dtype: int, block_size: int, n: int, offset: in
         return ST_MAGIC, None
     if (h["dtype"] != dtype or h["block_size"] != block_size or h["n"] != n
             or h["offset"] != offset or h["rank"] != rank or h["world"] != world
-            or h["mode"] not in (MODE_RAW, MODE_COMPRESSED, MODE_BLOCK, MODE_CODED)):
+            or h["mode"] not in ((MODE_RAW, MODE_COMPRESSED, MODE_BLOCK, MODE_CODED) if coded
+                                 else (MODE_RAW, MODE_COMPRESSED, MODE_BLOCK))):
         return ST_FIELD, None
     p = h["n_changed"]
     if p > (n_blocks(n, block_size) if h["mode"] == MODE_BLOCK else n) or h["total_len"] > s.size:
@@ -327,12 +329,13 @@ def _check_header(s: np.ndarray, dtype: int, block_size: int, n: int, offset: in
 
 
 def decode_stream(s: np.ndarray, dtype: int, block_size: int, n: int, offset: int,
-                  rank: int, world: int, cache_slice: np.ndarray):
-    """Receiver side for one stream [CIERA 3.1, Alg. 1 receiver].
+                  rank: int, world: int, cache_slice: np.ndarray, coded: bool = False):
+    """Receiver side for one stream [CIERA 3.1, Alg. 1 receiver].  coded: the
+    tensor is declared to carry mode-3 streams (R35).
 
     Returns (values or None, new cache slice or None, status bits)."""
     s = np.asarray(s, dtype=np.uint8)
-    st, h = _check_header(s, dtype, block_size, n, offset, rank, world)
+    st, h = _check_header(s, dtype, block_size, n, offset, rank, world, coded)
     if st:
         return None, None, st
     pos = HEADER_BYTES
@@ -371,7 +374,7 @@ def decode_stream(s: np.ndarray, dtype: int, block_size: int, n: int, offset: in
 
 def decode(streams: Sequence[np.ndarray], rows: int, cols: int, dtype: int,
            block_size: int, world: int, cache_full: np.ndarray,
-           out_full: Optional[np.ndarray] = None):
+           out_full: Optional[np.ndarray] = None, coded: bool = False):
     """Rebuild the full tensor from all W ranks' streams and update the cache.
 
     streams[r] is rank r's receive slot (at least total_len bytes).  Returns
@@ -385,7 +388,7 @@ def decode(streams: Sequence[np.ndarray], rows: int, cols: int, dtype: int,
     for r in range(world):
         off, n = shard(rows, cols, world, r)
         x, ex, st = decode_stream(streams[r], dtype, block_size, n, off, r, world,
-                                  cache[off:off + n])
+                                  cache[off:off + n], coded)
         status |= st
         if x is None:
             continue
@@ -657,12 +660,16 @@ def _decode_blocks(s, pos, c, n, block_size, sm, ex, dtype):
 #   R34 decode checks: a chunk table entry that goes backwards, exceeds the
 #       chunk length or the data, has a byte count not a multiple of 4, data
 #       without changes or changes without data, rANS data shorter than its
-#       states, or a last entry other than (n_changed, data bytes) is
+#       states or longer than the dense form, or a last entry other than
+#       (n_changed, data bytes) is
 #       ST_LENGTH and the chunk is not decoded.  Within a chunk, a change past
 #       its end, an exponent wider than the field, words missing or left
 #       over, a final state other than 2^16, or dense data whose differences
 #       from the cache number other than c, is ST_PATCH.  The bitmap verdict
 #       is unspecified alongside ST_LENGTH or ST_PATCH.
+#   R35 a receiver accepts mode 3 only for a tensor it declared coded (the
+#       decode of such tensors carries the rANS decoder); otherwise the mode
+#       is a field mismatch (ST_FIELD).
 # Parity unpinned against the pages (they fix no ANS model or layout); the
 # pins are the rANS definition's closed forms, its entropy bound, per-state
 # independence, and round trips.
@@ -965,8 +972,8 @@ def _decode_coded(s, pos, h, n, block_size, sm, ex, dtype):
         c, nbytes = cc - pc, cb - pb
         bad = (cc < pc or cb < pb or cb > D or c > length or nbytes % 4 != 0 or (c == 0) != (nbytes == 0)
                or (k == nch - 1 and (cc != P or cb != D)))
-        if not bad and c > 0 and nbytes != pad4(length) and nbytes < 4 * rans_lanes(c):
-            bad = True
+        if not bad and c > 0 and nbytes != pad4(length) and (nbytes < 4 * rans_lanes(c) or nbytes > pad4(length)):
+            bad = True                          # rANS data holds its states and is shorter than dense
         if bad:
             st |= ST_LENGTH
         elif c > 0:

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert L.ciera_abi_version() == 2
+    assert L.ciera_abi_version() == 3
     assert L.ciera_status_str(0) == "ok"
     assert "buffer" in L.ciera_status_str(2)
 
@@ -151,3 +151,34 @@ def test_scratch_sizes_grow_with_work():
     assert 0 < a < b and a % 256 == 0
     d = L.decode_item(t1, 0x30000, 1 << 20, 0x50000, 0x20000)
     assert L.ciera_decode_scratch_bytes([d] * 10) > L.ciera_decode_scratch_bytes([d])
+
+
+def test_coded_patch_arguments_without_device():
+    """compress = 3 needs the tensor flag CIERA_TENSOR_CODED; unknown flag bits
+    are invalid; a coded shard of more than 256 encode tiles is unsupported."""
+    with pytest.raises(L.CieraError) as e:
+        L.ciera_plan(L.Tensor(4, 4, 1, 512, 1, flags=2), 100)
+    assert e.value.code == 1
+    assert L.ciera_plan(L.Tensor(4, 4, 1, 512, 1, flags=L.CIERA_TENSOR_CODED), 100).raw_stream_bytes == 64 + 32
+
+    def scratch(t, compress):
+        return L.ciera_encode_scratch_bytes([L.encode_item(t, 0, compress, 0x10000, 0x20000, 0x30000,
+                                                           64 + 2 * t.rows * t.cols)])
+
+    flag = L.CIERA_TENSOR_CODED
+    assert scratch(L.Tensor(2048, 1024, 1, 512, 1, flags=flag), 3) > 0          # 256 tiles of 8192 values
+    with pytest.raises(L.CieraError) as e:
+        scratch(L.Tensor(2049, 1024, 1, 512, 1, flags=flag), 3)                  # 257 tiles
+    assert e.value.code == 3
+    assert scratch(L.Tensor(2049, 1024, 1, 512, 1), 1) > 0                      # element patches: any size
+    # coded tiles keep a 4096-byte region per chunk row plus 8 info words
+    assert scratch(L.Tensor(8, 1024, 1, 512, 1, flags=flag), 3) >= scratch(L.Tensor(8, 1024, 1, 512, 1), 1) + 32
+    it = L.encode_item(L.Tensor(64, 64, 1, 512, 2), 0, 3, 0x10000, 0x20000, 0x30000, 64 + 32 * 64 * 2)
+    need = L.ciera_encode_scratch_bytes([it])
+    with pytest.raises(L.CieraError) as e:       # no CIERA_TENSOR_CODED flag
+        L.ciera_encode([it], 0x40000, need, stream=0)
+    assert e.value.code == 1
+    it = L.encode_item(L.Tensor(64, 64, 1, 512, 2, flags=flag), 0, 4, 0x10000, 0x20000, 0x30000, 64 + 32 * 64 * 2)
+    with pytest.raises(L.CieraError) as e:       # compress beyond 3
+        L.ciera_encode([it], 0x40000, need, stream=0)
+    assert e.value.code == 1

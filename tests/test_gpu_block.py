@@ -28,11 +28,12 @@ def run_block(shapes, dtype, world, block, w0, w1, edits=None, variant=None):
     block variant (or `variant` per tensor), optionally edit stream bytes, decode;
     compare everything with the oracle.  Returns (gpu status, oracle status)."""
     odt = DT[dtype]
-    codec = LayerCodec(shapes, dtype, world, block, "cuda", 10_000)
+    variant = variant or [B.BLOCK] * len(shapes)
+    coded = [v == B.CODED for v in variant]
+    codec = LayerCodec(shapes, dtype, world, block, "cuda", 10_000, coded=coded)
     d0 = [x.to("cuda").contiguous() for x in w0]
     d1 = [x.to("cuda").contiguous() for x in w1]
     codec.seed_cache(d0)
-    variant = variant or [B.BLOCK] * len(shapes)
 
     def shards(ws, r):
         return [ws[i].reshape(-1)[slice(*(lambda o, n: (o, o + n))(*codec.shard(i, r)))].clone()
@@ -66,6 +67,8 @@ def run_block(shapes, dtype, world, block, w0, w1, edits=None, variant=None):
             if variant[i] == B.BLOCK:
                 s, h1 = O.encode_block(x1[off:off + n], o_hash[(i, r)], odt, block, True, off, r, world)
                 assert np.array_equal(_hashes_np(codec.hash_cache(i, r)), h1), f"hash cache {i} {r}"
+            elif variant[i] == B.CODED:
+                s = O.encode_coded(x1[off:off + n], cache0[off:off + n], odt, block, True, off, r, world)
             else:
                 s = O.encode(x1[off:off + n], cache0[off:off + n], odt, block, bool(variant[i]), off, r, world)
             if not edits:
@@ -78,7 +81,7 @@ def run_block(shapes, dtype, world, block, w0, w1, edits=None, variant=None):
         for (ei, er, o, b) in edits or []:
             if ei == i:
                 o_slots[er][o:o + len(b)] = np.frombuffer(bytes(b), dtype=np.uint8)
-        o_out, o_cache, ost = O.decode(o_slots, rows, cols, odt, block, world, cache0)
+        o_out, o_cache, ost = O.decode(o_slots, rows, cols, odt, block, world, cache0, coded=coded[i])
         o_status |= ost
         if not edits:
             assert np.array_equal(to_np(codec.out_view(i)), x1), f"tensor {i}: decode(encode(x)) != x"

@@ -196,7 +196,7 @@ def test_known_answer_stream_layout():
     want += struct.pack("<IIII", 1100, 4096, 1110, 4096 + len(d1))
     want += bytes(ex1[:4096]) + d1
     assert s.tobytes() == bytes(want)
-    out, ex, st = O.decode_stream(s, O.BF16, 64, 8192, 7, 1, 2, cache)
+    out, ex, st = O.decode_stream(s, O.BF16, 64, 8192, 7, 1, 2, cache, coded=True)
     assert st == 0 and np.array_equal(out, x1)
 
 
@@ -216,6 +216,9 @@ def test_known_answer_padding_and_no_change():
     assert s[176:].tobytes() == d
     s0 = O.encode_coded(x0, cache, O.BF16, 64, True)
     assert O.parse_header(s0)["mode"] == O.MODE_CODED and s0.size == 164
+    # a receiver that did not declare the tensor coded rejects mode 3 as a field mismatch
+    assert O.decode_stream(s, O.BF16, 64, 100, 0, 0, 1, cache)[2] == O.ST_FIELD
+    assert O.decode_stream(s, O.BF16, 64, 100, 0, 0, 1, cache, coded=True)[2] == 0
     assert O.parse_header(O.encode_coded(x1, cache, O.BF16, 64, False))["mode"] == O.MODE_RAW
 
 
@@ -248,7 +251,7 @@ def test_round_trip_random_chunks_and_specials():
             x1 = ((x0 & ~idt(em << shift)) | (e1.astype(idt) << shift)).astype(idt)
             cache = O.cache_update(x0, dt)
             s = O.encode_coded(x1, cache, dt, 64, True, 0, 0, 1)
-            out, ex, st = O.decode_stream(s, dt, 64, n, 0, 0, 1, cache)
+            out, ex, st = O.decode_stream(s, dt, 64, n, 0, 0, 1, cache, coded=True)
             assert st == 0 and np.array_equal(out, x1) and np.array_equal(ex, O.cache_update(x1, dt)), (dt, n, f)
 
 
@@ -277,7 +280,7 @@ def _coded_case(n=12000, f=0.02, seed=9):
 
 
 def _status(s, cache, n):
-    return O.decode_stream(s, O.BF16, 64, n, 0, 0, 1, cache)[2]
+    return O.decode_stream(s, O.BF16, 64, n, 0, 0, 1, cache, coded=True)[2]
 
 
 def test_coded_decode_status_classes():
@@ -334,4 +337,4 @@ def test_coded_decode_flags_words_and_ranges():
     i = int(np.nonzero(((x1 >> 7) & 0xFF).astype(np.uint8)[:4096] != cache[:4096])[0][0])
     t = s.copy()
     t[dpos + i] = cache[i]
-    assert O.decode_stream(t, O.BF16, 64, 8192, 0, 0, 1, cache)[2] & O.ST_PATCH
+    assert O.decode_stream(t, O.BF16, 64, 8192, 0, 0, 1, cache, coded=True)[2] & O.ST_PATCH

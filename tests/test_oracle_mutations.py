@@ -139,12 +139,12 @@ def _index_plus_one(orig_enc, orig_dec):
             rec[:, :4] = idx.astype("<u4").view(np.uint8).reshape(p, 4)
         return s
 
-    def dec(s, dtype, B, n, off, rank, world, cache_slice):
+    def dec(s, dtype, B, n, off, rank, world, cache_slice, coded=False):
         s = np.asarray(s, np.uint8).copy()
         try:
             h = O.parse_header(s)
         except ValueError:
-            return orig_dec(s, dtype, B, n, off, rank, world, cache_slice)
+            return orig_dec(s, dtype, B, n, off, rank, world, cache_slice, coded)
         if h["magic"] == O.MAGIC and h["mode"] == O.MODE_COMPRESSED and 0 < h["n_changed"] <= n:
             p = h["n_changed"]
             pb = 64 + O.sm_section_bytes(n, dtype) + O.bitmap_bytes(n, B)
@@ -152,13 +152,13 @@ def _index_plus_one(orig_enc, orig_dec):
                 rec = s[pb:pb + 5 * p].reshape(p, 5)
                 idx = rec[:, :4].copy().view("<u4").reshape(-1) - 1
                 rec[:, :4] = idx.astype("<u4").view(np.uint8).reshape(p, 4)
-        return orig_dec(s, dtype, B, n, off, rank, world, cache_slice)
+        return orig_dec(s, dtype, B, n, off, rank, world, cache_slice, coded)
     return enc, dec
 
 
 def _decode_skips_patches(orig):
-    def dec(s, dtype, B, n, off, rank, world, cache_slice):
-        x, ex, st = orig(s, dtype, B, n, off, rank, world, cache_slice)
+    def dec(s, dtype, B, n, off, rank, world, cache_slice, coded=False):
+        x, ex, st = orig(s, dtype, B, n, off, rank, world, cache_slice, coded)
         if x is None or O.parse_header(np.asarray(s, np.uint8))["mode"] == O.MODE_RAW:
             return x, ex, st
         sm = O.sign_mantissa_field(x, dtype)
