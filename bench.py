@@ -43,7 +43,7 @@ DTYPES = {"bf16": ("bfloat16", 2, "int16"), "fp16": ("float16", 2, "int16"), "fp
 
 def workload_name(args):
     return (f"olmoe_moe_layer_{args.dtype}_" + ("clustered" if args.clustered else "uniform")
-            + ("_blockhash" if getattr(args, "variant", "patches") == "block" else ""))
+            + {"block": "_blockhash", "coded": "_coded"}.get(getattr(args, "variant", "patches"), ""))
 
 
 def log(*a):
@@ -58,9 +58,10 @@ def parse():
     ap.add_argument("--frac", type=float, default=0.01)
     ap.add_argument("--clustered", action="store_true")
     ap.add_argument("--dtype", choices=sorted(DTYPES), default="bf16")
-    ap.add_argument("--variant", choices=["patches", "block"], default="patches",
+    ap.add_argument("--variant", choices=["patches", "block", "coded"], default="patches",
                     help="patches: per-value (index, exponent) records, as planned; block: the pages' "
-                         "block-hash variant for every tensor")
+                         "block-hash variant for every tensor; coded: the changes range-ANS coded "
+                         "(stream mode 3) for every tensor")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -152,7 +153,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(specs, w0, w1, wl["world"], wl["block"], A, args.cpu_seconds, args.dtype,
-                           wl["variant"] == "block")
+                           wl["variant"])
 
     out = {
         "metric": f"encode/decode GB/s ({args.dtype} OLMoE MoE layer, {args.frac * 100:g}% exp change) "
@@ -265,8 +266,9 @@ def setup(args):
     torch.cuda.synchronize()
     log(f"generated {N} weights in {time.time() - t0:.1f}s")
 
-    A = LayerCodec(shapes, tdt, world, blk, dev, ppm)
-    Bc = LayerCodec(shapes, tdt, world, blk, dev, ppm, cache=A.cache)
+    coded = args.variant == "coded"
+    A = LayerCodec(shapes, tdt, world, blk, dev, ppm, coded=[coded] * len(specs))
+    Bc = LayerCodec(shapes, tdt, world, blk, dev, ppm, cache=A.cache, coded=[coded] * len(specs))
 
     def shards(ws, r):
         out = []
@@ -279,7 +281,7 @@ def setup(args):
     # block variant keeps per-rank hash caches instead, seeded from W0 and
     # shared by both states like the exponent cache.
     block = args.variant == "block"
-    comp = [L.BLOCK] * len(specs) if block else None
+    comp = [L.BLOCK] * len(specs) if block else [L.CODED] * len(specs) if coded else None
     A.seed_cache(w0)
     if block:
         Bc.share_hash_caches(A)
@@ -324,7 +326,7 @@ def setup(args):
         dec_bytes = stream_bytes + N + E * N + P_total     # read streams + cache, write values + changed cache
         enc_bytes = E * n_enc + n_enc + enc_stream_bytes   # read shard + cache slice, write streams
     log(f"P={P_total} ({P_total / N:.4%}), streams {stream_bytes} B vs raw {raw_bytes} B "
-        f"(ratio {raw_bytes / stream_bytes:.4f}), {'BLOCK' if block else 'COMPRESSED'} streams "
+        f"(ratio {raw_bytes / stream_bytes:.4f}), {'BLOCK' if block else 'CODED' if coded else 'COMPRESSED'} streams "
         f"{int((hA['mode'] != 0).sum())}/{len(hA['mode'])}")
 
     # prepared launches (tables uploaded once)
@@ -521,7 +523,7 @@ def pipeline(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16", block_variant=False):
+def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16", variant="patches"):
     """The oracle, as it stands, on a bounded sample of the same workload:
     for whole tensors in layer order, encode rank 0's shard and decode the
     full tensor from all 16 streams, until the CPU time budget is spent.  Its
@@ -533,6 +535,7 @@ def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16", blo
 
     odt = {"bf16": O.BF16, "fp16": O.FP16, "fp32": O.FP32}[dtype]
     E = O.elem_bytes(odt)
+    block_variant = variant == "block"
 
     def bits(t):
         if E == 4:
@@ -553,6 +556,8 @@ def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16", blo
                 t = time.perf_counter()
             if block_variant:
                 st, _ = O.encode_block(x1[off:off + n], h0, odt, block, True, off, r, world)
+            elif variant == "coded":
+                st = O.encode_coded(x1[off:off + n], cache[off:off + n], odt, block, True, off, r, world)
             else:
                 st = O.encode(x1[off:off + n], cache[off:off + n], odt, block, bool(codec.plans[i].compress),
                               off, r, world)
@@ -564,7 +569,8 @@ def cpu_baseline(specs, w0, w1, world, block, codec, budget_s, dtype="bf16", blo
                 logical += E * n
             streams.append(st)
         t = time.perf_counter()
-        out, new_cache, status = O.decode(streams, s.rows, s.cols, odt, block, world, cache)
+        out, new_cache, status = O.decode(streams, s.rows, s.cols, odt, block, world, cache,
+                                          coded=variant == "coded")
         t_dec += time.perf_counter() - t
         assert status == 0 and np.array_equal(out, x1)
         logical += E * s.numel

@@ -37,7 +37,7 @@
  *     0; the table holds two u32 per chunk: the changed values and the data
  *     bytes of this and all earlier chunks.  A chunk's data is dense -- its
  *     exponent bytes, zero-padded to a multiple of 4 -- when that is what its
- *     byte count says, else range-ANS data: L = min(64, ceil(c/8)) final coder
+ *     byte count says, else range-ANS data: L = min(64, ceil(c/4)) final coder
  *     states (u32), 16-bit words, a zero word when their number is odd.  Change
  *     j of the chunk (index order) belongs to state j mod L and is four
  *     symbols: its gap bucket b = bit length of (gap + 1), gap = index -

@@ -783,7 +783,7 @@ __global__ __launch_bounds__(kThreads) void hash_seed_kernel(const uint8_t* __re
 // ------------------------------------------- entropy-coded patches (encode)
 // [CIERA 3.1; Algorithm 1] the changed exponents travel ANS-coded.  Each chunk
 // of 4096 values (a row of a tile, from the shard's first value) codes its c
-// changes with range ANS over L = min(64, ceil(c/8)) interleaved 32-bit
+// changes with range ANS over L = min(64, ceil(c/4)) interleaved 32-bit
 // states, one per lane of one wave; change j goes to state j mod L.  Per
 // change four symbols, in decode order: the gap bucket b = bit length of
 // (gap + 1), gap = index - previous index - 1 (previous = -1 at the chunk
@@ -803,7 +803,7 @@ constexpr uint32_t kChunkMaxChanges = 1024;
 constexpr uint32_t kRansLow = 1u << 16;
 
 __device__ __forceinline__ uint32_t pad4u(uint32_t v) { return (v + 3u) & ~3u; }
-__device__ __forceinline__ uint32_t rans_lanes(uint32_t c) { return min(64u, (c + 7u) / 8u); }
+__device__ __forceinline__ uint32_t rans_lanes(uint32_t c) { return min(64u, (c + 3u) / 4u); }
 
 // Bytes of a chunk's data from its changes, words and form.
 __device__ __forceinline__ uint32_t coded_bytes(uint32_t c, uint32_t words, bool dense, uint32_t len) {
@@ -813,18 +813,27 @@ __device__ __forceinline__ uint32_t coded_bytes(uint32_t c, uint32_t words, bool
 
 // Gap-bucket frequencies (sum 2^12) for c changes among len values; lane i < 13
 // gets bucket i+1's frequency f and start cum.  q = 1 - c/len in 32-bit fixed
-// point; S_i = q^(2^i - 1) by repeated squaring (S_i = S_{i-1} * q^(2^(i-1)));
-// bucket b takes S_{b-1} - S_b (the last, S_12) as a share of 2^12, at least
-// 1; the largest, first of equals, absorbs the rounding.  Wave-wide.
+// point; S_i = q^(2^i - 1) by repeated squaring (S_1 = q, S_{i+1} = S_i *
+// q^(2^i) and q^(2^(i+1)) = (q^(2^i))^2, each product's high 32 bits); bucket
+// b takes S_{b-1} - S_b (the last, S_12) as a share of 2^12, at least 1; the
+// largest, first of equals, absorbs the rounding.  Wave-wide.
 __device__ __forceinline__ void gap_table(uint32_t c, uint32_t len, uint32_t& f, uint32_t& cum) {
   const uint32_t lane = lane_id();
   const uint32_t i = min(lane, 12u);
-  uint64_t Q = ((uint64_t)(len - c) << 32) / len, S = 1ull << 32;
-  for (uint32_t k = 0; k < i; ++k) {
-    S = (S * Q) >> 32;
-    Q = (Q * Q) >> 32;
+  // q < 2^32 as c >= 1 (a whole chunk, len = 2^12, needs no division)
+  const uint32_t q = len == (uint32_t)kSub ? (len - c) << 20 : (uint32_t)(((uint64_t)(len - c) << 32) / len);
+  // lane i: S_i (S_0 = 2^32, kept as 0 with the flag `one`) and S_{i+1}
+  uint32_t Q = q, S = q;  // S_1, q^(2^1) below
+  for (uint32_t k = 1; k < i; ++k) {
+    Q = __umulhi(Q, Q);
+    S = __umulhi(S, Q);
   }
-  const uint64_t share = i < 12u ? S - ((S * Q) >> 32) : S;
+  // now S = S_i for i >= 1; the next factor is q^(2^i)
+  const uint32_t Qn = i >= 1 ? __umulhi(Q, Q) : q;
+  uint64_t share;
+  if (i == 0) share = (1ull << 32) - q;                      // S_0 - S_1
+  else if (i < 12u) share = (uint64_t)S - __umulhi(S, Qn);  // S_i - S_{i+1}
+  else share = S;                                            // S_12
   uint32_t fv = lane < 13u ? max(1u, (uint32_t)(share >> 20)) : 0u;
   uint32_t tot = fv, mx = fv;
 #pragma unroll
@@ -865,16 +874,16 @@ __device__ __forceinline__ uint32_t class_of_slot(uint32_t slot) {
 }
 
 // rANS-codes one chunk's c (1..1024) changes, listed in LDS in index order as
-// offset | old exponent << 12 | new exponent << 20, with one wave, and returns
-// the number of words.  With region_end (the end of the chunk's 4096-byte
+// offset | old exponent << 12 | new exponent << 20, with one wave (gap-bucket
+// frequencies and starts from gap_table in gf and gcum), and returns the
+// number of words.  With region_end (the end of the chunk's 4096-byte
 // stash region) the words go backwards from it, so they lie in decode order,
 // and the final states just below them when the data fits the region;
 // nothing is written below region_end - 4096.  Without it nothing is written.
-__device__ uint32_t rans_encode_chunk(const uint32_t* list, uint32_t c, uint32_t len, uint8_t* region_end) {
+__device__ uint32_t rans_encode_chunk(const uint32_t* list, uint32_t c, uint32_t gf, uint32_t gcum,
+                                      uint8_t* region_end) {
   const uint32_t lane = lane_id();
   const uint32_t L = rans_lanes(c);
-  uint32_t gf, gcum;
-  gap_table(c, len, gf, gcum);
   uint32_t x = kRansLow;
   uint32_t R = 0;  // words written so far, counted from the end (uniform)
   // One sub-step, backwards: states about to code a symbol of frequency f
@@ -999,9 +1008,11 @@ __device__ void split_tile_coded(const EncItem& d, uint32_t local, const EncArgs
       uint32_t words = 0;
       bool dense = c[r] > kChunkMaxChanges;
       if (c[r] > 0 && !dense) {  // measure, then write only coded data that is shorter than dense
-        words = rans_encode_chunk(s_list[r], c[r], len, nullptr);
+        uint32_t gf, gcum;
+        gap_table(c[r], len, gf, gcum);
+        words = rans_encode_chunk(s_list[r], c[r], gf, gcum, nullptr);
         dense = coded_bytes(c[r], words, false, len) >= pad4u(len);
-        if (!dense) (void)rans_encode_chunk(s_list[r], c[r], len, regions + (uint32_t)(s0 + r + 1) * kSub);
+        if (!dense) (void)rans_encode_chunk(s_list[r], c[r], gf, gcum, regions + (uint32_t)(s0 + r + 1) * kSub);
       }
       if (lane == 0) s_info[s0 + r] = c[r] | (dense ? 0u : words << 13) | ((dense ? 1u : 0u) << 26);
     }
@@ -1624,9 +1635,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   __shared__ uint32_t s_ex[T / 4];   // the tile's exponents: cached, then patched in place
   __shared__ uint32_t s_sum[kDecThreads / 64];
   // coded patches (the tensor's streams may be CODED): each row's chunk data
-  // and gap-bucket starts
   __shared__ uint32_t s_win[CODED ? U : 1][CODED ? kSub / 4 : 1];
-  __shared__ uint32_t s_cum[CODED ? U : 1][16];
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t tpi = tpr * world;
@@ -1822,8 +1831,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
         if (tid < (uint32_t)U) s_sum[tid] = 0;  // differences per dense row (s_expbm is clear already)
         __syncthreads();
         uint8_t* const s_exb = reinterpret_cast<uint8_t*>(s_ex);
-        auto mark = [&](uint32_t v) {  // value v of the tile was patched
-          const uint32_t bb = (uint32_t)(((ts + v) >> lb) - tb0);
+        auto mark = [&](uint32_t v) {  // value v of the tile was patched (the tile starts a block)
+          const uint32_t bb = v >> lb;
           atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
         };
 #pragma unroll
@@ -1862,12 +1871,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
           const uint16_t* words = reinterpret_cast<const uint16_t*>(&s_win[u][Lr]);
           uint32_t gf, gcum;
           gap_table(cu, len[u], gf, gcum);
-          // bucket starts in LDS (lanes 13-15: 4096, above every slot), read back
-          // as broadcasts for each bucket decode
-          if (lane < 16u) s_cum[u][lane] = lane < 13u ? gcum : 4096u;
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // other lanes read them below
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          // bucket starts 1..12, the same in every lane (scalar registers)
+          uint32_t cum[13];
+#pragma unroll
+          for (int i = 1; i < 13; ++i) cum[i] = __builtin_amdgcn_readlane(gcum, i);
           uint32_t x = lane < Lr ? s_win[u][lane] : kRansLow;
           uint32_t ptr = 0, run = 0, err = 0;
           auto renorm = [&]() {
@@ -1886,14 +1893,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
           const uint32_t steps = (cu + Lr - 1u) / Lr;
           for (uint32_t t = 0; t < steps; ++t) {  // uniform
             const bool act = lane < Lr && t * Lr + lane < cu;
-            uint32_t slot = x & 4095u, bk = 0;
+            // bucket: the last start <= slot (cb), the next one (nb), their count (bk)
+            uint32_t slot = x & 4095u, bk = 1, cb = 0, nb = 4096u;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const v4u cq = *reinterpret_cast<const v4u*>(&s_cum[u][4 * q]);
-              bk += (cq.x <= slot ? 1u : 0u) + (cq.y <= slot ? 1u : 0u) + (cq.z <= slot ? 1u : 0u) +
-                    (cq.w <= slot ? 1u : 0u);
+            for (int i = 1; i < 13; ++i) {
+              const bool le = cum[i] <= slot;
+              bk += le ? 1u : 0u;
+              cb = le ? cum[i] : cb;
             }
-            const uint32_t fb = __shfl(gf, (int)(bk - 1u)), cb = __shfl(gcum, (int)(bk - 1u));
+#pragma unroll
+            for (int i = 12; i > 0; --i) nb = cum[i] > slot ? cum[i] : nb;
+            const uint32_t fb = nb - cb;
             if (act) x = fb * (x >> 12) + slot - cb;
             renorm();
             uint32_t g1 = 1;

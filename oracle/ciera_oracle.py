@@ -634,7 +634,7 @@ def _decode_blocks(s, pos, c, n, block_size, sm, ex, dtype):
 #       data is shorter than the dense form, else dense: the chunk's new
 #       exponent bytes, zero-padded to a multiple of 4.  A chunk without
 #       changes sends nothing.
-#   R31 rANS data: L = min(64, ceil(c/8)) coder states; change j (in index
+#   R31 rANS data: L = min(64, ceil(c/4)) coder states; change j (in index
 #       order) goes to state j mod L.  Per change four symbols, in decode
 #       order: the gap bucket b = bit length of (gap + 1), where gap = index
 #       minus previous index minus 1 (the first change of a chunk counts from
@@ -697,7 +697,7 @@ def chunk_length(n: int, k: int) -> int:
 
 
 def rans_lanes(c: int) -> int:
-    return min(64, (c + 7) // 8)
+    return min(64, (c + 3) // 4)
 
 
 def gap_bucket_freqs(c: int, length: int) -> List[int]:

@@ -92,8 +92,8 @@ def test_interleaved_states_match_single_state_coding():
 
 
 def test_lane_counts():
-    assert [O.rans_lanes(c) for c in (1, 8, 9, 16, 17, 100, 504, 505, 512, 1024, 4096)] == \
-        [1, 1, 2, 2, 3, 13, 63, 64, 64, 64, 64]
+    assert [O.rans_lanes(c) for c in (1, 4, 5, 8, 9, 100, 252, 253, 256, 1024, 4096)] == \
+        [1, 1, 2, 2, 3, 25, 63, 64, 64, 64, 64]
 
 
 def test_chunk_symbols_worked_by_hand():
@@ -257,9 +257,9 @@ def test_round_trip_random_chunks_and_specials():
 
 def test_bits_per_change_near_entropy():
     """At 1% uniform +-1 changes a change costs the entropy of a geometric gap
-    (8.08 bits) plus 1.01 bits of class, plus the states' start-up (16 bits
-    per state, about 6 states per 41 changes): under 13 bits, against 40
-    bits as a (u32, u8) record."""
+    (8.08 bits) plus 1.01 bits of class, plus the states' start-up and final
+    flush (about 16 bits per state, 11 states per 41 changes): under 17 bits,
+    against 40 bits as a (u32, u8) record."""
     rng = np.random.default_rng(8)
     n = 131072
     old = rng.integers(100, 130, n).astype(np.uint8)
@@ -268,7 +268,7 @@ def test_bits_per_change_near_entropy():
     tot = sum(len(O.encode_chunk(new[k * 4096:(k + 1) * 4096], old[k * 4096:(k + 1) * 4096]))
               for k in range(O.n_chunks(n)))
     bits = 8 * tot / int(m.sum())
-    assert 9.0 < bits < 13.0, bits
+    assert 9.0 < bits < 17.0, bits
 
 
 def _coded_case(n=12000, f=0.02, seed=9):
@@ -302,9 +302,9 @@ def test_coded_decode_status_classes():
     assert edit(tpos + 8 * (nch - 1) + 4, tab[-1] - 4) & O.ST_LENGTH  # last entry short of the data
     assert edit(tpos + 0, tab[2] + 1) & O.ST_LENGTH                  # goes backwards
     assert edit(tpos + 4, tab[1] + 2) & O.ST_LENGTH                  # not a multiple of 4
-    t = s.copy()                                                      # a state flipped
-    t[dpos] ^= 1
-    assert _status(t, cache, n) & O.ST_PATCH
+    t = s.copy()                                                      # a state bit above the slot flipped
+    t[dpos + 2] ^= 0x10
+    assert _status(t, cache, n) & (O.ST_PATCH | O.ST_BITMAP)
     t = s.copy()                                                      # total beyond the data
     t[32:40] = np.frombuffer((s.size + 4).to_bytes(8, "little"), dtype=np.uint8)
     assert _status(np.concatenate([t, np.zeros(4, np.uint8)]), cache, n) & O.ST_LENGTH
