@@ -35,13 +35,14 @@ def exp_field_gpu(w: torch.Tensor) -> torch.Tensor:
 
 
 def run_layer(specs, w_prev, w_next, dtype, world, ppm, codec=None, sample=(), seed_cache=True,
-              expect_modes=None):
+              expect_modes=None, coded=False):
     """Encode every rank (rank 0 prepared, the others one-shot), decode with the
     prepared batch, check properties at full size and sampled tensors against
     the oracle.  Returns the codec (cache carried) and a summary."""
     shapes = [(s.rows, s.cols) for s in specs]
+    comp = [3] * len(specs) if coded else None  # coded patches for every tensor
     if codec is None:
-        codec = LayerCodec(shapes, dtype, world, 512, "cuda", ppm)
+        codec = LayerCodec(shapes, dtype, world, 512, "cuda", ppm, coded=[coded] * len(specs))
     else:
         codec.plans = [__import__("lossless_weight_compression_amd").ciera_plan(t, ppm) for t in codec.tensors]
     if seed_cache:
@@ -57,9 +58,9 @@ def run_layer(specs, w_prev, w_next, dtype, world, ppm, codec=None, sample=(), s
             off, n = codec.shard(i, r)
             shards.append(w_next[i].reshape(-1)[off:off + n])
         if r == 0:
-            codec.prepare_encode(0, shards).launch()
+            codec.prepare_encode(0, shards, compress=comp).launch()
         else:
-            codec.encode(r, shards)
+            codec.encode(r, shards, compress=comp)
     torch.cuda.synchronize()
     # sampled streams against the oracle
     o_streams = {}
@@ -69,8 +70,11 @@ def run_layer(specs, w_prev, w_next, dtype, world, ppm, codec=None, sample=(), s
         o_streams[i] = []
         for r in range(world):
             off, n = O.shard(s.rows, s.cols, world, r)
-            st = O.encode(x[off:off + n], ocache[i][off:off + n], ODT[dtype], 512,
-                          bool(codec.plans[i].compress), off, r, world)
+            if coded:
+                st = O.encode_coded(x[off:off + n], ocache[i][off:off + n], ODT[dtype], 512, True, off, r, world)
+            else:
+                st = O.encode(x[off:off + n], ocache[i][off:off + n], ODT[dtype], 512,
+                              bool(codec.plans[i].compress), off, r, world)
             got = codec.slot(i, r)[:st.size].cpu().numpy()
             assert np.array_equal(got, st), f"tensor {i} rank {r}: stream differs from the oracle"
             o_streams[i].append(st)
@@ -85,7 +89,7 @@ def run_layer(specs, w_prev, w_next, dtype, world, ppm, codec=None, sample=(), s
     # sampled decode against the oracle
     for i in sample:
         s = specs[i]
-        out, cache, st = O.decode(o_streams[i], s.rows, s.cols, ODT[dtype], 512, world, ocache[i])
+        out, cache, st = O.decode(o_streams[i], s.rows, s.cols, ODT[dtype], 512, world, ocache[i], coded=coded)
         assert st == 0
         assert np.array_equal(to_np(codec.out_view(i)), out)
         assert np.array_equal(codec.cache_view(i).cpu().numpy(), cache)
@@ -128,6 +132,29 @@ def test_olmoe_layer_bf16(frac, clustered):
     say(f"[gpu]   compression ratio {res['ratio']:.4f}")
     # raw/compressed ~ 2 / (1 + 5f) either way (clustered shards with > ~20% changes go RAW)
     assert abs(res["ratio"] - EXPECTED_RATIO[frac]) < (0.01 if not clustered else 0.03)
+
+
+# raw/streams with coded patches (a change costs about 16 bits at 1%)
+EXPECTED_RATIO_CODED = {0.01: 1.956, 0.1: 1.780}
+
+
+@pytest.mark.parametrize("frac,clustered,sample", [(0.01, False, (0, 97, 191)), (0.1, False, (0, 191)),
+                                                   (0.01, True, (0, 97, 191))])
+def test_olmoe_layer_bf16_coded(frac, clustered, sample):
+    """The full layer with every tensor's changes range-ANS coded (stream mode
+    3), in the prepared launch bench.py --variant coded times."""
+    say(f"[gpu] OLMoE layer bf16 coded f={frac} clustered={clustered}")
+    specs, cfg, world, w0, w1 = _layer("layer", frac, clustered)
+    ppm = int(round(frac * 1e6))
+
+    def modes_all_coded(m, codec):
+        assert (m == O.MODE_CODED).all()
+
+    _, res = run_layer(specs, w0, w1, torch.bfloat16, world, ppm, sample=sample, coded=True,
+                       expect_modes=modes_all_coded)
+    say(f"[gpu]   compression ratio {res['ratio']:.4f}")
+    if not clustered:
+        assert abs(res["ratio"] - EXPECTED_RATIO_CODED[frac]) < 0.01
 
 
 @pytest.mark.parametrize("frac", [0.0, 0.01, 0.1])
