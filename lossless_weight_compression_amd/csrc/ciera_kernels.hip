@@ -1636,6 +1636,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   __shared__ uint32_t s_sum[kDecThreads / 64];
   // coded patches (the tensor's streams may be CODED): each row's chunk data
   __shared__ uint32_t s_win[CODED ? U : 1][CODED ? kSub / 4 : 1];
+  __shared__ uint8_t s_mark[CODED ? U : 1][64];  // coded: blocks of each row that were patched
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t tpi = tpr * world;
@@ -1679,6 +1680,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     s_hdr[4 * tid] = h.x; s_hdr[4 * tid + 1] = h.y; s_hdr[4 * tid + 2] = h.z; s_hdr[4 * tid + 3] = h.w;
   }
   if (tid < BMW) s_expbm[tid] = 0;
+  if (CODED && tid < (uint32_t)U * 64u) s_mark[tid >> 6][tid & 63u] = 0;
   // the cached exponents go to LDS now: the header read above already waits
   // for the bulk loads (loads complete in order), and patches overwrite them
   // after the next barrier
@@ -1940,13 +1942,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
                   err |= CIERA_ST_PATCH;
                 } else {
                   rowex[idx] = (uint8_t)nv;
-                  mark(u * kDecRow + idx);
+                  s_mark[u][idx >> lb] = 1;  // plain stores: lanes hitting one block write the same value
                 }
               }
             }
           }
           if (ptr + (ptr & 1u) != navail || (lane < Lr && x != kRansLow)) err |= CIERA_ST_PATCH;
           if (err) report(status_out, err);
+          // the row's patched blocks (at most 64: B >= 64) into the tile's bits
+          const uint32_t nbr = (uint32_t)kSub >> lb, rb0 = u * nbr;  // blocks per row; the row's first
+          const uint64_t rowbm = __ballot(lane < nbr && s_mark[u][lane] != 0);
+          if (lane == 0 && rowbm) {
+            if (nbr >= 32u) {  // whole words
+              atomicOr(&s_expbm[rb0 >> 5], (uint32_t)rowbm);
+              if (nbr == 64u) atomicOr(&s_expbm[(rb0 >> 5) + 1], (uint32_t)(rowbm >> 32));
+            } else {  // the row's bits lie inside one word
+              atomicOr(&s_expbm[rb0 >> 5], (uint32_t)rowbm << (rb0 & 31u));
+            }
+          }
         }
         __syncthreads();
         uint32_t eb = 0;
