@@ -130,6 +130,11 @@ def main():
         f"p90 {dec_ms[9 * len(dec_ms) // 10] * 1e3:.1f})")
 
     E = wl["E"]
+
+    def pct(ms):  # median and p10/p90 of a sorted list of per-step times (ms), in us
+        return {"median_us": round(ms[len(ms) // 2] * 1e3, 2), "p10_us": round(ms[len(ms) // 10] * 1e3, 2),
+                "p90_us": round(ms[9 * len(ms) // 10] * 1e3, 2)}
+
     logical = E * n_enc + E * N
     value = logical / (ms_step * 1e-3) / 1e9
     dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
@@ -144,7 +149,8 @@ def main():
     if os.path.exists(tf):
         t = json.load(open(tf))
         if t.get("kernel_source_sha256") == sha and t.get("workload") == "olmoe_layer_bf16_1pct_uniform" \
-                and not args.clustered and wl["ppm"] == 10000 and args.dtype == "bf16":
+                and not args.clustered and wl["ppm"] == 10000 and args.dtype == "bf16" \
+                and args.variant == "patches":
             traffic = t.get("hbm_bytes_per_launch")
             enc_traffic = t.get("encode_kernel_bytes_per_launch", 0) + t.get("encode_finish_kernel_bytes_per_launch", 0)
 
@@ -173,14 +179,14 @@ def main():
                    "experts": 64, "tensors": len(specs), "elements": N, "world": wl["world"],
                    "block_size": wl["block"], "change_frac": args.frac,
                    "step": "plan(192) + encode(rank 0 shard) + decode(full layer, 16 streams)"},
-        "encode": {"avg_us": round(enc_avg * 1e3, 2), "elements": n_enc,
+        "encode": {"avg_us": round(enc_avg * 1e3, 2), **pct(enc_ms), "elements": n_enc,
                    "logical_GBps": round(E * n_enc / (enc_avg * 1e-3) / 1e9, 1),
                    "algorithmic_bytes": enc_bytes, "achieved_GBps": round(enc_gbps, 1),
                    "hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
                    "traffic_bytes": enc_traffic,
                    "traffic_frac": None if enc_traffic is None
                    else round(enc_traffic / (enc_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "decode": {"avg_us": round(dec_avg * 1e3, 2), "elements": N,
+        "decode": {"avg_us": round(dec_avg * 1e3, 2), **pct(dec_ms), "elements": N,
                    "logical_GBps": round(E * N / (dec_avg * 1e-3) / 1e9, 1),
                    "algorithmic_bytes": dec_bytes, "achieved_GBps": round(dec_gbps, 1),
                    "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4)},
@@ -192,7 +198,8 @@ def main():
                          "inputs in HBM)"},
         "compression_ratio": round(wl["raw_bytes"] / wl["stream_bytes"], 4),
         ("changed_blocks" if wl["variant"] == "block" else "changed_exponents"): wl["P_total"],
-        "roofline": {"bound": "hbm", "kernel": f"decode_kernel<{args.dtype},2>",
+        "roofline": {"bound": "hbm",
+                     "kernel": f"decode_kernel<{args.dtype},2{',coded' if args.variant == 'coded' else ''}>",
                      "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      # the same launch on the HBM bytes it actually moves (rocprofv3 counters)
