@@ -35,7 +35,7 @@ from __future__ import annotations
 
 import dataclasses
 import hashlib
-from typing import Iterable, List, Optional, Sequence, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 

@@ -15,7 +15,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 from lossless_weight_compression_amd import _binding as B  # noqa: E402
-from tests.gpu_harness import DT, say, to_np  # noqa: E402
+from tests.gpu_harness import say, to_np  # noqa: E402
 from tests.test_gpu_block import run_block  # noqa: E402
 
 _SHIFT = {torch.bfloat16: (7, 0xFF, torch.int16), torch.float16: (10, 0x1F, torch.int16),

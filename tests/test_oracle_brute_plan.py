@@ -1,6 +1,5 @@
 """Brute force of the oracle against its scalar twin, decode validation classes,
 and the plan's hand-computed decision table."""
-import itertools
 
 import numpy as np
 import pytest

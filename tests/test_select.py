@@ -133,7 +133,6 @@ def test_c_select_matches_oracle_random_gains():
 
 
 def test_c_select_rejects_null():
-    import ctypes
     lib = L._binding._lib
     assert lib.ciera_select(None, 0, 0, None) == 0
     assert lib.ciera_select(None, 1, 0, None) == L._binding.CIERA_ERR_INVALID_ARG
