@@ -1617,6 +1617,192 @@ __global__ __launch_bounds__(kThreads) void encode_finish_tile_kernel(FinArgs f,
   }
 }
 
+// Validation of a stream's 64-byte header h (16 words) for shard (n, off) of
+// rank r: 0, or the status bit of the first failing class -- magic/version,
+// a field mismatch (mode 3 only where the tensor is declared coded), or
+// lengths inconsistent with the mode or beyond the slot (mode 3: only the
+// table's place is checked here, the rest per chunk).
+template <int DT, bool CODED>
+__device__ __forceinline__ uint32_t header_status(const uint32_t* h, uint64_t n, uint64_t off, uint32_t r,
+                                                  uint32_t world, uint32_t B, uint64_t nb, uint64_t nbm,
+                                                  uint64_t slot) {
+  constexpr int E = Tr<DT>::E;
+  const uint32_t h_dtype = (h[1] >> 16) & 0xFFu, h_mode = h[1] >> 24;
+  const uint64_t h_n = h[4] | ((uint64_t)h[5] << 32);
+  const uint64_t P = h[6] | ((uint64_t)h[7] << 32);
+  const uint64_t h_tot = h[8] | ((uint64_t)h[9] << 32);
+  const uint64_t h_off = h[10] | ((uint64_t)h[11] << 32);
+  if (h[0] != 0x52454943u || (h[1] & 0xFFFFu) != 1u) return CIERA_ST_MAGIC;
+  if (h_dtype != (uint32_t)DT || h[2] != B || h_n != n || h_off != off || h[12] != r || h[13] != world ||
+      h_mode > (CODED ? kCoded : kBlockVariant))
+    return CIERA_ST_FIELD;
+  if (h_mode == kCoded) {  // the chunk table gives the length; checked per chunk
+    const uint64_t dpos = ((kHeader + sm_sec<DT>(n) + nbm + 3) & ~3ull) + 8 * ((n + kSub - 1) / kSub);
+    if (P > n || h_tot > slot || (P ? h_tot < dpos : h_tot != kHeader + sm_sec<DT>(n))) return CIERA_ST_LENGTH;
+    return 0;
+  }
+  const uint64_t want = h_mode == 0   ? kHeader + n * E
+                        : h_mode == 1 ? kHeader + sm_sec<DT>(n) + (P ? nbm + 5 * P : 0)
+                                      : kHeader + sm_sec<DT>(n) + (P ? nbm + P * B : 0);
+  if (P > (h_mode == 2 ? nb : n) || h_tot > slot || h_tot != want) return CIERA_ST_LENGTH;
+  return 0;
+}
+
+// Chunk k's table entries (k-1 and k: cumulative changes pc, cc and bytes pb,
+// cb) checked against the chunk (len values) and the data (D bytes, nch
+// chunks, P changes): true when the entry is consistent.  c and bytes: the
+// chunk's changes and data bytes.
+__device__ __forceinline__ bool chunk_entry_ok(uint32_t pc, uint32_t pb, uint32_t cc, uint32_t cb, uint64_t k,
+                                               uint64_t nch, uint32_t len, uint64_t D, uint64_t P) {
+  const uint32_t c = cc - pc, bytes = cb - pb;
+  if (cc < pc || cb < pb || cb > D || c > len || (bytes & 3u) != 0 || ((c == 0) != (bytes == 0)) ||
+      (k == nch - 1 && (cc != P || cb != D)))
+    return false;
+  // coded data holds its states and is shorter than the dense form
+  return !(c > 0 && bytes != pad4u(len) && (bytes < 4u * rans_lanes(c) || bytes > pad4u(len)));
+}
+
+// Decodes one chunk's coded data (win: the data in LDS, nbytes bytes; c
+// changes among len values) with one wave.  Every active lane calls
+// emit(j, idx, cls, esc, ok) for change j: chunk offset idx, step class cls,
+// escaped exponent esc, ok = idx inside the chunk; emit returns status bits.
+// Returns the status bits: ST_PATCH for words missing or left over, a final
+// state other than 2^16, a change past the chunk, and emit's.
+template <class Emit>
+__device__ __forceinline__ uint32_t rans_decode_wave(const uint32_t* win, uint32_t nbytes, uint32_t c, uint32_t len,
+                                                    Emit&& emit) {
+  const uint32_t lane = lane_id();
+  const uint32_t Lr = rans_lanes(c);
+  const uint32_t navail = (nbytes - 4u * Lr) / 2u;
+  const uint16_t* words = reinterpret_cast<const uint16_t*>(win + Lr);
+  uint32_t gf, gcum;
+  gap_table(c, len, gf, gcum);
+  // bucket starts 1..12, the same in every lane (scalar registers)
+  uint32_t cum[13];
+#pragma unroll
+  for (int i = 1; i < 13; ++i) cum[i] = __builtin_amdgcn_readlane(gcum, i);
+  uint32_t x = lane < Lr ? win[lane] : kRansLow;
+  uint32_t ptr = 0, run = 0, err = 0;
+  auto renorm = [&]() {
+    const bool need = lane < Lr && x < kRansLow;
+    const uint64_t m = __ballot(need);
+    if (need) {
+      const uint32_t pos = ptr + lanes_below(m);
+      uint32_t w = 0;
+      if (pos < navail) w = words[pos];
+      else err |= CIERA_ST_PATCH;
+      x = (x << 16) | w;
+    }
+    ptr += (uint32_t)__popcll(m);
+  };
+  const uint32_t steps = (c + Lr - 1u) / Lr;
+  for (uint32_t t = 0; t < steps; ++t) {  // uniform
+    const uint32_t j = t * Lr + lane;
+    const bool act = lane < Lr && j < c;
+    // bucket: the last start <= slot (cb), the next one (nb), their count (bk)
+    uint32_t slot = x & 4095u, bk = 1, cb = 0, nb = 4096u;
+#pragma unroll
+    for (int i = 1; i < 13; ++i) {
+      const bool le = cum[i] <= slot;
+      bk += le ? 1u : 0u;
+      cb = le ? cum[i] : cb;
+    }
+#pragma unroll
+    for (int i = 12; i > 0; --i) nb = cum[i] > slot ? cum[i] : nb;
+    if (act) x = (nb - cb) * (x >> 12) + slot - cb;
+    renorm();
+    uint32_t g1 = 1;
+    if (act) {
+      const uint32_t kb = bk - 1u;
+      g1 = (1u << kb) | (x & ((1u << kb) - 1u));
+      x >>= kb;
+    }
+    renorm();
+    slot = x & 4095u;
+    const uint32_t cls = class_of_slot(slot);
+    if (act) x = class_freq(cls) * (x >> 12) + slot - class_start(cls);
+    renorm();
+    uint32_t esc = 0;
+    if (act && cls == 14u) {
+      esc = x & 0xFFu;
+      x >>= 8;
+    }
+    renorm();
+    uint32_t incl = act ? g1 : 0u;  // indices: running sum of gap + 1 in change order
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t tt = __shfl_up(incl, o);
+      if (lane >= (uint32_t)o) incl += tt;
+    }
+    const uint32_t idx = run + incl - 1u;
+    run += __shfl(incl, 63);
+    if (act) {
+      const bool ok = idx < len;
+      if (!ok) err |= CIERA_ST_PATCH;
+      err |= emit(j, idx, cls, esc, ok);
+    }
+  }
+  if (ptr + (ptr & 1u) != navail || (lane < Lr && x != kRansLow)) err |= CIERA_ST_PATCH;
+  return err;
+}
+
+// Coded rows decoded ahead of the merge: one 64-thread workgroup per chunk
+// slot of the decode grid (U rows per decode tile), so that many resident
+// waves hide the decoder's dependent steps.  A chunk whose header and table
+// entry are valid, whose data is coded, and whose changes fit the first bytes
+// of its own output region (4 per change: offset | step class << 12 |
+// escaped exponent << 16, all ones for a change past the chunk, as two 16-bit
+// stores) leaves them there; the merge reads them before it writes the
+// values.  Other chunks are left to the merge.
+template <int DT, int U>
+__global__ __launch_bounds__(64) void coded_prepass_kernel(const DecItem* __restrict__ items, uint32_t item0,
+                                                           uint32_t tpr, uint32_t world, uint32_t* status_out,
+                                                           uint32_t batch_id) {
+  constexpr int E = Tr<DT>::E;
+  __shared__ uint32_t s_h[16];
+  __shared__ uint32_t s_w[kSub / 4];
+  const uint32_t lane = threadIdx.x;
+  const uint32_t cpr = tpr * U, cpi = cpr * world;  // chunk slots per rank and per item
+  const uint32_t blk = blockIdx.x / cpi;
+  const uint32_t rel = blockIdx.x - blk * cpi;
+  const uint32_t r = rel / cpr;
+  const uint64_t k = rel - r * cpr;
+  const DecItem d = items[item0 + blk];
+  if (d.batch_id != batch_id) return;  // uniform
+  const uint64_t off = ((uint64_t)r * d.q + min<uint64_t>(r, d.rem)) * d.cols;
+  const uint64_t n = (d.q + (r < d.rem ? 1u : 0u)) * d.cols;
+  const uint64_t nch = (n + kSub - 1) / kSub;
+  if (k >= nch) return;
+  const uint8_t* st = d.streams + (uint64_t)r * d.slot;
+  const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;
+  const uint64_t nb = (n + B - 1) >> lb, nbm = (nb + 7) / 8;
+  if (lane < 16) s_h[lane] = gp(reinterpret_cast<const uint32_t*>(st))[lane];
+  __syncthreads();
+  if (header_status<DT, true>(s_h, n, off, r, world, B, nb, nbm, d.slot)) return;  // the merge reports it
+  const uint64_t P = s_h[6] | ((uint64_t)s_h[7] << 32), h_tot = s_h[8] | ((uint64_t)s_h[9] << 32);
+  if ((s_h[1] >> 24) != kCoded || P == 0) return;
+  const uint64_t tpos = (kHeader + sm_sec<DT>(n) + nbm + 3) & ~3ull, dpos = tpos + 8 * nch;
+  const G1 uint32_t* e = gp(reinterpret_cast<const uint32_t*>(st + tpos + 8 * k));
+  const uint32_t cc = e[0], cb = e[1], pc = k > 0 ? e[-2] : 0u, pb = k > 0 ? e[-1] : 0u;
+  const uint32_t len = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
+  if (!chunk_entry_ok(pc, pb, cc, cb, k, nch, len, h_tot - dpos, P)) return;
+  const uint32_t c = cc - pc, bytes = cb - pb;
+  if (c == 0 || bytes == pad4u(len) || c > len * E / 4) return;  // nothing, dense, or records do not fit
+  const G1 uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st + dpos + pb));
+  for (uint32_t w = lane; w < bytes / 4; w += 64) s_w[w] = src[w];
+  __syncthreads();
+  G1 uint16_t* rec = gp(reinterpret_cast<uint16_t*>(d.out + (off + k * kSub) * E));
+  const uint32_t err = rans_decode_wave(s_w, bytes, c, len, [rec](uint32_t j, uint32_t idx, uint32_t cls, uint32_t esc,
+                                                                   bool ok) -> uint32_t {
+    const uint32_t v = ok ? idx | (cls << 12) | (esc << 16) : 0xFFFFFFFFu;
+    rec[2 * j] = (uint16_t)v;
+    rec[2 * j + 1] = (uint16_t)(v >> 16);
+    return 0u;
+  });
+  if (err) report(status_out, err);
+}
+
 // --------------------------------------------------------------------- decode
 // One workgroup per tile of U*4096 values of one rank's stream.  The bulk loads
 // (sign|mantissa bytes and cached exponents) are issued before the header and
@@ -1681,6 +1867,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   }
   if (tid < BMW) s_expbm[tid] = 0;
   if (CODED && tid < (uint32_t)U * 64u) s_mark[tid >> 6][tid & 63u] = 0;
+  if (CODED && tid < (uint32_t)U) s_sum[tid] = 0;  // coded: differences per dense row
   // the cached exponents go to LDS now: the header read above already waits
   // for the bulk loads (loads complete in order), and patches overwrite them
   // after the next barrier
@@ -1693,26 +1880,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
     }
   }
   __syncthreads();
-  const uint32_t h_dtype = (s_hdr[1] >> 16) & 0xFFu, h_mode = s_hdr[1] >> 24;
-  const uint64_t h_n = s_hdr[4] | ((uint64_t)s_hdr[5] << 32);
+  const uint32_t h_mode = s_hdr[1] >> 24;
   const uint64_t P = s_hdr[6] | ((uint64_t)s_hdr[7] << 32);
   const uint64_t h_tot = s_hdr[8] | ((uint64_t)s_hdr[9] << 32);
-  const uint64_t h_off = s_hdr[10] | ((uint64_t)s_hdr[11] << 32);
-  uint32_t bad = 0;
-  if (s_hdr[0] != 0x52454943u || (s_hdr[1] & 0xFFFFu) != 1u) {
-    bad = CIERA_ST_MAGIC;
-  } else if (h_dtype != (uint32_t)DT || s_hdr[2] != B || h_n != n || h_off != off || s_hdr[12] != r ||
-             s_hdr[13] != world || h_mode > (CODED ? kCoded : kBlockVariant)) {
-    bad = CIERA_ST_FIELD;
-  } else if (h_mode == kCoded) {  // the chunk table gives the length; checked per chunk
-    const uint64_t dpos = ((kHeader + sm_sec<DT>(n) + nbm + 3) & ~3ull) + 8 * ((n + kSub - 1) / kSub);
-    if (P > n || h_tot > d.slot || (P ? h_tot < dpos : h_tot != kHeader + sm_sec<DT>(n))) bad = CIERA_ST_LENGTH;
-  } else {
-    const uint64_t want = h_mode == 0   ? kHeader + n * E
-                          : h_mode == 1 ? kHeader + sm_sec<DT>(n) + (P ? nbm + 5 * P : 0)
-                                        : kHeader + sm_sec<DT>(n) + (P ? nbm + P * B : 0);
-    if (P > (h_mode == 2 ? nb : n) || h_tot > d.slot || h_tot != want) bad = CIERA_ST_LENGTH;
-  }
+  const uint32_t bad = header_status<DT, CODED>(s_hdr, n, off, r, world, B, nb, nbm, d.slot);
   if (bad) {
     if (t_in == 0 && tid == 0) report(status_out, bad);
     return;  // uniform
@@ -1802,50 +1973,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
         if (tid * 32 < nbt) bm_got = bits_of(load_bits_w(bm, tb0 + tid * 32), min(32u, nbt - tid * 32));
         if (te == n && tid == 0 && (nb & 7u) != 0) bm_tail = gp(bm)[nbm - 1] >> (nb & 7u);
         uint32_t c[U], nbytes[U], start[U], len[U];
-        bool dense[U], coded[U];
+        bool dense[U], coded[U], recs[U];
         uint32_t e = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const uint64_t k = (uint64_t)t_in * U + (uint64_t)u;
           c[u] = nbytes[u] = start[u] = len[u] = 0;
-          dense[u] = coded[u] = false;
+          dense[u] = coded[u] = recs[u] = false;
           if (k >= nch) continue;
           const G1 uint32_t* ent = gp(reinterpret_cast<const uint32_t*>(st + tpos + 8 * k));
           const uint32_t cc = ent[0], cb = ent[1];
           const uint32_t pc = k > 0 ? ent[-2] : 0u, pb = k > 0 ? ent[-1] : 0u;
           len[u] = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
-          const uint32_t cu = cc - pc, bu = cb - pb;
-          bool badk = cc < pc || cb < pb || cb > D || cu > len[u] || (bu & 3u) != 0 || ((cu == 0) != (bu == 0)) ||
-                      (k == nch - 1 && (cc != P || cb != D));
-          if (!badk && cu > 0 && bu != pad4u(len[u]) && (bu < 4u * rans_lanes(cu) || bu > pad4u(len[u])))
-            badk = true;  // coded data holds its states and is shorter than the dense form
-          if (badk) {
+          if (!chunk_entry_ok(pc, pb, cc, cb, k, nch, len[u], D, P)) {
             e |= CIERA_ST_LENGTH;
             continue;
           }
-          c[u] = cu;
-          nbytes[u] = bu;
+          c[u] = cc - pc;
+          nbytes[u] = cb - pb;
           start[u] = pb;
-          dense[u] = cu > 0 && bu == pad4u(len[u]);
-          coded[u] = cu > 0 && !dense[u];
+          dense[u] = c[u] > 0 && nbytes[u] == pad4u(len[u]);
+          coded[u] = c[u] > 0 && !dense[u];
+          recs[u] = coded[u] && c[u] <= len[u] * E / 4;  // decoded ahead into the row's output region
         }
         if (tid == 0 && e) report(status_out, e);
-        if (tid < (uint32_t)U) s_sum[tid] = 0;  // differences per dense row (s_expbm is clear already)
-        __syncthreads();
         uint8_t* const s_exb = reinterpret_cast<uint8_t*>(s_ex);
-        auto mark = [&](uint32_t v) {  // value v of the tile was patched (the tile starts a block)
-          const uint32_t bb = v >> lb;
-          atomicOr(&s_expbm[bb >> 5], 1u << (bb & 31u));
-        };
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const uint32_t vo = (uint32_t)u * kDecRow + tid * kEPT;
-          const G1 uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st + dpos + start[u]));
-          if (coded[u] && tid * 4 < nbytes[u] / 4) {  // coded data to LDS, 16 bytes per thread
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (tid * 4 + (uint32_t)q < nbytes[u] / 4) s_win[u][tid * 4 + q] = src[tid * 4 + q];
-          }
           if (dense[u] && cnt[u] > 0) {  // this thread's 16 values of a dense row
             uint32_t dw[4];
             load_words<4>(st + dpos + start[u] + tid * kEPT, (uint32_t)cnt[u], false, dw);
@@ -1861,96 +2016,54 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
             v4u nv;
             nv.x = dw[0]; nv.y = dw[1]; nv.z = dw[2]; nv.w = dw[3];
             *reinterpret_cast<v4u*>(s_exb + vo) = nv;
-            if (diff) mark(vo);  // 16 values lie in one block (B >= 64)
+            if (diff) s_mark[u][(tid * kEPT) >> lb] = 1;  // 16 values lie in one block (B >= 64)
             if (wide) report(status_out, CIERA_ST_PATCH);
             atomicAdd(&s_sum[u], diff);
           }
-        }
-        __syncthreads();
-        if ((int)wave < U && coded[wave]) {  // uniform per wave
-          const uint32_t u = wave, cu = c[u], Lr = rans_lanes(cu);
-          const uint32_t navail = (nbytes[u] - 4u * Lr) / 2u;
-          const uint16_t* words = reinterpret_cast<const uint16_t*>(&s_win[u][Lr]);
-          uint32_t gf, gcum;
-          gap_table(cu, len[u], gf, gcum);
-          // bucket starts 1..12, the same in every lane (scalar registers)
-          uint32_t cum[13];
-#pragma unroll
-          for (int i = 1; i < 13; ++i) cum[i] = __builtin_amdgcn_readlane(gcum, i);
-          uint32_t x = lane < Lr ? s_win[u][lane] : kRansLow;
-          uint32_t ptr = 0, run = 0, err = 0;
-          auto renorm = [&]() {
-            const bool need = lane < Lr && x < kRansLow;
-            const uint64_t m = __ballot(need);
-            if (need) {
-              const uint32_t pos = ptr + lanes_below(m);
-              uint32_t w = 0;
-              if (pos < navail) w = words[pos];
-              else err |= CIERA_ST_PATCH;
-              x = (x << 16) | w;
-            }
-            ptr += (uint32_t)__popcll(m);
-          };
-          uint8_t* const rowex = s_exb + u * kDecRow;
-          const uint32_t steps = (cu + Lr - 1u) / Lr;
-          for (uint32_t t = 0; t < steps; ++t) {  // uniform
-            const bool act = lane < Lr && t * Lr + lane < cu;
-            // bucket: the last start <= slot (cb), the next one (nb), their count (bk)
-            uint32_t slot = x & 4095u, bk = 1, cb = 0, nb = 4096u;
-#pragma unroll
-            for (int i = 1; i < 13; ++i) {
-              const bool le = cum[i] <= slot;
-              bk += le ? 1u : 0u;
-              cb = le ? cum[i] : cb;
-            }
-#pragma unroll
-            for (int i = 12; i > 0; --i) nb = cum[i] > slot ? cum[i] : nb;
-            const uint32_t fb = nb - cb;
-            if (act) x = fb * (x >> 12) + slot - cb;
-            renorm();
-            uint32_t g1 = 1;
-            if (act) {
-              const uint32_t kb = bk - 1u;
-              g1 = (1u << kb) | (x & ((1u << kb) - 1u));
-              x >>= kb;
-            }
-            renorm();
-            slot = x & 4095u;
-            const uint32_t cls = class_of_slot(slot);
-            if (act) x = class_freq(cls) * (x >> 12) + slot - class_start(cls);
-            renorm();
-            uint32_t esc = 0;
-            if (act && cls == 14u) {
-              esc = x & 0xFFu;
-              x >>= 8;
-            }
-            renorm();
-            uint32_t incl = act ? g1 : 0u;  // indices: running sum of gap + 1 in change order
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-              const uint32_t tt = __shfl_up(incl, o);
-              if (lane >= (uint32_t)o) incl += tt;
-            }
-            const uint32_t idx = run + incl - 1u;
-            run += __shfl(incl, 63);
-            if (act) {
-              if (idx >= len[u]) {
+          if (recs[u]) {  // the row's changes, as the prepass left them, applied by every thread
+            const G1 uint16_t* rec = gp(reinterpret_cast<const uint16_t*>(out + ((uint64_t)t_in * T + u * kDecRow) * E));
+            uint32_t err = 0;
+            for (uint32_t j = tid; j < c[u]; j += kDecThreads) {
+              const uint32_t v = rec[2 * j] | ((uint32_t)rec[2 * j + 1] << 16);
+              if (v == 0xFFFFFFFFu) continue;  // a change past the chunk (reported by the prepass)
+              const uint32_t idx = v & 0xFFFu, cls = (v >> 12) & 0xFu, esc = (v >> 16) & 0xFFu;
+              uint8_t* const rowex = s_exb + u * kDecRow;
+              const uint32_t nv = cls == 14u ? esc : (rowex[idx] + class_step(cls)) & 0xFFu;
+              if (nv > Tr<DT>::EMASK) {
                 err |= CIERA_ST_PATCH;
               } else {
-                const uint32_t nv = cls == 14u ? esc : (rowex[idx] + class_step(cls)) & 0xFFu;
-                if (nv > Tr<DT>::EMASK) {
-                  err |= CIERA_ST_PATCH;
-                } else {
-                  rowex[idx] = (uint8_t)nv;
-                  s_mark[u][idx >> lb] = 1;  // plain stores: lanes hitting one block write the same value
-                }
+                rowex[idx] = (uint8_t)nv;
+                s_mark[u][idx >> lb] = 1;
               }
             }
+            if (err) report(status_out, err);
+          } else if (coded[u] && tid * 16 < nbytes[u]) {  // coded data the merge decodes itself, to LDS
+            const G1 uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st + dpos + start[u]));
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (tid * 4 + (uint32_t)q < nbytes[u] / 4) s_win[u][tid * 4 + q] = src[tid * 4 + q];
           }
-          if (ptr + (ptr & 1u) != navail || (lane < Lr && x != kRansLow)) err |= CIERA_ST_PATCH;
+        }
+        __syncthreads();
+        if ((int)wave < U && coded[wave] && !recs[wave]) {  // uniform per wave: wave u decodes row u
+          const uint32_t u = wave;
+          uint8_t* const rowex = s_exb + u * kDecRow;
+          const uint32_t err = rans_decode_wave(&s_win[u][0], nbytes[u], c[u], len[u],
+                                                [&](uint32_t, uint32_t idx, uint32_t cls, uint32_t esc,
+                                                    bool ok) -> uint32_t {
+            if (!ok) return 0u;
+            const uint32_t nv = cls == 14u ? esc : (rowex[idx] + class_step(cls)) & 0xFFu;
+            if (nv > Tr<DT>::EMASK) return CIERA_ST_PATCH;
+            rowex[idx] = (uint8_t)nv;
+            s_mark[u][idx >> lb] = 1;  // plain stores: lanes hitting one block write the same value
+            return 0u;
+          });
           if (err) report(status_out, err);
-          // the row's patched blocks (at most 64: B >= 64) into the tile's bits
-          const uint32_t nbr = (uint32_t)kSub >> lb, rb0 = u * nbr;  // blocks per row; the row's first
+        }
+        __syncthreads();
+        if ((int)wave < U && (dense[wave] || coded[wave])) {  // the row's patched blocks into the tile's bits
+          const uint32_t u = wave;
+          const uint32_t nbr = (uint32_t)kSub >> lb, rb0 = u * nbr;  // blocks per row (<= 64); the row's first
           const uint64_t rowbm = __ballot(lane < nbr && s_mark[u][lane] != 0);
           if (lane == 0 && rowbm) {
             if (nbr >= 32u) {  // whole words
@@ -2321,14 +2434,18 @@ static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem
                                      hipStream_t s) {
   (void)hipGetLastError();
   const dim3 grid(nitems * tpr * world), block(kDecThreads);
-#define CIERA_DEC(DT, U)                                                                                   \
-  do {                                                                                                     \
-    if (coded)                                                                                             \
-      hipLaunchKernelGGL((decode_kernel<DT, U, true>), grid, block, 0, s, items, item0, tpr, world, status, \
-                         batch_id);                                                                        \
-    else                                                                                                   \
-      hipLaunchKernelGGL((decode_kernel<DT, U, false>), grid, block, 0, s, items, item0, tpr, world,       \
-                         status, batch_id);                                                                \
+  const dim3 pgrid(nitems * tpr * world * (uint32_t)u);  // coded prepass: one workgroup per chunk slot
+#define CIERA_DEC(DT, U)                                                                                    \
+  do {                                                                                                      \
+    if (coded) {                                                                                            \
+      hipLaunchKernelGGL((coded_prepass_kernel<DT, U>), pgrid, dim3(64), 0, s, items, item0, tpr, world, status, \
+                         batch_id);                                                                         \
+      hipLaunchKernelGGL((decode_kernel<DT, U, true>), grid, block, 0, s, items, item0, tpr, world, status,  \
+                         batch_id);                                                                         \
+    } else {                                                                                                \
+      hipLaunchKernelGGL((decode_kernel<DT, U, false>), grid, block, 0, s, items, item0, tpr, world,        \
+                         status, batch_id);                                                                 \
+    }                                                                                                       \
   } while (0)
   if (dtype == 1) {
     switch (u) {
