@@ -812,42 +812,43 @@ __device__ __forceinline__ uint32_t coded_bytes(uint32_t c, uint32_t words, bool
 }
 
 // Gap-bucket frequencies (sum 2^12) for c changes among len values; lane i < 13
-// gets bucket i+1's frequency f and start cum.  q = 1 - c/len in 32-bit fixed
-// point; S_i = q^(2^i - 1) by repeated squaring (S_1 = q, S_{i+1} = S_i *
-// q^(2^i) and q^(2^(i+1)) = (q^(2^i))^2, each product's high 32 bits); bucket
-// b takes S_{b-1} - S_b (the last, S_12) as a share of 2^12, at least 1; the
-// largest, first of equals, absorbs the rounding.  Wave-wide.
+// of each group of GS lanes gets bucket i+1's frequency f and start cum (each
+// group may hold its own c and len).  q = 1 - c/len in 32-bit fixed point;
+// S_i = q^(2^i - 1) by repeated squaring (S_1 = q, S_{i+1} = S_i * q^(2^i)
+// and q^(2^(i+1)) = (q^(2^i))^2, each product's high 32 bits); bucket b takes
+// S_{b-1} - S_b (the last, S_12) as a share of 2^12, at least 1; the largest,
+// first of equals, absorbs the rounding.  Wave-wide.
+template <int GS = 64>
 __device__ __forceinline__ void gap_table(uint32_t c, uint32_t len, uint32_t& f, uint32_t& cum) {
-  const uint32_t lane = lane_id();
-  const uint32_t i = min(lane, 12u);
+  const uint32_t lane = lane_id(), gl = lane & (GS - 1u);
+  const uint32_t i = min(gl, 12u);
   // q < 2^32 as c >= 1 (a whole chunk, len = 2^12, needs no division)
   const uint32_t q = len == (uint32_t)kSub ? (len - c) << 20 : (uint32_t)(((uint64_t)(len - c) << 32) / len);
-  // lane i: S_i (S_0 = 2^32, kept as 0 with the flag `one`) and S_{i+1}
-  uint32_t Q = q, S = q;  // S_1, q^(2^1) below
+  uint32_t Q = q, S = q;  // S_1 and q^(2^0); lane i advances to S_i and q^(2^(i-1))
   for (uint32_t k = 1; k < i; ++k) {
     Q = __umulhi(Q, Q);
     S = __umulhi(S, Q);
   }
-  // now S = S_i for i >= 1; the next factor is q^(2^i)
-  const uint32_t Qn = i >= 1 ? __umulhi(Q, Q) : q;
+  const uint32_t Qn = i >= 1 ? __umulhi(Q, Q) : q;  // q^(2^i)
   uint64_t share;
   if (i == 0) share = (1ull << 32) - q;                      // S_0 - S_1
   else if (i < 12u) share = (uint64_t)S - __umulhi(S, Qn);  // S_i - S_{i+1}
   else share = S;                                            // S_12
-  uint32_t fv = lane < 13u ? max(1u, (uint32_t)(share >> 20)) : 0u;
+  uint32_t fv = gl < 13u ? max(1u, (uint32_t)(share >> 20)) : 0u;
   uint32_t tot = fv, mx = fv;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    tot += __shfl_xor(tot, o);
-    mx = max(mx, __shfl_xor(mx, o));
+  for (int o = GS / 2; o > 0; o >>= 1) {
+    tot += __shfl_xor(tot, o, GS);
+    mx = max(mx, __shfl_xor(mx, o, GS));
   }
-  const uint64_t tops = __ballot(lane < 13u && fv == mx);
-  if (lane == (uint32_t)__ffsll((unsigned long long)tops) - 1u) fv = fv + 4096u - tot;
+  const uint64_t tops = __ballot(gl < 13u && fv == mx);
+  const uint64_t mine = GS == 64 ? tops : (tops >> (lane - gl)) & ((1ull << (GS & 63)) - 1ull);
+  if (gl == (uint32_t)__ffsll((unsigned long long)mine) - 1u) fv = fv + 4096u - tot;
   uint32_t incl = fv;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o);
-    if (lane >= (uint32_t)o) incl += t;
+  for (int o = 1; o < GS; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o, GS);
+    if (gl >= (uint32_t)o) incl += t;
   }
   f = fv;
   cum = incl - fv;
@@ -1746,60 +1747,187 @@ __device__ __forceinline__ uint32_t rans_decode_wave(const uint32_t* win, uint32
   return err;
 }
 
-// Coded rows decoded ahead of the merge: one 64-thread workgroup per chunk
-// slot of the decode grid (U rows per decode tile), so that many resident
-// waves hide the decoder's dependent steps.  A chunk whose header and table
-// entry are valid, whose data is coded, and whose changes fit the first bytes
-// of its own output region (4 per change: offset | step class << 12 |
-// escaped exponent << 16, all ones for a change past the chunk, as two 16-bit
-// stores) leaves them there; the merge reads them before it writes the
-// values.  Other chunks are left to the merge.
+// rans_decode_wave for 64/GS chunks at once, one per group of GS lanes: each
+// lane passes its group's chunk (win, nbytes, c, len; c = 0 for a group
+// without one) and emit(j, idx, cls, esc, ok) is called for the group's
+// changes.  The bucket starts are per group, held in every lane.  Returns the
+// lane's status bits, as rans_decode_wave.
+template <int GS, class Emit>
+__device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint32_t nbytes, uint32_t c,
+                                                       uint32_t len, Emit&& emit) {
+  const uint32_t lane = lane_id(), gl = lane & (GS - 1u), g0 = lane - gl;
+  const uint64_t gmask = GS == 64 ? ~0ull : ((1ull << (GS & 63)) - 1ull) << g0;
+  const bool live = c > 0;
+  const uint32_t Lr = live ? rans_lanes(c) : 0u;
+  const uint32_t navail = live ? (nbytes - 4u * Lr) / 2u : 0u;
+  const uint16_t* words = reinterpret_cast<const uint16_t*>(win + Lr);
+  uint32_t gf, gcum;
+  gap_table<GS>(live ? c : 1u, live ? len : (uint32_t)kSub, gf, gcum);
+  uint32_t cum[13];
+  cum[0] = 0;
+#pragma unroll
+  for (int i = 1; i < 13; ++i) cum[i] = __shfl(gcum, i, GS);
+  uint32_t x = gl < Lr ? win[gl] : kRansLow;
+  uint32_t ptr = 0, run = 0, err = 0;
+  auto renorm = [&]() {
+    const bool need = gl < Lr && x < kRansLow;
+    const uint64_t m = __ballot(need) & gmask;
+    if (need) {
+      const uint32_t pos = ptr + lanes_below(m);
+      uint32_t w = 0;
+      if (pos < navail) w = words[pos];
+      else err |= CIERA_ST_PATCH;
+      x = (x << 16) | w;
+    }
+    ptr += (uint32_t)__popcll(m);
+  };
+  uint32_t steps = Lr ? (c + Lr - 1u) / Lr : 0u;  // the most rounds of any group
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) steps = max(steps, (uint32_t)__shfl_xor(steps, o));
+  for (uint32_t t = 0; t < steps; ++t) {  // uniform
+    const uint32_t j = t * Lr + gl;
+    const bool act = gl < Lr && j < c;
+    uint32_t slot = x & 4095u, bk = 1, cb = 0, nb = 4096u;
+#pragma unroll
+    for (int i = 1; i < 13; ++i) {
+      const bool le = cum[i] <= slot;
+      bk += le ? 1u : 0u;
+      cb = le ? cum[i] : cb;
+    }
+#pragma unroll
+    for (int i = 12; i > 0; --i) nb = cum[i] > slot ? cum[i] : nb;
+    if (act) x = (nb - cb) * (x >> 12) + slot - cb;
+    renorm();
+    uint32_t g1 = 1;
+    if (act) {
+      const uint32_t kb = bk - 1u;
+      g1 = (1u << kb) | (x & ((1u << kb) - 1u));
+      x >>= kb;
+    }
+    renorm();
+    slot = x & 4095u;
+    const uint32_t cls = class_of_slot(slot);
+    if (act) x = class_freq(cls) * (x >> 12) + slot - class_start(cls);
+    renorm();
+    uint32_t esc = 0;
+    if (act && cls == 14u) {
+      esc = x & 0xFFu;
+      x >>= 8;
+    }
+    renorm();
+    uint32_t incl = act ? g1 : 0u;
+#pragma unroll
+    for (int o = 1; o < GS; o <<= 1) {
+      const uint32_t tt = __shfl_up(incl, o, GS);
+      if (gl >= (uint32_t)o) incl += tt;
+    }
+    const uint32_t idx = run + incl - 1u;
+    run += __shfl(incl, GS - 1, GS);
+    if (act) {
+      const bool ok = idx < len;
+      if (!ok) err |= CIERA_ST_PATCH;
+      err |= emit(j, idx, cls, esc, ok);
+    }
+  }
+  if (live && (ptr + (ptr & 1u) != navail || (gl < Lr && x != kRansLow))) err |= CIERA_ST_PATCH;
+  return err;
+}
+
+// Coded rows decoded ahead of the merge, so that many resident waves hide the
+// decoder's dependent steps.  One wave per four consecutive chunk slots of a
+// rank's stream (U rows per decode tile): when each of the four chunks is small
+// (at most 64 changes and 1 KB of data) it decodes all four at once, 16 lanes
+// each; otherwise it decodes them one after another with all its lanes.  A chunk whose header and table entry are valid, whose data is
+// coded and whose changes fit the first bytes of its own output region (4 per
+// change: offset | step class << 12 | escaped exponent << 16, all ones for a
+// change past the chunk, as two 16-bit stores) leaves them there; the merge
+// reads them before it writes the values.  Other chunks are left to the merge.
+constexpr uint32_t kPackMax = 64;        // changes of a chunk decoded in a 16-lane group
+constexpr uint32_t kPackBytes = 1024;    // its data, at most
 template <int DT, int U>
 __global__ __launch_bounds__(64) void coded_prepass_kernel(const DecItem* __restrict__ items, uint32_t item0,
-                                                           uint32_t tpr, uint32_t world, uint32_t* status_out,
-                                                           uint32_t batch_id) {
+                                                            uint32_t tpr, uint32_t world, uint32_t* status_out,
+                                                            uint32_t batch_id) {
   constexpr int E = Tr<DT>::E;
   __shared__ uint32_t s_h[16];
-  __shared__ uint32_t s_w[kSub / 4];
-  const uint32_t lane = threadIdx.x;
-  const uint32_t cpr = tpr * U, cpi = cpr * world;  // chunk slots per rank and per item
-  const uint32_t blk = blockIdx.x / cpi;
-  const uint32_t rel = blockIdx.x - blk * cpi;
-  const uint32_t r = rel / cpr;
-  const uint64_t k = rel - r * cpr;
+  __shared__ uint32_t s_c[4][4];           // per chunk: changes (0 unless decoded here), bytes, start, length
+  __shared__ uint32_t s_w[kSub / 4];       // chunk data: one chunk's, or four of 1 KB each
+  const uint32_t tid = threadIdx.x, lane = lane_id();
+  const uint32_t cpr = tpr * U, qpr = (cpr + 3) / 4, qpi = qpr * world;  // chunk slots, quads
+  const uint32_t blk = blockIdx.x / qpi;
+  const uint32_t rel = blockIdx.x - blk * qpi;
+  const uint32_t r = rel / qpr;
+  const uint64_t k0 = 4ull * (rel - r * qpr);
   const DecItem d = items[item0 + blk];
   if (d.batch_id != batch_id) return;  // uniform
   const uint64_t off = ((uint64_t)r * d.q + min<uint64_t>(r, d.rem)) * d.cols;
   const uint64_t n = (d.q + (r < d.rem ? 1u : 0u)) * d.cols;
   const uint64_t nch = (n + kSub - 1) / kSub;
-  if (k >= nch) return;
+  if (k0 >= nch) return;
   const uint8_t* st = d.streams + (uint64_t)r * d.slot;
   const uint32_t B = d.block_size;
   const uint32_t lb = (uint32_t)__ffs(B) - 1u;
   const uint64_t nb = (n + B - 1) >> lb, nbm = (nb + 7) / 8;
-  if (lane < 16) s_h[lane] = gp(reinterpret_cast<const uint32_t*>(st))[lane];
+  if (tid < 16) s_h[tid] = gp(reinterpret_cast<const uint32_t*>(st))[tid];
   __syncthreads();
   if (header_status<DT, true>(s_h, n, off, r, world, B, nb, nbm, d.slot)) return;  // the merge reports it
   const uint64_t P = s_h[6] | ((uint64_t)s_h[7] << 32), h_tot = s_h[8] | ((uint64_t)s_h[9] << 32);
   if ((s_h[1] >> 24) != kCoded || P == 0) return;
   const uint64_t tpos = (kHeader + sm_sec<DT>(n) + nbm + 3) & ~3ull, dpos = tpos + 8 * nch;
-  const G1 uint32_t* e = gp(reinterpret_cast<const uint32_t*>(st + tpos + 8 * k));
-  const uint32_t cc = e[0], cb = e[1], pc = k > 0 ? e[-2] : 0u, pb = k > 0 ? e[-1] : 0u;
-  const uint32_t len = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
-  if (!chunk_entry_ok(pc, pb, cc, cb, k, nch, len, h_tot - dpos, P)) return;
-  const uint32_t c = cc - pc, bytes = cb - pb;
-  if (c == 0 || bytes == pad4u(len) || c > len * E / 4) return;  // nothing, dense, or records do not fit
-  const G1 uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st + dpos + pb));
-  for (uint32_t w = lane; w < bytes / 4; w += 64) s_w[w] = src[w];
+  if (tid < 4u) {  // chunk k0 + tid's entry, checked; c stays 0 unless it is decoded here
+    uint32_t c = 0, bytes = 0, pb = 0, len = 0;
+    const uint64_t k = k0 + tid;
+    if (k < nch) {
+      const G1 uint32_t* e = gp(reinterpret_cast<const uint32_t*>(st + tpos + 8 * k));
+      const uint32_t cc = e[0], cb = e[1], pc = k > 0 ? e[-2] : 0u;
+      pb = k > 0 ? e[-1] : 0u;
+      len = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
+      if (chunk_entry_ok(pc, pb, cc, cb, k, nch, len, h_tot - dpos, P) && cc > pc && cb - pb != pad4u(len) &&
+          cc - pc <= len * E / 4) {  // coded, and its records fit
+        c = cc - pc;
+        bytes = cb - pb;
+      }
+    }
+    s_c[tid][0] = c; s_c[tid][1] = bytes; s_c[tid][2] = pb; s_c[tid][3] = len;
+  }
   __syncthreads();
-  G1 uint16_t* rec = gp(reinterpret_cast<uint16_t*>(d.out + (off + k * kSub) * E));
-  const uint32_t err = rans_decode_wave(s_w, bytes, c, len, [rec](uint32_t j, uint32_t idx, uint32_t cls, uint32_t esc,
-                                                                   bool ok) -> uint32_t {
-    const uint32_t v = ok ? idx | (cls << 12) | (esc << 16) : 0xFFFFFFFFu;
-    rec[2 * j] = (uint16_t)v;
-    rec[2 * j + 1] = (uint16_t)(v >> 16);
-    return 0u;
-  });
+  bool any = false, packed = true;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    any |= s_c[g][0] > 0;
+    packed &= s_c[g][0] <= kPackMax && s_c[g][1] <= kPackBytes;
+  }
+  if (!any) return;
+  const G1 uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st + dpos));
+  auto decode_one = [&](uint32_t g, auto gs) -> uint32_t {
+    constexpr int GS = decltype(gs)::value;
+    const uint32_t cg = s_c[g][0], bg = s_c[g][1], pg = s_c[g][2], lg = s_c[g][3];
+    uint32_t* const win = &s_w[GS == 16 ? g * (kPackBytes / 4) : 0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the window's last reader is done
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (cg) {  // only a chunk decoded here is read
+      for (uint32_t w = lane & (GS - 1u); w < bg / 4; w += GS) win[w] = src[pg / 4 + w];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // the lanes read each other's words
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    G1 uint16_t* rec = gp(reinterpret_cast<uint16_t*>(d.out + (off + (k0 + g) * kSub) * E));
+    auto emit = [rec](uint32_t j, uint32_t idx, uint32_t cls, uint32_t esc, bool ok) -> uint32_t {
+      const uint32_t v = ok ? idx | (cls << 12) | (esc << 16) : 0xFFFFFFFFu;
+      rec[2 * j] = (uint16_t)v;
+      rec[2 * j + 1] = (uint16_t)(v >> 16);
+      return 0u;
+    };
+    return rans_decode_groups<GS>(win, bg, cg, lg, emit);
+  };
+  uint32_t err = 0;
+  if (packed) {  // four small chunks at once, 16 lanes each
+    err = decode_one(lane >> 4, std::integral_constant<int, 16>{});
+  } else {  // one after another, with all lanes
+    for (uint32_t g = 0; g < 4; ++g)
+      if (s_c[g][0]) err |= decode_one(g, std::integral_constant<int, 64>{});  // uniform
+  }
   if (err) report(status_out, err);
 }
 
@@ -2434,7 +2562,7 @@ static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem
                                      hipStream_t s) {
   (void)hipGetLastError();
   const dim3 grid(nitems * tpr * world), block(kDecThreads);
-  const dim3 pgrid(nitems * tpr * world * (uint32_t)u);  // coded prepass: one workgroup per chunk slot
+  const dim3 pgrid(nitems * world * ((tpr * (uint32_t)u + 3) / 4));  // coded prepass: four chunk slots each
 #define CIERA_DEC(DT, U)                                                                                    \
   do {                                                                                                      \
     if (coded) {                                                                                            \
