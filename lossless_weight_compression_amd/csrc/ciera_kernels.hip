@@ -1752,9 +1752,9 @@ __device__ __forceinline__ uint32_t rans_decode_wave(const uint32_t* win, uint32
 // without one) and emit(j, idx, cls, esc, ok) is called for the group's
 // changes.  The bucket starts are per group, held in every lane.  Returns the
 // lane's status bits, as rans_decode_wave.
-template <int GS, class Emit>
+template <int GS, bool LSEARCH, class Emit>
 __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint32_t nbytes, uint32_t c,
-                                                       uint32_t len, Emit&& emit) {
+                                                       uint32_t len, uint32_t* lcum, Emit&& emit) {
   const uint32_t lane = lane_id(), gl = lane & (GS - 1u), g0 = lane - gl;
   const uint64_t gmask = GS == 64 ? ~0ull : ((1ull << (GS & 63)) - 1ull) << g0;
   const bool live = c > 0;
@@ -1764,9 +1764,17 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
   uint32_t gf, gcum;
   gap_table<GS>(live ? c : 1u, live ? len : (uint32_t)kSub, gf, gcum);
   uint32_t cum[13];
-  cum[0] = 0;
+  uint32_t* const gc = lcum + (g0 / GS) * 16u;  // LSEARCH: the group's starts, then 4096 up to 16 entries
+  if constexpr (LSEARCH) {
+    if (gl < 16u) gc[gl] = gl < 13u ? gcum : 4096u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    cum[0] = 0;
 #pragma unroll
-  for (int i = 1; i < 13; ++i) cum[i] = __shfl(gcum, i, GS);
+    for (int i = 1; i < 13; ++i) cum[i] = __shfl(gcum, i, GS);
+  }
   uint32_t x = gl < Lr ? win[gl] : kRansLow;
   uint32_t ptr = 0, run = 0, err = 0;
   auto renorm = [&]() {
@@ -1788,14 +1796,27 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
     const uint32_t j = t * Lr + gl;
     const bool act = gl < Lr && j < c;
     uint32_t slot = x & 4095u, bk = 1, cb = 0, nb = 4096u;
+    if constexpr (LSEARCH) {  // the last start <= slot: four halving steps over 16 entries
+      uint32_t lo = 0;
 #pragma unroll
-    for (int i = 1; i < 13; ++i) {
-      const bool le = cum[i] <= slot;
-      bk += le ? 1u : 0u;
-      cb = le ? cum[i] : cb;
+      for (uint32_t st = 8; st > 0; st >>= 1) {
+        const uint32_t v = gc[lo + st];
+        const bool le = v <= slot;
+        lo = le ? lo + st : lo;
+        cb = le ? v : cb;
+      }
+      bk = lo + 1u;
+      nb = gc[lo + 1u];
+    } else {
+#pragma unroll
+      for (int i = 1; i < 13; ++i) {
+        const bool le = cum[i] <= slot;
+        bk += le ? 1u : 0u;
+        cb = le ? cum[i] : cb;
+      }
+#pragma unroll
+      for (int i = 12; i > 0; --i) nb = cum[i] > slot ? cum[i] : nb;
     }
-#pragma unroll
-    for (int i = 12; i > 0; --i) nb = cum[i] > slot ? cum[i] : nb;
     if (act) x = (nb - cb) * (x >> 12) + slot - cb;
     renorm();
     uint32_t g1 = 1;
@@ -1842,6 +1863,8 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
 // change: offset | step class << 12 | escaped exponent << 16, all ones for a
 // change past the chunk, as two 16-bit stores) leaves them there; the merge
 // reads them before it writes the values.  Other chunks are left to the merge.
+template <int GS>
+constexpr bool kLsearch = true;          // gap buckets by a search over starts in LDS
 constexpr uint32_t kPackMax = 64;        // changes of a chunk decoded in a 16-lane group
 constexpr uint32_t kPackBytes = 1024;    // its data, at most
 template <int DT, int U>
@@ -1852,6 +1875,7 @@ __global__ __launch_bounds__(64) void coded_prepass_kernel(const DecItem* __rest
   __shared__ uint32_t s_h[16];
   __shared__ uint32_t s_c[4][4];           // per chunk: changes (0 unless decoded here), bytes, start, length
   __shared__ uint32_t s_w[kSub / 4];       // chunk data: one chunk's, or four of 1 KB each
+  __shared__ uint32_t s_lc[64];            // gap-bucket starts, 16 entries per chunk decoded at once
   const uint32_t tid = threadIdx.x, lane = lane_id();
   const uint32_t cpr = tpr * U, qpr = (cpr + 3) / 4, qpi = qpr * world;  // chunk slots, quads
   const uint32_t blk = blockIdx.x / qpi;
@@ -1919,7 +1943,7 @@ __global__ __launch_bounds__(64) void coded_prepass_kernel(const DecItem* __rest
       rec[2 * j + 1] = (uint16_t)(v >> 16);
       return 0u;
     };
-    return rans_decode_groups<GS>(win, bg, cg, lg, emit);
+    return rans_decode_groups<GS, kLsearch<GS>>(win, bg, cg, lg, s_lc, emit);
   };
   uint32_t err = 0;
   if (packed) {  // four small chunks at once, 16 lanes each

@@ -97,6 +97,38 @@ def test_exact_1024_and_1025_changes_per_chunk():
     assert g == 0 and o == 0
 
 
+# Changes per 4096-value chunk of one shard, around the decoder's grouping of
+# four consecutive chunks: quads whose chunks all hold at most 64 changes are
+# decoded together, 16 lanes per chunk; any other quad one chunk at a time.
+QUAD_COUNTS = [64, 1, 0, 64,      # packed, two chunks at the limit
+               65, 2, 3, 0,       # one chunk past it
+               0, 0, 0, 0,        # nothing to decode
+               1024, 5, 64, 0,    # the most a coded chunk holds, beside small ones
+               7, 0, 300]         # a quad cut short by the end of the shard
+
+
+@pytest.mark.parametrize("dtype,world", [(torch.bfloat16, 1), (torch.bfloat16, 2), (torch.float32, 1),
+                                         (torch.float16, 2)])
+def test_chunk_quads_at_the_packing_limit(dtype, world):
+    """Exact change counts per chunk at and past 64 in every quad position,
+    empty quads, a full 1024-change chunk and a ragged last quad; escapes
+    included.  Each rank's shard holds the same count pattern."""
+    nch = len(QUAD_COUNTS)
+    rows = nch * world
+    spec = W.TensorSpec("q", rows, 4096)
+    w0 = W.base_weights(spec, W.tensor_seed("quads", str(dtype), world), dtype)
+    rng = np.random.default_rng(world * 7 + rows)
+    m = torch.zeros(rows * 4096, dtype=torch.bool)
+    for r in range(world):
+        for k, c in enumerate(QUAD_COUNTS):
+            base = (r * nch + k) * 4096
+            m[base + torch.from_numpy(rng.choice(4096, c, replace=False))] = True
+    w1 = exponent_steps(w0, m, [1, -1, 2, 100], W.tensor_seed("quads-p", str(dtype), world))
+    say(f"[gpu] coded quads {dtype} W={world}")
+    g, o = run_block([(rows, 4096)], dtype, world, 512, [w0], [w1], variant=[B.CODED])
+    assert g == 0 and o == 0
+
+
 @pytest.mark.parametrize("frac", [0.0, 0.001, 0.01, 0.1])
 def test_coded_olmoe_expert_mixed_with_other_modes(frac):
     """One OLMoE expert, 16 ranks, in one batch: gate coded, up with element
