@@ -1752,6 +1752,24 @@ __device__ __forceinline__ uint32_t rans_decode_wave(const uint32_t* win, uint32
 // without one) and emit(j, idx, cls, esc, ok) is called for the group's
 // changes.  The bucket starts are per group, held in every lane.  Returns the
 // lane's status bits, as rans_decode_wave.
+// Inclusive sum of v over each group of GS (16 or 64) lanes, in lane order,
+// with DPP row operations (a row is 16 lanes): shifts by 1, 2, 4 and 8 within
+// rows (lanes shifted in from outside the row read 0), then, for a whole wave,
+// the last lane of row 0 added to row 1 and of row 2 to row 3, and the last
+// lane of row 1 to rows 2 and 3.  Every lane must be active.
+template <int GS>
+__device__ __forceinline__ uint32_t group_incl_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  if constexpr (GS == 64) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  }
+  return v;
+}
+
 template <int GS, bool LSEARCH, class Emit>
 __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint32_t nbytes, uint32_t c,
                                                        uint32_t len, uint32_t* lcum, Emit&& emit) {
@@ -1836,14 +1854,9 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
       x >>= 8;
     }
     renorm();
-    uint32_t incl = act ? g1 : 0u;
-#pragma unroll
-    for (int o = 1; o < GS; o <<= 1) {
-      const uint32_t tt = __shfl_up(incl, o, GS);
-      if (gl >= (uint32_t)o) incl += tt;
-    }
+    const uint32_t incl = group_incl_sum<GS>(act ? g1 : 0u);
     const uint32_t idx = run + incl - 1u;
-    run += __shfl(incl, GS - 1, GS);
+    run += GS == 64 ? (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) : __shfl(incl, GS - 1, GS);
     if (act) {
       const bool ok = idx < len;
       if (!ok) err |= CIERA_ST_PATCH;
