@@ -253,9 +253,13 @@ ciera_status_t ciera_decode_scratch_bytes(const ciera_decode_item_t* items, uint
  * cache equal to the exponents of the rebuilt values.  RAW streams are copied
  * and refresh the cache too.  Validation sets CIERA_ST_* bits in *status_dev
  * (a device uint32_t the caller zeroed); a shard whose header or lengths are
- * bad is left untouched, a shard with bad patches or bitmap is rebuilt in an
- * unspecified way -- in no case is memory outside the item's buffers touched.
- * `items` is a host array.  Scratch as for encode. */
+ * bad is left untouched (CODED: a chunk whose table entry is bad), a shard
+ * with bad patches or bitmap is rebuilt in an unspecified way -- in no case is
+ * memory outside the item's buffers touched.  For a CODED stream the decode
+ * first writes each coded chunk's changes as 4-byte records at the start of
+ * that chunk's part of out_full, then overwrites them with the values.
+ * out_full must not overlap the streams or the cache.  `items` is a host
+ * array.  Scratch as for encode. */
 ciera_status_t ciera_decode(const ciera_decode_item_t* items, uint32_t count,
                             uint32_t* status_dev, void* scratch, uint64_t scratch_bytes,
                             void* stream);
