@@ -215,8 +215,9 @@ ciera_status_t ciera_encode_scratch_bytes(const ciera_encode_item_t* items, uint
  * ascending (index, exponent) patch list, or a RAW stream when the plan says so
  * or when the compressed stream would not be shorter.  Each stream's header
  * (total_len, n_changed, mode) is written on the device; the host is never
- * synchronized.  Bytes of a stream past its total_len are unspecified.
- * `items` is a host array.  Scratch: a device buffer of at least
+ * synchronized.  Bytes of a stream past its total_len are unspecified.  A
+ * stream's first 64 + n*e bytes must not overlap its shard or its cache slice
+ * (the hash cache for compress = 2): INVALID_ARG.  `items` is a host array.  Scratch: a device buffer of at least
  * ciera_encode_scratch_bytes, 256-byte aligned, used only until the call's
  * kernels complete.  Encode cannot fail on data: every bit pattern is valid. */
 ciera_status_t ciera_encode(const ciera_encode_item_t* items, uint32_t count, void* scratch,
@@ -258,8 +259,8 @@ ciera_status_t ciera_decode_scratch_bytes(const ciera_decode_item_t* items, uint
  * memory outside the item's buffers touched.  For a CODED stream the decode
  * first writes each coded chunk's changes as 4-byte records at the start of
  * that chunk's part of out_full, then overwrites them with the values.
- * out_full must not overlap the streams or the cache.  `items` is a host
- * array.  Scratch as for encode. */
+ * out_full, the cache and the W slots must not overlap: INVALID_ARG.
+ * `items` is a host array.  Scratch as for encode. */
 ciera_status_t ciera_decode(const ciera_decode_item_t* items, uint32_t count,
                             uint32_t* status_dev, void* scratch, uint64_t scratch_bytes,
                             void* stream);

@@ -34,6 +34,13 @@ uint32_t elem_bytes(uint32_t dt) { return dt == CIERA_FP32 ? 4u : 2u; }
 uint32_t sm_bits(uint32_t dt) { return dt == CIERA_BF16 ? 8u : dt == CIERA_FP32 ? 24u : 11u; }
 bool pow2(uint32_t x) { return x && !(x & (x - 1)); }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Whether the byte ranges [a, a + alen) and [b, b + blen) share a byte.
+bool overlap(const void* a, uint64_t alen, const void* b, uint64_t blen) {
+  if (alen == 0 || blen == 0) return false;
+  const unsigned __int128 a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + blen && b0 < a0 + alen;
+}
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 uint64_t bitmap_bytes(uint64_t n, uint32_t B) { return ((n + B - 1) / B + 7) / 8; }
 
@@ -387,6 +394,13 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     if (n && it.compress == kBlockVariant && !aligned(it.cache_full, 16)) return CIERA_ERR_INVALID_ARG;
     if (!it.stream || !aligned(it.stream, 16)) return CIERA_ERR_INVALID_ARG;
     if (it.stream_capacity < kHeader + n * elem_bytes(it.t.dtype)) return CIERA_ERR_BUFFER_TOO_SMALL;
+    // the stream written is disjoint from the shard and the cache slice read
+    const uint64_t wlen = kHeader + n * elem_bytes(it.t.dtype);
+    const uint64_t clen = it.compress == kBlockVariant ? (n + it.t.block_size - 1) / it.t.block_size * 16 : n;
+    const uint8_t* cptr = it.compress == kBlockVariant ? it.cache_full : it.cache_full + off;
+    if (overlap(it.stream, wlen, it.shard, n * elem_bytes(it.t.dtype)) ||
+        (it.cache_full && overlap(it.stream, wlen, cptr, clen)))
+      return CIERA_ERR_INVALID_ARG;
   }
   BatchImpl* b = impl(batch);
   b->batch_id = next_id();
@@ -524,6 +538,14 @@ ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t c
     if (it.slot_bytes % 16 != 0) return CIERA_ERR_INVALID_ARG;
     if (it.slot_bytes < kHeader + n0 * elem_bytes(it.t.dtype)) return CIERA_ERR_BUFFER_TOO_SMALL;
     if (it.t.rows * it.t.cols && (!it.out_full || !aligned(it.out_full, 16) || !it.cache_full))
+      return CIERA_ERR_INVALID_ARG;
+    // the rebuilt values, the cache and the streams are disjoint
+    const uint64_t N = it.t.rows * it.t.cols;
+    const unsigned __int128 sb = (unsigned __int128)it.slot_bytes * it.t.world;
+    const uint64_t slen = sb > (unsigned __int128)UINT64_MAX ? UINT64_MAX : (uint64_t)sb;
+    if (overlap(it.out_full, N * elem_bytes(it.t.dtype), it.cache_full, N) ||
+        overlap(it.out_full, N * elem_bytes(it.t.dtype), it.streams, slen) ||
+        overlap(it.cache_full, N, it.streams, slen))
       return CIERA_ERR_INVALID_ARG;
   }
   BatchImpl* b = impl(batch);

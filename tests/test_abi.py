@@ -143,6 +143,37 @@ def test_encode_decode_validation_without_device():
         L.ciera_decode([d], 0, 0x40000, need, stream=0)          # no status word
 
 
+def test_overlapping_buffers_are_rejected_without_device():
+    """Encode: the stream written must not overlap the shard or the cache
+    slice it reads; decode: the rebuilt values, the cache and the W slots are
+    disjoint.  Checked on the host before any device call (fake addresses)."""
+    t = L.Tensor(64, 64, 1, 512, 2)               # shards of 32x64 bf16: 4096 B; stream <= 4160 B
+    cap = 64 + 32 * 64 * 2
+
+    def enc(shard, cache_full, stream):
+        it = L.encode_item(t, 1, 1, shard, cache_full, stream, cap)
+        L.ciera_encode([it], 0x900000, L.ciera_encode_scratch_bytes([it]), stream=0)
+
+    for shard, cache, stream in [(0x10000, 0x20000, 0x10000 + 4096 - 16),   # stream ends in the shard
+                                 (0x10000 + 4096 - 16, 0x20000, 0x10000),   # shard starts in the stream
+                                 (0x10000, 0x30000 - 2048 - 16, 0x30000)]:  # rank 1's cache slice
+        with pytest.raises(L.CieraError) as e:
+            enc(shard, cache, stream)
+        assert e.value.code == 1, (hex(shard), hex(cache), hex(stream))
+    slot = cap + 16
+    d_ok = dict(streams=0x100000, out_full=0x200000, cache=0x300000)
+    bad = [dict(out_full=0x100000 + 2 * slot - 16),     # values start in the last slot
+           dict(cache=0x200000 + 2 * 4096 - 1),         # cache starts in the values' last byte
+           dict(cache=0x100000 - 4096 + 1),              # cache ends in the first slot
+           dict(out_full=0x300000 - 8192 + 16)]          # values end in the cache
+    for kw in bad:
+        a = dict(d_ok, **kw)
+        di = L.decode_item(t, a["streams"], slot, a["out_full"], a["cache"])
+        with pytest.raises(L.CieraError) as e:
+            L.ciera_decode([di], 0x800000, 0x900000, L.ciera_decode_scratch_bytes([di]), stream=0)
+        assert e.value.code == 1, kw
+
+
 def test_scratch_sizes_grow_with_work():
     t1 = L.Tensor(2048, 1024, 1, 512, 16)
     it = L.encode_item(t1, 0, 1, 0x10000, 0x20000, 0x30000, 1 << 30)
