@@ -805,6 +805,17 @@ constexpr uint32_t kRansLow = 1u << 16;
 __device__ __forceinline__ uint32_t pad4u(uint32_t v) { return (v + 3u) & ~3u; }
 __device__ __forceinline__ uint32_t rans_lanes(uint32_t c) { return min(64u, (c + 3u) / 4u); }
 
+// Length of the row starting at value r0 of a shard of n values (0 past it),
+// with n passed through an empty asm statement so that the compiler cannot
+// fold the result from what it assumed about full tiles: it once compiled a
+// dense first row of the last, partial tile with the full row length.
+__device__ __forceinline__ uint32_t row_len(uint64_t n, uint64_t r0) {
+  uint32_t lo = (uint32_t)n, hi = (uint32_t)(n >> 32);
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  const uint64_t m = lo | ((uint64_t)hi << 32);
+  return r0 < m ? (uint32_t)min<uint64_t>(kSub, m - r0) : 0u;
+}
+
 // Bytes of a chunk's data from its changes, words and form.
 __device__ __forceinline__ uint32_t coded_bytes(uint32_t c, uint32_t words, bool dense, uint32_t len) {
   if (c == 0) return 0;
@@ -1004,8 +1015,7 @@ __device__ void split_tile_coded(const EncItem& d, uint32_t local, const EncArgs
     __syncthreads();
     if ((int)wave < P2) {  // uniform per wave: wave r codes row s0 + r
       const int r = (int)wave;
-      const uint64_t r0 = base + (uint64_t)(s0 + r) * kSub;
-      const uint32_t len = r0 < n ? (uint32_t)min<uint64_t>(kSub, n - r0) : 0u;
+      const uint32_t len = row_len(n, base + (uint64_t)(s0 + r) * kSub);
       uint32_t words = 0;
       bool dense = c[r] > kChunkMaxChanges;
       if (c[r] > 0 && !dense) {  // measure, then write only coded data that is shorter than dense
@@ -1060,8 +1070,7 @@ __device__ void split_tile_coded(const EncItem& d, uint32_t local, const EncArgs
     uint32_t bytes = 0, chg = 0;
 #pragma unroll
     for (int r = 0; r < S; ++r) {
-      const uint64_t r0 = base + (uint64_t)r * kSub;
-      const uint32_t len = r0 < n ? (uint32_t)min<uint64_t>(kSub, n - r0) : 0u;
+      const uint32_t len = row_len(n, base + (uint64_t)r * kSub);
       const uint32_t w = s_info[r];
       bytes += coded_bytes(w & 0x1FFFu, (w >> 13) & 0x1FFFu, (w >> 26) & 1u, len);
       chg += w & 0x1FFFu;

@@ -129,6 +129,30 @@ def test_chunk_quads_at_the_packing_limit(dtype, world):
     assert g == 0 and o == 0
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("tail,tail_changes", [(1666, 1255), (1666, 600), (3000, 40), (2295, 1697)])
+def test_partial_first_row_of_last_tile(dtype, tail, tail_changes):
+    """A shard of six whole chunks and a partial one that opens the last
+    encode tile (tiles of two rows), with few changes elsewhere: the partial
+    chunk is dense by its count (more than 1024), or coded.  Its data length
+    counts toward the stream's total length (a dense partial first row was
+    once sized as a whole row)."""
+    world, nch = 2, 6
+    per = nch * 4096 + tail
+    spec = W.TensorSpec("t", per * world, 1)
+    w0 = W.base_weights(spec, W.tensor_seed("tail", str(dtype), tail, tail_changes), dtype)
+    rng = np.random.default_rng(tail + tail_changes)
+    m = torch.zeros(per * world, dtype=torch.bool)
+    for r in range(world):
+        for k in range(nch):
+            m[r * per + k * 4096 + torch.from_numpy(rng.choice(4096, 40, replace=False))] = True
+        m[r * per + nch * 4096 + torch.from_numpy(rng.choice(tail, tail_changes, replace=False))] = True
+    w1 = exponent_steps(w0, m, [1, -1], W.tensor_seed("tail-p", str(dtype), tail))
+    say(f"[gpu] coded partial first row {dtype} tail {tail} changes {tail_changes}")
+    g, o = run_block([(per * world, 1)], dtype, world, 512, [w0], [w1], variant=[B.CODED])
+    assert g == 0 and o == 0
+
+
 @pytest.mark.parametrize("frac", [0.0, 0.001, 0.01, 0.1])
 def test_coded_olmoe_expert_mixed_with_other_modes(frac):
     """One OLMoE expert, 16 ranks, in one batch: gate coded, up with element
