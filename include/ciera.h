@@ -97,7 +97,19 @@ typedef enum {
   CIERA_ERR_DEVICE = 4            /* a HIP runtime call failed */
 } ciera_status_t;
 
-/* Bits OR-ed into *status_dev by ciera_decode (the caller zeroes it first). */
+/* Bits OR-ed into *status_dev by ciera_decode (the caller zeroes it first).
+ * They are format validation, not an integrity check: they flag a stream that
+ * does not parse as a stream of its shard (so that its decode never reaches
+ * outside its buffers), not every edit of a well-formed one.  Edits that decode
+ * with status 0 and a different output include: any sign|mantissa byte; any
+ * byte of a RAW body; a patch record's exponent byte; a record's index moved
+ * within its block without passing a neighbour; BLOCK payload bytes; and in
+ * CODED data, bits of a coder state that the raw-bit symbols of a gap absorb
+ * (the low bits of a state at a change's first step pass through to its gap's
+ * raw bits and leave the state as before: every later change of the chunk
+ * moves by the same amount, and only a move across a block boundary or past
+ * the chunk is flagged).  Integrity in transit is the transport's; the pages'
+ * payload carries no checksum either. */
 #define CIERA_ST_MAGIC 1u  /* bad magic or version */
 #define CIERA_ST_FIELD 2u  /* dtype, B, n, offset, rank, world or mode mismatch */
 #define CIERA_ST_LENGTH 4u /* total_len / n_changed inconsistent or beyond the slot; CODED: a

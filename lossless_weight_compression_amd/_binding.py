@@ -128,13 +128,40 @@ def _check(code: int, where: str) -> None:
         raise CieraError(code, where)
 
 
-def _ptr(t) -> Optional[int]:
-    """Device address of a torch tensor (or an int address, or None)."""
+def _torch_dtype(ciera_dtype: int):
+    import torch
+    return {CIERA_BF16: torch.bfloat16, CIERA_FP32: torch.float32, CIERA_FP16: torch.float16}[ciera_dtype]
+
+
+def _ptr(t, what: str = "buffer", dtype=None, numel: Optional[int] = None,
+         min_numel: Optional[int] = None) -> Optional[int]:
+    """Device address of a torch tensor (or an int address, or None).  The
+    library reads and writes memory from that address on, so a torch tensor
+    must be contiguous, of the element type and count the call implies (where
+    it is given) and on a GPU; a strided view or a shard of another length
+    would otherwise be read as the wrong memory (ValueError)."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: not contiguous (shape {tuple(t.shape)}, stride {t.stride()})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what}: {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {min_numel} needed")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: on {t.device}, not on a GPU")
     return t.data_ptr()
+
+
+def _u8(t, what: str, min_numel: int) -> Optional[int]:
+    """A byte buffer (cache, stream, scratch, status) of at least min_numel bytes."""
+    if t is None or isinstance(t, int):
+        return t
+    return _ptr(t, what, min_numel=-(-min_numel // t.element_size()))
 
 
 def _stream(stream) -> Optional[int]:
@@ -205,11 +232,21 @@ def ciera_decode_scratch_bytes(items: Sequence[DecodeItem]) -> int:
 def encode_item(t: Tensor, rank: int, compress: int, shard, cache_full, stream_buf,
                 capacity: Optional[int] = None) -> EncodeItem:
     cap = capacity if capacity is not None else stream_buf.numel() * stream_buf.element_size()
-    return EncodeItem(t, rank, int(compress), _ptr(shard), _ptr(cache_full), _ptr(stream_buf), cap)
+    off, n = ciera_shard(t, rank)
+    state = (16 * (-(-n // t.block_size)) if compress == BLOCK else t.rows * t.cols)
+    return EncodeItem(t, rank, int(compress),
+                      _ptr(shard, "shard", None if isinstance(shard, int) else _torch_dtype(t.dtype), n),
+                      _u8(cache_full, "hash cache" if compress == BLOCK else "cache", state),
+                      _u8(stream_buf, "stream", 0), cap)
 
 
 def decode_item(t: Tensor, streams, slot_bytes: int, out_full, cache_full) -> DecodeItem:
-    return DecodeItem(t, _ptr(streams), slot_bytes, _ptr(out_full), _ptr(cache_full))
+    N = t.rows * t.cols
+    return DecodeItem(t, _u8(streams, "streams", slot_bytes * t.world),
+                      slot_bytes,
+                      _ptr(out_full, "out_full", None if out_full is None or isinstance(out_full, int)
+                           else _torch_dtype(t.dtype), N),
+                      _u8(cache_full, "cache", N))
 
 
 def ciera_encode(items: Sequence[EncodeItem], scratch, scratch_bytes: Optional[int] = None,
@@ -227,13 +264,18 @@ def ciera_decode(items: Sequence[DecodeItem], status, scratch, scratch_bytes: Op
 
 
 def ciera_cache_update(t: Tensor, weights_full, cache_full, stream=None) -> None:
-    _check(_lib.ciera_cache_update(byref(t), _ptr(weights_full), _ptr(cache_full), _stream(stream)),
+    N = t.rows * t.cols
+    w = _ptr(weights_full, "weights_full",
+             None if weights_full is None or isinstance(weights_full, int) else _torch_dtype(t.dtype), N)
+    _check(_lib.ciera_cache_update(byref(t), w, _u8(cache_full, "cache", N), _stream(stream)),
            "ciera_cache_update")
 
 
 def ciera_hash_update(t: Tensor, rank: int, shard, hash_cache, stream=None) -> None:
-    _check(_lib.ciera_hash_update(byref(t), rank, _ptr(shard), _ptr(hash_cache), _stream(stream)),
-           "ciera_hash_update")
+    off, n = ciera_shard(t, rank)
+    x = _ptr(shard, "shard", None if shard is None or isinstance(shard, int) else _torch_dtype(t.dtype), n)
+    _check(_lib.ciera_hash_update(byref(t), rank, x, _u8(hash_cache, "hash cache", 16 * (-(-n // t.block_size))),
+                                  _stream(stream)), "ciera_hash_update")
 
 
 def ciera_encode_prepare(items: Sequence[EncodeItem], scratch, scratch_bytes: Optional[int] = None,

@@ -136,8 +136,9 @@ class LayerCodec:
             a = self.stream_off[i] + rank * self.slot_bytes[i]
             state = (self.hash_cache(i, rank).data_ptr() if c == B.BLOCK
                      else self.cache.data_ptr() + self.cache_off[i])
-            items.append(B.EncodeItem(t, rank, c, B._ptr(shards[i]), state,
-                                      self.streams.data_ptr() + a, self.slot_bytes[i]))
+            _, n = self.shard(i, rank)
+            x = B._ptr(shards[i], f"shard of tensor {i}", self.dtype, n)
+            items.append(B.EncodeItem(t, rank, c, x, state, self.streams.data_ptr() + a, self.slot_bytes[i]))
         return items
 
     def encode_scratch(self, items: Sequence[B.EncodeItem]) -> torch.Tensor:

@@ -213,3 +213,31 @@ def test_coded_patch_arguments_without_device():
     with pytest.raises(L.CieraError) as e:       # compress beyond 3
         L.ciera_encode([it], 0x40000, need, stream=0)
     assert e.value.code == 1
+
+
+def test_binding_rejects_tensors_it_would_misread():
+    """A torch tensor handed to the binding must be contiguous, of the element
+    type and count the call implies, and on a GPU; otherwise the library would
+    read the wrong memory (a transposed weight encoded from its storage order).
+    Checked before any device call."""
+    import torch
+
+    t = L.Tensor(64, 64, L.CIERA_BF16, 512, 2)          # rank 0: 32 x 64 values
+    B = L._binding
+    w = torch.zeros(64, 64, dtype=torch.bfloat16)
+    cases = [
+        (lambda: B._ptr(w.t(), "shard"), "not contiguous"),
+        (lambda: L.encode_item(t, 0, 1, w[:32].t(), 0x20000, 0x30000, 8192), "not contiguous"),
+        (lambda: L.encode_item(t, 0, 1, w[:32].view(torch.int16), 0x20000, 0x30000, 8192), "dtype"),
+        (lambda: L.encode_item(t, 0, 1, w[:31], 0x20000, 0x30000, 8192), "elements"),
+        (lambda: L.encode_item(t, 0, 1, w[:32], 0x20000, 0x30000, 8192), "not on a GPU"),
+        (lambda: L.encode_item(t, 0, 1, 0x10000, torch.zeros(100, dtype=torch.uint8), 0x30000, 8192),
+         "at least 4096"),
+        (lambda: L.decode_item(t, 0x30000, 8208, torch.zeros(4095, dtype=torch.bfloat16), 0x20000), "elements"),
+        (lambda: L.ciera_cache_update(t, w.to(torch.float32), 0x20000, stream=0), "dtype"),
+        (lambda: L.ciera_hash_update(t, 1, w[32:].t(), 0x20000, stream=0), "not contiguous"),
+    ]
+    for call, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            call()
+    assert B._ptr(None) is None and B._ptr(0x1234) == 0x1234

@@ -112,6 +112,41 @@ def test_corruption_classes():
     assert _status(_set(s, 64 + n + nbm - 1, bytes([bm[-1] | 0x80])), cache) == O.ST_BITMAP
 
 
+def test_status_is_format_validation_not_integrity():
+    """Reading R36: the status bits flag streams that do not parse; edits that
+    leave a well-formed stream decode with status 0 and a different output.
+    Each case below is one such edit, with the exact status the oracle gives."""
+    x, cache, s = _valid()
+    n, B = 3000, 64
+    p = O.parse_header(s)["n_changed"]
+    pb = 64 + n + O.bitmap_bytes(n, B)
+    recs = [(int.from_bytes(s[pb + 5 * k:pb + 5 * k + 4].tobytes(), "little"), int(s[pb + 5 * k + 4]))
+            for k in range(p)]
+
+    def dec(t):
+        return O.decode([t], n, 1, O.BF16, B, 1, cache)
+
+    out0 = dec(s)[0]
+    assert np.array_equal(out0, x)
+    # a sign|mantissa byte: not checked at all
+    out, _, st = dec(_set(s, 64 + 17, bytes([s[64 + 17] ^ 0x01])))
+    assert st == 0 and np.nonzero(out != x)[0].tolist() == [17]
+    # a record's exponent byte: any value is a valid exponent
+    out, _, st = dec(_set(s, pb + 4, bytes([s[pb + 4] ^ 0x01])))
+    assert st == 0 and np.nonzero(out != x)[0].tolist() == [recs[0][0]]
+    # a record's index moved inside its block, still between its neighbours:
+    # the change lands on the wrong value (and the one it left keeps the cache)
+    k = next(k for k in range(1, p - 1) if recs[k][0] % B != B - 1
+             and recs[k][0] + 1 < recs[k + 1][0] and (recs[k][0] + 1) // B == recs[k][0] // B)
+    i = recs[k][0]
+    out, _, st = dec(_set(s, pb + 5 * k, (i + 1).to_bytes(4, "little")))
+    assert st == 0 and set(np.nonzero(out != x)[0].tolist()) <= {i, i + 1} and not np.array_equal(out, x)
+    # the same index moved into the next block: the bitmap no longer matches
+    j = next(j for j in range(1, p - 1) if (recs[j - 1][0] // B) < (recs[j][0] // B) < (recs[j + 1][0] // B) - 1)
+    to = (recs[j][0] // B + 1) * B
+    assert _status(_set(s, pb + 5 * j, to.to_bytes(4, "little")), cache) == O.ST_BITMAP
+
+
 # -------------------------------------------------------------------- plan
 # Default cost model: link 8,000 B/us, HBM 5,600,000 B/us, fixed 5,000 ns,
 # encode overlapped.  Worked by hand, W = 16, bf16, B = 512:
