@@ -246,6 +246,16 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
                                     uint64_t scratch_bytes, ciera_batch_t* batch, void* stream);
 ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream);
 
+/* ciera_set_sync_polls -- the tiles of an element-patch or RAW shard of at
+ * most 256 encode tiles finish the stream themselves: each publishes its change
+ * count and reads its siblings' (the item's total decides the mode, the counts
+ * before it place its records).  A tile polls a sibling's count at most `polls`
+ * times (0: the default, about a millisecond) and otherwise counts that
+ * sibling's changes itself from the shard and the cache, so the streams are the
+ * same either way; a small value exercises that path.  Process-wide; takes
+ * effect at the next launch.  Host only. */
+void ciera_set_sync_polls(uint32_t polls);
+
 /* The W received streams of one tensor. */
 typedef struct {
   ciera_tensor_t t;

@@ -10,4 +10,5 @@ from ._binding import (Batch, CieraError, CostModel, DecodeItem, EncodeItem, Pla
                        ciera_abi_version, ciera_cache_update, ciera_decode, ciera_decode_launch,
                        ciera_decode_prepare, ciera_decode_scratch_bytes, ciera_encode,
                        ciera_encode_launch, ciera_encode_prepare, ciera_encode_scratch_bytes, ciera_hash_update,
-                       ciera_plan, ciera_select, ciera_shard, ciera_status_str, decode_item, encode_item)
+                       ciera_plan, ciera_select, ciera_set_sync_polls, ciera_shard, ciera_status_str, decode_item,
+                       encode_item)

@@ -21,7 +21,7 @@ HEADER_BYTES = 64
 EXPORTS = ["ciera_plan", "ciera_select", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
            "ciera_encode_prepare", "ciera_encode_launch", "ciera_decode_scratch_bytes",
            "ciera_decode", "ciera_decode_prepare", "ciera_decode_launch", "ciera_cache_update",
-           "ciera_hash_update",
+           "ciera_hash_update", "ciera_set_sync_polls",
            "ciera_status_str", "ciera_abi_version", "ciera_last_error"]
 
 
@@ -110,6 +110,7 @@ def _load() -> ctypes.CDLL:
         "ciera_decode_launch": (c_int, [POINTER(Batch), c_void_p]),
         "ciera_cache_update": (c_int, [POINTER(Tensor), c_void_p, c_void_p, c_void_p]),
         "ciera_hash_update": (c_int, [POINTER(Tensor), c_uint32, c_void_p, c_void_p, c_void_p]),
+        "ciera_set_sync_polls": (None, [c_uint32]),
         "ciera_status_str": (c_char_p, [c_int]),
         "ciera_abi_version": (c_uint32, []),
         "ciera_last_error": (c_char_p, []),
@@ -211,6 +212,12 @@ def ciera_shard(t: Tensor, rank: int) -> Tuple[int, int]:
     off, n = c_uint64(), c_uint64()
     _check(_lib.ciera_shard(byref(t), rank, byref(off), byref(n)), "ciera_shard")
     return off.value, n.value
+
+
+def ciera_set_sync_polls(polls: int) -> None:
+    """Bound on an encode tile's polls of a sibling's count before it counts
+    that sibling's changes itself (0: the default)."""
+    _lib.ciera_set_sync_polls(polls)
 
 
 def ciera_encode_scratch_bytes(items: Sequence[EncodeItem]) -> int:

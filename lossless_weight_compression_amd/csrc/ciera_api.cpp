@@ -130,6 +130,10 @@ hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t stream) 
   return hipSuccess;
 }
 
+// Polls of a sibling tile's count before an encode tile counts its changes
+// itself (0: the kernel's default).
+std::atomic<uint32_t> g_sync_polls{0};
+
 // Batch ids: distinct per prepare, never 0.
 std::atomic<uint32_t> g_ids{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u};
 uint32_t next_id() {
@@ -145,6 +149,7 @@ struct Group {
   uint32_t tpi;          // encode: tiles per item
   uint32_t tpr, world;   // decode: tiles per rank, world
   uint32_t coded;        // items with coded patches (encode) / tensors flagged coded (decode)
+  uint32_t self;         // encode: tiles that finish their items themselves (split_tile_self)
   uint64_t tile0;        // encode: the group's first tile in the batch's count array
   uint64_t stash0;       // encode: word offset of the group's first tile stash
 };
@@ -157,7 +162,7 @@ struct BatchImpl {
   uint32_t batch_id, reserved0;
   uint32_t launches, any_compress;
   uint32_t fin_wg, reserved1;  // encode finishing kernel: workgroups per item
-  uint64_t off_counts, off_stash, off_items;
+  uint64_t off_counts, off_stash, off_items, off_sync;
   Group g[kMaxGroups];
 };
 static_assert(sizeof(BatchImpl) <= sizeof(ciera_batch_t), "batch handle too small");
@@ -187,12 +192,17 @@ struct EncPlan {
   std::vector<uint32_t> order;  // items in group order
   std::vector<Group> groups;
   std::vector<uint64_t> tile0, stash;  // per item in group order
-  uint64_t off_items = 0, off_counts = 0, off_stash = 0, upload = 0, total = 0;
+  uint64_t off_items = 0, off_sync = 0, off_counts = 0, off_stash = 0, upload = 0, total = 0;
 };
+
+// Whether an item's own tiles finish it (element patches and RAW of at most
+// kSelfTiles tiles) rather than a finishing kernel (larger items, the
+// block-hash variant and coded patches).
+bool self_finished(uint32_t compress, uint64_t tpi) { return compress <= 1 && tpi <= kSelfTiles; }
 
 ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncPlan* pl) {
   if (count && !items) return CIERA_ERR_INVALID_ARG;
-  std::map<std::tuple<uint32_t, uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
+  std::map<std::tuple<uint32_t, uint32_t, uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
   for (uint32_t i = 0; i < count; ++i) {
     const ciera_encode_item_t& it = items[i];
     ciera_status_t s = check_tensor(&it.t);
@@ -207,7 +217,7 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     const uint32_t coded = it.compress == kCoded ? 1u : 0u;
     // coded patches are finished one workgroup per tile, kThreads tiles per item at most
     if (coded && tpi > (uint64_t)kThreads) return CIERA_ERR_UNSUPPORTED;
-    by[std::make_tuple(it.t.dtype, S, (uint32_t)tpi, coded)].push_back(i);
+    by[std::make_tuple(it.t.dtype, S, (uint32_t)tpi, coded, self_finished(it.compress, tpi) ? 1u : 0u)].push_back(i);
   }
   if (by.size() > (size_t)kMaxGroups) return CIERA_ERR_UNSUPPORTED;
   uint64_t tiles = 0, words = 0;
@@ -217,12 +227,13 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     g.unit = std::get<1>(kv.first);
     g.tpi = std::get<2>(kv.first);
     g.coded = std::get<3>(kv.first);
+    g.self = std::get<4>(kv.first);
     g.item0 = (uint32_t)pl->order.size();
     g.nitems = (uint32_t)kv.second.size();
     if ((uint64_t)g.nitems * g.tpi >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
     g.tile0 = tiles;
     g.stash0 = words;
-    const uint64_t cap = stash_cap(g.unit, g.coded != 0);
+    const uint64_t cap = g.self ? 0 : stash_cap(g.unit, g.coded != 0);
     for (uint32_t k = 0; k < g.nitems; ++k) {
       pl->tile0.push_back(tiles);
       pl->stash.push_back(words);
@@ -233,7 +244,8 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     pl->groups.push_back(g);
   }
   pl->off_items = 256;
-  pl->upload = pl->off_items + sizeof(EncItem) * (uint64_t)count;
+  pl->off_sync = align_up(pl->off_items + sizeof(EncItem) * (uint64_t)count, 256);
+  pl->upload = pl->off_sync + 8 * tiles;  // the sync words are uploaded as zeros
   pl->off_counts = align_up(pl->upload, 256);
   pl->off_stash = align_up(pl->off_counts + 4 * tiles, 256);
   pl->total = align_up(pl->off_stash + 4 * words, 256);
@@ -428,7 +440,8 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     d.stash = pl.stash[j];
     d.tvals = (uint32_t)kSub * S;
     d.tpi = (uint32_t)std::max<uint64_t>(1, (n + d.tvals - 1) / d.tvals);
-    d.cap = stash_cap(S, it.compress == kCoded);
+    const bool self = self_finished(it.compress, d.tpi);
+    d.cap = self ? 0u : stash_cap(S, it.compress == kCoded);
     d.rank = it.rank;
     d.world = it.t.world;
     d.block_size = it.t.block_size;
@@ -437,7 +450,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     d.elem_bytes = elem_bytes(it.t.dtype);
     d.batch_id = b->batch_id;
     any |= d.compress != 0;
-    if (d.compress) max_bytes = std::max<uint64_t>(max_bytes, n * d.elem_bytes);
+    if (d.compress && !self) max_bytes = std::max<uint64_t>(max_bytes, n * d.elem_bytes);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (hipError_t e = upload(scratch, blob.data(), blob.size(), st)) return device_error("descriptor upload", e);
@@ -451,6 +464,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
   b->off_counts = pl.off_counts;
   b->off_stash = pl.off_stash;
   b->off_items = pl.off_items;
+  b->off_sync = pl.off_sync;
   for (size_t g = 0; g < pl.groups.size(); ++g) b->g[g] = pl.groups[g];
   return CIERA_OK;
 }
@@ -472,6 +486,9 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
     a.tpi = g.tpi;
     a.counts = counts;
     a.stash = stash;
+    a.sync = reinterpret_cast<uint64_t*>(b->scratch + b->off_sync);
+    a.self = g.self;
+    a.polls = g_sync_polls.load(std::memory_order_relaxed);
     if (hipError_t e = launch_encode(g.dtype, g.unit, g.nitems, a, b->batch_id, st))
       return device_error("encode launch", e);
   }
@@ -480,6 +497,7 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
   // per item, over windows of tiles, for larger items
   for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
     const Group& g = b->g[gi];
+    if (g.self) continue;  // finished by its own tiles
     hipError_t e;
     if (g.tpi <= (uint32_t)kThreads) {
       FinArgs f{};
@@ -500,6 +518,8 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
   b->launches += 1;
   return CIERA_OK;
 }
+
+void ciera_set_sync_polls(uint32_t polls) { g_sync_polls.store(polls, std::memory_order_relaxed); }
 
 ciera_status_t ciera_encode(const ciera_encode_item_t* items, uint32_t count, void* scratch,
                             uint64_t scratch_bytes, void* stream) {

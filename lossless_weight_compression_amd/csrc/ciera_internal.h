@@ -14,6 +14,10 @@ constexpr uint64_t kHeader = 64;
 constexpr uint32_t kBlockVariant = 2;  // EncItem::compress of the block-hash variant; stream mode 2
 constexpr uint32_t kCoded = 3;         // EncItem::compress of entropy-coded patches; stream mode 3
 constexpr uint32_t kCodedInfo = 8;     // words after a coded tile's stash data: one per chunk row
+// Element-patch and RAW shards of at most this many encode tiles are finished
+// by their own tiles (split_tile_self, one launch, no stash); larger ones, the
+// block-hash variant and coded patches by a finishing kernel.
+constexpr uint32_t kSelfTiles = 256;
 
 // Decode workgroups: kDecThreads threads, 16 values each per chunk row; a tile
 // is U chunk rows.  (512- and 1024-thread groups, which put more data behind
@@ -69,12 +73,17 @@ struct DecItem {
 //            the tile a 4096-byte region (its coded or dense data), then
 //            kCodedInfo words, one per row: changes | words << 13 | dense << 26;
 //            the tile's count is then data bytes | changes << 16
+//   sync   : u64 per tile of the groups whose tiles finish their items
+//            themselves: epoch << 32 | changes of the tile (zeroed by prepare)
 struct EncArgs {
   const EncItem* items;
   uint32_t item0;      // first item of the group
   uint32_t tpi;        // tiles per item in the group
   uint32_t* counts;    // the batch's per-tile counts
   uint32_t* stash;     // the batch's stash words
+  uint64_t* sync;      // the batch's sync words (EncItem::tile0 indexes them too)
+  uint32_t self;       // the group's tiles finish their items (compress 0/1, tpi <= kSelfTiles)
+  uint32_t polls;      // self: polls of a sibling's slot before counting its changes (0: default)
 };
 
 // The per-tile finishing kernel of one group (at most kThreads tiles per

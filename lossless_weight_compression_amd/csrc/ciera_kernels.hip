@@ -516,6 +516,63 @@ __device__ __forceinline__ void chunk_store(uint8_t* stream, uint64_t c0, int cn
   }
 }
 
+// The sign|mantissa section bytes of one 16-value chunk as little-endian words
+// (bf16 16 bytes in 4 words, fp32 48 in 12, fp16 22 in 6), from its raw words.
+template <int DT>
+constexpr int kSmWords = DT == 1 ? 4 : DT == 2 ? 12 : 6;
+template <int DT>
+__device__ __forceinline__ void chunk_sm_words(const uint32_t* xw, uint32_t o[kSmWords<DT>]) {
+  if constexpr (DT == 1) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = bf16x4_sm(xw[2 * q], xw[2 * q + 1]);
+  } else {
+    uint32_t sm[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t v = Tr<DT>::E == 2 ? (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu : xw[j];
+      sm[j] = sm_of<DT>(v);
+    }
+    if constexpr (DT == 3) {
+      pack11x16(sm, o);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a = sm[4 * q], b = sm[4 * q + 1], c = sm[4 * q + 2], d = sm[4 * q + 3];
+        o[3 * q] = a | (b << 24);
+        o[3 * q + 1] = (b >> 8) | (c << 16);
+        o[3 * q + 2] = (c >> 16) | (d << 8);
+      }
+    }
+  }
+}
+
+// Stores the section bytes of the first cnt values of a chunk, given as the
+// words chunk_sm_words made, at p = section start + the chunk's offset (16-byte
+// aligned for bf16 and fp32, even for fp16).
+template <int DT>
+__device__ __forceinline__ void store_sm_words(uint8_t* p, int cnt, const uint32_t o[kSmWords<DT>]) {
+  if constexpr (DT == 1) {
+    store_words<4>(p, (uint32_t)cnt, true, o);
+  } else if constexpr (DT == 2) {
+    store_words<12>(p, 3u * (uint32_t)cnt, true, o);
+  } else if (cnt == 16) {
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) == 0) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) gp(reinterpret_cast<uint32_t*>(p))[i] = o[i];
+      gp(reinterpret_cast<uint16_t*>(p + 20))[0] = (uint16_t)o[5];
+    } else {  // p = 4q + 2
+      gp(reinterpret_cast<uint16_t*>(p))[0] = (uint16_t)o[0];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) gp(reinterpret_cast<uint32_t*>(p + 2))[i] = (o[i] >> 16) | (o[i + 1] << 16);
+    }
+  } else {
+    const int nb = (11 * cnt + 7) / 8;
+#pragma unroll
+    for (int b = 0; b < 22; ++b)
+      if (b < nb) gp(p)[b] = (uint8_t)(o[b >> 2] >> (8 * (b & 3)));
+  }
+}
+
 // Exclusive prefix of v over the workgroup's threads in thread order, and the
 // total.  Contains one barrier; s_red (4 words) must not be in use by another
 // call until every thread has passed a later barrier.
@@ -650,7 +707,7 @@ __device__ __forceinline__ void tile_block_hashes(const uint32_t (&ex)[S][4], ui
 // changed blocks, B per block in block order, into its stash (T bytes: every
 // block fits).
 template <int DT, int S>
-__device__ void split_tile_block(const EncItem& d, uint32_t local, const EncArgs& a) {
+__device__ __forceinline__ void split_tile_block(const EncItem& d, uint32_t local, const EncArgs& a) {
   constexpr int E = Tr<DT>::E;
   constexpr uint32_t T = (uint32_t)kSub * S;
   constexpr int XW = 4 * E;
@@ -944,7 +1001,7 @@ __device__ uint32_t rans_encode_chunk(const uint32_t* list, uint32_t c, uint32_t
 // rows at a time, or dense) in the row's stash region, its info word after
 // the regions, and the tile's count (data bytes | changes << 16).
 template <int DT, int S>
-__device__ void split_tile_coded(const EncItem& d, uint32_t local, const EncArgs& a) {
+__device__ __forceinline__ void split_tile_coded(const EncItem& d, uint32_t local, const EncArgs& a) {
   constexpr int E = Tr<DT>::E;
   constexpr uint32_t T = (uint32_t)kSub * S;
   constexpr int XW = 4 * E;
@@ -1079,6 +1136,266 @@ __device__ void split_tile_coded(const EncItem& d, uint32_t local, const EncArgs
   }
 }
 
+// The 64-byte stream header (little-endian): "CIER", version 1, dtype, mode
+// (0 RAW, 1 COMPRESSED, 2 BLOCK), block size, n, changed values (blocks for
+// BLOCK) P, total length, offset, rank, world.
+template <int DT>
+__device__ __forceinline__ void write_header(const EncItem& d, uint64_t P, uint32_t mode, uint64_t total) {
+  uint32_t h[16];
+  h[0] = 0x52454943u;  // "CIER"
+  h[1] = 1u | ((uint32_t)DT << 16) | (mode << 24);
+  h[2] = d.block_size;
+  h[3] = 0;
+  h[4] = (uint32_t)d.n; h[5] = (uint32_t)(d.n >> 32);
+  h[6] = (uint32_t)P; h[7] = (uint32_t)(P >> 32);
+  h[8] = (uint32_t)total; h[9] = (uint32_t)(total >> 32);
+  h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
+  h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v4u o;
+    o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
+    stg16(d.stream + 16 * q, o);
+  }
+}
+
+// ------------------------------------------- encode, tiles that finish themselves
+// Element patches and RAW (compress 0 or 1) of items of at most kSelfTiles
+// tiles.  After the compare each tile publishes its change count in its slot
+// of the batch's sync array -- one 64-bit word, epoch << 32 | count, written
+// with a device-scope atomic -- and waits until every tile of its item has
+// published in this launch's epoch.  The counts give the item's total, hence
+// the mode [CIERA 3.2: compressed only when smaller], and the tile's exclusive
+// prefix, hence where its records go.  Only then does the tile store its
+// sign|mantissa bytes (or its raw values), its bitmap bytes and its records,
+// and tile 0 the header: nothing is written before the mode is known, so the
+// RAW fallback needs no rewrite and no second launch finishes the stream.
+//
+// The epoch is the tile's own slot's previous epoch plus one: every launch
+// advances every slot of the item by one (the slots are zeroed when the batch
+// is prepared), so the tiles of an item agree on it without a host value, and
+// a replayed launch never mistakes the last launch's counts for its own.  The
+// tiles of an item are consecutive workgroups and publish before they wait, so
+// a waiting tile needs only its siblings to be dispatched: at most
+// kSelfTiles / 8 + 1 of them share an XCD, far fewer than an XCD runs at once.
+// The wait is a shortcut, not a dependency: after `polls` polls of a slot
+// (EncArgs::polls) a tile counts that sibling's changes itself from the shard
+// and the cache, so it finishes with the same result however the workgroups
+// are scheduled.
+constexpr uint32_t kSelfPolls = 1u << 16;  // default bound, about a millisecond
+
+// Changes of tile k of item d (tvals values per tile), counted by the whole
+// workgroup from the shard and the cache one value per thread at a time (a
+// rare path, kept small so that it costs the kernel no registers).  Contains
+// two barriers.
+template <int DT>
+__device__ __forceinline__ uint32_t tile_changes(const EncItem& d, uint64_t k, uint32_t* s_red) {
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint64_t v0 = k * d.tvals, v1 = min<uint64_t>(d.n, v0 + d.tvals);
+  uint32_t c = 0;
+  for (uint64_t i = v0 + tid; i < v1; i += kThreads) {
+    const uint32_t v = Tr<DT>::E == 2 ? (uint32_t)gp(reinterpret_cast<const uint16_t*>(d.x))[i]
+                                      : gp(reinterpret_cast<const uint32_t*>(d.x))[i];
+    c += exp_of<DT>(v) != (uint32_t)gp(d.cache)[i] ? 1u : 0u;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  __syncthreads();  // s_red is free
+  if (lane == 0) s_red[wave] = c;
+  __syncthreads();
+  return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+}
+
+template <int DT, int S>
+__device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local, const EncArgs& a) {
+  constexpr int E = Tr<DT>::E;
+  constexpr uint32_t T = (uint32_t)kSub * S;
+  constexpr int XW = 4 * E;  // words of 16 raw values
+  __shared__ uint32_t s_wtot[4 * S];
+  __shared__ uint64_t s_chg[4 * S];  // one bit per 16-value chunk of the tile, in value order
+  __shared__ uint32_t s_sum[2];      // the item's changes, those of the tiles before
+  __shared__ uint32_t s_miss[kSelfTiles / 32];  // tiles whose counts did not come in time
+  __shared__ uint32_t s_red[kThreads / 64];
+
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint64_t base = (uint64_t)local * T;
+  const uint64_t n = d.n;
+  const uint32_t B = d.block_size;
+  const uint32_t lb = (uint32_t)__ffs(B) - 1u;  // B is a power of two (checked by the API)
+  uint64_t* const sync = a.sync + d.tile0;      // the item's slots
+  uint64_t mine_old = 0;                        // this tile's slot as the last launch left it
+  if (tid == 0) mine_old = __hip_atomic_load(sync + local, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // loads, split and compare; the section words stay in registers until the
+  // mode is known (a RAW stream reads its values again)
+  uint32_t smw[S][kSmWords<DT>], mask[S], expk[S][4];
+  int cnt[S];
+  {
+    uint32_t xw[S][XW], cw[S][4];
+    const bool full = d.cache_aligned != 0 && base + T <= n;  // uniform
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+      cnt[s] = full ? 16 : (c0 < n ? (int)min<uint64_t>(16, n - c0) : 0);
+      if (cnt[s] > 0) {
+        load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
+        load_words<4, kNtBulk<DT>>(d.cache + c0, (uint32_t)cnt[s], full || d.cache_aligned != 0, cw[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      mask[s] = 0;
+      expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
+      if (full) mask[s] = chunk_exps<DT, true>(xw[s], cw[s], 16, expk[s]);
+      else if (cnt[s] > 0) mask[s] = chunk_exps<DT, false>(xw[s], cw[s], cnt[s], expk[s]);
+      chunk_sm_words<DT>(xw[s], smw[s]);
+    }
+  }
+
+  // the tile's change count, chunk-row major (= ascending value index)
+  uint32_t lpre[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t chg = __ballot(mask[s] != 0);
+    const uint32_t c = (uint32_t)__popc(mask[s]);
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+      const uint64_t m = __ballot((c >> b) & 1u);
+      pre += lanes_below(m) << b;
+      tot += (uint32_t)__popcll(m) << b;
+    }
+    lpre[s] = pre;
+    if (lane == 0) {
+      s_wtot[s * 4 + wave] = tot;
+      s_chg[s * 4 + wave] = chg;
+    }
+  }
+  if (tid < kSelfTiles / 32) s_miss[tid] = 0;
+  __syncthreads();
+  uint32_t agg = 0, before[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t t = s_wtot[s * 4 + w];
+      if (w == (int)wave) before[s] = agg;
+      agg += t;
+    }
+  }
+
+  // publish, then wait for the item's other tiles (wave 0, lanes over tiles)
+  if (wave == 0) {
+    const uint32_t epoch = __shfl((uint32_t)(mine_old >> 32), 0) + 1u;
+    if (lane == 0)
+      __hip_atomic_store(sync + local, ((uint64_t)epoch << 32) | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t polls = a.polls ? a.polls : kSelfPolls;
+    uint32_t tot = 0, pre = 0;
+    for (uint32_t k = lane; k < d.tpi; k += 64) {
+      uint64_t v = 0;
+      bool got = false;
+      for (uint32_t i = 0; i < polls; ++i) {
+        v = __hip_atomic_load(sync + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(v >> 32) == epoch) {
+          got = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (got) {
+        tot += (uint32_t)v;
+        pre += k < local ? (uint32_t)v : 0u;
+      } else {
+        atomicOr(&s_miss[k >> 5], 1u << (k & 31u));
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      tot += __shfl_xor(tot, o);
+      pre += __shfl_xor(pre, o);
+    }
+    if (lane == 0) {
+      s_sum[0] = tot;
+      s_sum[1] = pre;
+    }
+  }
+  __syncthreads();
+  uint32_t tot_miss = 0, pre_miss = 0;  // the late tiles, counted here
+  for (uint32_t w = 0; w < (d.tpi + 31) / 32; ++w) {  // uniform
+    uint32_t m = s_miss[w];
+    while (m) {
+      const uint32_t k = 32 * w + (uint32_t)__ffs(m) - 1u;
+      m &= m - 1;
+      const uint32_t ck = tile_changes<DT>(d, k, s_red);
+      tot_miss += ck;
+      pre_miss += k < local ? ck : 0u;
+    }
+  }
+  const uint64_t P = (uint64_t)s_sum[0] + tot_miss;
+  const uint32_t excl = s_sum[1] + pre_miss;
+  const uint64_t nbm = (((n + B - 1) >> lb) + 7) / 8;
+  const uint64_t smsec = sm_sec<DT>(n);
+  const uint64_t comp = kHeader + smsec + (P ? nbm + 5 * P : 0);
+  const uint64_t raw = kHeader + n * E;
+  const bool cmode = d.compress != 0 && comp < raw;
+
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+    if (cnt[s] > 0) {
+      if (cmode) {
+        store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
+      } else {  // RAW: the values as stored
+        uint32_t rw[XW];
+        load_words<XW>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, rw);
+        store_words<XW>(d.stream + kHeader + c0 * E, (uint32_t)cnt[s] * E, true, rw);
+      }
+    }
+  }
+  if (local == 0 && tid == 0) write_header<DT>(d, P, cmode ? 1u : 0u, cmode ? comp : raw);
+  if (!cmode || P == 0) return;
+
+  // the tile's bitmap bytes (a tile spans whole bitmap bytes)
+  const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
+  const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
+  const uint32_t tbytes = (tblocks + 7) / 8;
+  if (tid < tbytes) {
+    const uint32_t L = B >> 4;  // chunks per block, >= 4
+    uint32_t byte = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t blk = tid * 8 + (uint32_t)k;
+      if (blk < tblocks) {
+        const uint32_t first = blk * L;
+        uint64_t any;
+        if (L < 64) {
+          any = (s_chg[first >> 6] >> (first & 63u)) & ((1ull << L) - 1ull);
+        } else {
+          any = 0;
+          for (uint32_t u = 0; u < L / 64; ++u) any |= s_chg[(first >> 6) + u];
+        }
+        if (any) byte |= 1u << k;
+      }
+    }
+    gp(d.stream)[kHeader + smsec + (base >> (lb + 3)) + tid] = (uint8_t)byte;
+  }
+
+  // the tile's records at their places in the patch list
+  const uint64_t pbase = kHeader + smsec + nbm;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    uint32_t m = mask[s];
+    uint64_t g = (uint64_t)excl + before[s] + lpre[s];
+    const uint32_t rel0 = (uint32_t)s * kSub + tid * kEPT;
+    while (m) {
+      const int j = __ffs(m) - 1;
+      m &= m - 1;
+      put_record(d.stream, comp, pbase + 5 * g, (uint32_t)(base + rel0 + (uint32_t)j), byte_of(expk[s], j));
+      ++g;
+    }
+  }
+}
+
 template <int DT, int S>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t batch_id) {
   constexpr int E = Tr<DT>::E;
@@ -1099,6 +1416,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
   }
   if (d.compress == kCoded) {  // uniform
     split_tile_coded<DT, S>(d, local, a);
+    return;
+  }
+  if (a.self) {  // uniform: compress 0 or 1, at most kSelfTiles tiles
+    split_tile_self<DT, S>(d, local, a);
     return;
   }
   const uint64_t base = (uint64_t)local * T;
@@ -1254,29 +1575,6 @@ __device__ void rederive_tile(const EncItem& d, uint64_t j, uint32_t r0, uint64_
     }
     run += tot;
     __syncthreads();  // s_red is read before it is written again
-  }
-}
-
-// The 64-byte stream header (little-endian): "CIER", version 1, dtype, mode
-// (0 RAW, 1 COMPRESSED, 2 BLOCK), block size, n, changed values (blocks for
-// BLOCK) P, total length, offset, rank, world.
-template <int DT>
-__device__ __forceinline__ void write_header(const EncItem& d, uint64_t P, uint32_t mode, uint64_t total) {
-  uint32_t h[16];
-  h[0] = 0x52454943u;  // "CIER"
-  h[1] = 1u | ((uint32_t)DT << 16) | (mode << 24);
-  h[2] = d.block_size;
-  h[3] = 0;
-  h[4] = (uint32_t)d.n; h[5] = (uint32_t)(d.n >> 32);
-  h[6] = (uint32_t)P; h[7] = (uint32_t)(P >> 32);
-  h[8] = (uint32_t)total; h[9] = (uint32_t)(total >> 32);
-  h[10] = (uint32_t)d.off; h[11] = (uint32_t)(d.off >> 32);
-  h[12] = d.rank; h[13] = d.world; h[14] = 0; h[15] = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    v4u o;
-    o.x = h[4 * q]; o.y = h[4 * q + 1]; o.z = h[4 * q + 2]; o.w = h[4 * q + 3];
-    stg16(d.stream + 16 * q, o);
   }
 }
 

@@ -109,26 +109,30 @@ def test_change_rates_and_raw_fallback(dtype, frac):
         assert modes == {O.MODE_COMPRESSED}
 
 
-# (rows, cols, dtype, dense tiles): 1051 encode tiles of 8192 values (the last
-# half full) go through the finishing kernel that scans tile counts in windows
-# of 1024; 256 tiles go through the one-workgroup-per-tile finishing kernel.
+# (rows, cols, dtype, B, dense regions of 8192 values).  Shards of at most
+# 2^21 values are encoded by one workgroup each; larger ones by the tiled split
+# kernel (tiles of 8192 values for B <= 1024, 16384 for B = 2048, 32768 for
+# B = 4096) and a finishing kernel: 1051 tiles go through the one that scans
+# tile counts in windows of 1024, 129 and 65 tiles through the one with a
+# workgroup per tile.  Dense regions (60%) overflow a tile's stash (a quarter
+# of the tile), whose records are then derived again from the shard.
 MANY_TILES = [
-    (2101, 4096, torch.bfloat16, (3, 1030, 1050)),
-    (2101, 4096, torch.float16, (3, 1030, 1050)),
-    (2048, 1024, torch.bfloat16, (0, 5, 255)),
-    (2047, 1024, torch.float32, (1, 254, 255)),
+    (2101, 4096, torch.bfloat16, 512, (3, 1030, 1050)),
+    (2101, 4096, torch.float16, 512, (3, 1030, 1050)),
+    (2049, 1024, torch.bfloat16, 2048, (0, 1, 60, 256)),
+    (2049, 1024, torch.float32, 4096, (4, 5, 6, 7, 200)),
+    (2048, 1024, torch.bfloat16, 512, (0, 5, 255)),     # 2^21 values: one workgroup
+    (2047, 1024, torch.float32, 512, (1, 254, 255)),
+    (2048, 1024, torch.float16, 64, (0, 128, 255)),
 ]
 
 
-@pytest.mark.parametrize("rows,cols,dtype,dense", MANY_TILES)
-def test_many_tiles_and_stash_overflow(rows, cols, dtype, dense):
-    """One shard of many encode tiles (8192 values each).  Tiles with more
-    changes than their stash holds (a quarter of the tile) -- here 60% in a few
-    tiles, among them the last, partial one -- have their records derived again
-    from the shard and the cache.  The rest changes at 1%, so the stream stays
+@pytest.mark.parametrize("rows,cols,dtype,B,dense", MANY_TILES)
+def test_many_tiles_and_stash_overflow(rows, cols, dtype, B, dense):
+    """One shard at one rank: dense regions among 1% changes; the stream stays
     COMPRESSED."""
     T = 8192
-    say(f"[gpu] many tiles {rows}x{cols} {dtype} dense {dense}")
+    say(f"[gpu] many tiles {rows}x{cols} {dtype} B={B} dense {dense}")
     spec = W.TensorSpec("big", rows, cols)
     w0 = W.base_weights(spec, W.tensor_seed("many", rows, cols), dtype)
     mask = W.mask_uniform(rows * cols, 0.01, W.tensor_seed("many-m", rows, cols))
@@ -137,7 +141,7 @@ def test_many_tiles_and_stash_overflow(rows, cols, dtype, dense):
         lo, hi = t * T, min(rows * cols, (t + 1) * T)
         mask[lo:hi] |= dense_m[lo:hi]
     w1 = W.perturb_exact(w0, mask, W.tensor_seed("many-p", rows, cols))
-    case = Case([(rows, cols)], dtype, 1)
+    case = Case([(rows, cols)], dtype, 1, B)
     res = case.run([w0], [w1], compress=[1])
     assert res["status"] == 0 and res["ostatus"] == 0
     h = O.parse_header(case.codec.slot(0, 0).cpu().numpy())
@@ -306,3 +310,28 @@ def test_encode_is_deterministic():
     for _ in range(3):
         case.run(w0, w1)
         assert torch.equal(first, case.codec.streams)
+
+
+@pytest.mark.parametrize("polls", [1, 4])
+def test_self_finishing_tiles_that_count_late_siblings(polls):
+    """Tiles that finish their item themselves poll each sibling's change count
+    a bounded number of times and otherwise count the sibling's changes from
+    the shard and the cache.  With one or four polls most siblings are counted
+    that way; every stream must still equal the oracle's, byte for byte
+    (shards of 1 to 48 tiles, COMPRESSED and RAW fallback, three types)."""
+    import lossless_weight_compression_amd as L
+    say(f"[gpu] self-finishing tiles, {polls} polls")
+    try:
+        L.ciera_set_sync_polls(polls)
+        for dtype in (torch.bfloat16, torch.float32, torch.float16):
+            specs = [W.TensorSpec("a", 512, 768), W.TensorSpec("b", 96, 4096), W.TensorSpec("c", 7, 5)]
+            w0, w1 = [], []
+            for i, s in enumerate(specs):
+                a = W.base_weights(s, W.tensor_seed("late", i), dtype)
+                m = W.mask_uniform(s.numel, (0.01, 0.3, 0.2)[i], W.tensor_seed("late-m", i))
+                w0.append(a)
+                w1.append(W.perturb_exact(a, m, W.tensor_seed("late-p", i)))
+            res = Case([(s.rows, s.cols) for s in specs], dtype, 2).run(w0, w1, compress=[1, 1, 1])
+            assert res["status"] == 0 and res["ostatus"] == 0
+    finally:
+        L.ciera_set_sync_polls(0)
