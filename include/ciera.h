@@ -256,6 +256,23 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream);
  * effect at the next launch.  Host only. */
 void ciera_set_sync_polls(uint32_t polls);
 
+/* ciera_encode_noalloc -- ciera_encode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same streams, byte for byte, with the library's own
+ * device array of CIERA_NOALLOC_SCRATCH_BYTES (one per device, held until the
+ * process ends) in place of a caller's scratch.  It calls no allocating HIP or
+ * library routine: the descriptors reach the device as kernel arguments of a
+ * small kernel, which also clears the count words the tiles publish.  Limits:
+ * element patches and RAW (compress 0 or 1) of shards of at most 256 encode
+ * tiles (2^21 values at B <= 1024), else CIERA_ERR_UNSUPPORTED; a batch whose
+ * scratch (ciera_encode_scratch_bytes) exceeds CIERA_NOALLOC_SCRATCH_BYTES
+ * (about 7,000 items of 16 tiles), CIERA_ERR_BUFFER_TOO_SMALL.  Every call on
+ * a device uses that device's one array and leaves its contents behind: calls
+ * that overlap in time on one device (other streams, other threads) race and
+ * must not be issued.  Argument checks as for ciera_encode. */
+#define CIERA_NOALLOC_SCRATCH_BYTES 1048576u
+ciera_status_t ciera_encode_noalloc(const ciera_encode_item_t* items, uint32_t count, void* stream);
+
 /* The W received streams of one tensor. */
 typedef struct {
   ciera_tensor_t t;

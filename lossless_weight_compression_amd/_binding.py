@@ -16,12 +16,13 @@ CIERA_TENSOR_CODED = 1  # Tensor.flags: the tensor's streams may be CODED
 CIERA_OK, CIERA_ERR_INVALID_ARG, CIERA_ERR_BUFFER_TOO_SMALL, CIERA_ERR_UNSUPPORTED, CIERA_ERR_DEVICE = range(5)
 CIERA_ST_MAGIC, CIERA_ST_FIELD, CIERA_ST_LENGTH, CIERA_ST_PATCH, CIERA_ST_BITMAP = 1, 2, 4, 8, 16
 HEADER_BYTES = 64
+CIERA_NOALLOC_SCRATCH_BYTES = 1 << 20  # the static scratch of ciera_encode_noalloc
 
 # every symbol include/ciera.h declares
 EXPORTS = ["ciera_plan", "ciera_select", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
            "ciera_encode_prepare", "ciera_encode_launch", "ciera_decode_scratch_bytes",
            "ciera_decode", "ciera_decode_prepare", "ciera_decode_launch", "ciera_cache_update",
-           "ciera_hash_update", "ciera_set_sync_polls",
+           "ciera_hash_update", "ciera_set_sync_polls", "ciera_encode_noalloc",
            "ciera_status_str", "ciera_abi_version", "ciera_last_error"]
 
 
@@ -111,6 +112,7 @@ def _load() -> ctypes.CDLL:
         "ciera_cache_update": (c_int, [POINTER(Tensor), c_void_p, c_void_p, c_void_p]),
         "ciera_hash_update": (c_int, [POINTER(Tensor), c_uint32, c_void_p, c_void_p, c_void_p]),
         "ciera_set_sync_polls": (None, [c_uint32]),
+        "ciera_encode_noalloc": (c_int, [POINTER(EncodeItem), c_uint32, c_void_p]),
         "ciera_status_str": (c_char_p, [c_int]),
         "ciera_abi_version": (c_uint32, []),
         "ciera_last_error": (c_char_p, []),
@@ -261,6 +263,12 @@ def ciera_encode(items: Sequence[EncodeItem], scratch, scratch_bytes: Optional[i
     nbytes = scratch_bytes if scratch_bytes is not None else scratch.numel() * scratch.element_size()
     _check(_lib.ciera_encode(_items_array(EncodeItem, items), len(items), _ptr(scratch), nbytes,
                              _stream(stream)), "ciera_encode")
+
+
+def ciera_encode_noalloc(items: Sequence[EncodeItem], stream=None) -> None:
+    """ciera_encode with the library's static device scratch (no allocation)."""
+    _check(_lib.ciera_encode_noalloc(_items_array(EncodeItem, items), len(items), _stream(stream)),
+           "ciera_encode_noalloc")
 
 
 def ciera_decode(items: Sequence[DecodeItem], status, scratch, scratch_bytes: Optional[int] = None,

@@ -387,15 +387,10 @@ ciera_status_t ciera_encode_scratch_bytes(const ciera_encode_item_t* items, uint
   return CIERA_OK;
 }
 
-ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t count, void* scratch,
-                                    uint64_t scratch_bytes, ciera_batch_t* batch, void* stream) {
-  if (!batch) return CIERA_ERR_INVALID_ARG;
-  std::memset(batch, 0, sizeof(*batch));
-  EncPlan pl;
-  ciera_status_t s = enc_layout(items, count, &pl);
-  if (s) return s;
-  if (!scratch || !aligned(scratch, 256)) return CIERA_ERR_INVALID_ARG;
-  if (scratch_bytes < pl.total) return CIERA_ERR_BUFFER_TOO_SMALL;
+namespace {
+
+// Every item checked as ciera_encode checks it (the layout checked the tensors).
+ciera_status_t check_encode_items(const ciera_encode_item_t* items, uint32_t count) {
   for (uint32_t i = 0; i < count; ++i) {
     const ciera_encode_item_t& it = items[i];
     uint64_t off, n;
@@ -414,13 +409,15 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
         (it.cache_full && overlap(it.stream, wlen, cptr, clen)))
       return CIERA_ERR_INVALID_ARG;
   }
-  BatchImpl* b = impl(batch);
-  b->batch_id = next_id();
-  std::vector<uint8_t> blob(pl.upload, 0);
-  reinterpret_cast<uint32_t*>(blob.data())[0] = b->batch_id;
-  EncItem* di = reinterpret_cast<EncItem*>(blob.data() + pl.off_items);
-  uint32_t any = 0;
-  uint64_t max_bytes = 0;  // largest shard that may need the RAW rewrite
+  return CIERA_OK;
+}
+
+// The batch's descriptors di[0..count) in group order; *any: some item may be
+// compressed; *max_bytes: the largest shard a finishing kernel may rewrite RAW.
+void fill_enc_items(const ciera_encode_item_t* items, uint32_t count, const EncPlan& pl, uint32_t batch_id,
+                    EncItem* di, uint32_t* any, uint64_t* max_bytes) {
+  *any = 0;
+  *max_bytes = 0;
   for (uint32_t j = 0; j < count; ++j) {
     const ciera_encode_item_t& it = items[pl.order[j]];
     uint64_t off, n;
@@ -448,12 +445,14 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
     d.compress = it.compress;
     d.cache_aligned = !blocks && aligned(d.cache, 16) ? 1u : 0u;
     d.elem_bytes = elem_bytes(it.t.dtype);
-    d.batch_id = b->batch_id;
-    any |= d.compress != 0;
-    if (d.compress && !self) max_bytes = std::max<uint64_t>(max_bytes, n * d.elem_bytes);
+    d.batch_id = batch_id;
+    *any |= d.compress != 0;
+    if (d.compress && !self) *max_bytes = std::max<uint64_t>(*max_bytes, n * d.elem_bytes);
   }
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (hipError_t e = upload(scratch, blob.data(), blob.size(), st)) return device_error("descriptor upload", e);
+}
+
+void set_enc_batch(BatchImpl* b, const EncPlan& pl, void* scratch, uint64_t scratch_bytes, uint32_t count,
+                   uint32_t any, uint64_t max_bytes) {
   b->magic = kEncMagic;
   b->scratch = static_cast<uint8_t*>(scratch);
   b->scratch_bytes = scratch_bytes;
@@ -466,6 +465,31 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
   b->off_items = pl.off_items;
   b->off_sync = pl.off_sync;
   for (size_t g = 0; g < pl.groups.size(); ++g) b->g[g] = pl.groups[g];
+}
+
+}  // namespace
+
+ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t count, void* scratch,
+                                    uint64_t scratch_bytes, ciera_batch_t* batch, void* stream) {
+  if (!batch) return CIERA_ERR_INVALID_ARG;
+  std::memset(batch, 0, sizeof(*batch));
+  EncPlan pl;
+  ciera_status_t s = enc_layout(items, count, &pl);
+  if (s) return s;
+  if (!scratch || !aligned(scratch, 256)) return CIERA_ERR_INVALID_ARG;
+  if (scratch_bytes < pl.total) return CIERA_ERR_BUFFER_TOO_SMALL;
+  if ((s = check_encode_items(items, count))) return s;
+  BatchImpl* b = impl(batch);
+  b->batch_id = next_id();
+  std::vector<uint8_t> blob(pl.upload, 0);  // descriptors; the sync words go up as zeros
+  reinterpret_cast<uint32_t*>(blob.data())[0] = b->batch_id;
+  uint32_t any;
+  uint64_t max_bytes;
+  fill_enc_items(items, count, pl, b->batch_id, reinterpret_cast<EncItem*>(blob.data() + pl.off_items), &any,
+                 &max_bytes);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipError_t e = upload(scratch, blob.data(), blob.size(), st)) return device_error("descriptor upload", e);
+  set_enc_batch(b, pl, scratch, scratch_bytes, count, any, max_bytes);
   return CIERA_OK;
 }
 
@@ -520,6 +544,38 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
 }
 
 void ciera_set_sync_polls(uint32_t polls) { g_sync_polls.store(polls, std::memory_order_relaxed); }
+
+static_assert(kStaticScratchBytes == CIERA_NOALLOC_SCRATCH_BYTES, "static scratch size");
+
+ciera_status_t ciera_encode_noalloc(const ciera_encode_item_t* items, uint32_t count, void* stream) {
+  if (count == 0) return CIERA_OK;
+  EncPlan pl;
+  ciera_status_t s = enc_layout(items, count, &pl);
+  if (s) return s;
+  if ((s = check_encode_items(items, count))) return s;
+  for (const Group& g : pl.groups)
+    if (!g.self) return CIERA_ERR_UNSUPPORTED;  // a finishing kernel would need a stash
+  if (pl.total > kStaticScratchBytes) return CIERA_ERR_BUFFER_TOO_SMALL;
+  void* base = nullptr;
+  if (hipError_t e = static_scratch(&base)) return device_error("static scratch lookup", e);
+  ciera_batch_t batch;
+  std::memset(&batch, 0, sizeof(batch));
+  BatchImpl* b = impl(&batch);
+  b->batch_id = next_id();
+  std::vector<EncItem> di(count);
+  uint32_t any;
+  uint64_t max_bytes;
+  fill_enc_items(items, count, pl, b->batch_id, di.data(), &any, &max_bytes);
+  uint8_t* const sb = static_cast<uint8_t*>(base);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // descriptors by kernel arguments; the sync words zeroed by the same launch
+  if (hipError_t e = launch_enc_desc(di.data(), count, reinterpret_cast<EncItem*>(sb + pl.off_items),
+                                     reinterpret_cast<uint64_t*>(sb + pl.off_sync), (pl.upload - pl.off_sync) / 8,
+                                     reinterpret_cast<uint32_t*>(sb), b->batch_id, st))
+    return device_error("descriptor launch", e);
+  set_enc_batch(b, pl, base, kStaticScratchBytes, count, any, max_bytes);
+  return ciera_encode_launch(&batch, stream);
+}
 
 ciera_status_t ciera_encode(const ciera_encode_item_t* items, uint32_t count, void* scratch,
                             uint64_t scratch_bytes, void* stream) {

@@ -14,6 +14,9 @@ constexpr uint64_t kHeader = 64;
 constexpr uint32_t kBlockVariant = 2;  // EncItem::compress of the block-hash variant; stream mode 2
 constexpr uint32_t kCoded = 3;         // EncItem::compress of entropy-coded patches; stream mode 3
 constexpr uint32_t kCodedInfo = 8;     // words after a coded tile's stash data: one per chunk row
+// Size of the device array that ciera_encode_noalloc uses as its scratch.
+constexpr uint64_t kStaticScratchBytes = (uint64_t)1 << 20;
+
 // Element-patch and RAW shards of at most this many encode tiles are finished
 // by their own tiles (split_tile_self, one launch, no stash); larger ones, the
 // block-hash variant and coded patches by a finishing kernel.
@@ -107,6 +110,15 @@ hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0,
 hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s);
 hipError_t launch_decode(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems,
                          uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id, hipStream_t s);
+// The calling thread's current device's copy of the library's static scratch
+// array (kStaticScratchBytes, 256-byte aligned): its device address, looked up
+// once per device.
+hipError_t static_scratch(void** ptr);
+// Writes n encode descriptors (host array) to dst on the device by kernel
+// arguments -- no host staging buffer, no copy -- zeroes nzero 64-bit words
+// at zero and stores batch_id at head.
+hipError_t launch_enc_desc(const EncItem* host_items, uint32_t n, EncItem* dst, uint64_t* zero, uint64_t nzero,
+                           uint32_t* head, uint32_t batch_id, hipStream_t s);
 hipError_t launch_cache_update(int dtype, const uint8_t* w, uint8_t* cache, uint64_t n, hipStream_t s);
 hipError_t launch_hash_seed(int dtype, const uint8_t* x, uint8_t* hashes, uint64_t n, uint32_t block_size, hipStream_t s);
 

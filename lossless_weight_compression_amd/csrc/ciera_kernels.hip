@@ -14,6 +14,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "ciera.h"
@@ -2824,6 +2826,69 @@ __global__ __launch_bounds__(kThreads) void cache_update_kernel(const uint8_t* _
 }
 
 }  // namespace
+
+// ----------------------------------------------- encode without allocation
+// Scratch of ciera_encode_noalloc, for callers that cannot allocate: one copy
+// per device, held until the process ends.  In host code this name stands for
+// the array only as a symbol; its device address comes from
+// hipGetSymbolAddress (static_scratch), never from the name itself.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+// Descriptors travel as kernel arguments, kDescPack per launch.
+constexpr uint32_t kDescPack = 30;
+struct EncDescPack {
+  EncItem item[kDescPack];
+};
+static_assert(sizeof(EncDescPack) <= 3584, "descriptor pack must fit the kernel arguments");
+
+__global__ __launch_bounds__(kThreads) void enc_desc_kernel(EncDescPack p, EncItem* __restrict__ dst, uint32_t n,
+                                                            uint64_t* __restrict__ zero, uint64_t nzero,
+                                                            uint32_t* __restrict__ head, uint32_t batch_id) {
+  constexpr uint32_t W = sizeof(EncItem) / 4;
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x, step = gridDim.x * blockDim.x;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(p.item);
+  for (uint32_t i = t; i < n * W; i += step) gp(reinterpret_cast<uint32_t*>(dst))[i] = src[i];
+  for (uint64_t i = t; i < nzero; i += step) gp(zero)[i] = 0;
+  if (t == 0 && head) gp(head)[0] = batch_id;
+}
+
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices] = {};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_enc_desc(const EncItem* host_items, uint32_t n, EncItem* dst, uint64_t* zero, uint64_t nzero,
+                           uint32_t* head, uint32_t batch_id, hipStream_t s) {
+  uint32_t done = 0;
+  do {  // at least one launch: it also zeroes and writes the head
+    EncDescPack p;
+    const uint32_t k = std::min(kDescPack, n - done);
+    std::memcpy(p.item, host_items + done, sizeof(EncItem) * k);
+    (void)hipGetLastError();
+    const uint32_t blocks = done == 0 ? (uint32_t)std::min<uint64_t>(1024, std::max<uint64_t>(1, (nzero + kThreads - 1) / kThreads)) : 1u;
+    hipLaunchKernelGGL(enc_desc_kernel, dim3(blocks), dim3(kThreads), 0, s, p, dst + done, k,
+                       done == 0 ? zero : nullptr, done == 0 ? nzero : 0ull, done == 0 ? head : nullptr, batch_id);
+    if (hipError_t e = hipGetLastError()) return e;
+    done += k;
+  } while (done < n);
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------- launchers
 // Each launcher clears the thread's last-error state first, so that the error it

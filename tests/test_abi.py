@@ -241,3 +241,27 @@ def test_binding_rejects_tensors_it_would_misread():
         with pytest.raises(ValueError, match=msg):
             call()
     assert B._ptr(None) is None and B._ptr(0x1234) == 0x1234
+
+
+def test_noalloc_limits_without_device():
+    """ciera_encode_noalloc refuses, before any device call, what its static
+    scratch cannot hold or what needs a finishing kernel."""
+    t = L.Tensor(64, 64, 1, 512, 2)
+    it = L.encode_item(t, 0, 1, 0x10000, 0x20000, 0x30000, 64 + 32 * 64 * 2)
+    for compress, code in ((2, 3), (4, 1)):
+        bad = L.encode_item(t, 0, compress, 0x10000, 0x20000, 0x30000, 64 + 32 * 64 * 2)
+        with pytest.raises(L.CieraError) as e:
+            L.ciera_encode_noalloc([bad], stream=0)
+        assert e.value.code == code
+    big = L.Tensor(1 << 21, 1, 1, 512, 1)            # 256 tiles: needs a stash-free path, fits
+    huge = L.Tensor((1 << 21) + 1, 1, 1, 512, 1)     # 257 tiles: would need a finishing kernel
+    with pytest.raises(L.CieraError) as e:
+        L.ciera_encode_noalloc([L.encode_item(huge, 0, 1, 0x10000, 0x20000, 0x40000000, 1 << 26)], stream=0)
+    assert e.value.code == 3
+    assert L.ciera_encode_scratch_bytes([L.encode_item(big, 0, 1, 0x10000, 0x20000, 0x40000000, 1 << 26)]) \
+        < L._binding.CIERA_NOALLOC_SCRATCH_BYTES
+    many = [it] * 9000                                # descriptors alone beyond 1 MiB
+    assert L.ciera_encode_scratch_bytes(many) > L._binding.CIERA_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(L.CieraError) as e:
+        L.ciera_encode_noalloc(many, stream=0)
+    assert e.value.code == 2
