@@ -1,10 +1,14 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
 times (batched, prepared launches).
 
-At these sizes every output is checked on the GPU by properties that hold at
-any size (decode(encode(x)) == x bit for bit, cache == exponent field of x,
-no status bits), and sampled tensors are compared byte for byte with the
-oracle: all 16 streams, the rebuilt values and the cache."""
+Every stream of every rank and tensor is compared byte for byte with the
+oracle's (for the coded variant, whose oracle is pure Python, every header's
+size and change count are checked against counts made here, and sampled
+tensors byte for byte); the GPU's cache before each iteration is compared with
+the oracle's; every output is checked on the GPU by properties that hold at
+any size (decode(encode(x)) == x bit for bit, cache == exponent field of x, no
+status bits); sampled tensors' rebuilt values and caches are compared with the
+oracle's decode."""
 import numpy as np
 import pytest
 import torch
@@ -36,9 +40,10 @@ def exp_field_gpu(w: torch.Tensor) -> torch.Tensor:
 
 def run_layer(specs, w_prev, w_next, dtype, world, ppm, codec=None, sample=(), seed_cache=True,
               expect_modes=None, coded=False):
-    """Encode every rank (rank 0 prepared, the others one-shot), decode with the
-    prepared batch, check properties at full size and sampled tensors against
-    the oracle.  Returns the codec (cache carried) and a summary."""
+    """Encode every rank (rank 0 prepared, the others one-shot), compare every
+    stream with the oracle, decode with the prepared batch, check properties at
+    full size and sampled tensors' decode against the oracle.  Returns the
+    codec (cache carried) and a summary."""
     shapes = [(s.rows, s.cols) for s in specs]
     comp = [3] * len(specs) if coded else None  # coded patches for every tensor
     if codec is None:
@@ -48,10 +53,6 @@ def run_layer(specs, w_prev, w_next, dtype, world, ppm, codec=None, sample=(), s
     if seed_cache:
         codec.seed_cache(w_prev)
     torch.cuda.synchronize()
-    # the oracle's view of the cache before this iteration, for the sampled tensors
-    ocache = {i: O.cache_update(to_np(w_prev[i]), ODT[dtype]) for i in sample}
-    for i in sample:
-        assert np.array_equal(codec.cache_view(i).cpu().numpy(), ocache[i]), f"cache before, tensor {i}"
     for r in range(world):
         shards = []
         for i in range(len(specs)):
@@ -62,22 +63,35 @@ def run_layer(specs, w_prev, w_next, dtype, world, ppm, codec=None, sample=(), s
         else:
             codec.encode(r, shards, compress=comp)
     torch.cuda.synchronize()
-    # sampled streams against the oracle
-    o_streams = {}
-    for i in sample:
+    # every stream against the oracle, tensor by tensor; the cache the encode
+    # read (encode leaves it alone) against the oracle's cache of w_prev
+    ocache, o_streams = {}, {}
+    shift, em = {O.BF16: (7, 0xFF), O.FP32: (23, 0xFF), O.FP16: (10, 0x1F)}[ODT[dtype]]
+    for i in range(len(specs)):
         s = specs[i]
         x = to_np(w_next[i])
-        o_streams[i] = []
+        oc = O.cache_update(to_np(w_prev[i]), ODT[dtype])
+        assert np.array_equal(codec.cache_view(i).cpu().numpy(), oc), f"cache before, tensor {i}"
+        if i in sample:
+            ocache[i] = oc
+            o_streams[i] = []
         for r in range(world):
             off, n = O.shard(s.rows, s.cols, world, r)
-            if coded:
-                st = O.encode_coded(x[off:off + n], ocache[i][off:off + n], ODT[dtype], 512, True, off, r, world)
-            else:
-                st = O.encode(x[off:off + n], ocache[i][off:off + n], ODT[dtype], 512,
-                              bool(codec.plans[i].compress), off, r, world)
-            got = codec.slot(i, r)[:st.size].cpu().numpy()
-            assert np.array_equal(got, st), f"tensor {i} rank {r}: stream differs from the oracle"
-            o_streams[i].append(st)
+            if not coded or i in sample:
+                if coded:
+                    st = O.encode_coded(x[off:off + n], oc[off:off + n], ODT[dtype], 512, True, off, r, world)
+                else:
+                    st = O.encode(x[off:off + n], oc[off:off + n], ODT[dtype], 512,
+                                  bool(codec.plans[i].compress), off, r, world)
+                got = codec.slot(i, r)[:st.size].cpu().numpy()
+                assert np.array_equal(got, st), f"tensor {i} rank {r}: stream differs from the oracle"
+                if i in sample:
+                    o_streams[i].append(st)
+            else:  # coded, not sampled: the header's size and change count
+                hd = O.parse_header(codec.slot(i, r)[:64].cpu().numpy())
+                changed = int(np.count_nonzero(((x[off:off + n] >> shift) & em) != oc[off:off + n]))
+                assert hd["n"] == n and hd["n_changed"] == changed and hd["offset"] == off, \
+                    f"tensor {i} rank {r}: header {hd}"
     status = codec.decode()
     torch.cuda.synchronize()
     assert status.item() == 0, f"decode status {status.item()}"
