@@ -311,6 +311,15 @@ ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t c
                                     ciera_batch_t* batch, void* stream);
 ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream);
 
+/* ciera_decode_launch_bounded -- ciera_decode_launch from a grid of at most
+ * max_workgroups workgroups per kernel launch, each decoding tiles of 8192
+ * values in turn (0: one workgroup per tile, as ciera_decode_launch).  For a
+ * decode that runs beside other work on another stream [CIERA 3.3: the codec
+ * overlapped with communication and compute]: the bound caps the compute units
+ * the decode holds at once.  Same results; tensors flagged CIERA_TENSOR_CODED
+ * are decoded as by ciera_decode_launch. */
+ciera_status_t ciera_decode_launch_bounded(ciera_batch_t* batch, uint32_t max_workgroups, void* stream);
+
 /* ciera_hash_update -- the block-hash variant's sender state [CIERA 3.1;
  * Algorithm 1 (HashCache)]: for rank's shard of t (n_r values), hash_cache
  * receives the 128-bit hash of every block's exponents, 16 bytes per block

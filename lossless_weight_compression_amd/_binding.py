@@ -22,7 +22,7 @@ CIERA_NOALLOC_SCRATCH_BYTES = 1 << 20  # the static scratch of ciera_encode_noal
 EXPORTS = ["ciera_plan", "ciera_select", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
            "ciera_encode_prepare", "ciera_encode_launch", "ciera_decode_scratch_bytes",
            "ciera_decode", "ciera_decode_prepare", "ciera_decode_launch", "ciera_cache_update",
-           "ciera_hash_update", "ciera_set_sync_polls", "ciera_encode_noalloc",
+           "ciera_hash_update", "ciera_set_sync_polls", "ciera_encode_noalloc", "ciera_decode_launch_bounded",
            "ciera_status_str", "ciera_abi_version", "ciera_last_error"]
 
 
@@ -109,6 +109,7 @@ def _load() -> ctypes.CDLL:
         "ciera_decode_prepare": (c_int, [POINTER(DecodeItem), c_uint32, c_void_p, c_void_p, c_uint64,
                                          POINTER(Batch), c_void_p]),
         "ciera_decode_launch": (c_int, [POINTER(Batch), c_void_p]),
+        "ciera_decode_launch_bounded": (c_int, [POINTER(Batch), c_uint32, c_void_p]),
         "ciera_cache_update": (c_int, [POINTER(Tensor), c_void_p, c_void_p, c_void_p]),
         "ciera_hash_update": (c_int, [POINTER(Tensor), c_uint32, c_void_p, c_void_p, c_void_p]),
         "ciera_set_sync_polls": (None, [c_uint32]),
@@ -317,3 +318,8 @@ def ciera_decode_prepare(items: Sequence[DecodeItem], status, scratch, scratch_b
 
 def ciera_decode_launch(batch: Batch, stream=None) -> None:
     _check(_lib.ciera_decode_launch(byref(batch), _stream(stream)), "ciera_decode_launch")
+
+
+def ciera_decode_launch_bounded(batch: Batch, max_workgroups: int, stream=None) -> None:
+    _check(_lib.ciera_decode_launch_bounded(byref(batch), max_workgroups, _stream(stream)),
+           "ciera_decode_launch_bounded")

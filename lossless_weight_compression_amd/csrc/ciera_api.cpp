@@ -657,6 +657,10 @@ ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t c
 }
 
 ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream) {
+  return ciera_decode_launch_bounded(batch, 0, stream);
+}
+
+ciera_status_t ciera_decode_launch_bounded(ciera_batch_t* batch, uint32_t max_workgroups, void* stream) {
   if (!batch) return CIERA_ERR_INVALID_ARG;
   BatchImpl* b = impl(batch);
   if (b->magic != kDecMagic) return CIERA_ERR_INVALID_ARG;
@@ -665,7 +669,7 @@ ciera_status_t ciera_decode_launch(ciera_batch_t* batch, void* stream) {
   for (uint32_t gi = 0; gi < b->ngroups; ++gi) {
     const Group& g = b->g[gi];
     if (hipError_t e = launch_decode(g.dtype, g.unit, g.coded != 0, items, g.item0, g.nitems, g.tpr, g.world, b->status_dev,
-                                     b->batch_id, st))
+                                     b->batch_id, max_workgroups, st))
       return device_error("decode launch", e);
   }
   b->launches += 1;

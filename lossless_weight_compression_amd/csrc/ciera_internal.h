@@ -108,8 +108,11 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
 hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0, uint32_t nitems, uint32_t wg_per_item,
                                 const uint32_t* counts, const uint32_t* stash, uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s);
+// max_wg: 0, or a bound on the workgroups of each launch (each then decodes
+// tiles in turn; groups of tensors flagged coded ignore it)
 hipError_t launch_decode(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems,
-                         uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id, hipStream_t s);
+                         uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id, uint32_t max_wg,
+                         hipStream_t s);
 // The calling thread's current device's copy of the library's static scratch
 // array (kStaticScratchBytes, 256-byte aligned): its device address, looked up
 // once per device.

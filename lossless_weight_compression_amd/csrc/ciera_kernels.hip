@@ -2282,10 +2282,12 @@ __global__ __launch_bounds__(64) void coded_prepass_kernel(const DecItem* __rest
 // (sign|mantissa bytes and cached exponents) are issued before the header and
 // the patch range are known, so their latency overlaps that chain.
 
+// Decode of tile `bid` of a group: item bid / (tpr * world), rank, tile in
+// the rank's stream.  Workgroup-wide; every return is uniform.
 template <int DT, int U, bool CODED>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __restrict__ items, uint32_t item0,
-                                                          uint32_t tpr, uint32_t world, uint32_t* status_out,
-                                                          uint32_t batch_id) {
+__device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, uint32_t item0, uint32_t tpr,
+                                            uint32_t world, uint32_t* status_out, uint32_t batch_id,
+                                            uint32_t bid) {
   constexpr int E = Tr<DT>::E;
   constexpr uint32_t T = (uint32_t)kDecRow * U;
   constexpr uint32_t BMW = (T / 64 + 31) / 32;  // words of per-tile block bits (B >= 64)
@@ -2300,9 +2302,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t tpi = tpr * world;
-  const uint32_t blk = blockIdx.x / tpi;
+  const uint32_t blk = bid / tpi;
   const uint32_t item = item0 + blk;
-  const uint32_t rel = blockIdx.x - blk * tpi;
+  const uint32_t rel = bid - blk * tpi;
   const uint32_t r = rel / tpr;
   const uint32_t t_in = rel - r * tpr;
   const DecItem d = items[item];
@@ -2805,6 +2807,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   }
 }
 
+template <int DT, int U, bool CODED>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __restrict__ items, uint32_t item0,
+                                                          uint32_t tpr, uint32_t world, uint32_t* status_out,
+                                                          uint32_t batch_id) {
+  decode_tile<DT, U, CODED>(items, item0, tpr, world, status_out, batch_id, blockIdx.x);
+}
+
+// The same decode from a grid of fewer workgroups than tiles, each taking
+// tiles bid, bid + gridDim.x, ... in turn: a caller that runs the decode beside
+// other work bounds the compute units it occupies.
+template <int DT, int U>
+__global__ __launch_bounds__(kDecThreads) void decode_bounded_kernel(const DecItem* __restrict__ items, uint32_t item0,
+                                                                  uint32_t tpr, uint32_t world, uint32_t* status_out,
+                                                                  uint32_t batch_id, uint32_t ntiles) {
+  for (uint32_t t = blockIdx.x; t < ntiles; t += gridDim.x) {  // uniform
+    decode_tile<DT, U, false>(items, item0, tpr, world, status_out, batch_id, t);
+    __syncthreads();  // the next tile reuses the LDS
+  }
+}
+
 // -------------------------------------------------------------- cache update
 
 template <int DT>
@@ -2968,9 +2990,29 @@ hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs&
 
 static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems,
                                      uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id,
-                                     hipStream_t s) {
+                                     uint32_t max_wg, hipStream_t s) {
   (void)hipGetLastError();
-  const dim3 grid(nitems * tpr * world), block(kDecThreads);
+  const uint32_t ntiles = nitems * tpr * world;
+  if (max_wg && max_wg < ntiles && !coded) {  // a bounded grid walks the tiles
+    const dim3 bgrid(max_wg), block(kDecThreads);
+#define CIERA_DECB(DT, U) \
+  hipLaunchKernelGGL((decode_bounded_kernel<DT, U>), bgrid, block, 0, s, items, item0, tpr, world, status, batch_id, ntiles)
+    switch (dtype * 8 + u) {
+      case 9: CIERA_DECB(1, 1); break;
+      case 10: CIERA_DECB(1, 2); break;
+      case 12: CIERA_DECB(1, 4); break;
+      case 17: CIERA_DECB(2, 1); break;
+      case 18: CIERA_DECB(2, 2); break;
+      case 20: CIERA_DECB(2, 4); break;
+      case 25: CIERA_DECB(3, 1); break;
+      case 26: CIERA_DECB(3, 2); break;
+      case 28: CIERA_DECB(3, 4); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef CIERA_DECB
+    return hipGetLastError();
+  }
+  const dim3 grid(ntiles), block(kDecThreads);
   const dim3 pgrid(nitems * world * ((tpr * (uint32_t)u + 3) / 4));  // coded prepass: four chunk slots each
 #define CIERA_DEC(DT, U)                                                                                    \
   do {                                                                                                      \
@@ -3013,14 +3055,14 @@ static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem
 }
 
 hipError_t launch_decode(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems, uint32_t tpr,
-                         uint32_t world, uint32_t* status, uint32_t batch_id,
+                         uint32_t world, uint32_t* status, uint32_t batch_id, uint32_t max_wg,
                          hipStream_t s) {
   const uint64_t tpi = (uint64_t)tpr * world;
   if (tpi * kDecThreads >= ((uint64_t)1 << 32)) return hipErrorInvalidValue;  // one item alone too large
   const uint32_t per = (uint32_t)std::max<uint64_t>(1, kMaxGrid / tpi);
   for (uint32_t i = 0; i < nitems; i += per) {
     if (hipError_t e = launch_decode_part(dtype, u, coded, items, item0 + i, std::min(per, nitems - i), tpr, world, status,
-                                          batch_id, s))
+                                          batch_id, max_wg, s))
       return e;
   }
   return hipSuccess;

@@ -153,15 +153,16 @@ class LayerCodec:
         items = items if items is not None else self.encode_items(rank, shards, compress)
         B.ciera_encode(items, self.encode_scratch(items), stream=stream)
 
-    def decode(self, stream=None, zero_status: bool = True) -> torch.Tensor:
+    def decode(self, stream=None, zero_status: bool = True, max_workgroups: int = 0) -> torch.Tensor:
         """Rebuild every tensor from its W slots and update the cache (one launch of
-        the prepared decode batch; its tables are uploaded on the first call)."""
+        the prepared decode batch; its tables are uploaded on the first call).
+        max_workgroups > 0 bounds the decode's grid (ciera_decode_launch_bounded)."""
         if zero_status:
             self.status.zero_()
         if self._dec_batch is None:
             self._dec_batch = B.ciera_decode_prepare(self._dec_items, self.status, self.dec_scratch,
                                                      stream=stream)
-        B.ciera_decode_launch(self._dec_batch, stream=stream)
+        B.ciera_decode_launch_bounded(self._dec_batch, max_workgroups, stream=stream)
         return self.status
 
     def prepare_encode(self, rank: int, shards: Sequence[torch.Tensor],
