@@ -71,6 +71,9 @@ def parse():
                          "kernel for scaling HBM byte counters)")
     ap.add_argument("--overlap", action="store_true",
                     help="measure the step alone, a bf16 GEMM alone and both on two streams")
+    ap.add_argument("--decode-grid", type=int, default=0,
+                    help="bound the decode's grid to this many workgroups (ciera_decode_launch_bounded; "
+                         "0: one per tile)")
     ap.add_argument("--gemm", type=int, nargs=3, default=[8192, 8192, 8192], metavar=("M", "N", "K"),
                     help="GEMM shape of --overlap and --pipeline")
     ap.add_argument("--pipeline", action="store_true",
@@ -454,6 +457,7 @@ def setup(args):
         f"(ratio {raw_bytes / stream_bytes:.4f}), {'BLOCK' if block else 'CODED' if coded else 'COMPRESSED'} streams "
         f"{int((hA['mode'] != 0).sum())}/{len(hA['mode'])}")
 
+    grid = getattr(args, "decode_grid", 0)  # bound on the decode's workgroups (0: one per tile)
     # prepared launches (tables uploaded once)
     plans_expected = [p.compress for p in A.plans]
     encA = A.prepare_encode(0, shards(w1, 0), compress=comp)
@@ -470,7 +474,7 @@ def setup(args):
         enc.launch(stream)
         if ev is not None:
             ev[1].record(stream)
-        codec.decode(stream, zero_status=False)
+        codec.decode(stream, zero_status=False, max_workgroups=grid)
         if ev is not None:
             ev[2].record(stream)
 
@@ -486,7 +490,7 @@ def setup(args):
         (encA if k % 2 == 0 else encB).launch(stream)
 
     def decode_only(k, stream):
-        (A if k % 2 == 0 else Bc).decode(stream, zero_status=False)
+        (A if k % 2 == 0 else Bc).decode(stream, zero_status=False, max_workgroups=grid)
 
     def release():
         """Drop the device buffers this workload holds."""
@@ -556,7 +560,7 @@ def overlap(args):
         "value": round(hidden, 4), "unit": "fraction", "higher_is_better": True, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "dtype": "u16+bf16", "data": "synthetic",
         "config": {"workload": workload_name(args),
-                   "change_frac": args.frac, "gemm_mnk": [M, Nn, K],
+                   "change_frac": args.frac, "gemm_mnk": [M, Nn, K], "decode_grid": args.decode_grid,
                    "streams": "GEMM on one stream, step on a second stream (default priorities)"},
         "gemm": dict(res["gemm"], tflops=round(flops / (tg * 1e-6) / 1e12, 1)),
         "step": res["step"], "both": res["both"],
