@@ -107,6 +107,18 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// min(k, n - x) for x < n, else 0 -- the values of a chunk, row or tile that
+// starts at x in a shard of n -- with a saturating subtraction instead of a
+// guarded one.  Written as `x < n ? min(k, n - x) : 0`, hipcc speculated the
+// guarded `n - x` into every thread as `sub nuw` feeding a `noundef` umin call;
+// constraint elimination then took n >= x as a fact for every thread, also for
+// threads past the shard's end, and folded the length of the first row of a
+// partial last tile to a whole row.  A saturating subtraction has no guard to
+// speculate and no wrap flag to reason from.
+__device__ __forceinline__ uint64_t left_in(uint64_t n, uint64_t x, uint64_t k) {
+  return min<uint64_t>(k, __builtin_elementwise_sub_sat(n, x));
+}
+
 // --------------------------------------------------------------- 16-value I/O
 
 // 16 values starting at p (p = base + c0*E, 16-byte aligned when cnt == 16).
@@ -669,7 +681,7 @@ __device__ __forceinline__ void tile_block_hashes(const uint32_t (&ex)[S][4], ui
     const uint64_t b0 = c0 & ~(uint64_t)(B - 1);  // the block's first value
     const uint32_t lc = (uint32_t)((c0 - b0) >> 4);
     L[s] = b0 < n ? min<uint64_t>(B, n - b0) : 0;
-    const uint32_t valid = L[s] > 16ull * lc ? (uint32_t)min<uint64_t>(16, L[s] - 16ull * lc) : 0u;
+    const uint32_t valid = (uint32_t)left_in(L[s], 16ull * lc, 16);
     uint64_t ta, tb;
     chunk_hash_terms(ex[s], lc, valid, ta, tb);
     ha[s] = group_sum(ta, g);
@@ -727,7 +739,7 @@ __device__ __forceinline__ void split_tile_block(const EncItem& d, uint32_t loca
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-    cnt[s] = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
+    cnt[s] = (int)left_in(n, c0, 16);
     if (cnt[s] > 0) load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
     ch[s][0] = ch[s][1] = 0;
     if ((c0 & (B - 1)) == 0 && c0 < n) {
@@ -764,7 +776,7 @@ __device__ __forceinline__ void split_tile_block(const EncItem& d, uint32_t loca
     }
   }
   __syncthreads();
-  const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
+  const uint64_t in_tile = left_in(n, base, T);
   const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
   if (tid == 0) {
     uint32_t c = 0;
@@ -816,7 +828,7 @@ __global__ __launch_bounds__(kThreads) void hash_seed_kernel(const uint8_t* __re
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-    const int cnt = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
+    const int cnt = (int)left_in(n, c0, 16);
     expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
     if (cnt > 0) {
       load_words<XW>(x + c0 * E, (uint32_t)cnt * E, true, xw[s]);
@@ -864,16 +876,8 @@ constexpr uint32_t kRansLow = 1u << 16;
 __device__ __forceinline__ uint32_t pad4u(uint32_t v) { return (v + 3u) & ~3u; }
 __device__ __forceinline__ uint32_t rans_lanes(uint32_t c) { return min(64u, (c + 3u) / 4u); }
 
-// Length of the row starting at value r0 of a shard of n values (0 past it),
-// with n passed through an empty asm statement so that the compiler cannot
-// fold the result from what it assumed about full tiles: it once compiled a
-// dense first row of the last, partial tile with the full row length.
-__device__ __forceinline__ uint32_t row_len(uint64_t n, uint64_t r0) {
-  uint32_t lo = (uint32_t)n, hi = (uint32_t)(n >> 32);
-  asm volatile("" : "+v"(lo), "+v"(hi));
-  const uint64_t m = lo | ((uint64_t)hi << 32);
-  return r0 < m ? (uint32_t)min<uint64_t>(kSub, m - r0) : 0u;
-}
+// Length of the row starting at value r0 of a shard of n values (0 past it).
+__device__ __forceinline__ uint32_t row_len(uint64_t n, uint64_t r0) { return (uint32_t)left_in(n, r0, kSub); }
 
 // Bytes of a chunk's data from its changes, words and form.
 __device__ __forceinline__ uint32_t coded_bytes(uint32_t c, uint32_t words, bool dense, uint32_t len) {
@@ -1025,7 +1029,7 @@ __device__ __forceinline__ void split_tile_coded(const EncItem& d, uint32_t loca
 #pragma unroll
     for (int r = 0; r < P2; ++r) {
       const uint64_t c0 = base + (uint64_t)(s0 + r) * kSub + (uint64_t)tid * kEPT;
-      const int cnt = c0 < n ? (int)min<uint64_t>(16, n - c0) : 0;
+      const int cnt = (int)left_in(n, c0, 16);
       uint32_t xw[XW];
       mask[r] = 0;
       expk[r][0] = expk[r][1] = expk[r][2] = expk[r][3] = 0;
@@ -1101,7 +1105,7 @@ __device__ __forceinline__ void split_tile_coded(const EncItem& d, uint32_t loca
   // bitmap bytes of the tile's blocks (a tile spans whole bitmap bytes), when
   // they lie inside the RAW length (otherwise the stream cannot be coded)
   const uint64_t smsec = sm_sec<DT>(n);
-  const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
+  const uint64_t in_tile = left_in(n, base, T);
   const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
   const uint64_t nbm = (((n + B - 1) >> lb) + 7) / 8;
   if (smsec + nbm <= n * E && tid < (tblocks + 7) / 8) {
@@ -1238,7 +1242,7 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-      cnt[s] = full ? 16 : (c0 < n ? (int)min<uint64_t>(16, n - c0) : 0);
+      cnt[s] = full ? 16 : ((int)left_in(n, c0, 16));
       if (cnt[s] > 0) {
         load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
         load_words<4, kNtBulk<DT>>(d.cache + c0, (uint32_t)cnt[s], full || d.cache_aligned != 0, cw[s]);
@@ -1358,7 +1362,7 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
   if (!cmode || P == 0) return;
 
   // the tile's bitmap bytes (a tile spans whole bitmap bytes)
-  const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
+  const uint64_t in_tile = left_in(n, base, T);
   const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
   const uint32_t tbytes = (tblocks + 7) / 8;
   if (tid < tbytes) {
@@ -1443,7 +1447,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
 #pragma unroll
     for (int s = 0; s < S; ++s) {  // all loads of the tile first
       const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-      cnt[s] = FULL ? 16 : (c0 < n ? (int)min<uint64_t>(16, n - c0) : 0);
+      cnt[s] = FULL ? 16 : ((int)left_in(n, c0, 16));
       if (cnt[s] > 0) {
         load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
         load_words<4, kNtBulk<DT>>(d.cache + c0, (uint32_t)cnt[s], FULL || caligned, cw[s]);
@@ -1504,7 +1508,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
   const uint64_t nbm = (nb + 7) / 8;
   const uint64_t smsec = sm_sec<DT>(n);
   if (smsec + nbm + 5 <= n * E) {
-    const uint64_t in_tile = min<uint64_t>(T, n > base ? n - base : 0);
+    const uint64_t in_tile = left_in(n, base, T);
     const uint32_t tblocks = (uint32_t)((in_tile + B - 1) >> lb);
     const uint32_t tbytes = (tblocks + 7) / 8;
     if (tid < tbytes) {
@@ -1560,7 +1564,7 @@ __device__ void rederive_tile(const EncItem& d, uint64_t j, uint32_t r0, uint64_
   uint32_t run = r0;
   for (uint32_t row = 0; row < d.tvals / kSub; ++row) {  // uniform
     const uint64_t c0 = j * d.tvals + (uint64_t)row * kSub + (uint64_t)tid * kEPT;
-    const int cnt = c0 < d.n ? (int)min<uint64_t>(16, d.n - c0) : 0;
+    const int cnt = (int)left_in(d.n, c0, 16);
     uint32_t xw[XW], cw[4], expk[4], mask = 0;
     if (cnt > 0) {
       load_words<XW>(d.x + c0 * E, (uint32_t)cnt * E, true, xw);
@@ -1824,7 +1828,7 @@ __device__ void finish_tile_coded(const FinArgs& f, const EncItem& d, uint32_t l
     const uint32_t w = info[r];
     const uint32_t c = w & 0x1FFFu, words = (w >> 13) & 0x1FFFu;
     const bool dense = (w >> 26) & 1u;
-    const uint32_t len = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
+    const uint32_t len = (uint32_t)left_in(n, k * kSub, kSub);
     const uint32_t bytes = coded_bytes(c, words, dense, len);
     uint8_t* dst = d.stream + dpos + cb;
     if (bytes > 0 && dense) {
@@ -2227,7 +2231,7 @@ __global__ __launch_bounds__(64) void coded_prepass_kernel(const DecItem* __rest
       const G1 uint32_t* e = gp(reinterpret_cast<const uint32_t*>(st + tpos + 8 * k));
       const uint32_t cc = e[0], cb = e[1], pc = k > 0 ? e[-2] : 0u;
       pb = k > 0 ? e[-1] : 0u;
-      len = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
+      len = (uint32_t)left_in(n, k * kSub, kSub);
       if (chunk_entry_ok(pc, pb, cc, cb, k, nch, len, h_tot - dpos, P) && cc > pc && cb - pb != pad4u(len) &&
           cc - pc <= len * E / 4) {  // coded, and its records fit
         c = cc - pc;
@@ -2327,7 +2331,7 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
-    cnt[u] = c0 < te ? (int)min<uint64_t>(16, te - c0) : 0;
+    cnt[u] = (int)left_in(te, c0, 16);
     if (cnt[u] > 0) {
       load_smw<DT, SW>(st + kHeader, c0, cnt[u], sw[u]);
       load_words<4, kNtBulk<DT>>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
@@ -2460,7 +2464,7 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
           const G1 uint32_t* ent = gp(reinterpret_cast<const uint32_t*>(st + tpos + 8 * k));
           const uint32_t cc = ent[0], cb = ent[1];
           const uint32_t pc = k > 0 ? ent[-2] : 0u, pb = k > 0 ? ent[-1] : 0u;
-          len[u] = (uint32_t)min<uint64_t>(kSub, n - k * kSub);
+          len[u] = (uint32_t)left_in(n, k * kSub, kSub);
           if (!chunk_entry_ok(pc, pb, cc, cb, k, nch, len[u], D, P)) {
             e |= CIERA_ST_LENGTH;
             continue;
@@ -2838,7 +2842,7 @@ __global__ __launch_bounds__(kThreads) void cache_update_kernel(const uint8_t* _
   for (uint64_t ch = (uint64_t)blockIdx.x * kThreads + threadIdx.x; ch < chunks;
        ch += (uint64_t)gridDim.x * kThreads) {
     const uint64_t c0 = ch * 16;
-    const int cnt = (int)min<uint64_t>(16, n - c0);
+    const int cnt = (int)left_in(n, c0, 16);
     uint32_t v[16], ex[4] = {0, 0, 0, 0};
     load16<DT>(w + c0 * E, cnt, v);
 #pragma unroll

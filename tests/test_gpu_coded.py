@@ -153,6 +153,41 @@ def test_partial_first_row_of_last_tile(dtype, tail, tail_changes):
     assert g == 0 and o == 0
 
 
+# (B, row of the last tile that the partial chunk opens, dtype): tiles hold
+# S = max(2, B / 512) rows; the shard is q * S + row whole chunks and a
+# partial one, so the partial chunk is row `row` of its tile (rows 1..S-1)
+PARTIAL_ROWS = ([(1024, 1, torch.bfloat16)] + [(2048, r, torch.bfloat16) for r in (1, 2, 3)]
+                + [(4096, r, torch.bfloat16) for r in range(1, 8)]
+                + [(2048, 3, torch.float32), (4096, 5, torch.float16), (4096, 7, torch.float32)])
+
+
+@pytest.mark.parametrize("dense", [True, False])
+@pytest.mark.parametrize("blk,row,dtype", PARTIAL_ROWS)
+def test_partial_chunk_at_every_row_of_the_last_tile(blk, row, dtype, dense):
+    """The partial chunk of a shard at each later row of the last encode tile,
+    dense by its count (more than 1024 changes) or coded, among whole chunks
+    with 40 changes each; the stream's total length and bytes must equal the
+    oracle's.  (The length of a partial row was once folded to a whole row's
+    when the partial chunk opened the tile.)"""
+    S = max(2, blk // 512)
+    nch = S + row
+    tail, tail_changes = (2295, 1697) if dense else (3000, 40)
+    world = 2
+    per = nch * 4096 + tail
+    spec = W.TensorSpec("t", per * world, 1)
+    w0 = W.base_weights(spec, W.tensor_seed("rows", str(dtype), blk, row, dense), dtype)
+    rng = np.random.default_rng(blk + 17 * row + dense)
+    m = torch.zeros(per * world, dtype=torch.bool)
+    for r in range(world):
+        for k in range(nch):
+            m[r * per + k * 4096 + torch.from_numpy(rng.choice(4096, 40, replace=False))] = True
+        m[r * per + nch * 4096 + torch.from_numpy(rng.choice(tail, tail_changes, replace=False))] = True
+    w1 = exponent_steps(w0, m, [1, -1], W.tensor_seed("rows-p", str(dtype), blk, row))
+    say(f"[gpu] coded partial chunk at row {row} of {S}, B={blk} {dtype} dense={dense}")
+    g, o = run_block([(per * world, 1)], dtype, world, blk, [w0], [w1], variant=[B.CODED])
+    assert g == 0 and o == 0
+
+
 @pytest.mark.parametrize("frac", [0.0, 0.001, 0.01, 0.1])
 def test_coded_olmoe_expert_mixed_with_other_modes(frac):
     """One OLMoE expert, 16 ranks, in one batch: gate coded, up with element
