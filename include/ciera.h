@@ -93,7 +93,7 @@ typedef enum {
   CIERA_ERR_INVALID_ARG = 1,      /* null / misaligned pointer, bad dtype, B, world, rank */
   CIERA_ERR_BUFFER_TOO_SMALL = 2, /* stream capacity, slot or scratch too small */
   CIERA_ERR_UNSUPPORTED = 3,      /* a shard of >= 2^32 values, sizes beyond 2^48, or a CODED
-                                     shard of more than 256 encode tiles */
+                                     shard of 2^31 values or more */
   CIERA_ERR_DEVICE = 4            /* a HIP runtime call failed */
 } ciera_status_t;
 
@@ -194,8 +194,9 @@ typedef struct {
   uint32_t rank;              /* < t.world */
   uint32_t compress;          /* 0 always RAW; 1 COMPRESSED (the plan's decision); 2 the
                                  block-hash variant (BLOCK); 3 CODED (t.flags must hold
-                                 CIERA_TENSOR_CODED; shards of at most 256 encode tiles,
-                                 e.g. 2^21 values at B <= 1024); each subject to the
+                                 CIERA_TENSOR_CODED; shards of fewer than 2^31 values,
+                                 so that the chunk table's u32 byte counts hold
+                                 their data); each subject to the
                                  length rule */
   const void* shard;          /* n_r values of t.dtype; 16-byte aligned */
   const uint8_t* cache_full;  /* compress 0/1/3: N = rows*cols cached exponents; [off_r, off_r+n_r)

@@ -215,8 +215,9 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     const uint64_t T = (uint64_t)kSub * S;
     const uint64_t tpi = std::max<uint64_t>(1, (n + T - 1) / T);
     const uint32_t coded = it.compress == kCoded ? 1u : 0u;
-    // coded patches are finished one workgroup per tile, kThreads tiles per item at most
-    if (coded && tpi > (uint64_t)kThreads) return CIERA_ERR_UNSUPPORTED;
+    // coded: the chunk table's u32 running byte counts hold the data of every
+    // chunk of the shard, 4096 bytes each at most
+    if (coded && n >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
     by[std::make_tuple(it.t.dtype, S, (uint32_t)tpi, coded, self_finished(it.compress, tpi) ? 1u : 0u)].push_back(i);
   }
   if (by.size() > (size_t)kMaxGroups) return CIERA_ERR_UNSUPPORTED;
@@ -523,7 +524,7 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
     const Group& g = b->g[gi];
     if (g.self) continue;  // finished by its own tiles
     hipError_t e;
-    if (g.tpi <= (uint32_t)kThreads) {
+    if (g.tpi <= (uint32_t)kThreads || g.coded) {
       FinArgs f{};
       f.items = items;
       f.counts = counts;
@@ -533,6 +534,11 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
       f.item0 = g.item0;
       f.tpi = g.tpi;
       f.cap = stash_cap(g.unit, g.coded != 0);
+      if (g.tpi > (uint32_t)kThreads) {  // coded items of many tiles: prefixes first, in the sync words
+        uint64_t* prefix = reinterpret_cast<uint64_t*>(b->scratch + b->off_sync);
+        f.prefix = prefix;
+        if ((e = launch_coded_scan(g.dtype, g.nitems, f, prefix, b->batch_id, st))) return device_error("encode scan launch", e);
+      }
       e = launch_encode_finish_tiles(g.dtype, g.nitems, f, b->batch_id, st);
     } else {
       e = launch_encode_finish(g.dtype, items, g.item0, g.nitems, b->fin_wg, counts, stash, b->batch_id, st);

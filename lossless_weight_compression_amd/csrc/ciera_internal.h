@@ -95,6 +95,8 @@ struct FinArgs {
   const EncItem* items;
   const uint32_t* counts;
   const uint32_t* stash;
+  const uint64_t* prefix;  // coded items of more than kThreads tiles: the scan kernel's per-tile
+                           // prefixes (indexed like counts); else null
   uint64_t tile0;   // the group's first tile (index into counts)
   uint64_t stash0;  // word offset of the group's first tile stash
   uint32_t item0, tpi, cap, pad;
@@ -108,6 +110,8 @@ hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, 
 hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0, uint32_t nitems, uint32_t wg_per_item,
                                 const uint32_t* counts, const uint32_t* stash, uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s);
+hipError_t launch_coded_scan(int dtype, uint32_t nitems, const FinArgs& f, uint64_t* prefix, uint32_t batch_id,
+                             hipStream_t s);
 // max_wg: 0, or a bound on the workgroups of each launch (each then decodes
 // tiles in turn; groups of tensors flagged coded ignore it)
 hipError_t launch_decode(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems,

@@ -1777,25 +1777,36 @@ __device__ void finish_tile_coded(const FinArgs& f, const EncItem& d, uint32_t l
   constexpr int E = Tr<DT>::E;
   __shared__ uint64_t s_r[2 * (kThreads / 64)];
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const uint32_t c_t = tid < f.tpi ? gp(f.counts)[t0 + tid] : 0u;
-  const uint32_t by = c_t & 0xFFFFu, ch = c_t >> 16;
-  uint64_t vb = by | ((uint64_t)(tid < local ? by : 0u) << 32);
-  uint64_t vc = ch | ((uint64_t)(tid < local ? ch : 0u) << 32);
+  // sb, sc: the item's data bytes and changes (low half) and those of the
+  // tiles before this one (high half)
+  uint64_t sb, sc;
+  if (f.prefix) {  // items of more than kThreads tiles: prefixes from the scan kernel
+    const G1 uint64_t* pre = gp(f.prefix + t0);
+    const uint64_t mine = pre[local], last = pre[f.tpi - 1];
+    const uint32_t c_last = gp(f.counts)[t0 + f.tpi - 1];
+    sb = ((uint32_t)last + (c_last & 0xFFFFu)) | ((mine & 0xFFFFFFFFull) << 32);
+    sc = ((uint32_t)(last >> 32) + (c_last >> 16)) | ((mine >> 32) << 32);
+  } else {
+    const uint32_t c_t = tid < f.tpi ? gp(f.counts)[t0 + tid] : 0u;
+    const uint32_t by = c_t & 0xFFFFu, ch = c_t >> 16;
+    uint64_t vb = by | ((uint64_t)(tid < local ? by : 0u) << 32);
+    uint64_t vc = ch | ((uint64_t)(tid < local ? ch : 0u) << 32);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    vb += __shfl_xor(vb, o);
-    vc += __shfl_xor(vc, o);
-  }
-  if (lane == 0) {
-    s_r[wave] = vb;
-    s_r[kThreads / 64 + wave] = vc;
-  }
-  __syncthreads();
-  uint64_t sb = 0, sc = 0;
+    for (int o = 32; o > 0; o >>= 1) {
+      vb += __shfl_xor(vb, o);
+      vc += __shfl_xor(vc, o);
+    }
+    if (lane == 0) {
+      s_r[wave] = vb;
+      s_r[kThreads / 64 + wave] = vc;
+    }
+    __syncthreads();
+    sb = sc = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
-    sb += s_r[w];
-    sc += s_r[kThreads / 64 + w];
+    for (int w = 0; w < kThreads / 64; ++w) {
+      sb += s_r[w];
+      sc += s_r[kThreads / 64 + w];
+    }
   }
   const uint64_t Dtot = (uint32_t)sb, P = (uint32_t)sc;
   const uint64_t n = d.n;
@@ -1848,6 +1859,32 @@ __device__ void finish_tile_coded(const FinArgs& f, const EncItem& d, uint32_t l
       e[0] = (uint32_t)cc;
       e[1] = (uint32_t)cb;
     }
+  }
+}
+
+// Coded items of more than kThreads tiles: the exclusive prefixes of the
+// tiles' data bytes and changes over each item, a window of kThreads tiles at
+// a time (one workgroup per item): prefix[t] = bytes before | changes before
+// << 32, for the finishing kernel's workgroups to read.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void coded_scan_kernel(FinArgs f, uint64_t* prefix, uint32_t batch_id) {
+  __shared__ uint64_t s_red[kThreads / 64];
+  const uint32_t tid = threadIdx.x;
+  const EncItem d = f.items[f.item0 + blockIdx.x];
+  if (d.batch_id != batch_id) return;  // uniform
+  const uint64_t t0 = f.tile0 + (uint64_t)blockIdx.x * f.tpi;
+  uint64_t run_b = 0, run_c = 0;
+  for (uint32_t w0 = 0; w0 < f.tpi; w0 += kThreads) {  // uniform
+    const uint32_t k = w0 + tid;
+    const uint32_t c = k < f.tpi ? gp(f.counts)[t0 + k] : 0u;
+    // a window's sums stay below 2^24, so the two halves never carry
+    const uint64_t v = (c & 0xFFFFu) | ((uint64_t)(c >> 16) << 32);
+    uint64_t tot;
+    const uint64_t ex = block_scan<uint64_t>(v, s_red, tot);
+    if (k < f.tpi) gp(prefix + t0)[k] = (run_b + (uint32_t)ex) | ((run_c + (ex >> 32)) << 32);
+    run_b += (uint32_t)tot;
+    run_c += tot >> 32;
+    __syncthreads();  // s_red is read before the next window writes it
   }
 }
 
@@ -2971,6 +3008,23 @@ hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0,
   else if (dtype == 3) hipLaunchKernelGGL((encode_finish_kernel<3>), grid, block, 0, s, items, item0, nitems, counts, stash, batch_id);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_coded_scan(int dtype, uint32_t nitems, const FinArgs& f, uint64_t* prefix, uint32_t batch_id,
+                             hipStream_t s) {
+  for (uint32_t i = 0; i < nitems; i += 65535u) {
+    (void)hipGetLastError();
+    FinArgs c = f;
+    c.item0 = f.item0 + i;
+    c.tile0 = f.tile0 + (uint64_t)i * f.tpi;
+    const dim3 grid(std::min(65535u, nitems - i)), block(kThreads);
+    if (dtype == 1) hipLaunchKernelGGL((coded_scan_kernel<1>), grid, block, 0, s, c, prefix, batch_id);
+    else if (dtype == 2) hipLaunchKernelGGL((coded_scan_kernel<2>), grid, block, 0, s, c, prefix, batch_id);
+    else if (dtype == 3) hipLaunchKernelGGL((coded_scan_kernel<3>), grid, block, 0, s, c, prefix, batch_id);
+    else return hipErrorInvalidValue;
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s) {

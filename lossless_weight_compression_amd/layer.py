@@ -129,7 +129,7 @@ class LayerCodec:
                      compress: Optional[Sequence[int]] = None) -> List[B.EncodeItem]:
         """compress[i]: 0 RAW, 1 COMPRESSED (default: the plan's), 2 the block-hash
         variant, which reads and updates rank's hash cache of tensor i, 3
-        entropy-coded patches (shards of at most 256 encode tiles)."""
+        entropy-coded patches (shards of fewer than 2^31 values)."""
         items = []
         for i, t in enumerate(self.tensors):
             c = self.plans[i].compress if compress is None else compress[i]

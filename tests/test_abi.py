@@ -186,7 +186,8 @@ def test_scratch_sizes_grow_with_work():
 
 def test_coded_patch_arguments_without_device():
     """compress = 3 needs the tensor flag CIERA_TENSOR_CODED; unknown flag bits
-    are invalid; a coded shard of more than 256 encode tiles is unsupported."""
+    are invalid; a coded shard of 2^31 values or more is unsupported (its chunk
+    table's u32 byte counts could overflow)."""
     with pytest.raises(L.CieraError) as e:
         L.ciera_plan(L.Tensor(4, 4, 1, 512, 1, flags=2), 100)
     assert e.value.code == 1
@@ -198,8 +199,10 @@ def test_coded_patch_arguments_without_device():
 
     flag = L.CIERA_TENSOR_CODED
     assert scratch(L.Tensor(2048, 1024, 1, 512, 1, flags=flag), 3) > 0          # 256 tiles of 8192 values
+    assert scratch(L.Tensor(2049, 1024, 1, 512, 1, flags=flag), 3) > 0          # 257 tiles: scanned first
+    assert scratch(L.Tensor((1 << 31) - 1, 1, 1, 512, 1, flags=flag), 3) > 0
     with pytest.raises(L.CieraError) as e:
-        scratch(L.Tensor(2049, 1024, 1, 512, 1, flags=flag), 3)                  # 257 tiles
+        scratch(L.Tensor(1 << 31, 1, 1, 512, 1, flags=flag), 3)
     assert e.value.code == 3
     assert scratch(L.Tensor(2049, 1024, 1, 512, 1), 1) > 0                      # element patches: any size
     # coded tiles keep a 4096-byte region per chunk row plus 8 info words

@@ -63,7 +63,12 @@ CODED_EDGE = [
     (96, 4096, 2, 4096, torch.float16, 0.0, (1,), ()),
     (1000, 1000, 16, 512, torch.bfloat16, 0.01, (1, -1), ()),
     (7168, 1, 16, 512, torch.bfloat16, 0.001, (1, -1), ()),
-    (2048, 1024, 1, 512, torch.bfloat16, 0.01, (1, -1), ()),            # 256 tiles: the most allowed
+    (2048, 1024, 1, 512, torch.bfloat16, 0.01, (1, -1), ()),            # 256 tiles: one reduction
+    (2101, 4096, 1, 512, torch.bfloat16, 0.01, (1, -1), ()),            # 1051 tiles: prefixes scanned
+    (2049, 1024, 1, 2048, torch.float16, 0.002, (1, -1, 3),             # 129 tiles of 16384 values,
+     ((0, 20000, 0.4), (2049 * 1024 - 5000, 2049 * 1024, 0.5))),        # dense runs at both ends
+    (3001, 1024, 3, 512, torch.float32, 0.005, (1, -1), ()),            # 126 tiles per rank, 3 ranks
+    (1200, 4096, 1, 512, torch.bfloat16, 0.3, (1, -1), ()),             # 601 tiles, RAW: not shorter
     (256, 1024, 1, 512, torch.bfloat16, 0.005, (1, -1),                 # dense chunks among coded ones
      ((4096, 8192, 0.6), (40000, 41000, 0.9), (262144 - 4096, 262144, 0.3))),
     (256, 1024, 1, 512, torch.bfloat16, 0.02, (1, -1, 3, -3, 50, 128), ()),  # many escapes
