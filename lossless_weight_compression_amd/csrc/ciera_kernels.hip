@@ -623,6 +623,33 @@ __device__ __forceinline__ void put_record(uint8_t* stream, uint64_t capacity, u
   }
 }
 
+// A thread's consecutive patch records -- the changes of one 16-value chunk
+// (mask), indices idx0 + bit, exponents from expk -- at 5-byte places from
+// byte pos of the stream.  Each record but the last goes out as one unaligned
+// 8-byte store that also carries the next record's first three bytes (the
+// next store rewrites them with the same values); the last as a 4-byte and a
+// 1-byte store, so no store reaches past the thread's own records.  gfx950
+// stores to global memory at any byte alignment.
+typedef uint32_t u32_any __attribute__((aligned(1)));
+typedef uint64_t u64_any __attribute__((aligned(1)));
+__device__ __forceinline__ void put_records(uint8_t* stream, uint64_t pos, uint32_t mask, uint32_t idx0,
+                                            const uint32_t expk[4]) {
+  if (!mask) return;
+  int j = __ffs(mask) - 1;
+  mask &= mask - 1;
+  while (mask) {
+    const int jn = __ffs(mask) - 1;
+    mask &= mask - 1;
+    const uint64_t v = (uint64_t)(idx0 + (uint32_t)j) | ((uint64_t)byte_of(expk, j) << 32) |
+                       ((uint64_t)((idx0 + (uint32_t)jn) & 0xFFFFFFu) << 40);
+    *(G1 u64_any*)(stream + pos) = v;
+    pos += 5;
+    j = jn;
+  }
+  *(G1 u32_any*)(stream + pos) = idx0 + (uint32_t)j;
+  gp(stream)[pos + 4] = (uint8_t)byte_of(expk, j);
+}
+
 // ----------------------------------------------- block-hash variant (encode)
 // [CIERA 3.1; Algorithm 1] as published: a 128-bit hash per block of B values
 // (two 64-bit halves from SplitMix64's output function), compared with the
@@ -1386,19 +1413,12 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
     gp(d.stream)[kHeader + smsec + (base >> (lb + 3)) + tid] = (uint8_t)byte;
   }
 
-  // the tile's records at their places in the patch list
+  // the tile's records at their places in the patch list (all inside comp)
   const uint64_t pbase = kHeader + smsec + nbm;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    uint32_t m = mask[s];
-    uint64_t g = (uint64_t)excl + before[s] + lpre[s];
-    const uint32_t rel0 = (uint32_t)s * kSub + tid * kEPT;
-    while (m) {
-      const int j = __ffs(m) - 1;
-      m &= m - 1;
-      put_record(d.stream, comp, pbase + 5 * g, (uint32_t)(base + rel0 + (uint32_t)j), byte_of(expk[s], j));
-      ++g;
-    }
+    const uint64_t g = (uint64_t)excl + before[s] + lpre[s];
+    put_records(d.stream, pbase + 5 * g, mask[s], (uint32_t)(base + (uint64_t)s * kSub + tid * kEPT), expk[s]);
   }
 }
 
