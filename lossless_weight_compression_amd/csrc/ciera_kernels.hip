@@ -1572,7 +1572,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
 // Tiles per window of the finishing kernel: counts are scanned in LDS a window
 // at a time.
 constexpr uint32_t kWin = 1024;
-constexpr uint64_t kGridMax = 2048;  // decode: longest patch list searched from a plain grid
+constexpr uint64_t kGridMax = 64;  // decode: longest patch list searched from a plain grid (one round)
 
 // Writes the patch records of tile j of item d (tvals values) again from the
 // shard and the cache, the first one as record number r0.  Workgroup-wide.
@@ -2621,8 +2621,8 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
     }
   } else {
   // 3. COMPRESSED: this tile's patch range [lo, hi).  Every wave finds it on its
-  //    own (two searches sharing a first round of 64 probes, then 32 lanes per
-  //    key), so the records can be read without a barrier in between.
+  //    own (two searches: a first round of 64 probes, then 32 lanes per key),
+  //    so the records can be read without a barrier in between.
   const uint64_t recs = kHeader + sm_sec<DT>(n) + nbm;
   uint32_t lo = 0, hi = 0;
   if (P > 0) {
@@ -2632,8 +2632,7 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
       uint64_t a0 = 0, z0 = 0, a1 = 0, z1 = 0;  // first p with idx[p] >= key lies in [a, z]
       {
         if (P <= kGridMax) {
-          // First round: 64 probes spread over the whole list; two rounds in
-          // all find both keys while P <= 64 * 32.
+          // Short lists: 64 probes, one per record, find both keys at once.
           const uint64_t step = (P + 63) / 64;
           const uint64_t p = (uint64_t)lane * step;
           uint32_t idx = 0, ex = 0;
@@ -2642,50 +2641,45 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
           if (m0) { a0 = (uint64_t)(63u - (uint32_t)__clzll(m0)) * step + 1; z0 = min<uint64_t>(P, a0 - 1 + step); }
           if (m1) { a1 = (uint64_t)(63u - (uint32_t)__clzll(m1)) * step + 1; z1 = min<uint64_t>(P, a1 - 1 + step); }
         } else {
-          // Longer lists: 32 lanes per key (lanes 0-31: ts, 32-63: te).  16
-          // lanes probe a window centred where the key falls if the changes
-          // are spread evenly (P * key / n), spaced so that it spans about
-          // +-3 standard deviations of that count (sqrt(P) / 2 at most); 16
-          // lanes probe every G-th record of the whole list, so a key outside
-          // the window (clustered changes) is still narrowed to G records.
-          // The answer lies in both intervals; at even change rates the next
-          // round ends the search, one round earlier than a grid alone.
-          // (Float estimates suffice: n < 2^32, and only the probe places,
-          // not the answer, depend on them.)
+          // Longer lists: 32 lanes per key (lanes 0-31: ts, 32-63: te) probe a
+          // window centred where the key falls if the changes are spread
+          // evenly (P * key / n), S records apart, so that it spans at least
+          // +-3 standard deviations of that count (sqrt(P) / 2 at most).  At
+          // even change rates the next round ends the search, and a tile
+          // touches only the lines around its own records: a grid over the
+          // whole list would bring every line of it into the L2 of each XCD
+          // that runs one of the stream's tiles.  A key outside its window
+          // (clustered changes) is left in [0, w] or past the window, and the
+          // rounds below narrow that 32-fold each.  (Float estimates suffice:
+          // n < 2^32, and only the probe places, not the answer, depend on
+          // them.)
           const uint32_t Pu = (uint32_t)P;
-          const uint64_t G = (P + 15) >> 4;
-          const uint32_t S = (uint32_t)(0.19f * __builtin_amdgcn_sqrtf((float)Pu)) + 1u;
+          const uint32_t S = (uint32_t)(0.095f * __builtin_amdgcn_sqrtf((float)Pu)) + 1u;
           const float fr = (float)Pu * __builtin_amdgcn_rcpf((float)(uint32_t)n);
           uint32_t w[2];
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const uint32_t e = min(Pu, (uint32_t)(fr * (float)(uint32_t)(k ? te : ts)));
-            w[k] = e > 8u * S ? e - 8u * S : 0u;
+            w[k] = e > 16u * S ? e - 16u * S : 0u;
           }
           const bool second = lane >= 32;
           const uint32_t key = (uint32_t)(second ? te : ts);
-          const uint32_t i = lane & 15u;
-          const uint64_t p = (lane & 16u) == 0 ? (uint64_t)(second ? w[1] : w[0]) + (uint64_t)i * S : (uint64_t)i * G;
+          const uint64_t p = (uint64_t)(second ? w[1] : w[0]) + (uint64_t)(lane & 31u) * S;
           uint32_t idx = 0, ex = 0;
           if (p < P) read_rec(st, recs, p, idx, ex);
           const uint64_t m = __ballot(p < P && idx < key);
           uint64_t a[2], z[2];
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
-            const uint32_t hw = (uint32_t)(m >> (32 * k)) & 0xFFFFu, hg = (uint32_t)(m >> (32 * k + 16)) & 0xFFFFu;
-            uint64_t wa = 0, wz = w[k], ga = 0, gz = 0;
-            if (hw) {
-              const uint32_t top = 31u - (uint32_t)__clz(hw);
-              wa = (uint64_t)w[k] + (uint64_t)top * S + 1;
-              wz = top == 15u ? P : min<uint64_t>(P, wa - 1 + S);
+            const uint32_t h = (uint32_t)(m >> (32 * k));
+            if (h) {  // past probe `top`; at or before the next one (or the end)
+              const uint32_t top = 31u - (uint32_t)__clz(h);
+              a[k] = (uint64_t)w[k] + (uint64_t)top * S + 1;
+              z[k] = top == 31u ? P : min<uint64_t>(P, a[k] - 1 + S);
+            } else {  // at or before the window's first probe
+              a[k] = 0;
+              z[k] = w[k];
             }
-            if (hg) {
-              const uint32_t top = 31u - (uint32_t)__clz(hg);
-              ga = (uint64_t)top * G + 1;
-              gz = top == 15u ? P : min<uint64_t>(P, ga - 1 + G);
-            }
-            a[k] = max(wa, ga);
-            z[k] = min(wz, gz);
           }
           a0 = a[0]; z0 = max(z[0], a[0]); a1 = a[1]; z1 = max(z[1], a[1]);
         }

@@ -148,19 +148,26 @@ def test_many_tiles_and_stash_overflow(rows, cols, dtype, B, dense):
     assert h["mode"] == O.MODE_COMPRESSED and h["n_changed"] > 0
 
 
-# Decode searches of long patch lists (more than 2048 records in a stream),
-# whose first round probes around the place an even spread predicts: shards of
-# 256 decode tiles (2048 x 1024 at one rank) whose changes are spread evenly,
-# or sit far from where an even spread puts them.  (name, uniform rate,
-# (first tile, last tile, rate) of denser regions in 8192-value tiles)
+# Decode searches of patch lists longer than 64 records, whose first round
+# probes a window around the place an even spread predicts: shards of 256
+# decode tiles (2048 x 1024 at one rank) whose changes are spread evenly, or
+# sit far from where an even spread puts them, so that most keys fall outside
+# their windows; lists from just above 64 records to above 2048.  (name,
+# uniform rate, (first tile, last tile, rate) of denser regions in 8192-value
+# tiles)
 LONG_LISTS = [
     ("even-10pct", 0.10, ()),
     ("even-1.5pct", 0.015, ()),
+    ("even-0.05pct", 0.0005, ()),
     ("first-tiles-only", 0.0, ((0, 1, 0.6),)),
     ("last-tile-only", 0.0, ((255, 255, 0.6),)),
     ("middle-cluster", 0.0005, ((100, 103, 0.6),)),
     ("every-eighth-tile", 0.0, tuple((t, t, 0.3) for t in range(3, 256, 8))),
     ("two-ends", 0.0, ((0, 0, 0.5), (250, 255, 0.2))),
+    ("one-tile-short-list", 0.0, ((100, 100, 0.1),)),
+    ("first-tile-short-list", 0.0, ((0, 0, 0.05),)),
+    ("last-tile-short-list", 0.0, ((255, 255, 0.05),)),
+    ("just-above-64", 0.0, ((10, 10, 0.01),)),
 ]
 
 
@@ -180,7 +187,7 @@ def test_long_patch_lists(name, frac, dense):
     res = case.run([w0], [w1], compress=[1])
     assert res["status"] == 0 and res["ostatus"] == 0
     h = O.parse_header(case.codec.slot(0, 0).cpu().numpy())
-    assert h["mode"] == O.MODE_COMPRESSED and h["n_changed"] > 2048
+    assert h["mode"] == O.MODE_COMPRESSED and h["n_changed"] > 64
 
 
 def test_specials_and_all_bf16_patterns():
