@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define CIERA_ABI_VERSION 3u
+#define CIERA_ABI_VERSION 4u
 #define CIERA_HEADER_BYTES 64u
 
 typedef enum { CIERA_BF16 = 1, CIERA_FP32 = 2, CIERA_FP16 = 3 } ciera_dtype_t;
@@ -274,14 +274,24 @@ void ciera_set_sync_polls(uint32_t polls);
 #define CIERA_NOALLOC_SCRATCH_BYTES 1048576u
 ciera_status_t ciera_encode_noalloc(const ciera_encode_item_t* items, uint32_t count, void* stream);
 
-/* The W received streams of one tensor. */
+/* The W received streams of one tensor, in one of two layouts: W slots of one
+ * buffer (`streams`, what a fixed-slot Allgather delivers), or W buffers
+ * anywhere (`rank_streams`, one per sending rank). */
 typedef struct {
   ciera_tensor_t t;
-  const uint8_t* streams; /* rank r's stream starts at streams + r*slot_bytes; 16-byte aligned */
+  const uint8_t* streams; /* rank r's stream starts at streams + r*slot_bytes; 16-byte aligned.
+                             NULL when rank_streams is given */
   uint64_t slot_bytes;    /* multiple of 16, >= the RAW length of rank 0's shard
-                             (ciera_plan's max_stream_bytes): every slot can hold any stream */
+                             (ciera_plan's max_stream_bytes): every slot can hold any stream.
+                             With rank_streams: the bytes readable at each rank's pointer */
   void* out_full;         /* N values, rebuilt; 16-byte aligned */
   uint8_t* cache_full;    /* N bytes: exponents of the previous iteration, updated in place */
+  const uint8_t* const* rank_streams; /* optional host array of t.world device pointers: rank r's
+                             stream at rank_streams[r], 16-byte aligned, slot_bytes readable
+                             there; none of the W ranges may overlap out_full or cache_full
+                             (they may overlap each other).  The pointers are copied into the
+                             decode scratch by ciera_decode / ciera_decode_prepare; the array
+                             need not outlive the call.  NULL: the slot layout of `streams` */
 } ciera_decode_item_t;
 
 /* ciera_decode_scratch_bytes -- device scratch ciera_decode needs for this batch. */
@@ -299,8 +309,11 @@ ciera_status_t ciera_decode_scratch_bytes(const ciera_decode_item_t* items, uint
  * memory outside the item's buffers touched.  For a CODED stream the decode
  * first writes each coded chunk's changes as 4-byte records at the start of
  * that chunk's part of out_full, then overwrites them with the values.
- * out_full, the cache and the W slots must not overlap: INVALID_ARG.
- * `items` is a host array.  Scratch as for encode. */
+ * out_full, the cache and the W slots (or the W rank_streams ranges) must not
+ * overlap: INVALID_ARG; so are both or neither of streams and rank_streams
+ * set, and a null or misaligned rank pointer.  `items` is a host array.
+ * Scratch as for encode (ciera_decode_scratch_bytes counts 8 bytes per rank
+ * pointer). */
 ciera_status_t ciera_decode(const ciera_decode_item_t* items, uint32_t count,
                             uint32_t* status_dev, void* scratch, uint64_t scratch_bytes,
                             void* stream);

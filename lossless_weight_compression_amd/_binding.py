@@ -66,7 +66,7 @@ class EncodeItem(ctypes.Structure):
 
 class DecodeItem(ctypes.Structure):
     _fields_ = [("t", Tensor), ("streams", c_void_p), ("slot_bytes", c_uint64),
-                ("out_full", c_void_p), ("cache_full", c_void_p)]
+                ("out_full", c_void_p), ("cache_full", c_void_p), ("rank_streams", c_void_p)]
 
 
 class Batch(ctypes.Structure):
@@ -250,13 +250,25 @@ def encode_item(t: Tensor, rank: int, compress: int, shard, cache_full, stream_b
                       _u8(stream_buf, "stream", 0), cap)
 
 
-def decode_item(t: Tensor, streams, slot_bytes: int, out_full, cache_full) -> DecodeItem:
+def decode_item(t: Tensor, streams, slot_bytes: int, out_full, cache_full, rank_streams=None) -> DecodeItem:
+    """The W streams of t either as W slots of slot_bytes in `streams`, or,
+    with streams None, as `rank_streams`: one buffer (or address) per rank,
+    each of at least slot_bytes bytes.  The item keeps the host array of rank
+    pointers alive."""
     N = t.rows * t.cols
-    return DecodeItem(t, _u8(streams, "streams", slot_bytes * t.world),
+    ranks = None
+    if rank_streams is not None:
+        if len(rank_streams) != t.world:
+            raise ValueError(f"rank_streams: {len(rank_streams)} buffers, expected {t.world}")
+        ranks = (c_void_p * t.world)(*[_u8(b, f"rank_streams[{r}]", slot_bytes) for r, b in enumerate(rank_streams)])
+    item = DecodeItem(t, _u8(streams, "streams", slot_bytes * t.world),
                       slot_bytes,
                       _ptr(out_full, "out_full", None if out_full is None or isinstance(out_full, int)
                            else _torch_dtype(t.dtype), N),
-                      _u8(cache_full, "cache", N))
+                      _u8(cache_full, "cache", N),
+                      None if ranks is None else ctypes.cast(ranks, c_void_p).value)
+    item._ranks = ranks
+    return item
 
 
 def ciera_encode(items: Sequence[EncodeItem], scratch, scratch_bytes: Optional[int] = None,

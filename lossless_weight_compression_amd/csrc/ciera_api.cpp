@@ -256,7 +256,7 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
 struct DecPlan {
   std::vector<uint32_t> order;
   std::vector<Group> groups;
-  uint64_t off_items = 0, total = 0;
+  uint64_t off_items = 0, off_ranks = 0, total = 0;  // ranks: the items' rank pointers, 8 bytes each
 };
 
 ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count, DecPlan* pl) {
@@ -288,8 +288,12 @@ ciera_status_t dec_layout(const ciera_decode_item_t* items, uint32_t count, DecP
     pl->order.insert(pl->order.end(), kv.second.begin(), kv.second.end());
     pl->groups.push_back(g);
   }
+  uint64_t nptr = 0;
+  for (uint32_t i = 0; i < count; ++i)
+    if (items[i].rank_streams) nptr += items[i].t.world;
   pl->off_items = 256;
-  pl->total = align_up(pl->off_items + sizeof(DecItem) * (uint64_t)count, 256);
+  pl->off_ranks = align_up(pl->off_items + sizeof(DecItem) * (uint64_t)count, 256);
+  pl->total = align_up(pl->off_ranks + 8 * nptr, 256);
   return CIERA_OK;
 }
 
@@ -616,29 +620,46 @@ ciera_status_t ciera_decode_prepare(const ciera_decode_item_t* items, uint32_t c
     const ciera_decode_item_t& it = items[i];
     uint64_t off, n0;
     shard_of(&it.t, 0, &off, &n0);
-    if (!it.streams || !aligned(it.streams, 16)) return CIERA_ERR_INVALID_ARG;
+    if ((it.streams != nullptr) == (it.rank_streams != nullptr)) return CIERA_ERR_INVALID_ARG;
+    if (it.streams && !aligned(it.streams, 16)) return CIERA_ERR_INVALID_ARG;
     if (it.slot_bytes % 16 != 0) return CIERA_ERR_INVALID_ARG;
     if (it.slot_bytes < kHeader + n0 * elem_bytes(it.t.dtype)) return CIERA_ERR_BUFFER_TOO_SMALL;
     if (it.t.rows * it.t.cols && (!it.out_full || !aligned(it.out_full, 16) || !it.cache_full))
       return CIERA_ERR_INVALID_ARG;
     // the rebuilt values, the cache and the streams are disjoint
-    const uint64_t N = it.t.rows * it.t.cols;
-    const unsigned __int128 sb = (unsigned __int128)it.slot_bytes * it.t.world;
-    const uint64_t slen = sb > (unsigned __int128)UINT64_MAX ? UINT64_MAX : (uint64_t)sb;
-    if (overlap(it.out_full, N * elem_bytes(it.t.dtype), it.cache_full, N) ||
-        overlap(it.out_full, N * elem_bytes(it.t.dtype), it.streams, slen) ||
-        overlap(it.cache_full, N, it.streams, slen))
-      return CIERA_ERR_INVALID_ARG;
+    const uint64_t N = it.t.rows * it.t.cols, obytes = N * elem_bytes(it.t.dtype);
+    if (overlap(it.out_full, obytes, it.cache_full, N)) return CIERA_ERR_INVALID_ARG;
+    if (it.streams) {
+      const unsigned __int128 sb = (unsigned __int128)it.slot_bytes * it.t.world;
+      const uint64_t slen = sb > (unsigned __int128)UINT64_MAX ? UINT64_MAX : (uint64_t)sb;
+      if (overlap(it.out_full, obytes, it.streams, slen) || overlap(it.cache_full, N, it.streams, slen))
+        return CIERA_ERR_INVALID_ARG;
+    } else {
+      for (uint32_t r = 0; r < it.t.world; ++r) {
+        const uint8_t* p = it.rank_streams[r];
+        if (!p || !aligned(p, 16)) return CIERA_ERR_INVALID_ARG;
+        if (overlap(it.out_full, obytes, p, it.slot_bytes) || overlap(it.cache_full, N, p, it.slot_bytes))
+          return CIERA_ERR_INVALID_ARG;
+      }
+    }
   }
   BatchImpl* b = impl(batch);
   b->batch_id = next_id();
   std::vector<uint8_t> blob(pl.total, 0);
   reinterpret_cast<uint32_t*>(blob.data())[0] = b->batch_id;
   DecItem* di = reinterpret_cast<DecItem*>(blob.data() + pl.off_items);
+  uint64_t nptr = 0;  // rank pointers placed so far
   for (uint32_t j = 0; j < count; ++j) {
     const ciera_decode_item_t& it = items[pl.order[j]];
     DecItem& d = di[j];
     d.streams = it.streams;
+    d.ranks = nullptr;
+    if (it.rank_streams) {
+      const uint64_t at = pl.off_ranks + 8 * nptr;
+      std::memcpy(blob.data() + at, it.rank_streams, 8 * (size_t)it.t.world);
+      d.ranks = reinterpret_cast<const uint8_t* const*>(static_cast<uint8_t*>(scratch) + at);
+      nptr += it.t.world;
+    }
     d.slot = it.slot_bytes;
     d.out = static_cast<uint8_t*>(it.out_full);
     d.cache = it.cache_full;

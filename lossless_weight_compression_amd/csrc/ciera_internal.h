@@ -54,8 +54,9 @@ struct EncItem {
 
 // One decode item: a tensor and its W receive slots.
 struct DecItem {
-  const uint8_t* streams;
-  uint64_t slot;
+  const uint8_t* streams;          // rank r's stream at streams + r * slot, when ranks is null
+  const uint8_t* const* ranks;     // else at ranks[r] (world pointers in the batch's scratch)
+  uint64_t slot;                   // bytes readable at every rank's stream
   uint8_t* out;
   uint8_t* cache;
   uint64_t q;              // rows / world: rows of every rank ...

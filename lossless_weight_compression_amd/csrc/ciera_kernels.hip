@@ -2237,6 +2237,12 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
   return err;
 }
 
+// Rank r's received stream of a decode item: in the item's slot layout, or at
+// the pointer the caller gave for that rank (read from the batch's scratch).
+__device__ __forceinline__ const uint8_t* rank_stream(const DecItem& d, uint32_t r) {
+  return d.ranks ? gp(d.ranks)[r] : d.streams + (uint64_t)r * d.slot;
+}
+
 // Coded rows decoded ahead of the merge, so that many resident waves hide the
 // decoder's dependent steps.  One wave per four consecutive chunk slots of a
 // rank's stream (U rows per decode tile): when each of the four chunks is small
@@ -2271,7 +2277,7 @@ __global__ __launch_bounds__(64) void coded_prepass_kernel(const DecItem* __rest
   const uint64_t n = (d.q + (r < d.rem ? 1u : 0u)) * d.cols;
   const uint64_t nch = (n + kSub - 1) / kSub;
   if (k0 >= nch) return;
-  const uint8_t* st = d.streams + (uint64_t)r * d.slot;
+  const uint8_t* st = rank_stream(d, r);
   const uint32_t B = d.block_size;
   const uint32_t lb = (uint32_t)__ffs(B) - 1u;
   const uint64_t nb = (n + B - 1) >> lb, nbm = (nb + 7) / 8;
@@ -2376,7 +2382,7 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
   const uint64_t ts = (uint64_t)t_in * T;
   if (ts >= n && t_in != 0) return;  // past this shard (uniform)
   const uint64_t te = min<uint64_t>(n, ts + T);
-  const uint8_t* st = d.streams + (uint64_t)r * d.slot;
+  const uint8_t* st = rank_stream(d, r);
   const uint32_t B = d.block_size;
   const uint32_t lb = (uint32_t)__ffs(B) - 1u;  // B is a power of two (checked by the API)
   const bool aligned = (off & 15u) == 0;

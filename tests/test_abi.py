@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert L.ciera_abi_version() == 3
+    assert L.ciera_abi_version() == 4
     assert L.ciera_status_str(0) == "ok"
     assert "buffer" in L.ciera_status_str(2)
 
@@ -172,6 +172,41 @@ def test_overlapping_buffers_are_rejected_without_device():
         with pytest.raises(L.CieraError) as e:
             L.ciera_decode([di], 0x800000, 0x900000, L.ciera_decode_scratch_bytes([di]), stream=0)
         assert e.value.code == 1, kw
+
+
+def test_rank_stream_pointers_without_device():
+    """Decode items whose W streams sit in W separate buffers (rank_streams):
+    exactly one of streams and rank_streams; every rank pointer non-null and
+    16-byte aligned; no rank's range may overlap the rebuilt values or the
+    cache; the scratch holds 8 bytes per rank pointer.  All refused on the host
+    before any device call (fake addresses)."""
+    t = L.Tensor(64, 64, 1, 512, 2)               # 2 ranks of 32x64 bf16
+    slot = 64 + 32 * 64 * 2 + 16
+    ranks = [0x100000, 0x140000]
+    ok = dict(streams=None, rank_streams=ranks, out_full=0x200000, cache=0x300000)
+    bad = [dict(streams=0x180000),                          # both layouts
+           dict(rank_streams=None),                         # neither
+           dict(rank_streams=[0x100000, 0x140008]),         # misaligned rank pointer
+           dict(rank_streams=[0x100000, 0]),                # null rank pointer
+           dict(rank_streams=[0x100000, 0x200000 + 8192 - 16]),   # rank 1 ends past the values' start
+           dict(rank_streams=[0x300000 - slot + 16, 0x140000])]   # rank 0 runs into the cache
+    for kw in bad:
+        a = dict(ok, **kw)
+        di = L.decode_item(t, a["streams"], slot, a["out_full"], a["cache"], rank_streams=a["rank_streams"])
+        with pytest.raises(L.CieraError) as e:
+            L.ciera_decode([di], 0x800000, 0x900000, L.ciera_decode_scratch_bytes([di]), stream=0)
+        assert e.value.code == 1, kw
+    with pytest.raises(ValueError):
+        L.decode_item(t, None, slot, 0x200000, 0x300000, rank_streams=[0x100000])
+    # 8 bytes per rank pointer, past the descriptors
+    t16 = L.Tensor(64, 64, 1, 512, 16)
+    slot16 = 64 + 4 * 64 * 2 + 16
+    d_slots = L.decode_item(t16, 0x100000, slot16, 0x200000, 0x300000)
+    d_ranks = L.decode_item(t16, None, slot16, 0x200000, 0x300000,
+                            rank_streams=[0x400000 + 0x1000 * r for r in range(16)])
+    base = L.ciera_decode_scratch_bytes([d_slots] * 40)
+    more = L.ciera_decode_scratch_bytes([d_ranks] * 40)
+    assert more - base >= 40 * 16 * 8 and (more - base) % 256 == 0
 
 
 def test_scratch_sizes_grow_with_work():
