@@ -39,9 +39,11 @@ __device__ __forceinline__ v4u ldg16(const void* p) { return *gp(reinterpret_cas
 // Non-temporal 16-byte load: for data read once (the bulk streams), which
 // then does not displace reused lines.  Used where a wave's 16-byte loads of
 // a chunk row cover whole 128-byte lines between them with at most two loads
-// per thread (bf16, fp16: 16 or 32 bytes per thread).  fp32 threads read 48 or
-// 64 contiguous bytes with three or four strided loads; non-temporal there
-// measured 15% slower (decode) and 19% slower (encode), so fp32 loads normally.
+// per thread: contiguous pieces, and bf16 and fp16 chunks (16 or 32 bytes per
+// thread).  A thread's 48 or 64 contiguous fp32 bytes, read with three or four
+// strided loads, measured 15% slower (decode) and 19% slower (encode) with
+// non-temporal loads, so those load normally; the hot paths read fp32 rows as
+// contiguous pieces instead (load_sm_pieces, load_x_pieces).
 template <int DT>
 constexpr bool kNtBulk = DT != 2;
 __device__ __forceinline__ v4u ldg16_nt(const void* p) {
@@ -368,6 +370,61 @@ __device__ __forceinline__ void load_smw(const uint8_t* sec, uint64_t c0, int cn
   }
 }
 
+// fp32 and fp16 sign|mantissa records are 3 and 11/8 bytes per value, so a
+// thread's 16-value chunk (48 or 22 bytes) is not a whole number of 16-byte
+// pieces and its loads would be strided across the wave: every instruction
+// would touch each line in part, and non-temporal loads then fetch lines
+// again.  A wave whose 1024 values of a row are all inside the shard reads its
+// row's records (3072 or 1408 bytes, 16-byte aligned) as contiguous pieces
+// instead -- lane t takes pieces t, t + 64 and t + 128 -- so that each load
+// covers whole lines, and the lanes then swap them through LDS.
+template <int DT>
+constexpr int kSmPieces = DT == 2 ? 3 : DT == 3 ? 2 : 0;  // 16-byte pieces per lane
+template <int DT>
+constexpr uint32_t kSmWaveRow = 1024u * Tr<DT>::SMBITS / 8;  // record bytes of a wave's row
+template <int DT>
+__device__ __forceinline__ void load_sm_pieces(const uint8_t* p, v4u pc[kSmPieces<DT> ? kSmPieces<DT> : 1]) {
+  const uint32_t lane = lane_id();
+#pragma unroll
+  for (int q = 0; q < kSmPieces<DT>; ++q) {
+    const uint32_t k = 64u * q + lane;
+    if (16u * k < kSmWaveRow<DT>) pc[q] = ldg16_nt(p + 16 * k);
+  }
+}
+// The pieces to `stage` (the wave's own kSmWaveRow bytes of LDS) and back as
+// this lane's chunk words, as load_smw gives them.  LDS accesses of one wave
+// complete in order; the wave barriers keep the compiler from moving them.
+template <int DT, int SW>
+__device__ __forceinline__ void swap_sm_pieces(uint32_t* stage, const v4u pc[kSmPieces<DT> ? kSmPieces<DT> : 1],
+                                               uint32_t w[SW]) {
+  const uint32_t lane = lane_id();
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < kSmPieces<DT>; ++q) {
+    const uint32_t k = 64u * q + lane;
+    if (16u * k < kSmWaveRow<DT>) *reinterpret_cast<v4u*>(stage + 4 * k) = pc[q];
+  }
+  __builtin_amdgcn_wave_barrier();
+  if constexpr (DT == 2) {  // 48 bytes at 48 * lane
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const v4u a = *reinterpret_cast<const v4u*>(stage + 12 * lane + 4 * q);
+      w[4 * q] = a.x; w[4 * q + 1] = a.y; w[4 * q + 2] = a.z; w[4 * q + 3] = a.w;
+    }
+  } else {  // fp16: 22 bytes at 22 * lane, as 6 aligned words shifted when it starts mid-word
+    const uint32_t b = 22u * lane, sh = b & 3u;
+    const uint32_t* q = stage + (b >> 2);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) w[i] = q[i];
+    if (sh) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) w[i] = (w[i] >> 16) | (w[i + 1] << 16);
+      w[5] >>= 16;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // sign|mantissa of value j from the raw words of a 16-value chunk (fp16: the
 // chunk's bit stream starting at bit 0 of w[0]).
 template <int DT>
@@ -585,6 +642,70 @@ __device__ __forceinline__ void store_sm_words(uint8_t* p, int cnt, const uint32
     for (int b = 0; b < 22; ++b)
       if (b < nb) gp(p)[b] = (uint8_t)(o[b >> 2] >> (8 * (b & 3)));
   }
+}
+
+// The encode's side of the same exchange: a wave's 1024 values of a chunk row
+// (2048 or 4096 bytes, 16-byte aligned) loaded as contiguous 16-byte pieces,
+// lane t taking pieces t + 64q, and swapped through `stage` (the wave's own
+// kXWaveRow bytes of LDS) into each lane's 16 values; and a wave's fp32 or
+// fp16 sign|mantissa records, 48 or 22 bytes per lane, put together in
+// `stage` and stored as contiguous pieces.  LDS accesses of one wave complete
+// in order; the wave barriers keep the compiler from moving them.
+template <int DT>
+constexpr uint32_t kXWaveRow = 1024u * Tr<DT>::E;
+template <int DT>
+__device__ __forceinline__ void load_x_pieces(const uint8_t* p, v4u pc[Tr<DT>::E]) {
+  const uint32_t lane = lane_id();
+#pragma unroll
+  for (int q = 0; q < Tr<DT>::E; ++q) pc[q] = ldg16_nt(p + 16 * (64u * q + lane));
+}
+template <int DT>
+__device__ __forceinline__ void swap_x_pieces(uint32_t* stage, const v4u pc[Tr<DT>::E], uint32_t xw[4 * Tr<DT>::E]) {
+  constexpr int E = Tr<DT>::E;
+  const uint32_t lane = lane_id();
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < E; ++q) *reinterpret_cast<v4u*>(stage + 4 * (64u * q + lane)) = pc[q];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    const v4u a = *reinterpret_cast<const v4u*>(stage + 4 * E * lane + 4 * q);
+    xw[4 * q] = a.x; xw[4 * q + 1] = a.y; xw[4 * q + 2] = a.z; xw[4 * q + 3] = a.w;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+template <int DT>
+__device__ __forceinline__ void store_sm_pieces(uint8_t* p, uint32_t* stage, const uint32_t o[kSmWords<DT>]) {
+  static_assert(DT == 2 || DT == 3, "fp32 and fp16 only");
+  constexpr uint32_t R = kSmWaveRow<DT>;
+  const uint32_t lane = lane_id();
+  __builtin_amdgcn_wave_barrier();
+  if constexpr (DT == 2) {  // 48 bytes at 48 * lane
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      v4u a;
+      a.x = o[4 * q]; a.y = o[4 * q + 1]; a.z = o[4 * q + 2]; a.w = o[4 * q + 3];
+      *reinterpret_cast<v4u*>(stage + 12 * lane + 4 * q) = a;
+    }
+  } else {  // 22 bytes at 22 * lane: whole words, and a half-word at one end
+    const uint32_t b = 22u * lane;
+    if ((b & 3u) == 0) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) stage[(b >> 2) + i] = o[i];
+      reinterpret_cast<uint16_t*>(stage)[(b + 20) >> 1] = (uint16_t)o[5];
+    } else {  // b = 4q + 2
+      reinterpret_cast<uint16_t*>(stage)[b >> 1] = (uint16_t)o[0];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) stage[((b + 2) >> 2) + i] = (o[i] >> 16) | (o[i + 1] << 16);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = 0; q < (int)((R / 16 + 63) / 64); ++q) {
+    const uint32_t k = 64u * q + lane;
+    if (16u * k < R) stg16(p + 16 * k, *reinterpret_cast<const v4u*>(stage + 4 * k));
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
 // Exclusive prefix of v over the workgroup's threads in thread order, and the
@@ -1249,6 +1370,7 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
   __shared__ uint32_t s_sum[2];      // the item's changes, those of the tiles before
   __shared__ uint32_t s_miss[kSelfTiles / 32];  // tiles whose counts did not come in time
   __shared__ uint32_t s_red[kThreads / 64];
+  __shared__ uint32_t s_stage[kThreads / 64][kXWaveRow<DT> / 4];  // each wave's exchange of pieces
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint64_t base = (uint64_t)local * T;
@@ -1260,23 +1382,30 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
   if (tid == 0) mine_old = __hip_atomic_load(sync + local, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // loads, split and compare; the section words stay in registers until the
-  // mode is known (a RAW stream reads its values again)
+  // mode is known (a RAW stream reads its values again).  A wave whose 1024
+  // values of row s are all in the shard loads them as contiguous pieces.
   uint32_t smw[S][kSmWords<DT>], mask[S], expk[S][4];
   int cnt[S];
+  bool whole[S];  // uniform per wave
   {
     uint32_t xw[S][XW], cw[S][4];
+    v4u pc[S][E];
     const bool full = d.cache_aligned != 0 && base + T <= n;  // uniform
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+      const uint64_t w0 = base + (uint64_t)s * kSub + (uint64_t)wave * 1024u;
+      whole[s] = w0 + 1024u <= n;
       cnt[s] = full ? 16 : ((int)left_in(n, c0, 16));
       if (cnt[s] > 0) {
-        load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
-        load_words<4, kNtBulk<DT>>(d.cache + c0, (uint32_t)cnt[s], full || d.cache_aligned != 0, cw[s]);
+        if (whole[s]) load_x_pieces<DT>(d.x + w0 * E, pc[s]);
+        else load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
+        load_words<4, true>(d.cache + c0, (uint32_t)cnt[s], full || d.cache_aligned != 0, cw[s]);
       }
     }
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+    for (int s = 0; s < S; ++s) {  // a row's swap just before its compare: one row's raw words live at a time
+      if (whole[s]) swap_x_pieces<DT>(&s_stage[wave][0], pc[s], xw[s]);
       mask[s] = 0;
       expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
       if (full) mask[s] = chunk_exps<DT, true>(xw[s], cw[s], 16, expk[s]);
@@ -1377,7 +1506,15 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
     const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
     if (cnt[s] > 0) {
       if (cmode) {
-        store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
+        if constexpr (DT != 1) {
+          if (whole[s])
+            store_sm_pieces<DT>(d.stream + kHeader + sm_off<DT>(base + (uint64_t)s * kSub + (uint64_t)wave * 1024u),
+                                &s_stage[wave][0], smw[s]);
+          else
+            store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
+        } else {
+          store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
+        }
       } else {  // RAW: the values as stored
         uint32_t rw[XW];
         load_words<XW>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, rw);
@@ -2363,6 +2500,8 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
   __shared__ uint32_t s_expbm[BMW];  // blocks of the tile that hold a patch
   __shared__ uint32_t s_ex[T / 4];   // the tile's exponents: cached, then patched in place
   __shared__ uint32_t s_sum[kDecThreads / 64];
+  constexpr bool XP = kSmPieces<DT> != 0;  // records of whole wave rows swapped through LDS
+  __shared__ uint32_t s_stage[XP ? kDecThreads / 64 : 1][XP ? kSmWaveRow<DT> / 4 : 1];
   // coded patches (the tensor's streams may be CODED): each row's chunk data
   __shared__ uint32_t s_win[CODED ? U : 1][CODED ? kSub / 4 : 1];
   __shared__ uint8_t s_mark[CODED ? U : 1][64];  // coded: blocks of each row that were patched
@@ -2390,14 +2529,19 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
 
   // 1. bulk loads, COMPRESSED layout (in bounds for either mode: a slot holds a RAW stream)
   uint32_t sw[U][SW], cw[U][4];
+  v4u pc[U][XP ? kSmPieces<DT> : 1];
+  bool whole[U];  // uniform per wave: the wave's 1024 values of row u are in the shard
   int cnt[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
+    const uint64_t w0 = ts + (uint64_t)u * kDecRow + (uint64_t)wave * 1024u;
+    whole[u] = XP && w0 + 1024u <= te;
     cnt[u] = (int)left_in(te, c0, 16);
     if (cnt[u] > 0) {
-      load_smw<DT, SW>(st + kHeader, c0, cnt[u], sw[u]);
-      load_words<4, kNtBulk<DT>>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);
+      if (whole[u]) load_sm_pieces<DT>(st + kHeader + sm_off<DT>(w0), pc[u]);
+      else load_smw<DT, SW>(st + kHeader, c0, cnt[u], sw[u]);
+      load_words<4, true>(cache + c0, (uint32_t)cnt[u], aligned, cw[u]);  // 16 contiguous bytes per lane
     }
   }
   const uint64_t nb = (n + B - 1) >> lb;
@@ -2421,6 +2565,11 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
       e.x = cw[u][0]; e.y = cw[u][1]; e.z = cw[u][2]; e.w = cw[u][3];
       *reinterpret_cast<v4u*>(&s_ex[((uint32_t)u * kDecRow + tid * kEPT) / 4]) = e;
     }
+  }
+  if constexpr (XP) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (whole[u]) swap_sm_pieces<DT, SW>(&s_stage[wave][0], pc[u], sw[u]);
   }
   __syncthreads();
   const uint32_t h_mode = s_hdr[1] >> 24;

@@ -190,6 +190,27 @@ def test_long_patch_lists(name, frac, dense):
     assert h["mode"] == O.MODE_COMPRESSED and h["n_changed"] > 64
 
 
+# Rows that some waves cover whole and others only in part: a wave whose 1024
+# values of a 4096-value row are all in the shard moves them as contiguous
+# 16-byte pieces swapped through LDS (encode loads of the values and fp32/fp16
+# record stores; decode record loads), the others lane by lane.  Shards end
+# inside a row at a wave boundary, just past one, mid-wave and one value short.
+WAVE_ROWS = [(1, 4096 + 1024), (1, 4096 + 1025), (1, 8192 + 3072 + 17), (1, 2 * 4096 - 1), (3, 7000),
+             (1, 1024), (1, 1023), (5, 4096 + 2048 + 7)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("world", [1, 2])
+def test_wave_rows_whole_and_partial(dtype, world):
+    say(f"[gpu] whole and partial wave rows {dtype} W={world}")
+    specs = [W.TensorSpec(f"w{i}", r * world, c) for i, (r, c) in enumerate(WAVE_ROWS)]
+    cfg = W.PairConfig("wave-rows", dtype=dtype, frac=0.02)
+    w0, w1 = _pairs(specs, cfg)
+    for compress in ([1] * len(specs), [0] * len(specs)):
+        res = Case([(s.rows, s.cols) for s in specs], dtype, world).run(w0, w1, compress=compress)
+        assert res["status"] == 0 and res["ostatus"] == 0
+
+
 def test_specials_and_all_bf16_patterns():
     """Every bf16 bit pattern (+-0, subnormals, Inf, all NaN payloads) survives."""
     say("[gpu] all 65536 bf16 patterns")
