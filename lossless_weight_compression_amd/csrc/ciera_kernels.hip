@@ -2501,7 +2501,9 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
   __shared__ uint32_t s_ex[T / 4];   // the tile's exponents: cached, then patched in place
   __shared__ uint32_t s_sum[kDecThreads / 64];
   constexpr bool XP = kSmPieces<DT> != 0;  // records of whole wave rows swapped through LDS
-  __shared__ uint32_t s_stage[XP ? kDecThreads / 64 : 1][XP ? kSmWaveRow<DT> / 4 : 1];
+  // each wave's exchange buffer: fp32/fp16 records in, bf16/fp32 values out
+  constexpr uint32_t kStage = DT == 3 ? kSmWaveRow<DT> : kSmWaveRow<DT> > 1024u * E ? kSmWaveRow<DT> : 1024u * E;
+  __shared__ uint32_t s_stage[kDecThreads / 64][kStage / 4];
   // coded patches (the tensor's streams may be CODED): each row's chunk data
   __shared__ uint32_t s_win[CODED ? U : 1][CODED ? kSub / 4 : 1];
   __shared__ uint8_t s_mark[CODED ? U : 1][64];  // coded: blocks of each row that were patched
@@ -2992,7 +2994,36 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
   for (int u = 0; u < U; ++u) {
     if (cnt[u] > 0) {
       const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
-      if constexpr (DT == 1) {
+      // A wave whose 1024 values of the row are all in the shard stores them as
+      // contiguous pieces through its LDS buffer: whole-line stores instead of
+      // 16-byte pieces strided 32 or 64 bytes apart (bf16 and fp32; the fp16
+      // join holds too many registers for it, 57 -> 82 VGPRs, and loses).
+      const uint64_t w0 = ts + (uint64_t)u * kDecRow + (uint64_t)wave * 1024u;
+      if (DT != 3 && aligned && w0 + 1024u <= te) {  // uniform per wave
+        uint32_t v[4 * E];
+        if constexpr (DT == 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bf16x4_join(sw[u][q], ex[u][q], v[2 * q], v[2 * q + 1]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
+        }
+        uint32_t* const sb = &s_stage[wave][0];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          v4u a;
+          a.x = v[4 * q]; a.y = v[4 * q + 1]; a.z = v[4 * q + 2]; a.w = v[4 * q + 3];
+          *reinterpret_cast<v4u*>(sb + 4 * E * lane + 4 * q) = a;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          const uint32_t k = 64u * q + lane;
+          stg16(out + w0 * E + 16 * k, *reinterpret_cast<const v4u*>(sb + 4 * k));
+        }
+        __builtin_amdgcn_wave_barrier();
+      } else if constexpr (DT == 1) {
         uint32_t o[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) bf16x4_join(sw[u][q], ex[u][q], o[2 * q], o[2 * q + 1]);
