@@ -1559,6 +1559,20 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
   }
 }
 
+// Groups of items whose tiles finish their own streams (element patches and
+// RAW of at most kSelfTiles tiles; a launch group holds no other items) take a
+// kernel of their own, so that its registers and occupancy are those of that
+// path alone (the other paths of encode_kernel need more).
+template <int DT, int S>
+__global__ __launch_bounds__(kThreads) void encode_self_kernel(EncArgs a, uint32_t batch_id) {
+  const uint32_t rel_item = blockIdx.x / a.tpi;
+  const uint32_t item = a.item0 + rel_item;
+  const uint32_t local = blockIdx.x - rel_item * a.tpi;
+  const EncItem d = a.items[item];
+  if (d.batch_id != batch_id) return;  // the scratch holds another batch (uniform)
+  split_tile_self<DT, S>(d, local, a);
+}
+
 template <int DT, int S>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t batch_id) {
   constexpr int E = Tr<DT>::E;
@@ -1579,10 +1593,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncArgs a, uint32_t ba
   }
   if (d.compress == kCoded) {  // uniform
     split_tile_coded<DT, S>(d, local, a);
-    return;
-  }
-  if (a.self) {  // uniform: compress 0 or 1, at most kSelfTiles tiles
-    split_tile_self<DT, S>(d, local, a);
     return;
   }
   const uint64_t base = (uint64_t)local * T;
@@ -3165,7 +3175,11 @@ static hipError_t launch_encode_part(int dtype, int sub, uint32_t nitems, const 
                                      hipStream_t s) {
   (void)hipGetLastError();
   const dim3 grid(nitems * a.tpi), block(kThreads);
-#define CIERA_ENC(DT, S) hipLaunchKernelGGL((encode_kernel<DT, S>), grid, block, 0, s, a, batch_id)
+#define CIERA_ENC(DT, S)                                                                \
+  do {                                                                                  \
+    if (a.self) hipLaunchKernelGGL((encode_self_kernel<DT, S>), grid, block, 0, s, a, batch_id); \
+    else hipLaunchKernelGGL((encode_kernel<DT, S>), grid, block, 0, s, a, batch_id);   \
+  } while (0)
 #define CIERA_ENC_DT(DT)                  \
   switch (sub) {                          \
     case 1: CIERA_ENC(DT, 1); break;      \
