@@ -653,6 +653,15 @@ __device__ __forceinline__ void store_sm_words(uint8_t* p, int cnt, const uint32
 // in order; the wave barriers keep the compiler from moving them.
 template <int DT>
 constexpr uint32_t kXWaveRow = 1024u * Tr<DT>::E;
+// LDS slot (16-byte unit) of piece q of lane t when every lane holds E (2 or 4)
+// consecutive pieces of a row: E * t + q, with q XOR-ed by the lane's group so
+// that the 16 lanes of one LDS pass fall on 16 different bank groups (E * t
+// alone would put 2 or 4 lanes on each).  Piece k of the row, lane-held by
+// lane k / E, is in slot xslot<E>(k / E, k % E).
+template <int E>
+__device__ __forceinline__ uint32_t xslot(uint32_t t, uint32_t q) {
+  return E * t + (q ^ ((t >> (E == 2 ? 3 : 2)) & (E - 1)));
+}
 template <int DT>
 __device__ __forceinline__ void load_x_pieces(const uint8_t* p, v4u pc[Tr<DT>::E]) {
   const uint32_t lane = lane_id();
@@ -665,11 +674,14 @@ __device__ __forceinline__ void swap_x_pieces(uint32_t* stage, const v4u pc[Tr<D
   const uint32_t lane = lane_id();
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int q = 0; q < E; ++q) *reinterpret_cast<v4u*>(stage + 4 * (64u * q + lane)) = pc[q];
+  for (int q = 0; q < E; ++q) {
+    const uint32_t k = 64u * q + lane;
+    *reinterpret_cast<v4u*>(stage + 4 * xslot<E>(k / E, k % E)) = pc[q];
+  }
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int q = 0; q < E; ++q) {
-    const v4u a = *reinterpret_cast<const v4u*>(stage + 4 * E * lane + 4 * q);
+    const v4u a = *reinterpret_cast<const v4u*>(stage + 4 * xslot<E>(lane, q));
     xw[4 * q] = a.x; xw[4 * q + 1] = a.y; xw[4 * q + 2] = a.z; xw[4 * q + 3] = a.w;
   }
   __builtin_amdgcn_wave_barrier();
@@ -3024,13 +3036,13 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
         for (int q = 0; q < E; ++q) {
           v4u a;
           a.x = v[4 * q]; a.y = v[4 * q + 1]; a.z = v[4 * q + 2]; a.w = v[4 * q + 3];
-          *reinterpret_cast<v4u*>(sb + 4 * E * lane + 4 * q) = a;
+          *reinterpret_cast<v4u*>(sb + 4 * xslot<E>(lane, q)) = a;
         }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int q = 0; q < E; ++q) {
           const uint32_t k = 64u * q + lane;
-          stg16(out + w0 * E + 16 * k, *reinterpret_cast<const v4u*>(sb + 4 * k));
+          stg16(out + w0 * E + 16 * k, *reinterpret_cast<const v4u*>(sb + 4 * xslot<E>(k / E, k % E)));
         }
         __builtin_amdgcn_wave_barrier();
       } else if constexpr (DT == 1) {
