@@ -3020,6 +3020,11 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
       // contiguous pieces through its LDS buffer: whole-line stores instead of
       // 16-byte pieces strided 32 or 64 bytes apart (bf16 and fp32; the fp16
       // join holds too many registers for it, 57 -> 82 VGPRs, and loses).
+      // The stores are non-temporal: written once, never read by this launch,
+      // and streamed out in address order instead of left dirty in the caches
+      // for the next kernel to write back (1% layer: decode 341 -> 322 us and
+      // the encode after it 34.9 -> 32.6 us in-step; alone, the decode takes 8
+      // us longer, as it now pays its own write-back).
       const uint64_t w0 = ts + (uint64_t)u * kDecRow + (uint64_t)wave * 1024u;
       if (DT != 3 && aligned && w0 + 1024u <= te) {  // uniform per wave
         uint32_t v[4 * E];
@@ -3042,7 +3047,7 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
 #pragma unroll
         for (int q = 0; q < E; ++q) {
           const uint32_t k = 64u * q + lane;
-          stg16(out + w0 * E + 16 * k, *reinterpret_cast<const v4u*>(sb + 4 * xslot<E>(k / E, k % E)));
+          stg16_nt(out + w0 * E + 16 * k, *reinterpret_cast<const v4u*>(sb + 4 * xslot<E>(k / E, k % E)));
         }
         __builtin_amdgcn_wave_barrier();
       } else if constexpr (DT == 1) {
@@ -3054,7 +3059,15 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
         uint32_t v[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
-        store16<DT>(out + c0 * E, cnt[u], v, aligned);
+        if (DT == 3 && cnt[u] == 16 && aligned) {  // fp16, lane by lane: non-temporal too
+          v4u a, b;
+          a.x = v[0] | (v[1] << 16); a.y = v[2] | (v[3] << 16); a.z = v[4] | (v[5] << 16); a.w = v[6] | (v[7] << 16);
+          b.x = v[8] | (v[9] << 16); b.y = v[10] | (v[11] << 16); b.z = v[12] | (v[13] << 16); b.w = v[14] | (v[15] << 16);
+          stg16_nt(out + c0 * E, a);
+          stg16_nt(out + c0 * E + 16, b);
+        } else {
+          store16<DT>(out + c0 * E, cnt[u], v, aligned);
+        }
       }
     }
     // cache write-back in whole 128-byte lines (8 lanes): scattered partial
