@@ -462,13 +462,15 @@ def setup(args):
     plans_expected = [p.compress for p in A.plans]
     encA = A.prepare_encode(0, shards(w1, 0), compress=comp)
     encB = Bc.prepare_encode(0, shards(w0, 0), compress=comp)
+    planner = {id(A): L.PlanBatch(A.tensors, ppm), id(Bc): L.PlanBatch(Bc.tensors, ppm)}
 
     def step(k, stream, ev=None):
         codec, enc = (A, encA) if k % 2 == 0 else (Bc, encB)
-        # plan: the per-tensor selector (host), consumed by the prepared batch
-        for i, t in enumerate(codec.tensors):
-            if L.ciera_plan(t, ppm).compress != plans_expected[i]:
-                raise RuntimeError("plan changed: the prepared batch would be stale")
+        # plan: the per-tensor selector (host, one call for the layer), consumed
+        # by the prepared batch
+        plans = planner[id(codec)].run()
+        if any(plans[i].compress != plans_expected[i] for i in range(len(plans_expected))):
+            raise RuntimeError("plan changed: the prepared batch would be stale")
         if ev is not None:
             ev[0].record(stream)
         enc.launch(stream)

@@ -171,6 +171,15 @@ typedef struct {
 ciera_status_t ciera_plan(const ciera_tensor_t* t, uint32_t change_ppm,
                           const ciera_cost_model_t* cm, ciera_plan_t* out);
 
+/* ciera_plan_batch -- ciera_plan for `count` tensors in one call (one plan per
+ * iteration of a whole layer without a call per tensor): out[i] is exactly
+ * ciera_plan(&t[i], change_ppm[i], cm, &out[i]).  t, change_ppm and out are host
+ * arrays of `count` entries.  Errors: INVALID_ARG for null arrays (count > 0);
+ * otherwise the status of the first tensor ciera_plan rejects (out[i] for that
+ * i and after it are then unspecified). */
+ciera_status_t ciera_plan_batch(const ciera_tensor_t* t, const uint32_t* change_ppm, uint32_t count,
+                                const ciera_cost_model_t* cm, ciera_plan_t* out);
+
 /* ciera_select -- benefit-driven selection under a cache budget [CIERA 3.2]:
  * among the tensors whose plan has a positive gain (plans[i].gain_ns > 0), rank
  * them by gain per byte of exponent cache, gain_ns / cache_bytes, descending

@@ -6,10 +6,10 @@ holds a layer's caches, receive slots and outputs in flat device buffers.
 Importing fails loudly when the library has not been built.
 """
 from ._binding import *  # noqa: F401,F403
-from ._binding import (Batch, CieraError, CostModel, DecodeItem, EncodeItem, Plan, Tensor,  # noqa: F401
+from ._binding import (Batch, CieraError, CostModel, DecodeItem, EncodeItem, Plan, PlanBatch, Tensor,  # noqa: F401
                        ciera_abi_version, ciera_cache_update, ciera_decode, ciera_decode_launch,
                        ciera_decode_launch_bounded, ciera_decode_prepare, ciera_decode_scratch_bytes, ciera_encode,
                        ciera_encode_noalloc,
                        ciera_encode_launch, ciera_encode_prepare, ciera_encode_scratch_bytes, ciera_hash_update,
-                       ciera_plan, ciera_select, ciera_set_sync_polls, ciera_shard, ciera_status_str, decode_item,
+                       ciera_plan, ciera_plan_batch, ciera_select, ciera_set_sync_polls, ciera_shard, ciera_status_str, decode_item,
                        encode_item)

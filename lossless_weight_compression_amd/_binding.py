@@ -19,7 +19,7 @@ HEADER_BYTES = 64
 CIERA_NOALLOC_SCRATCH_BYTES = 1 << 20  # the static scratch of ciera_encode_noalloc
 
 # every symbol include/ciera.h declares
-EXPORTS = ["ciera_plan", "ciera_select", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
+EXPORTS = ["ciera_plan", "ciera_plan_batch", "ciera_select", "ciera_shard", "ciera_encode_scratch_bytes", "ciera_encode",
            "ciera_encode_prepare", "ciera_encode_launch", "ciera_decode_scratch_bytes",
            "ciera_decode", "ciera_decode_prepare", "ciera_decode_launch", "ciera_cache_update",
            "ciera_hash_update", "ciera_set_sync_polls", "ciera_encode_noalloc", "ciera_decode_launch_bounded",
@@ -97,6 +97,8 @@ def _load() -> ctypes.CDLL:
         raise ImportError(f"two HIP runtimes are mapped into this process: {sorted(runtimes)}")
     sig = {
         "ciera_plan": (c_int, [POINTER(Tensor), c_uint32, POINTER(CostModel), POINTER(Plan)]),
+        "ciera_plan_batch": (c_int, [POINTER(Tensor), POINTER(c_uint32), c_uint32, POINTER(CostModel),
+                                     POINTER(Plan)]),
         "ciera_select": (c_int, [POINTER(Plan), c_uint32, c_uint64, POINTER(c_uint32)]),
         "ciera_shard": (c_int, [POINTER(Tensor), c_uint32, POINTER(c_uint64), POINTER(c_uint64)]),
         "ciera_encode_scratch_bytes": (c_int, [POINTER(EncodeItem), c_uint32, POINTER(c_uint64)]),
@@ -199,6 +201,35 @@ def ciera_plan(t: Tensor, change_ppm: int, cost: Optional[CostModel] = None) -> 
     _check(_lib.ciera_plan(byref(t), change_ppm, byref(cost) if cost is not None else None,
                            byref(out)), "ciera_plan")
     return out
+
+
+class PlanBatch:
+    """Host arrays for ciera_plan_batch over a fixed list of tensors, built once
+    so that a per-iteration plan of a whole layer is one library call."""
+
+    def __init__(self, tensors: Sequence[Tensor], change_ppm, cost: Optional[CostModel] = None):
+        n = len(tensors)
+        self.count = n
+        self.tensors = (Tensor * max(n, 1))(*tensors)
+        ppm = [change_ppm] * n if isinstance(change_ppm, int) else list(change_ppm)
+        if len(ppm) != n:
+            raise ValueError(f"change_ppm: {len(ppm)} rates for {n} tensors")
+        self.ppm = (c_uint32 * max(n, 1))(*ppm)
+        self.cost = cost
+        self.out = (Plan * max(n, 1))()
+
+    def run(self):
+        """Plans of every tensor (the array is reused by the next run)."""
+        _check(_lib.ciera_plan_batch(self.tensors, self.ppm, self.count,
+                                     byref(self.cost) if self.cost is not None else None, self.out),
+               "ciera_plan_batch")
+        return self.out
+
+
+def ciera_plan_batch(tensors: Sequence[Tensor], change_ppm, cost: Optional[CostModel] = None) -> List[Plan]:
+    """ciera_plan of every tensor in one call (change_ppm: one rate or one per tensor)."""
+    b = PlanBatch(tensors, change_ppm, cost)
+    return [Plan.from_buffer_copy(p) for p in b.run()[:b.count]]
 
 
 def ciera_select(plans: Sequence[Plan], cache_budget_bytes: int) -> List[int]:

@@ -359,6 +359,14 @@ ciera_status_t ciera_plan(const ciera_tensor_t* t, uint32_t change_ppm, const ci
   return CIERA_OK;
 }
 
+ciera_status_t ciera_plan_batch(const ciera_tensor_t* t, const uint32_t* change_ppm, uint32_t count,
+                                const ciera_cost_model_t* cm, ciera_plan_t* out) {
+  if (count && (!t || !change_ppm || !out)) return CIERA_ERR_INVALID_ARG;
+  for (uint32_t i = 0; i < count; ++i)
+    if (ciera_status_t s = ciera_plan(t + i, change_ppm[i], cm, out + i)) return s;
+  return CIERA_OK;
+}
+
 ciera_status_t ciera_select(const ciera_plan_t* plans, uint32_t count, uint64_t cache_budget_bytes,
                             uint32_t* compress_out) {
   if (count && (!plans || !compress_out)) return CIERA_ERR_INVALID_ARG;

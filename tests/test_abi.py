@@ -174,6 +174,34 @@ def test_overlapping_buffers_are_rejected_without_device():
         assert e.value.code == 1, kw
 
 
+def test_plan_batch_equals_plan_per_tensor():
+    """ciera_plan_batch gives exactly ciera_plan for every tensor (random shapes,
+    types, worlds, block sizes and change rates, default and custom cost
+    models); a rejected tensor gives its status; null arrays are invalid."""
+    import random
+    rng = random.Random(5)
+    ts, ppm = [], []
+    for _ in range(400):
+        dt = rng.choice([L.CIERA_BF16, L.CIERA_FP32, L.CIERA_FP16])
+        ts.append(L.Tensor(rng.randint(1, 4000), rng.randint(1, 9000), dt, 1 << rng.randint(6, 12),
+                           rng.randint(1, 64)))
+        ppm.append(rng.choice([0, 1, 100, 10_000, 100_000, 300_000, 1_000_000]))
+    for cost in (None, L.CostModel(12_000, 4_000_000, 3_000, 0)):
+        got = L.ciera_plan_batch(ts, ppm, cost)
+        want = [L.ciera_plan(t, p, cost) for t, p in zip(ts, ppm)]
+        assert [g.as_dict() for g in got] == [w.as_dict() for w in want]
+        pb = L.PlanBatch(ts, ppm, cost)
+        assert [p.as_dict() for p in pb.run()] == [w.as_dict() for w in want]
+    bad = ts[:3] + [L.Tensor(4, 4, 9, 512, 1)] + ts[3:5]
+    with pytest.raises(L.CieraError) as e:
+        L.ciera_plan_batch(bad, 100)
+    assert e.value.code == 1
+    with pytest.raises(ValueError):
+        L.PlanBatch(ts[:3], [1, 2])
+    assert L._binding._lib.ciera_plan_batch(None, None, 0, None, None) == 0
+    assert L._binding._lib.ciera_plan_batch(None, None, 2, None, None) == 1
+
+
 def test_rank_stream_pointers_without_device():
     """Decode items whose W streams sit in W separate buffers (rank_streams):
     exactly one of streams and rank_streams; every rank pointer non-null and
