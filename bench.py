@@ -127,7 +127,7 @@ def measure(args, pool):
     for k in range(args.warmup):
         step(k, stream)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
@@ -246,6 +246,57 @@ def measure(args, pool):
     print(json.dumps(out), flush=True)
 
 
+class TimingEvent:
+    """A HIP timing event recorded without the system-scope fence
+    (hipEventDisableSystemFence).  torch's events carry that fence: every
+    record writes back and invalidates the GPU caches, which cost the step
+    about 15 us (three records per step) and slowed the kernel after each
+    record.  These events only time the work between them, as torch.cuda.Event
+    does (record on a stream, elapsed_time in ms)."""
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            from lossless_weight_compression_amd import _binding
+            paths = sorted(_binding._hip_runtimes())
+            if len(paths) != 1:
+                raise RuntimeError(f"expected one HIP runtime in the process, found {paths}")
+            lib = ctypes.CDLL(paths[0])
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000)  # hipEventDisableSystemFence
+        if rc:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self, stream=None):
+        import torch
+        rc = self._lib().hipEventRecord(self.ev, (stream or torch.cuda.current_stream()).cuda_stream)
+        if rc:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if rc:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self.ev and self._hip is not None:
+            self._hip.hipEventDestroy(self.ev)
+
+
 def steady_copy_gbps():
     """Bytes moved (read + write) per second by a 1 GiB device-to-device copy
     (torch copy_), median of 10 back-to-back copies after 3 untimed ones."""
@@ -257,7 +308,7 @@ def steady_copy_gbps():
         b.copy_(a)
     evs = []
     for _ in range(10):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record()
         b.copy_(a)
         e1.record()
@@ -279,7 +330,7 @@ def copy_references(wl, stream, k0, enc_bytes, dec_bytes, reps=20):
     cd_a, cd_b = cd[:dec_bytes // 2], cd[dec_bytes // 2:]
     te, td = [], []
     for k in range(k0, k0 + reps + 2):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [TimingEvent() for _ in range(4)]
         wl["decode_only"](k, stream)
         e[0].record(stream)
         with torch.cuda.stream(stream):
@@ -313,7 +364,7 @@ def clustered_run(args, stream):
     steps = max(10, args.steps // 2)
     for k in range(args.warmup):
         wl["step"](k, stream)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
     for k in range(steps):
         wl["step"](args.warmup + k, stream, evs[k])
     torch.cuda.synchronize()
@@ -343,7 +394,7 @@ def isolated(wl, stream, k0, reps):
     flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda")  # 1 GiB
     enc, dec = [], []
     for k in range(k0, k0 + reps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [TimingEvent() for _ in range(4)]
         flush.sum()
         e[0].record(stream)
         wl["encode_only"](k, stream)
