@@ -1325,6 +1325,16 @@ __device__ __forceinline__ void write_header(const EncItem& d, uint64_t P, uint3
   }
 }
 
+// dst[b] = src[b] for b in [lo, hi), by the whole workgroup; dst and src have
+// the same alignment modulo 16 (16-byte pieces between byte-wise ends).
+__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, uint64_t lo, uint64_t hi) {
+  const uint32_t tid = threadIdx.x;
+  const uint64_t a = min(hi, (lo + 15) & ~15ull), e = max(a, hi & ~15ull);
+  for (uint64_t b = lo + tid; b < a; b += kThreads) gp(dst)[b] = gp(src)[b];
+  for (uint64_t q = a / 16 + tid; q < e / 16; q += kThreads) stg16(dst + 16 * q, ldg16(src + 16 * q));
+  for (uint64_t b = e + tid; b < hi; b += kThreads) gp(dst)[b] = gp(src)[b];
+}
+
 // ------------------------------------------- encode, tiles that finish themselves
 // Element patches and RAW (compress 0 or 1) of items of at most kSelfTiles
 // tiles.  After the compare each tile publishes its change count in its slot
@@ -1332,10 +1342,13 @@ __device__ __forceinline__ void write_header(const EncItem& d, uint64_t P, uint3
 // with a device-scope atomic -- and waits until every tile of its item has
 // published in this launch's epoch.  The counts give the item's total, hence
 // the mode [CIERA 3.2: compressed only when smaller], and the tile's exclusive
-// prefix, hence where its records go.  Only then does the tile store its
-// sign|mantissa bytes (or its raw values), its bitmap bytes and its records,
-// and tile 0 the header: nothing is written before the mode is known, so the
-// RAW fallback needs no rewrite and no second launch finishes the stream.
+// prefix, hence where its records go.  The tile stores its sign|mantissa
+// bytes while it waits (their place does not depend on the counts); once the
+// mode is known it stores its bitmap bytes and its records, and tile 0 the
+// header.  When the total makes the stream RAW although the plan compressed it
+// (rare), every tile rewrites the bytes of the raw body it owns -- those its
+// sign|mantissa stores went to, and an even share of the rest -- so that no
+// byte has two writers and no second launch finishes the stream.
 //
 // The epoch is the tile's own slot's previous epoch plus one: every launch
 // advances every slot of the item by one (the slots are zeroed when the batch
@@ -1458,11 +1471,35 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
     }
   }
 
-  // publish, then wait for the item's other tiles (wave 0, lanes over tiles)
+  // publish (wave 0)
+  uint32_t epoch = 0;
   if (wave == 0) {
-    const uint32_t epoch = __shfl((uint32_t)(mine_old >> 32), 0) + 1u;
+    epoch = __shfl((uint32_t)(mine_old >> 32), 0) + 1u;
     if (lane == 0)
       __hip_atomic_store(sync + local, ((uint64_t)epoch << 32) | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the sign|mantissa records go out now, while the siblings' counts come in:
+  // a COMPRESSED stream keeps them; a RAW one (rare) is rewritten below by
+  // the tiles that own its bytes
+  if (d.compress != 0) {  // uniform
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+      if (cnt[s] > 0) {
+        if constexpr (DT != 1) {
+          if (whole[s])
+            store_sm_pieces<DT>(d.stream + kHeader + sm_off<DT>(base + (uint64_t)s * kSub + (uint64_t)wave * 1024u),
+                                &s_stage[wave][0], smw[s]);
+          else
+            store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
+        } else {
+          store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
+        }
+      }
+    }
+  }
+  // wait for the item's other tiles (wave 0, lanes over tiles)
+  if (wave == 0) {
     const uint32_t polls = a.polls ? a.polls : kSelfPolls;
     uint32_t tot = 0, pre = 0;
     for (uint32_t k = lane; k < d.tpi; k += 64) {
@@ -1513,26 +1550,28 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
   const uint64_t raw = kHeader + n * E;
   const bool cmode = d.compress != 0 && comp < raw;
 
+  if (d.compress == 0) {  // RAW by plan: the values as stored
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-    if (cnt[s] > 0) {
-      if (cmode) {
-        if constexpr (DT != 1) {
-          if (whole[s])
-            store_sm_pieces<DT>(d.stream + kHeader + sm_off<DT>(base + (uint64_t)s * kSub + (uint64_t)wave * 1024u),
-                                &s_stage[wave][0], smw[s]);
-          else
-            store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
-        } else {
-          store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
-        }
-      } else {  // RAW: the values as stored
+    for (int s = 0; s < S; ++s) {
+      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+      if (cnt[s] > 0) {
         uint32_t rw[XW];
         load_words<XW>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, rw);
         store_words<XW>(d.stream + kHeader + c0 * E, (uint32_t)cnt[s] * E, true, rw);
       }
     }
+  } else if (!cmode) {
+    // RAW although planned compressed: the raw body (the shard's bytes) is
+    // split between the tiles so that each byte has one writer -- tile k
+    // takes the bytes its records went to above, [sm_off(kT), sm_off((k+1)T)),
+    // and an even share of the rest, [S + kD, S + (k+1)D) with S the record
+    // section's bytes.  Its own record stores are complete first (barrier).
+    __syncthreads();
+    const uint64_t rb = n * E;
+    const uint64_t r1 = local + 1 < d.tpi ? sm_off<DT>(base + T) : smsec;
+    const uint64_t D = ((rb - smsec + d.tpi - 1) / d.tpi + 15) & ~15ull;
+    copy_bytes(d.stream + kHeader, d.x, sm_off<DT>(base), r1);
+    copy_bytes(d.stream + kHeader, d.x, min(rb, smsec + local * D), min(rb, smsec + (local + 1) * D));
   }
   if (local == 0 && tid == 0) write_header<DT>(d, P, cmode ? 1u : 0u, cmode ? comp : raw);
   if (!cmode || P == 0) return;

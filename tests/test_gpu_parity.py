@@ -109,6 +109,32 @@ def test_change_rates_and_raw_fallback(dtype, frac):
         assert modes == {O.MODE_COMPRESSED}
 
 
+# RAW fallback of shards of several encode tiles whose last tile is partial:
+# the tiles store their sign|mantissa records before the item's total is
+# known, and a RAW stream is then rewritten by the tiles that own its bytes.
+# Tiles of 8192, 16384 and 32768 values (B 512, 2048, 4096); lengths that end
+# mid-chunk (fp16: inside an 11-bit value's bytes); change rates from all RAW
+# to around the break-even, so that one batch mixes both modes.
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("B", [512, 2048, 4096])
+def test_raw_fallback_of_multi_tile_shards(dtype, B):
+    say(f"[gpu] RAW fallback multi-tile {dtype} B={B}")
+    specs = [W.TensorSpec("a", 1, 30001), W.TensorSpec("b", 3, 25013), W.TensorSpec("c", 2, 65536 + 4097),
+             W.TensorSpec("d", 1, 8192 * 3 + 15)]
+    fracs = [0.6, 0.3, 0.18, 0.22] if dtype != torch.float32 else [0.6, 0.4, 0.3, 0.2]
+    w0, w1 = [], []
+    for i, (sp, f) in enumerate(zip(specs, fracs)):
+        a = W.base_weights(sp, W.tensor_seed("rawfb", i), dtype)
+        m = W.mask_uniform(sp.numel, f, W.tensor_seed("rawfb-m", i, B))
+        w0.append(a)
+        w1.append(W.perturb_exact(a, m, W.tensor_seed("rawfb-p", i, B)))
+    case = Case([(sp.rows, sp.cols) for sp in specs], dtype, 1, B)
+    res = case.run(w0, w1, compress=[1] * len(specs))
+    assert res["status"] == 0 and res["ostatus"] == 0
+    modes = [int(O.parse_header(case.codec.slot(i, 0).cpu().numpy())["mode"]) for i in range(len(specs))]
+    assert modes[0] == O.MODE_RAW and O.MODE_RAW in modes
+
+
 # (rows, cols, dtype, B, dense regions of 8192 values).  Shards of at most
 # 2^21 values are encoded by one workgroup each; larger ones by the tiled split
 # kernel (tiles of 8192 values for B <= 1024, 16384 for B = 2048, 32768 for
