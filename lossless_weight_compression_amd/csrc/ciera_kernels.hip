@@ -2564,9 +2564,15 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
   constexpr bool XP = kSmPieces<DT> != 0;  // records of whole wave rows swapped through LDS
   // each wave's exchange buffer: fp32/fp16 records in, bf16/fp32 values out
   constexpr uint32_t kStage = DT == 3 ? kSmWaveRow<DT> : kSmWaveRow<DT> > 1024u * E ? kSmWaveRow<DT> : 1024u * E;
-  __shared__ uint32_t s_stage[kDecThreads / 64][kStage / 4];
-  // coded patches (the tensor's streams may be CODED): each row's chunk data
-  __shared__ uint32_t s_win[CODED ? U : 1][CODED ? kSub / 4 : 1];
+  // coded patches (the tensor's streams may be CODED): each row's chunk data.
+  // It shares LDS with the exchange buffers: the exchanges run before the
+  // first barrier (records in) and after the patch phase (values out), the
+  // chunk data only in between, with barriers on both sides.
+  constexpr uint32_t kStageWords = kDecThreads / 64 * (kStage / 4);
+  constexpr uint32_t kWinWords = CODED ? (uint32_t)U * (kSub / 4) : 1u;
+  __shared__ uint32_t s_share[kStageWords > kWinWords ? kStageWords : kWinWords];
+  uint32_t (*const s_stage)[kStage / 4] = reinterpret_cast<uint32_t (*)[kStage / 4]>(s_share);
+  uint32_t (*const s_win)[CODED ? kSub / 4 : 1] = reinterpret_cast<uint32_t (*)[CODED ? kSub / 4 : 1]>(s_share);
   __shared__ uint8_t s_mark[CODED ? U : 1][64];  // coded: blocks of each row that were patched
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
