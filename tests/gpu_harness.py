@@ -44,11 +44,13 @@ class Case:
         self.codec = LayerCodec(self.shapes, dtype, world, block_size, "cuda", change_ppm)
 
     def run(self, w0: List[torch.Tensor], w1: List[torch.Tensor], compress: Optional[Sequence[int]] = None,
-            tensors: Optional[Sequence[int]] = None, edits=None) -> dict:
+            tensors: Optional[Sequence[int]] = None, edits=None, valid_edits_decode: bool = False) -> dict:
         """Seed the cache from w0, encode w1 for every rank (one batched call per
         rank), apply byte ``edits`` [(tensor, rank, offset, bytes)] to the
         streams on both sides, decode, and compare with the oracle.  ``tensors``
-        limits the oracle comparison (all by default)."""
+        limits the oracle comparison (all by default).  With
+        ``valid_edits_decode``, edited streams that both sides decode with
+        status 0 must also give the oracle's values and cache."""
         c = self.codec
         dev = [x.to("cuda").contiguous() for x in w0]
         c.seed_cache(dev)
@@ -101,6 +103,9 @@ class Case:
                 assert np.array_equal(g_out, o_out), f"tensor {i}: decoded values differ"
                 assert np.array_equal(g_out, x1), f"tensor {i}: decode(encode(x)) != x"
                 assert np.array_equal(g_cache, o_cache), f"tensor {i}: caches differ"
+            elif valid_edits_decode and o_st == 0 and res["status"] == 0:
+                assert np.array_equal(to_np(c.out_view(i)), o_out), f"tensor {i}: edited stream, values differ"
+                assert np.array_equal(c.cache_view(i).cpu().numpy(), o_cache), f"tensor {i}: edited stream, caches differ"
         return res
 
     @staticmethod

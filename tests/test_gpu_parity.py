@@ -353,6 +353,65 @@ def test_patch_record_order_errors_at_many_positions(frac):
             assert g & ~O.ST_BITMAP == o & ~O.ST_BITMAP, (kind, i, g, o)
 
 
+# Patch ranges of decode tiles (8192 values) whose element-patch lists are
+# longer than 64 records: both tiles that share a boundary look for its place
+# in the list, each on its own, probing a window around where an even spread
+# puts it, so they must agree on it whatever the records hold.  (rows, cols,
+# world, change rate): 490 records in six tiles, 121 in two, 1626 in two
+# (about 813 a tile), 2446 in six.
+RANGE_CASES = [(64, 3000, 4, 0.01), (16, 3000, 4, 0.01), (16, 1024, 1, 0.10), (64, 3000, 4, 0.05)]
+
+
+@pytest.mark.parametrize("rows,cols,world,frac", RANGE_CASES)
+def test_patch_ranges_at_tile_boundaries(rows, cols, world, frac):
+    """Records swapped, repeated or moved across each tile boundary, and swapped
+    at the places where the boundary's window begins and ends: the oracle's
+    status, and where an edited list is still well formed, its values and
+    cache."""
+    T, B = 8192, 64
+    say(f"[gpu] patch ranges at tile boundaries {rows}x{cols} W={world} f={frac}")
+    spec = W.TensorSpec("ranges", rows, cols)
+    a = W.base_weights(spec, W.tensor_seed("ranges", rows, cols), torch.bfloat16)
+    m = W.mask_uniform(spec.numel, frac, W.tensor_seed("ranges-m", rows, cols))
+    w0, w1 = [a], [W.perturb_exact(a, m, W.tensor_seed("ranges-p", rows, cols))]
+    ref = Case([(rows, cols)], torch.bfloat16, world, B)
+    ref.run(w0, w1, compress=[1])
+    r = 0
+    n = O.shard(rows, cols, world, r)[1]
+    s = ref.codec.slot(0, r).cpu().numpy()
+    h = O.parse_header(s)
+    p = int(h["n_changed"])
+    assert h["mode"] == O.MODE_COMPRESSED and p > 64 and n > T
+    pb = 64 + n + O.bitmap_bytes(n, B)
+    rec = [bytes(s[pb + 5 * i:pb + 5 * i + 5]) for i in range(p)]
+    idx = np.array([int.from_bytes(x[:4], "little") for x in rec])
+    edits = []
+    for b in range(T, n, T):
+        q = int(np.searchsorted(idx, b))  # first record of the tile that starts at b
+        assert 0 < q < p
+        for i in (q - 2, q - 1, q):
+            if 0 <= i and i + 1 < p:
+                edits.append((f"swap {i}", [(0, r, pb + 5 * i, rec[i + 1]), (0, r, pb + 5 * i + 5, rec[i])]))
+                edits.append((f"repeat {i}", [(0, r, pb + 5 * i + 5, rec[i])]))
+        if idx[q - 1] < b - 1:  # still ascending: the record moves to the tile before
+            edits.append((f"move {q} to {b - 1}", [(0, r, pb + 5 * q, int(b - 1).to_bytes(4, "little"))]))
+        if idx[q] > b:  # a record of the tile before moves to b
+            edits.append((f"move {q - 1} to {b}", [(0, r, pb + 5 * (q - 1), int(b).to_bytes(4, "little"))]))
+        for d in (16, 32, 48, 64, 65):  # near the ends of the probed windows (+-16 S records)
+            for i in (q - d, q + d - 1):
+                if 0 <= i and i + 1 < p:
+                    edits.append((f"swap {i}", [(0, r, pb + 5 * i, rec[i + 1]), (0, r, pb + 5 * i + 5, rec[i])]))
+    assert len(edits) > 10
+    for name, e in edits:
+        res = Case([(rows, cols)], torch.bfloat16, world, B).run(w0, w1, compress=[1], edits=e,
+                                                                 valid_edits_decode=True)
+        g, o = res["status"], res["ostatus"]
+        if o & O.ST_PATCH:  # bitmap bit unspecified alongside a patch error
+            g &= ~O.ST_BITMAP
+            o &= ~O.ST_BITMAP
+        assert g == o, (name, g, o)
+
+
 def test_encode_is_deterministic():
     """Two encodes of the same inputs give identical bytes (no order dependence between workgroups)."""
     specs = W.olmoe_expert_specs()
