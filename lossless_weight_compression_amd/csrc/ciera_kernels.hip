@@ -2231,95 +2231,6 @@ __device__ __forceinline__ bool chunk_entry_ok(uint32_t pc, uint32_t pb, uint32_
   return !(c > 0 && bytes != pad4u(len) && (bytes < 4u * rans_lanes(c) || bytes > pad4u(len)));
 }
 
-// Decodes one chunk's coded data (win: the data in LDS, nbytes bytes; c
-// changes among len values) with one wave.  Every active lane calls
-// emit(j, idx, cls, esc, ok) for change j: chunk offset idx, step class cls,
-// escaped exponent esc, ok = idx inside the chunk; emit returns status bits.
-// Returns the status bits: ST_PATCH for words missing or left over, a final
-// state other than 2^16, a change past the chunk, and emit's.
-template <class Emit>
-__device__ __forceinline__ uint32_t rans_decode_wave(const uint32_t* win, uint32_t nbytes, uint32_t c, uint32_t len,
-                                                    Emit&& emit) {
-  const uint32_t lane = lane_id();
-  const uint32_t Lr = rans_lanes(c);
-  const uint32_t navail = (nbytes - 4u * Lr) / 2u;
-  const uint16_t* words = reinterpret_cast<const uint16_t*>(win + Lr);
-  uint32_t gf, gcum;
-  gap_table(c, len, gf, gcum);
-  // bucket starts 1..12, the same in every lane (scalar registers)
-  uint32_t cum[13];
-#pragma unroll
-  for (int i = 1; i < 13; ++i) cum[i] = __builtin_amdgcn_readlane(gcum, i);
-  uint32_t x = lane < Lr ? win[lane] : kRansLow;
-  uint32_t ptr = 0, run = 0, err = 0;
-  auto renorm = [&]() {
-    const bool need = lane < Lr && x < kRansLow;
-    const uint64_t m = __ballot(need);
-    if (need) {
-      const uint32_t pos = ptr + lanes_below(m);
-      uint32_t w = 0;
-      if (pos < navail) w = words[pos];
-      else err |= CIERA_ST_PATCH;
-      x = (x << 16) | w;
-    }
-    ptr += (uint32_t)__popcll(m);
-  };
-  const uint32_t steps = (c + Lr - 1u) / Lr;
-  for (uint32_t t = 0; t < steps; ++t) {  // uniform
-    const uint32_t j = t * Lr + lane;
-    const bool act = lane < Lr && j < c;
-    // bucket: the last start <= slot (cb), the next one (nb), their count (bk)
-    uint32_t slot = x & 4095u, bk = 1, cb = 0, nb = 4096u;
-#pragma unroll
-    for (int i = 1; i < 13; ++i) {
-      const bool le = cum[i] <= slot;
-      bk += le ? 1u : 0u;
-      cb = le ? cum[i] : cb;
-    }
-#pragma unroll
-    for (int i = 12; i > 0; --i) nb = cum[i] > slot ? cum[i] : nb;
-    if (act) x = (nb - cb) * (x >> 12) + slot - cb;
-    renorm();
-    uint32_t g1 = 1;
-    if (act) {
-      const uint32_t kb = bk - 1u;
-      g1 = (1u << kb) | (x & ((1u << kb) - 1u));
-      x >>= kb;
-    }
-    renorm();
-    slot = x & 4095u;
-    const uint32_t cls = class_of_slot(slot);
-    if (act) x = class_freq(cls) * (x >> 12) + slot - class_start(cls);
-    renorm();
-    uint32_t esc = 0;
-    if (act && cls == 14u) {
-      esc = x & 0xFFu;
-      x >>= 8;
-    }
-    renorm();
-    uint32_t incl = act ? g1 : 0u;  // indices: running sum of gap + 1 in change order
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t tt = __shfl_up(incl, o);
-      if (lane >= (uint32_t)o) incl += tt;
-    }
-    const uint32_t idx = run + incl - 1u;
-    run += __shfl(incl, 63);
-    if (act) {
-      const bool ok = idx < len;
-      if (!ok) err |= CIERA_ST_PATCH;
-      err |= emit(j, idx, cls, esc, ok);
-    }
-  }
-  if (ptr + (ptr & 1u) != navail || (lane < Lr && x != kRansLow)) err |= CIERA_ST_PATCH;
-  return err;
-}
-
-// rans_decode_wave for 64/GS chunks at once, one per group of GS lanes: each
-// lane passes its group's chunk (win, nbytes, c, len; c = 0 for a group
-// without one) and emit(j, idx, cls, esc, ok) is called for the group's
-// changes.  The bucket starts are per group, held in every lane.  Returns the
-// lane's status bits, as rans_decode_wave.
 // Inclusive sum of v over each group of GS (16 or 64) lanes, in lane order,
 // with DPP row operations (a row is 16 lanes): shifts by 1, 2, 4 and 8 within
 // rows (lanes shifted in from outside the row read 0), then, for a whole wave,
@@ -2338,7 +2249,16 @@ __device__ __forceinline__ uint32_t group_incl_sum(uint32_t v) {
   return v;
 }
 
-template <int GS, bool LSEARCH, class Emit>
+// Decodes 64/GS chunks' coded data at once, one chunk per group of GS (16 or
+// 64) lanes: each lane passes its group's chunk (win: the data in LDS, nbytes
+// bytes; c changes among len values; c = 0 for a group without one) and, for
+// change j of the chunk, an active lane calls emit(j, idx, cls, esc, ok):
+// chunk offset idx, step class cls, escaped exponent esc, ok = idx inside the
+// chunk; emit returns status bits.  lcum: 16 words of LDS per group for its
+// gap-bucket starts, which each step searches.  Returns the lane's status
+// bits: ST_PATCH for words missing or left over, a final state other than
+// 2^16, a change past the chunk, and emit's.
+template <int GS, class Emit>
 __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint32_t nbytes, uint32_t c,
                                                        uint32_t len, uint32_t* lcum, Emit&& emit) {
   const uint32_t lane = lane_id(), gl = lane & (GS - 1u), g0 = lane - gl;
@@ -2349,18 +2269,11 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
   const uint16_t* words = reinterpret_cast<const uint16_t*>(win + Lr);
   uint32_t gf, gcum;
   gap_table<GS>(live ? c : 1u, live ? len : (uint32_t)kSub, gf, gcum);
-  uint32_t cum[13];
-  uint32_t* const gc = lcum + (g0 / GS) * 16u;  // LSEARCH: the group's starts, then 4096 up to 16 entries
-  if constexpr (LSEARCH) {
-    if (gl < 16u) gc[gl] = gl < 13u ? gcum : 4096u;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  } else {
-    cum[0] = 0;
-#pragma unroll
-    for (int i = 1; i < 13; ++i) cum[i] = __shfl(gcum, i, GS);
-  }
+  uint32_t* const gc = lcum + (g0 / GS) * 16u;  // the group's starts, then 4096 up to 16 entries
+  if (gl < 16u) gc[gl] = gl < 13u ? gcum : 4096u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint32_t x = gl < Lr ? win[gl] : kRansLow;
   uint32_t ptr = 0, run = 0, err = 0;
   auto renorm = [&]() {
@@ -2381,28 +2294,17 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
   for (uint32_t t = 0; t < steps; ++t) {  // uniform
     const uint32_t j = t * Lr + gl;
     const bool act = gl < Lr && j < c;
-    uint32_t slot = x & 4095u, bk = 1, cb = 0, nb = 4096u;
-    if constexpr (LSEARCH) {  // the last start <= slot: four halving steps over 16 entries
-      uint32_t lo = 0;
+    // bucket: the last start <= slot (cb; four halving steps over 16
+    // entries), the next one (nb), their count (bk)
+    uint32_t slot = x & 4095u, cb = 0, lo = 0;
 #pragma unroll
-      for (uint32_t st = 8; st > 0; st >>= 1) {
-        const uint32_t v = gc[lo + st];
-        const bool le = v <= slot;
-        lo = le ? lo + st : lo;
-        cb = le ? v : cb;
-      }
-      bk = lo + 1u;
-      nb = gc[lo + 1u];
-    } else {
-#pragma unroll
-      for (int i = 1; i < 13; ++i) {
-        const bool le = cum[i] <= slot;
-        bk += le ? 1u : 0u;
-        cb = le ? cum[i] : cb;
-      }
-#pragma unroll
-      for (int i = 12; i > 0; --i) nb = cum[i] > slot ? cum[i] : nb;
+    for (uint32_t st = 8; st > 0; st >>= 1) {
+      const uint32_t v = gc[lo + st];
+      const bool le = v <= slot;
+      lo = le ? lo + st : lo;
+      cb = le ? v : cb;
     }
+    const uint32_t bk = lo + 1u, nb = gc[lo + 1u];
     if (act) x = (nb - cb) * (x >> 12) + slot - cb;
     renorm();
     uint32_t g1 = 1;
@@ -2450,8 +2352,6 @@ __device__ __forceinline__ const uint8_t* rank_stream(const DecItem& d, uint32_t
 // change: offset | step class << 12 | escaped exponent << 16, all ones for a
 // change past the chunk, as two 16-bit stores) leaves them there; the merge
 // reads them before it writes the values.  Other chunks are left to the merge.
-template <int GS>
-constexpr bool kLsearch = true;          // gap buckets by a search over starts in LDS
 constexpr uint32_t kPackMax = 64;        // changes of a chunk decoded in a 16-lane group
 constexpr uint32_t kPackBytes = 1024;    // its data, at most
 template <int DT, int U>
@@ -2530,7 +2430,7 @@ __global__ __launch_bounds__(64) void coded_prepass_kernel(const DecItem* __rest
       rec[2 * j + 1] = (uint16_t)(v >> 16);
       return 0u;
     };
-    return rans_decode_groups<GS, kLsearch<GS>>(win, bg, cg, lg, s_lc, emit);
+    return rans_decode_groups<GS>(win, bg, cg, lg, s_lc, emit);
   };
   uint32_t err = 0;
   if (packed) {  // four small chunks at once, 16 lanes each
@@ -2574,6 +2474,7 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
   uint32_t (*const s_stage)[kStage / 4] = reinterpret_cast<uint32_t (*)[kStage / 4]>(s_share);
   uint32_t (*const s_win)[CODED ? kSub / 4 : 1] = reinterpret_cast<uint32_t (*)[CODED ? kSub / 4 : 1]>(s_share);
   __shared__ uint8_t s_mark[CODED ? U : 1][64];  // coded: blocks of each row that were patched
+  __shared__ uint32_t s_lcm[CODED ? U : 1][16];  // coded: gap-bucket starts of each row the merge decodes
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint32_t tpi = tpr * world;
@@ -2809,9 +2710,9 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
         if ((int)wave < U && coded[wave] && !recs[wave]) {  // uniform per wave: wave u decodes row u
           const uint32_t u = wave;
           uint8_t* const rowex = s_exb + u * kDecRow;
-          const uint32_t err = rans_decode_wave(&s_win[u][0], nbytes[u], c[u], len[u],
-                                                [&](uint32_t, uint32_t idx, uint32_t cls, uint32_t esc,
-                                                    bool ok) -> uint32_t {
+          const uint32_t err = rans_decode_groups<64>(&s_win[u][0], nbytes[u], c[u], len[u], &s_lcm[u][0],
+                                                      [&](uint32_t, uint32_t idx, uint32_t cls, uint32_t esc,
+                                                          bool ok) -> uint32_t {
             if (!ok) return 0u;
             const uint32_t nv = cls == 14u ? esc : (rowex[idx] + class_step(cls)) & 0xFFu;
             if (nv > Tr<DT>::EMASK) return CIERA_ST_PATCH;
@@ -3135,6 +3036,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecItem* __re
   decode_tile<DT, U, CODED>(items, item0, tpr, world, status_out, batch_id, blockIdx.x);
 }
 
+// The bf16 decode with coded rows, held to eight waves per SIMD: left to
+// itself the compiler gives it 106 scalar registers, which allow seven; at
+// eight it keeps the excess in vector-register lanes, without scratch
+// (bf16, 10% change: coded decode 534 -> 505 us; 1%: unchanged).  fp16 and
+// fp32 would spill to scratch at eight.
+template <int U>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(8))) void decode_coded_bf16_kernel(
+    const DecItem* __restrict__ items, uint32_t item0, uint32_t tpr, uint32_t world, uint32_t* status_out,
+    uint32_t batch_id) {
+  decode_tile<1, U, true>(items, item0, tpr, world, status_out, batch_id, blockIdx.x);
+}
+
 // The same decode from a grid of fewer workgroups than tiles, each taking
 // tiles bid, bid + gridDim.x, ... in turn: a caller that runs the decode beside
 // other work bounds the compute units it occupies.
@@ -3330,6 +3243,17 @@ hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs&
   return hipSuccess;
 }
 
+template <int DT, int U>
+static void launch_coded_merge(dim3 grid, hipStream_t s, const DecItem* items, uint32_t item0, uint32_t tpr,
+                               uint32_t world, uint32_t* status, uint32_t batch_id) {
+  if constexpr (DT == 1)
+    hipLaunchKernelGGL((decode_coded_bf16_kernel<U>), grid, dim3(kDecThreads), 0, s, items, item0, tpr, world, status,
+                       batch_id);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT, U, true>), grid, dim3(kDecThreads), 0, s, items, item0, tpr, world, status,
+                       batch_id);
+}
+
 static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem* items, uint32_t item0, uint32_t nitems,
                                      uint32_t tpr, uint32_t world, uint32_t* status, uint32_t batch_id,
                                      uint32_t max_wg, hipStream_t s) {
@@ -3342,13 +3266,10 @@ static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem
     switch (dtype * 8 + u) {
       case 9: CIERA_DECB(1, 1); break;
       case 10: CIERA_DECB(1, 2); break;
-      case 12: CIERA_DECB(1, 4); break;
       case 17: CIERA_DECB(2, 1); break;
       case 18: CIERA_DECB(2, 2); break;
-      case 20: CIERA_DECB(2, 4); break;
       case 25: CIERA_DECB(3, 1); break;
       case 26: CIERA_DECB(3, 2); break;
-      case 28: CIERA_DECB(3, 4); break;
       default: return hipErrorInvalidValue;
     }
 #undef CIERA_DECB
@@ -3361,8 +3282,7 @@ static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem
     if (coded) {                                                                                            \
       hipLaunchKernelGGL((coded_prepass_kernel<DT, U>), pgrid, dim3(64), 0, s, items, item0, tpr, world, status, \
                          batch_id);                                                                         \
-      hipLaunchKernelGGL((decode_kernel<DT, U, true>), grid, block, 0, s, items, item0, tpr, world, status,  \
-                         batch_id);                                                                         \
+      launch_coded_merge<DT, U>(grid, s, items, item0, tpr, world, status, batch_id);                      \
     } else {                                                                                                \
       hipLaunchKernelGGL((decode_kernel<DT, U, false>), grid, block, 0, s, items, item0, tpr, world,        \
                          status, batch_id);                                                                 \
@@ -3372,21 +3292,18 @@ static hipError_t launch_decode_part(int dtype, int u, bool coded, const DecItem
     switch (u) {
       case 1: CIERA_DEC(1, 1); break;
       case 2: CIERA_DEC(1, 2); break;
-      case 4: CIERA_DEC(1, 4); break;
       default: return hipErrorInvalidValue;
     }
   } else if (dtype == 2) {
     switch (u) {
       case 1: CIERA_DEC(2, 1); break;
       case 2: CIERA_DEC(2, 2); break;
-      case 4: CIERA_DEC(2, 4); break;
       default: return hipErrorInvalidValue;
     }
   } else if (dtype == 3) {
     switch (u) {
       case 1: CIERA_DEC(3, 1); break;
       case 2: CIERA_DEC(3, 2); break;
-      case 4: CIERA_DEC(3, 4); break;
       default: return hipErrorInvalidValue;
     }
   } else {
