@@ -1111,10 +1111,10 @@ __device__ __forceinline__ uint32_t class_of_slot(uint32_t slot) {
 // rANS-codes one chunk's c (1..1024) changes, listed in LDS in index order as
 // offset | old exponent << 12 | new exponent << 20, with one wave (gap-bucket
 // frequencies and starts from gap_table in gf and gcum), and returns the
-// number of words.  With region_end (the end of the chunk's 4096-byte
-// stash region) the words go backwards from it, so they lie in decode order,
-// and the final states just below them when the data fits the region;
-// nothing is written below region_end - 4096.  Without it nothing is written.
+// number of words.  The words go backwards from region_end (the end of the
+// chunk's 4096-byte stash region), so they lie in decode order, and the final
+// states just below them when the data fits the region; nothing is written
+// below region_end - 4096.
 __device__ uint32_t rans_encode_chunk(const uint32_t* list, uint32_t c, uint32_t gf, uint32_t gcum,
                                       uint8_t* region_end) {
   const uint32_t lane = lane_id();
@@ -1129,7 +1129,7 @@ __device__ uint32_t rans_encode_chunk(const uint32_t* list, uint32_t c, uint32_t
     const uint32_t cnt = (uint32_t)__popcll(m);
     if (emit) {
       const uint32_t pos = R + cnt - lanes_below(m);  // words from the end, lower lanes first in decode order
-      if (region_end && 2u * pos <= 4096u) gp(reinterpret_cast<uint16_t*>(region_end - 2u * pos))[0] = (uint16_t)x;
+      if (2u * pos <= 4096u) gp(reinterpret_cast<uint16_t*>(region_end - 2u * pos))[0] = (uint16_t)x;
       x >>= 16;
     }
     R += cnt;
@@ -1154,7 +1154,7 @@ __device__ uint32_t rans_encode_chunk(const uint32_t* list, uint32_t c, uint32_t
     step(act && b > 1u, g1 - (1u << (b - 1u)), 1u, b - 1u, true);
     step(act, cb, fb, 12u, false);
   }
-  if (region_end && lane < L && 4u * L + 2u * R <= 4096u) {
+  if (lane < L && 4u * L + 2u * R <= 4096u) {
     G1 uint16_t* q = gp(reinterpret_cast<uint16_t*>(region_end - 2u * R - 4u * L + 4u * lane));
     q[0] = (uint16_t)x;
     q[1] = (uint16_t)(x >> 16);
@@ -1241,12 +1241,11 @@ __device__ __forceinline__ void split_tile_coded(const EncItem& d, uint32_t loca
       const uint32_t len = row_len(n, base + (uint64_t)(s0 + r) * kSub);
       uint32_t words = 0;
       bool dense = c[r] > kChunkMaxChanges;
-      if (c[r] > 0 && !dense) {  // measure, then write only coded data that is shorter than dense
+      if (c[r] > 0 && !dense) {  // coded into the region's end (writes past its start are dropped)
         uint32_t gf, gcum;
         gap_table(c[r], len, gf, gcum);
-        words = rans_encode_chunk(s_list[r], c[r], gf, gcum, nullptr);
-        dense = coded_bytes(c[r], words, false, len) >= pad4u(len);
-        if (!dense) (void)rans_encode_chunk(s_list[r], c[r], gf, gcum, regions + (uint32_t)(s0 + r + 1) * kSub);
+        words = rans_encode_chunk(s_list[r], c[r], gf, gcum, regions + (uint32_t)(s0 + r + 1) * kSub);
+        dense = coded_bytes(c[r], words, false, len) >= pad4u(len);  // then the dense bytes below replace it
       }
       if (lane == 0) s_info[s0 + r] = c[r] | (dense ? 0u : words << 13) | ((dense ? 1u : 0u) << 26);
     }
