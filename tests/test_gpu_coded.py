@@ -15,7 +15,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 from lossless_weight_compression_amd import _binding as B  # noqa: E402
-from tests.gpu_harness import say, to_np  # noqa: E402
+from tests.gpu_harness import DT, say, to_np  # noqa: E402
 from tests.test_gpu_block import run_block  # noqa: E402
 
 _SHIFT = {torch.bfloat16: (7, 0xFF, torch.int16), torch.float16: (10, 0x1F, torch.int16),
@@ -99,6 +99,29 @@ def test_exact_1024_and_1025_changes_per_chunk():
     w1 = exponent_steps(w0, m, [1, -1], 5)
     say("[gpu] coded 1024/1025")
     g, o = run_block([(2, 4096)], dtype, 1, 512, [w0], [w1], variant=[B.CODED])
+    assert g == 0 and o == 0
+
+
+# A last chunk shorter than 4096 values with more changes than its part of the
+# output holds as 4-byte records (c > len * 2 / 4 for the two-byte types), yet
+# coded shorter than dense: the prepass leaves it, and the merge decodes it
+# itself.  (tail values, change rate in the tail)
+MERGE_DECODED = [(100, 0.65), (37, 0.7), (1500, 0.6)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("tail,frac", MERGE_DECODED)
+def test_coded_chunks_the_merge_decodes_itself(dtype, tail, frac):
+    cols = 4096 + tail
+    w0, w1 = _pair(1, cols, dtype, 0.0, ("merge-decoded", str(dtype), tail, frac), (1,), ((4096, cols, frac),))
+    odt = DT[dtype]
+    ex0 = O.exponent_field(to_np(w0), odt)[4096:]
+    ex1 = O.exponent_field(to_np(w1), odt)[4096:]
+    c = int(np.count_nonzero(ex0 != ex1))
+    data = O.encode_chunk(ex1, ex0)
+    assert c * 4 > tail * 2 and len(data) < O.pad4(tail), (c, len(data))  # the case meant
+    say(f"[gpu] coded chunk of {tail} values, {c} changes, decoded by the merge, {dtype}")
+    g, o = run_block([(1, cols)], dtype, 1, 512, [w0], [w1], variant=[B.CODED])
     assert g == 0 and o == 0
 
 
