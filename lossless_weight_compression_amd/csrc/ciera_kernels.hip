@@ -668,6 +668,24 @@ __device__ __forceinline__ void load_x_pieces(const uint8_t* p, v4u pc[Tr<DT>::E
 #pragma unroll
   for (int q = 0; q < Tr<DT>::E; ++q) pc[q] = ldg16_nt(p + 16 * (64u * q + lane));
 }
+// load_x_pieces for a row of which only the first nb bytes (a multiple of the
+// value size) lie in the shard: pieces past them read as zeros, and the piece
+// that holds the last of them is read byte by byte.
+template <int DT>
+__device__ __forceinline__ void load_x_pieces_upto(const uint8_t* p, uint32_t nb, v4u pc[Tr<DT>::E]) {
+  const uint32_t lane = lane_id();
+#pragma unroll
+  for (int q = 0; q < Tr<DT>::E; ++q) {
+    const uint32_t o = 16u * (64u * q + lane);
+    if (o + 16u <= nb) {
+      pc[q] = ldg16_nt(p + o);
+    } else {
+      uint32_t w[4] = {0, 0, 0, 0};
+      if (o < nb) load_words<4>(p + o, nb - o, false, w);
+      pc[q].x = w[0]; pc[q].y = w[1]; pc[q].z = w[2]; pc[q].w = w[3];
+    }
+  }
+}
 template <int DT>
 __device__ __forceinline__ void swap_x_pieces(uint32_t* stage, const v4u pc[Tr<DT>::E], uint32_t xw[4 * Tr<DT>::E]) {
   constexpr int E = Tr<DT>::E;
@@ -1341,8 +1359,9 @@ __device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, uin
 // with a device-scope atomic -- and waits until every tile of its item has
 // published in this launch's epoch.  The counts give the item's total, hence
 // the mode [CIERA 3.2: compressed only when smaller], and the tile's exclusive
-// prefix, hence where its records go.  The tile stores its sign|mantissa
-// bytes while it waits (their place does not depend on the counts); once the
+// prefix, hence where its records go.  The tile stores each row's
+// sign|mantissa bytes as soon as the row is compared (their place does not
+// depend on the counts); once the
 // mode is known it stores its bitmap bytes and its records, and tile 0 the
 // header.  When the total makes the stream RAW although the plan compressed it
 // (rare), every tile rewrites the bytes of the raw body it owns -- those its
@@ -1405,36 +1424,55 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
   uint64_t mine_old = 0;                        // this tile's slot as the last launch left it
   if (tid == 0) mine_old = __hip_atomic_load(sync + local, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // loads, split and compare; the section words stay in registers until the
-  // mode is known (a RAW stream reads its values again).  A wave whose 1024
-  // values of row s are all in the shard loads them as contiguous pieces.
-  uint32_t smw[S][kSmWords<DT>], mask[S], expk[S][4];
+  // loads, split and compare, row by row: a wave loads its 1024 values of a
+  // row as contiguous pieces (those past the shard as zeros) and swaps them
+  // through LDS into each lane's 16 values; the row's sign|mantissa words are
+  // stored as soon as it is compared (a RAW stream reads its values again).
+  uint32_t mask[S], expk[S][4];
+  uint32_t smw[DT == 1 ? 1 : S][kSmWords<DT>];  // fp32/fp16: the records, kept for the stores below
   int cnt[S];
   bool whole[S];  // uniform per wave
   {
-    uint32_t xw[S][XW], cw[S][4];
+    uint32_t cw[S][4];
     v4u pc[S][E];
     const bool full = d.cache_aligned != 0 && base + T <= n;  // uniform
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
+    // Rows are loaded AH ahead of the one compared, so that a wave holds the
+    // raw words of at most AH + 1 rows at a time (registers for occupancy)
+    // while keeping that many rows of loads in flight.
+    constexpr int AH = S < 2 ? S : 2;
+    auto issue = [&](int s) {
       const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
       const uint64_t w0 = base + (uint64_t)s * kSub + (uint64_t)wave * 1024u;
       whole[s] = w0 + 1024u <= n;
       cnt[s] = full ? 16 : ((int)left_in(n, c0, 16));
-      if (cnt[s] > 0) {
-        if (whole[s]) load_x_pieces<DT>(d.x + w0 * E, pc[s]);
-        else load_words<XW, kNtBulk<DT>>(d.x + c0 * E, (uint32_t)cnt[s] * E, true, xw[s]);
-        load_words<4, true>(d.cache + c0, (uint32_t)cnt[s], full || d.cache_aligned != 0, cw[s]);
-      }
-    }
+      if (whole[s]) load_x_pieces<DT>(d.x + w0 * E, pc[s]);
+      else load_x_pieces_upto<DT>(d.x + w0 * E, (uint32_t)left_in(n, w0, 1024u) * E, pc[s]);
+      if (cnt[s] > 0) load_words<4, true>(d.cache + c0, (uint32_t)cnt[s], full || d.cache_aligned != 0, cw[s]);
+    };
 #pragma unroll
-    for (int s = 0; s < S; ++s) {  // a row's swap just before its compare: one row's raw words live at a time
-      if (whole[s]) swap_x_pieces<DT>(&s_stage[wave][0], pc[s], xw[s]);
+    for (int s = 0; s < AH; ++s) issue(s);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (s + AH < S) issue(s + AH);
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t xw[XW];
+      swap_x_pieces<DT>(&s_stage[wave][0], pc[s], xw);
       mask[s] = 0;
       expk[s][0] = expk[s][1] = expk[s][2] = expk[s][3] = 0;
-      if (full) mask[s] = chunk_exps<DT, true>(xw[s], cw[s], 16, expk[s]);
-      else if (cnt[s] > 0) mask[s] = chunk_exps<DT, false>(xw[s], cw[s], cnt[s], expk[s]);
-      chunk_sm_words<DT>(xw[s], smw[s]);
+      if (full) mask[s] = chunk_exps<DT, true>(xw, cw[s], 16, expk[s]);
+      else if (cnt[s] > 0) mask[s] = chunk_exps<DT, false>(xw, cw[s], cnt[s], expk[s]);
+      if constexpr (DT == 1) {
+        // bf16: the row's sign|mantissa bytes go out now, lane by lane (a
+        // COMPRESSED stream keeps them; a RAW one, rare, is rewritten below
+        // by the tiles that own its bytes)
+        if (d.compress != 0 && cnt[s] > 0) {
+          chunk_sm_words<DT>(xw, smw[0]);
+          store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(base + (uint64_t)s * kSub + (uint64_t)tid * kEPT),
+                             cnt[s], smw[0]);
+        }
+      } else {
+        chunk_sm_words<DT>(xw, smw[s]);
+      }
     }
   }
 
@@ -1477,23 +1515,19 @@ __device__ __forceinline__ void split_tile_self(const EncItem& d, uint32_t local
     if (lane == 0)
       __hip_atomic_store(sync + local, ((uint64_t)epoch << 32) | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  // the sign|mantissa records go out now, while the siblings' counts come in:
-  // a COMPRESSED stream keeps them; a RAW one (rare) is rewritten below by
-  // the tiles that own its bytes
-  if (d.compress != 0) {  // uniform
+  // fp32/fp16: the records go out now, while the siblings' counts come in,
+  // whole rows put together in LDS (the same buffer as the value swaps, so
+  // not between them)
+  if constexpr (DT != 1) {
+    if (d.compress != 0) {  // uniform
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
-      if (cnt[s] > 0) {
-        if constexpr (DT != 1) {
-          if (whole[s])
-            store_sm_pieces<DT>(d.stream + kHeader + sm_off<DT>(base + (uint64_t)s * kSub + (uint64_t)wave * 1024u),
-                                &s_stage[wave][0], smw[s]);
-          else
-            store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
-        } else {
+      for (int s = 0; s < S; ++s) {
+        const uint64_t c0 = base + (uint64_t)s * kSub + (uint64_t)tid * kEPT;
+        if (whole[s])
+          store_sm_pieces<DT>(d.stream + kHeader + sm_off<DT>(base + (uint64_t)s * kSub + (uint64_t)wave * 1024u),
+                              &s_stage[wave][0], smw[s]);
+        else if (cnt[s] > 0)
           store_sm_words<DT>(d.stream + kHeader + sm_off<DT>(c0), cnt[s], smw[s]);
-        }
       }
     }
   }
