@@ -551,7 +551,7 @@ ciera_status_t ciera_encode_launch(ciera_batch_t* batch, void* stream) {
         f.prefix = prefix;
         if ((e = launch_coded_scan(g.dtype, g.nitems, f, prefix, b->batch_id, st))) return device_error("encode scan launch", e);
       }
-      e = launch_encode_finish_tiles(g.dtype, g.nitems, f, b->batch_id, st);
+      e = launch_encode_finish_tiles(g.dtype, g.coded != 0, g.nitems, f, b->batch_id, st);
     } else {
       e = launch_encode_finish(g.dtype, items, g.item0, g.nitems, b->fin_wg, counts, stash, b->batch_id, st);
     }

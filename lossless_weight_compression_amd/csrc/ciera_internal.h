@@ -110,7 +110,8 @@ struct FinArgs {
 hipError_t launch_encode(int dtype, int sub, uint32_t nitems, const EncArgs& a, uint32_t batch_id, hipStream_t s);
 hipError_t launch_encode_finish(int dtype, const EncItem* items, uint32_t item0, uint32_t nitems, uint32_t wg_per_item,
                                 const uint32_t* counts, const uint32_t* stash, uint32_t batch_id, hipStream_t s);
-hipError_t launch_encode_finish_tiles(int dtype, uint32_t nitems, const FinArgs& f, uint32_t batch_id, hipStream_t s);
+hipError_t launch_encode_finish_tiles(int dtype, bool coded, uint32_t nitems, const FinArgs& f, uint32_t batch_id,
+                                      hipStream_t s);
 hipError_t launch_coded_scan(int dtype, uint32_t nitems, const FinArgs& f, uint64_t* prefix, uint32_t batch_id,
                              hipStream_t s);
 // max_wg: 0, or a bound on the workgroups of each launch (each then decodes
