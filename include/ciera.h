@@ -270,9 +270,11 @@ void ciera_set_sync_polls(uint32_t polls);
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation): the same streams, byte for byte, with the library's own
  * device array of CIERA_NOALLOC_SCRATCH_BYTES (one per device, held until the
- * process ends) in place of a caller's scratch.  It calls no allocating HIP or
- * library routine: the descriptors reach the device as kernel arguments of a
- * small kernel, which also clears the count words the tiles publish.  Limits:
+ * process ends) in place of a caller's scratch.  It allocates no memory,
+ * device or host: no hipMalloc or other allocating HIP or library routine, no
+ * heap -- the batch's launch groups and descriptors are laid out in fixed-size
+ * arrays, and the descriptors reach the device as kernel arguments of a small
+ * kernel, which also clears the count words the tiles publish.  Limits:
  * element patches and RAW (compress 0 or 1) of shards of at most 256 encode
  * tiles (2^21 values at B <= 1024), else CIERA_ERR_UNSUPPORTED; a batch whose
  * scratch (ciera_encode_scratch_bytes) exceeds CIERA_NOALLOC_SCRATCH_BYTES

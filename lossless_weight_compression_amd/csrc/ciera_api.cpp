@@ -200,25 +200,46 @@ struct EncPlan {
 // block-hash variant and coded patches).
 bool self_finished(uint32_t compress, uint64_t tpi) { return compress <= 1 && tpi <= kSelfTiles; }
 
+// An encode item's launch group: (dtype, S, tiles per item, coded, self),
+// after the checks of its tensor, rank and size.
+using EncKey = std::tuple<uint32_t, uint32_t, uint32_t, uint32_t, uint32_t>;
+ciera_status_t enc_item_key(const ciera_encode_item_t& it, EncKey* key) {
+  ciera_status_t s = check_tensor(&it.t);
+  if (s) return s;
+  if (it.rank >= it.t.world) return CIERA_ERR_INVALID_ARG;
+  uint64_t off, n;
+  shard_of(&it.t, it.rank, &off, &n);
+  if (n >= ((uint64_t)1 << 32)) return CIERA_ERR_UNSUPPORTED;
+  const uint32_t S = enc_sub(it.t.block_size, n);
+  const uint64_t T = (uint64_t)kSub * S;
+  const uint64_t tpi = std::max<uint64_t>(1, (n + T - 1) / T);
+  const uint32_t coded = it.compress == kCoded ? 1u : 0u;
+  // coded: the chunk table's u32 running byte counts hold the data of every
+  // chunk of the shard, 4096 bytes each at most
+  if (coded && n >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
+  *key = std::make_tuple(it.t.dtype, S, (uint32_t)tpi, coded, self_finished(it.compress, tpi) ? 1u : 0u);
+  return CIERA_OK;
+}
+
+// Scratch offsets of an encode batch of `count` items, `tiles` tiles and
+// `words` stash words: descriptors, sync words (uploaded as zeros), counts,
+// stashes.
+void enc_offsets(uint32_t count, uint64_t tiles, uint64_t words, EncPlan* pl) {
+  pl->off_items = 256;
+  pl->off_sync = align_up(pl->off_items + sizeof(EncItem) * (uint64_t)count, 256);
+  pl->upload = pl->off_sync + 8 * tiles;
+  pl->off_counts = align_up(pl->upload, 256);
+  pl->off_stash = align_up(pl->off_counts + 4 * tiles, 256);
+  pl->total = align_up(pl->off_stash + 4 * words, 256);
+}
+
 ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncPlan* pl) {
   if (count && !items) return CIERA_ERR_INVALID_ARG;
-  std::map<std::tuple<uint32_t, uint32_t, uint32_t, uint32_t, uint32_t>, std::vector<uint32_t>> by;
+  std::map<EncKey, std::vector<uint32_t>> by;
   for (uint32_t i = 0; i < count; ++i) {
-    const ciera_encode_item_t& it = items[i];
-    ciera_status_t s = check_tensor(&it.t);
-    if (s) return s;
-    if (it.rank >= it.t.world) return CIERA_ERR_INVALID_ARG;
-    uint64_t off, n;
-    shard_of(&it.t, it.rank, &off, &n);
-    if (n >= ((uint64_t)1 << 32)) return CIERA_ERR_UNSUPPORTED;
-    const uint32_t S = enc_sub(it.t.block_size, n);
-    const uint64_t T = (uint64_t)kSub * S;
-    const uint64_t tpi = std::max<uint64_t>(1, (n + T - 1) / T);
-    const uint32_t coded = it.compress == kCoded ? 1u : 0u;
-    // coded: the chunk table's u32 running byte counts hold the data of every
-    // chunk of the shard, 4096 bytes each at most
-    if (coded && n >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
-    by[std::make_tuple(it.t.dtype, S, (uint32_t)tpi, coded, self_finished(it.compress, tpi) ? 1u : 0u)].push_back(i);
+    EncKey key;
+    if (ciera_status_t s = enc_item_key(items[i], &key)) return s;
+    by[key].push_back(i);
   }
   if (by.size() > (size_t)kMaxGroups) return CIERA_ERR_UNSUPPORTED;
   uint64_t tiles = 0, words = 0;
@@ -244,12 +265,7 @@ ciera_status_t enc_layout(const ciera_encode_item_t* items, uint32_t count, EncP
     pl->order.insert(pl->order.end(), kv.second.begin(), kv.second.end());
     pl->groups.push_back(g);
   }
-  pl->off_items = 256;
-  pl->off_sync = align_up(pl->off_items + sizeof(EncItem) * (uint64_t)count, 256);
-  pl->upload = pl->off_sync + 8 * tiles;  // the sync words are uploaded as zeros
-  pl->off_counts = align_up(pl->upload, 256);
-  pl->off_stash = align_up(pl->off_counts + 4 * tiles, 256);
-  pl->total = align_up(pl->off_stash + 4 * words, 256);
+  enc_offsets(count, tiles, words, pl);
   return CIERA_OK;
 }
 
@@ -427,15 +443,11 @@ ciera_status_t check_encode_items(const ciera_encode_item_t* items, uint32_t cou
 
 // The batch's descriptors di[0..count) in group order; *any: some item may be
 // compressed; *max_bytes: the largest shard a finishing kernel may rewrite RAW.
-void fill_enc_items(const ciera_encode_item_t* items, uint32_t count, const EncPlan& pl, uint32_t batch_id,
-                    EncItem* di, uint32_t* any, uint64_t* max_bytes) {
-  *any = 0;
-  *max_bytes = 0;
-  for (uint32_t j = 0; j < count; ++j) {
-    const ciera_encode_item_t& it = items[pl.order[j]];
+void fill_enc_item(const ciera_encode_item_t& it, uint64_t tile0, uint64_t stash, uint32_t batch_id, EncItem& d,
+                   uint32_t* any, uint64_t* max_bytes) {
+  {
     uint64_t off, n;
     shard_of(&it.t, it.rank, &off, &n);
-    EncItem& d = di[j];
     d.x = static_cast<const uint8_t*>(it.shard);
     const bool blocks = it.compress == kBlockVariant;
     // the block-hash variant reads and updates the shard's hash cache instead
@@ -446,8 +458,8 @@ void fill_enc_items(const ciera_encode_item_t* items, uint32_t count, const EncP
     d.off = off;
     d.capacity = it.stream_capacity;
     const uint32_t S = enc_sub(it.t.block_size, n);
-    d.tile0 = pl.tile0[j];
-    d.stash = pl.stash[j];
+    d.tile0 = tile0;
+    d.stash = stash;
     d.tvals = (uint32_t)kSub * S;
     d.tpi = (uint32_t)std::max<uint64_t>(1, (n + d.tvals - 1) / d.tvals);
     const bool self = self_finished(it.compress, d.tpi);
@@ -463,21 +475,28 @@ void fill_enc_items(const ciera_encode_item_t* items, uint32_t count, const EncP
     if (d.compress && !self) *max_bytes = std::max<uint64_t>(*max_bytes, n * d.elem_bytes);
   }
 }
+void fill_enc_items(const ciera_encode_item_t* items, uint32_t count, const EncPlan& pl, uint32_t batch_id,
+                    EncItem* di, uint32_t* any, uint64_t* max_bytes) {
+  *any = 0;
+  *max_bytes = 0;
+  for (uint32_t j = 0; j < count; ++j)
+    fill_enc_item(items[pl.order[j]], pl.tile0[j], pl.stash[j], batch_id, di[j], any, max_bytes);
+}
 
-void set_enc_batch(BatchImpl* b, const EncPlan& pl, void* scratch, uint64_t scratch_bytes, uint32_t count,
-                   uint32_t any, uint64_t max_bytes) {
+void set_enc_batch(BatchImpl* b, const EncPlan& pl, const Group* groups, uint32_t ngroups, void* scratch,
+                   uint64_t scratch_bytes, uint32_t count, uint32_t any, uint64_t max_bytes) {
   b->magic = kEncMagic;
   b->scratch = static_cast<uint8_t*>(scratch);
   b->scratch_bytes = scratch_bytes;
   b->count = count;
-  b->ngroups = (uint32_t)pl.groups.size();
+  b->ngroups = ngroups;
   b->any_compress = any;
   b->fin_wg = (uint32_t)std::min<uint64_t>(64, std::max<uint64_t>(1, (max_bytes + 65535) / 65536));
   b->off_counts = pl.off_counts;
   b->off_stash = pl.off_stash;
   b->off_items = pl.off_items;
   b->off_sync = pl.off_sync;
-  for (size_t g = 0; g < pl.groups.size(); ++g) b->g[g] = pl.groups[g];
+  for (uint32_t g = 0; g < ngroups; ++g) b->g[g] = groups[g];
 }
 
 }  // namespace
@@ -502,7 +521,7 @@ ciera_status_t ciera_encode_prepare(const ciera_encode_item_t* items, uint32_t c
                  &max_bytes);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (hipError_t e = upload(scratch, blob.data(), blob.size(), st)) return device_error("descriptor upload", e);
-  set_enc_batch(b, pl, scratch, scratch_bytes, count, any, max_bytes);
+  set_enc_batch(b, pl, pl.groups.data(), (uint32_t)pl.groups.size(), scratch, scratch_bytes, count, any, max_bytes);
   return CIERA_OK;
 }
 
@@ -567,12 +586,54 @@ static_assert(kStaticScratchBytes == CIERA_NOALLOC_SCRATCH_BYTES, "static scratc
 
 ciera_status_t ciera_encode_noalloc(const ciera_encode_item_t* items, uint32_t count, void* stream) {
   if (count == 0) return CIERA_OK;
-  EncPlan pl;
-  ciera_status_t s = enc_layout(items, count, &pl);
-  if (s) return s;
-  if ((s = check_encode_items(items, count))) return s;
-  for (const Group& g : pl.groups)
-    if (!g.self) return CIERA_ERR_UNSUPPORTED;  // a finishing kernel would need a stash
+  if (!items) return CIERA_ERR_INVALID_ARG;
+  // The groups and the descriptors are laid out as ciera_encode lays them out
+  // (same checks in the same order, groups in ascending key order), without
+  // heap memory: the keys in a fixed array, each group's descriptors found by
+  // a pass over the items, sent a kernel argument pack at a time.
+  EncKey keys[kMaxGroups];
+  uint32_t nkeys = 0;
+  bool too_many = false;
+  for (uint32_t i = 0; i < count; ++i) {
+    EncKey key;
+    if (ciera_status_t s = enc_item_key(items[i], &key)) return s;
+    const EncKey* hit = std::find(keys, keys + nkeys, key);
+    if (hit == keys + nkeys) {
+      if (nkeys == (uint32_t)kMaxGroups) too_many = true;
+      else keys[nkeys++] = key;
+    }
+  }
+  if (too_many) return CIERA_ERR_UNSUPPORTED;
+  std::sort(keys, keys + nkeys);
+  Group groups[kMaxGroups];
+  uint64_t tiles = 0;
+  uint32_t item0 = 0;
+  bool all_self = true;
+  for (uint32_t k = 0; k < nkeys; ++k) {
+    Group& g = groups[k];
+    g = Group{};
+    g.dtype = std::get<0>(keys[k]);
+    g.unit = std::get<1>(keys[k]);
+    g.tpi = std::get<2>(keys[k]);
+    g.coded = std::get<3>(keys[k]);
+    g.self = std::get<4>(keys[k]);
+    g.item0 = item0;
+    for (uint32_t i = 0; i < count; ++i) {
+      EncKey key;
+      (void)enc_item_key(items[i], &key);  // checked above
+      if (key == keys[k]) ++g.nitems;
+    }
+    if ((uint64_t)g.nitems * g.tpi >= ((uint64_t)1 << 31)) return CIERA_ERR_UNSUPPORTED;
+    g.tile0 = tiles;
+    g.stash0 = 0;
+    tiles += (uint64_t)g.nitems * g.tpi;
+    item0 += g.nitems;
+    all_self = all_self && g.self;
+  }
+  EncPlan pl;  // offsets only
+  enc_offsets(count, tiles, 0, &pl);
+  if (ciera_status_t s = check_encode_items(items, count)) return s;
+  if (!all_self) return CIERA_ERR_UNSUPPORTED;  // a finishing kernel would need a stash
   if (pl.total > kStaticScratchBytes) return CIERA_ERR_BUFFER_TOO_SMALL;
   void* base = nullptr;
   if (hipError_t e = static_scratch(&base)) return device_error("static scratch lookup", e);
@@ -580,18 +641,39 @@ ciera_status_t ciera_encode_noalloc(const ciera_encode_item_t* items, uint32_t c
   std::memset(&batch, 0, sizeof(batch));
   BatchImpl* b = impl(&batch);
   b->batch_id = next_id();
-  std::vector<EncItem> di(count);
-  uint32_t any;
-  uint64_t max_bytes;
-  fill_enc_items(items, count, pl, b->batch_id, di.data(), &any, &max_bytes);
   uint8_t* const sb = static_cast<uint8_t*>(base);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // descriptors by kernel arguments; the sync words zeroed by the same launch
-  if (hipError_t e = launch_enc_desc(di.data(), count, reinterpret_cast<EncItem*>(sb + pl.off_items),
-                                     reinterpret_cast<uint64_t*>(sb + pl.off_sync), (pl.upload - pl.off_sync) / 8,
-                                     reinterpret_cast<uint32_t*>(sb), b->batch_id, st))
-    return device_error("descriptor launch", e);
-  set_enc_batch(b, pl, base, kStaticScratchBytes, count, any, max_bytes);
+  EncItem* const dst = reinterpret_cast<EncItem*>(sb + pl.off_items);
+  constexpr uint32_t kPack = 30;  // descriptors per launch_enc_desc call (it cuts larger counts itself)
+  EncItem pack[kPack];
+  uint32_t np = 0, sent = 0, any = 0;
+  uint64_t max_bytes = 0;
+  // descriptors by kernel arguments; the first launch also zeroes the sync
+  // words the tiles publish in and writes the batch id
+  auto flush = [&]() -> hipError_t {
+    hipError_t e = launch_enc_desc(pack, np, dst + sent, sent == 0 ? reinterpret_cast<uint64_t*>(sb + pl.off_sync)
+                                                                   : nullptr,
+                                   sent == 0 ? (pl.upload - pl.off_sync) / 8 : 0,
+                                   sent == 0 ? reinterpret_cast<uint32_t*>(sb) : nullptr, b->batch_id, st);
+    sent += np;
+    np = 0;
+    return e;
+  };
+  for (uint32_t k = 0; k < nkeys; ++k) {
+    uint64_t tile = groups[k].tile0;
+    for (uint32_t i = 0; i < count; ++i) {
+      EncKey key;
+      (void)enc_item_key(items[i], &key);
+      if (key != keys[k]) continue;
+      fill_enc_item(items[i], tile, 0, b->batch_id, pack[np++], &any, &max_bytes);
+      tile += groups[k].tpi;
+      if (np == kPack)
+        if (hipError_t e = flush()) return device_error("descriptor launch", e);
+    }
+  }
+  if (np)
+    if (hipError_t e = flush()) return device_error("descriptor launch", e);
+  set_enc_batch(b, pl, groups, nkeys, base, kStaticScratchBytes, count, any, max_bytes);
   return ciera_encode_launch(&batch, stream);
 }
 
