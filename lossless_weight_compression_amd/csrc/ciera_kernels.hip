@@ -1120,7 +1120,7 @@ __device__ __forceinline__ uint32_t class_step(uint32_t cls) {
 }
 __device__ __forceinline__ uint32_t class_freq(uint32_t cls) { return cls < 2u ? 2032u : (cls < 14u ? 2u : 8u); }
 __device__ __forceinline__ uint32_t class_start(uint32_t cls) {
-  return cls < 2u ? 2032u * cls : (cls < 14u ? 4064u + 2u * (cls - 2u) : 4088u);
+  return cls < 2u ? (cls ? 2032u : 0u) : (cls < 14u ? 4064u + 2u * (cls - 2u) : 4088u);
 }
 __device__ __forceinline__ uint32_t class_of_slot(uint32_t slot) {
   return slot < 2032u ? 0u : slot < 4064u ? 1u : slot < 4088u ? 2u + ((slot - 4064u) >> 1) : 14u;
@@ -2326,15 +2326,15 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint32_t x = gl < Lr ? win[gl] : kRansLow;
   uint32_t ptr = 0, run = 0, err = 0;
+  // Lanes past the states (and groups without a chunk) hold kRansLow and
+  // never change, so x < kRansLow alone picks the lanes that take a word.  A
+  // word past the data reads as 0; the final count check flags it.
   auto renorm = [&]() {
-    const bool need = gl < Lr && x < kRansLow;
-    const uint64_t m = __ballot(need) & gmask;
-    if (need) {
+    const uint64_t m = __builtin_amdgcn_uicmp(x, kRansLow, 36) & gmask;  // 36: unsigned less-than
+    if (x < kRansLow) {
       const uint32_t pos = ptr + lanes_below(m);
-      uint32_t w = 0;
-      if (pos < navail) w = words[pos];
-      else err |= CIERA_ST_PATCH;
-      x = (x << 16) | w;
+      const uint32_t w = words[pos < navail ? pos : 0u];
+      x = (x << 16) | (pos < navail ? w : 0u);
     }
     ptr += (uint32_t)__popcll(m);
   };
@@ -2344,18 +2344,14 @@ __device__ __forceinline__ uint32_t rans_decode_groups(const uint32_t* win, uint
   for (uint32_t t = 0; t < steps; ++t) {  // uniform
     const uint32_t j = t * Lr + gl;
     const bool act = gl < Lr && j < c;
-    // bucket: the last start <= slot (cb; four halving steps over 16
-    // entries), the next one (nb), their count (bk)
-    uint32_t slot = x & 4095u, cb = 0, lo = 0;
+    // bucket: the last start <= slot (four halving steps over 16 entries;
+    // the first start is 0), its start (cb), the next one (nb), their count
+    // (bk)
+    uint32_t slot = x & 4095u, lo = 0;
 #pragma unroll
-    for (uint32_t st = 8; st > 0; st >>= 1) {
-      const uint32_t v = gc[lo + st];
-      const bool le = v <= slot;
-      lo = le ? lo + st : lo;
-      cb = le ? v : cb;
-    }
-    const uint32_t bk = lo + 1u, nb = gc[lo + 1u];
-    if (act) x = (nb - cb) * (x >> 12) + slot - cb;
+    for (uint32_t st = 8; st > 0; st >>= 1) lo = gc[lo + st] <= slot ? lo + st : lo;
+    const uint32_t bk = lo + 1u, cb = gc[lo], nb = gc[lo + 1u];
+    if (act) x = __umul24(nb - cb, x >> 12) + slot - cb;  // both factors below 2^24
     renorm();
     uint32_t g1 = 1;
     if (act) {
