@@ -2508,8 +2508,8 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
   __shared__ uint32_t s_ex[T / 4];   // the tile's exponents: cached, then patched in place
   __shared__ uint32_t s_sum[kDecThreads / 64];
   constexpr bool XP = kSmPieces<DT> != 0;  // records of whole wave rows swapped through LDS
-  // each wave's exchange buffer: fp32/fp16 records in, bf16/fp32 values out
-  constexpr uint32_t kStage = DT == 3 ? kSmWaveRow<DT> : kSmWaveRow<DT> > 1024u * E ? kSmWaveRow<DT> : 1024u * E;
+  // each wave's exchange buffer: fp32/fp16 records in, values out
+  constexpr uint32_t kStage = kSmWaveRow<DT> > 1024u * E ? kSmWaveRow<DT> : 1024u * E;
   // coded patches (the tensor's streams may be CODED): each row's chunk data.
   // It shares LDS with the exchange buffers: the exchanges run before the
   // first barrier (records in) and after the patch phase (values out), the
@@ -3010,19 +3010,28 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
       const uint64_t c0 = ts + (uint64_t)u * kDecRow + (uint64_t)tid * kEPT;
       // A wave whose 1024 values of the row are all in the shard stores them as
       // contiguous pieces through its LDS buffer: whole-line stores instead of
-      // 16-byte pieces strided 32 or 64 bytes apart (bf16 and fp32; the fp16
-      // join holds too many registers for it, 57 -> 82 VGPRs, and loses).
+      // 16-byte pieces strided 32 or 64 bytes apart.
       // The stores are non-temporal: written once, never read by this launch,
       // and streamed out in address order instead of left dirty in the caches
       // for the next kernel to write back (1% layer: decode 341 -> 322 us and
       // the encode after it 34.9 -> 32.6 us in-step; alone, the decode takes 8
       // us longer, as it now pays its own write-back).
       const uint64_t w0 = ts + (uint64_t)u * kDecRow + (uint64_t)wave * 1024u;
-      if (DT != 3 && aligned && w0 + 1024u <= te) {  // uniform per wave
+      uint32_t hv[DT == 3 ? 8 : 1];  // fp16: two values per word, joined once for either store
+      if constexpr (DT == 3) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          hv[q] = join<DT>(sm_from_words<DT>(sw[u], 2 * q), byte_of(ex[u], 2 * q)) |
+                  (join<DT>(sm_from_words<DT>(sw[u], 2 * q + 1), byte_of(ex[u], 2 * q + 1)) << 16);
+      }
+      if (aligned && w0 + 1024u <= te) {  // uniform per wave
         uint32_t v[4 * E];
         if constexpr (DT == 1) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) bf16x4_join(sw[u][q], ex[u][q], v[2 * q], v[2 * q + 1]);
+        } else if constexpr (DT == 3) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = hv[q];
         } else {
 #pragma unroll
           for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
@@ -3047,19 +3056,24 @@ __device__ __forceinline__ void decode_tile(const DecItem* __restrict__ items, u
 #pragma unroll
         for (int q = 0; q < 4; ++q) bf16x4_join(sw[u][q], ex[u][q], o[2 * q], o[2 * q + 1]);
         store_words<8>(out + c0 * E, (uint32_t)cnt[u] * E, aligned, o);
+      } else if constexpr (DT == 3) {
+        if (cnt[u] == 16 && aligned) {  // lane by lane: non-temporal too
+          v4u a, b;
+          a.x = hv[0]; a.y = hv[1]; a.z = hv[2]; a.w = hv[3];
+          b.x = hv[4]; b.y = hv[5]; b.z = hv[6]; b.w = hv[7];
+          stg16_nt(out + c0 * E, a);
+          stg16_nt(out + c0 * E + 16, b);
+        } else {
+          uint32_t v[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = (hv[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+          store16<DT>(out + c0 * E, cnt[u], v, aligned);
+        }
       } else {
         uint32_t v[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = join<DT>(sm_from_words<DT>(sw[u], j), byte_of(ex[u], j));
-        if (DT == 3 && cnt[u] == 16 && aligned) {  // fp16, lane by lane: non-temporal too
-          v4u a, b;
-          a.x = v[0] | (v[1] << 16); a.y = v[2] | (v[3] << 16); a.z = v[4] | (v[5] << 16); a.w = v[6] | (v[7] << 16);
-          b.x = v[8] | (v[9] << 16); b.y = v[10] | (v[11] << 16); b.z = v[12] | (v[13] << 16); b.w = v[14] | (v[15] << 16);
-          stg16_nt(out + c0 * E, a);
-          stg16_nt(out + c0 * E + 16, b);
-        } else {
-          store16<DT>(out + c0 * E, cnt[u], v, aligned);
-        }
+        store16<DT>(out + c0 * E, cnt[u], v, aligned);
       }
     }
     // cache write-back in whole 128-byte lines (8 lanes): scattered partial
