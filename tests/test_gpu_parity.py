@@ -219,7 +219,8 @@ def test_long_patch_lists(name, frac, dense):
 # Rows that some waves cover whole and others only in part: a wave whose 1024
 # values of a 4096-value row are all in the shard moves them as contiguous
 # 16-byte pieces swapped through LDS (encode loads of the values and fp32/fp16
-# record stores; decode record loads), the others lane by lane.  Shards end
+# record stores; decode fp32/fp16 record loads and the rebuilt values of every
+# type), the others lane by lane.  Shards end
 # inside a row at a wave boundary, just past one, mid-wave and one value short.
 WAVE_ROWS = [(1, 4096 + 1024), (1, 4096 + 1025), (1, 8192 + 3072 + 17), (1, 2 * 4096 - 1), (3, 7000),
              (1, 1024), (1, 1023), (5, 4096 + 2048 + 7)]
